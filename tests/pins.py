@@ -1,0 +1,257 @@
+"""Pin checks for the oracle: each function raises AssertionError when the
+oracle disagrees with something fixed independently of it (a brute force, a
+closed form from the proofs, a library routine, an exact enumeration).
+
+They are plain functions so that ``test_oracle_mutations.py`` can plant a
+plausible mistake in the oracle and confirm that some pin fails.
+"""
+
+import itertools
+import math
+from fractions import Fraction
+
+import mpmath
+import numpy as np
+from scipy.optimize import brentq, minimize
+
+from oracle import compress as oc
+from oracle import decode as od
+
+mpmath.mp.dps = 50
+
+
+# ---------------------------------------------------------------- PoissonComp
+def check_water_level_bruteforce(tq, b_free):
+    """Every j in 0..|U| is tried in exact rationals; the valid one (the top j
+    saturate, the rest do not, and the rates sum to the budget) must give the
+    oracle's c."""
+    tq = [int(x) for x in tq]
+    j_star, num, den = oc.water_level(np.array(tq, dtype=np.int64), b_free)
+    if den == 0:
+        assert b_free >= len(tq)
+        return
+    c_or = Fraction(num, den)
+    srt = sorted(tq, reverse=True)
+    valid = []
+    for j in range(len(srt)):
+        # candidate: the top j saturate, the others get c * tau
+        c = Fraction(b_free - j, sum(srt[j:]))
+        if c < 0:
+            continue
+        total = sum(min(Fraction(1), c * t) for t in srt)
+        if total == b_free:
+            valid.append(c)
+    assert valid, "brute force found no water level"
+    assert all(v == valid[0] for v in valid)
+    assert c_or == valid[0], (c_or, valid[0])
+    # the exact rates sum to the budget
+    total = sum(min(Fraction(1), c_or * t) for t in tq)
+    assert total == b_free
+
+
+def check_water_level_brentq(tau, budget, n_sink, n_local):
+    """scipy brentq on sum_U min(1, c tau) - B_U must find the oracle's c."""
+    sl = oc.compress_slice(tau, budget, n_sink, n_local, 0, 0, 0)
+    tq = sl["tq"][~sl["forced"]].astype(np.float64)
+    b_free = budget - int(sl["forced"].sum())
+    if sl["den"] == 0:
+        return
+    f = lambda c: np.minimum(1.0, c * tq).sum() - b_free  # noqa: E731
+    c_ref = brentq(f, 0.0, 1.0, xtol=1e-300, rtol=1e-15, maxiter=500)
+    c_or = sl["num"] / sl["den"]
+    assert abs(c_or - c_ref) <= 1e-12 * c_ref, (c_or, c_ref)
+
+
+def check_rates_sum(tau, budget, n_sink, n_local):
+    """sum_i r_i = budget: exactly in rationals, and to 1e-6 in float."""
+    sl = oc.compress_slice(tau, budget, n_sink, n_local, 0, 0, 0)
+    r = sl["r"].astype(np.float64)
+    assert abs(r.sum() - budget) <= 1e-6 * budget, (r.sum(), budget)
+    if sl["den"]:
+        in_h = sl["in_h"]
+        exact = int(in_h.sum()) * sl["den"] + \
+            int(sl["tq"][~in_h].sum()) * sl["num"]
+        assert exact == budget * sl["den"]
+    # monotone in tau among the free tokens; H/L partition
+    free = ~sl["forced"]
+    o = np.argsort(sl["tq"][free], kind="stable")
+    assert np.all(np.diff(sl["r"][free][o]) >= 0)
+    assert np.all(sl["in_h"] ^ sl["in_l"])
+    assert np.all(sl["r"][sl["in_l"]] < 1.0) and np.all(sl["r"] > 0)
+    assert np.all(sl["in_h"][sl["forced"]])
+
+
+# ---------------------------------------------------------------- shrinkage
+def check_shrinkage_lbfgsb(w, r):
+    """Theorem 1: the Definition 2 coefficients minimise eq. 6 over the box
+    [r_i, 1]; scipy's L-BFGS-B from several starts must agree."""
+    beta = od.shrinkage_beta(w, r)
+    lam = od.lambdas(w, r, beta)
+    f = lambda x: od_mse_plain(x, w, r)  # noqa: E731
+
+    def grad(x):
+        bias = np.sum(w * (1 - x))
+        return -2 * w * bias + 2 * w * w * x * (1 - r) / r
+
+    best = None
+    for x0 in (r.copy(), np.ones_like(r), 0.5 * (r + 1)):
+        res = minimize(f, x0, jac=grad, method="L-BFGS-B",
+                       bounds=list(zip(r, np.ones_like(r))),
+                       options=dict(ftol=1e-15, gtol=1e-13, maxiter=10000))
+        if best is None or res.fun < best.fun:
+            best = res
+    assert np.max(np.abs(best.x - lam)) <= 1e-6, (best.x, lam)
+    # and the fixed point: beta = sum w (1 - lambda)
+    assert abs(np.sum(w * (1 - lam)) - beta) <= 1e-12 * max(beta, 1e-300)
+
+
+def od_mse_plain(lam, w, r):
+    """eq. 6 written out independently of the oracle's own mse()."""
+    bias = 0.0
+    var = 0.0
+    for li, wi, ri in zip(lam, w, r):
+        bias += wi - li * wi
+        var += li * li * wi * wi * (1 - ri) / ri
+    return bias * bias + var
+
+
+def check_kkt(w, r):
+    """First-order conditions of eq. 6 on the box (proof of Theorem 1):
+    df/dlambda_i = -2 w_i beta + 2 w_i^2 lambda_i (1 - r_i)/r_i is >= 0 at the
+    lower bound, 0 inside and <= 0 at the upper bound."""
+    beta = od.shrinkage_beta(w, r)
+    lam = od.lambdas(w, r, beta)
+    assert np.all(lam >= r * (1 - 1e-15)) and np.all(lam <= 1.0)
+    bias = np.sum(w * (1 - lam))
+    gr = -2 * w * bias + 2 * w * w * lam * (1 - r) / r
+    tol = 1e-9 * np.max(np.abs(2 * w * bias)) + 1e-300
+    at_lo = np.isclose(lam, r, rtol=0, atol=1e-14)
+    at_hi = np.isclose(lam, 1.0, rtol=0, atol=1e-14)
+    inner = ~(at_lo | at_hi)
+    assert np.all(gr[at_lo & ~at_hi] >= -tol)
+    assert np.all(gr[at_hi & ~at_lo] <= tol)
+    assert np.all(np.abs(gr[inner]) <= tol)
+    # better than both endpoints of the box (Figure 2's shape)
+    m = od_mse_plain(lam, w, r)
+    assert m <= od_mse_plain(np.ones_like(r), w, r) * (1 + 1e-12)
+    assert m <= od_mse_plain(r, w, r) * (1 + 1e-12)
+
+
+# ---------------------------------------------------------------- certificate
+def check_bernstein_root(V, b, delta):
+    """Lemma 1's proof: t = D * (eps^ - beta/D) is the positive root of
+    t^2 = 2 l (V + b t / 3), and Bernstein's two-sided tail
+    2 exp(-t^2 / (2V + 2bt/3)) equals delta there."""
+    D = 3.0
+    e = float(od.eps_hat(0.0, V, b, D, delta))
+    t = mpmath.mpf(e) * D
+    l = mpmath.log(mpmath.mpf(2) / mpmath.mpf(delta))
+    lhs = t * t
+    rhs = 2 * l * (mpmath.mpf(V) + mpmath.mpf(b) * t / 3)
+    assert abs(lhs - rhs) <= 1e-12 * abs(rhs), (lhs, rhs)
+    tail = 2 * mpmath.exp(-t * t / (2 * mpmath.mpf(V) + 2 * mpmath.mpf(b) * t / 3))
+    assert abs(tail - delta) <= 1e-10 * delta, (tail, delta)
+    # and with a bias: eps^ D = beta + t
+    e2 = float(od.eps_hat(0.7, V, b, D, delta))
+    assert abs(e2 * D - 0.7 - float(t)) <= 1e-12 * (float(t) + 0.7)
+
+
+def enumerate_estimator(wH, w, r, lam):
+    """All 2^|L| outcomes of the Poisson sample: returns (values, probs)."""
+    nl = len(w)
+    vals = []
+    probs = []
+    for z in itertools.product((0, 1), repeat=nl):
+        z = np.array(z)
+        vals.append(np.sum(wH) + np.sum(z * lam * w / r))
+        probs.append(np.prod(np.where(z == 1, r, 1 - r)))
+    return np.array(vals), np.array(probs)
+
+
+def check_enumeration(wH, w, r, delta, estimator=od.EST_CLIP):
+    """Exact enumeration with exact weights (the perfect sketch): the bias is
+    -beta(L), the variance V(L) (proof of Theorem 1), and
+    Pr(|D^ - D|/D > eps^(L)) <= delta (Lemma 1)."""
+    D = float(np.sum(wH) + np.sum(w))
+    pos = np.arange(len(w))
+    plan = od.plan_row(w, r, pos, D, 1e9, delta, estimator)
+    vals, probs = enumerate_estimator(wH, w, r, plan["lam"])
+    mean = float(np.sum(vals * probs))
+    var = float(np.sum((vals - mean) ** 2 * probs))
+    beta_l = float(np.sum(w * (1 - plan["lam"])))
+    assert abs((mean - D) + beta_l) <= 1e-10 * D, (mean - D, -beta_l)
+    assert abs(var - plan["V_L"]) <= 1e-9 * max(var, 1e-300), (var, plan["V_L"])
+    assert abs(plan["beta_L"] - beta_l) <= 1e-12 * D
+    fail = float(np.sum(probs[np.abs(vals - D) / D > plan["eps_hat0"]]))
+    assert fail <= delta, (fail, delta)
+    if estimator == od.EST_UNBIASED:
+        assert abs(mean - D) <= 1e-12 * D
+
+
+# ---------------------------------------------------------------- gains / k*
+def mp_eps(beta_i, v_i, b_i, keep, D, delta):
+    l = mpmath.log(mpmath.mpf(2) / mpmath.mpf(delta))
+    a = l / 3
+    be = mpmath.fsum(mpmath.mpf(x) for x, k in zip(beta_i, keep) if k)
+    V = mpmath.fsum(mpmath.mpf(x) for x, k in zip(v_i, keep) if k)
+    bs = [mpmath.mpf(x) for x, k in zip(b_i, keep) if k]
+    b = max(bs) if bs else mpmath.mpf(0)
+    return (be + a * b + mpmath.sqrt((a * b) ** 2 + 2 * V * l)) / mpmath.mpf(D)
+
+
+def check_gains_loo(beta_i, v_i, b_i, D, delta):
+    """eq. 9 by brute force: recompute eps^(L \\ {i}) from scratch at 50
+    digits for every i and compare with the closed form (R11)."""
+    n = len(beta_i)
+    g = od.gains(beta_i, v_i, b_i, D, delta)
+    full = mp_eps(beta_i, v_i, b_i, [True] * n, D, delta)
+    for i in range(n):
+        keep = [True] * n
+        keep[i] = False
+        ref = full - mp_eps(beta_i, v_i, b_i, keep, D, delta)
+        assert abs(mpmath.mpf(g[i]) - ref) <= 1e-11 * abs(full) + 1e-300, \
+            (i, g[i], ref)
+        assert g[i] >= 0.0
+
+
+def check_kstar_bruteforce(w, r, D, eps, delta):
+    """eq. 10 by brute force: recompute eps^(L_g[k:]) from scratch for every
+    k at 50 digits; it must be non-increasing and give the oracle's k*."""
+    n = len(w)
+    pos = np.arange(n)
+    plan = od.plan_row(w, r, pos, D, eps, delta)
+    if plan["order"] is None:
+        assert plan["eps_hat0"] < eps
+        return plan
+    order = plan["order"]
+    # order must sort the closed-form gains descending, ties by position
+    g = plan["gains"]
+    for a_, b_ in zip(order[:-1], order[1:]):
+        assert g[a_] > g[b_] or (g[a_] == g[b_] and pos[a_] < pos[b_])
+    prev = None
+    k_ref = None
+    for k in range(n + 1):
+        keep = [False] * n
+        for idx in order[k:]:
+            keep[idx] = True
+        e = mp_eps(plan["beta_i"], plan["v_i"], plan["b_i"], keep, D, delta)
+        if prev is not None:
+            assert e <= prev * (1 + mpmath.mpf("1e-14")) + mpmath.mpf("1e-300")
+        prev = e
+        if k_ref is None and e < eps:
+            k_ref = k
+        assert abs(mpmath.mpf(plan["suffix"][k]) - e) <= 1e-12 * abs(e) + 1e-300
+    assert plan["k_star"] == k_ref, (plan["k_star"], k_ref)
+    return plan
+
+
+def check_range_bound(w, r):
+    """Lemma 1's proof bounds each centred term X_i = lambda_i w_i (Z_i - r_i)
+    / r_i by b_i; the bound is attained by one of the two outcomes."""
+    beta = od.shrinkage_beta(w, r)
+    lam = od.lambdas(w, r, beta)
+    _, _, b_i = od.cert_terms(w, r, lam)
+    x1 = np.abs(lam * w * (1 - r) / r)
+    x0 = np.abs(lam * w * (0 - r) / r)
+    top = np.maximum(x0, x1)
+    assert np.allclose(top, b_i, rtol=1e-13, atol=0)

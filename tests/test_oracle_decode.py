@@ -1,0 +1,265 @@
+"""Pins for the KVFetch oracle (CPU only)."""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import compress as oc
+from oracle import decode as od
+from tests import pins
+from workloads import bf16_to_f32, make_decode_workload
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_lr(rng, n, spread=3.0):
+    w = np.exp(rng.normal(0, spread, n))
+    r = rng.uniform(0.02, 0.95, n)
+    return w, r
+
+
+def test_shrinkage_golden():
+    with open(os.path.join(GOLDEN, "shrinkage_small.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        w, r = np.array(c["w"]), np.array(c["r"])
+        beta = od.shrinkage_beta(w, r)
+        assert abs(beta - c["beta"]) <= 1e-14 * c["beta"]
+        lam = od.lambdas(w, r, beta)
+        assert np.allclose(lam, c["lam"], rtol=0, atol=1e-14)
+        bi, vi, b_i = od.cert_terms(w, r, lam)
+        assert abs(vi.sum() - c["V"]) <= 1e-14 * c["V"]
+        b1, b2, im = od.top2(b_i)
+        assert (abs(b1 - c["b"]), abs(b2 - c["b2"]), im) == \
+            (pytest.approx(0, abs=1e-14), pytest.approx(0, abs=1e-14),
+             c["argmax_unique"])
+        assert od.mse(lam, w, r) == pytest.approx(c["mse"], rel=1e-14)
+        assert od.mse(np.ones_like(r), w, r) == pytest.approx(
+            c["mse_unbiased"], rel=1e-14)
+        assert od.mse(r, w, r) == pytest.approx(c["mse_lower"], rel=1e-14)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_shrinkage_is_mse_minimiser(seed):
+    rng = np.random.default_rng(100 + seed)
+    w, r = _rand_lr(rng, int(rng.integers(2, 13)))
+    pins.check_shrinkage_lbfgsb(w, r)
+    pins.check_kkt(w, r)
+
+
+def _heavy(rng, n):
+    w = np.exp(rng.normal(0, 1, n))
+    r = rng.uniform(0.2, 0.9, n)
+    k = max(1, n // 8)
+    w[:k] *= 50.0
+    r[:k] = rng.uniform(0.02, 0.1, k)
+    return w, r
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_shrinkage_heavy_tokens(seed):
+    """Heavy tokens with small r. At the fixed point beta* >= max_i w_i(1-r_i)
+    (below that, the heaviest token alone would contribute more than beta), so
+    lambda_i >= r_i holds without the lower clip."""
+    rng = np.random.default_rng(150 + seed)
+    w, r = _heavy(rng, int(rng.integers(4, 13)))
+    beta = od.shrinkage_beta(w, r)
+    assert beta >= np.max(w * (1 - r)) * (1 - 1e-15)
+    assert beta <= np.sum(w * (1 - r)) * (1 + 1e-15)
+    pins.check_shrinkage_lbfgsb(w, r)
+    pins.check_kkt(w, r)
+    pins.check_range_bound(w, r)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_kkt_large(seed):
+    rng = np.random.default_rng(200 + seed)
+    w, r = _rand_lr(rng, 5000, spread=4.0)
+    pins.check_kkt(w, r)
+
+
+@pytest.mark.parametrize("V,b,delta", [(1.0, 0.5, 0.05), (1e-6, 3.0, 0.1),
+                                       (250.0, 1e-9, 0.01), (0.0, 2.0, 0.2)])
+def test_bernstein_root(V, b, delta):
+    pins.check_bernstein_root(V, b, delta)
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("est", [od.EST_CLIP, od.EST_UNBIASED])
+def test_exact_enumeration(seed, est):
+    rng = np.random.default_rng(300 + seed)
+    nl = int(rng.integers(1, 12))
+    w, r = _rand_lr(rng, nl, spread=1.5)
+    wH = np.exp(rng.normal(0, 1, 3))
+    pins.check_enumeration(wH, w, r, float(rng.choice([0.05, 0.1, 0.3])), est)
+
+
+def _plan_terms(seed, n):
+    rng = np.random.default_rng(400 + seed)
+    w, r = _rand_lr(rng, n, spread=2.0)
+    beta = od.shrinkage_beta(w, r)
+    lam = od.lambdas(w, r, beta)
+    return w, r, od.cert_terms(w, r, lam)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_gains_leave_one_out(seed):
+    w, r, (bi, vi, b_i) = _plan_terms(seed, 48)
+    D = float(w.sum() + 5.0)
+    pins.check_gains_loo(bi, vi, b_i, D, 0.05)
+    # a tied maximum: removing either copy leaves b unchanged
+    b_t = b_i.copy()
+    j = int(np.argmax(b_t))
+    b_t[(j + 1) % b_t.size] = b_t[j]
+    pins.check_gains_loo(bi, vi, b_t, D, 0.05)
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("eps", [0.02, 0.1, 0.3])
+def test_kstar_bruteforce(seed, eps):
+    rng = np.random.default_rng(500 + seed)
+    w, r = _rand_lr(rng, int(rng.integers(8, 64)), spread=2.0)
+    D = float(w.sum() * rng.uniform(1.0, 3.0))
+    pins.check_kstar_bruteforce(w, r, D, eps, 0.05)
+
+
+def _c1_inputs(seed=0, budget=None, n=None):
+    w = make_decode_workload("c1", seed=seed, n=n, budget=budget)
+    kf = bf16_to_f32(w["host_kv"][..., 0, :])
+    vf = bf16_to_f32(w["host_kv"][..., 1, :])
+    cm = oc.compress(w["tau"], kf, vf, w["budget"], w["n_sink"], w["n_local"],
+                     w["seed"])
+    sl = cm[0][0]
+    return w, sl
+
+
+def _decode_c1(w, sl, eps, weights, estimator=od.EST_CLIP):
+    return od.decode_group(bf16_to_f32(w["q"][0]), sl["resident_kv"],
+                           sl["resident_idx"], bf16_to_f32(w["sketch"][0, 0]),
+                           w["proj"][0], sl["r"], bf16_to_f32(w["host_kv"][0, 0]),
+                           eps, w["delta"], estimator, weights)
+
+
+@pytest.mark.parametrize("weights", [od.W_SKETCH, od.W_PERFECT])
+def test_fetch_all_is_exact_attention(weights):
+    """eps -> 0 forces k* = |L|: the output is textbook attention (eq. 1)."""
+    w, sl = _c1_inputs()
+    heads, union = _decode_c1(w, sl, 1e-300, weights)
+    hd = heads[0]
+    assert hd["k_star"] == int(sl["in_l"].sum())
+    kv = bf16_to_f32(w["host_kv"][0, 0])
+    o_ref, logd = od.exact_attention(bf16_to_f32(w["q"][0, 0]), kv[:, 0], kv[:, 1])
+    assert np.allclose(hd["o"], o_ref, rtol=1e-12, atol=1e-12)
+    assert abs(math.log(hd["d_hat"]) + hd["m"] - logd) < 1e-12
+    assert set(union.tolist()) == set(np.nonzero(sl["in_l"] & ~sl["in_s"])[0])
+
+
+def test_all_resident_is_exact():
+    """eta = 1: L is empty, eps^ = 0 and the estimate is exact."""
+    w, sl = _c1_inputs(budget=1024)
+    assert sl["in_l"].sum() == 0
+    heads, union = _decode_c1(w, sl, 0.1, od.W_SKETCH)
+    kv = bf16_to_f32(w["host_kv"][0, 0])
+    o_ref, logd = od.exact_attention(bf16_to_f32(w["q"][0, 0]), kv[:, 0], kv[:, 1])
+    assert heads[0]["eps_hat0"] == 0.0 and heads[0]["k_star"] == 0
+    assert np.allclose(heads[0]["o"], o_ref, rtol=1e-12, atol=1e-12)
+    assert union.size == 0
+
+
+def test_perfect_sketch_denominator_is_exact():
+    """With exact planning weights D~ equals the full denominator."""
+    w, sl = _c1_inputs()
+    heads, _ = _decode_c1(w, sl, 0.1, od.W_PERFECT)
+    kv = bf16_to_f32(w["host_kv"][0, 0])
+    _, logd = od.exact_attention(bf16_to_f32(w["q"][0, 0]), kv[:, 0], kv[:, 1])
+    assert abs(math.log(heads[0]["dnorm"]) + heads[0]["m"] - logd) < 1e-12
+
+
+def test_plan_scale_invariance():
+    """Shifting every logit by a constant (scaling all weights and D~) leaves
+    lambda, eps^, the gain order and k* unchanged (reading R5)."""
+    rng = np.random.default_rng(7)
+    w, r = _rand_lr(rng, 300, 2.0)
+    D = float(w.sum() * 1.5)
+    pos = np.arange(300)
+    a = od.plan_row(w, r, pos, D, 0.05, 0.05)
+    b = od.plan_row(w * 2.0 ** -30, r, pos, D * 2.0 ** -30, 0.05, 0.05)
+    assert np.allclose(a["lam"], b["lam"], rtol=1e-12)
+    assert a["k_star"] == b["k_star"] and a["k_star"] > 0
+    assert abs(a["eps_hat"] - b["eps_hat"]) <= 1e-12 * a["eps_hat"]
+    assert np.array_equal(a["order"][:a["k_star"]], b["order"][:b["k_star"]])
+
+
+def test_monte_carlo_coverage_perfect():
+    """Theorem 2 with exact weights: over fresh Poisson samples the estimate
+    stays within eps^(L') of D with frequency >= 1 - delta."""
+    w, sl = _c1_inputs()
+    delta = w["delta"]
+    kv = bf16_to_f32(w["host_kv"][0, 0])
+    qv = bf16_to_f32(w["q"][0, 0])
+    _, logd = od.exact_attention(qv, kv[:, 0], kv[:, 1])
+    n_trials = 150
+    fails = 0
+    for s in range(n_trials):
+        cm = oc.compress_slice(w["tau"][0, 0], w["budget"], w["n_sink"],
+                               w["n_local"], 1000 + s, 0, 0)
+        idx = cm["resident_idx"]
+        res_kv = np.stack([kv[idx, 0], kv[idx, 1]], axis=1)
+        heads, _ = od.decode_group(qv[None], res_kv, idx,
+                                   bf16_to_f32(w["sketch"][0, 0]), w["proj"][0],
+                                   cm["r"], kv, 0.1, delta, od.EST_CLIP,
+                                   od.W_PERFECT)
+        hd = heads[0]
+        err = abs(math.exp(math.log(hd["d_hat"]) + hd["m"] - logd) - 1.0)
+        fails += err > hd["eps_hat"]
+    assert fails <= delta * n_trials + 3 * math.sqrt(delta * n_trials)
+
+
+def test_monte_carlo_coverage_plan_vectorised():
+    """The same property over 10^5 samples of a fixed plan (Theorem 2 holds
+    for any sample-independent coefficients and order)."""
+    rng = np.random.default_rng(11)
+    w, r = _rand_lr(rng, 2000, 1.5)
+    wH = np.exp(rng.normal(2, 1, 50))
+    D = float(wH.sum() + w.sum())
+    delta = 0.1
+    plan = od.plan_row(w, r, np.arange(w.size), D, 0.05, delta)
+    k = plan["k_star"]
+    assert k > 0
+    fetched = np.zeros(w.size, dtype=bool)
+    fetched[plan["order"][:k]] = True
+    coef = plan["lam"] * w / r
+    fails = 0
+    n_tot = 0
+    for chunk in range(10):
+        z = rng.random((10000, w.size)) < r
+        est = wH.sum() + w[fetched].sum() + (z[:, ~fetched] * coef[~fetched]).sum(1)
+        fails += int(np.sum(np.abs(est - D) / D > plan["eps_hat"]))
+        n_tot += 10000
+    assert fails / n_tot <= delta
+
+
+def test_c2_shape_runs_and_certifies():
+    """A reduced c2 layer: every decision ends with eps^(L') < eps and the
+    fetch union is disjoint from the resident set."""
+    w = make_decode_workload("c2", seed=1, n=4096, G=2)
+    kf = bf16_to_f32(w["host_kv"][..., 0, :])
+    vf = bf16_to_f32(w["host_kv"][..., 1, :])
+    cm = oc.compress(w["tau"], kf, vf, w["budget"], w["n_sink"], w["n_local"],
+                     w["seed"])
+    res_kv = [[cm[0][g]["resident_kv"] for g in range(2)]]
+    res_idx = [[cm[0][g]["resident_idx"] for g in range(2)]]
+    r = np.stack([cm[0][g]["r"] for g in range(2)])[None]
+    heads, unions = od.decode_step(bf16_to_f32(w["q"]), res_kv, res_idx,
+                                   bf16_to_f32(w["sketch"]), w["proj"], r,
+                                   bf16_to_f32(w["host_kv"]), w["eps"], w["delta"])
+    for h in range(w["Hq"]):
+        hd = heads[0][h]
+        assert hd["eps_hat"] < w["eps"]
+        if hd["k_star"]:
+            assert hd["suffix"][hd["k_star"] - 1] >= w["eps"]
+    for g in range(2):
+        assert not set(unions[0][g].tolist()) & set(res_idx[0][g].tolist())

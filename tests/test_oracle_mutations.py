@@ -1,0 +1,192 @@
+"""Plant plausible mistakes in the oracle (CPU only) and confirm that at
+least one pin catches each of them. Nothing here touches the library."""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import compress as oc
+from oracle import decode as od
+from tests import pins
+
+
+def _orig(mod, name):
+    return getattr(mod, name)
+
+
+def _w_r(seed, n, spread=2.0):
+    rng = np.random.default_rng(seed)
+    return np.exp(rng.normal(0, spread, n)), rng.uniform(0.02, 0.95, n)
+
+
+def run_pins():
+    """A compact battery of the pins; returns the names of those that fail."""
+    failed = []
+
+    def attempt(name, fn):
+        try:
+            fn()
+        except (AssertionError, ValueError, ZeroDivisionError):
+            failed.append(name)
+
+    w, r = _w_r(1, 10)
+    attempt("lbfgsb", lambda: pins.check_shrinkage_lbfgsb(w, r))
+    attempt("lbfgsb_heavy", lambda: pins.check_shrinkage_lbfgsb(*_heavy(8, 10)))
+    attempt("kkt", lambda: pins.check_kkt(*_w_r(2, 400)))
+    attempt("kkt_heavy", lambda: pins.check_kkt(*_heavy(9, 400)))
+    attempt("golden_shrink", _golden_shrink)
+    attempt("bernstein", lambda: pins.check_bernstein_root(1.0, 0.5, 0.05))
+    attempt("range", lambda: pins.check_range_bound(*_w_r(3, 50)))
+    we, re_ = _w_r(4, 9, 1.5)
+    attempt("enum", lambda: pins.check_enumeration(np.ones(2), we, re_, 0.1))
+    wg, rg = _w_r(5, 30)
+    lam = od.lambdas(wg, rg, od.shrinkage_beta(wg, rg))
+    bi, vi, b_i = od.cert_terms(wg, rg, lam)
+    attempt("gains", lambda: pins.check_gains_loo(bi, vi, b_i, wg.sum() + 3, 0.05))
+    wk, rk = _w_r(6, 40)
+    attempt("kstar", lambda: pins.check_kstar_bruteforce(wk, rk, wk.sum() * 1.3,
+                                                         0.05, 0.05))
+    rng = np.random.default_rng(7)
+    tq = rng.integers(1, 2 ** 16, size=25)
+    attempt("waterfill", lambda: [pins.check_water_level_bruteforce(tq, b)
+                                  for b in (1, 5, 12, 24)])
+    tau = rng.beta(0.5, 5, size=3000).astype(np.float32)
+    attempt("rates", lambda: pins.check_rates_sum(tau, 300, 4, 16))
+    attempt("golden_wf", _golden_wf)
+    return failed
+
+
+def _heavy(seed, n):
+    """A few heavy tokens with small inclusion probabilities: the regime in
+    which the lower end of the clip box is active."""
+    rng = np.random.default_rng(seed)
+    w = np.exp(rng.normal(0, 1, n))
+    r = rng.uniform(0.2, 0.9, n)
+    k = max(1, n // 8)
+    w[:k] *= 50.0
+    r[:k] = rng.uniform(0.02, 0.1, k)
+    return w, r
+
+
+def _golden_shrink():
+    w = np.array([4.0, 1.0, 0.01])
+    r = np.array([0.5, 0.5, 0.5])
+    beta = od.shrinkage_beta(w, r)
+    assert abs(beta - 2.0) < 1e-12
+    assert np.allclose(od.lambdas(w, r, beta), [0.5, 1.0, 1.0], atol=1e-12)
+
+
+def _golden_wf():
+    sl = oc.compress_slice(np.array([1.0, 0.75, 0.5, 0.125, 0.125], np.float32),
+                           3, 1, 0, 0, 0, 0)
+    assert sl["in_h"].tolist() == [True, True, False, False, False]
+    assert sl["r"][2] == np.float32(2 / 3)
+
+
+def test_unmutated_oracle_passes_all_pins():
+    assert run_pins() == []
+
+
+def _eps_no_ab(beta, var, bmax, dnorm, delta):
+    l, a = od.bernstein_consts(delta)
+    return (beta + np.sqrt((a * bmax) ** 2 + 2.0 * var * l)) / dnorm
+
+
+def _eps_log10(beta, var, bmax, dnorm, delta):
+    l = math.log10(2.0 / delta)
+    a = l / 3
+    return (beta + a * bmax + np.sqrt((a * bmax) ** 2 + 2.0 * var * l)) / dnorm
+
+
+def _lam_no_1mr(w, r, beta):
+    with np.errstate(divide="ignore", invalid="ignore"):
+        x = beta * r / w
+    return np.where(w > 0, np.minimum(1.0, np.maximum(r, x)), 1.0)
+
+
+def _lam_swapped(w, r, beta):
+    with np.errstate(divide="ignore", invalid="ignore"):
+        x = beta * (1.0 - r) / (w * r)
+    return np.where(w > 0, np.minimum(1.0, np.maximum(r, x)), 1.0)
+
+
+def _terms_no_1mr(w, r, lam):
+    return w * (1 - lam), lam * lam * w * w / r, lam * w * np.maximum(r, 1 - r) / r
+
+
+def _terms_min(w, r, lam):
+    return (w * (1 - lam), lam * lam * w * w * (1 - r) / r,
+            lam * w * np.minimum(r, 1 - r) / r)
+
+
+def _gains_no_argmax(beta_i, v_i, b_i, dnorm, delta):
+    l, a = od.bernstein_consts(delta)
+    V = float(np.sum(v_i))
+    b1 = float(b_i.max())
+    s = math.sqrt((a * b1) ** 2 + 2.0 * V * l)
+    sp = np.sqrt((a * b1) ** 2 + 2.0 * np.maximum(V - v_i, 0) * l)
+    return (beta_i + 2.0 * v_i * l / (s + sp)) / dnorm
+
+
+def _suffix_prefix(order, beta_i, v_i, b_i, dnorm, delta):
+    bs, vs, bb = beta_i[order], v_i[order], b_i[order]
+    sb = np.concatenate([[0.0], np.cumsum(bs)])[::-1]
+    sv = np.concatenate([[0.0], np.cumsum(vs)])[::-1]
+    mb = np.concatenate([[0.0], np.maximum.accumulate(bb)])[::-1]
+    return od.eps_hat(sb, sv, mb, dnorm, delta)
+
+
+def _order_ascending(g, pos):
+    return np.lexsort((pos, g))
+
+
+def _wl_offbyone(tq_free, b_free):
+    j, num, den = _orig_wl(tq_free, b_free)
+    if den == 0 or j == 0:
+        return j, num, den
+    srt = np.sort(np.asarray(tq_free, np.int64))[::-1]
+    return j - 1, num + 1, int(srt[j - 1:].sum())
+
+
+def _rates_strict(tq, forced, num, den):
+    r, in_h = _orig_rates(tq, forced, num, den)
+    if den == 0:
+        return r, in_h
+    free = ~forced
+    prod = tq[free].astype(np.int64) * np.int64(num)
+    in_h[free] = prod > den
+    r[free] = np.where(prod > den, np.float32(1.0),
+                       np.minimum(r[free], oc.ONE_MINUS_ULP))
+    return r, in_h
+
+
+def _beta_upper(w, r, max_iter=200):
+    return float(np.sum(w * (1.0 - r)))
+
+
+_orig_wl = oc.water_level
+_orig_rates = oc.rates
+
+MUTATIONS = [
+    ("eps_hat drops the b*l/3 term", od, "eps_hat", _eps_no_ab),
+    ("eps_hat uses log10", od, "eps_hat", _eps_log10),
+    ("lambda drops the (1-r) factor", od, "lambdas", _lam_no_1mr),
+    ("lambda with r and 1-r swapped", od, "lambdas", _lam_swapped),
+    ("variance term drops (1-r)", od, "cert_terms", _terms_no_1mr),
+    ("range term uses min(r, 1-r)", od, "cert_terms", _terms_min),
+    ("gains ignore the unique argmax", od, "gains", _gains_no_argmax),
+    ("suffix sums taken as prefix sums", od, "suffix_eps", _suffix_prefix),
+    ("gain order ascending", od, "gain_order", _order_ascending),
+    ("water level one saturated token short", oc, "water_level", _wl_offbyone),
+    ("exact saturation left in L", oc, "rates", _rates_strict),
+    ("beta* is the bracket's upper end", od, "shrinkage_beta", _beta_upper),
+]
+
+
+@pytest.mark.parametrize("label,mod,name,fn", MUTATIONS,
+                         ids=[m[0] for m in MUTATIONS])
+def test_mutation_is_caught(monkeypatch, label, mod, name, fn):
+    monkeypatch.setattr(mod, name, fn)
+    failed = run_pins()
+    assert failed, f"no pin caught: {label}"
