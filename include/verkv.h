@@ -1,0 +1,200 @@
+/*
+ * verkv.h -- C ABI of the VerKV hot path on AMD Instinct MI355X (gfx950).
+ *
+ * Two operations from "Verify Before You Fetch: Reliable KV Cache
+ * Compression for LLM Inference" (Jha, Kumar, Chowdhury, Agrawal, Desai):
+ *
+ *   vkv_compress     PoissonComp, Algorithm 1 and section 4.1 (eq. 3): water-fill
+ *                    the inclusion probabilities r_i = min(1, c tau_i) so that
+ *                    they sum to the budget, split H (r = 1) from L (r < 1),
+ *                    draw the Poisson sample S (independent Bernoulli(r_i))
+ *                    and compact the resident rows H u S.
+ *   vkv_decode_step  KVFetch, Algorithm 2 and section 4.2: sketch weights, the
+ *                    bounded-shrinkage estimator (Definition 2, eq. 5), the
+ *                    Bernstein certificate (Lemma 1, eq. 7), and when it fails
+ *                    the gains (eq. 9), the fetch count k* (eq. 10, Theorem 2),
+ *                    the gather of the chosen rows from pinned host memory and
+ *                    the corrected attention output (section 3, eq. 1).
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer is owned by the caller. "dev" marks device memory, "host"
+ *     marks pinned host memory (hipHostMalloc) that the GPU reads directly.
+ *     The library never allocates, frees or keeps a pointer after a call.
+ *   - bfloat16 values are passed as uint16_t bit patterns.
+ *   - Work is enqueued on `stream` (a hipStream_t, NULL = default stream) and
+ *     the outputs are valid once the stream has been synchronised.
+ *   - Argument checks run on the host before anything is launched and return
+ *     VKV_EINVAL (or VKV_ENOTPINNED for host_kv); nothing is enqueued then.
+ *   - Conditions only the GPU can see (a resident count above `cap`, a fetch
+ *     union above `fetch_cap`, malformed r or resident lists) are ORed into the
+ *     caller's device status word; vkv_check_status() reads and maps it.
+ *   - vkv_last_error() returns a thread-local message for the last failure.
+ *   - The workspace needs no initialisation; its size comes from the matching
+ *     *_workspace_bytes() call for the same arguments.
+ */
+#ifndef VERKV_H
+#define VERKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  VKV_OK = 0,
+  VKV_EINVAL = 1,       /* bad shape, pointer, range or workspace size       */
+  VKV_ENOTPINNED = 2,   /* host_kv is not device-accessible pinned memory    */
+  VKV_EOVERFLOW = 3,    /* a device-side capacity (cap, fetch_cap) overflowed */
+  VKV_EHIP = 4,         /* a HIP runtime call failed                         */
+  VKV_EUNSUPPORTED = 5, /* valid but unsupported configuration               */
+  VKV_EDATA = 6         /* malformed inputs seen on the device               */
+} vkv_status;
+
+/* Device status word bits (ORed by the kernels of one call). */
+#define VKV_STATUS_RESIDENT_OVERFLOW 0x1u /* compress: |H u S| > cap          */
+#define VKV_STATUS_FETCH_OVERFLOW 0x2u    /* decode: union > fetch_cap        */
+#define VKV_STATUS_BAD_R 0x4u             /* decode: r outside (0, 1]         */
+#define VKV_STATUS_BAD_RESIDENT 0x8u      /* decode: resident list malformed, */
+                                          /* or a token with r = 1 missing   */
+
+/* Estimators for the L part (Definition 2): clipped shrinkage, or the
+ * unbiased lambda = 1 estimator (the PoissonComp-only baseline). */
+enum { VKV_EST_CLIP = 0, VKV_EST_UNBIASED = 1 };
+/* Planning weights on L: from the key sketch (what a deployment does), or
+ * the exact weights (the "perfect sketch" of section 4.2; reads every key of
+ * L from host memory, so it is a slow test mode). */
+enum { VKV_W_SKETCH = 0, VKV_W_PERFECT = 1 };
+
+/*
+ * PoissonComp over n_layers x n_kv_heads independent slices of n_tokens.
+ *
+ * tau      dev [n_layers][n_kv_heads][n_tokens] f32. Importance scores in [0,1]
+ *          (section 4.1 maps other ranges through a softmax first; that is the
+ *          caller's job). They are read on a 2^-32 grid and floored at one
+ *          step, so every token gets r > 0; values outside [0,1] are clamped.
+ * k, v     dev [n_layers][n_kv_heads][n_tokens][head_dim] bf16 prefill keys and
+ *          values; may be NULL when resident_kv is NULL.
+ * budget   expected number of GPU-resident rows per slice (eta * n rounded);
+ *          it includes the forced sink/local tokens and must exceed their
+ *          count (unless every token is forced).
+ * n_sink, n_local  the first n_sink and last n_local tokens go to H.
+ * seed     Philox4x32-10 key; the draw for (layer0 + l, head, token) is
+ *          counter (token, head, layer0 + l, 0) so any slice can be redrawn
+ *          alone.
+ * cap      resident-row capacity per slice (>= 1).
+ * Outputs (dev): r [n_layers][n_kv_heads][n_tokens] f32 (exactly 1.0 on H,
+ * below 1 on L); resident_idx [n_layers][n_kv_heads][cap] i32 ascending
+ * positions of H u S; resident_count [n_layers][n_kv_heads] i32 (the true
+ * count even when it exceeds cap; then only cap rows are written and the
+ * status word gets VKV_STATUS_RESIDENT_OVERFLOW); resident_kv (may be NULL)
+ * [n_layers][n_kv_heads][cap][2][head_dim] bf16, each row K then V;
+ * water_level (may be NULL) [n_layers][n_kv_heads] f64, c in units of tau
+ * (+inf when every token is in H).
+ * status   dev u32 [1], cleared at the start of the call.
+ * Supported: head_dim = 128, 1 <= n_tokens <= 2^24.
+ */
+typedef struct {
+  int32_t n_layers, n_kv_heads, n_tokens, head_dim;
+  int32_t layer0;
+  const float *tau;
+  const uint16_t *k;
+  const uint16_t *v;
+  int64_t budget;
+  int32_t n_sink, n_local;
+  uint64_t seed;
+  int32_t cap;
+  float *r;
+  int32_t *resident_idx;
+  int32_t *resident_count;
+  uint16_t *resident_kv;
+  double *water_level;
+  uint32_t *status;
+  void *workspace;
+  size_t workspace_bytes;
+} vkv_compress_args;
+
+/*
+ * One KVFetch decode step for one layer: every request and every query head.
+ *
+ * Shapes: B = batch, Hq query heads over G KV heads (Hq/G in {1,2,4,8}),
+ * head_dim d = 128, n tokens, sketch_dim s in {16, 32}.
+ * q            dev [B][Hq][d] bf16.
+ * resident_kv  dev [B][G][cap][2][d] bf16 (rows of H u S, K then V), with
+ * resident_idx dev [B][G][cap] i32 ascending positions and
+ * resident_count dev [B][G] i32 (as written by vkv_compress).
+ * sketch       dev [B][G][n][s] bf16 projected keys sk_i = P_g^T k_i.
+ * proj         dev [G][d][s] f32 projection P_g (q is projected inside).
+ * r            dev [B][G][n] f32 inclusion probabilities, H <=> r == 1.
+ * host_kv      host [B][G][n][2][d] bf16 full cache in pinned memory
+ *              (hipHostMalloc); rows chosen for fetching are read from it.
+ * eps, delta   tolerance (eps > 0, 0 < delta < 1) of the (eps, delta)
+ *              guarantee on the attention denominator.
+ * estimator    VKV_EST_CLIP or VKV_EST_UNBIASED; weights VKV_W_SKETCH or
+ *              VKV_W_PERFECT.
+ * fetch_cap    staging rows per (request, KV head) (1..n).
+ * Outputs (dev): out [B][Hq][d] f32 attention output; d_hat and log_shift
+ * [B][Hq] f32 with D^ = d_hat * exp(log_shift); eps_hat0 / eps_hat [B][Hq] f32,
+ * the certificate before fetching and after (on L'); k_star [B][Hq] i32;
+ * fetch_idx [B][G][fetch_cap] i32 ascending positions fetched for the KV head
+ * (the union over its query heads, minus S); fetch_count [B][G] i32 (true
+ * count, see VKV_STATUS_FETCH_OVERFLOW); host_bytes u64 [1] bytes read from
+ * host_kv this step; row_stats (may be NULL) [B][Hq][8] f64 =
+ * {m, D~ (scaled by exp(-m)), beta*, beta(L), V(L), b(L), eps^(L), eps^(L')}.
+ * status   dev u32 [1], cleared at the start of the call.
+ */
+typedef struct {
+  int32_t batch, n_q_heads, n_kv_heads, head_dim, n_tokens, sketch_dim, cap;
+  const uint16_t *q;
+  const uint16_t *resident_kv;
+  const int32_t *resident_idx;
+  const int32_t *resident_count;
+  const uint16_t *sketch;
+  const float *proj;
+  const float *r;
+  const uint16_t *host_kv;
+  float eps, delta;
+  int32_t estimator, weights, fetch_cap;
+  float *out;
+  float *d_hat;
+  float *log_shift;
+  float *eps_hat0;
+  float *eps_hat;
+  int32_t *k_star;
+  int32_t *fetch_idx;
+  int32_t *fetch_count;
+  uint64_t *host_bytes;
+  double *row_stats;
+  uint32_t *status;
+  void *workspace;
+  size_t workspace_bytes;
+} vkv_decode_args;
+
+/* Workspace sizes in bytes for these arguments (0 if the shapes are invalid). */
+size_t vkv_compress_workspace_bytes(const vkv_compress_args *a);
+size_t vkv_decode_workspace_bytes(const vkv_decode_args *a);
+
+/* Enqueue one PoissonComp pass (see vkv_compress_args). */
+vkv_status vkv_compress(const vkv_compress_args *a, void *stream);
+
+/* Enqueue one KVFetch decode step (see vkv_decode_args). */
+vkv_status vkv_decode_step(const vkv_decode_args *a, void *stream);
+
+/* Synchronise `stream`, read the device status word and map it to a status:
+ * VKV_OK, VKV_EOVERFLOW (capacity bits) or VKV_EDATA (data bits). The word
+ * itself is returned through *bits when bits != NULL. */
+vkv_status vkv_check_status(const uint32_t *status, void *stream,
+                            uint32_t *bits);
+
+/* Thread-local text describing the last non-OK status of this thread. */
+const char *vkv_last_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t vkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VERKV_H */

@@ -1,0 +1,184 @@
+"""Shared helpers for the GPU parity tests: build one decode case from the
+seeded workloads, run the library and the oracle on identical inputs, and
+compare them by the parity rules:
+
+* bit-exact: r, the H/L partition, the sample, resident lists and counts,
+  the water level;
+* exact up to documented ties: k* per query head and the fetch union per KV
+  head. A head whose k* differs is tie-accepted when the oracle's own
+  certificate at both k values is within 1e-5 relative of eps (the stopping
+  test is a near tie) or every token between the two cut points has a gain
+  within 1e-5 relative of the gain at k*;
+* numeric: beta* within 1e-6 relative, eps^(L), eps^(L') and D^ within 1e-4
+  relative, the output within 1e-3 relative L2.
+"""
+
+import math
+import sys
+
+import numpy as np
+
+from oracle import compress as oc
+from oracle import decode as od
+from workloads import bf16_to_f32, c3_shift_queries, make_decode_workload
+
+TOL_BETA = 1e-6
+TOL_EPS = 1e-4
+TOL_D = 1e-4
+TOL_O = 1e-3
+TIE = 1e-5
+
+
+def say(msg):
+    sys.stderr.write(msg + "\n")
+    sys.stderr.flush()
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def build_case(cfg, seed=0, cap_slack=64, shift_from=None, **kw):
+    """Workload + oracle compression (decode inputs shared by both sides)."""
+    w = make_decode_workload(cfg, seed=seed, with_queries=True, **kw)
+    if shift_from is not None:
+        w["shift_from"] = shift_from
+    B, G = w["B"], w["G"]
+    kf = bf16_to_f32(w["host_kv"][..., 0, :])
+    vf = bf16_to_f32(w["host_kv"][..., 1, :])
+    cm = oc.compress(w["tau"], kf, vf, w["budget"], w["n_sink"], w["n_local"],
+                     w["seed"])
+    counts = np.array([[cm[b][g]["resident_idx"].size for g in range(G)]
+                       for b in range(B)])
+    cap = int(counts.max()) + cap_slack
+    w["cm"] = cm
+    w["cap"] = cap
+    w["r_all"] = np.stack([np.stack([cm[b][g]["r"] for g in range(G)])
+                           for b in range(B)])
+    if cfg == "c3" and w.get("shift_from", B) < B:
+        res = np.zeros((B, G, w["n"]), dtype=bool)
+        for b in range(B):
+            for g in range(G):
+                res[b, g, cm[b][g]["resident_idx"]] = True
+        w["q"] = c3_shift_queries(w, res, w["r_all"])
+    return w
+
+
+def device_inputs(w):
+    torch = torch_mod()
+    B, G, n, cap, d = w["B"], w["G"], w["n"], w["cap"], w["d"]
+    ridx = np.zeros((B, G, cap), dtype=np.int32)
+    rkv = np.zeros((B, G, cap, 2, d), dtype=np.uint16)
+    rcnt = np.zeros((B, G), dtype=np.int32)
+    for b in range(B):
+        for g in range(G):
+            idx = w["cm"][b][g]["resident_idx"]
+            ridx[b, g, :idx.size] = idx
+            rkv[b, g, :idx.size] = w["host_kv"][b, g, idx]
+            rcnt[b, g] = idx.size
+    dev = torch.device("cuda")
+
+    def t(a, dtype):
+        return torch.from_numpy(np.ascontiguousarray(a).view(dtype)).to(dev)
+
+    return dict(
+        q=t(w["q"], np.int16), resident_kv=t(rkv, np.int16),
+        resident_idx=t(ridx, np.int32), resident_count=t(rcnt, np.int32),
+        sketch=t(w["sketch"], np.int16), proj=t(w["proj"], np.float32),
+        r=t(w["r_all"], np.float32),
+        host_kv=torch.from_numpy(w["host_kv"].view(np.int16)).pin_memory())
+
+
+def run_library(w, dev, eps, delta, est=0, weights=0, fetch_cap=None):
+    from verified_sparse_kv_amd import verkv as vk
+    torch = torch_mod()
+    step = vk.DecodeStep(w["B"], w["Hq"], w["G"], w["n"], w["s"], w["cap"],
+                         fetch_cap or w["n"], torch.device("cuda"))
+    step.bind(dev["q"], dev["resident_kv"], dev["resident_idx"],
+              dev["resident_count"], dev["sketch"], dev["proj"], dev["r"],
+              dev["host_kv"], eps, delta, est, weights)
+    out = step.launch()
+    rc, bits = step.check_status()
+    res = {k: v.cpu().numpy() for k, v in out.items()}
+    res["rc"] = rc
+    res["bits"] = bits
+    return res
+
+
+def run_oracle(w, eps, delta, est=0, weights=0):
+    B, G = w["B"], w["G"]
+    res_kv = [[w["cm"][b][g]["resident_kv"] for g in range(G)] for b in range(B)]
+    res_idx = [[w["cm"][b][g]["resident_idx"] for g in range(G)] for b in range(B)]
+    return od.decode_step(bf16_to_f32(w["q"]), res_kv, res_idx,
+                          bf16_to_f32(w["sketch"]), w["proj"], w["r_all"],
+                          bf16_to_f32(w["host_kv"]), eps, delta, est, weights)
+
+
+def _rel(a, b):
+    return abs(a - b) / max(abs(b), 1e-300)
+
+
+def compare(w, gpu, heads, unions, eps, est=0, max_tie_frac=0.01):
+    """Apply the parity rules; returns a summary dict (raises on failure)."""
+    B, Hq, G = w["B"], w["Hq"], w["G"]
+    grp = Hq // G
+    assert gpu["rc"] == 0, f"status bits {gpu['bits']:#x}"
+    ties = 0
+    tie_rows = set()
+    worst = dict(beta=0.0, eps0=0.0, eps1=0.0, dhat=0.0, o=0.0)
+    for b in range(B):
+        for h in range(Hq):
+            hd = heads[b][h]
+            st = gpu["row_stats"][b, h]
+            # beta*
+            if est == od.EST_CLIP and hd["beta_star"] > 0:
+                e = _rel(st[2], hd["beta_star"])
+                worst["beta"] = max(worst["beta"], e)
+                assert e <= TOL_BETA, (b, h, st[2], hd["beta_star"])
+            e = _rel(float(gpu["eps_hat0"][b, h]), hd["eps_hat0"])
+            worst["eps0"] = max(worst["eps0"], e)
+            assert e <= TOL_EPS, (b, h, gpu["eps_hat0"][b, h], hd["eps_hat0"])
+            kg, ko = int(gpu["k_star"][b, h]), hd["k_star"]
+            if kg != ko:
+                assert hd["order"] is not None and kg > 0, (b, h, kg, ko)
+                suf = hd["suffix"]
+                near = all(abs(suf[k] - eps) <= TIE * eps for k in (kg, ko)
+                           if k < suf.size)
+                lo_k, hi_k = min(kg, ko), max(kg, ko)
+                g = hd["gains"][hd["order"]]
+                gk = g[max(ko - 1, 0)]
+                gap = np.all(np.abs(g[max(lo_k - 1, 0):hi_k] - gk) <= TIE * gk)
+                assert near or gap, (b, h, kg, ko, suf[kg], suf[ko], eps)
+                ties += 1
+                tie_rows.add((b, h))
+                continue
+            e = _rel(float(gpu["eps_hat"][b, h]), hd["eps_hat"])
+            worst["eps1"] = max(worst["eps1"], e)
+            assert e <= TOL_EPS, (b, h, gpu["eps_hat"][b, h], hd["eps_hat"])
+            logd_g = math.log(float(gpu["d_hat"][b, h])) + float(gpu["log_shift"][b, h])
+            logd_o = math.log(hd["d_hat"]) + hd["m"]
+            e = abs(math.expm1(logd_g - logd_o))
+            worst["dhat"] = max(worst["dhat"], e)
+            assert e <= TOL_D, (b, h, logd_g, logd_o)
+            o_g = gpu["out"][b, h].astype(np.float64)
+            e = float(np.linalg.norm(o_g - hd["o"]) / np.linalg.norm(hd["o"]))
+            worst["o"] = max(worst["o"], e)
+            assert e <= TOL_O, (b, h, e)
+    n_rows = B * Hq
+    assert ties <= max(1, max_tie_frac * n_rows), (ties, n_rows)
+    # fetch unions per KV head (exact unless a head of the group is a tie)
+    fetched = 0
+    for b in range(B):
+        for g in range(G):
+            cnt = int(gpu["fetch_count"][b, g])
+            got = gpu["fetch_idx"][b, g, :cnt]
+            assert np.all(np.diff(got) > 0)
+            fetched += cnt
+            if any((b, g * grp + j) in tie_rows for j in range(grp)):
+                continue
+            assert np.array_equal(got, unions[b][g]), (b, g, cnt, unions[b][g].size)
+    assert int(gpu["host_bytes"][0]) == fetched * 512
+    return dict(ties=ties, rows=n_rows, fetched=fetched, worst=worst,
+                fetch_frac=fetched / (B * G * w["n"]),
+                kstar_mean=float(np.mean(gpu["k_star"])))

@@ -1,0 +1,165 @@
+"""The C ABI on the CPU: the library loads, exports every function that
+include/verkv.h declares, the ctypes structs match the C layout, and host-side
+validation rejects bad arguments before anything is launched."""
+
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "verkv.h")
+
+vk = pytest.importorskip("verified_sparse_kv_amd.verkv")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(vkv_\w+)\s*\(", src,
+                                 re.MULTILINE)))
+
+
+def test_exports_every_declared_function():
+    names = header_functions()
+    assert set(names) == set(vk.EXPORTS), names
+    lib = ctypes.CDLL(vk.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", vk.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    for name in names:
+        assert re.search(rf"\bT {name}$", out, re.MULTILINE), name
+
+
+def _c_layout(struct, fields):
+    prog = ["#include <stdio.h>", "#include <stddef.h>", '#include "verkv.h"',
+            "int main(void) {", f'  printf("%zu\\n", sizeof({struct}));']
+    for f in fields:
+        prog.append(f'  printf("%zu\\n", offsetof({struct}, {f}));')
+    prog.append("  return 0; }")
+    with tempfile.TemporaryDirectory() as td:
+        c = os.path.join(td, "p.c")
+        exe = os.path.join(td, "p")
+        open(c, "w").write("\n".join(prog))
+        subprocess.run(["gcc", "-I", os.path.dirname(HEADER), c, "-o", exe],
+                       check=True)
+        vals = [int(x) for x in subprocess.run([exe], capture_output=True,
+                                               text=True).stdout.split()]
+    return vals[0], vals[1:]
+
+
+@pytest.mark.parametrize("cls,cname", [(vk.CompressArgs, "vkv_compress_args"),
+                                       (vk.DecodeArgs, "vkv_decode_args")])
+def test_struct_layout_matches_c(cls, cname):
+    fields = [f for f, _ in cls._fields_]
+    size, offs = _c_layout(cname, fields)
+    assert ctypes.sizeof(cls) == size
+    for f, o in zip(fields, offs):
+        assert getattr(cls, f).offset == o, f
+
+
+def _compress_args(**kw):
+    a = vk.CompressArgs(n_layers=2, n_kv_heads=3, n_tokens=5000, head_dim=128,
+                        layer0=0, budget=600, n_sink=4, n_local=32, seed=1,
+                        cap=1000)
+    fake = ctypes.c_void_p(0x1000)
+    for f in ("tau", "r", "resident_idx", "resident_count", "status"):
+        setattr(a, f, fake)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _decode_args(**kw):
+    a = vk.DecodeArgs(batch=2, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                      n_tokens=4096, sketch_dim=32, cap=600, eps=0.1, delta=0.05,
+                      estimator=0, weights=0, fetch_cap=4096)
+    fake = ctypes.c_void_p(0x1000)
+    for f in ("q", "resident_kv", "resident_idx", "resident_count", "sketch",
+              "proj", "r", "host_kv", "out", "d_hat", "log_shift", "eps_hat0",
+              "eps_hat", "k_star", "fetch_idx", "fetch_count", "host_bytes",
+              "status"):
+        setattr(a, f, fake)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_workspace_sizes():
+    a = _compress_args()
+    w1 = vk.vkv_compress_workspace_bytes(a)
+    assert w1 > 0 and w1 % 256 == 0
+    w2 = vk.vkv_compress_workspace_bytes(_compress_args(n_tokens=50000))
+    assert w2 > w1
+    assert vk.vkv_compress_workspace_bytes(_compress_args(head_dim=64)) == 0
+    d = _decode_args()
+    dw = vk.vkv_decode_workspace_bytes(d)
+    assert dw > 0
+    assert vk.vkv_decode_workspace_bytes(_decode_args(fetch_cap=8)) < dw
+    assert vk.vkv_decode_workspace_bytes(_decode_args(n_q_heads=20)) == 0
+    # the shapes named in the configs fit easily in 288 GB
+    big = _decode_args(batch=16, n_tokens=32768, cap=4600, fetch_cap=32768)
+    assert vk.vkv_decode_workspace_bytes(big) < 8 * 2 ** 30
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(n_layers=0), vk.VKV_EINVAL, "n_layers"),
+    (dict(head_dim=64), vk.VKV_EINVAL, "head_dim"),
+    (dict(n_tokens=(1 << 21) + 1), vk.VKV_EINVAL, "n_tokens"),
+    (dict(budget=30), vk.VKV_EINVAL, "smaller than"),
+    (dict(budget=36), vk.VKV_EINVAL, "exceed"),
+    (dict(cap=0), vk.VKV_EINVAL, "cap"),
+    (dict(tau=None), vk.VKV_EINVAL, "required"),
+    (dict(resident_kv=ctypes.c_void_p(0x1000)), vk.VKV_EINVAL, "k and v"),
+    (dict(workspace=None), vk.VKV_EINVAL, "workspace"),
+])
+def test_compress_validation(kw, code, frag):
+    a = _compress_args(**kw)
+    if "workspace" not in kw:
+        a.workspace = ctypes.c_void_p(0x1000)
+        a.workspace_bytes = 1
+    assert vk.vkv_compress(a, None) == code
+    msg = vk.vkv_last_error()
+    assert frag in msg, msg
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(eps=0.0), vk.VKV_EINVAL, "eps"),
+    (dict(eps=float("inf")), vk.VKV_EINVAL, "eps"),
+    (dict(delta=1.0), vk.VKV_EINVAL, "delta"),
+    (dict(delta=0.0), vk.VKV_EINVAL, "delta"),
+    (dict(n_q_heads=20), vk.VKV_EINVAL, "multiple"),
+    (dict(n_q_heads=24), vk.VKV_EUNSUPPORTED, "= 3"),
+    (dict(n_q_heads=48, n_kv_heads=4), vk.VKV_EUNSUPPORTED, "12"),
+    (dict(sketch_dim=24), vk.VKV_EUNSUPPORTED, "sketch_dim"),
+    (dict(fetch_cap=0), vk.VKV_EINVAL, "fetch_cap"),
+    (dict(fetch_cap=5000), vk.VKV_EINVAL, "fetch_cap"),
+    (dict(n_tokens=1 << 24), vk.VKV_EINVAL, "n_tokens"),
+    (dict(estimator=7), vk.VKV_EINVAL, "estimator"),
+    (dict(weights=3), vk.VKV_EINVAL, "weights"),
+    (dict(sketch=None), vk.VKV_EINVAL, "sketch"),
+    (dict(k_star=None), vk.VKV_EINVAL, "output"),
+    (dict(host_kv=None), vk.VKV_EINVAL, "required"),
+])
+def test_decode_validation(kw, code, frag):
+    a = _decode_args(**kw)
+    a.workspace = ctypes.c_void_p(0x1000)
+    a.workspace_bytes = 1 << 40
+    assert vk.vkv_decode_step(a, None) == code
+    msg = vk.vkv_last_error()
+    assert frag in msg, msg
+
+
+def test_decode_workspace_too_small():
+    a = _decode_args()
+    a.workspace = ctypes.c_void_p(0x1000)
+    a.workspace_bytes = 16
+    assert vk.vkv_decode_step(a, None) == vk.VKV_EINVAL
+    assert "workspace" in vk.vkv_last_error()
+
+
+def test_version():
+    assert vk.vkv_version() >= 100

@@ -1,0 +1,168 @@
+// C ABI of the VerKV hot path: argument validation, workspace sizing, the
+// pinned-memory check and dispatch to the kernels. See include/verkv.h.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "vkv_common.h"
+#include "vkv_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+vkv_status fail(vkv_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+vkv_status hip_fail(hipError_t e, const char *what) {
+  return fail(VKV_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define REQUIRE(cond, ...)                          \
+  do {                                              \
+    if (!(cond)) return fail(VKV_EINVAL, __VA_ARGS__); \
+  } while (0)
+
+// Forced tokens: the first n_sink and the last n_local (they may overlap).
+int64_t forced_count(int64_t n, int64_t n_sink, int64_t n_local) {
+  if (n_sink + n_local >= n) return n;
+  return n_sink + n_local;
+}
+
+vkv_status check_compress_shapes(const vkv_compress_args *a) {
+  REQUIRE(a != nullptr, "compress: args is NULL");
+  REQUIRE(a->n_layers >= 1 && a->n_kv_heads >= 1,
+          "compress: n_layers and n_kv_heads must be >= 1");
+  REQUIRE((int64_t)a->n_layers * a->n_kv_heads <= 65535,
+          "compress: n_layers * n_kv_heads must be <= 65535");
+  REQUIRE(a->n_tokens >= 1 && a->n_tokens <= (1 << 21),
+          "compress: n_tokens must be in [1, 2^21]");
+  REQUIRE(a->head_dim == vkv::kHeadDim, "compress: head_dim must be 128");
+  REQUIRE(a->layer0 >= 0, "compress: layer0 must be >= 0");
+  REQUIRE(a->n_sink >= 0 && a->n_local >= 0,
+          "compress: n_sink and n_local must be >= 0");
+  REQUIRE(a->cap >= 1, "compress: cap must be >= 1");
+  return VKV_OK;
+}
+
+vkv_status check_decode_shapes(const vkv_decode_args *a) {
+  REQUIRE(a != nullptr, "decode: args is NULL");
+  REQUIRE(a->batch >= 1 && a->batch <= 65535, "decode: batch must be in [1, 65535]");
+  REQUIRE(a->n_kv_heads >= 1 && a->n_kv_heads <= 65535,
+          "decode: n_kv_heads must be in [1, 65535]");
+  REQUIRE(a->n_q_heads >= a->n_kv_heads && a->n_q_heads % a->n_kv_heads == 0,
+          "decode: n_q_heads must be a multiple of n_kv_heads");
+  const int grp = a->n_q_heads / a->n_kv_heads;
+  if (!(grp == 1 || grp == 2 || grp == 4 || grp == 8))
+    return fail(VKV_EUNSUPPORTED, "decode: n_q_heads / n_kv_heads = %d (supported: 1, 2, 4, 8)", grp);
+  REQUIRE(a->head_dim == vkv::kHeadDim, "decode: head_dim must be 128");
+  REQUIRE(a->n_tokens >= 1 && a->n_tokens < (1 << 24),
+          "decode: n_tokens must be in [1, 2^24)");
+  if (!(a->sketch_dim == 16 || a->sketch_dim == 32))
+    return fail(VKV_EUNSUPPORTED, "decode: sketch_dim %d (supported: 16, 32)", a->sketch_dim);
+  REQUIRE(a->cap >= 1, "decode: cap must be >= 1");
+  REQUIRE(a->fetch_cap >= 1 && a->fetch_cap <= a->n_tokens,
+          "decode: fetch_cap must be in [1, n_tokens]");
+  return VKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *vkv_last_error(void) { return g_err; }
+
+int32_t vkv_version(void) { return 100; }
+
+size_t vkv_compress_workspace_bytes(const vkv_compress_args *a) {
+  if (check_compress_shapes(a) != VKV_OK) return 0;
+  return vkv::compress_layout(*a).total;
+}
+
+size_t vkv_decode_workspace_bytes(const vkv_decode_args *a) {
+  if (check_decode_shapes(a) != VKV_OK) return 0;
+  return vkv::decode_layout(*a).total;
+}
+
+vkv_status vkv_compress(const vkv_compress_args *a, void *stream) {
+  vkv_status st = check_compress_shapes(a);
+  if (st != VKV_OK) return st;
+  REQUIRE(a->tau && a->r && a->resident_idx && a->resident_count && a->status,
+          "compress: tau, r, resident_idx, resident_count and status are required");
+  REQUIRE(a->resident_kv == nullptr || (a->k && a->v),
+          "compress: k and v are required when resident_kv is given");
+  const int64_t n = a->n_tokens;
+  const int64_t nf = forced_count(n, a->n_sink, a->n_local);
+  const int64_t b_free = a->budget - nf;
+  REQUIRE(b_free >= 0, "compress: budget %lld is smaller than the %lld forced tokens",
+          (long long)a->budget, (long long)nf);
+  REQUIRE(nf == n || b_free >= 1,
+          "compress: budget must exceed the forced tokens so that every token gets r > 0");
+  REQUIRE(a->budget <= (1 << 21), "compress: budget must be <= 2^21");
+  const vkv::CompressLayout L = vkv::compress_layout(*a);
+  REQUIRE(a->workspace != nullptr && a->workspace_bytes >= L.total,
+          "compress: workspace of %zu bytes needed", L.total);
+  const hipError_t e = vkv::launch_compress(*a, L, b_free, (int32_t)nf,
+                                            static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "compress launch");
+  return VKV_OK;
+}
+
+vkv_status vkv_decode_step(const vkv_decode_args *a, void *stream) {
+  vkv_status st = check_decode_shapes(a);
+  if (st != VKV_OK) return st;
+  REQUIRE(a->eps > 0.0f && isfinite(a->eps), "decode: eps must be > 0");
+  REQUIRE(a->delta > 0.0f && a->delta < 1.0f, "decode: delta must be in (0, 1)");
+  REQUIRE(a->estimator == VKV_EST_CLIP || a->estimator == VKV_EST_UNBIASED,
+          "decode: unknown estimator %d", a->estimator);
+  REQUIRE(a->weights == VKV_W_SKETCH || a->weights == VKV_W_PERFECT,
+          "decode: unknown weights mode %d", a->weights);
+  REQUIRE(a->q && a->resident_kv && a->resident_idx && a->resident_count && a->r &&
+              a->host_kv,
+          "decode: q, resident_kv, resident_idx, resident_count, r and host_kv are required");
+  REQUIRE(a->weights == VKV_W_PERFECT || (a->sketch && a->proj),
+          "decode: sketch and proj are required in sketch mode");
+  REQUIRE(a->out && a->d_hat && a->log_shift && a->eps_hat0 && a->eps_hat &&
+              a->k_star && a->fetch_idx && a->fetch_count && a->host_bytes && a->status,
+          "decode: every output pointer except row_stats is required");
+  const vkv::DecodeLayout L = vkv::decode_layout(*a);
+  REQUIRE(a->workspace != nullptr && a->workspace_bytes >= L.total,
+          "decode: workspace of %zu bytes needed", L.total);
+  // host_kv must be pinned host memory the GPU can read
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, a->host_kv);
+  if (e != hipSuccess || attr.type != hipMemoryTypeHost || attr.devicePointer == nullptr) {
+    (void)hipGetLastError();
+    return fail(VKV_ENOTPINNED,
+                "decode: host_kv is not device-accessible pinned host memory (%s)",
+                e != hipSuccess ? hipGetErrorString(e) : "wrong memory type");
+  }
+  const uint16_t *hkv = static_cast<const uint16_t *>(attr.devicePointer);
+  e = vkv::launch_decode(*a, L, hkv, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return VKV_OK;
+}
+
+vkv_status vkv_check_status(const uint32_t *status, void *stream, uint32_t *bits) {
+  REQUIRE(status != nullptr, "check_status: status is NULL");
+  uint32_t h = 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(&h, status, sizeof(h), hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return hip_fail(e, "check_status copy");
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "check_status sync");
+  if (bits) *bits = h;
+  if (h & (VKV_STATUS_BAD_R | VKV_STATUS_BAD_RESIDENT))
+    return fail(VKV_EDATA, "device status 0x%x: malformed r or resident list", h);
+  if (h & (VKV_STATUS_RESIDENT_OVERFLOW | VKV_STATUS_FETCH_OVERFLOW))
+    return fail(VKV_EOVERFLOW, "device status 0x%x: capacity exceeded", h);
+  return VKV_OK;
+}
+
+}  // extern "C"

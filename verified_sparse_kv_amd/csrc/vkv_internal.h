@@ -1,0 +1,65 @@
+// Internal declarations shared by the C ABI (vkv_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "verkv.h"
+
+namespace vkv {
+
+// Carves 256-byte aligned regions out of one caller workspace.
+struct Carve {
+  size_t off = 0;
+  template <typename T>
+  size_t take(size_t count) {
+    off = (off + 255) & ~size_t(255);
+    const size_t o = off;
+    off += count * sizeof(T);
+    return o;
+  }
+};
+
+template <typename T>
+static inline T *at(void *base, size_t off) {
+  return reinterpret_cast<T *>(static_cast<char *>(base) + off);
+}
+
+// ------------------------------------------------------------ compression
+constexpr int kCompChunk = 4096;   // tokens per workgroup
+constexpr int kCompBins = 2048;    // 11-bit radix digits over 33-bit scores
+
+struct CompressSlice {
+  uint64_t lo;        // lower edge of the current bracket of score values
+  uint64_t s_below;   // sum of free scores below the bracket
+  uint64_t num, den;  // water level c = num / den (grid units); den 0 => inf
+  uint32_t c_above;   // free tokens at or above the bracket's upper edge
+  uint32_t n_free;    // free (non-forced) tokens
+  int32_t done;       // water level known
+  int32_t all_sat;    // every free token saturates (L empty)
+  uint32_t arrive;    // last-block counter
+  uint32_t pad[3];
+};
+
+struct CompressLayout {
+  int n_slices, ncc, nwords;
+  size_t slices, hcnt, hsum, ccnt, bits, total;
+};
+
+CompressLayout compress_layout(const vkv_compress_args &a);
+hipError_t launch_compress(const vkv_compress_args &a, const CompressLayout &L,
+                           int64_t b_free, int32_t n_forced, hipStream_t s);
+
+// ------------------------------------------------------------ decoding
+struct DecodeLayout {
+  int grp, nch, ncr, ncf, nwords, chunk;
+  size_t shat, ell, hpart, resbits, fbits, pmax, rows, groups, bbins, cpart,
+      dpart, sbins, cand, fcnt, apart, staging, total;
+};
+
+DecodeLayout decode_layout(const vkv_decode_args &a);
+hipError_t launch_decode(const vkv_decode_args &a, const DecodeLayout &L,
+                         const uint16_t *host_kv_dev, hipStream_t s);
+
+}  // namespace vkv

@@ -1,0 +1,293 @@
+"""Thin Python binding of libverkv.so (include/verkv.h).
+
+Argument marshalling only: every step of compression and decoding runs in
+the HIP library. PyTorch supplies device memory, pinned host memory and the
+current stream. Importing this module loads the library and raises if it is
+missing or does not export the ABI; there is no fallback.
+
+The functions named like the C entry points (``vkv_compress``,
+``vkv_decode_step``, ``vkv_*_workspace_bytes``, ``vkv_check_status``,
+``vkv_last_error``) take the ctypes argument structs directly; ``compress``
+and ``decode_step`` allocate outputs and workspace as torch tensors.
+"""
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libverkv.so")
+
+VKV_OK, VKV_EINVAL, VKV_ENOTPINNED, VKV_EOVERFLOW, VKV_EHIP, \
+    VKV_EUNSUPPORTED, VKV_EDATA = range(7)
+STATUS_NAMES = {0: "VKV_OK", 1: "VKV_EINVAL", 2: "VKV_ENOTPINNED",
+                3: "VKV_EOVERFLOW", 4: "VKV_EHIP", 5: "VKV_EUNSUPPORTED",
+                6: "VKV_EDATA"}
+STATUS_RESIDENT_OVERFLOW = 0x1
+STATUS_FETCH_OVERFLOW = 0x2
+STATUS_BAD_R = 0x4
+STATUS_BAD_RESIDENT = 0x8
+EST_CLIP, EST_UNBIASED = 0, 1
+W_SKETCH, W_PERFECT = 0, 1
+
+EXPORTS = ("vkv_compress_workspace_bytes", "vkv_decode_workspace_bytes",
+           "vkv_compress", "vkv_decode_step", "vkv_check_status",
+           "vkv_last_error", "vkv_version")
+
+_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+
+
+class CompressArgs(ctypes.Structure):
+    _fields_ = [("n_layers", _i32), ("n_kv_heads", _i32), ("n_tokens", _i32),
+                ("head_dim", _i32), ("layer0", _i32),
+                ("tau", _p), ("k", _p), ("v", _p),
+                ("budget", ctypes.c_int64), ("n_sink", _i32), ("n_local", _i32),
+                ("seed", ctypes.c_uint64), ("cap", _i32),
+                ("r", _p), ("resident_idx", _p), ("resident_count", _p),
+                ("resident_kv", _p), ("water_level", _p), ("status", _p),
+                ("workspace", _p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [("batch", _i32), ("n_q_heads", _i32), ("n_kv_heads", _i32),
+                ("head_dim", _i32), ("n_tokens", _i32), ("sketch_dim", _i32),
+                ("cap", _i32),
+                ("q", _p), ("resident_kv", _p), ("resident_idx", _p),
+                ("resident_count", _p), ("sketch", _p), ("proj", _p), ("r", _p),
+                ("host_kv", _p),
+                ("eps", ctypes.c_float), ("delta", ctypes.c_float),
+                ("estimator", _i32), ("weights", _i32), ("fetch_cap", _i32),
+                ("out", _p), ("d_hat", _p), ("log_shift", _p), ("eps_hat0", _p),
+                ("eps_hat", _p), ("k_star", _p), ("fetch_idx", _p),
+                ("fetch_count", _p), ("host_bytes", _p), ("row_stats", _p),
+                ("status", _p), ("workspace", _p),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+class VerKVError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{STATUS_NAMES.get(code, code)}: {msg}")
+        self.code = code
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m verified_sparse_kv_amd.build` (there is no fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name in EXPORTS:
+        if not hasattr(lib, name):
+            raise ImportError(f"{LIB_PATH} does not export {name}")
+    lib.vkv_compress_workspace_bytes.argtypes = [ctypes.POINTER(CompressArgs)]
+    lib.vkv_compress_workspace_bytes.restype = ctypes.c_size_t
+    lib.vkv_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeArgs)]
+    lib.vkv_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.vkv_compress.argtypes = [ctypes.POINTER(CompressArgs), _p]
+    lib.vkv_compress.restype = ctypes.c_int
+    lib.vkv_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _p]
+    lib.vkv_decode_step.restype = ctypes.c_int
+    lib.vkv_check_status.argtypes = [_p, _p, ctypes.POINTER(ctypes.c_uint32)]
+    lib.vkv_check_status.restype = ctypes.c_int
+    lib.vkv_last_error.argtypes = []
+    lib.vkv_last_error.restype = ctypes.c_char_p
+    lib.vkv_version.argtypes = []
+    lib.vkv_version.restype = ctypes.c_int32
+    return lib
+
+
+LIB = _load()
+
+
+# ------------------------------------------------------------ C-named calls
+def vkv_compress_workspace_bytes(args):
+    return int(LIB.vkv_compress_workspace_bytes(ctypes.byref(args)))
+
+
+def vkv_decode_workspace_bytes(args):
+    return int(LIB.vkv_decode_workspace_bytes(ctypes.byref(args)))
+
+
+def vkv_compress(args, stream=None):
+    return int(LIB.vkv_compress(ctypes.byref(args), stream))
+
+
+def vkv_decode_step(args, stream=None):
+    return int(LIB.vkv_decode_step(ctypes.byref(args), stream))
+
+
+def vkv_check_status(status_ptr, stream=None):
+    bits = ctypes.c_uint32(0)
+    rc = int(LIB.vkv_check_status(status_ptr, stream, ctypes.byref(bits)))
+    return rc, int(bits.value)
+
+
+def vkv_last_error():
+    return LIB.vkv_last_error().decode()
+
+
+def vkv_version():
+    return int(LIB.vkv_version())
+
+
+def _check(rc):
+    if rc != VKV_OK:
+        raise VerKVError(rc, vkv_last_error())
+
+
+# ------------------------------------------------------------ torch helpers
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, dtype, shape, name, device=True):
+    torch = _torch()
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if not device and (t.is_cuda or not t.is_pinned()):
+        raise ValueError(f"{name}: must be pinned host memory")
+    return torch
+
+
+def compress(tau, k, v, budget, n_sink, n_local, seed, cap, layer0=0,
+             with_kv=True, stream=None, workspace=None):
+    """PoissonComp. tau [Lyr][G][n] f32, k/v [Lyr][G][n][d] int16 (bf16
+    bits) on the device. Returns a dict of device tensors."""
+    torch = _torch()
+    Ly, G, n = tau.shape
+    _need(tau, torch.float32, (Ly, G, n), "tau")
+    d = 128
+    if with_kv:
+        _need(k, torch.int16, (Ly, G, n, d), "k")
+        _need(v, torch.int16, (Ly, G, n, d), "v")
+    dev = tau.device
+    out = dict(
+        r=torch.empty((Ly, G, n), dtype=torch.float32, device=dev),
+        resident_idx=torch.empty((Ly, G, cap), dtype=torch.int32, device=dev),
+        resident_count=torch.empty((Ly, G), dtype=torch.int32, device=dev),
+        resident_kv=(torch.empty((Ly, G, cap, 2, d), dtype=torch.int16,
+                                 device=dev) if with_kv else None),
+        water_level=torch.empty((Ly, G), dtype=torch.float64, device=dev),
+        status=torch.zeros((1,), dtype=torch.int32, device=dev))
+    a = CompressArgs(n_layers=Ly, n_kv_heads=G, n_tokens=n, head_dim=d,
+                     layer0=layer0, tau=_ptr(tau),
+                     k=_ptr(k) if with_kv else None,
+                     v=_ptr(v) if with_kv else None, budget=int(budget),
+                     n_sink=n_sink, n_local=n_local,
+                     seed=int(seed) & 0xFFFFFFFFFFFFFFFF, cap=cap,
+                     r=_ptr(out["r"]), resident_idx=_ptr(out["resident_idx"]),
+                     resident_count=_ptr(out["resident_count"]),
+                     resident_kv=_ptr(out["resident_kv"]),
+                     water_level=_ptr(out["water_level"]),
+                     status=_ptr(out["status"]))
+    nbytes = vkv_compress_workspace_bytes(a)
+    if nbytes == 0:
+        _check(vkv_compress(a, _stream(stream)))
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = nbytes
+    _check(vkv_compress(a, _stream(stream)))
+    out["workspace"] = workspace
+    out["_args"] = a
+    return out
+
+
+class DecodeStep:
+    """Reusable decode-step launcher: outputs and workspace are allocated once
+    for a shape, so repeated steps only marshal pointers and launch."""
+
+    def __init__(self, B, Hq, G, n, s, cap, fetch_cap, device, d=128):
+        torch = _torch()
+        self.shape = (B, Hq, G, n, s, cap, fetch_cap)
+        self.out = dict(
+            out=torch.empty((B, Hq, d), dtype=torch.float32, device=device),
+            d_hat=torch.empty((B, Hq), dtype=torch.float32, device=device),
+            log_shift=torch.empty((B, Hq), dtype=torch.float32, device=device),
+            eps_hat0=torch.empty((B, Hq), dtype=torch.float32, device=device),
+            eps_hat=torch.empty((B, Hq), dtype=torch.float32, device=device),
+            k_star=torch.empty((B, Hq), dtype=torch.int32, device=device),
+            fetch_idx=torch.empty((B, G, fetch_cap), dtype=torch.int32,
+                                  device=device),
+            fetch_count=torch.empty((B, G), dtype=torch.int32, device=device),
+            host_bytes=torch.zeros((1,), dtype=torch.int64, device=device),
+            row_stats=torch.empty((B, Hq, 8), dtype=torch.float64,
+                                  device=device),
+            status=torch.zeros((1,), dtype=torch.int32, device=device))
+        self.args = DecodeArgs(batch=B, n_q_heads=Hq, n_kv_heads=G, head_dim=d,
+                               n_tokens=n, sketch_dim=s, cap=cap,
+                               fetch_cap=fetch_cap)
+        for key in ("out", "d_hat", "log_shift", "eps_hat0", "eps_hat", "k_star",
+                    "fetch_idx", "fetch_count", "host_bytes", "row_stats",
+                    "status"):
+            setattr(self.args, key, _ptr(self.out[key]))
+        nbytes = vkv_decode_workspace_bytes(self.args)
+        if nbytes == 0:
+            raise VerKVError(VKV_EINVAL, vkv_last_error())
+        self.workspace = torch.empty((nbytes,), dtype=torch.uint8, device=device)
+        self.args.workspace = _ptr(self.workspace)
+        self.args.workspace_bytes = nbytes
+
+    def bind(self, q, resident_kv, resident_idx, resident_count, sketch, proj, r,
+             host_kv, eps, delta, estimator=EST_CLIP, weights=W_SKETCH):
+        torch = _torch()
+        B, Hq, G, n, s, cap, _ = self.shape
+        d = 128
+        _need(q, torch.int16, (B, Hq, d), "q")
+        _need(resident_kv, torch.int16, (B, G, cap, 2, d), "resident_kv")
+        _need(resident_idx, torch.int32, (B, G, cap), "resident_idx")
+        _need(resident_count, torch.int32, (B, G), "resident_count")
+        _need(r, torch.float32, (B, G, n), "r")
+        _need(host_kv, torch.int16, (B, G, n, 2, d), "host_kv", device=False)
+        if weights == W_SKETCH:
+            _need(sketch, torch.int16, (B, G, n, s), "sketch")
+            _need(proj, torch.float32, (G, d, s), "proj")
+        a = self.args
+        a.q, a.resident_kv = _ptr(q), _ptr(resident_kv)
+        a.resident_idx, a.resident_count = _ptr(resident_idx), _ptr(resident_count)
+        a.sketch, a.proj, a.r = _ptr(sketch), _ptr(proj), _ptr(r)
+        a.host_kv = _ptr(host_kv)
+        a.eps, a.delta = float(eps), float(delta)
+        a.estimator, a.weights = int(estimator), int(weights)
+        self._keep = (q, resident_kv, resident_idx, resident_count, sketch, proj,
+                      r, host_kv)
+        return self
+
+    def launch(self, stream=None):
+        _check(vkv_decode_step(self.args, _stream(stream)))
+        return self.out
+
+    def check_status(self, stream=None):
+        rc, bits = vkv_check_status(_ptr(self.out["status"]), _stream(stream))
+        return rc, bits
+
+
+def decode_step(q, resident_kv, resident_idx, resident_count, sketch, proj, r,
+                host_kv, eps, delta, fetch_cap=None, estimator=EST_CLIP,
+                weights=W_SKETCH, stream=None):
+    """One KVFetch decode step (allocates outputs and workspace)."""
+    B, Hq, _ = q.shape
+    _, G, cap = resident_idx.shape
+    n = r.shape[-1]
+    s = sketch.shape[-1] if sketch is not None else 32
+    step = DecodeStep(B, Hq, G, n, s, cap, fetch_cap or n, q.device)
+    step.bind(q, resident_kv, resident_idx, resident_count, sketch, proj, r,
+              host_kv, eps, delta, estimator, weights)
+    return step.launch(stream)
