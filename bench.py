@@ -1,0 +1,267 @@
+#!/usr/bin/env python3
+"""Benchmark of one verified decode step (KVFetch) on one MI355X.
+
+Default workload (the metric's configuration): a Qwen3-4B-shaped decode layer
+with 32 query heads over 8 KV heads, head_dim 128, 32768 tokens of context,
+batch 1, 1/16 of the cache resident, a 32-dim bf16 key sketch, eps = 0.1,
+delta = 0.05. The cache is compressed once by the library (PoissonComp);
+then every timed step runs the whole decode path -- sketch scan, exact
+resident logits, shrinkage fixed point, certificate, gain selection, fetch
+from pinned host memory and corrected attention -- for a fresh query.
+
+Prints one JSON line. ``value`` is q-head x context tokens per second over
+the timed steps (inputs resident in HBM, full cache in pinned host memory).
+The ``roofline`` object covers the longest-running HBM-bound kernel, timed
+with HIP events recorded by the library on its own stream inside the timed
+region; ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("verified decode steps/sec (q-heads x ctx tokens/s) at 32K; "
+          "% HBM peak; fetch %")
+HBM_PEAK_GBS = 8000.0
+ROW_BYTES = 2 * 128 * 2  # one token's K and V rows in bf16
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4"])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU work budget of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(w, counts):
+    """Compulsory HBM bytes of one step and of each HBM-bound kernel.
+
+    Step: sketch + r for every (request, KV head, token), the resident K and V
+    rows with their positions, and q in / out (17 + 129 eta bytes per q-head
+    x token at s = 32, d = 128, 4 query heads per KV head).
+    Per kernel: the sketch scan reads the sketch and r; the resident-logit
+    kernel reads the resident K rows and positions; every estimator pass
+    (beta levels, certificate, selection, marking) reads the fp32 sketch
+    logit of each (query head, token) and r shared by the group's heads; the
+    attention kernel reads the resident V rows and positions and writes out.
+    The gather is bound by the host link and reported separately.
+    """
+    B, Hq, G, n, s, d = w["B"], w["Hq"], w["G"], w["n"], w["s"], w["d"]
+    grp = Hq // G
+    rows = int(counts.sum())
+    scan = B * G * n * (2 * s + 4)
+    est = B * Hq * n * 4 + B * G * n * 4
+    per = {"scan": scan, "resident": rows * (2 * d + 4),
+           "attn": rows * (2 * d + 4) + B * Hq * d * 4}
+    for k in ("beta0", "beta1", "beta2", "beta3", "cert", "select0", "mark"):
+        per[k] = est
+    del grp
+    return dict(step=scan + rows * (4 * d + 4) + B * Hq * d * (2 + 4),
+                kernels=per)
+
+
+def cpu_baseline(w, seconds):
+    """The oracle (never tuned) decoding KV-head groups of the same layer until
+    `seconds` of CPU work have been spent."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import compress as oc
+    from oracle import decode as od
+    from workloads import bf16_to_f32
+
+    B, G, Hq, n = w["B"], w["G"], w["Hq"], w["n"]
+    grp = Hq // G
+    units = 0
+    groups = 0
+    spent = 0.0
+    prepared = {}
+    while spent < seconds and groups < 1000:
+        b, g = (groups // G) % B, groups % G
+        if (b, g) not in prepared:
+            sl = oc.compress_slice(w["tau"][b, g], w["budget"], w["n_sink"],
+                                   w["n_local"], w["seed"], b, g)
+            kv = bf16_to_f32(w["host_kv"][b, g])
+            idx = sl["resident_idx"]
+            prepared[(b, g)] = (sl["r"], idx,
+                                np.stack([kv[idx, 0], kv[idx, 1]], axis=1), kv,
+                                bf16_to_f32(w["sketch"][b, g]))
+        r, idx, res_kv, kv, sk = prepared[(b, g)]
+        q = bf16_to_f32(w["q_steps"][groups % len(w["q_steps"])]
+                        [b, g * grp:(g + 1) * grp])
+        t0 = time.perf_counter()
+        od.decode_group(q, res_kv, idx, sk, w["proj"][g], r, kv, w["eps"],
+                        w["delta"])
+        spent += time.perf_counter() - t0
+        units += grp * n
+        groups += 1
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": units / spent, "unit": "q-head*ctx-tokens/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"{groups} decisions-groups (one KV head, {grp} query "
+                      f"heads, {n} tokens, fresh query each) of the same "
+                      f"layer, fp64 numpy, {spent:.1f} s; "
+                      f"host cores available: {len(os.sched_getaffinity(0))}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); the "
+              "decode step shards by request and KV head with no exchange, "
+              "so per-GPU throughput is the figure to scale.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from verified_sparse_kv_amd import verkv as vk
+    from workloads import c3_shift_queries, make_decode_workload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    w = make_decode_workload(args.config, seed=args.seed, with_queries=False)
+    B, Hq, G, n, s, d = w["B"], w["Hq"], w["G"], w["n"], w["s"], w["d"]
+
+    # ---- PoissonComp by the library (prefill time, untimed)
+    t_tau = torch.from_numpy(w["tau"]).to(dev)
+    t_k = torch.from_numpy(np.ascontiguousarray(
+        w["host_kv"][:, :, :, 0, :]).view(np.int16)).to(dev)
+    t_v = torch.from_numpy(np.ascontiguousarray(
+        w["host_kv"][:, :, :, 1, :]).view(np.int16)).to(dev)
+    cap = int(w["budget"] + 8 * math.sqrt(w["budget"]) + 64)
+    comp = vk.compress(t_tau, t_k, t_v, w["budget"], w["n_sink"], w["n_local"],
+                       w["seed"], cap)
+    rc, bits = vk.vkv_check_status(vk._ptr(comp["status"]), vk._stream(None))
+    assert rc == 0, (rc, bits)
+    del t_k, t_v
+    counts = comp["resident_count"].cpu().numpy()
+
+    # ---- queries: a fresh one per step
+    nq = max(args.steps, 1)
+    rng = np.random.default_rng([2, args.seed, 4242])
+    qs = [rng.standard_normal((B, Hq, d), dtype=np.float32) for _ in range(nq)]
+    from workloads import bf16_bits
+    qs = [bf16_bits(q) for q in qs]
+    if args.config == "c3":
+        r_np = comp["r"].cpu().numpy()
+        ridx = comp["resident_idx"].cpu().numpy()
+        masks = np.zeros((B, G, n), dtype=bool)
+        for b in range(B):
+            for g in range(G):
+                masks[b, g, ridx[b, g, :counts[b, g]]] = True
+        qs = [c3_shift_queries(w, masks, r_np, step=i) for i in range(nq)]
+    w["q_steps"] = qs
+    t_qs = [torch.from_numpy(q.view(np.int16)).to(dev) for q in qs]
+    sketch = torch.from_numpy(w["sketch"].view(np.int16)).to(dev)
+    proj = torch.from_numpy(w["proj"]).to(dev)
+    host_kv = torch.from_numpy(w["host_kv"].view(np.int16)).pin_memory()
+
+    step = vk.DecodeStep(B, Hq, G, n, s, cap, n, dev)
+    step.bind(t_qs[0], comp["resident_kv"], comp["resident_idx"],
+              comp["resident_count"], sketch, proj, comp["r"], host_kv,
+              w["eps"], w["delta"])
+    names = vk.decode_phase_names()
+    P = len(names)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(P + 1)]
+              for _ in range(args.steps)]
+    for ev in events:
+        for e in ev:
+            e.record()
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        step.args.q = vk._ptr(t_qs[i % nq])
+        step.set_phase_events(None)
+        step.launch()
+    torch.cuda.synchronize()
+
+    ks = []
+    hb = []
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step.args.q = vk._ptr(t_qs[i])
+        step.set_phase_events(events[i])
+        step.launch()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    rc, bits = step.check_status()
+    assert rc == 0, (rc, bits, vk.vkv_last_error())
+    ms = (t1 - t0) * 1e3 / max(args.steps, 1)
+
+    # per-kernel times from the library's events
+    ph = np.zeros(P)
+    for ev in events:
+        for j in range(P):
+            ph[j] += ev[j].elapsed_time(ev[j + 1])
+    ph_us = ph * 1e3 / max(args.steps, 1)
+    out = step.out
+    host_bytes = int(out["host_bytes"][0])
+    ks = out["k_star"].cpu().numpy()
+    fetch_pct = 100.0 * host_bytes / (B * G * n * ROW_BYTES)
+
+    ab = algorithmic_bytes(w, counts)
+    units = B * Hq * n
+    value = units / (ms * 1e-3)
+    # roofline of the longest HBM-bound kernel (the gather is bound by the
+    # host link and reported separately)
+    cand = ab["kernels"]
+    dom = max(cand, key=lambda k: ph_us[names.index(k)])
+    t_dom = ph_us[names.index(dom)] * 1e-6
+    achieved = cand[dom] / t_dom / 1e9
+    t_gather = ph_us[names.index("gather")] * 1e-6
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "q-head*ctx-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": {"c2": "Qwen3-4B-shaped decode layer, 32K context",
+                         "c3": "Qwen3-4B-shaped decode layer, batch 16, 32K, "
+                               "fetch active",
+                         "c4": "Ministral-8B-shaped decode layer, 128K "
+                               "context"}[args.config],
+            "batch": B, "q_heads": Hq, "kv_heads": G, "head_dim": d,
+            "ctx_tokens": n, "budget": w["budget"], "sketch_dim": s,
+            "n_sink": w["n_sink"], "n_local": w["n_local"], "eps": w["eps"],
+            "delta": w["delta"], "parallelism": "none (1 GPU)"},
+        "steps_per_s": 1e3 / ms,
+        "hbm_peak_pct": 100.0 * ab["step"] / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        "fetch_pct": fetch_pct,
+        "host_bytes_per_step": host_bytes,
+        "host_fetch_gbs": host_bytes / t_gather / 1e9 if t_gather > 0 else None,
+        "decisions_fetching_pct": 100.0 * float(np.mean(ks > 0)),
+        "kernel_us": {k: round(float(v), 2) for k, v in zip(names, ph_us)},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes": cand[dom]},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

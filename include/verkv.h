@@ -93,7 +93,8 @@ enum { VKV_W_SKETCH = 0, VKV_W_PERFECT = 1 };
  * water_level (may be NULL) [n_layers][n_kv_heads] f64, c in units of tau
  * (+inf when every token is in H).
  * status   dev u32 [1], cleared at the start of the call.
- * Supported: head_dim = 128, 1 <= n_tokens <= 2^24.
+ * Supported: head_dim = 128, 1 <= n_tokens <= 2^21 and budget <= 2^21, so that
+ * every integer product of the water-level solve stays below 2^53.
  */
 typedef struct {
   int32_t n_layers, n_kv_heads, n_tokens, head_dim;
@@ -143,6 +144,9 @@ typedef struct {
  * host_kv this step; row_stats (may be NULL) [B][Hq][8] f64 =
  * {m, D~ (scaled by exp(-m)), beta*, beta(L), V(L), b(L), eps^(L), eps^(L')}.
  * status   dev u32 [1], cleared at the start of the call.
+ * phase_events  optional timing hook: NULL, or vkv_decode_phase_count() + 1
+ *          hipEvent_t handles (created by the caller); event 0 is recorded on
+ *          `stream` before the first kernel and event i + 1 after kernel i.
  */
 typedef struct {
   int32_t batch, n_q_heads, n_kv_heads, head_dim, n_tokens, sketch_dim, cap;
@@ -167,6 +171,7 @@ typedef struct {
   uint64_t *host_bytes;
   double *row_stats;
   uint32_t *status;
+  void **phase_events;
   void *workspace;
   size_t workspace_bytes;
 } vkv_decode_args;
@@ -189,6 +194,11 @@ vkv_status vkv_check_status(const uint32_t *status, void *stream,
 
 /* Thread-local text describing the last non-OK status of this thread. */
 const char *vkv_last_error(void);
+
+/* Kernels one decode step launches, in order, and their names (for the
+ * phase_events timing hook); NULL for an index out of range. */
+int32_t vkv_decode_phase_count(void);
+const char *vkv_decode_phase_name(int32_t i);
 
 /* Library version as major*10000 + minor*100 + patch. */
 int32_t vkv_version(void);

@@ -163,3 +163,11 @@ def test_decode_workspace_too_small():
 
 def test_version():
     assert vk.vkv_version() >= 100
+
+
+def test_phase_names():
+    names = vk.decode_phase_names()
+    assert len(names) == vk.vkv_decode_phase_count() >= 10
+    assert names[0] == "scan" and names[-1] == "attn"
+    assert vk.vkv_decode_phase_name(len(names)) is None
+    assert vk.vkv_decode_phase_name(-1) is None

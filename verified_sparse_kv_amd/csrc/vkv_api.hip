@@ -80,6 +80,10 @@ const char *vkv_last_error(void) { return g_err; }
 
 int32_t vkv_version(void) { return 100; }
 
+int32_t vkv_decode_phase_count(void) { return vkv::decode_phase_count(); }
+
+const char *vkv_decode_phase_name(int32_t i) { return vkv::decode_phase_name(i); }
+
 size_t vkv_compress_workspace_bytes(const vkv_compress_args *a) {
   if (check_compress_shapes(a) != VKV_OK) return 0;
   return vkv::compress_layout(*a).total;

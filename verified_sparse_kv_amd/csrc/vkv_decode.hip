@@ -35,6 +35,8 @@
 // go through the same inline functions and the library is built with
 // floating-point contraction off, so every pass sees identical values.
 
+#include <algorithm>
+
 #include "vkv_common.h"
 #include "vkv_internal.h"
 
@@ -203,6 +205,34 @@ __device__ __forceinline__ int row_of(const DParams &p, int b, int g, int h,
   return b * p.Hq + g * grp + h;
 }
 
+// Rows [lo, hi) of `total` handled by part `idx` of `parts` (even split).
+__device__ __forceinline__ void split_range(int total, int parts, int idx,
+                                            int &lo, int &hi) {
+  lo = (int)(((long long)total * idx) / parts);
+  hi = (int)(((long long)total * (idx + 1)) / parts);
+}
+
+// Inclusive prefix sum over the lanes of a wave (lane order).
+template <typename T>
+__device__ __forceinline__ T wave_incl_scan(T v, int lane) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) {
+    const T o = __shfl_up(v, m, kWave);
+    if (lane >= m) v += o;
+  }
+  return v;
+}
+
+// Inclusive prefix maximum over the lanes of a wave.
+__device__ __forceinline__ uint32_t wave_incl_max(uint32_t v, int lane) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) {
+    const uint32_t o = __shfl_up(v, m, kWave);
+    if (lane >= m) v = max(v, o);
+  }
+  return v;
+}
+
 // ------------------------------------------------------------ dk_scan
 template <int GRP, int SD>
 __global__ __launch_bounds__(kBlock) void dk_scan(DParams p) {
@@ -249,18 +279,30 @@ __global__ __launch_bounds__(kBlock) void dk_scan(DParams p) {
       }
     }
   }
-  // projected, pre-scaled queries
-  if (threadIdx.x < GRP * SD) {
-    const int h = threadIdx.x / SD, j = threadIdx.x % SD;
-    const float *P = p.proj + (size_t)g * kHeadDim * SD;
-    const uint16_t *qh = p.q + (size_t)row_of(p, b, g, h, GRP) * kHeadDim;
-    float acc = 0.0f;
-    for (int e = 0; e < kHeadDim; ++e)
-      acc = __builtin_fmaf(P[e * SD + j], __uint_as_float((uint32_t)qh[e] << 16),
-                           acc);
-    s_qp[h][j] = acc * kInvSqrtD;
+  // projected, pre-scaled queries: stage q and P_g in LDS, then one output
+  // per thread
+  {
+    __shared__ float s_proj[kHeadDim * SD];
+    __shared__ float s_q[GRP][kHeadDim];
+    const float4 *P4 =
+        reinterpret_cast<const float4 *>(p.proj + (size_t)g * kHeadDim * SD);
+    for (int i = threadIdx.x; i < kHeadDim * SD / 4; i += kBlock)
+      reinterpret_cast<float4 *>(s_proj)[i] = P4[i];
+    for (int i = threadIdx.x; i < GRP * kHeadDim; i += kBlock) {
+      const int h = i / kHeadDim, e = i % kHeadDim;
+      s_q[h][e] = __uint_as_float(
+          (uint32_t)p.q[(size_t)row_of(p, b, g, h, GRP) * kHeadDim + e] << 16);
+    }
+    __syncthreads();
+    if (threadIdx.x < GRP * SD) {
+      const int h = threadIdx.x / SD, j = threadIdx.x % SD;
+      float acc = 0.0f;
+      for (int e = 0; e < kHeadDim; ++e)
+        acc = __builtin_fmaf(s_proj[e * SD + j], s_q[h][e], acc);
+      s_qp[h][j] = acc * kInvSqrtD;
+    }
+    __syncthreads();
   }
-  __syncthreads();
   const int u = lane % LPT;
   float qv[GRP][8];
 #pragma unroll
@@ -277,22 +319,33 @@ __global__ __launch_bounds__(kBlock) void dk_scan(DParams p) {
   const float *rr = p.r + (size_t)bg * p.n;
   const int base = c * p.chunk;
   const int lim = min(base + p.chunk, p.n);
-  for (int i0 = base; i0 < lim; i0 += TPI) {
-    const int i = i0 + threadIdx.x / LPT;
-    if (i < lim) {
-      const uint4 raw =
-          *reinterpret_cast<const uint4 *>(sk + (size_t)i * SD + u * 8);
+  constexpr int UNR = 4;  // sketch rows in flight per lane
+  for (int i0 = base; i0 < lim; i0 += TPI * UNR) {
+    uint4 raw[UNR];
+    float rv[UNR];
+#pragma unroll
+    for (int k = 0; k < UNR; ++k) {
+      const int i = i0 + k * TPI + threadIdx.x / LPT;
+      if (i < lim) {
+        raw[k] = *reinterpret_cast<const uint4 *>(sk + (size_t)i * SD + u * 8);
+        rv[k] = rr[i];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < UNR; ++k) {
+      const int i = i0 + k * TPI + threadIdx.x / LPT;
+      if (i >= lim) continue;
       float f[8];
-      unpack8(raw, f);
+      unpack8(raw[k], f);
       float dot[GRP];
 #pragma unroll
       for (int h = 0; h < GRP; ++h) {
         float acc = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) acc = __builtin_fmaf(qv[h][k], f[k], acc);
+        for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(qv[h][e], f[e], acc);
         dot[h] = group_sum<LPT>(acc);
       }
-      const float ri = rr[i];
+      const float ri = rv[k];
       if (!(ri > 0.0f && ri <= 1.0f)) bad = true;
       const bool in_l = ri < 1.0f;
       if (u == 0 && !in_l) ++n_h;
@@ -412,6 +465,7 @@ __global__ __launch_bounds__(kBlock) void dk_scan_exact(DParams p) {
 }
 
 // ------------------------------------------------------------ dk_resident
+// The group's resident rows are split evenly over gridDim.x workgroups.
 template <int GRP>
 __global__ __launch_bounds__(kBlock) void dk_resident(DParams p) {
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -436,11 +490,11 @@ __global__ __launch_bounds__(kBlock) void dk_resident(DParams p) {
 #pragma unroll
   for (int h = 0; h < GRP; ++h) mx[h] = -INFINITY;
   uint32_t n_h = 0;
-  const int base = c * p.chunk;
-  const int lim = min(base + p.chunk, cnt);
-  for (int j0 = base; j0 < lim; j0 += kBlock / 16) {
+  int lo, hi;
+  split_range(cnt, gridDim.x, c, lo, hi);
+  for (int j0 = lo; j0 < hi; j0 += kBlock / 16) {
     const int j = j0 + threadIdx.x / 16;
-    if (j < lim) {
+    if (j < hi) {
       const int pos = ridx[j];
       const bool ok = pos >= 0 && pos < p.n && (j == 0 || ridx[j - 1] < pos);
       const uint4 raw = *reinterpret_cast<const uint4 *>(
@@ -468,28 +522,32 @@ __global__ __launch_bounds__(kBlock) void dk_resident(DParams p) {
     }
   }
   if (bad) atomicOr(p.status, VKV_STATUS_BAD_RESIDENT);
+  const int np = p.nch + p.ncr;
 #pragma unroll
   for (int h = 0; h < GRP; ++h) {
     const float v = block_max<float>(mx[h], s_red);
     if (threadIdx.x == 0)
-      p.pmax[(size_t)row_of(p, b, g, h, GRP) * (p.nch + p.ncr) + p.nch + c] = v;
+      p.pmax[(size_t)row_of(p, b, g, h, GRP) * np + p.nch + c] = v;
   }
   const uint32_t th = block_sum<uint32_t>(n_h, s_ured);
-  if (threadIdx.x == 0) p.hpart[(size_t)bg * (p.nch + p.ncr) + p.nch + c] = th;
+  if (threadIdx.x == 0) p.hpart[(size_t)bg * np + p.nch + c] = th;
   if (!last_block_arrive(&p.groups[bg].arrive[ARR_RES], gridDim.x)) return;
-  // shift per row; every token with r == 1 must be resident
-  const int np = p.nch + p.ncr;
-  if (threadIdx.x < GRP) {
-    const int row = row_of(p, b, g, threadIdx.x, GRP);
+  // shift per row (one wave per head); every token with r == 1 must be resident
+  const int wave = threadIdx.x / kWave;
+  for (int h = wave; h < GRP; h += kBlock / kWave) {
+    const int row = row_of(p, b, g, h, GRP);
     float m = -INFINITY;
-    for (int i = 0; i < np; ++i) m = fmaxf(m, p.pmax[(size_t)row * np + i]);
-    p.rows[row].m = m;
+    for (int i = lane; i < np; i += kWave) m = fmaxf(m, p.pmax[(size_t)row * np + i]);
+    m = wave_max(m);
+    if (lane == 0) p.rows[row].m = m;
   }
-  if (threadIdx.x == 0) {
+  if (wave == 0) {
     uint32_t all_h = 0, res_h = 0;
-    for (int i = 0; i < p.nch; ++i) all_h += p.hpart[(size_t)bg * np + i];
-    for (int i = 0; i < p.ncr; ++i) res_h += p.hpart[(size_t)bg * np + p.nch + i];
-    if (all_h != res_h) atomicOr(p.status, VKV_STATUS_BAD_RESIDENT);
+    for (int i = lane; i < p.nch; i += kWave) all_h += p.hpart[(size_t)bg * np + i];
+    for (int i = lane; i < p.ncr; i += kWave) res_h += p.hpart[(size_t)bg * np + p.nch + i];
+    all_h = wave_sum(all_h);
+    res_h = wave_sum(res_h);
+    if (lane == 0 && all_h != res_h) atomicOr(p.status, VKV_STATUS_BAD_RESIDENT);
   }
 }
 
@@ -579,12 +637,13 @@ __global__ __launch_bounds__(kBlock) void dk_beta(DParams p, int lev) {
   if (lev == 0) {
     const int cnt = max(0, min(p.rcount[bg], p.cap));
     const int32_t *ridx = p.ridx + (size_t)bg * p.cap;
-    const int jlim = min(base + p.chunk, cnt);
+    int jlo, jhi;
+    split_range(cnt, gridDim.x, c, jlo, jhi);
 #pragma unroll
     for (int h = 0; h < GRP; ++h) {
       const int row = row_of(p, b, g, h, GRP);
       double sh = 0.0;
-      for (int j = base + threadIdx.x; j < jlim; j += kBlock) {
+      for (int j = jlo + threadIdx.x; j < jhi; j += kBlock) {
         const int pos = ridx[j];
         if (pos >= 0 && pos < p.n && rr[pos] >= 1.0f)
           sh += (double)expf(p.ell[(size_t)row * p.cap + j] - s_m[h]);
@@ -605,70 +664,94 @@ __global__ __launch_bounds__(kBlock) void dk_beta(DParams p, int lev) {
     }
   }
   if (!last_block_arrive(&p.groups[bg].arrive[ARR_BETA], gridDim.x)) return;
-  // ---- last block: one thread per head scans the edges
-  if (threadIdx.x < GRP) {
-    const int h = threadIdx.x;
+  // ---- last block: one wave per head scans the edges of the bracket.
+  // h(e_j) = C(j) + W(j) - e_j (1 + R(j)) with C, W, R the prefix sums of the
+  // difference arrays; h decreases, so the root lies after the last edge
+  // with h > 0.
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  constexpr int PER = 5;  // 64 lanes x 5 >= 257 edges
+  for (int h = wave; h < GRP; h += kBlock / kWave) {
     const int row = row_of(p, b, g, h, GRP);
     RowState &rs = p.rows[row];
     double *gb = p.bbins + (size_t)row * 3 * kBetaEdges;
     if (lev == 0) {
       double dl = 0.0, dh = 0.0;
-      for (int i = 0; i < p.nch; ++i) {
+      for (int i = lane; i < p.nch; i += kWave) {
         const double2 v = p.dpart[(size_t)row * p.nch + i];
         dl += v.x;
         dh += v.y;
       }
-      rs.dnorm = dh + dl;
-      if (p.est != VKV_EST_CLIP) {
-        rs.bdone = 1;
-        rs.beta = 0.0;
+      dl = wave_sum(dl);
+      dh = wave_sum(dh);
+      if (lane == 0) {
+        rs.dnorm = dh + dl;
+        if (p.est != VKV_EST_CLIP) {
+          rs.bdone = 1;
+          rs.beta = 0.0;
+        }
       }
     }
     if (s_active[h]) {
       const uint32_t pa = s_pa[h];
-      double C = 0.0, W = 0.0, R = 0.0;
-      double hprev = 0.0;
-      int root = -1;
-      double h_at[2] = {0.0, 0.0};
-      for (int j = 0; j <= nb; ++j) {
-        C += gb[j];
-        W += gb[kBetaEdges + j];
-        R += gb[2 * kBetaEdges + j];
-        if (lev == 0 && j == 255) break;  // +inf edge
-        const double e = (double)__uint_as_float(pa + ((uint32_t)j << shift));
-        const double hv = C + W - e * (1.0 + R);
-        if (j < nb && hv > 0.0) {
-          root = j;
-          h_at[0] = hv;
-        }
-        if (j == root + 1) h_at[1] = hv;
-        hprev = hv;
+      const int nedge = lev == 0 ? 255 : nb + 1;  // level 0 stops before +inf
+      double C[PER], W[PER], R[PER];
+      double tc = 0.0, tw = 0.0, tr = 0.0;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int j = lane * PER + k;
+        const bool in = j < nedge;
+        tc += in ? gb[j] : 0.0;
+        tw += in ? gb[kBetaEdges + j] : 0.0;
+        tr += in ? gb[2 * kBetaEdges + j] : 0.0;
+        C[k] = tc;
+        W[k] = tw;
+        R[k] = tr;
       }
-      (void)hprev;
-      if (root < 0) {
-        if (lev == 0) {  // no weight in L
+      const double oc = wave_incl_scan(tc, lane) - tc;
+      const double ow = wave_incl_scan(tw, lane) - tw;
+      const double orr = wave_incl_scan(tr, lane) - tr;
+      double Hv[PER];
+      int best = -1;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int j = lane * PER + k;
+        const double e = (double)__uint_as_float(pa + ((uint32_t)j << shift));
+        Hv[k] = (oc + C[k]) + (ow + W[k]) - e * (1.0 + (orr + R[k]));
+        if (j < nedge && j < nb && Hv[k] > 0.0) best = j;
+      }
+      int root = best;
+      for (int m = 32; m >= 1; m >>= 1) root = max(root, __shfl_xor(root, m, kWave));
+      // values at the root edge and the next one
+      double h0 = 0.0, h1 = 0.0;
+      const int r0 = max(root, 0), r1 = r0 + 1;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        if (lane * PER + k == r0) h0 = Hv[k];
+        if (lane * PER + k == r1) h1 = Hv[k];
+      }
+      h0 = __shfl(h0, r0 / PER, kWave);
+      h1 = __shfl(h1, min(r1 / PER, kWave - 1), kWave);
+      if (lane == 0) {
+        if (root < 0 && lev == 0) {  // no weight in L
           rs.beta = 0.0;
           rs.bdone = 1;
         } else {
-          root = 0;
-        }
-      }
-      if (root >= 0) {
-        const uint32_t pj = pa + ((uint32_t)root << shift);
-        if (lev < 3) {
-          rs.bpre = pj;
-        } else {
-          const double e0 = (double)__uint_as_float(pj);
-          const double e1 = (double)__uint_as_float(pj + 1u);
-          const double d = h_at[0] - h_at[1];
-          double bt = d > 0.0 ? e0 + h_at[0] * (e1 - e0) / d : e0;
-          bt = fmin(fmax(bt, e0), e1);
-          rs.beta = bt;
-          rs.bdone = 1;
+          const uint32_t pj = pa + ((uint32_t)r0 << shift);
+          if (lev < 3) {
+            rs.bpre = pj;
+          } else {
+            const double e0 = (double)__uint_as_float(pj);
+            const double e1 = (double)__uint_as_float(pj + 1u);
+            const double d = h0 - h1;
+            double bt = d > 0.0 ? e0 + h0 * (e1 - e0) / d : e0;
+            bt = fmin(fmax(bt, e0), e1);
+            rs.beta = bt;
+            rs.bdone = 1;
+          }
         }
       }
     }
-    for (int i = 0; i < 3 * kBetaEdges; ++i) gb[i] = 0.0;
+    for (int i = lane; i < 3 * kBetaEdges; i += kWave) gb[i] = 0.0;
   }
 }
 
@@ -757,18 +840,26 @@ __global__ __launch_bounds__(kBlock) void dk_cert(DParams p) {
     }
   }
   if (!last_block_arrive(&p.groups[bg].arrive[ARR_CERT], gridDim.x)) return;
-  if (threadIdx.x < GRP) {
-    const int row = row_of(p, b, g, threadIdx.x, GRP);
+  for (int h = wave; h < GRP; h += kBlock / kWave) {
+    const int row = row_of(p, b, g, h, GRP);
     RowState &rs = p.rows[row];
     double tb = 0.0, tv = 0.0;
     float y1 = 0.0f, y2 = 0.0f;
     int yq = 0x7fffffff;
-    for (int i = 0; i < p.nch; ++i) {
+    for (int i = lane; i < p.nch; i += kWave) {
       const CertPart cp = p.cpart[(size_t)row * p.nch + i];
       tb += cp.beta;
       tv += cp.var;
       top2_merge(y1, yq, y2, cp.b1, cp.p1, cp.b2);
     }
+    tb = wave_sum(tb);
+    tv = wave_sum(tv);
+    for (int m = 32; m >= 1; m >>= 1) {
+      const float o1 = shfl_xor(y1, m), o2 = shfl_xor(y2, m);
+      const int oq = shfl_xor(yq, m);
+      top2_merge(y1, yq, y2, o1, oq, o2);
+    }
+    if (lane != 0) continue;
     const double a = p.a_delta, l = p.l_delta;
     rs.betaL = tb;
     rs.VL = tv;
@@ -836,21 +927,15 @@ __device__ void sel_resolve(RowState &rs, const SelBin *bins, int d,
     lv += vs[k];
     lmax = max(lmax, bm[k]);
   }
-  // sums over lanes above (higher bins) and max over lanes below
-  unsigned long long ab = 0, av = 0;
-  uint32_t ac = 0, bmax_below = 0;
-  for (int o = 1; o < kWave; ++o) {
-    const uint32_t oc = __shfl(lc, (lane + o) % kWave, kWave);
-    const unsigned long long ob = __shfl(lb, (lane + o) % kWave, kWave);
-    const unsigned long long ov = __shfl(lv, (lane + o) % kWave, kWave);
-    const uint32_t om = __shfl(lmax, (lane + o) % kWave, kWave);
-    if (lane + o < kWave) {
-      ac += oc;
-      ab += ob;
-      av += ov;
-    }
-    if (lane - (kWave - o) >= 0) bmax_below = max(bmax_below, om);
-  }
+  // sums over the lanes above (higher bins) and max over the lanes below
+  const uint32_t ic = wave_incl_scan<uint32_t>(lc, lane);
+  const unsigned long long ib = wave_incl_scan<unsigned long long>(lb, lane);
+  const unsigned long long iv = wave_incl_scan<unsigned long long>(lv, lane);
+  const uint32_t ac = __shfl(ic, kWave - 1, kWave) - ic;
+  const unsigned long long ab = __shfl(ib, kWave - 1, kWave) - ib;
+  const unsigned long long av = __shfl(iv, kWave - 1, kWave) - iv;
+  uint32_t bmax_below = __shfl_up(wave_incl_max(lmax, lane), 1, kWave);
+  if (lane == 0) bmax_below = 0u;
   // evaluate eps^(tail_x) for each local bin, top to bottom
   int best = -1;
   {
@@ -1284,27 +1369,28 @@ __global__ __launch_bounds__(kBlock) void dk_gather(DParams p) {
   const uint16_t *src_base = p.host_kv + (size_t)bg * p.n * 2 * kHeadDim;
   uint16_t *dst_base = p.staging + (size_t)bg * p.fetch_cap * 2 * kHeadDim;
   const uint32_t units = total * 32u;
-  for (uint32_t u0 = threadIdx.x; u0 < units; u0 += 4 * kBlock) {
-    uint4 v[4];
-    uint32_t slot[4], part[4];
-    bool ok[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t u = u0 + k * kBlock;
-      const uint32_t row = u >> 5;
-      part[k] = u & 31u;
-      slot[k] = offset + row;
-      ok[k] = u < units && slot[k] < (uint32_t)p.fetch_cap;
-      if (ok[k])
-        v[k] = *reinterpret_cast<const uint4 *>(
-            src_base + (size_t)s_pos[row] * 2 * kHeadDim + part[k] * 8);
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (ok[k])
-        *reinterpret_cast<uint4 *>(dst_base + (size_t)slot[k] * 2 * kHeadDim +
-                                   part[k] * 8) = v[k];
+  const uint32_t lim = min(units, ((uint32_t)p.fetch_cap > offset
+                                       ? ((uint32_t)p.fetch_cap - offset) * 32u
+                                       : 0u));
+  auto src_of = [&](uint32_t u) {
+    return reinterpret_cast<const uint4 *>(
+        src_base + (size_t)s_pos[u >> 5] * 2 * kHeadDim + (u & 31u) * 8);
+  };
+  auto dst_of = [&](uint32_t u) {
+    return reinterpret_cast<uint4 *>(
+        dst_base + (size_t)(offset + (u >> 5)) * 2 * kHeadDim + (u & 31u) * 8);
+  };
+  uint32_t u = threadIdx.x;
+  // four 16-byte host loads in flight per lane before their stores
+  for (; u + 3 * kBlock < lim; u += 4 * kBlock) {
+    const uint4 v0 = *src_of(u), v1 = *src_of(u + kBlock),
+                v2 = *src_of(u + 2 * kBlock), v3 = *src_of(u + 3 * kBlock);
+    *dst_of(u) = v0;
+    *dst_of(u + kBlock) = v1;
+    *dst_of(u + 2 * kBlock) = v2;
+    *dst_of(u + 3 * kBlock) = v3;
   }
+  for (; u < lim; u += kBlock) *dst_of(u) = *src_of(u);
   if (c == p.nch - 1 && threadIdx.x == 0) {
     const uint32_t all = offset + total;
     p.fcount[bg] = (int32_t)all;
@@ -1315,18 +1401,40 @@ __global__ __launch_bounds__(kBlock) void dk_gather(DParams p) {
 }
 
 // ------------------------------------------------------------ attention
+constexpr int kMaxFetchRowsPerBlock = 512;
+
+// Coefficient of one resident row for one head: w on H and on F_h, and
+// lambda w / r on S \ F_h.
+template <int GRP>
+__device__ __forceinline__ float resident_alpha(const DParams &p,
+                                                const RowState &rs, int row,
+                                                int pos, float ri, float ell,
+                                                double a, double l) {
+  const float w = expf(ell - rs.m);
+  if (ri >= 1.0f) return w;
+  const Terms t = token_terms(p.shat[(size_t)row * p.n + pos], ri, rs.m,
+                              (float)rs.beta, p.est);
+  if (rs.fetch && rs.kstar > 0 &&
+      is_member(make_key(token_gain(t, pos, rs, a, l), pos), rs))
+    return w;
+  return t.lam * w / ri;
+}
+
+// gridDim.x = ncr resident-row blocks followed by ncf fetched-row blocks;
+// each writes a partial (shift, sum of weights, weighted sum of V) per head.
 template <int GRP>
 __global__ __launch_bounds__(kBlock) void dk_attn(DParams p) {
   const int x = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int bg = b * p.G + g;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int u = lane % 16;       // 8 dims per lane
-  const int grp16 = threadIdx.x / 16;  // row slot within an iteration
+  const int u = lane % 16;             // 8 dims per lane
+  const int slot = threadIdx.x / 16;   // row slot within an iteration
   __shared__ RowState s_rs[GRP];
-  __shared__ float s_lg[GRP][1024];
+  __shared__ float s_lg[GRP][kMaxFetchRowsPerBlock];
   __shared__ float s_o[kBlock / kWave][GRP][kHeadDim];
   __shared__ float s_d[kBlock / kWave][GRP];
   __shared__ float s_red[kBlock / kWave];
+  __shared__ float s_scale[kBlock / kWave][512];  // ncr + ncf <= 512
   if (threadIdx.x < GRP) s_rs[threadIdx.x] = p.rows[row_of(p, b, g, threadIdx.x, GRP)];
   __syncthreads();
   const double a = p.a_delta, l = p.l_delta;
@@ -1339,14 +1447,14 @@ __global__ __launch_bounds__(kBlock) void dk_attn(DParams p) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc[h][k] = 0.0f;
   }
-  const bool resident_part = x < p.ncr;
-  if (resident_part) {
+  if (x < p.ncr) {
     const int cnt = max(0, min(p.rcount[bg], p.cap));
-    const int base = x * p.chunk, lim = min(base + p.chunk, cnt);
+    int lo, hi;
+    split_range(cnt, p.ncr, x, lo, hi);
     const int32_t *ridx = p.ridx + (size_t)bg * p.cap;
-    for (int j0 = base; j0 < lim; j0 += kBlock / 16) {
-      const int j = j0 + grp16;
-      if (j >= lim) continue;
+    for (int j0 = lo; j0 < hi; j0 += kBlock / 16) {
+      const int j = j0 + slot;
+      if (j >= hi) continue;
       const int pos = ridx[j];
       if (pos < 0 || pos >= p.n) continue;
       const float ri = rr[pos];
@@ -1356,30 +1464,21 @@ __global__ __launch_bounds__(kBlock) void dk_attn(DParams p) {
       unpack8(raw, vv);
 #pragma unroll
       for (int h = 0; h < GRP; ++h) {
-        const RowState &rs = s_rs[h];
         const int row = row_of(p, b, g, h, GRP);
-        const float w = expf(p.ell[(size_t)row * p.cap + j] - rs.m);
-        float alpha = w;
-        if (ri < 1.0f) {
-          const Terms t = token_terms(p.shat[(size_t)row * p.n + pos], ri, rs.m,
-                                      (float)rs.beta, p.est);
-          bool member = false;
-          if (rs.fetch && rs.kstar > 0)
-            member = is_member(make_key(token_gain(t, pos, rs, a, l), pos), rs);
-          if (!member) alpha = t.lam * w / ri;
-        }
+        const float alpha = resident_alpha<GRP>(
+            p, s_rs[h], row, pos, ri, p.ell[(size_t)row * p.cap + j], a, l);
         dsum[h] += alpha;
 #pragma unroll
         for (int k = 0; k < 8; ++k) acc[h][k] = __builtin_fmaf(alpha, vv[k], acc[h][k]);
       }
     }
   } else {
-    const int fx = x - p.ncr;
     const int fc = max(0, min(p.fcount[bg], p.fetch_cap));
-    const int base = fx * p.chunk, lim = min(base + p.chunk, fc);
+    int lo, hi;
+    split_range(fc, p.ncf, x - p.ncr, lo, hi);
     const int32_t *fidx = p.fidx + (size_t)bg * p.fetch_cap;
     const uint16_t *st = p.staging + (size_t)bg * p.fetch_cap * 2 * kHeadDim;
-    if (base < lim) {
+    if (lo < hi) {
       float qv[GRP][8];
 #pragma unroll
       for (int h = 0; h < GRP; ++h) {
@@ -1387,53 +1486,72 @@ __global__ __launch_bounds__(kBlock) void dk_attn(DParams p) {
             p.q + (size_t)row_of(p, b, g, h, GRP) * kHeadDim + u * 8);
         unpack8(raw, qv[h]);
       }
-      // pass 1: exact logits of fetched rows (member heads only)
-      for (int j0 = base; j0 < lim; j0 += kBlock / 16) {
-        const int j = j0 + grp16;
-        if (j >= lim) continue;
-        const int pos = fidx[j];
-        const float ri = rr[pos];
-        const uint4 raw = *reinterpret_cast<const uint4 *>(st + (size_t)j * 2 * kHeadDim + u * 8);
-        float kk[8];
-        unpack8(raw, kk);
+      // sub-blocks of at most kMaxFetchRowsPerBlock rows; the running shift
+      // only grows, and earlier sums are rescaled when it does
+      for (int sub = lo; sub < hi; sub += kMaxFetchRowsPerBlock) {
+        const int shi = min(sub + kMaxFetchRowsPerBlock, hi);
+        float mb[GRP];
 #pragma unroll
-        for (int h = 0; h < GRP; ++h) {
-          float accd = 0.0f;
+        for (int h = 0; h < GRP; ++h) mb[h] = -INFINITY;
+        // pass 1: exact logits of the fetched rows that belong to F_h
+        for (int j0 = sub; j0 < shi; j0 += kBlock / 16) {
+          const int j = j0 + slot;
+          if (j >= shi) continue;
+          const int pos = fidx[j];
+          const float ri = rr[pos];
+          const uint4 raw =
+              *reinterpret_cast<const uint4 *>(st + (size_t)j * 2 * kHeadDim + u * 8);
+          float kk[8];
+          unpack8(raw, kk);
 #pragma unroll
-          for (int k = 0; k < 8; ++k) accd = __builtin_fmaf(qv[h][k], kk[k], accd);
-          const float lg = group_sum<16>(accd) * kInvSqrtD;
-          const RowState &rs = s_rs[h];
-          bool member = false;
-          if (rs.fetch && rs.kstar > 0) {
-            const int row = row_of(p, b, g, h, GRP);
-            const Terms t = token_terms(p.shat[(size_t)row * p.n + pos], ri, rs.m,
-                                        (float)rs.beta, p.est);
-            member = is_member(make_key(token_gain(t, pos, rs, a, l), pos), rs);
+          for (int h = 0; h < GRP; ++h) {
+            float accd = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) accd = __builtin_fmaf(qv[h][k], kk[k], accd);
+            const float lg = group_sum<16>(accd) * kInvSqrtD;
+            const RowState &rs = s_rs[h];
+            bool member = false;
+            if (rs.fetch && rs.kstar > 0) {
+              const int row = row_of(p, b, g, h, GRP);
+              const Terms t = token_terms(p.shat[(size_t)row * p.n + pos], ri, rs.m,
+                                          (float)rs.beta, p.est);
+              member = is_member(make_key(token_gain(t, pos, rs, a, l), pos), rs);
+            }
+            const float v = member ? lg : -INFINITY;
+            if (u == 0) s_lg[h][j - sub] = v;
+            mb[h] = fmaxf(mb[h], v);
           }
-          const float v = member ? lg : -INFINITY;
-          if (u == 0) s_lg[h][j - base] = v;
-          mloc[h] = fmaxf(mloc[h], v);
         }
-      }
-#pragma unroll
-      for (int h = 0; h < GRP; ++h) mloc[h] = block_max<float>(mloc[h], s_red);
-      __syncthreads();
-      // pass 2: weights and values
-      for (int j0 = base; j0 < lim; j0 += kBlock / 16) {
-        const int j = j0 + grp16;
-        if (j >= lim) continue;
-        const uint4 raw = *reinterpret_cast<const uint4 *>(st + (size_t)j * 2 * kHeadDim +
-                                                           kHeadDim + u * 8);
-        float vv[8];
-        unpack8(raw, vv);
 #pragma unroll
         for (int h = 0; h < GRP; ++h) {
-          const float lg = s_lg[h][j - base];
-          const float alpha = lg == -INFINITY ? 0.0f : expf(lg - mloc[h]);
-          dsum[h] += alpha;
+          const float m2 = fmaxf(mloc[h], block_max<float>(mb[h], s_red));
+          if (m2 > mloc[h]) {
+            const float sc = expf(mloc[h] - m2);
+            dsum[h] *= sc;
 #pragma unroll
-          for (int k = 0; k < 8; ++k) acc[h][k] = __builtin_fmaf(alpha, vv[k], acc[h][k]);
+            for (int k = 0; k < 8; ++k) acc[h][k] *= sc;
+            mloc[h] = m2;
+          }
         }
+        __syncthreads();
+        // pass 2: weights and values
+        for (int j0 = sub; j0 < shi; j0 += kBlock / 16) {
+          const int j = j0 + slot;
+          if (j >= shi) continue;
+          const uint4 raw = *reinterpret_cast<const uint4 *>(
+              st + (size_t)j * 2 * kHeadDim + kHeadDim + u * 8);
+          float vv[8];
+          unpack8(raw, vv);
+#pragma unroll
+          for (int h = 0; h < GRP; ++h) {
+            const float lg = s_lg[h][j - sub];
+            const float alpha = lg == -INFINITY ? 0.0f : expf(lg - mloc[h]);
+            dsum[h] += alpha;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[h][k] = __builtin_fmaf(alpha, vv[k], acc[h][k]);
+          }
+        }
+        __syncthreads();
       }
     }
   }
@@ -1461,39 +1579,46 @@ __global__ __launch_bounds__(kBlock) void dk_attn(DParams p) {
     }
   }
   __syncthreads();
+  const int np = p.ncr + p.ncf;
   for (int i = threadIdx.x; i < GRP * kHeadDim; i += kBlock) {
     const int h = i / kHeadDim, e = i % kHeadDim;
     float o = 0.0f;
     for (int w = 0; w < kBlock / kWave; ++w) o += s_o[w][h][e];
-    p.apart[(size_t)row_of(p, b, g, h, GRP) * (p.ncr + p.ncf) + x].o[e] = o;
+    p.apart[(size_t)row_of(p, b, g, h, GRP) * np + x].o[e] = o;
   }
   if (threadIdx.x < GRP) {
     const int h = threadIdx.x;
     float d = 0.0f;
     for (int w = 0; w < kBlock / kWave; ++w) d += s_d[w][h];
-    AttnPart *ap = p.apart + (size_t)row_of(p, b, g, h, GRP) * (p.ncr + p.ncf) + x;
+    AttnPart *ap = p.apart + (size_t)row_of(p, b, g, h, GRP) * np + x;
     ap->d = d;
     ap->m = mloc[h];
   }
   if (!last_block_arrive(&p.groups[bg].arrive[ARR_ATTN], gridDim.x)) return;
-  // ---- merge partial softmax sums by log-sum-exp; write the outputs
-  const int np = p.ncr + p.ncf;
-  for (int h = 0; h < GRP; ++h) {
+  // ---- merge the partial softmax sums by log-sum-exp (one wave per head)
+  for (int h = wave; h < GRP; h += kBlock / kWave) {
     const int row = row_of(p, b, g, h, GRP);
     const AttnPart *ap = p.apart + (size_t)row * np;
     float M = -INFINITY;
-    for (int i = 0; i < np; ++i)
+    for (int i = lane; i < np; i += kWave)
       if (ap[i].d > 0.0f) M = fmaxf(M, ap[i].m);
+    M = wave_max(M);
     float D = 0.0f;
-    for (int i = 0; i < np; ++i)
-      if (ap[i].d > 0.0f) D += ap[i].d * expf(ap[i].m - M);
-    for (int e = threadIdx.x; e < kHeadDim; e += kBlock) {
+    for (int i = lane; i < np; i += kWave) {
+      const float sc = ap[i].d > 0.0f ? expf(ap[i].m - M) : 0.0f;
+      s_scale[wave][i] = sc;
+      D += ap[i].d * sc;
+    }
+    D = wave_sum(D);
+    for (int e = lane; e < kHeadDim; e += kWave) {
       float o = 0.0f;
-      for (int i = 0; i < np; ++i)
-        if (ap[i].d > 0.0f) o += ap[i].o[e] * expf(ap[i].m - M);
+      for (int i = 0; i < np; ++i) {
+        const float sc = s_scale[wave][i];
+        if (sc != 0.0f) o += ap[i].o[e] * sc;
+      }
       p.out[(size_t)row * kHeadDim + e] = o / D;
     }
-    if (threadIdx.x == 0) {
+    if (lane == 0) {
       const RowState &rs = p.rows[row];
       p.d_hat[row] = D;
       p.log_shift[row] = M;
@@ -1501,52 +1626,94 @@ __global__ __launch_bounds__(kBlock) void dk_attn(DParams p) {
       p.eps_hat[row] = rs.fetch ? rs.eps1 : (float)rs.eps0;
       p.k_star[row] = rs.fetch ? rs.kstar : 0;
       if (p.row_stats) {
-        double *st = p.row_stats + (size_t)row * 8;
-        st[0] = rs.m;
-        st[1] = rs.dnorm;
-        st[2] = rs.beta;
-        st[3] = rs.betaL;
-        st[4] = rs.VL;
-        st[5] = rs.b1;
-        st[6] = rs.eps0;
-        st[7] = rs.fetch ? rs.eps1 : rs.eps0;
+        double *sr = p.row_stats + (size_t)row * 8;
+        sr[0] = rs.m;
+        sr[1] = rs.dnorm;
+        sr[2] = rs.beta;
+        sr[3] = rs.betaL;
+        sr[4] = rs.VL;
+        sr[5] = rs.b1;
+        sr[6] = rs.eps0;
+        sr[7] = rs.fetch ? rs.eps1 : rs.eps0;
       }
     }
   }
 }
 
+// Records the timing event after kernel `k` when the caller asked for it.
+struct PhaseMark {
+  void **ev;
+  hipStream_t s;
+  void operator()(int k) const {
+    if (ev) (void)hipEventRecord(static_cast<hipEvent_t>(ev[k]), s);
+  }
+};
+
 template <int GRP>
-hipError_t run(const DParams &p, hipStream_t s, int sd) {
+hipError_t run(const DParams &p, hipStream_t s, int sd, void **events) {
   const dim3 blk(kBlock);
   const dim3 gch((unsigned)p.nch, (unsigned)p.G, (unsigned)p.B);
   const dim3 gres((unsigned)p.ncr, (unsigned)p.G, (unsigned)p.B);
+  const PhaseMark mark{events, s};
+  int k = 0;
+  mark(k++);
   if (p.weights == VKV_W_PERFECT)
     dk_scan_exact<GRP><<<gch, blk, 0, s>>>(p);
   else if (sd == 32)
     dk_scan<GRP, 32><<<gch, blk, 0, s>>>(p);
   else
     dk_scan<GRP, 16><<<gch, blk, 0, s>>>(p);
+  mark(k++);
   dk_resident<GRP><<<gres, blk, 0, s>>>(p);
-  for (int lev = 0; lev < 4; ++lev) dk_beta<GRP><<<gch, blk, 0, s>>>(p, lev);
+  mark(k++);
+  for (int lev = 0; lev < 4; ++lev) {
+    dk_beta<GRP><<<gch, blk, 0, s>>>(p, lev);
+    mark(k++);
+  }
   dk_cert<GRP><<<gch, blk, 0, s>>>(p);
-  for (int pass = 0; pass < 3; ++pass) dk_select<GRP><<<gch, blk, 0, s>>>(p);
+  mark(k++);
+  for (int pass = 0; pass < 3; ++pass) {
+    dk_select<GRP><<<gch, blk, 0, s>>>(p);
+    mark(k++);
+  }
   dk_finish<GRP><<<dim3((unsigned)GRP, (unsigned)p.G, (unsigned)p.B), blk, 0, s>>>(p);
+  mark(k++);
   dk_mark<GRP><<<gch, blk, 0, s>>>(p);
+  mark(k++);
   dk_gather<GRP><<<gch, blk, 0, s>>>(p);
+  mark(k++);
   dk_attn<GRP><<<dim3((unsigned)(p.ncr + p.ncf), (unsigned)p.G, (unsigned)p.B), blk, 0, s>>>(p);
+  mark(k++);
   return hipGetLastError();
 }
 
+const char *const kPhaseNames[] = {
+    "scan", "resident", "beta0", "beta1", "beta2", "beta3", "cert",
+    "select0", "select1", "select2", "finish", "mark", "gather", "attn"};
+
 }  // namespace
+
+int decode_phase_count() {
+  return (int)(sizeof(kPhaseNames) / sizeof(kPhaseNames[0]));
+}
+
+const char *decode_phase_name(int i) {
+  return (i >= 0 && i < decode_phase_count()) ? kPhaseNames[i] : nullptr;
+}
 
 DecodeLayout decode_layout(const vkv_decode_args &a) {
   DecodeLayout L{};
   L.grp = a.n_q_heads / a.n_kv_heads;
-  L.chunk = 1024;
+  L.chunk = 512;
   L.nch = (a.n_tokens + L.chunk - 1) / L.chunk;
+  // workgroups per group for the resident rows and for the fetched rows:
+  // about 2048 workgroups per launch in total, at least 64 rows each
+  const long long groups_ll = (long long)a.batch * a.n_kv_heads;
+  const int target = (int)((2048 + groups_ll - 1) / groups_ll);
   const int rmax = a.cap < a.n_tokens ? a.cap : a.n_tokens;
-  L.ncr = (rmax + L.chunk - 1) / L.chunk;
-  L.ncf = (a.fetch_cap + L.chunk - 1) / L.chunk;
+  // (each at most 256, so the merge sees at most 512 partial sums)
+  L.ncr = std::max(1, std::min(std::min(target, 256), (rmax + 63) / 64));
+  L.ncf = std::max(1, std::min(std::min(target / 2, 256), (a.fetch_cap + 63) / 64));
   L.nwords = (a.n_tokens + 31) / 32;
   const size_t B = (size_t)a.batch, Hq = (size_t)a.n_q_heads,
                G = (size_t)a.n_kv_heads, n = (size_t)a.n_tokens;
@@ -1628,10 +1795,10 @@ hipError_t launch_decode(const vkv_decode_args &a, const DecodeLayout &L,
   p.est = a.estimator;
   p.weights = a.weights;
   switch (L.grp) {
-    case 1: return run<1>(p, s, a.sketch_dim);
-    case 2: return run<2>(p, s, a.sketch_dim);
-    case 4: return run<4>(p, s, a.sketch_dim);
-    case 8: return run<8>(p, s, a.sketch_dim);
+    case 1: return run<1>(p, s, a.sketch_dim, a.phase_events);
+    case 2: return run<2>(p, s, a.sketch_dim, a.phase_events);
+    case 4: return run<4>(p, s, a.sketch_dim, a.phase_events);
+    case 8: return run<8>(p, s, a.sketch_dim, a.phase_events);
     default: return hipErrorInvalidValue;
   }
 }

@@ -59,6 +59,8 @@ struct DecodeLayout {
 };
 
 DecodeLayout decode_layout(const vkv_decode_args &a);
+int decode_phase_count();
+const char *decode_phase_name(int i);
 hipError_t launch_decode(const vkv_decode_args &a, const DecodeLayout &L,
                          const uint16_t *host_kv_dev, hipStream_t s);
 

@@ -31,7 +31,8 @@ W_SKETCH, W_PERFECT = 0, 1
 
 EXPORTS = ("vkv_compress_workspace_bytes", "vkv_decode_workspace_bytes",
            "vkv_compress", "vkv_decode_step", "vkv_check_status",
-           "vkv_last_error", "vkv_version")
+           "vkv_last_error", "vkv_version", "vkv_decode_phase_count",
+           "vkv_decode_phase_name")
 
 _p = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -60,7 +61,7 @@ class DecodeArgs(ctypes.Structure):
                 ("out", _p), ("d_hat", _p), ("log_shift", _p), ("eps_hat0", _p),
                 ("eps_hat", _p), ("k_star", _p), ("fetch_idx", _p),
                 ("fetch_count", _p), ("host_bytes", _p), ("row_stats", _p),
-                ("status", _p), ("workspace", _p),
+                ("status", _p), ("phase_events", _p), ("workspace", _p),
                 ("workspace_bytes", ctypes.c_size_t)]
 
 
@@ -93,6 +94,10 @@ def _load():
     lib.vkv_last_error.restype = ctypes.c_char_p
     lib.vkv_version.argtypes = []
     lib.vkv_version.restype = ctypes.c_int32
+    lib.vkv_decode_phase_count.argtypes = []
+    lib.vkv_decode_phase_count.restype = ctypes.c_int32
+    lib.vkv_decode_phase_name.argtypes = [ctypes.c_int32]
+    lib.vkv_decode_phase_name.restype = ctypes.c_char_p
     return lib
 
 
@@ -128,6 +133,19 @@ def vkv_last_error():
 
 def vkv_version():
     return int(LIB.vkv_version())
+
+
+def vkv_decode_phase_count():
+    return int(LIB.vkv_decode_phase_count())
+
+
+def vkv_decode_phase_name(i):
+    v = LIB.vkv_decode_phase_name(int(i))
+    return None if v is None else v.decode()
+
+
+def decode_phase_names():
+    return [vkv_decode_phase_name(i) for i in range(vkv_decode_phase_count())]
 
 
 def _check(rc):
@@ -269,6 +287,15 @@ class DecodeStep:
         self._keep = (q, resident_kv, resident_idx, resident_count, sketch, proj,
                       r, host_kv)
         return self
+
+    def set_phase_events(self, events):
+        """Attach phase_count()+1 recorded torch.cuda.Event objects (or None)."""
+        if events is None:
+            self._ev = None
+            self.args.phase_events = None
+            return
+        self._ev = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+        self.args.phase_events = ctypes.cast(self._ev, ctypes.c_void_p)
 
     def launch(self, stream=None):
         _check(vkv_decode_step(self.args, _stream(stream)))
