@@ -147,6 +147,8 @@ typedef struct {
  * phase_events  optional timing hook: NULL, or vkv_decode_phase_count() + 1
  *          hipEvent_t handles (created by the caller); event 0 is recorded on
  *          `stream` before the first kernel and event i + 1 after kernel i.
+ *          NULL entries are skipped, so a caller can time one kernel without
+ *          putting a record between every pair of kernels.
  */
 typedef struct {
   int32_t batch, n_q_heads, n_kv_heads, head_dim, n_tokens, sketch_dim, cap;

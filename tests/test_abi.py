@@ -167,7 +167,7 @@ def test_version():
 
 def test_phase_names():
     names = vk.decode_phase_names()
-    assert len(names) == vk.vkv_decode_phase_count() >= 10
+    assert len(names) == vk.vkv_decode_phase_count() >= 5
     assert names[0] == "scan" and names[-1] == "attn"
     assert vk.vkv_decode_phase_name(len(names)) is None
     assert vk.vkv_decode_phase_name(-1) is None

@@ -263,3 +263,26 @@ def test_c2_shape_runs_and_certifies():
             assert hd["suffix"][hd["k_star"] - 1] >= w["eps"]
     for g in range(2):
         assert not set(unions[0][g].tolist()) & set(res_idx[0][g].tolist())
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_fixed_point_single_breakpoint_form(seed):
+    """Because beta* >= max_i w_i(1 - r_i), every token sits on or above its
+    lower clip at the root, so beta* is also the root of
+    sum_i max(0, w_i - beta r_i/(1 - r_i)) - beta, a function with one
+    breakpoint per token (scipy brentq on that form must agree)."""
+    from scipy.optimize import brentq
+    rng = np.random.default_rng(600 + seed)
+    if seed % 2:
+        w, r = _heavy(rng, int(rng.integers(3, 300)))
+    else:
+        w, r = _rand_lr(rng, int(rng.integers(3, 3000)), spread=3.0)
+    beta = od.shrinkage_beta(w, r)
+    rho = r / (1 - r)
+    f = lambda b: float(np.sum(np.maximum(0.0, w - b * rho))) - b  # noqa: E731
+    ref = brentq(f, 0.0, float(np.sum(w)), xtol=1e-300, rtol=1e-15, maxiter=500)
+    assert abs(beta - ref) <= 1e-12 * ref
+    # and the two-breakpoint residual of Definition 2 is never below the
+    # one-breakpoint form
+    for b in np.linspace(0, 2 * beta, 9):
+        assert od.shrink_residual(b, w, r) <= f(b) + 1e-13 * float(np.sum(w))

@@ -3,29 +3,27 @@
 //
 // A "group" is one (request b, KV head g) with its GRP = Hq/G query heads
 // ("rows"). Token passes split the n positions into chunks of `chunk` tokens,
-// one workgroup per (chunk, g, b); every row-level decision is taken by the
-// last workgroup of the group to finish a pass ("last block done"), so a
-// launch never waits on another workgroup.
+// one workgroup per (chunk, g, b); where a pass ends in a row-level decision
+// it is taken by the last workgroup of the group to finish ("last block
+// done"), so a launch never waits on another workgroup. The planning steps
+// run one workgroup per row and need no cross-workgroup step at all.
 //
 //  dk_scan      sketch logits s_i = <P_g^T q, sk_i>/sqrt(d) for every token and
 //               the GRP heads at once (one sketch row serves all of them).
 //  dk_resident  exact logits l_j = <q, k_j>/sqrt(d) on the resident rows,
 //               residency bitmap, common shift m = max(max_R l, max_L s).
-//  dk_beta x4   Definition 2 fixed point beta = sum_L w~(1 - lambda(beta)):
-//               h(beta) is piecewise linear with breakpoints w~(1-r) and
-//               w~(1-r)/r; four radix levels over the fp32 bit patterns of the
-//               breakpoints (8+8+8+7 bits) bracket the root between adjacent
-//               floats, where h is linear and the root is solved exactly.
-//               Level 0 also forms D~ = sum_H w + sum_L w~.
-//  dk_cert      lambda_i, beta(L), V(L), top-2 of b_i -> eps^(L) (eq. 7).
-//  dk_select x3 radix select driven by the stopping rule (eq. 10): keys are
-//               (gain bits, inverted position) so descending key order is
-//               L_g; per-bin counts and fixed-point sums of beta_i and v_i let
-//               the last block find the bin where eps^(L_g[k:]) first drops
-//               below eps without sorting L. Small bins are collected.
-//  dk_finish    sorts the collected bin in LDS and walks it to the exact k*.
-//  dk_mark      fetch set of the KV head = union over its heads of
-//               {key >= threshold} minus the resident rows (bitmap + counts).
+//  dk_plan_a    per row: D~ = sum_H w + sum_L w~; the Definition 2 fixed point
+//               beta* by four radix levels over the fp32 bit patterns of the
+//               breakpoints of a piecewise-linear h(beta), then an exact linear
+//               solve between adjacent floats; lambda_i, beta(L), V(L), top-2
+//               of b_i -> eps^(L) (Lemma 1, eq. 7).
+//  dk_plan_b    per row that fails the certificate: radix select driven by
+//               the stopping rule (eq. 10) over keys (gain bits, inverted
+//               position), whose descending order is L_g; per-bin counts and
+//               fixed-point sums of beta_i and v_i find the bin where
+//               eps^(L_g[k:]) first drops below eps without sorting L; the
+//               last bin is rank-sorted in LDS and walked to the exact k*.
+//               Then F_h minus S is ORed into the KV head's fetch bitmap.
 //  dk_gather    ascending fetch list; rows copied from pinned host memory by
 //               GPU loads (zero-copy) into device staging.
 //  dk_attn      weights w on H u F_h, lambda w / r on S \ F_h, exact logits of
@@ -43,39 +41,24 @@
 namespace vkv {
 namespace {
 
-constexpr int kCand = 2048;      // candidates the finisher sorts in LDS
-constexpr int kBetaEdges = 257;  // difference arrays per radix level
-constexpr int kSelBins = 256;
+constexpr int kChunk = 512;      // tokens per workgroup in token passes
+constexpr int kCand = 2048;      // candidates per round of the streaming selection
 constexpr float kInvSqrtD = 0.08838834764831845f;  // 1/sqrt(128)
-
-enum { MODE_HIST = 0, MODE_COLLECT = 1, MODE_COLLECTED = 2, MODE_DONE = 3 };
 
 struct RowState {
   float m;                // common shift of the planning and resident logits
-  int32_t bdone;          // beta* known
-  uint32_t bpre;          // bit pattern of the beta bracket's lower edge
   int32_t fetch;          // eps^(L) >= eps
   double dnorm;           // D~ * exp(-m)
   double beta;            // beta*
   double betaL, VL;       // beta(L), V(L) (float64 sums of fp32 terms)
   double s_full;          // sqrt((a b)^2 + 2 V l)
+  float s_full_f;         // the same in fp32 (the gain formula's s)
   double eps0;            // eps^(L)
   float b1, b2;           // largest and second largest b_i (with multiplicity)
   int32_t amax;           // position of the unique argmax of b_i, else -1
   int32_t eb, ev;         // fixed-point exponents for beta_i and v_i
-  int32_t mode;           // selection state (MODE_*)
-  int32_t level;          // next radix digit (MODE_HIST)
-  int32_t shift;          // tokens match when (key >> shift) == pre
-  uint32_t bin_cnt;       // tokens in the crossing bin
-  uint32_t ncand;         // candidates collected
-  uint32_t cntA;          // tokens fetched above the current bracket
-  uint32_t bB;            // max b_i (float bits) below the current bracket
   int32_t kstar;
-  unsigned long long pre;
-  unsigned long long bL_fx, VL_fx;   // fixed-point totals over L
-  unsigned long long betaA, VA;      // fixed-point sums fetched above
-  unsigned long long T;              // member iff (key >> T_shift) >= T
-  int32_t T_shift;
+  unsigned long long T;   // F_h = {i in L : key_i >= T}
   float eps1;             // eps^(L') after fetching
 };
 
@@ -83,29 +66,29 @@ struct GroupState {
   uint32_t arrive[8];
 };
 
+// State of a row's beta* iteration between launches.
+struct BetaState {
+  double lo, hi;        // bracket of the root
+  double prev_cnt;      // |A| whose Newton step gave lo (-1: none)
+  double beta;          // beta* once done
+  double dnorm;         // D~ * exp(-m)
+  int32_t done, pad;
+};
+
+// Certificate terms of one chunk of a row.
 struct CertPart {
-  double beta, var;
-  float b1, b2;
-  int32_t p1, pad;
+  double tb, tv;        // sums of beta_i and v_i
+  float x1, x2;         // largest and second largest b_i
+  int32_t p1, pad;      // position of x1 (smallest on ties)
 };
 
-struct SelBin {
-  uint32_t cnt, bmax;
-  unsigned long long bsum, vsum;
+// Candidate bound of a row and its fixed-point totals over L.
+struct SelState {
+  unsigned long long lo_key, tot_b, tot_v;
+  uint32_t take, pad;   // keys >= lo_key
 };
 
-struct Cand {
-  unsigned long long key, bfx, vfx;
-  uint32_t rb, pad;
-};
-
-struct AttnPart {
-  float m, d;
-  float o[kHeadDim];
-  float pad[2];
-};
-
-enum { ARR_RES = 0, ARR_BETA = 1, ARR_CERT = 2, ARR_SEL = 3, ARR_ATTN = 4 };
+enum { ARR_RES = 0, ARR_ATTN = 1 };
 
 struct DParams {
   const uint16_t *q, *rkv, *sketch, *host_kv;
@@ -122,15 +105,21 @@ struct DParams {
   uint32_t *hpart;
   RowState *rows;
   GroupState *groups;
-  double *bbins;
-  double2 *dpart;
-  CertPart *cpart;
-  SelBin *sbins;
-  Cand *cand;
-  uint32_t *fcnt;
-  AttnPart *apart;
+  double *bpart;     // [2][row][nrc][kBetaRec] beta pass records
+  BetaState *bstate; // [2][row]
+  double *rbeta;     // [row][2] beta*, D~
+  CertPart *cpart;   // [row][nrc]
+  uint32_t *khist;   // [row][nrc][2048] key histograms
+  unsigned long long *tpart;  // [row][nrc][2] fixed-point totals
+  SelState *sel;     // [row]
+  uint32_t *ccount;  // [row] candidates collected
+  unsigned long long *candk, *candb, *candv;  // [row][kCandMax]
+  uint32_t *candr;   // [row][kCandMax]
+  uint32_t *rpart;   // [row][nrc] max b_i below the candidate bound
+  float2 *apart;     // [row][ncr + ncf] (shift, sum of weights)
+  float *aparto;     // [row][d][npad] weighted sums of V, part index fastest
   uint16_t *staging;
-  int B, Hq, G, n, cap, fetch_cap, nch, ncr, ncf, nwords, chunk;
+  int B, Hq, G, n, cap, fetch_cap, nch, ncr, ncf, npad, nwords, chunk, nrc;
   float eps;
   double l_delta, a_delta;
   int est, weights;
@@ -141,23 +130,29 @@ struct Terms {
   float wt, lam, bi, vi, rb;
 };
 
-// Planning weight w~ = exp(s - m), lambda (Definition 2) and the three
-// certificate terms of Lemma 1 for one token of L.
-__device__ __forceinline__ Terms token_terms(float s, float r, float m,
-                                             float beta, int est) {
+// lambda (Definition 2) and the three certificate terms of Lemma 1 for one
+// token of L with planning weight wt.
+__device__ __forceinline__ Terms token_terms_w(float wt, float r, float beta,
+                                               int est) {
   Terms t;
-  t.wt = expf(s - m);
+  t.wt = wt;
   float lam = 1.0f;
-  if (est == VKV_EST_CLIP && t.wt > 0.0f) {
-    const float x = beta * r / (t.wt * (1.0f - r));
+  if (est == VKV_EST_CLIP && wt > 0.0f) {
+    const float x = beta * r / (wt * (1.0f - r));
     lam = fminf(1.0f, fmaxf(r, x));
   }
   t.lam = lam;
-  t.bi = t.wt * (1.0f - lam);
-  const float lw = lam * t.wt;
+  t.bi = wt * (1.0f - lam);
+  const float lw = lam * wt;
   t.vi = lw * lw * (1.0f - r) / r;
   t.rb = lw * fmaxf(r, 1.0f - r) / r;
   return t;
+}
+
+// The same from the planning logit s and the shift m (w~ = exp(s - m)).
+__device__ __forceinline__ Terms token_terms(float s, float r, float m,
+                                             float beta, int est) {
+  return token_terms_w(expf(s - m), r, beta, est);
 }
 
 // eq. 7 in float64.
@@ -167,19 +162,23 @@ __device__ __forceinline__ double eps_of(double beta, double var, double b,
   return (beta + ab + sqrt(ab * ab + 2.0 * var * l)) / dn;
 }
 
-// Gain g_i * D~ (eq. 9, cancellation-free form), rounded to float for the key.
+// Gain g_i * D~ (eq. 9, cancellation-free form). With b' the largest b after
+// removing token i (b itself unless i is the unique argmax),
+//   s  = sqrt((a b)^2 + 2 V l),  s' = sqrt((a b')^2 + 2 (V - v_i) l),
+//   g_i D~ = beta_i + a (b - b') + [a^2 (b - b')(b + b') + 2 v_i l] / (s + s').
+// V - v_i is formed in float64 (it cancels when one token dominates V); the
+// rest is fp32, which only perturbs the order of gains equal to ~1e-7.
 __device__ __forceinline__ float token_gain(const Terms &t, int pos,
-                                            const RowState &rs, double a,
-                                            double l) {
-  const double b1 = rs.b1;
-  const double bp = (pos == rs.amax) ? (double)rs.b2 : b1;
-  const double vi = t.vi;
-  const double vp = fmax(rs.VL - vi, 0.0);
-  const double sp = sqrt(a * a * bp * bp + 2.0 * vp * l);
-  const double num = a * a * (b1 - bp) * (b1 + bp) + 2.0 * vi * l;
-  const double den = rs.s_full + sp;
-  const double frac = den > 0.0 ? num / den : 0.0;
-  return (float)((double)t.bi + a * (b1 - bp) + frac);
+                                            const RowState &rs, float a,
+                                            float l) {
+  const float b1 = rs.b1;
+  const float bp = (pos == rs.amax) ? rs.b2 : b1;
+  const float vp = (float)fmax(rs.VL - (double)t.vi, 0.0);
+  const float sp = sqrtf(a * a * bp * bp + 2.0f * vp * l);
+  const float num = a * a * (b1 - bp) * (b1 + bp) + 2.0f * t.vi * l;
+  const float den = rs.s_full_f + sp;
+  const float frac = den > 0.0f ? num / den : 0.0f;
+  return t.bi + a * (b1 - bp) + frac;
 }
 
 // Descending key order = gain descending, then position ascending.
@@ -194,11 +193,8 @@ __device__ __forceinline__ unsigned long long to_fx(float x, int e) {
 
 __device__ __forceinline__ bool is_member(unsigned long long key,
                                           const RowState &rs) {
-  return (key >> rs.T_shift) >= rs.T;
+  return key >= rs.T;
 }
-
-__device__ __forceinline__ int sel_off(int d) { return d < 6 ? 47 - 8 * d : 0; }
-__device__ __forceinline__ int sel_width(int d) { return d < 6 ? 8 : 7; }
 
 __device__ __forceinline__ int row_of(const DParams &p, int b, int g, int h,
                                       int grp) {
@@ -251,16 +247,10 @@ __global__ __launch_bounds__(kBlock) void dk_scan(DParams p) {
     if (threadIdx.x < 8) p.groups[bg].arrive[threadIdx.x] = 0u;
     for (int h = 0; h < GRP; ++h) {
       const int row = row_of(p, b, g, h, GRP);
-      double *bb = p.bbins + (size_t)row * 3 * kBetaEdges;
-      for (int i = threadIdx.x; i < 3 * kBetaEdges; i += kBlock) bb[i] = 0.0;
-      SelBin *sb = p.sbins + (size_t)row * kSelBins;
-      for (int i = threadIdx.x; i < kSelBins; i += kBlock)
-        sb[i] = SelBin{0u, 0u, 0ull, 0ull};
       if (threadIdx.x == 0) {
         RowState z{};
         z.amax = -1;
         z.T = ~0ull;
-        z.mode = MODE_DONE;
         p.rows[row] = z;
       }
     }
@@ -380,16 +370,10 @@ __global__ __launch_bounds__(kBlock) void dk_scan_exact(DParams p) {
     if (threadIdx.x < 8) p.groups[bg].arrive[threadIdx.x] = 0u;
     for (int h = 0; h < GRP; ++h) {
       const int row = row_of(p, b, g, h, GRP);
-      double *bb = p.bbins + (size_t)row * 3 * kBetaEdges;
-      for (int i = threadIdx.x; i < 3 * kBetaEdges; i += kBlock) bb[i] = 0.0;
-      SelBin *sb = p.sbins + (size_t)row * kSelBins;
-      for (int i = threadIdx.x; i < kSelBins; i += kBlock)
-        sb[i] = SelBin{0u, 0u, 0ull, 0ull};
       if (threadIdx.x == 0) {
         RowState z{};
         z.amax = -1;
         z.T = ~0ull;
-        z.mode = MODE_DONE;
         p.rows[row] = z;
       }
     }
@@ -551,211 +535,61 @@ __global__ __launch_bounds__(kBlock) void dk_resident(DParams p) {
   }
 }
 
-// ------------------------------------------------------------ dk_beta
-// Radix level `lev` of the beta* search (digit widths 8, 8, 8, 7 over the
-// float bit pattern; level 0 digits are the exponent field).
-template <int GRP>
-__global__ __launch_bounds__(kBlock) void dk_beta(DParams p, int lev) {
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int bg = b * p.G + g;
-  const int shift = lev == 0 ? 23 : (lev == 1 ? 15 : (lev == 2 ? 7 : 0));
-  const int nb = lev == 3 ? 128 : 256;
-  __shared__ double s_bins[GRP][3][kBetaEdges];
-  __shared__ double s_dred[kBlock / kWave];
-  __shared__ float s_m[GRP];
-  __shared__ uint32_t s_pa[GRP];
-  __shared__ int s_active[GRP];
-  if (threadIdx.x < GRP) {
-    const RowState &rs = p.rows[row_of(p, b, g, threadIdx.x, GRP)];
-    s_m[threadIdx.x] = rs.m;
-    s_pa[threadIdx.x] = rs.bpre;
-    s_active[threadIdx.x] = (p.est == VKV_EST_CLIP) && !rs.bdone;
-  }
-  __syncthreads();
-  bool any = lev == 0;
-  for (int h = 0; h < GRP; ++h) any |= s_active[h] != 0;
-  if (!any) return;
-  for (int i = threadIdx.x; i < GRP * 3 * kBetaEdges; i += kBlock)
-    (&s_bins[0][0][0])[i] = 0.0;
-  __syncthreads();
-  double baseC[GRP], baseW[GRP], baseR[GRP], sumL[GRP];
-#pragma unroll
-  for (int h = 0; h < GRP; ++h) baseC[h] = baseW[h] = baseR[h] = sumL[h] = 0.0;
-  const float *rr = p.r + (size_t)bg * p.n;
-  const int base = c * p.chunk;
-  const int lim = min(base + p.chunk, p.n);
-  for (int i = base + threadIdx.x; i < lim; i += kBlock) {
-    const float ri = rr[i];
-    if (!(ri < 1.0f)) continue;
-#pragma unroll
-    for (int h = 0; h < GRP; ++h) {
-      const int row = row_of(p, b, g, h, GRP);
-      const float wt = expf(p.shat[(size_t)row * p.n + i] - s_m[h]);
-      if (lev == 0) sumL[h] += (double)wt;
-      if (!s_active[h] || !(wt > 0.0f)) continue;
-      const float lo = wt * (1.0f - ri);
-      const float hi = lo / ri;
-      const float rho = ri / (1.0f - ri);
-      const uint32_t pa = s_pa[h];
-      const uint32_t pb = pa + ((uint32_t)nb << shift);
-      const uint32_t lb = __float_as_uint(lo), hb = __float_as_uint(hi);
-      const int pl = lb < pa ? -1 : (lb >= pb ? nb : (int)((lb - pa) >> shift));
-      const int ph = hb < pa ? -1 : (hb >= pb ? nb : (int)((hb - pa) >> shift));
-      // constant lo_i on edges [0, pl]
-      if (pl >= 0) {
-        baseC[h] += (double)lo;
-        if (pl < nb) unsafeAtomicAdd(&s_bins[h][0][pl + 1], -(double)lo);
-      }
-      // linear w~ - e rho on edges [pl + 1, ph]
-      if (pl + 1 <= ph) {
-        if (pl + 1 == 0) {
-          baseW[h] += (double)wt;
-          baseR[h] += (double)rho;
-        } else {
-          unsafeAtomicAdd(&s_bins[h][1][pl + 1], (double)wt);
-          unsafeAtomicAdd(&s_bins[h][2][pl + 1], (double)rho);
-        }
-        if (ph < nb) {
-          unsafeAtomicAdd(&s_bins[h][1][ph + 1], -(double)wt);
-          unsafeAtomicAdd(&s_bins[h][2][ph + 1], -(double)rho);
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int h = 0; h < GRP; ++h) {
-    const double bc = block_sum<double>(baseC[h], s_dred);
-    const double bw = block_sum<double>(baseW[h], s_dred);
-    const double br = block_sum<double>(baseR[h], s_dred);
-    if (threadIdx.x == 0) {
-      s_bins[h][0][0] += bc;
-      s_bins[h][1][0] += bw;
-      s_bins[h][2][0] += br;
-    }
-  }
-  // level 0: per-chunk parts of D~ (L from the sketch, H from resident rows)
-  if (lev == 0) {
-    const int cnt = max(0, min(p.rcount[bg], p.cap));
-    const int32_t *ridx = p.ridx + (size_t)bg * p.cap;
-    int jlo, jhi;
-    split_range(cnt, gridDim.x, c, jlo, jhi);
-#pragma unroll
-    for (int h = 0; h < GRP; ++h) {
-      const int row = row_of(p, b, g, h, GRP);
-      double sh = 0.0;
-      for (int j = jlo + threadIdx.x; j < jhi; j += kBlock) {
-        const int pos = ridx[j];
-        if (pos >= 0 && pos < p.n && rr[pos] >= 1.0f)
-          sh += (double)expf(p.ell[(size_t)row * p.cap + j] - s_m[h]);
-      }
-      const double tsh = block_sum<double>(sh, s_dred);
-      const double tsl = block_sum<double>(sumL[h], s_dred);
-      if (threadIdx.x == 0) p.dpart[(size_t)row * p.nch + c] = make_double2(tsl, tsh);
-    }
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < GRP * 3 * kBetaEdges; i += kBlock) {
-    const double v = (&s_bins[0][0][0])[i];
-    if (v != 0.0) {
-      const int h = i / (3 * kBetaEdges), rest = i % (3 * kBetaEdges);
-      unsafeAtomicAdd(p.bbins + (size_t)row_of(p, b, g, h, GRP) * 3 * kBetaEdges +
-                          rest,
-                      v);
-    }
-  }
-  if (!last_block_arrive(&p.groups[bg].arrive[ARR_BETA], gridDim.x)) return;
-  // ---- last block: one wave per head scans the edges of the bracket.
-  // h(e_j) = C(j) + W(j) - e_j (1 + R(j)) with C, W, R the prefix sums of the
-  // difference arrays; h decreases, so the root lies after the last edge
-  // with h > 0.
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  constexpr int PER = 5;  // 64 lanes x 5 >= 257 edges
-  for (int h = wave; h < GRP; h += kBlock / kWave) {
-    const int row = row_of(p, b, g, h, GRP);
-    RowState &rs = p.rows[row];
-    double *gb = p.bbins + (size_t)row * 3 * kBetaEdges;
-    if (lev == 0) {
-      double dl = 0.0, dh = 0.0;
-      for (int i = lane; i < p.nch; i += kWave) {
-        const double2 v = p.dpart[(size_t)row * p.nch + i];
-        dl += v.x;
-        dh += v.y;
-      }
-      dl = wave_sum(dl);
-      dh = wave_sum(dh);
-      if (lane == 0) {
-        rs.dnorm = dh + dl;
-        if (p.est != VKV_EST_CLIP) {
-          rs.bdone = 1;
-          rs.beta = 0.0;
-        }
-      }
-    }
-    if (s_active[h]) {
-      const uint32_t pa = s_pa[h];
-      const int nedge = lev == 0 ? 255 : nb + 1;  // level 0 stops before +inf
-      double C[PER], W[PER], R[PER];
-      double tc = 0.0, tw = 0.0, tr = 0.0;
-#pragma unroll
-      for (int k = 0; k < PER; ++k) {
-        const int j = lane * PER + k;
-        const bool in = j < nedge;
-        tc += in ? gb[j] : 0.0;
-        tw += in ? gb[kBetaEdges + j] : 0.0;
-        tr += in ? gb[2 * kBetaEdges + j] : 0.0;
-        C[k] = tc;
-        W[k] = tw;
-        R[k] = tr;
-      }
-      const double oc = wave_incl_scan(tc, lane) - tc;
-      const double ow = wave_incl_scan(tw, lane) - tw;
-      const double orr = wave_incl_scan(tr, lane) - tr;
-      double Hv[PER];
-      int best = -1;
-#pragma unroll
-      for (int k = 0; k < PER; ++k) {
-        const int j = lane * PER + k;
-        const double e = (double)__uint_as_float(pa + ((uint32_t)j << shift));
-        Hv[k] = (oc + C[k]) + (ow + W[k]) - e * (1.0 + (orr + R[k]));
-        if (j < nedge && j < nb && Hv[k] > 0.0) best = j;
-      }
-      int root = best;
-      for (int m = 32; m >= 1; m >>= 1) root = max(root, __shfl_xor(root, m, kWave));
-      // values at the root edge and the next one
-      double h0 = 0.0, h1 = 0.0;
-      const int r0 = max(root, 0), r1 = r0 + 1;
-#pragma unroll
-      for (int k = 0; k < PER; ++k) {
-        if (lane * PER + k == r0) h0 = Hv[k];
-        if (lane * PER + k == r1) h1 = Hv[k];
-      }
-      h0 = __shfl(h0, r0 / PER, kWave);
-      h1 = __shfl(h1, min(r1 / PER, kWave - 1), kWave);
-      if (lane == 0) {
-        if (root < 0 && lev == 0) {  // no weight in L
-          rs.beta = 0.0;
-          rs.bdone = 1;
-        } else {
-          const uint32_t pj = pa + ((uint32_t)r0 << shift);
-          if (lev < 3) {
-            rs.bpre = pj;
-          } else {
-            const double e0 = (double)__uint_as_float(pj);
-            const double e1 = (double)__uint_as_float(pj + 1u);
-            const double d = h0 - h1;
-            double bt = d > 0.0 ? e0 + h0 * (e1 - e0) / d : e0;
-            bt = fmin(fmax(bt, e0), e1);
-            rs.beta = bt;
-            rs.bdone = 1;
-          }
-        }
-      }
-    }
-    for (int i = lane; i < 3 * kBetaEdges; i += kWave) gb[i] = 0.0;
-  }
+// ------------------------------------------------------------ planning
+// The plan of Algorithm 2 for every (request, query head) ("row"):
+//   D~ -> beta* -> certificate (Lemma 1, eq. 7) -> k* (eq. 10) -> F_h.
+// Data-parallel passes over a row's tokens run as launches of kBlock-thread
+// workgroups, one per chunk of kRowChunk tokens of a row; each writes a
+// partial record, and every workgroup of the next launch combines the
+// records of its row itself (in one fixed order, so all of them get
+// bit-identical results). No workgroup ever waits for another.
+//
+// beta*: at the root, beta* >= max_i w~_i (1 - r_i) (below that the heaviest
+// token alone would give more than beta), so every token is at or above its
+// lower clip and the Definition 2 fixed point is also the unique root of
+//     h(beta) = sum_i max(0, w~_i - beta rho_i) - beta,  rho_i = r_i/(1-r_i),
+// a convex, decreasing, piecewise-linear function. Pass 0 gives the sums at
+// beta = 0 and the lower bound above; each later pass evaluates, at
+// kBetaPts points of the bracket [lo, hi], the sums of w~ and rho over the
+// active set A(beta) = {w~_i > beta rho_i} and its size. The Newton step
+// from a point with h >= 0, beta' = sum_A w~ / (1 + sum_A rho), never
+// overshoots the root (convexity); it is the root itself when no breakpoint
+// lies between the point and the next evaluated point (equal active counts)
+// or when the next pass finds the same active set at beta'. Since h' <= -1,
+// beta + h(beta) bounds the root from above. A row still open after the
+// last Newton launch finishes in the certificate launch, where each of its
+// workgroups iterates over the whole row (rare; same arithmetic).
+//
+// Selection: keys (gain bits, inverted position) order L as L_g
+// (descending). A count histogram of the top 11 key bits gives a key bound
+// lo with at most kCandMax keys in [lo, inf); those candidates are collected
+// with their fixed-point beta_i and v_i and their range term b_i, and one
+// workgroup per row sorts them and walks the stopping rule to the exact k*.
+// If fetching every candidate still leaves eps^ >= eps, that workgroup runs
+// the streaming selection below instead. All sums of the selection are
+// fixed-point integers, so a rest's sum is the total minus the fetched part
+// exactly.
+constexpr int kPlanThreads = 1024;  // row-level workgroups
+constexpr int kPlanWaves = kPlanThreads / kWave;
+constexpr int kSelUnroll = 4;       // streamed tokens per thread in flight
+constexpr int kRowChunk = 2048;     // tokens per workgroup in row passes
+constexpr int kRowTok = kRowChunk / kBlock;
+constexpr int kBetaPts = 4;         // points of h per Newton pass
+constexpr int kBetaRec = 3 * kBetaPts;
+constexpr int kBetaLaunches = 5;    // pass 0 and four Newton passes
+constexpr int kBetaPassMax = 96;    // never reached: the bracket shrinks >= 2x
+constexpr int kCandMax = 4096;      // candidates sorted by the walk
+constexpr int kSelDigit = 11;
+constexpr int kSelBinsP = 1 << kSelDigit;
+constexpr int kSelLevels = 5;       // five 11-bit digits cover the 55-bit key
+constexpr unsigned long long kKeyEnd = 1ull << 55;  // above every key
+__device__ __forceinline__ int sel_off(int d) { return 44 - kSelDigit * d; }
+
+// rho = r / (1 - r); the same expression in every pass.
+__device__ __forceinline__ float plan_rho(float r) {
+  return r * __builtin_amdgcn_rcpf(1.0f - r);
 }
 
-// ------------------------------------------------------------ dk_cert
 __device__ __forceinline__ void top2_merge(float &x1, int &p1, float &x2,
                                            float y1, int q1, float y2) {
   if (y1 > x1 || (y1 == x1 && q1 < p1)) {
@@ -767,583 +601,1124 @@ __device__ __forceinline__ void top2_merge(float &x1, int &p1, float &x2,
   }
 }
 
-template <int GRP>
-__global__ __launch_bounds__(kBlock) void dk_cert(DParams p) {
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int bg = b * p.G + g;
-  __shared__ double s_dred[kBlock / kWave];
-  __shared__ float s_w1[kBlock / kWave], s_w2[kBlock / kWave];
-  __shared__ int s_wp[kBlock / kWave];
-  __shared__ float s_m[GRP], s_beta[GRP];
-  if (threadIdx.x < GRP) {
-    const RowState &rs = p.rows[row_of(p, b, g, threadIdx.x, GRP)];
-    s_m[threadIdx.x] = rs.m;
-    s_beta[threadIdx.x] = (float)rs.beta;
-  }
-  __syncthreads();
-  double sb[GRP], sv[GRP];
-  float x1[GRP], x2[GRP];
-  int p1[GRP];
-#pragma unroll
-  for (int h = 0; h < GRP; ++h) {
-    sb[h] = sv[h] = 0.0;
-    x1[h] = x2[h] = 0.0f;
-    p1[h] = 0x7fffffff;
-  }
-  const float *rr = p.r + (size_t)bg * p.n;
-  const int base = c * p.chunk;
-  const int lim = min(base + p.chunk, p.n);
-  for (int i = base + threadIdx.x; i < lim; i += kBlock) {
-    const float ri = rr[i];
-    if (!(ri < 1.0f)) continue;
-#pragma unroll
-    for (int h = 0; h < GRP; ++h) {
-      const int row = row_of(p, b, g, h, GRP);
-      const Terms t =
-          token_terms(p.shat[(size_t)row * p.n + i], ri, s_m[h], s_beta[h], p.est);
-      sb[h] += (double)t.bi;
-      sv[h] += (double)t.vi;
-      top2_merge(x1[h], p1[h], x2[h], t.rb, i, 0.0f);
-    }
-  }
+// Block-wide sums of NV values for THREADS threads in a fixed order; every
+// thread gets the totals. `red` holds (THREADS / 64 + 1) * NV entries.
+template <typename T, int NV, int THREADS>
+__device__ __forceinline__ void blk_reduce(T (&v)[NV], T *red) {
+  constexpr int W = THREADS / kWave;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
 #pragma unroll
-  for (int h = 0; h < GRP; ++h) {
-    const double tb = block_sum<double>(sb[h], s_dred);
-    const double tv = block_sum<double>(sv[h], s_dred);
-    float a1 = x1[h], a2 = x2[h];
-    int q1 = p1[h];
-    for (int m = 32; m >= 1; m >>= 1) {
-      const float o1 = shfl_xor(a1, m), o2 = shfl_xor(a2, m);
-      const int oq = shfl_xor(q1, m);
-      top2_merge(a1, q1, a2, o1, oq, o2);
-    }
-    __syncthreads();
-    if (lane == 0) {
-      s_w1[wave] = a1;
-      s_w2[wave] = a2;
-      s_wp[wave] = q1;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      float y1 = s_w1[0], y2 = s_w2[0];
-      int yq = s_wp[0];
-      for (int w = 1; w < kBlock / kWave; ++w) top2_merge(y1, yq, y2, s_w1[w], s_wp[w], s_w2[w]);
-      CertPart cp;
-      cp.beta = tb;
-      cp.var = tv;
-      cp.b1 = y1;
-      cp.b2 = y2;
-      cp.p1 = yq;
-      cp.pad = 0;
-      p.cpart[(size_t)row_of(p, b, g, h, GRP) * p.nch + c] = cp;
-    }
-  }
-  if (!last_block_arrive(&p.groups[bg].arrive[ARR_CERT], gridDim.x)) return;
-  for (int h = wave; h < GRP; h += kBlock / kWave) {
-    const int row = row_of(p, b, g, h, GRP);
-    RowState &rs = p.rows[row];
-    double tb = 0.0, tv = 0.0;
-    float y1 = 0.0f, y2 = 0.0f;
-    int yq = 0x7fffffff;
-    for (int i = lane; i < p.nch; i += kWave) {
-      const CertPart cp = p.cpart[(size_t)row * p.nch + i];
-      tb += cp.beta;
-      tv += cp.var;
-      top2_merge(y1, yq, y2, cp.b1, cp.p1, cp.b2);
-    }
-    tb = wave_sum(tb);
-    tv = wave_sum(tv);
-    for (int m = 32; m >= 1; m >>= 1) {
-      const float o1 = shfl_xor(y1, m), o2 = shfl_xor(y2, m);
-      const int oq = shfl_xor(yq, m);
-      top2_merge(y1, yq, y2, o1, oq, o2);
-    }
-    if (lane != 0) continue;
-    const double a = p.a_delta, l = p.l_delta;
-    rs.betaL = tb;
-    rs.VL = tv;
-    rs.b1 = y1;
-    rs.b2 = y2;
-    rs.amax = (y2 < y1) ? yq : -1;
-    rs.s_full = sqrt(a * a * (double)y1 * (double)y1 + 2.0 * tv * l);
-    const double e0 = ((double)tb + a * (double)y1 + rs.s_full) / rs.dnorm;
-    rs.eps0 = e0;
-    if (e0 < (double)p.eps) {
-      rs.fetch = 0;
-      rs.kstar = 0;
-      rs.eps1 = (float)e0;
-      rs.mode = MODE_DONE;
-      rs.T = ~0ull;
-      rs.T_shift = 0;
-    } else {
-      rs.fetch = 1;
-      int eb = 0, ev = 0;
-      if (tb > 0.0) { (void)frexp(tb, &eb); eb = 61 - eb; } else { eb = 0; }
-      if (tv > 0.0) { (void)frexp(tv, &ev); ev = 61 - ev; } else { ev = 0; }
-      rs.eb = eb;
-      rs.ev = ev;
-      rs.mode = MODE_HIST;
-      rs.level = 0;
-      rs.shift = 55;
-      rs.pre = 0ull;
-      rs.cntA = 0u;
-      rs.betaA = 0ull;
-      rs.VA = 0ull;
-      rs.bB = 0u;
-      rs.bL_fx = 0ull;
-      rs.VL_fx = 0ull;
-      rs.ncand = 0u;
-      rs.T = ~0ull;
-      rs.T_shift = 0;
-    }
-  }
-}
-
-// ------------------------------------------------------------ selection
-// Resolve one radix level for one row with a single wave. `bins` holds the
-// 2^width bins of digit `d`; updates the row state.
-__device__ void sel_resolve(RowState &rs, const SelBin *bins, int d,
-                            const DParams &p, int lane) {
-  const int w = sel_width(d), off = sel_off(d);
-  const int nbins = 1 << w;
-  const int per = nbins / kWave;  // 4 or 2
-  const double a = p.a_delta, l = p.l_delta;
-  const double sb = ldexp(1.0, -rs.eb), sv = ldexp(1.0, -rs.ev);
-  // lane-local bins x = lane * per + k
-  uint32_t cnt[4];
-  unsigned long long bs[4], vs[4];
-  uint32_t bm[4];
-  uint32_t lc = 0, lmax = 0;
-  unsigned long long lb = 0, lv = 0;
-  for (int k = 0; k < per; ++k) {
-    const SelBin sbn = bins[lane * per + k];
-    cnt[k] = sbn.cnt;
-    bs[k] = sbn.bsum;
-    vs[k] = sbn.vsum;
-    bm[k] = sbn.bmax;
-    lc += cnt[k];
-    lb += bs[k];
-    lv += vs[k];
-    lmax = max(lmax, bm[k]);
-  }
-  // sums over the lanes above (higher bins) and max over the lanes below
-  const uint32_t ic = wave_incl_scan<uint32_t>(lc, lane);
-  const unsigned long long ib = wave_incl_scan<unsigned long long>(lb, lane);
-  const unsigned long long iv = wave_incl_scan<unsigned long long>(lv, lane);
-  const uint32_t ac = __shfl(ic, kWave - 1, kWave) - ic;
-  const unsigned long long ab = __shfl(ib, kWave - 1, kWave) - ib;
-  const unsigned long long av = __shfl(iv, kWave - 1, kWave) - iv;
-  uint32_t bmax_below = __shfl_up(wave_incl_max(lmax, lane), 1, kWave);
-  if (lane == 0) bmax_below = 0u;
-  // evaluate eps^(tail_x) for each local bin, top to bottom
-  int best = -1;
-  {
-    uint32_t c_ge = ac;
-    unsigned long long b_ge = ab, v_ge = av;
-    for (int k = per - 1; k >= 0; --k) {
-      c_ge += cnt[k];
-      b_ge += bs[k];
-      v_ge += vs[k];
-      uint32_t bt = max(rs.bB, bmax_below);
-      for (int k2 = 0; k2 < k; ++k2) bt = max(bt, bm[k2]);
-      const double tb = (double)(rs.bL_fx - rs.betaA - b_ge) * sb;
-      const double tv = (double)(rs.VL_fx - rs.VA - v_ge) * sv;
-      const double e = eps_of(tb, tv, (double)__uint_as_float(bt), rs.dnorm, a, l);
-      if (e < (double)p.eps && best < 0) best = lane * per + k;
-    }
-  }
-  int top = best;
-  for (int m = 32; m >= 1; m >>= 1) top = max(top, __shfl_xor(top, m, kWave));
-  if (top < 0) top = 0;  // unreachable: the bracket bottom always certifies
-  if (lane == top / per) {
-    const int k = top % per;
-    uint32_t c_gt = ac;
-    unsigned long long b_gt = ab, v_gt = av;
-    for (int k2 = per - 1; k2 > k; --k2) {
-      c_gt += cnt[k2];
-      b_gt += bs[k2];
-      v_gt += vs[k2];
-    }
-    uint32_t bt = max(rs.bB, bmax_below);
-    for (int k2 = 0; k2 < k; ++k2) bt = max(bt, bm[k2]);
-    const uint32_t cb = cnt[k];
-    const unsigned long long pre2 = (rs.pre << w) | (unsigned long long)top;
-    const unsigned long long fa_b = rs.betaA + b_gt + bs[k];
-    const unsigned long long fa_v = rs.VA + v_gt + vs[k];
-    const double e_through = eps_of((double)(rs.bL_fx - fa_b) * sb,
-                                    (double)(rs.VL_fx - fa_v) * sv,
-                                    (double)__uint_as_float(bt), rs.dnorm, a, l);
-    if (cb == 0u) {
-      rs.kstar = (int)(rs.cntA + c_gt);
-      rs.T = pre2 + 1ull;
-      rs.T_shift = off;
-      rs.eps1 = (float)e_through;
-      rs.mode = MODE_DONE;
-    } else if (cb == 1u || d == 6) {
-      rs.kstar = (int)(rs.cntA + c_gt + cb);
-      rs.T = pre2;
-      rs.T_shift = off;
-      rs.eps1 = (float)e_through;
-      rs.mode = MODE_DONE;
-    } else {
-      rs.cntA += c_gt;
-      rs.betaA += b_gt;
-      rs.VA += v_gt;
-      rs.bB = bt;
-      rs.pre = pre2;
-      rs.shift = off;
-      rs.bin_cnt = cb;
-      if (cb <= (uint32_t)kCand) {
-        rs.mode = MODE_COLLECT;
-        rs.ncand = 0u;
-      } else {
-        rs.mode = MODE_HIST;
-        rs.level = d + 1;
-      }
-    }
-  }
-}
-
-template <int GRP>
-__global__ __launch_bounds__(kBlock) void dk_select(DParams p) {
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int bg = b * p.G + g;
-  __shared__ SelBin s_bins[GRP][kSelBins];
-  __shared__ RowState s_rs[GRP];
-  __shared__ unsigned long long s_ured[kBlock / kWave];
-  if (threadIdx.x < GRP) s_rs[threadIdx.x] = p.rows[row_of(p, b, g, threadIdx.x, GRP)];
+  for (int k = 0; k < NV; ++k) v[k] = wave_sum(v[k]);
   __syncthreads();
-  bool any = false;
-  for (int h = 0; h < GRP; ++h)
-    any |= s_rs[h].fetch && (s_rs[h].mode == MODE_HIST || s_rs[h].mode == MODE_COLLECT);
-  if (!any) return;
-  for (int i = threadIdx.x; i < GRP * kSelBins; i += kBlock)
-    (&s_bins[0][0])[i] = SelBin{0u, 0u, 0ull, 0ull};
-  __syncthreads();
-  const double a = p.a_delta, l = p.l_delta;
-  unsigned long long tb[GRP], tv[GRP];
+  if (lane == 0) {
 #pragma unroll
-  for (int h = 0; h < GRP; ++h) tb[h] = tv[h] = 0ull;
-  const float *rr = p.r + (size_t)bg * p.n;
-  const int base = c * p.chunk;
-  const int lim = min(base + p.chunk, p.n);
-  for (int i = base + threadIdx.x; i < lim; i += kBlock) {
-    const float ri = rr[i];
-    if (!(ri < 1.0f)) continue;
-#pragma unroll
-    for (int h = 0; h < GRP; ++h) {
-      const RowState &rs = s_rs[h];
-      if (!rs.fetch) continue;
-      const int mode = rs.mode;
-      if (mode != MODE_HIST && mode != MODE_COLLECT) continue;
-      const int row = row_of(p, b, g, h, GRP);
-      const Terms t = token_terms(p.shat[(size_t)row * p.n + i], ri, rs.m,
-                                  (float)rs.beta, p.est);
-      const unsigned long long bfx = to_fx(t.bi, rs.eb);
-      const unsigned long long vfx = to_fx(t.vi, rs.ev);
-      if (mode == MODE_HIST && rs.level == 0) {
-        tb[h] += bfx;
-        tv[h] += vfx;
-      }
-      const unsigned long long key = make_key(token_gain(t, i, rs, a, l), i);
-      if ((key >> rs.shift) != rs.pre) continue;
-      if (mode == MODE_HIST) {
-        const int d = rs.level;
-        const int dig = (int)((key >> sel_off(d)) & ((1ull << sel_width(d)) - 1));
-        SelBin &sb = s_bins[h][dig];
-        atomicAdd(&sb.cnt, 1u);
-        atomicAdd(&sb.bsum, bfx);
-        atomicAdd(&sb.vsum, vfx);
-        atomicMax(&sb.bmax, __float_as_uint(t.rb));
-      } else {
-        const uint32_t slot = atomicAdd(&p.rows[row].ncand, 1u);
-        if (slot < (uint32_t)kCand) {
-          Cand cd;
-          cd.key = key;
-          cd.bfx = bfx;
-          cd.vfx = vfx;
-          cd.rb = __float_as_uint(t.rb);
-          cd.pad = 0u;
-          p.cand[(size_t)row * kCand + slot] = cd;
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int h = 0; h < GRP; ++h) {
-    const RowState &rs = s_rs[h];
-    if (!(rs.fetch && rs.mode == MODE_HIST)) continue;
-    const int row = row_of(p, b, g, h, GRP);
-    if (rs.level == 0) {
-      const unsigned long long xb = block_sum<unsigned long long>(tb[h], s_ured);
-      const unsigned long long xv = block_sum<unsigned long long>(tv[h], s_ured);
-      if (threadIdx.x == 0) {
-        atomicAdd(&p.rows[row].bL_fx, xb);
-        atomicAdd(&p.rows[row].VL_fx, xv);
-      }
-    }
+    for (int k = 0; k < NV; ++k) red[wave * NV + k] = v[k];
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < GRP * kSelBins; i += kBlock) {
-    const int h = i / kSelBins, x = i % kSelBins;
-    const RowState &rs = s_rs[h];
-    if (!(rs.fetch && rs.mode == MODE_HIST)) continue;
-    const SelBin &sb = s_bins[h][x];
-    if (sb.cnt == 0u) continue;
-    SelBin *gbn = p.sbins + (size_t)row_of(p, b, g, h, GRP) * kSelBins + x;
-    atomicAdd(&gbn->cnt, sb.cnt);
-    atomicAdd(&gbn->bsum, sb.bsum);
-    atomicAdd(&gbn->vsum, sb.vsum);
-    atomicMax(&gbn->bmax, sb.bmax);
+  if (threadIdx.x < NV) {
+    T t = red[threadIdx.x];
+    for (int w = 1; w < W; ++w) t += red[w * NV + threadIdx.x];
+    red[W * NV + threadIdx.x] = t;
   }
-  if (!last_block_arrive(&p.groups[bg].arrive[ARR_SEL], gridDim.x)) return;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  for (int h = wave; h < GRP; h += kBlock / kWave) {
-    const int row = row_of(p, b, g, h, GRP);
-    RowState &rs = p.rows[row];
-    if (!rs.fetch) continue;
-    if (rs.mode == MODE_COLLECT) {
-      if (lane == 0) rs.mode = MODE_COLLECTED;
-      continue;
-    }
-    if (rs.mode != MODE_HIST) continue;
-    SelBin *gbn = p.sbins + (size_t)row * kSelBins;
-    sel_resolve(rs, gbn, rs.level, p, lane);
-    for (int x = lane; x < kSelBins; x += kWave) gbn[x] = SelBin{0u, 0u, 0ull, 0ull};
-  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < NV; ++k) v[k] = red[W * NV + k];
+}
+template <typename T, int NV>
+__device__ __forceinline__ void plan_reduce(T (&v)[NV], T *red) {
+  blk_reduce<T, NV, kPlanThreads>(v, red);
 }
 
-// One workgroup per row: finish the selection (fallback radix levels over the
-// whole row if a bin stayed large, then sort the collected bin and walk it).
-template <int GRP>
-__global__ __launch_bounds__(kBlock) void dk_finish(DParams p) {
-  const int h = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int bg = b * p.G + g;
-  const int row = row_of(p, b, g, h, GRP);
-  RowState &grs = p.rows[row];
-  __shared__ RowState s_rs;
-  __shared__ SelBin s_bins[kSelBins];
-  __shared__ unsigned long long s_key[kCand];
-  __shared__ uint32_t s_idx[kCand];
+// Block-wide maximum for THREADS threads; `scratch` holds THREADS / 64.
+template <typename T, int THREADS>
+__device__ __forceinline__ T blk_max(T v, T *scratch) {
+  v = wave_max(v);
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) scratch[threadIdx.x / kWave] = v;
+  __syncthreads();
+  T t = scratch[0];
+#pragma unroll
+  for (int i = 1; i < THREADS / kWave; ++i) t = scratch[i] > t ? scratch[i] : t;
+  return t;
+}
+template <typename T>
+__device__ __forceinline__ T plan_max(T v, T *scratch) {
+  return blk_max<T, kPlanThreads>(v, scratch);
+}
+
+// LDS of the streaming selection: the count histogram, then the collected
+// candidates.
+union SelLds {
+  uint32_t hist[kSelBinsP];
+  struct {
+    unsigned long long key[kCand];
+    unsigned long long bfx[kCand];
+    unsigned long long vfx[kCand];
+    uint32_t rb[kCand];
+  } cand;
+};
+
+// Selection (eq. 10) and marking of F_h minus S for one row by one
+// 1024-thread workgroup that streams the row itself, with no limit on how
+// many tokens are fetched. It is the fallback of the candidate walk, taken
+// when the collected candidates cannot certify the row; `rs` (LDS) holds the
+// row's certificate and receives k*, T and eps^(L').
+__device__ void select_row(const DParams &p, int row, int bg, RowState &rs,
+                           SelLds &lds) {
+  const int n = p.n;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  __shared__ unsigned long long s_u[kPlanWaves * 4 + 4];
+  __shared__ uint32_t s_m[kPlanWaves];
   __shared__ uint32_t s_cnt;
-  __shared__ unsigned long long s_scan[kBlock / kWave + 1];
-  __shared__ uint32_t s_uscan[kBlock / kWave + 1];
-  __shared__ int s_best;
-  if (threadIdx.x == 0) s_rs = grs;
-  __syncthreads();
-  if (!s_rs.fetch || s_rs.mode == MODE_DONE) return;
+  __shared__ unsigned long long s_lo;  // the resolved lower key bound
+  __shared__ int s_more;               // another count level is needed
+  __shared__ int s_j[kPlanWaves];
+  const float *rr = p.r + (size_t)bg * n;
+  const float *sh = p.shat + (size_t)row * n;
+  const float m = rs.m;
+  const float betaf = (float)rs.beta;
+  const float af = (float)p.a_delta, lf = (float)p.l_delta;
   const double a = p.a_delta, l = p.l_delta;
-  const float *rr = p.r + (size_t)bg * p.n;
-  const float *sh = p.shat + (size_t)row * p.n;
-  // fallback: remaining radix levels over the whole row
-  while (s_rs.mode == MODE_HIST) {
-    for (int x = threadIdx.x; x < kSelBins; x += kBlock) s_bins[x] = SelBin{0u, 0u, 0ull, 0ull};
-    __syncthreads();
-    const int d = s_rs.level;
-    for (int i = threadIdx.x; i < p.n; i += kBlock) {
-      const float ri = rr[i];
-      if (!(ri < 1.0f)) continue;
-      const Terms t = token_terms(sh[i], ri, s_rs.m, (float)s_rs.beta, p.est);
-      const unsigned long long key = make_key(token_gain(t, i, s_rs, a, l), i);
-      if ((key >> s_rs.shift) != s_rs.pre) continue;
-      const int dig = (int)((key >> sel_off(d)) & ((1ull << sel_width(d)) - 1));
-      atomicAdd(&s_bins[dig].cnt, 1u);
-      atomicAdd(&s_bins[dig].bsum, to_fx(t.bi, s_rs.eb));
-      atomicAdd(&s_bins[dig].vsum, to_fx(t.vi, s_rs.ev));
-      atomicMax(&s_bins[dig].bmax, __float_as_uint(t.rb));
-    }
-    __syncthreads();
-    if (threadIdx.x < kWave) sel_resolve(s_rs, s_bins, d, p, threadIdx.x);
-    __syncthreads();
-  }
-  if (s_rs.mode == MODE_DONE) {
-    if (threadIdx.x == 0) grs = s_rs;
-    return;
-  }
-  // the crossing bin's tokens: collected by dk_select, or here
-  if (s_rs.mode == MODE_COLLECT) {
-    if (threadIdx.x == 0) s_cnt = 0u;
-    __syncthreads();
-    for (int i = threadIdx.x; i < p.n; i += kBlock) {
-      const float ri = rr[i];
-      if (!(ri < 1.0f)) continue;
-      const Terms t = token_terms(sh[i], ri, s_rs.m, (float)s_rs.beta, p.est);
-      const unsigned long long key = make_key(token_gain(t, i, s_rs, a, l), i);
-      if ((key >> s_rs.shift) != s_rs.pre) continue;
-      const uint32_t slot = atomicAdd(&s_cnt, 1u);
-      if (slot < (uint32_t)kCand) {
-        Cand cd;
-        cd.key = key;
-        cd.bfx = to_fx(t.bi, s_rs.eb);
-        cd.vfx = to_fx(t.vi, s_rs.ev);
-        cd.rb = __float_as_uint(t.rb);
-        cd.pad = 0u;
-        p.cand[(size_t)row * kCand + slot] = cd;
+  const int eb = rs.eb, ev = rs.ev;
+  const double sbs = ldexp(1.0, -eb), svs = ldexp(1.0, -ev);
+  const uint32_t *rbits = p.resbits + (size_t)bg * p.nwords;
+  uint32_t *fb = p.fbits + (size_t)bg * p.nwords;
+  constexpr unsigned long long kKeyEnd = 1ull << 55;  // above every key
+
+  // One pass over L with every lane active: g(i, valid, key, terms).
+  auto stream = [&](auto &&g) {
+    for (int base = 0; base < n; base += kSelUnroll * kPlanThreads) {
+      float r8[kSelUnroll], s8[kSelUnroll];
+#pragma unroll
+      for (int u = 0; u < kSelUnroll; ++u) {
+        const int i = base + u * kPlanThreads + (int)threadIdx.x;
+        r8[u] = i < n ? rr[i] : 1.0f;
+        s8[u] = i < n ? sh[i] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < kSelUnroll; ++u) {
+        const int i = base + u * kPlanThreads + (int)threadIdx.x;
+        const bool valid = r8[u] < 1.0f;
+        Terms t{};
+        unsigned long long key = 0ull;
+        if (valid) {
+          t = token_terms_w(expf(s8[u] - m), r8[u], betaf, p.est);
+          key = make_key(token_gain(t, i, rs, af, lf), i);
+        }
+        g(i, valid, key, t);
       }
     }
-    __syncthreads();
-  } else {
-    if (threadIdx.x == 0) s_cnt = s_rs.ncand;
-    __syncthreads();
-  }
-  const uint32_t nc = min(s_cnt, (uint32_t)kCand);
-  const Cand *cand = p.cand + (size_t)row * kCand;
-  // bitonic sort (descending key) of the candidates
-  uint32_t np2 = 1;
-  while (np2 < nc) np2 <<= 1;
-  for (uint32_t i = threadIdx.x; i < np2; i += kBlock) {
-    s_key[i] = i < nc ? cand[i].key : 0ull;
-    s_idx[i] = i;
-  }
-  __syncthreads();
-  for (uint32_t k = 2; k <= np2; k <<= 1) {
-    for (uint32_t j = k >> 1; j > 0; j >>= 1) {
-      for (uint32_t i = threadIdx.x; i < np2; i += kBlock) {
-        const uint32_t ixj = i ^ j;
-        if (ixj > i) {
-          const bool desc = (i & k) == 0;
-          const unsigned long long ki = s_key[i], kj = s_key[ixj];
-          if (desc ? (ki < kj) : (ki > kj)) {
-            s_key[i] = kj;
-            s_key[ixj] = ki;
-            const uint32_t t = s_idx[i];
-            s_idx[i] = s_idx[ixj];
-            s_idx[ixj] = t;
+  };
+
+  // totals over L (first count pass), and what has been fetched so far
+  unsigned long long tot_b = 0ull, tot_v = 0ull;
+  unsigned long long fet_b = 0ull, fet_v = 0ull;
+  uint32_t fet_c = 0u;
+  unsigned long long hi_key = kKeyEnd;
+  bool first = true;
+  // every round fetches at least one more token, so |L| + 1 rounds suffice
+  for (int round = 0; round <= n; ++round) {
+    // ---- count levels: lo with |[lo, hi_key)| <= kCand, as large as useful
+    unsigned long long pre = 0ull;
+    uint32_t base_cnt = 0u;
+    for (int d = 0; d < kSelLevels; ++d) {
+      const int off = sel_off(d);
+      for (int i = threadIdx.x; i < kSelBinsP; i += kPlanThreads) lds.hist[i] = 0u;
+      __syncthreads();
+      unsigned long long lb_ = 0ull, lv_ = 0ull;
+      stream([&](int, bool valid, unsigned long long key, const Terms &t) {
+        if (!valid) return;
+        if (first && d == 0) {
+          lb_ += to_fx(t.bi, eb);
+          lv_ += to_fx(t.vi, ev);
+        }
+        if (key >= hi_key || (key >> (off + kSelDigit)) != pre) return;
+        atomicAdd(&lds.hist[(int)((key >> off) & (kSelBinsP - 1))], 1u);
+      });
+      if (first && d == 0) {
+        unsigned long long tv2[2] = {lb_, lv_};
+        plan_reduce<unsigned long long, 2>(tv2, s_u);
+        tot_b = tv2[0];
+        tot_v = tv2[1];
+      }
+      __syncthreads();
+      if (wave == 0) {
+        // lane owns bins [lane * 32, lane * 32 + 32); c_ge(j) = keys in bins >= j
+        constexpr int PER = kSelBinsP / kWave;
+        uint32_t lc = 0u;
+        for (int k = 0; k < PER; ++k) lc += lds.hist[lane * PER + k];
+        const uint32_t incl = wave_incl_scan<uint32_t>(lc, lane);
+        const uint32_t above = __shfl(incl, kWave - 1, kWave) - incl;
+        const uint32_t budget = (uint32_t)kCand - base_cnt;
+        int j0 = kSelBinsP;  // smallest bin whose suffix fits
+        uint32_t c = above;
+        if (c <= budget) {
+          for (int k = PER - 1; k >= 0; --k) {
+            const uint32_t c2 = c + lds.hist[lane * PER + k];
+            if (c2 > budget) break;
+            c = c2;
+            j0 = lane * PER + k;
+          }
+        }
+        int jm = j0;
+        for (int s2 = 32; s2 >= 1; s2 >>= 1) jm = min(jm, __shfl_xor(jm, s2, kWave));
+        // keys in bins >= jm
+        uint32_t take = 0u;
+        if (jm < kSelBinsP && lane == jm / PER) {
+          take = above;
+          for (int k = PER - 1; k >= jm % PER; --k) take += lds.hist[lane * PER + k];
+        }
+        take = wave_sum(take) + base_cnt;
+        if (lane == 0) {
+          const unsigned long long bin_lo =
+              ((pre << kSelDigit) | (unsigned long long)min(jm, kSelBinsP - 1)) << off;
+          const unsigned long long top = (pre + 1ull) << (off + kSelDigit);
+          if (jm == 0) {
+            s_lo = pre << (off + kSelDigit);
+            s_more = 0;
+          } else if (d == kSelLevels - 1 || take >= (uint32_t)kCand / 2) {
+            s_lo = jm == kSelBinsP ? top : bin_lo;
+            s_more = 0;
+          } else {
+            // refine the bin just below: it alone would overflow the budget
+            s_lo = (pre << kSelDigit) | (unsigned long long)(jm - 1);
+            s_j[0] = (int)take;
+            s_more = 1;
           }
         }
       }
       __syncthreads();
+      if (!s_more) break;
+      pre = s_lo;
+      base_cnt = (uint32_t)s_j[0];
+      __syncthreads();
     }
-  }
-  // walk: fetching the first k+1 sorted candidates (k = 0..nc-1)
-  const uint32_t per = (nc + kBlock - 1) / kBlock;
-  const uint32_t lo = threadIdx.x * per, hi = min(lo + per, nc);
-  unsigned long long mb = 0, mv = 0;
-  uint32_t mmax_after = 0;
-  for (uint32_t k = lo; k < hi; ++k) {
-    const Cand &cd = cand[s_idx[k]];
-    mb += cd.bfx;
-    mv += cd.vfx;
-  }
-  unsigned long long tot_b, tot_v;
-  const unsigned long long pb = block_exclusive_scan<unsigned long long>(mb, s_scan, &tot_b);
-  const unsigned long long pv = block_exclusive_scan<unsigned long long>(mv, s_scan, &tot_v);
-  // suffix max of b over candidates after position k: reverse scan of maxima
-  uint32_t my_max = 0;
-  for (uint32_t k = lo; k < hi; ++k) my_max = max(my_max, cand[s_idx[k]].rb);
-  // max over threads with higher index
-  __shared__ uint32_t s_tmax[kBlock];
-  s_tmax[threadIdx.x] = my_max;
-  __syncthreads();
-  uint32_t after = 0;
-  for (int t2 = threadIdx.x + 1; t2 < kBlock; ++t2) after = max(after, s_tmax[t2]);
-  int best = 0x7fffffff;
-  double best_e = 0.0;
-  {
-    // walk local range backwards to know the suffix max, then forwards
-    uint32_t sufmax[1];
-    (void)sufmax;
-    unsigned long long cb = pb, cv = pv;
-    for (uint32_t k = lo; k < hi; ++k) {
-      const Cand &cd = cand[s_idx[k]];
-      cb += cd.bfx;
-      cv += cd.vfx;
-      uint32_t bt = max(s_rs.bB, after);
-      for (uint32_t k2 = k + 1; k2 < hi; ++k2) bt = max(bt, cand[s_idx[k2]].rb);
-      const double tb = (double)(s_rs.bL_fx - s_rs.betaA - cb) * ldexp(1.0, -s_rs.eb);
-      const double tv = (double)(s_rs.VL_fx - s_rs.VA - cv) * ldexp(1.0, -s_rs.ev);
-      const double e = eps_of(tb, tv, (double)__uint_as_float(bt), s_rs.dnorm, a, l);
-      if (e < (double)p.eps) {
-        best = (int)k;
-        best_e = e;
-        break;
+    first = false;
+    const unsigned long long lo_key = s_lo;
+
+    // ---- collect [lo_key, hi_key); max of b_i below lo_key
+    if (threadIdx.x == 0) s_cnt = 0u;
+    __syncthreads();
+    uint32_t below_max = 0u;
+    unsigned long long cb_ = 0ull, cv_ = 0ull;
+    stream([&](int, bool valid, unsigned long long key, const Terms &t) {
+      const bool sel = valid && key >= lo_key && key < hi_key;
+      if (valid && key < lo_key) below_max = max(below_max, __float_as_uint(t.rb));
+      const unsigned long long msk = __ballot(sel);
+      if (msk == 0ull) return;
+      const int leader = __ffsll((long long)msk) - 1;
+      uint32_t slot0 = 0u;
+      if (lane == leader) slot0 = atomicAdd(&s_cnt, (uint32_t)__popcll(msk));
+      slot0 = __shfl(slot0, leader, kWave);
+      if (sel) {
+        const uint32_t slot =
+            slot0 + (uint32_t)__popcll(msk & ((1ull << lane) - 1ull));
+        const unsigned long long bx = to_fx(t.bi, eb), vx = to_fx(t.vi, ev);
+        cb_ += bx;
+        cv_ += vx;
+        if (slot < (uint32_t)kCand) {
+          lds.cand.key[slot] = key;
+          lds.cand.bfx[slot] = bx;
+          lds.cand.vfx[slot] = vx;
+          lds.cand.rb[slot] = __float_as_uint(t.rb);
+        }
+      }
+    });
+    unsigned long long cs[2] = {cb_, cv_};
+    plan_reduce<unsigned long long, 2>(cs, s_u);
+    below_max = plan_max<uint32_t>(below_max, s_m);
+    const int nc = (int)min(s_cnt, (uint32_t)kCand);
+    const double e_below =
+        eps_of((double)(tot_b - fet_b - cs[0]) * sbs,
+               (double)(tot_v - fet_v - cs[1]) * svs,
+               (double)__uint_as_float(below_max), rs.dnorm, a, l);
+    if (!(e_below < (double)p.eps) && lo_key > 0ull) {
+      // not enough: every candidate is fetched, the region moves below
+      for (int c = threadIdx.x; c < nc; c += kPlanThreads) {
+        const int pos = (int)(0xFFFFFFu - (uint32_t)(lds.cand.key[c] & 0xFFFFFFull));
+        if (!((rbits[pos / 32] >> (pos % 32)) & 1u)) atomicOr(fb + pos / 32, 1u << (pos % 32));
+      }
+      fet_c += (uint32_t)nc;
+      fet_b += cs[0];
+      fet_v += cs[1];
+      hi_key = lo_key;
+      __syncthreads();
+      continue;
+    }
+
+    // ---- rank sort of the candidates by key, descending (keys are unique)
+    constexpr int PT = kCand / kPlanThreads;
+    unsigned long long mk[PT], mb[PT], mv[PT];
+    uint32_t mr[PT];
+    int rank[PT];
+#pragma unroll
+    for (int q = 0; q < PT; ++q) {
+      const int c = threadIdx.x + q * kPlanThreads;
+      rank[q] = -1;
+      if (c < nc) {
+        mk[q] = lds.cand.key[c];
+        mb[q] = lds.cand.bfx[c];
+        mv[q] = lds.cand.vfx[c];
+        mr[q] = lds.cand.rb[c];
+        int rk = 0;
+        for (int o = 0; o < nc; ++o) rk += lds.cand.key[o] > mk[q] ? 1 : 0;
+        rank[q] = rk;
       }
     }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < PT; ++q) {
+      if (rank[q] >= 0) {
+        lds.cand.key[rank[q]] = mk[q];
+        lds.cand.bfx[rank[q]] = mb[q];
+        lds.cand.vfx[rank[q]] = mv[q];
+        lds.cand.rb[rank[q]] = mr[q];
+      }
+    }
+    __syncthreads();
+
+    // ---- walk: fetching sorted candidates 0..k (k = 0..nc-1); each thread
+    // owns PT consecutive positions
+    const int k0 = threadIdx.x * PT;
+    unsigned long long lb2 = 0ull, lv2 = 0ull;
+    uint32_t lmax = 0u;
+#pragma unroll
+    for (int q = 0; q < PT; ++q) {
+      if (k0 + q < nc) {
+        lb2 += lds.cand.bfx[k0 + q];
+        lv2 += lds.cand.vfx[k0 + q];
+        lmax = max(lmax, lds.cand.rb[k0 + q]);
+      }
+    }
+    // exclusive prefix sums over threads, max of b_i over later threads
+    const unsigned long long ib = wave_incl_scan<unsigned long long>(lb2, lane);
+    const unsigned long long iv = wave_incl_scan<unsigned long long>(lv2, lane);
+    uint32_t rmax = lmax;  // suffix max over this lane and the lanes above
+    for (int o = 1; o < kWave; o <<= 1) {
+      const uint32_t v = __shfl_down(rmax, o, kWave);
+      if (lane + o < kWave) rmax = max(rmax, v);
+    }
+    uint32_t after = __shfl_down(rmax, 1, kWave);
+    if (lane == kWave - 1) after = 0u;
+    __syncthreads();
+    if (lane == kWave - 1) {
+      s_u[2 * wave] = ib;
+      s_u[2 * wave + 1] = iv;
+    }
+    if (lane == 0) s_m[wave] = rmax;
+    __syncthreads();
+    unsigned long long base_b = 0ull, base_v = 0ull;
+    for (int w = 0; w < kPlanWaves; ++w) {
+      if (w < wave) {
+        base_b += s_u[2 * w];
+        base_v += s_u[2 * w + 1];
+      }
+      if (w > wave) after = max(after, s_m[w]);
+    }
+    after = max(after, below_max);
+    unsigned long long cb = base_b + ib - lb2, cvv = base_v + iv - lv2;
+    int best = 0x7fffffff;
+    double best_e = 0.0;
+#pragma unroll
+    for (int q = 0; q < PT; ++q) {
+      const int k = k0 + q;
+      if (k >= nc || best != 0x7fffffff) continue;
+      cb += lds.cand.bfx[k];
+      cvv += lds.cand.vfx[k];
+      uint32_t bt = after;
+      for (int q2 = q + 1; q2 < PT; ++q2)
+        if (k0 + q2 < nc) bt = max(bt, lds.cand.rb[k0 + q2]);
+      const double e = eps_of((double)(tot_b - fet_b - cb) * sbs,
+                              (double)(tot_v - fet_v - cvv) * svs,
+                              (double)__uint_as_float(bt), rs.dnorm, a, l);
+      if (e < (double)p.eps) {
+        best = k;
+        best_e = e;
+      }
+    }
+    int first_k = best;
+    first_k = -plan_max<int>(-first_k, s_j);
+    // (fetching every candidate certifies, so first_k < nc; the guard keeps
+    // the state sane if rounding ever said otherwise)
+    const int kk = first_k < nc ? first_k : nc - 1;
+    if (best == first_k && best != 0x7fffffff) {
+      rs.kstar = (int)(fet_c + (uint32_t)best + 1u);
+      rs.T = lds.cand.key[best];
+      rs.eps1 = (float)best_e;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0 && first_k >= nc) {
+      rs.kstar = (int)(fet_c + (uint32_t)nc);
+      rs.T = nc > 0 ? lds.cand.key[nc - 1] : (hi_key == kKeyEnd ? ~0ull : hi_key);
+      rs.eps1 = (float)e_below;
+    }
+    // mark the fetched candidates
+    for (int c = threadIdx.x; c <= kk; c += kPlanThreads) {
+      const int pos = (int)(0xFFFFFFu - (uint32_t)(lds.cand.key[c] & 0xFFFFFFull));
+      if (!((rbits[pos / 32] >> (pos % 32)) & 1u)) atomicOr(fb + pos / 32, 1u << (pos % 32));
+    }
+    __syncthreads();
+    break;
   }
-  (void)mmax_after;
-  __shared__ int s_bt[kBlock / kWave];
-  const int bmin = -block_max<int>(-best, s_bt);
-  if (threadIdx.x == 0) s_best = bmin;
+}
+
+
+// ------------------------------------------------------------ row passes
+// This thread's tokens of chunk c of a row: r and w~ = exp(s - m) (0, with
+// r = 1, outside L or past n). Token u is c * kRowChunk + u * kBlock + tid.
+__device__ __forceinline__ void row_tokens(const DParams &p, int row, int bg,
+                                           int c, float m,
+                                           float (&w8)[kRowTok],
+                                           float (&r8)[kRowTok]) {
+  const float *rr = p.r + (size_t)bg * p.n;
+  const float *sh = p.shat + (size_t)row * p.n;
+  float s8[kRowTok];
+#pragma unroll
+  for (int u = 0; u < kRowTok; ++u) {
+    const int i = c * kRowChunk + u * kBlock + (int)threadIdx.x;
+    r8[u] = i < p.n ? rr[i] : 1.0f;
+    s8[u] = i < p.n ? sh[i] : 0.0f;
+  }
+#pragma unroll
+  for (int u = 0; u < kRowTok; ++u) w8[u] = r8[u] < 1.0f ? expf(s8[u] - m) : 0.0f;
+}
+__device__ __forceinline__ int row_pos(int c, int u) {
+  return c * kRowChunk + u * kBlock + (int)threadIdx.x;
+}
+
+// Points of h evaluated by a Newton pass: lo and three points geometrically
+// closer to it than to hi (Newton usually lands just below the root).
+__device__ __forceinline__ void beta_points(const BetaState &st,
+                                            double (&pts)[kBetaPts]) {
+  const double span = st.hi - st.lo;
+  pts[0] = st.lo;
+  pts[1] = st.lo + span * 0x1p-6;
+  pts[2] = st.lo + span * 0x1p-3;
+  pts[3] = st.lo + span * 0.5;
+}
+
+// State after pass 0 from its totals {sum_L w~, sum rho over w~ > 0, |A(0)|,
+// max w~(1 - r), sum_H w}.
+__device__ __forceinline__ BetaState beta_init(const double (&v)[kBetaRec],
+                                               int est) {
+  BetaState st{};
+  st.dnorm = v[0] + v[4];
+  if (est != VKV_EST_CLIP || !(v[2] > 0.0)) {
+    st.done = 1;
+    return st;
+  }
+  // (w~(1 - r) was rounded once in fp32: step below it to stay a bound)
+  const double lb = v[3] * (1.0 - 0x1p-22);
+  const double nx = v[0] / (1.0 + v[1]);
+  st.lo = fmax(nx, lb);
+  st.hi = v[0];
+  st.prev_cnt = st.lo == nx ? v[2] : -1.0;  // |A| whose Newton step gave lo
+  st.beta = st.lo;
+  if (!(st.hi > st.lo)) st.done = 1;
+  return st;
+}
+
+// One bracketed Newton step from the sums v at the points of `st` (per
+// point: sum w~, sum rho, |A|).
+__device__ __forceinline__ BetaState beta_advance(BetaState st,
+                                                  const double (&v)[kBetaRec]) {
+  double pts[kBetaPts];
+  beta_points(st, pts);
+  if (v[2] == st.prev_cnt) {  // the set that produced lo is active at lo
+    st.beta = st.lo;
+    st.done = 1;
+    return st;
+  }
+  int jl = -1;
+#pragma unroll
+  for (int j = 0; j < kBetaPts; ++j)
+    if (v[3 * j] - pts[j] * (1.0 + v[3 * j + 1]) >= 0.0) jl = j;
+  if (jl < 0) {  // h(lo) < 0 only by rounding: the step from lo is the root
+    st.beta = v[0] / (1.0 + v[1]);
+    st.done = 1;
+    return st;
+  }
+  const double sw = v[3 * jl], sr = v[3 * jl + 1], c = v[3 * jl + 2];
+  const double nb = sw / (1.0 + sr);
+  if (jl + 1 < kBetaPts && v[3 * (jl + 1) + 2] == c) {  // h linear up to there
+    st.beta = nb;
+    st.done = 1;
+    return st;
+  }
+  double nhi = fmin(st.hi, pts[jl] + (sw - pts[jl] * (1.0 + sr)));
+  if (jl + 1 < kBetaPts) nhi = fmin(nhi, pts[jl + 1]);
+  st.lo = fmax(nb, pts[jl]);
+  st.hi = nhi;
+  st.prev_cnt = c;
+  st.beta = st.lo;
+  if (!(st.hi > st.lo)) st.done = 1;
+  return st;
+}
+
+// Adds token (w~, r)'s terms at the points to v.
+__device__ __forceinline__ void beta_accumulate(const double (&pts)[kBetaPts],
+                                                float wt, float ri,
+                                                double (&v)[kBetaRec]) {
+  if (!(wt > 0.0f)) return;
+  const double w = (double)wt, rh = (double)plan_rho(ri);
+#pragma unroll
+  for (int j = 0; j < kBetaPts; ++j) {
+    if (w - pts[j] * rh > 0.0) {
+      v[3 * j] += w;
+      v[3 * j + 1] += rh;
+      v[3 * j + 2] += 1.0;
+    }
+  }
+}
+
+// Fixed-order totals of a row's S records; slot `max_slot` (>= 0) is
+// combined by maximum. The same in every workgroup.
+__device__ __forceinline__ void combine_beta(const double *rec, int S,
+                                             int max_slot,
+                                             double (&tot)[kBetaRec],
+                                             double *red, double *mscr) {
+#pragma unroll
+  for (int k = 0; k < kBetaRec; ++k) tot[k] = 0.0;
+  double mx = 0.0;
+  for (int t = threadIdx.x; t < S; t += kBlock) {
+#pragma unroll
+    for (int k = 0; k < kBetaRec; ++k) {
+      const double x = rec[(size_t)t * kBetaRec + k];
+      if (k == max_slot) mx = fmax(mx, x);
+      else tot[k] += x;
+    }
+  }
+  blk_reduce<double, kBetaRec, kBlock>(tot, red);
+  if (max_slot >= 0) tot[max_slot] = blk_max<double, kBlock>(mx, mscr);
+}
+
+// Pass `pass` of the beta* iteration: 0 is pass 0, later ones are Newton
+// passes. Grid (chunks, Hq, B).
+template <int GRP>
+__global__ __launch_bounds__(kBlock) void dk_rbeta(DParams p, int pass) {
+  const int c = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
+  const int row = b * p.Hq + hq, bg = b * p.G + hq / GRP;
+  const size_t rows = (size_t)p.B * p.Hq;
+  __shared__ double s_red[(kBlock / kWave + 1) * kBetaRec];
+  __shared__ double s_mx[kBlock / kWave];
+  const float m = p.rows[row].m;
+  float w8[kRowTok], r8[kRowTok];
+  row_tokens(p, row, bg, c, m, w8, r8);
+  double v[kBetaRec];
+#pragma unroll
+  for (int k = 0; k < kBetaRec; ++k) v[k] = 0.0;
+  double *out = p.bpart + (((size_t)(pass & 1) * rows + row) * p.nrc + c) * kBetaRec;
+  if (pass == 0) {
+    double lb = 0.0;
+#pragma unroll
+    for (int u = 0; u < kRowTok; ++u) {
+      if (!(r8[u] < 1.0f)) continue;
+      v[0] += (double)w8[u];
+      if (w8[u] > 0.0f) {
+        v[1] += (double)plan_rho(r8[u]);
+        v[2] += 1.0;
+        lb = fmax(lb, (double)(w8[u] * (1.0f - r8[u])));
+      }
+    }
+    if (c == 0) {  // H part of D~ from the exact resident logits
+      const float *rr = p.r + (size_t)bg * p.n;
+      const int cnt = max(0, min(p.rcount[bg], p.cap));
+      const int32_t *ridx = p.ridx + (size_t)bg * p.cap;
+      const float *el = p.ell + (size_t)row * p.cap;
+      for (int j = threadIdx.x; j < cnt; j += kBlock) {
+        const int pos = ridx[j];
+        const float e = el[j];
+        if (pos >= 0 && pos < p.n && rr[pos] >= 1.0f) v[4] += (double)expf(e - m);
+      }
+    }
+    blk_reduce<double, kBetaRec, kBlock>(v, s_red);
+    lb = blk_max<double, kBlock>(lb, s_mx);
+    if (threadIdx.x == 0) {
+#pragma unroll
+      for (int k = 0; k < kBetaRec; ++k) out[k] = k == 3 ? lb : v[k];
+    }
+    return;
+  }
+  const int q = (pass - 1) & 1;
+  const double *rec = p.bpart + ((size_t)q * rows + row) * p.nrc * kBetaRec;
+  BetaState st;
+  if (pass == 1) {
+    double tot[kBetaRec];
+    combine_beta(rec, p.nrc, 3, tot, s_red, s_mx);
+    st = beta_init(tot, p.est);
+  } else {
+    st = p.bstate[(size_t)q * rows + row];
+    if (!st.done) {
+      double tot[kBetaRec];
+      combine_beta(rec, p.nrc, -1, tot, s_red, s_mx);
+      st = beta_advance(st, tot);
+    }
+  }
+  if (c == 0 && threadIdx.x == 0) p.bstate[(size_t)(pass & 1) * rows + row] = st;
+  if (st.done) return;
+  double pts[kBetaPts];
+  beta_points(st, pts);
+#pragma unroll
+  for (int u = 0; u < kRowTok; ++u) beta_accumulate(pts, w8[u], r8[u], v);
+  blk_reduce<double, kBetaRec, kBlock>(v, s_red);
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int k = 0; k < kBetaRec; ++k) out[k] = v[k];
+  }
+}
+
+// Certificate terms (Lemma 1) at beta*. Settles beta* from the last Newton
+// pass first; a row still open iterates here over all of its tokens.
+template <int GRP>
+__global__ __launch_bounds__(kBlock) void dk_rcert(DParams p) {
+  const int c = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
+  const int row = b * p.Hq + hq, bg = b * p.G + hq / GRP;
+  const size_t rows = (size_t)p.B * p.Hq;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  __shared__ double s_red[(kBlock / kWave + 1) * kBetaRec];
+  __shared__ double s_mx[kBlock / kWave];
+  __shared__ float s_f1[kBlock / kWave], s_f2[kBlock / kWave];
+  __shared__ int s_i[kBlock / kWave];
+  const float m = p.rows[row].m;
+  float w8[kRowTok], r8[kRowTok];
+  row_tokens(p, row, bg, c, m, w8, r8);
+  const int q = (kBetaLaunches - 1) & 1;
+  BetaState st = p.bstate[(size_t)q * rows + row];
+  if (!st.done) {
+    double tot[kBetaRec];
+    combine_beta(p.bpart + ((size_t)q * rows + row) * p.nrc * kBetaRec, p.nrc,
+                 -1, tot, s_red, s_mx);
+    st = beta_advance(st, tot);
+  }
+  if (!st.done) {
+    // rare: more Newton passes, each over the whole row by this workgroup
+    const float *rr = p.r + (size_t)bg * p.n;
+    const float *sh = p.shat + (size_t)row * p.n;
+    for (int it = 0; it < kBetaPassMax && !st.done; ++it) {
+      double pts[kBetaPts], v[kBetaRec];
+      beta_points(st, pts);
+#pragma unroll
+      for (int k = 0; k < kBetaRec; ++k) v[k] = 0.0;
+      for (int i = threadIdx.x; i < p.n; i += kBlock) {
+        const float ri = rr[i];
+        if (ri < 1.0f) beta_accumulate(pts, expf(sh[i] - m), ri, v);
+      }
+      blk_reduce<double, kBetaRec, kBlock>(v, s_red);
+      st = beta_advance(st, v);
+    }
+    if (!st.done) st.beta = st.lo;
+  }
+  const double beta = st.beta;
+  if (c == 0 && threadIdx.x == 0) {
+    p.rbeta[2 * row] = beta;
+    p.rbeta[2 * row + 1] = st.dnorm;
+  }
+  const float betaf = (float)beta;
+  double cv[2] = {0.0, 0.0};
+  float x1 = 0.0f, x2 = 0.0f;
+  int p1 = 0x7fffffff;
+#pragma unroll
+  for (int u = 0; u < kRowTok; ++u) {
+    if (!(r8[u] < 1.0f)) continue;
+    const Terms t = token_terms_w(w8[u], r8[u], betaf, p.est);
+    cv[0] += (double)t.bi;
+    cv[1] += (double)t.vi;
+    top2_merge(x1, p1, x2, t.rb, row_pos(c, u), 0.0f);
+  }
+  blk_reduce<double, 2, kBlock>(cv, s_red);
+#pragma unroll
+  for (int s2 = 32; s2 >= 1; s2 >>= 1) {
+    const float o1 = shfl_xor(x1, s2), o2 = shfl_xor(x2, s2);
+    const int oq = shfl_xor(p1, s2);
+    top2_merge(x1, p1, x2, o1, oq, o2);
+  }
+  if (lane == 0) {
+    s_f1[wave] = x1;
+    s_f2[wave] = x2;
+    s_i[wave] = p1;
+  }
   __syncthreads();
-  if (best == s_best && best != 0x7fffffff) {
-    RowState rs = s_rs;
-    rs.kstar = (int)(rs.cntA + (uint32_t)best + 1u);
-    rs.T = s_key[best];
-    rs.T_shift = 0;
-    rs.eps1 = (float)best_e;
-    rs.mode = MODE_DONE;
-    grs = rs;
-  } else if (threadIdx.x == 0 && s_best == 0x7fffffff) {
-    // unreachable: fetching the whole bin always certifies
-    RowState rs = s_rs;
-    rs.kstar = (int)(rs.cntA + nc);
-    rs.T = nc ? s_key[nc - 1] : (rs.pre << rs.shift);
-    rs.T_shift = 0;
-    rs.eps1 = 0.0f;
-    rs.mode = MODE_DONE;
-    grs = rs;
+  if (threadIdx.x == 0) {
+    float y1 = s_f1[0], y2 = s_f2[0];
+    int yq = s_i[0];
+    for (int w = 1; w < kBlock / kWave; ++w) top2_merge(y1, yq, y2, s_f1[w], s_i[w], s_f2[w]);
+    CertPart cp;
+    cp.tb = cv[0];
+    cp.tv = cv[1];
+    cp.x1 = y1;
+    cp.x2 = y2;
+    cp.p1 = yq;
+    cp.pad = 0;
+    p.cpart[(size_t)row * p.nrc + c] = cp;
+  }
+}
+
+// The certificate of a row from its chunk records: every workgroup of the
+// row computes the same RowState.
+__device__ __forceinline__ void row_certificate(const DParams &p, int row,
+                                                RowState &rs, double *red,
+                                                float *f1, float *f2, int *pi) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  double cv[2] = {0.0, 0.0};
+  float x1 = 0.0f, x2 = 0.0f;
+  int p1 = 0x7fffffff;
+  for (int t = threadIdx.x; t < p.nrc; t += kBlock) {
+    const CertPart cp = p.cpart[(size_t)row * p.nrc + t];
+    cv[0] += cp.tb;
+    cv[1] += cp.tv;
+    top2_merge(x1, p1, x2, cp.x1, cp.p1, cp.x2);
+  }
+  blk_reduce<double, 2, kBlock>(cv, red);
+#pragma unroll
+  for (int s2 = 32; s2 >= 1; s2 >>= 1) {
+    const float o1 = shfl_xor(x1, s2), o2 = shfl_xor(x2, s2);
+    const int oq = shfl_xor(p1, s2);
+    top2_merge(x1, p1, x2, o1, oq, o2);
+  }
+  if (lane == 0) {
+    f1[wave] = x1;
+    f2[wave] = x2;
+    pi[wave] = p1;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float y1 = f1[0], y2 = f2[0];
+    int yq = pi[0];
+    for (int w = 1; w < kBlock / kWave; ++w) top2_merge(y1, yq, y2, f1[w], pi[w], f2[w]);
+    const double a = p.a_delta, l = p.l_delta;
+    const double tb = cv[0], tv = cv[1];
+    const double dnorm = p.rbeta[2 * row + 1];
+    RowState z{};
+    z.m = p.rows[row].m;
+    z.dnorm = dnorm;
+    z.beta = p.rbeta[2 * row];
+    z.betaL = tb;
+    z.VL = tv;
+    z.b1 = y1;
+    z.b2 = y2;
+    z.amax = (y2 < y1) ? yq : -1;
+    z.s_full = sqrt(a * a * (double)y1 * (double)y1 + 2.0 * tv * l);
+    const float af = (float)a, lf = (float)l;
+    z.s_full_f = sqrtf(af * af * y1 * y1 + 2.0f * (float)tv * lf);
+    const double e0 = (tb + a * (double)y1 + z.s_full) / dnorm;
+    z.eps0 = e0;
+    z.eps1 = (float)e0;
+    z.kstar = 0;
+    z.T = ~0ull;
+    z.fetch = e0 < (double)p.eps ? 0 : 1;
+    int eb = 0, ev = 0;
+    if (tb > 0.0) { (void)frexp(tb, &eb); eb = 61 - eb; }
+    if (tv > 0.0) { (void)frexp(tv, &ev); ev = 61 - ev; }
+    z.eb = eb;
+    z.ev = ev;
+    rs = z;
+  }
+  __syncthreads();
+}
+
+// Certificate of the row (workgroup 0 stores it), then for a row that
+// fetches: the count histogram of the top 11 key bits and the fixed-point
+// totals of beta_i and v_i over the chunk.
+template <int GRP>
+__global__ __launch_bounds__(kBlock) void dk_rcount(DParams p) {
+  const int c = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
+  const int row = b * p.Hq + hq, bg = b * p.G + hq / GRP;
+  __shared__ RowState rs;
+  __shared__ double s_red[(kBlock / kWave + 1) * 2];
+  __shared__ unsigned long long s_ured[(kBlock / kWave + 1) * 2];
+  __shared__ float s_f1[kBlock / kWave], s_f2[kBlock / kWave];
+  __shared__ int s_i[kBlock / kWave];
+  __shared__ uint32_t s_hist[kSelBinsP];
+  const float m = p.rows[row].m;
+  float w8[kRowTok], r8[kRowTok];
+  row_tokens(p, row, bg, c, m, w8, r8);
+  for (int i = threadIdx.x; i < kSelBinsP; i += kBlock) s_hist[i] = 0u;
+  row_certificate(p, row, rs, s_red, s_f1, s_f2, s_i);
+  if (c == 0 && threadIdx.x == 0) p.rows[row] = rs;
+  if (!rs.fetch) return;
+  const float betaf = (float)rs.beta;
+  const float af = (float)p.a_delta, lf = (float)p.l_delta;
+  const int eb = rs.eb, ev = rs.ev;
+  unsigned long long tx[2] = {0ull, 0ull};
+#pragma unroll
+  for (int u = 0; u < kRowTok; ++u) {
+    if (!(r8[u] < 1.0f)) continue;
+    const int i = row_pos(c, u);
+    const Terms t = token_terms_w(w8[u], r8[u], betaf, p.est);
+    const unsigned long long key = make_key(token_gain(t, i, rs, af, lf), i);
+    atomicAdd(&s_hist[(int)(key >> sel_off(0))], 1u);
+    tx[0] += to_fx(t.bi, eb);
+    tx[1] += to_fx(t.vi, ev);
+  }
+  blk_reduce<unsigned long long, 2, kBlock>(tx, s_ured);
+  if (threadIdx.x == 0) {
+    p.tpart[((size_t)row * p.nrc + c) * 2] = tx[0];
+    p.tpart[((size_t)row * p.nrc + c) * 2 + 1] = tx[1];
+  }
+  uint32_t *hp = p.khist + ((size_t)row * p.nrc + c) * kSelBinsP;
+  for (int i = threadIdx.x; i < kSelBinsP; i += kBlock) hp[i] = s_hist[i];
+}
+
+// One workgroup per row: the row's histogram and totals, and the key bound
+// lo with at most kCandMax keys in [lo, inf).
+template <int GRP>
+__global__ __launch_bounds__(kPlanThreads) void dk_rresolve(DParams p) {
+  const int hq = blockIdx.x, b = blockIdx.y;
+  const int row = b * p.Hq + hq;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  __shared__ unsigned long long s_u[(kPlanWaves + 1) * 2];
+  __shared__ uint32_t s_w[kPlanWaves];
+  __shared__ int s_j[kPlanWaves];
+  __shared__ uint32_t s_take;
+  if (!p.rows[row].fetch) return;
+  // bins 2t and 2t + 1 of this thread, summed over the chunks
+  uint32_t h0 = 0u, h1 = 0u;
+  const uint32_t *hp = p.khist + (size_t)row * p.nrc * kSelBinsP;
+  for (int s = 0; s < p.nrc; ++s) {
+    const uint2 x = *reinterpret_cast<const uint2 *>(hp + (size_t)s * kSelBinsP + 2 * threadIdx.x);
+    h0 += x.x;
+    h1 += x.y;
+  }
+  unsigned long long tot[2] = {0ull, 0ull};
+  for (int s = threadIdx.x; s < p.nrc; s += kPlanThreads) {
+    tot[0] += p.tpart[((size_t)row * p.nrc + s) * 2];
+    tot[1] += p.tpart[((size_t)row * p.nrc + s) * 2 + 1];
+  }
+  plan_reduce<unsigned long long, 2>(tot, s_u);
+  // keys in bins above this thread's: suffix sums over threads
+  const uint32_t mine = h0 + h1;
+  uint32_t suf = mine;  // inclusive suffix within the wave
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint32_t x = __shfl_down(suf, o, kWave);
+    if (lane + o < kWave) suf += x;
+  }
+  if (lane == 0) s_w[wave] = suf;  // the wave's total
+  __syncthreads();
+  uint32_t above = suf - mine;
+  for (int w = wave + 1; w < kPlanWaves; ++w) above += s_w[w];
+  const uint32_t c1 = above + h1, c0 = c1 + h0;  // keys in bins >= 2t+1, >= 2t
+  int j = kSelBinsP;
+  if (c0 <= (uint32_t)kCandMax) j = 2 * threadIdx.x;
+  else if (c1 <= (uint32_t)kCandMax) j = 2 * threadIdx.x + 1;
+  const int j0 = -plan_max<int>(-j, s_j);
+  if (j0 < kSelBinsP && (j0 >> 1) == (int)threadIdx.x) s_take = (j0 & 1) ? c1 : c0;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    SelState ss;
+    ss.lo_key = j0 < kSelBinsP ? ((unsigned long long)j0 << sel_off(0)) : kKeyEnd;
+    ss.tot_b = tot[0];
+    ss.tot_v = tot[1];
+    ss.take = j0 < kSelBinsP ? s_take : 0u;
+    ss.pad = 0u;
+    p.sel[row] = ss;
+    p.ccount[row] = 0u;
+  }
+}
+
+// Candidates: the chunk's keys in [lo, inf) with their fixed-point beta_i,
+// v_i and b_i, appended to the row's list; the max of b_i below lo.
+template <int GRP>
+__global__ __launch_bounds__(kBlock) void dk_rcollect(DParams p) {
+  const int c = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
+  const int row = b * p.Hq + hq, bg = b * p.G + hq / GRP;
+  __shared__ RowState rs;
+  __shared__ uint32_t s_scan[kBlock / kWave + 1];
+  __shared__ uint32_t s_m[kBlock / kWave];
+  __shared__ uint32_t s_base;
+  if (threadIdx.x == 0) rs = p.rows[row];
+  const float m = p.rows[row].m;
+  float w8[kRowTok], r8[kRowTok];
+  row_tokens(p, row, bg, c, m, w8, r8);
+  __syncthreads();
+  if (!rs.fetch) return;
+  const unsigned long long lo_key = p.sel[row].lo_key;
+  const float betaf = (float)rs.beta;
+  const float af = (float)p.a_delta, lf = (float)p.l_delta;
+  unsigned long long key8[kRowTok];
+  uint32_t below = 0u, cnt = 0u;
+#pragma unroll
+  for (int u = 0; u < kRowTok; ++u) {
+    key8[u] = 0ull;
+    if (!(r8[u] < 1.0f)) continue;
+    const int i = row_pos(c, u);
+    const Terms t = token_terms_w(w8[u], r8[u], betaf, p.est);
+    key8[u] = make_key(token_gain(t, i, rs, af, lf), i);
+    if (key8[u] >= lo_key) ++cnt;
+    else below = max(below, __float_as_uint(t.rb));
+  }
+  uint32_t total;
+  const uint32_t off = block_exclusive_scan(cnt, s_scan, &total);
+  if (threadIdx.x == 0) s_base = total ? atomicAdd(p.ccount + row, total) : 0u;
+  below = blk_max<uint32_t, kBlock>(below, s_m);
+  if (threadIdx.x == 0) p.rpart[(size_t)row * p.nrc + c] = below;
+  const uint32_t base = s_base + off;
+  if (cnt == 0u) return;
+  const int eb = rs.eb, ev = rs.ev;
+  uint32_t k = 0u;
+#pragma unroll
+  for (int u = 0; u < kRowTok; ++u) {
+    if (!(r8[u] < 1.0f) || key8[u] < lo_key) continue;
+    const uint32_t slot = base + k++;
+    if (slot >= (uint32_t)kCandMax) continue;
+    const Terms t = token_terms_w(w8[u], r8[u], betaf, p.est);
+    const size_t at = (size_t)row * kCandMax + slot;
+    p.candk[at] = key8[u];
+    p.candb[at] = to_fx(t.bi, eb);
+    p.candv[at] = to_fx(t.vi, ev);
+    p.candr[at] = __float_as_uint(t.rb);
+  }
+}
+
+// Candidate select: per-bin counts, fixed-point sums of beta_i and v_i and
+// the max of b_i over eight key bits at a time.
+constexpr int kWalkBins = 256;
+struct WalkBin {
+  uint32_t cnt, bmax;
+  unsigned long long bsum, vsum;
+};
+
+union WalkLds {
+  struct {
+    unsigned long long key[kCandMax];
+    unsigned long long bfx[kCandMax];
+    unsigned long long vfx[kCandMax];
+    uint32_t rb[kCandMax];
+    WalkBin bin[kWalkBins];
+  } c;
+  SelLds sel;
+};
+
+// State of the candidate select between its levels.
+struct WalkState {
+  unsigned long long pre;     // key bits above the current digit
+  unsigned long long ab, av;  // fixed-point sums fetched above the bracket
+  unsigned long long T;       // F_h = keys >= T, once done
+  uint32_t ac;                // candidates fetched above the bracket
+  uint32_t bmax;              // max b_i certainly left in the rest
+  int32_t off, w;             // current digit: key bits [off, off + w)
+  int32_t done, kstar;
+  float eps1;
+};
+
+// One 1024-thread workgroup per fetching row: the stopping rule (eq. 10)
+// over the collected candidates by a radix select. Each level bins the
+// candidates inside the current bracket by eight key bits; with the fetched
+// part F(j) = (fetched above) + (bins >= j), eps^ of L \ F(j) falls as j
+// falls, and the highest bin j* with eps^ < eps holds the last token of
+// F_h: if it holds one candidate that is k*, otherwise j* becomes the
+// bracket of the next level. F_h minus S then goes into the KV head's fetch
+// bitmap. When the candidates cannot certify the row it runs the streaming
+// selection instead.
+template <int GRP>
+__global__ __launch_bounds__(kPlanThreads) void dk_rwalk(DParams p) {
+  const int hq = blockIdx.x, b = blockIdx.y;
+  const int row = b * p.Hq + hq, bg = b * p.G + hq / GRP;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  __shared__ WalkLds lds;
+  __shared__ RowState rs;
+  __shared__ WalkState ws;
+  __shared__ unsigned long long s_u[(kPlanWaves + 1) * 2];
+  __shared__ uint32_t s_m[kPlanWaves];
+  if (threadIdx.x == 0) rs = p.rows[row];
+  __syncthreads();
+  if (!rs.fetch) return;
+  const SelState ss = p.sel[row];
+  const uint32_t ncount = p.ccount[row];
+  const int nc = (int)min(ncount, (uint32_t)kCandMax);
+  const double a = p.a_delta, l = p.l_delta;
+  const double sbs = ldexp(1.0, -rs.eb), svs = ldexp(1.0, -rs.ev);
+  const size_t cb0 = (size_t)row * kCandMax;
+  uint32_t below = 0u;
+  for (int s = threadIdx.x; s < p.nrc; s += kPlanThreads)
+    below = max(below, p.rpart[(size_t)row * p.nrc + s]);
+  below = plan_max<uint32_t>(below, s_m);
+  unsigned long long cs[2] = {0ull, 0ull};
+  for (int k = threadIdx.x; k < nc; k += kPlanThreads) {
+    cs[0] += p.candb[cb0 + k];
+    cs[1] += p.candv[cb0 + k];
+  }
+  plan_reduce<unsigned long long, 2>(cs, s_u);
+  // fetching every candidate leaves exactly the tokens below lo
+  const double e_below =
+      eps_of((double)(ss.tot_b - cs[0]) * sbs, (double)(ss.tot_v - cs[1]) * svs,
+             (double)__uint_as_float(below), rs.dnorm, a, l);
+  if (!(e_below < (double)p.eps) || ncount != ss.take || nc == 0) {
+    __syncthreads();
+    select_row(p, row, bg, rs, lds.sel);
+    __syncthreads();
+    if (threadIdx.x == 0) p.rows[row] = rs;
+    return;
+  }
+  unsigned long long kmin = ~0ull, kmax = 0ull;
+  for (int k = threadIdx.x; k < nc; k += kPlanThreads) {
+    const unsigned long long key = p.candk[cb0 + k];
+    lds.c.key[k] = key;
+    lds.c.bfx[k] = p.candb[cb0 + k];
+    lds.c.vfx[k] = p.candv[cb0 + k];
+    lds.c.rb[k] = p.candr[cb0 + k];
+    kmin = min(kmin, key);
+    kmax = max(kmax, key);
+  }
+  kmax = plan_max<unsigned long long>(kmax, s_u);
+  kmin = ~plan_max<unsigned long long>(~kmin, s_u);
+  if (threadIdx.x == 0) {
+    // the first digit starts where the candidates' keys start to differ
+    const int span = kmax == kmin ? 0 : 64 - __clzll((long long)(kmax ^ kmin));
+    WalkState z{};
+    z.off = max(0, span - 8);
+    z.w = max(1, span - z.off);
+    z.pre = kmax >> (z.off + z.w);
+    z.bmax = below;
+    ws = z;
+  }
+  __syncthreads();
+  for (int level = 0; level < 10; ++level) {  // at most 7 eight-bit digits
+    if (threadIdx.x < kWalkBins) lds.c.bin[threadIdx.x] = WalkBin{0u, 0u, 0ull, 0ull};
+    __syncthreads();
+    const int off = ws.off, w = ws.w;
+    const unsigned long long pre = ws.pre;
+    for (int k = threadIdx.x; k < nc; k += kPlanThreads) {
+      const unsigned long long key = lds.c.key[k];
+      if ((key >> (off + w)) != pre) continue;
+      WalkBin &x = lds.c.bin[(int)((key >> off) & ((1ull << w) - 1ull))];
+      atomicAdd(&x.cnt, 1u);
+      atomicAdd(&x.bsum, lds.c.bfx[k]);
+      atomicAdd(&x.vsum, lds.c.vfx[k]);
+      atomicMax(&x.bmax, lds.c.rb[k]);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // lane owns bins 4 lane .. 4 lane + 3
+      constexpr int PER = kWalkBins / kWave;
+      uint32_t lc = 0u, lmx = 0u;
+      unsigned long long lb = 0ull, lv = 0ull;
+#pragma unroll
+      for (int q = 0; q < PER; ++q) {
+        const WalkBin &x = lds.c.bin[lane * PER + q];
+        lc += x.cnt;
+        lb += x.bsum;
+        lv += x.vsum;
+        lmx = max(lmx, x.bmax);
+      }
+      // sums over the lanes above, max over the lanes below
+      uint32_t sc = lc;
+      unsigned long long sb = lb, sv = lv;
+      for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t xc = __shfl_down(sc, o, kWave);
+        const unsigned long long xb = __shfl_down(sb, o, kWave), xv = __shfl_down(sv, o, kWave);
+        if (lane + o < kWave) {
+          sc += xc;
+          sb += xb;
+          sv += xv;
+        }
+      }
+      sc -= lc;
+      sb -= lb;
+      sv -= lv;
+      uint32_t pm = lmx;
+      for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t x = __shfl_up(pm, o, kWave);
+        if (lane >= o) pm = max(pm, x);
+      }
+      uint32_t mlow = __shfl_up(pm, 1, kWave);
+      if (lane == 0) mlow = 0u;
+      mlow = max(mlow, ws.bmax);
+      // the lane's highest bin whose fetched-through eps^ is below eps
+      int best = -1;
+      {
+        uint32_t c = sc;
+        unsigned long long fb = ws.ab + sb, fv = ws.av + sv;
+        for (int q = PER - 1; q >= 0 && best < 0; --q) {
+          const WalkBin &x = lds.c.bin[lane * PER + q];
+          c += x.cnt;
+          fb += x.bsum;
+          fv += x.vsum;
+          uint32_t mb = mlow;
+          for (int q2 = 0; q2 < q; ++q2) mb = max(mb, lds.c.bin[lane * PER + q2].bmax);
+          const double e = eps_of((double)(ss.tot_b - fb) * sbs,
+                                  (double)(ss.tot_v - fv) * svs,
+                                  (double)__uint_as_float(mb), rs.dnorm, a, l);
+          if (x.cnt > 0u && e < (double)p.eps) best = lane * PER + q;
+        }
+      }
+      int top = best;
+      for (int o = 32; o >= 1; o >>= 1) top = max(top, __shfl_xor(top, o, kWave));
+      if (top < 0) top = 0;  // unreachable: fetching every candidate certifies
+      if (lane == top / PER) {
+        const int q = top % PER;
+        uint32_t c = sc;
+        unsigned long long fb = ws.ab + sb, fv = ws.av + sv;
+        for (int q2 = PER - 1; q2 > q; --q2) {
+          const WalkBin &x = lds.c.bin[lane * PER + q2];
+          c += x.cnt;
+          fb += x.bsum;
+          fv += x.vsum;
+        }
+        uint32_t mb = mlow;
+        for (int q2 = 0; q2 < q; ++q2) mb = max(mb, lds.c.bin[lane * PER + q2].bmax);
+        const WalkBin &x = lds.c.bin[top];
+        if (x.cnt <= 1u || off == 0) {
+          const double e = eps_of((double)(ss.tot_b - fb - x.bsum) * sbs,
+                                  (double)(ss.tot_v - fv - x.vsum) * svs,
+                                  (double)__uint_as_float(mb), rs.dnorm, a, l);
+          ws.kstar = (int)(ws.ac + c + x.cnt);
+          ws.eps1 = (float)e;
+          ws.pre = (pre << w) | (unsigned long long)top;  // the last key's digits
+          ws.done = 1;
+        } else {
+          ws.ac += c;
+          ws.ab = fb;
+          ws.av = fv;
+          ws.bmax = mb;
+          ws.pre = (pre << w) | (unsigned long long)top;
+          const int noff = max(0, off - 8);
+          ws.w = off - noff;
+          ws.off = noff;
+        }
+      }
+    }
+    __syncthreads();
+    if (ws.done) break;
+  }
+  // the last fetched key: the one candidate whose bits above `off` are pre
+  {
+    const int off = ws.off;
+    const unsigned long long pre = ws.pre;
+    for (int k = threadIdx.x; k < nc; k += kPlanThreads)
+      if ((lds.c.key[k] >> off) == pre) ws.T = lds.c.key[k];
+  }
+  __syncthreads();
+  const unsigned long long T = ws.T;
+  const uint32_t *rbits = p.resbits + (size_t)bg * p.nwords;
+  uint32_t *fbm = p.fbits + (size_t)bg * p.nwords;
+  for (int k = threadIdx.x; k < nc; k += kPlanThreads) {
+    const unsigned long long key = lds.c.key[k];
+    if (key < T) continue;
+    const int pos = (int)(0xFFFFFFu - (uint32_t)(key & 0xFFFFFFull));
+    if (!((rbits[pos / 32] >> (pos % 32)) & 1u)) atomicOr(fbm + pos / 32, 1u << (pos % 32));
+  }
+  if (threadIdx.x == 0) {
+    rs.kstar = ws.kstar;
+    rs.T = T;
+    rs.eps1 = ws.eps1;
+    p.rows[row] = rs;
   }
 }
 
 // ------------------------------------------------------------ fetch
-template <int GRP>
-__global__ __launch_bounds__(kBlock) void dk_mark(DParams p) {
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int bg = b * p.G + g;
-  __shared__ RowState s_rs[GRP];
-  __shared__ uint32_t s_red[kBlock / kWave];
-  if (threadIdx.x < GRP) s_rs[threadIdx.x] = p.rows[row_of(p, b, g, threadIdx.x, GRP)];
-  __syncthreads();
-  bool any = false;
-  for (int h = 0; h < GRP; ++h) any |= s_rs[h].fetch && s_rs[h].kstar > 0;
-  const double a = p.a_delta, l = p.l_delta;
-  const float *rr = p.r + (size_t)bg * p.n;
-  const uint32_t *rb = p.resbits + (size_t)bg * p.nwords;
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int base = c * p.chunk;
-  uint32_t count = 0;
-  if (any) {
-    for (int k = 0; k < p.chunk / kBlock; ++k) {
-      const int i = base + k * kBlock + threadIdx.x;
-      bool f = false;
-      if (i < p.n) {
-        const float ri = rr[i];
-        if (ri < 1.0f && !((rb[i / 32] >> (i % 32)) & 1u)) {
-#pragma unroll
-          for (int h = 0; h < GRP; ++h) {
-            const RowState &rs = s_rs[h];
-            if (!rs.fetch || rs.kstar == 0 || f) continue;
-            const int row = row_of(p, b, g, h, GRP);
-            const Terms t = token_terms(p.shat[(size_t)row * p.n + i], ri, rs.m,
-                                        (float)rs.beta, p.est);
-            f = is_member(make_key(token_gain(t, i, rs, a, l), i), rs);
-          }
-        }
-      }
-      count += f ? 1u : 0u;
-      const unsigned long long m = __ballot(f);
-      const int w0 = (base + k * kBlock + wave * kWave) / 32;
-      if (lane == 0 && w0 < p.nwords) p.fbits[(size_t)bg * p.nwords + w0] = (uint32_t)m;
-      if (lane == 32 && w0 + 1 < p.nwords)
-        p.fbits[(size_t)bg * p.nwords + w0 + 1] = (uint32_t)(m >> 32);
-    }
-  }
-  const uint32_t tot = block_sum<uint32_t>(count, s_red);
-  if (threadIdx.x == 0) p.fcnt[(size_t)bg * p.nch + c] = tot;
-}
-
 template <int GRP>
 __global__ __launch_bounds__(kBlock) void dk_gather(DParams p) {
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int bg = b * p.G + g;
   __shared__ int s_pos[4096];
   __shared__ uint32_t s_red[kBlock / kWave + 1];
-  uint32_t before = 0;
-  for (int i = threadIdx.x; i < c; i += kBlock) before += p.fcnt[(size_t)bg * p.nch + i];
-  const uint32_t offset = block_sum<uint32_t>(before, s_red);
+  // rows fetched before this chunk: population count of the earlier words
   const int wpc = p.chunk / 32;
   const int w0 = c * wpc;
+  uint32_t before = 0;
+  for (int i = threadIdx.x; i < w0; i += kBlock)
+    before += (uint32_t)__popc(p.fbits[(size_t)bg * p.nwords + i]);
+  const uint32_t offset = block_sum<uint32_t>(before, s_red);
   uint32_t total = 0;
   // chunk sizes are at most 4096 tokens (128 words)
   uint32_t word = 0;
@@ -1409,7 +1784,7 @@ template <int GRP>
 __device__ __forceinline__ float resident_alpha(const DParams &p,
                                                 const RowState &rs, int row,
                                                 int pos, float ri, float ell,
-                                                double a, double l) {
+                                                float a, float l) {
   const float w = expf(ell - rs.m);
   if (ri >= 1.0f) return w;
   const Terms t = token_terms(p.shat[(size_t)row * p.n + pos], ri, rs.m,
@@ -1434,10 +1809,10 @@ __global__ __launch_bounds__(kBlock) void dk_attn(DParams p) {
   __shared__ float s_o[kBlock / kWave][GRP][kHeadDim];
   __shared__ float s_d[kBlock / kWave][GRP];
   __shared__ float s_red[kBlock / kWave];
-  __shared__ float s_scale[kBlock / kWave][512];  // ncr + ncf <= 512
+  __shared__ float s_scale[kBlock / kWave][kWave];  // ncr + ncf <= 64
   if (threadIdx.x < GRP) s_rs[threadIdx.x] = p.rows[row_of(p, b, g, threadIdx.x, GRP)];
   __syncthreads();
-  const double a = p.a_delta, l = p.l_delta;
+  const float a = (float)p.a_delta, l = (float)p.l_delta;
   const float *rr = p.r + (size_t)bg * p.n;
   float acc[GRP][8], dsum[GRP], mloc[GRP];
 #pragma unroll
@@ -1584,37 +1959,37 @@ __global__ __launch_bounds__(kBlock) void dk_attn(DParams p) {
     const int h = i / kHeadDim, e = i % kHeadDim;
     float o = 0.0f;
     for (int w = 0; w < kBlock / kWave; ++w) o += s_o[w][h][e];
-    p.apart[(size_t)row_of(p, b, g, h, GRP) * np + x].o[e] = o;
+    p.aparto[((size_t)row_of(p, b, g, h, GRP) * kHeadDim + e) * p.npad + x] = o;
   }
   if (threadIdx.x < GRP) {
     const int h = threadIdx.x;
     float d = 0.0f;
     for (int w = 0; w < kBlock / kWave; ++w) d += s_d[w][h];
-    AttnPart *ap = p.apart + (size_t)row_of(p, b, g, h, GRP) * np + x;
-    ap->d = d;
-    ap->m = mloc[h];
+    p.apart[(size_t)row_of(p, b, g, h, GRP) * np + x] = make_float2(mloc[h], d);
   }
   if (!last_block_arrive(&p.groups[bg].arrive[ARR_ATTN], gridDim.x)) return;
-  // ---- merge the partial softmax sums by log-sum-exp (one wave per head)
+  // ---- merge the partial softmax sums by log-sum-exp (one wave per head);
+  // at most 64 partials, one per lane, and each output dimension reads its
+  // partials as consecutive 16-byte vectors
   for (int h = wave; h < GRP; h += kBlock / kWave) {
     const int row = row_of(p, b, g, h, GRP);
-    const AttnPart *ap = p.apart + (size_t)row * np;
-    float M = -INFINITY;
-    for (int i = lane; i < np; i += kWave)
-      if (ap[i].d > 0.0f) M = fmaxf(M, ap[i].m);
-    M = wave_max(M);
-    float D = 0.0f;
-    for (int i = lane; i < np; i += kWave) {
-      const float sc = ap[i].d > 0.0f ? expf(ap[i].m - M) : 0.0f;
-      s_scale[wave][i] = sc;
-      D += ap[i].d * sc;
-    }
-    D = wave_sum(D);
+    const float2 md = lane < np ? p.apart[(size_t)row * np + lane] : make_float2(0.0f, 0.0f);
+    const float M = wave_max(md.y > 0.0f ? md.x : -INFINITY);
+    const float sc = md.y > 0.0f ? expf(md.x - M) : 0.0f;
+    const float D = wave_sum(md.y * sc);
+    s_scale[wave][lane] = sc;
+    __builtin_amdgcn_wave_barrier();
     for (int e = lane; e < kHeadDim; e += kWave) {
+      const float4 *src = reinterpret_cast<const float4 *>(
+          p.aparto + ((size_t)row * kHeadDim + e) * p.npad);
       float o = 0.0f;
-      for (int i = 0; i < np; ++i) {
-        const float sc = s_scale[wave][i];
-        if (sc != 0.0f) o += ap[i].o[e] * sc;
+      for (int q4 = 0; q4 < p.npad / 4; ++q4) {
+        const float4 v = src[q4];
+        const float *sp = &s_scale[wave][q4 * 4];
+        o += sp[0] != 0.0f ? v.x * sp[0] : 0.0f;
+        o += sp[1] != 0.0f ? v.y * sp[1] : 0.0f;
+        o += sp[2] != 0.0f ? v.z * sp[2] : 0.0f;
+        o += sp[3] != 0.0f ? v.w * sp[3] : 0.0f;
       }
       p.out[(size_t)row * kHeadDim + e] = o / D;
     }
@@ -1645,7 +2020,7 @@ struct PhaseMark {
   void **ev;
   hipStream_t s;
   void operator()(int k) const {
-    if (ev) (void)hipEventRecord(static_cast<hipEvent_t>(ev[k]), s);
+    if (ev && ev[k]) (void)hipEventRecord(static_cast<hipEvent_t>(ev[k]), s);
   }
 };
 
@@ -1666,19 +2041,21 @@ hipError_t run(const DParams &p, hipStream_t s, int sd, void **events) {
   mark(k++);
   dk_resident<GRP><<<gres, blk, 0, s>>>(p);
   mark(k++);
-  for (int lev = 0; lev < 4; ++lev) {
-    dk_beta<GRP><<<gch, blk, 0, s>>>(p, lev);
+  const dim3 grow((unsigned)p.nrc, (unsigned)p.Hq, (unsigned)p.B);
+  const dim3 gone((unsigned)p.Hq, (unsigned)p.B);
+  for (int j = 0; j < kBetaLaunches; ++j) {
+    dk_rbeta<GRP><<<grow, blk, 0, s>>>(p, j);
     mark(k++);
   }
-  dk_cert<GRP><<<gch, blk, 0, s>>>(p);
+  dk_rcert<GRP><<<grow, blk, 0, s>>>(p);
   mark(k++);
-  for (int pass = 0; pass < 3; ++pass) {
-    dk_select<GRP><<<gch, blk, 0, s>>>(p);
-    mark(k++);
-  }
-  dk_finish<GRP><<<dim3((unsigned)GRP, (unsigned)p.G, (unsigned)p.B), blk, 0, s>>>(p);
+  dk_rcount<GRP><<<grow, blk, 0, s>>>(p);
   mark(k++);
-  dk_mark<GRP><<<gch, blk, 0, s>>>(p);
+  dk_rresolve<GRP><<<gone, dim3(kPlanThreads), 0, s>>>(p);
+  mark(k++);
+  dk_rcollect<GRP><<<grow, blk, 0, s>>>(p);
+  mark(k++);
+  dk_rwalk<GRP><<<gone, dim3(kPlanThreads), 0, s>>>(p);
   mark(k++);
   dk_gather<GRP><<<gch, blk, 0, s>>>(p);
   mark(k++);
@@ -1688,8 +2065,8 @@ hipError_t run(const DParams &p, hipStream_t s, int sd, void **events) {
 }
 
 const char *const kPhaseNames[] = {
-    "scan", "resident", "beta0", "beta1", "beta2", "beta3", "cert",
-    "select0", "select1", "select2", "finish", "mark", "gather", "attn"};
+    "scan",  "resident", "beta0",   "beta1",   "beta2", "beta3", "beta4",
+    "cert",  "count",    "resolve", "collect", "walk",  "gather", "attn"};
 
 }  // namespace
 
@@ -1704,16 +2081,17 @@ const char *decode_phase_name(int i) {
 DecodeLayout decode_layout(const vkv_decode_args &a) {
   DecodeLayout L{};
   L.grp = a.n_q_heads / a.n_kv_heads;
-  L.chunk = 512;
+  L.chunk = kChunk;
   L.nch = (a.n_tokens + L.chunk - 1) / L.chunk;
   // workgroups per group for the resident rows and for the fetched rows:
   // about 2048 workgroups per launch in total, at least 64 rows each
   const long long groups_ll = (long long)a.batch * a.n_kv_heads;
   const int target = (int)((2048 + groups_ll - 1) / groups_ll);
   const int rmax = a.cap < a.n_tokens ? a.cap : a.n_tokens;
-  // (each at most 256, so the merge sees at most 512 partial sums)
-  L.ncr = std::max(1, std::min(std::min(target, 256), (rmax + 63) / 64));
-  L.ncf = std::max(1, std::min(std::min(target / 2, 256), (a.fetch_cap + 63) / 64));
+  // (each at most 32, so the merge sees at most 64 partial sums)
+  L.ncr = std::max(1, std::min(std::min(target, 32), (rmax + 63) / 64));
+  L.ncf = std::max(1, std::min(std::min(target, 32), (a.fetch_cap + 63) / 64));
+  L.npad = (L.ncr + L.ncf + 3) / 4 * 4;
   L.nwords = (a.n_tokens + 31) / 32;
   const size_t B = (size_t)a.batch, Hq = (size_t)a.n_q_heads,
                G = (size_t)a.n_kv_heads, n = (size_t)a.n_tokens;
@@ -1727,13 +2105,22 @@ DecodeLayout decode_layout(const vkv_decode_args &a) {
   L.fbits = c.take<uint32_t>(groups * L.nwords);
   L.pmax = c.take<float>(rows * (L.nch + L.ncr));
   L.hpart = c.take<uint32_t>(groups * (L.nch + L.ncr));  // H counts per chunk
-  L.bbins = c.take<double>(rows * 3 * kBetaEdges);
-  L.cpart = c.take<CertPart>(rows * L.nch);
-  L.dpart = c.take<double2>(rows * L.nch);
-  L.sbins = c.take<SelBin>(rows * kSelBins);
-  L.cand = c.take<Cand>(rows * kCand);
-  L.fcnt = c.take<uint32_t>(groups * L.nch);
-  L.apart = c.take<AttnPart>(rows * (L.ncr + L.ncf));
+  L.nrc = (a.n_tokens + kRowChunk - 1) / kRowChunk;
+  L.bpart = c.take<double>(2 * rows * L.nrc * (size_t)kBetaRec);
+  L.bstate = c.take<BetaState>(2 * rows);
+  L.rbeta = c.take<double>(2 * rows);
+  L.cpart = c.take<CertPart>(rows * L.nrc);
+  L.khist = c.take<uint32_t>(rows * L.nrc * (size_t)kSelBinsP);
+  L.tpart = c.take<unsigned long long>(rows * L.nrc * 2);
+  L.sel = c.take<SelState>(rows);
+  L.ccount = c.take<uint32_t>(rows);
+  L.candk = c.take<unsigned long long>(rows * (size_t)kCandMax);
+  L.candb = c.take<unsigned long long>(rows * (size_t)kCandMax);
+  L.candv = c.take<unsigned long long>(rows * (size_t)kCandMax);
+  L.candr = c.take<uint32_t>(rows * (size_t)kCandMax);
+  L.rpart = c.take<uint32_t>(rows * L.nrc);
+  L.apart = c.take<float2>(rows * (L.ncr + L.ncf));
+  L.aparto = c.take<float>(rows * kHeadDim * (size_t)L.npad);
   L.staging = c.take<uint16_t>(groups * (size_t)a.fetch_cap * 2 * kHeadDim);
   L.total = (c.off + 255) & ~size_t(255);
   return L;
@@ -1770,13 +2157,23 @@ hipError_t launch_decode(const vkv_decode_args &a, const DecodeLayout &L,
   p.fbits = at<uint32_t>(w, L.fbits);
   p.pmax = at<float>(w, L.pmax);
   p.hpart = at<uint32_t>(w, L.hpart);
-  p.bbins = at<double>(w, L.bbins);
+  p.bpart = at<double>(w, L.bpart);
+  p.bstate = at<BetaState>(w, L.bstate);
+  p.rbeta = at<double>(w, L.rbeta);
   p.cpart = at<CertPart>(w, L.cpart);
-  p.dpart = at<double2>(w, L.dpart);
-  p.sbins = at<SelBin>(w, L.sbins);
-  p.cand = at<Cand>(w, L.cand);
-  p.fcnt = at<uint32_t>(w, L.fcnt);
-  p.apart = at<AttnPart>(w, L.apart);
+  p.khist = at<uint32_t>(w, L.khist);
+  p.tpart = at<unsigned long long>(w, L.tpart);
+  p.sel = at<SelState>(w, L.sel);
+  p.ccount = at<uint32_t>(w, L.ccount);
+  p.candk = at<unsigned long long>(w, L.candk);
+  p.candb = at<unsigned long long>(w, L.candb);
+  p.candv = at<unsigned long long>(w, L.candv);
+  p.candr = at<uint32_t>(w, L.candr);
+  p.rpart = at<uint32_t>(w, L.rpart);
+  p.nrc = L.nrc;
+  p.apart = at<float2>(w, L.apart);
+  p.aparto = at<float>(w, L.aparto);
+  p.npad = L.npad;
   p.staging = at<uint16_t>(w, L.staging);
   p.B = a.batch;
   p.Hq = a.n_q_heads;

@@ -289,12 +289,14 @@ class DecodeStep:
         return self
 
     def set_phase_events(self, events):
-        """Attach phase_count()+1 recorded torch.cuda.Event objects (or None)."""
+        """Attach phase_count()+1 torch.cuda.Event objects (or None); None
+        entries of the list are skipped by the library."""
         if events is None:
             self._ev = None
             self.args.phase_events = None
             return
-        self._ev = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+        self._ev = (ctypes.c_void_p * len(events))(
+            *[None if e is None else e.cuda_event for e in events])
         self.args.phase_events = ctypes.cast(self._ev, ctypes.c_void_p)
 
     def launch(self, stream=None):
