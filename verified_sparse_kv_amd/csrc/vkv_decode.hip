@@ -219,16 +219,6 @@ __device__ __forceinline__ T wave_incl_scan(T v, int lane) {
   return v;
 }
 
-// Inclusive prefix maximum over the lanes of a wave.
-__device__ __forceinline__ uint32_t wave_incl_max(uint32_t v, int lane) {
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) {
-    const uint32_t o = __shfl_up(v, m, kWave);
-    if (lane >= m) v = max(v, o);
-  }
-  return v;
-}
-
 // ------------------------------------------------------------ dk_scan
 template <int GRP, int SD>
 __global__ __launch_bounds__(kBlock) void dk_scan(DParams p) {
@@ -601,49 +591,102 @@ __device__ __forceinline__ void top2_merge(float &x1, int &p1, float &x2,
   }
 }
 
-// Block-wide sums of NV values for THREADS threads in a fixed order; every
-// thread gets the totals. `red` holds (THREADS / 64 + 1) * NV entries.
-template <typename T, int NV, int THREADS>
-__device__ __forceinline__ void blk_reduce(T (&v)[NV], T *red) {
-  constexpr int W = THREADS / kWave;
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+// Block-wide combination of NV values per thread for THREADS threads, in a
+// fixed order, through LDS only (cross-lane shuffles are slow on this path):
+// every thread stores its values, 16 threads per value fold a sixteenth each
+// (stride 16, so a wave reads consecutive words), and NV threads fold the
+// sixteen partials. Every thread gets the results; the same inputs give the
+// same bits in every workgroup.
+template <typename T>
+struct OpSum {
+  __device__ static T f(T a, T b) { return a + b; }
+};
+template <typename T>
+struct OpMax {
+  __device__ static T f(T a, T b) { return a > b ? a : b; }
+};
+template <typename T, int NV, int THREADS, typename OP>
+__device__ __forceinline__ void blk_combine(T (&v)[NV]) {
+  static_assert(NV * 16 <= THREADS && THREADS % 16 == 0, "shape");
+  constexpr int LD = THREADS + 8;  // pitch between values: spreads the banks
+  __shared__ T buf[NV * LD + NV * 16 + NV];
+  T *part = buf + NV * LD;
+  T *tot = part + NV * 16;
+  __syncthreads();  // an earlier call may still be reading tot
 #pragma unroll
-  for (int k = 0; k < NV; ++k) v[k] = wave_sum(v[k]);
+  for (int k = 0; k < NV; ++k) buf[k * LD + threadIdx.x] = v[k];
   __syncthreads();
-  if (lane == 0) {
-#pragma unroll
-    for (int k = 0; k < NV; ++k) red[wave * NV + k] = v[k];
+  if (threadIdx.x < NV * 16) {
+    const int k = threadIdx.x / 16, j = threadIdx.x % 16;
+    T acc = buf[k * LD + j];
+    for (int i = 1; i < THREADS / 16; ++i) acc = OP::f(acc, buf[k * LD + i * 16 + j]);
+    part[k * 16 + j] = acc;
   }
   __syncthreads();
   if (threadIdx.x < NV) {
-    T t = red[threadIdx.x];
-    for (int w = 1; w < W; ++w) t += red[w * NV + threadIdx.x];
-    red[W * NV + threadIdx.x] = t;
+    T acc = part[threadIdx.x * 16];
+    for (int j = 1; j < 16; ++j) acc = OP::f(acc, part[threadIdx.x * 16 + j]);
+    tot[threadIdx.x] = acc;
   }
   __syncthreads();
 #pragma unroll
-  for (int k = 0; k < NV; ++k) v[k] = red[W * NV + k];
+  for (int k = 0; k < NV; ++k) v[k] = tot[k];
+}
+template <typename T, int NV, int THREADS>
+__device__ __forceinline__ void blk_reduce(T (&v)[NV]) {
+  blk_combine<T, NV, THREADS, OpSum<T>>(v);
 }
 template <typename T, int NV>
-__device__ __forceinline__ void plan_reduce(T (&v)[NV], T *red) {
-  blk_reduce<T, NV, kPlanThreads>(v, red);
+__device__ __forceinline__ void plan_reduce(T (&v)[NV]) {
+  blk_combine<T, NV, kPlanThreads, OpSum<T>>(v);
 }
-
-// Block-wide maximum for THREADS threads; `scratch` holds THREADS / 64.
 template <typename T, int THREADS>
-__device__ __forceinline__ T blk_max(T v, T *scratch) {
-  v = wave_max(v);
-  __syncthreads();
-  if (threadIdx.x % kWave == 0) scratch[threadIdx.x / kWave] = v;
-  __syncthreads();
-  T t = scratch[0];
-#pragma unroll
-  for (int i = 1; i < THREADS / kWave; ++i) t = scratch[i] > t ? scratch[i] : t;
-  return t;
+__device__ __forceinline__ T blk_max(T x) {
+  T v[1] = {x};
+  blk_combine<T, 1, THREADS, OpMax<T>>(v);
+  return v[0];
 }
 template <typename T>
-__device__ __forceinline__ T plan_max(T v, T *scratch) {
-  return blk_max<T, kPlanThreads>(v, scratch);
+__device__ __forceinline__ T plan_max(T x) {
+  return blk_max<T, kPlanThreads>(x);
+}
+
+// Block-wide top two of (value, position) pairs as top2_merge keeps them
+// (the merge does not depend on order), through LDS.
+template <int THREADS>
+__device__ __forceinline__ void blk_top2(float &x1, int &p1, float &x2) {
+  __shared__ float b1[THREADS + 17], b2[THREADS + 17];
+  __shared__ int bp[THREADS + 17];
+  __syncthreads();
+  b1[threadIdx.x] = x1;
+  b2[threadIdx.x] = x2;
+  bp[threadIdx.x] = p1;
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    float y1 = b1[threadIdx.x], y2 = b2[threadIdx.x];
+    int yq = bp[threadIdx.x];
+    for (int i = 1; i < THREADS / 16; ++i) {
+      const int t = i * 16 + threadIdx.x;
+      top2_merge(y1, yq, y2, b1[t], bp[t], b2[t]);
+    }
+    b1[THREADS + threadIdx.x] = y1;
+    b2[THREADS + threadIdx.x] = y2;
+    bp[THREADS + threadIdx.x] = yq;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float y1 = b1[THREADS], y2 = b2[THREADS];
+    int yq = bp[THREADS];
+    for (int j = 1; j < 16; ++j)
+      top2_merge(y1, yq, y2, b1[THREADS + j], bp[THREADS + j], b2[THREADS + j]);
+    b1[THREADS + 16] = y1;
+    b2[THREADS + 16] = y2;
+    bp[THREADS + 16] = yq;
+  }
+  __syncthreads();
+  x1 = b1[THREADS + 16];
+  x2 = b2[THREADS + 16];
+  p1 = bp[THREADS + 16];
 }
 
 // LDS of the streaming selection: the count histogram, then the collected
@@ -737,7 +780,7 @@ __device__ void select_row(const DParams &p, int row, int bg, RowState &rs,
       });
       if (first && d == 0) {
         unsigned long long tv2[2] = {lb_, lv_};
-        plan_reduce<unsigned long long, 2>(tv2, s_u);
+        plan_reduce<unsigned long long, 2>(tv2);
         tot_b = tv2[0];
         tot_v = tv2[1];
       }
@@ -825,8 +868,8 @@ __device__ void select_row(const DParams &p, int row, int bg, RowState &rs,
       }
     });
     unsigned long long cs[2] = {cb_, cv_};
-    plan_reduce<unsigned long long, 2>(cs, s_u);
-    below_max = plan_max<uint32_t>(below_max, s_m);
+    plan_reduce<unsigned long long, 2>(cs);
+    below_max = plan_max<uint32_t>(below_max);
     const int nc = (int)min(s_cnt, (uint32_t)kCand);
     const double e_below =
         eps_of((double)(tot_b - fet_b - cs[0]) * sbs,
@@ -937,7 +980,7 @@ __device__ void select_row(const DParams &p, int row, int bg, RowState &rs,
       }
     }
     int first_k = best;
-    first_k = -plan_max<int>(-first_k, s_j);
+    first_k = -plan_max<int>(-first_k);
     // (fetching every candidate certifies, so first_k < nc; the guard keeps
     // the state sane if rounding ever said otherwise)
     const int kk = first_k < nc ? first_k : nc - 1;
@@ -964,21 +1007,26 @@ __device__ void select_row(const DParams &p, int row, int bg, RowState &rs,
 
 
 // ------------------------------------------------------------ row passes
-// This thread's tokens of chunk c of a row: r and w~ = exp(s - m) (0, with
-// r = 1, outside L or past n). Token u is c * kRowChunk + u * kBlock + tid.
-__device__ __forceinline__ void row_tokens(const DParams &p, int row, int bg,
-                                           int c, float m,
-                                           float (&w8)[kRowTok],
-                                           float (&r8)[kRowTok]) {
+// This thread's tokens of chunk c of a row: r and the planning logit s (r = 1
+// past n). Token u is c * kRowChunk + u * kBlock + tid. The kernels issue
+// these loads first and their other loads right after, so that they wait
+// for memory once.
+__device__ __forceinline__ void row_load(const DParams &p, int row, int bg,
+                                         int c, float (&r8)[kRowTok],
+                                         float (&s8)[kRowTok]) {
   const float *rr = p.r + (size_t)bg * p.n;
   const float *sh = p.shat + (size_t)row * p.n;
-  float s8[kRowTok];
 #pragma unroll
   for (int u = 0; u < kRowTok; ++u) {
     const int i = c * kRowChunk + u * kBlock + (int)threadIdx.x;
     r8[u] = i < p.n ? rr[i] : 1.0f;
     s8[u] = i < p.n ? sh[i] : 0.0f;
   }
+}
+// w~ = exp(s - m) on L, 0 elsewhere.
+__device__ __forceinline__ void row_weights(float m, const float (&r8)[kRowTok],
+                                            const float (&s8)[kRowTok],
+                                            float (&w8)[kRowTok]) {
 #pragma unroll
   for (int u = 0; u < kRowTok; ++u) w8[u] = r8[u] < 1.0f ? expf(s8[u] - m) : 0.0f;
 }
@@ -1071,25 +1119,27 @@ __device__ __forceinline__ void beta_accumulate(const double (&pts)[kBetaPts],
   }
 }
 
-// Fixed-order totals of a row's S records; slot `max_slot` (>= 0) is
-// combined by maximum. The same in every workgroup.
-__device__ __forceinline__ void combine_beta(const double *rec, int S,
-                                             int max_slot,
-                                             double (&tot)[kBetaRec],
-                                             double *red, double *mscr) {
+// This thread's share (records t, t + kBlock, ...) of a row's S chunk
+// records; with LB, slot 3 (the lower bound of pass 0) combines by maximum.
+template <bool LB>
+__device__ __forceinline__ void beta_rec_load(const double *rec, int S,
+                                              double (&v)[kBetaRec]) {
 #pragma unroll
-  for (int k = 0; k < kBetaRec; ++k) tot[k] = 0.0;
-  double mx = 0.0;
+  for (int k = 0; k < kBetaRec; ++k) v[k] = 0.0;
   for (int t = threadIdx.x; t < S; t += kBlock) {
 #pragma unroll
     for (int k = 0; k < kBetaRec; ++k) {
       const double x = rec[(size_t)t * kBetaRec + k];
-      if (k == max_slot) mx = fmax(mx, x);
-      else tot[k] += x;
+      v[k] = (LB && k == 3) ? fmax(v[k], x) : v[k] + x;
     }
   }
-  blk_reduce<double, kBetaRec, kBlock>(tot, red);
-  if (max_slot >= 0) tot[max_slot] = blk_max<double, kBlock>(mx, mscr);
+}
+// Fixed-order totals of the shares: the same in every workgroup.
+template <bool LB>
+__device__ __forceinline__ void beta_rec_total(double (&v)[kBetaRec]) {
+  const double mx = v[3];
+  blk_reduce<double, kBetaRec, kBlock>(v);
+  if (LB) v[3] = blk_max<double, kBlock>(mx);
 }
 
 // Pass `pass` of the beta* iteration: 0 is pass 0, later ones are Newton
@@ -1099,11 +1149,20 @@ __global__ __launch_bounds__(kBlock) void dk_rbeta(DParams p, int pass) {
   const int c = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
   const int row = b * p.Hq + hq, bg = b * p.G + hq / GRP;
   const size_t rows = (size_t)p.B * p.Hq;
-  __shared__ double s_red[(kBlock / kWave + 1) * kBetaRec];
-  __shared__ double s_mx[kBlock / kWave];
+  float w8[kRowTok], r8[kRowTok], s8[kRowTok];
+  row_load(p, row, bg, c, r8, s8);
   const float m = p.rows[row].m;
-  float w8[kRowTok], r8[kRowTok];
-  row_tokens(p, row, bg, c, m, w8, r8);
+  // the previous pass: this thread's share of the records, and the state
+  const int q = (pass - 1) & 1;
+  double rv[kBetaRec];
+  BetaState st{};
+  if (pass >= 1) {
+    const double *rec = p.bpart + ((size_t)q * rows + row) * p.nrc * kBetaRec;
+    if (pass == 1) beta_rec_load<true>(rec, p.nrc, rv);
+    else beta_rec_load<false>(rec, p.nrc, rv);
+    if (pass >= 2) st = p.bstate[(size_t)q * rows + row];
+  }
+  row_weights(m, r8, s8, w8);
   double v[kBetaRec];
 #pragma unroll
   for (int k = 0; k < kBetaRec; ++k) v[k] = 0.0;
@@ -1131,28 +1190,20 @@ __global__ __launch_bounds__(kBlock) void dk_rbeta(DParams p, int pass) {
         if (pos >= 0 && pos < p.n && rr[pos] >= 1.0f) v[4] += (double)expf(e - m);
       }
     }
-    blk_reduce<double, kBetaRec, kBlock>(v, s_red);
-    lb = blk_max<double, kBlock>(lb, s_mx);
+    blk_reduce<double, kBetaRec, kBlock>(v);
+    lb = blk_max<double, kBlock>(lb);
     if (threadIdx.x == 0) {
 #pragma unroll
       for (int k = 0; k < kBetaRec; ++k) out[k] = k == 3 ? lb : v[k];
     }
     return;
   }
-  const int q = (pass - 1) & 1;
-  const double *rec = p.bpart + ((size_t)q * rows + row) * p.nrc * kBetaRec;
-  BetaState st;
   if (pass == 1) {
-    double tot[kBetaRec];
-    combine_beta(rec, p.nrc, 3, tot, s_red, s_mx);
-    st = beta_init(tot, p.est);
-  } else {
-    st = p.bstate[(size_t)q * rows + row];
-    if (!st.done) {
-      double tot[kBetaRec];
-      combine_beta(rec, p.nrc, -1, tot, s_red, s_mx);
-      st = beta_advance(st, tot);
-    }
+    beta_rec_total<true>(rv);
+    st = beta_init(rv, p.est);
+  } else if (!st.done) {
+    beta_rec_total<false>(rv);
+    st = beta_advance(st, rv);
   }
   if (c == 0 && threadIdx.x == 0) p.bstate[(size_t)(pass & 1) * rows + row] = st;
   if (st.done) return;
@@ -1160,7 +1211,7 @@ __global__ __launch_bounds__(kBlock) void dk_rbeta(DParams p, int pass) {
   beta_points(st, pts);
 #pragma unroll
   for (int u = 0; u < kRowTok; ++u) beta_accumulate(pts, w8[u], r8[u], v);
-  blk_reduce<double, kBetaRec, kBlock>(v, s_red);
+  blk_reduce<double, kBetaRec, kBlock>(v);
   if (threadIdx.x == 0) {
 #pragma unroll
     for (int k = 0; k < kBetaRec; ++k) out[k] = v[k];
@@ -1174,21 +1225,18 @@ __global__ __launch_bounds__(kBlock) void dk_rcert(DParams p) {
   const int c = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
   const int row = b * p.Hq + hq, bg = b * p.G + hq / GRP;
   const size_t rows = (size_t)p.B * p.Hq;
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  __shared__ double s_red[(kBlock / kWave + 1) * kBetaRec];
-  __shared__ double s_mx[kBlock / kWave];
-  __shared__ float s_f1[kBlock / kWave], s_f2[kBlock / kWave];
-  __shared__ int s_i[kBlock / kWave];
+  float w8[kRowTok], r8[kRowTok], s8[kRowTok];
+  row_load(p, row, bg, c, r8, s8);
   const float m = p.rows[row].m;
-  float w8[kRowTok], r8[kRowTok];
-  row_tokens(p, row, bg, c, m, w8, r8);
   const int q = (kBetaLaunches - 1) & 1;
+  double rv[kBetaRec];
+  beta_rec_load<false>(p.bpart + ((size_t)q * rows + row) * p.nrc * kBetaRec,
+                       p.nrc, rv);
   BetaState st = p.bstate[(size_t)q * rows + row];
+  row_weights(m, r8, s8, w8);
   if (!st.done) {
-    double tot[kBetaRec];
-    combine_beta(p.bpart + ((size_t)q * rows + row) * p.nrc * kBetaRec, p.nrc,
-                 -1, tot, s_red, s_mx);
-    st = beta_advance(st, tot);
+    beta_rec_total<false>(rv);
+    st = beta_advance(st, rv);
   }
   if (!st.done) {
     // rare: more Newton passes, each over the whole row by this workgroup
@@ -1203,7 +1251,7 @@ __global__ __launch_bounds__(kBlock) void dk_rcert(DParams p) {
         const float ri = rr[i];
         if (ri < 1.0f) beta_accumulate(pts, expf(sh[i] - m), ri, v);
       }
-      blk_reduce<double, kBetaRec, kBlock>(v, s_red);
+      blk_reduce<double, kBetaRec, kBlock>(v);
       st = beta_advance(st, v);
     }
     if (!st.done) st.beta = st.lo;
@@ -1225,73 +1273,59 @@ __global__ __launch_bounds__(kBlock) void dk_rcert(DParams p) {
     cv[1] += (double)t.vi;
     top2_merge(x1, p1, x2, t.rb, row_pos(c, u), 0.0f);
   }
-  blk_reduce<double, 2, kBlock>(cv, s_red);
-#pragma unroll
-  for (int s2 = 32; s2 >= 1; s2 >>= 1) {
-    const float o1 = shfl_xor(x1, s2), o2 = shfl_xor(x2, s2);
-    const int oq = shfl_xor(p1, s2);
-    top2_merge(x1, p1, x2, o1, oq, o2);
-  }
-  if (lane == 0) {
-    s_f1[wave] = x1;
-    s_f2[wave] = x2;
-    s_i[wave] = p1;
-  }
-  __syncthreads();
+  blk_reduce<double, 2, kBlock>(cv);
+  blk_top2<kBlock>(x1, p1, x2);
   if (threadIdx.x == 0) {
-    float y1 = s_f1[0], y2 = s_f2[0];
-    int yq = s_i[0];
-    for (int w = 1; w < kBlock / kWave; ++w) top2_merge(y1, yq, y2, s_f1[w], s_i[w], s_f2[w]);
     CertPart cp;
     cp.tb = cv[0];
     cp.tv = cv[1];
-    cp.x1 = y1;
-    cp.x2 = y2;
-    cp.p1 = yq;
+    cp.x1 = x1;
+    cp.x2 = x2;
+    cp.p1 = p1;
     cp.pad = 0;
     p.cpart[(size_t)row * p.nrc + c] = cp;
   }
 }
 
-// The certificate of a row from its chunk records: every workgroup of the
-// row computes the same RowState.
-__device__ __forceinline__ void row_certificate(const DParams &p, int row,
-                                                RowState &rs, double *red,
-                                                float *f1, float *f2, int *pi) {
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  double cv[2] = {0.0, 0.0};
-  float x1 = 0.0f, x2 = 0.0f;
-  int p1 = 0x7fffffff;
+// This thread's share of a row's certificate records.
+struct CertShare {
+  double cv[2];
+  float x1, x2;
+  int p1;
+};
+__device__ __forceinline__ CertShare cert_rec_load(const DParams &p, int row) {
+  CertShare z;
+  z.cv[0] = z.cv[1] = 0.0;
+  z.x1 = z.x2 = 0.0f;
+  z.p1 = 0x7fffffff;
   for (int t = threadIdx.x; t < p.nrc; t += kBlock) {
     const CertPart cp = p.cpart[(size_t)row * p.nrc + t];
-    cv[0] += cp.tb;
-    cv[1] += cp.tv;
-    top2_merge(x1, p1, x2, cp.x1, cp.p1, cp.x2);
+    z.cv[0] += cp.tb;
+    z.cv[1] += cp.tv;
+    top2_merge(z.x1, z.p1, z.x2, cp.x1, cp.p1, cp.x2);
   }
-  blk_reduce<double, 2, kBlock>(cv, red);
-#pragma unroll
-  for (int s2 = 32; s2 >= 1; s2 >>= 1) {
-    const float o1 = shfl_xor(x1, s2), o2 = shfl_xor(x2, s2);
-    const int oq = shfl_xor(p1, s2);
-    top2_merge(x1, p1, x2, o1, oq, o2);
-  }
-  if (lane == 0) {
-    f1[wave] = x1;
-    f2[wave] = x2;
-    pi[wave] = p1;
-  }
-  __syncthreads();
+  return z;
+}
+
+// The certificate of a row from its chunk records (this thread's share in
+// `sh`): every workgroup of the row computes the same RowState.
+__device__ __forceinline__ void row_certificate(const DParams &p, CertShare sh,
+                                                float m, double beta,
+                                                double dnorm, RowState &rs) {
+  double cv[2] = {sh.cv[0], sh.cv[1]};
+  float x1 = sh.x1, x2 = sh.x2;
+  int p1 = sh.p1;
+  blk_reduce<double, 2, kBlock>(cv);
+  blk_top2<kBlock>(x1, p1, x2);
   if (threadIdx.x == 0) {
-    float y1 = f1[0], y2 = f2[0];
-    int yq = pi[0];
-    for (int w = 1; w < kBlock / kWave; ++w) top2_merge(y1, yq, y2, f1[w], pi[w], f2[w]);
+    const float y1 = x1, y2 = x2;
+    const int yq = p1;
     const double a = p.a_delta, l = p.l_delta;
     const double tb = cv[0], tv = cv[1];
-    const double dnorm = p.rbeta[2 * row + 1];
     RowState z{};
-    z.m = p.rows[row].m;
+    z.m = m;
     z.dnorm = dnorm;
-    z.beta = p.rbeta[2 * row];
+    z.beta = beta;
     z.betaL = tb;
     z.VL = tv;
     z.b1 = y1;
@@ -1324,16 +1358,15 @@ __global__ __launch_bounds__(kBlock) void dk_rcount(DParams p) {
   const int c = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
   const int row = b * p.Hq + hq, bg = b * p.G + hq / GRP;
   __shared__ RowState rs;
-  __shared__ double s_red[(kBlock / kWave + 1) * 2];
-  __shared__ unsigned long long s_ured[(kBlock / kWave + 1) * 2];
-  __shared__ float s_f1[kBlock / kWave], s_f2[kBlock / kWave];
-  __shared__ int s_i[kBlock / kWave];
   __shared__ uint32_t s_hist[kSelBinsP];
+  float w8[kRowTok], r8[kRowTok], s8[kRowTok];
+  row_load(p, row, bg, c, r8, s8);
   const float m = p.rows[row].m;
-  float w8[kRowTok], r8[kRowTok];
-  row_tokens(p, row, bg, c, m, w8, r8);
+  const CertShare cs = cert_rec_load(p, row);
+  const double beta = p.rbeta[2 * row], dnorm = p.rbeta[2 * row + 1];
   for (int i = threadIdx.x; i < kSelBinsP; i += kBlock) s_hist[i] = 0u;
-  row_certificate(p, row, rs, s_red, s_f1, s_f2, s_i);
+  row_weights(m, r8, s8, w8);
+  row_certificate(p, cs, m, beta, dnorm, rs);
   if (c == 0 && threadIdx.x == 0) p.rows[row] = rs;
   if (!rs.fetch) return;
   const float betaf = (float)rs.beta;
@@ -1350,7 +1383,7 @@ __global__ __launch_bounds__(kBlock) void dk_rcount(DParams p) {
     tx[0] += to_fx(t.bi, eb);
     tx[1] += to_fx(t.vi, ev);
   }
-  blk_reduce<unsigned long long, 2, kBlock>(tx, s_ured);
+  blk_reduce<unsigned long long, 2, kBlock>(tx);
   if (threadIdx.x == 0) {
     p.tpart[((size_t)row * p.nrc + c) * 2] = tx[0];
     p.tpart[((size_t)row * p.nrc + c) * 2 + 1] = tx[1];
@@ -1366,11 +1399,9 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rresolve(DParams p) {
   const int hq = blockIdx.x, b = blockIdx.y;
   const int row = b * p.Hq + hq;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  __shared__ unsigned long long s_u[(kPlanWaves + 1) * 2];
   __shared__ uint32_t s_w[kPlanWaves];
-  __shared__ int s_j[kPlanWaves];
   __shared__ uint32_t s_take;
-  if (!p.rows[row].fetch) return;
+  const int fetch = p.rows[row].fetch;
   // bins 2t and 2t + 1 of this thread, summed over the chunks
   uint32_t h0 = 0u, h1 = 0u;
   const uint32_t *hp = p.khist + (size_t)row * p.nrc * kSelBinsP;
@@ -1384,7 +1415,8 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rresolve(DParams p) {
     tot[0] += p.tpart[((size_t)row * p.nrc + s) * 2];
     tot[1] += p.tpart[((size_t)row * p.nrc + s) * 2 + 1];
   }
-  plan_reduce<unsigned long long, 2>(tot, s_u);
+  if (!fetch) return;
+  plan_reduce<unsigned long long, 2>(tot);
   // keys in bins above this thread's: suffix sums over threads
   const uint32_t mine = h0 + h1;
   uint32_t suf = mine;  // inclusive suffix within the wave
@@ -1400,7 +1432,7 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rresolve(DParams p) {
   int j = kSelBinsP;
   if (c0 <= (uint32_t)kCandMax) j = 2 * threadIdx.x;
   else if (c1 <= (uint32_t)kCandMax) j = 2 * threadIdx.x + 1;
-  const int j0 = -plan_max<int>(-j, s_j);
+  const int j0 = -plan_max<int>(-j);
   if (j0 < kSelBinsP && (j0 >> 1) == (int)threadIdx.x) s_take = (j0 & 1) ? c1 : c0;
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -1423,15 +1455,14 @@ __global__ __launch_bounds__(kBlock) void dk_rcollect(DParams p) {
   const int row = b * p.Hq + hq, bg = b * p.G + hq / GRP;
   __shared__ RowState rs;
   __shared__ uint32_t s_scan[kBlock / kWave + 1];
-  __shared__ uint32_t s_m[kBlock / kWave];
   __shared__ uint32_t s_base;
+  float w8[kRowTok], r8[kRowTok], s8[kRowTok];
+  row_load(p, row, bg, c, r8, s8);
   if (threadIdx.x == 0) rs = p.rows[row];
-  const float m = p.rows[row].m;
-  float w8[kRowTok], r8[kRowTok];
-  row_tokens(p, row, bg, c, m, w8, r8);
+  const unsigned long long lo_key = p.sel[row].lo_key;
   __syncthreads();
   if (!rs.fetch) return;
-  const unsigned long long lo_key = p.sel[row].lo_key;
+  row_weights(rs.m, r8, s8, w8);
   const float betaf = (float)rs.beta;
   const float af = (float)p.a_delta, lf = (float)p.l_delta;
   unsigned long long key8[kRowTok];
@@ -1449,7 +1480,7 @@ __global__ __launch_bounds__(kBlock) void dk_rcollect(DParams p) {
   uint32_t total;
   const uint32_t off = block_exclusive_scan(cnt, s_scan, &total);
   if (threadIdx.x == 0) s_base = total ? atomicAdd(p.ccount + row, total) : 0u;
-  below = blk_max<uint32_t, kBlock>(below, s_m);
+  below = blk_max<uint32_t, kBlock>(below);
   if (threadIdx.x == 0) p.rpart[(size_t)row * p.nrc + c] = below;
   const uint32_t base = s_base + off;
   if (cnt == 0u) return;
@@ -1517,27 +1548,41 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rwalk(DParams p) {
   __shared__ WalkLds lds;
   __shared__ RowState rs;
   __shared__ WalkState ws;
-  __shared__ unsigned long long s_u[(kPlanWaves + 1) * 2];
-  __shared__ uint32_t s_m[kPlanWaves];
+  // every load first: the row, the chunk maxima and all candidate slots
+  // (those past the count are read but not used)
+  constexpr int PT = kCandMax / kPlanThreads;
+  const size_t cb0 = (size_t)row * kCandMax;
   if (threadIdx.x == 0) rs = p.rows[row];
-  __syncthreads();
-  if (!rs.fetch) return;
   const SelState ss = p.sel[row];
   const uint32_t ncount = p.ccount[row];
-  const int nc = (int)min(ncount, (uint32_t)kCandMax);
-  const double a = p.a_delta, l = p.l_delta;
-  const double sbs = ldexp(1.0, -rs.eb), svs = ldexp(1.0, -rs.ev);
-  const size_t cb0 = (size_t)row * kCandMax;
   uint32_t below = 0u;
   for (int s = threadIdx.x; s < p.nrc; s += kPlanThreads)
     below = max(below, p.rpart[(size_t)row * p.nrc + s]);
-  below = plan_max<uint32_t>(below, s_m);
-  unsigned long long cs[2] = {0ull, 0ull};
-  for (int k = threadIdx.x; k < nc; k += kPlanThreads) {
-    cs[0] += p.candb[cb0 + k];
-    cs[1] += p.candv[cb0 + k];
+  unsigned long long ck[PT], cbx[PT], cvx[PT];
+  uint32_t crb[PT];
+#pragma unroll
+  for (int q = 0; q < PT; ++q) {
+    const size_t at = cb0 + threadIdx.x + (size_t)q * kPlanThreads;
+    ck[q] = p.candk[at];
+    cbx[q] = p.candb[at];
+    cvx[q] = p.candv[at];
+    crb[q] = p.candr[at];
   }
-  plan_reduce<unsigned long long, 2>(cs, s_u);
+  __syncthreads();
+  if (!rs.fetch) return;
+  const int nc = (int)min(ncount, (uint32_t)kCandMax);
+  const double a = p.a_delta, l = p.l_delta;
+  const double sbs = ldexp(1.0, -rs.eb), svs = ldexp(1.0, -rs.ev);
+  below = plan_max<uint32_t>(below);
+  unsigned long long cs[2] = {0ull, 0ull};
+#pragma unroll
+  for (int q = 0; q < PT; ++q) {
+    if ((int)threadIdx.x + q * kPlanThreads < nc) {
+      cs[0] += cbx[q];
+      cs[1] += cvx[q];
+    }
+  }
+  plan_reduce<unsigned long long, 2>(cs);
   // fetching every candidate leaves exactly the tokens below lo
   const double e_below =
       eps_of((double)(ss.tot_b - cs[0]) * sbs, (double)(ss.tot_v - cs[1]) * svs,
@@ -1550,17 +1595,19 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rwalk(DParams p) {
     return;
   }
   unsigned long long kmin = ~0ull, kmax = 0ull;
-  for (int k = threadIdx.x; k < nc; k += kPlanThreads) {
-    const unsigned long long key = p.candk[cb0 + k];
-    lds.c.key[k] = key;
-    lds.c.bfx[k] = p.candb[cb0 + k];
-    lds.c.vfx[k] = p.candv[cb0 + k];
-    lds.c.rb[k] = p.candr[cb0 + k];
-    kmin = min(kmin, key);
-    kmax = max(kmax, key);
+#pragma unroll
+  for (int q = 0; q < PT; ++q) {
+    const int k = (int)threadIdx.x + q * kPlanThreads;
+    if (k >= nc) continue;
+    lds.c.key[k] = ck[q];
+    lds.c.bfx[k] = cbx[q];
+    lds.c.vfx[k] = cvx[q];
+    lds.c.rb[k] = crb[q];
+    kmin = min(kmin, ck[q]);
+    kmax = max(kmax, ck[q]);
   }
-  kmax = plan_max<unsigned long long>(kmax, s_u);
-  kmin = ~plan_max<unsigned long long>(~kmin, s_u);
+  kmax = plan_max<unsigned long long>(kmax);
+  kmin = ~plan_max<unsigned long long>(~kmin);
   if (threadIdx.x == 0) {
     // the first digit starts where the candidates' keys start to differ
     const int span = kmax == kmin ? 0 : 64 - __clzll((long long)(kmax ^ kmin));
@@ -1626,11 +1673,9 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rwalk(DParams p) {
       // the lane's highest bin whose fetched-through eps^ is below eps
       int best = -1;
       {
-        uint32_t c = sc;
         unsigned long long fb = ws.ab + sb, fv = ws.av + sv;
         for (int q = PER - 1; q >= 0 && best < 0; --q) {
           const WalkBin &x = lds.c.bin[lane * PER + q];
-          c += x.cnt;
           fb += x.bsum;
           fv += x.vsum;
           uint32_t mb = mlow;
@@ -1706,71 +1751,81 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rwalk(DParams p) {
 }
 
 // ------------------------------------------------------------ fetch
-template <int GRP>
-__global__ __launch_bounds__(kBlock) void dk_gather(DParams p) {
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+// Workgroups per KV head that copy fetched rows: enough host loads in
+// flight for the link, few enough that most compute units stay free for the
+// attention over the resident rows running in the same launch (host loads
+// queued in a compute unit delay every other load issued there).
+constexpr int kGatherWG = 8;
+
+// Gather by workgroup j of a KV head: chunks [j nch / kGatherWG, (j + 1) nch
+// / kGatherWG) of the fetch bitmap in order; for each, its part of the
+// ascending fetch list and its rows, copied from pinned host memory by GPU
+// loads (zero-copy) into device staging.
+__device__ __forceinline__ void gather_part(const DParams &p, int j, int g,
+                                            int b) {
   const int bg = b * p.G + g;
   __shared__ int s_pos[4096];
   __shared__ uint32_t s_red[kBlock / kWave + 1];
-  // rows fetched before this chunk: population count of the earlier words
+  int c0, c1;
+  split_range(p.nch, kGatherWG, j, c0, c1);
   const int wpc = p.chunk / 32;
-  const int w0 = c * wpc;
+  const uint32_t *fb = p.fbits + (size_t)bg * p.nwords;
+  // rows fetched before the first chunk: population count of earlier words
   uint32_t before = 0;
-  for (int i = threadIdx.x; i < w0; i += kBlock)
-    before += (uint32_t)__popc(p.fbits[(size_t)bg * p.nwords + i]);
-  const uint32_t offset = block_sum<uint32_t>(before, s_red);
-  uint32_t total = 0;
-  // chunk sizes are at most 4096 tokens (128 words)
-  uint32_t word = 0;
-  if ((int)threadIdx.x < wpc && w0 + (int)threadIdx.x < p.nwords)
-    word = p.fbits[(size_t)bg * p.nwords + w0 + threadIdx.x];
-  const uint32_t at0 = block_exclusive_scan<uint32_t>((uint32_t)__popc(word), s_red, &total);
-  {
-    uint32_t w = word, o = at0;
-    while (w) {
-      const int bit = __ffs(w) - 1;
-      s_pos[o++] = (w0 + (int)threadIdx.x) * 32 + bit;
-      w &= w - 1;
-    }
-  }
-  __syncthreads();
-  int32_t *fidx = p.fidx + (size_t)bg * p.fetch_cap;
-  for (uint32_t k = threadIdx.x; k < total; k += kBlock) {
-    const uint32_t slot = offset + k;
-    if (slot < (uint32_t)p.fetch_cap) fidx[slot] = s_pos[k];
-  }
-  // copy host rows (K then V, 512 bytes) into staging, 16 bytes per lane;
-  // four rows' worth of loads are issued before their stores
+  for (int i = threadIdx.x; i < c0 * wpc && i < p.nwords; i += kBlock)
+    before += (uint32_t)__popc(fb[i]);
+  uint32_t offset = block_sum<uint32_t>(before, s_red);
   const uint16_t *src_base = p.host_kv + (size_t)bg * p.n * 2 * kHeadDim;
   uint16_t *dst_base = p.staging + (size_t)bg * p.fetch_cap * 2 * kHeadDim;
-  const uint32_t units = total * 32u;
-  const uint32_t lim = min(units, ((uint32_t)p.fetch_cap > offset
-                                       ? ((uint32_t)p.fetch_cap - offset) * 32u
-                                       : 0u));
-  auto src_of = [&](uint32_t u) {
-    return reinterpret_cast<const uint4 *>(
-        src_base + (size_t)s_pos[u >> 5] * 2 * kHeadDim + (u & 31u) * 8);
-  };
-  auto dst_of = [&](uint32_t u) {
-    return reinterpret_cast<uint4 *>(
-        dst_base + (size_t)(offset + (u >> 5)) * 2 * kHeadDim + (u & 31u) * 8);
-  };
-  uint32_t u = threadIdx.x;
-  // four 16-byte host loads in flight per lane before their stores
-  for (; u + 3 * kBlock < lim; u += 4 * kBlock) {
-    const uint4 v0 = *src_of(u), v1 = *src_of(u + kBlock),
-                v2 = *src_of(u + 2 * kBlock), v3 = *src_of(u + 3 * kBlock);
-    *dst_of(u) = v0;
-    *dst_of(u + kBlock) = v1;
-    *dst_of(u + 2 * kBlock) = v2;
-    *dst_of(u + 3 * kBlock) = v3;
+  int32_t *fidx = p.fidx + (size_t)bg * p.fetch_cap;
+  for (int c = c0; c < c1; ++c) {
+    const int w0 = c * wpc;
+    // chunk sizes are at most 4096 tokens (128 words)
+    uint32_t word = 0, total = 0;
+    if ((int)threadIdx.x < wpc && w0 + (int)threadIdx.x < p.nwords) word = fb[w0 + threadIdx.x];
+    const uint32_t at0 = block_exclusive_scan<uint32_t>((uint32_t)__popc(word), s_red, &total);
+    {
+      uint32_t w = word, o = at0;
+      while (w) {
+        const int bit = __ffs(w) - 1;
+        s_pos[o++] = (w0 + (int)threadIdx.x) * 32 + bit;
+        w &= w - 1;
+      }
+    }
+    __syncthreads();
+    for (uint32_t k = threadIdx.x; k < total; k += kBlock) {
+      const uint32_t slot = offset + k;
+      if (slot < (uint32_t)p.fetch_cap) fidx[slot] = s_pos[k];
+    }
+    // rows (K then V, 512 bytes) in 16-byte units, four in flight per lane
+    const uint32_t lim = min(total * 32u, ((uint32_t)p.fetch_cap > offset
+                                               ? ((uint32_t)p.fetch_cap - offset) * 32u
+                                               : 0u));
+    auto src_of = [&](uint32_t u) {
+      return reinterpret_cast<const uint4 *>(
+          src_base + (size_t)s_pos[u >> 5] * 2 * kHeadDim + (u & 31u) * 8);
+    };
+    auto dst_of = [&](uint32_t u) {
+      return reinterpret_cast<uint4 *>(
+          dst_base + (size_t)(offset + (u >> 5)) * 2 * kHeadDim + (u & 31u) * 8);
+    };
+    uint32_t u = threadIdx.x;
+    for (; u + 3 * kBlock < lim; u += 4 * kBlock) {
+      const uint4 v0 = *src_of(u), v1 = *src_of(u + kBlock),
+                  v2 = *src_of(u + 2 * kBlock), v3 = *src_of(u + 3 * kBlock);
+      *dst_of(u) = v0;
+      *dst_of(u + kBlock) = v1;
+      *dst_of(u + 2 * kBlock) = v2;
+      *dst_of(u + 3 * kBlock) = v3;
+    }
+    for (; u < lim; u += kBlock) *dst_of(u) = *src_of(u);
+    offset += total;
+    __syncthreads();  // s_pos is rewritten by the next chunk
   }
-  for (; u < lim; u += kBlock) *dst_of(u) = *src_of(u);
-  if (c == p.nch - 1 && threadIdx.x == 0) {
-    const uint32_t all = offset + total;
-    p.fcount[bg] = (int32_t)all;
-    if (all > (uint32_t)p.fetch_cap) atomicOr(p.status, VKV_STATUS_FETCH_OVERFLOW);
-    const uint32_t moved = min(all, (uint32_t)p.fetch_cap);
+  if (j == kGatherWG - 1 && threadIdx.x == 0) {
+    p.fcount[bg] = (int32_t)offset;
+    if (offset > (uint32_t)p.fetch_cap) atomicOr(p.status, VKV_STATUS_FETCH_OVERFLOW);
+    const uint32_t moved = min(offset, (uint32_t)p.fetch_cap);
     atomicAdd(p.host_bytes, (unsigned long long)moved * 2ull * kHeadDim * 2ull);
   }
 }
@@ -1795,11 +1850,12 @@ __device__ __forceinline__ float resident_alpha(const DParams &p,
   return t.lam * w / ri;
 }
 
-// gridDim.x = ncr resident-row blocks followed by ncf fetched-row blocks;
-// each writes a partial (shift, sum of weights, weighted sum of V) per head.
+// Partial x of a KV head's attention: x < ncr covers a share of the resident
+// rows, x >= ncr a share of the fetched rows; each writes a partial (shift,
+// sum of weights, weighted sum of V) per head.
 template <int GRP>
-__global__ __launch_bounds__(kBlock) void dk_attn(DParams p) {
-  const int x = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+__device__ __forceinline__ void attn_part(const DParams &p, int x, int g,
+                                          int b) {
   const int bg = b * p.G + g;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int u = lane % 16;             // 8 dims per lane
@@ -1809,7 +1865,6 @@ __global__ __launch_bounds__(kBlock) void dk_attn(DParams p) {
   __shared__ float s_o[kBlock / kWave][GRP][kHeadDim];
   __shared__ float s_d[kBlock / kWave][GRP];
   __shared__ float s_red[kBlock / kWave];
-  __shared__ float s_scale[kBlock / kWave][kWave];  // ncr + ncf <= 64
   if (threadIdx.x < GRP) s_rs[threadIdx.x] = p.rows[row_of(p, b, g, threadIdx.x, GRP)];
   __syncthreads();
   const float a = (float)p.a_delta, l = (float)p.l_delta;
@@ -1967,10 +2022,16 @@ __global__ __launch_bounds__(kBlock) void dk_attn(DParams p) {
     for (int w = 0; w < kBlock / kWave; ++w) d += s_d[w][h];
     p.apart[(size_t)row_of(p, b, g, h, GRP) * np + x] = make_float2(mloc[h], d);
   }
-  if (!last_block_arrive(&p.groups[bg].arrive[ARR_ATTN], gridDim.x)) return;
-  // ---- merge the partial softmax sums by log-sum-exp (one wave per head);
-  // at most 64 partials, one per lane, and each output dimension reads its
-  // partials as consecutive 16-byte vectors
+}
+
+// Merge of a KV head's partial softmax sums by log-sum-exp (one wave per
+// head): at most 64 partials, one per lane, and each output dimension reads
+// its partials as consecutive 16-byte vectors.
+template <int GRP>
+__device__ __forceinline__ void attn_merge(const DParams &p, int g, int b) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int np = p.ncr + p.ncf;
+  __shared__ float s_scale[kBlock / kWave][kWave];  // ncr + ncf <= 64
   for (int h = wave; h < GRP; h += kBlock / kWave) {
     const int row = row_of(p, b, g, h, GRP);
     const float2 md = lane < np ? p.apart[(size_t)row * np + lane] : make_float2(0.0f, 0.0f);
@@ -2015,6 +2076,26 @@ __global__ __launch_bounds__(kBlock) void dk_attn(DParams p) {
   }
 }
 
+// The gather (bound by the host link) and the attention over the resident
+// rows, which does not depend on it, in one launch: blocks x < ncr take a
+// share of the resident rows, the others a share of the fetch bitmap.
+template <int GRP>
+__global__ __launch_bounds__(kBlock) void dk_fetch(DParams p) {
+  const int x = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  if (x < p.ncr) attn_part<GRP>(p, x, g, b);
+  else gather_part(p, x - p.ncr, g, b);
+}
+
+// The fetched rows' share of the attention, then the merge by the last
+// block of each KV head.
+template <int GRP>
+__global__ __launch_bounds__(kBlock) void dk_attn(DParams p) {
+  const int g = blockIdx.y, b = blockIdx.z;
+  attn_part<GRP>(p, p.ncr + (int)blockIdx.x, g, b);
+  if (!last_block_arrive(&p.groups[b * p.G + g].arrive[ARR_ATTN], gridDim.x)) return;
+  attn_merge<GRP>(p, g, b);
+}
+
 // Records the timing event after kernel `k` when the caller asked for it.
 struct PhaseMark {
   void **ev;
@@ -2057,16 +2138,16 @@ hipError_t run(const DParams &p, hipStream_t s, int sd, void **events) {
   mark(k++);
   dk_rwalk<GRP><<<gone, dim3(kPlanThreads), 0, s>>>(p);
   mark(k++);
-  dk_gather<GRP><<<gch, blk, 0, s>>>(p);
+  dk_fetch<GRP><<<dim3((unsigned)(p.ncr + kGatherWG), (unsigned)p.G, (unsigned)p.B), blk, 0, s>>>(p);
   mark(k++);
-  dk_attn<GRP><<<dim3((unsigned)(p.ncr + p.ncf), (unsigned)p.G, (unsigned)p.B), blk, 0, s>>>(p);
+  dk_attn<GRP><<<dim3((unsigned)p.ncf, (unsigned)p.G, (unsigned)p.B), blk, 0, s>>>(p);
   mark(k++);
   return hipGetLastError();
 }
 
 const char *const kPhaseNames[] = {
     "scan",  "resident", "beta0",   "beta1",   "beta2", "beta3", "beta4",
-    "cert",  "count",    "resolve", "collect", "walk",  "gather", "attn"};
+    "cert",  "count",    "resolve", "collect", "walk",  "fetch", "attn"};
 
 }  // namespace
 
