@@ -56,14 +56,13 @@ def algorithmic_bytes(w, counts, fetching_rows, host_bytes):
     sketch logit of every (query head, token); the resident-logit kernel
     reads the resident K rows and positions and writes one logit per
     (query head, row); every planning pass over the tokens (beta passes,
-    certificate, key count, candidate collection) reads the sketch logits of
-    its rows and r of their KV heads (the count and collection passes only
-    for the rows that fetch); the attention kernel reads the resident V rows
-    and positions and writes out. The gather is bound by the host link and
+    certificate, candidate keys) reads the sketch logits of its rows and r of
+    their KV heads (the candidate pass only for the rows that fetch). The gather is bound by the host link and
     reported separately (it runs in one launch with the attention over the
     resident rows, which hides behind it); the resolve and walk steps touch
-    only per-row summaries. The last attention launch reads the fetched rows
-    from staging and writes the outputs.
+    only per-row summaries. The gather workgroups also form the attention
+    over the rows they read; the last launch only merges per-KV-head partial
+    sums and writes the outputs.
     """
     B, Hq, G, n, s, d = w["B"], w["Hq"], w["G"], w["n"], w["s"], w["d"]
     grp = Hq // G
@@ -72,8 +71,7 @@ def algorithmic_bytes(w, counts, fetching_rows, host_bytes):
     ftok = fetching_rows * n * 4 + min(fetching_rows, B * G) * n * 4
     per = {"scan": B * G * n * (2 * s + 4) + B * Hq * n * 4,
            "resident": rows * (2 * d + 4) + rows * grp * 4,
-           "beta0": tok, "cert": tok, "count": ftok, "collect": ftok,
-           "attn": host_bytes + B * Hq * d * 4}
+           "beta0": tok, "cert": tok, "cand": ftok}
     return dict(step=B * G * n * (2 * s + 4) + rows * (4 * d + 4)
                 + B * Hq * d * (2 + 4), kernels=per)
 

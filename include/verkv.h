@@ -134,7 +134,9 @@ typedef struct {
  *              guarantee on the attention denominator.
  * estimator    VKV_EST_CLIP or VKV_EST_UNBIASED; weights VKV_W_SKETCH or
  *              VKV_W_PERFECT.
- * fetch_cap    staging rows per (request, KV head) (1..n).
+ * fetch_cap    most rows read from host_kv per (request, KV head) (1..n); rows
+ *              of a larger union are neither listed nor read, and the status
+ *              word gets VKV_STATUS_FETCH_OVERFLOW.
  * Outputs (dev): out [B][Hq][d] f32 attention output; d_hat and log_shift
  * [B][Hq] f32 with D^ = d_hat * exp(log_shift); eps_hat0 / eps_hat [B][Hq] f32,
  * the certificate before fetching and after (on L'); k_star [B][Hq] i32;

@@ -98,7 +98,8 @@ def test_workspace_sizes():
     d = _decode_args()
     dw = vk.vkv_decode_workspace_bytes(d)
     assert dw > 0
-    assert vk.vkv_decode_workspace_bytes(_decode_args(fetch_cap=8)) < dw
+    assert vk.vkv_decode_workspace_bytes(_decode_args(n_tokens=1024, fetch_cap=1024)) < dw
+    assert vk.vkv_decode_workspace_bytes(_decode_args(cap=300)) < dw
     assert vk.vkv_decode_workspace_bytes(_decode_args(n_q_heads=20)) == 0
     # the shapes named in the configs fit easily in 288 GB
     big = _decode_args(batch=16, n_tokens=32768, cap=4600, fetch_cap=32768)

@@ -2,32 +2,30 @@
 // section 4.2; Definition 2, Lemma 1, eqs. 5-10, Theorem 2).
 //
 // A "group" is one (request b, KV head g) with its GRP = Hq/G query heads
-// ("rows"). Token passes split the n positions into chunks of `chunk` tokens,
-// one workgroup per (chunk, g, b); where a pass ends in a row-level decision
-// it is taken by the last workgroup of the group to finish ("last block
-// done"), so a launch never waits on another workgroup. The planning steps
-// run one workgroup per row and need no cross-workgroup step at all.
+// ("rows"). Kernels, in launch order:
 //
 //  dk_scan      sketch logits s_i = <P_g^T q, sk_i>/sqrt(d) for every token and
 //               the GRP heads at once (one sketch row serves all of them).
 //  dk_resident  exact logits l_j = <q, k_j>/sqrt(d) on the resident rows,
 //               residency bitmap, common shift m = max(max_R l, max_L s).
-//  dk_plan_a    per row: D~ = sum_H w + sum_L w~; the Definition 2 fixed point
-//               beta* by four radix levels over the fp32 bit patterns of the
-//               breakpoints of a piecewise-linear h(beta), then an exact linear
-//               solve between adjacent floats; lambda_i, beta(L), V(L), top-2
-//               of b_i -> eps^(L) (Lemma 1, eq. 7).
-//  dk_plan_b    per row that fails the certificate: radix select driven by
-//               the stopping rule (eq. 10) over keys (gain bits, inverted
-//               position), whose descending order is L_g; per-bin counts and
-//               fixed-point sums of beta_i and v_i find the bin where
-//               eps^(L_g[k:]) first drops below eps without sorting L; the
-//               last bin is rank-sorted in LDS and walked to the exact k*.
-//               Then F_h minus S is ORed into the KV head's fetch bitmap.
-//  dk_gather    ascending fetch list; rows copied from pinned host memory by
-//               GPU loads (zero-copy) into device staging.
-//  dk_attn      weights w on H u F_h, lambda w / r on S \ F_h, exact logits of
-//               fetched rows, partial softmax sums merged by log-sum-exp.
+//  dk_rbeta x5  D~ = sum_H w + sum_L w~, then the Definition 2 fixed point
+//               beta* by a bracketed Newton iteration on a convex piecewise-
+//               linear function (one launch per pass).
+//  dk_rcert     lambda_i, beta(L), V(L) and the top two b_i per chunk
+//               (Lemma 1, eq. 7).
+//  dk_rcand     eps^(L) and, for a row that must fetch, the gain keys (eq. 9)
+//               and each workgroup's local top candidates.
+//  dk_rwalk     per row: the stopping rule (eq. 10) over the candidates by a
+//               radix select, F_h into the row's and the KV head's bitmaps.
+//  dk_fetch     the attention over the resident rows, and in the same launch
+//               the gather of F_h minus S from pinned host memory by GPU
+//               loads (zero-copy) with the attention over those rows.
+//  dk_attn      merge of the partial softmax sums by log-sum-exp.
+//
+// Passes over a row's tokens run as many workgroups per row; every
+// workgroup combines the partial records of the previous launch itself, so
+// no workgroup waits for another. dk_resident alone ends in a "last block
+// done" step per group.
 //
 // All per-token recomputations (weights, lambda, certificate terms, gains)
 // go through the same inline functions and the library is built with
@@ -82,13 +80,8 @@ struct CertPart {
   int32_t p1, pad;      // position of x1 (smallest on ties)
 };
 
-// Candidate bound of a row and its fixed-point totals over L.
-struct SelState {
-  unsigned long long lo_key, tot_b, tot_v;
-  uint32_t take, pad;   // keys >= lo_key
-};
 
-enum { ARR_RES = 0, ARR_ATTN = 1 };
+enum { ARR_RES = 0 };
 
 struct DParams {
   const uint16_t *q, *rkv, *sketch, *host_kv;
@@ -101,6 +94,7 @@ struct DParams {
   uint32_t *status;
   float *shat, *ell;
   uint32_t *resbits, *fbits;
+  uint32_t *hbits;   // [row][nwords] F_h of each row
   float *pmax;
   uint32_t *hpart;
   RowState *rows;
@@ -109,16 +103,16 @@ struct DParams {
   BetaState *bstate; // [2][row]
   double *rbeta;     // [row][2] beta*, D~
   CertPart *cpart;   // [row][nrc]
-  uint32_t *khist;   // [row][nrc][2048] key histograms
-  unsigned long long *tpart;  // [row][nrc][2] fixed-point totals
-  SelState *sel;     // [row]
-  uint32_t *ccount;  // [row] candidates collected
-  unsigned long long *candk, *candb, *candv;  // [row][kCandMax]
-  uint32_t *candr;   // [row][kCandMax]
-  uint32_t *rpart;   // [row][nrc] max b_i below the candidate bound
+  // candidate workgroups: [row][kSelWG] counts, local bounds, max b_i of
+  // the keys not written, fixed-point totals; candidates [row][kCandMax]
+  uint32_t *ccount;
+  unsigned long long *clo;
+  uint32_t *rpart;
+  unsigned long long *tpart;
+  unsigned long long *candk, *candb, *candv;
+  uint32_t *candr;
   float2 *apart;     // [row][ncr + ncf] (shift, sum of weights)
   float *aparto;     // [row][d][npad] weighted sums of V, part index fastest
-  uint16_t *staging;
   int B, Hq, G, n, cap, fetch_cap, nch, ncr, ncf, npad, nwords, chunk, nrc;
   float eps;
   double l_delta, a_delta;
@@ -191,11 +185,6 @@ __device__ __forceinline__ unsigned long long to_fx(float x, int e) {
   return (unsigned long long)__double2ull_rn(ldexp((double)x, e));
 }
 
-__device__ __forceinline__ bool is_member(unsigned long long key,
-                                          const RowState &rs) {
-  return key >= rs.T;
-}
-
 __device__ __forceinline__ int row_of(const DParams &p, int b, int g, int h,
                                       int grp) {
   return b * p.Hq + g * grp + h;
@@ -256,6 +245,8 @@ __global__ __launch_bounds__(kBlock) void dk_scan(DParams p) {
       if (w0 + w < p.nwords) {
         p.resbits[(size_t)bg * p.nwords + w0 + w] = 0u;
         p.fbits[(size_t)bg * p.nwords + w0 + w] = 0u;
+        for (int h = 0; h < GRP; ++h)
+          p.hbits[(size_t)row_of(p, b, g, h, GRP) * p.nwords + w0 + w] = 0u;
       }
     }
   }
@@ -378,6 +369,8 @@ __global__ __launch_bounds__(kBlock) void dk_scan_exact(DParams p) {
       if (w0 + w < p.nwords) {
         p.resbits[(size_t)bg * p.nwords + w0 + w] = 0u;
         p.fbits[(size_t)bg * p.nwords + w0 + w] = 0u;
+        for (int h = 0; h < GRP; ++h)
+          p.hbits[(size_t)row_of(p, b, g, h, GRP) * p.nwords + w0 + w] = 0u;
       }
     }
   }
@@ -551,14 +544,15 @@ __global__ __launch_bounds__(kBlock) void dk_resident(DParams p) {
 // workgroups iterates over the whole row (rare; same arithmetic).
 //
 // Selection: keys (gain bits, inverted position) order L as L_g
-// (descending). A count histogram of the top 11 key bits gives a key bound
-// lo with at most kCandMax keys in [lo, inf); those candidates are collected
-// with their fixed-point beta_i and v_i and their range term b_i, and one
-// workgroup per row sorts them and walks the stopping rule to the exact k*.
-// If fetching every candidate still leaves eps^ >= eps, that workgroup runs
-// the streaming selection below instead. All sums of the selection are
-// fixed-point integers, so a rest's sum is the total minus the fetched part
-// exactly.
+// (descending). Each of kSelWG workgroups per row takes a block-cyclic
+// share of the row's tokens and writes its keys at or above a local bound
+// lo_s (at most kCandWG of them) with their fixed-point beta_i and v_i and
+// range term b_i. One workgroup per row then runs the stopping rule on the
+// union to the exact k* and threshold T; that is the answer whenever T >=
+// max_s lo_s (every key >= T was written). Otherwise, or when fetching every
+// candidate cannot certify the row, it runs the streaming selection below
+// instead. All sums of the selection are fixed-point integers, so a rest's
+// sum is the total minus the fetched part exactly.
 constexpr int kPlanThreads = 1024;  // row-level workgroups
 constexpr int kPlanWaves = kPlanThreads / kWave;
 constexpr int kSelUnroll = 4;       // streamed tokens per thread in flight
@@ -726,7 +720,7 @@ __device__ void select_row(const DParams &p, int row, int bg, RowState &rs,
   const double sbs = ldexp(1.0, -eb), svs = ldexp(1.0, -ev);
   const uint32_t *rbits = p.resbits + (size_t)bg * p.nwords;
   uint32_t *fb = p.fbits + (size_t)bg * p.nwords;
-  constexpr unsigned long long kKeyEnd = 1ull << 55;  // above every key
+  uint32_t *hb = p.hbits + (size_t)row * p.nwords;
 
   // One pass over L with every lane active: g(i, valid, key, terms).
   auto stream = [&](auto &&g) {
@@ -879,6 +873,7 @@ __device__ void select_row(const DParams &p, int row, int bg, RowState &rs,
       // not enough: every candidate is fetched, the region moves below
       for (int c = threadIdx.x; c < nc; c += kPlanThreads) {
         const int pos = (int)(0xFFFFFFu - (uint32_t)(lds.cand.key[c] & 0xFFFFFFull));
+        atomicOr(hb + pos / 32, 1u << (pos % 32));
         if (!((rbits[pos / 32] >> (pos % 32)) & 1u)) atomicOr(fb + pos / 32, 1u << (pos % 32));
       }
       fet_c += (uint32_t)nc;
@@ -998,6 +993,7 @@ __device__ void select_row(const DParams &p, int row, int bg, RowState &rs,
     // mark the fetched candidates
     for (int c = threadIdx.x; c <= kk; c += kPlanThreads) {
       const int pos = (int)(0xFFFFFFu - (uint32_t)(lds.cand.key[c] & 0xFFFFFFull));
+      atomicOr(hb + pos / 32, 1u << (pos % 32));
       if (!((rbits[pos / 32] >> (pos % 32)) & 1u)) atomicOr(fb + pos / 32, 1u << (pos % 32));
     }
     __syncthreads();
@@ -1350,153 +1346,150 @@ __device__ __forceinline__ void row_certificate(const DParams &p, CertShare sh,
   __syncthreads();
 }
 
+// Candidate workgroups per row and the candidates each may write. Their
+// tokens are split block-cyclically (blocks of kSelBlk positions), so that a
+// run of high-gain positions is spread over all of them.
+constexpr int kSelWG = 16;
+constexpr int kCandWG = kCandMax / kSelWG;
+constexpr int kSelBlk = 64;
+constexpr int kSelIt = 8;  // tokens per thread whose keys stay in registers
+
 // Certificate of the row (workgroup 0 stores it), then for a row that
-// fetches: the count histogram of the top 11 key bits and the fixed-point
-// totals of beta_i and v_i over the chunk.
+// fetches: this workgroup's keys, their count histogram over the top 11 key
+// bits and the fixed-point totals of beta_i and v_i; its local bound lo_s,
+// the smallest bin edge with at most kCandWG of its keys at or above it; and
+// those keys, written with their fixed-point beta_i, v_i and b_i. Keys below
+// lo_s are not written; their largest b_i is.
 template <int GRP>
-__global__ __launch_bounds__(kBlock) void dk_rcount(DParams p) {
-  const int c = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
+__global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
+  const int s = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
   const int row = b * p.Hq + hq, bg = b * p.G + hq / GRP;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   __shared__ RowState rs;
   __shared__ uint32_t s_hist[kSelBinsP];
-  float w8[kRowTok], r8[kRowTok], s8[kRowTok];
-  row_load(p, row, bg, c, r8, s8);
+  __shared__ uint32_t s_cnt;
+  __shared__ int s_j0;
+  const float *rr = p.r + (size_t)bg * p.n;
+  const float *sh = p.shat + (size_t)row * p.n;
+  const int n = p.n;
+  // token of iteration it for this thread
+  auto pos_of = [&](int it) {
+    return ((it * (kBlock / kSelBlk) + (int)threadIdx.x / kSelBlk) * kSelWG + s) * kSelBlk +
+           (int)threadIdx.x % kSelBlk;
+  };
+  const int nblk = (n + kSelBlk - 1) / kSelBlk;
+  const int iters = ((nblk + kSelWG - 1) / kSelWG + kBlock / kSelBlk - 1) / (kBlock / kSelBlk);
+  // loads first: the first kSelIt tokens, the certificate records
+  float r8[kSelIt], s8[kSelIt];
+#pragma unroll
+  for (int it = 0; it < kSelIt; ++it) {
+    const int i = pos_of(it);
+    r8[it] = (it < iters && i < n) ? rr[i] : 1.0f;
+    s8[it] = (it < iters && i < n) ? sh[i] : 0.0f;
+  }
   const float m = p.rows[row].m;
   const CertShare cs = cert_rec_load(p, row);
   const double beta = p.rbeta[2 * row], dnorm = p.rbeta[2 * row + 1];
   for (int i = threadIdx.x; i < kSelBinsP; i += kBlock) s_hist[i] = 0u;
-  row_weights(m, r8, s8, w8);
+  if (threadIdx.x == 0) s_cnt = 0u;
   row_certificate(p, cs, m, beta, dnorm, rs);
-  if (c == 0 && threadIdx.x == 0) p.rows[row] = rs;
+  if (s == 0 && threadIdx.x == 0) p.rows[row] = rs;
   if (!rs.fetch) return;
   const float betaf = (float)rs.beta;
   const float af = (float)p.a_delta, lf = (float)p.l_delta;
   const int eb = rs.eb, ev = rs.ev;
+  auto key_of = [&](int i, float ri, float si, Terms &t) {
+    t = token_terms_w(expf(si - m), ri, betaf, p.est);
+    return make_key(token_gain(t, i, rs, af, lf), i);
+  };
+  // ---- keys: histogram and totals
+  unsigned long long key8[kSelIt];
+  uint32_t rb8[kSelIt];
   unsigned long long tx[2] = {0ull, 0ull};
 #pragma unroll
-  for (int u = 0; u < kRowTok; ++u) {
-    if (!(r8[u] < 1.0f)) continue;
-    const int i = row_pos(c, u);
-    const Terms t = token_terms_w(w8[u], r8[u], betaf, p.est);
-    const unsigned long long key = make_key(token_gain(t, i, rs, af, lf), i);
+  for (int it = 0; it < kSelIt; ++it) {
+    key8[it] = 0ull;
+    rb8[it] = 0u;
+    if (!(r8[it] < 1.0f)) continue;
+    Terms t;
+    key8[it] = key_of(pos_of(it), r8[it], s8[it], t);
+    rb8[it] = __float_as_uint(t.rb);
+    atomicAdd(&s_hist[(int)(key8[it] >> sel_off(0))], 1u);
+    tx[0] += to_fx(t.bi, eb);
+    tx[1] += to_fx(t.vi, ev);
+  }
+  for (int it = kSelIt; it < iters; ++it) {  // long rows: recomputed below
+    const int i = pos_of(it);
+    if (i >= n) continue;
+    const float ri = rr[i];
+    if (!(ri < 1.0f)) continue;
+    Terms t;
+    const unsigned long long key = key_of(i, ri, sh[i], t);
     atomicAdd(&s_hist[(int)(key >> sel_off(0))], 1u);
     tx[0] += to_fx(t.bi, eb);
     tx[1] += to_fx(t.vi, ev);
   }
   blk_reduce<unsigned long long, 2, kBlock>(tx);
-  if (threadIdx.x == 0) {
-    p.tpart[((size_t)row * p.nrc + c) * 2] = tx[0];
-    p.tpart[((size_t)row * p.nrc + c) * 2 + 1] = tx[1];
+  // ---- local bound: lane owns bins [lane * 32, lane * 32 + 32)
+  if (wave == 0) {
+    constexpr int PER = kSelBinsP / kWave;
+    uint32_t lc = 0u;
+    for (int k = 0; k < PER; ++k) lc += s_hist[lane * PER + k];
+    const uint32_t incl = wave_incl_scan<uint32_t>(lc, lane);
+    uint32_t c = __shfl(incl, kWave - 1, kWave) - incl;  // keys in lanes above
+    int j = kSelBinsP;
+    if (c <= (uint32_t)kCandWG) {
+      for (int k = PER - 1; k >= 0; --k) {
+        c += s_hist[lane * PER + k];
+        if (c > (uint32_t)kCandWG) break;
+        j = lane * PER + k;
+      }
+    }
+    for (int o = 32; o >= 1; o >>= 1) j = min(j, __shfl_xor(j, o, kWave));
+    if (lane == 0) s_j0 = j;
   }
-  uint32_t *hp = p.khist + ((size_t)row * p.nrc + c) * kSelBinsP;
-  for (int i = threadIdx.x; i < kSelBinsP; i += kBlock) hp[i] = s_hist[i];
-}
-
-// One workgroup per row: the row's histogram and totals, and the key bound
-// lo with at most kCandMax keys in [lo, inf).
-template <int GRP>
-__global__ __launch_bounds__(kPlanThreads) void dk_rresolve(DParams p) {
-  const int hq = blockIdx.x, b = blockIdx.y;
-  const int row = b * p.Hq + hq;
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  __shared__ uint32_t s_w[kPlanWaves];
-  __shared__ uint32_t s_take;
-  const int fetch = p.rows[row].fetch;
-  // bins 2t and 2t + 1 of this thread, summed over the chunks
-  uint32_t h0 = 0u, h1 = 0u;
-  const uint32_t *hp = p.khist + (size_t)row * p.nrc * kSelBinsP;
-  for (int s = 0; s < p.nrc; ++s) {
-    const uint2 x = *reinterpret_cast<const uint2 *>(hp + (size_t)s * kSelBinsP + 2 * threadIdx.x);
-    h0 += x.x;
-    h1 += x.y;
-  }
-  unsigned long long tot[2] = {0ull, 0ull};
-  for (int s = threadIdx.x; s < p.nrc; s += kPlanThreads) {
-    tot[0] += p.tpart[((size_t)row * p.nrc + s) * 2];
-    tot[1] += p.tpart[((size_t)row * p.nrc + s) * 2 + 1];
-  }
-  if (!fetch) return;
-  plan_reduce<unsigned long long, 2>(tot);
-  // keys in bins above this thread's: suffix sums over threads
-  const uint32_t mine = h0 + h1;
-  uint32_t suf = mine;  // inclusive suffix within the wave
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t x = __shfl_down(suf, o, kWave);
-    if (lane + o < kWave) suf += x;
-  }
-  if (lane == 0) s_w[wave] = suf;  // the wave's total
   __syncthreads();
-  uint32_t above = suf - mine;
-  for (int w = wave + 1; w < kPlanWaves; ++w) above += s_w[w];
-  const uint32_t c1 = above + h1, c0 = c1 + h0;  // keys in bins >= 2t+1, >= 2t
-  int j = kSelBinsP;
-  if (c0 <= (uint32_t)kCandMax) j = 2 * threadIdx.x;
-  else if (c1 <= (uint32_t)kCandMax) j = 2 * threadIdx.x + 1;
-  const int j0 = -plan_max<int>(-j);
-  if (j0 < kSelBinsP && (j0 >> 1) == (int)threadIdx.x) s_take = (j0 & 1) ? c1 : c0;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    SelState ss;
-    ss.lo_key = j0 < kSelBinsP ? ((unsigned long long)j0 << sel_off(0)) : kKeyEnd;
-    ss.tot_b = tot[0];
-    ss.tot_v = tot[1];
-    ss.take = j0 < kSelBinsP ? s_take : 0u;
-    ss.pad = 0u;
-    p.sel[row] = ss;
-    p.ccount[row] = 0u;
-  }
-}
-
-// Candidates: the chunk's keys in [lo, inf) with their fixed-point beta_i,
-// v_i and b_i, appended to the row's list; the max of b_i below lo.
-template <int GRP>
-__global__ __launch_bounds__(kBlock) void dk_rcollect(DParams p) {
-  const int c = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
-  const int row = b * p.Hq + hq, bg = b * p.G + hq / GRP;
-  __shared__ RowState rs;
-  __shared__ uint32_t s_scan[kBlock / kWave + 1];
-  __shared__ uint32_t s_base;
-  float w8[kRowTok], r8[kRowTok], s8[kRowTok];
-  row_load(p, row, bg, c, r8, s8);
-  if (threadIdx.x == 0) rs = p.rows[row];
-  const unsigned long long lo_key = p.sel[row].lo_key;
-  __syncthreads();
-  if (!rs.fetch) return;
-  row_weights(rs.m, r8, s8, w8);
-  const float betaf = (float)rs.beta;
-  const float af = (float)p.a_delta, lf = (float)p.l_delta;
-  unsigned long long key8[kRowTok];
-  uint32_t below = 0u, cnt = 0u;
+  const unsigned long long lo =
+      s_j0 < kSelBinsP ? ((unsigned long long)s_j0 << sel_off(0)) : kKeyEnd;
+  // ---- the keys at or above lo, and the max of b_i below it
+  const size_t seg = ((size_t)row * kSelWG + s) * kCandWG;
+  uint32_t below = 0u;
+  auto emit = [&](int i, float ri, float si, unsigned long long key) {
+    const uint32_t slot = atomicAdd(&s_cnt, 1u);
+    Terms t;
+    key_of(i, ri, si, t);
+    if (slot < (uint32_t)kCandWG) {
+      p.candk[seg + slot] = key;
+      p.candb[seg + slot] = to_fx(t.bi, eb);
+      p.candv[seg + slot] = to_fx(t.vi, ev);
+      p.candr[seg + slot] = __float_as_uint(t.rb);
+    }
+  };
 #pragma unroll
-  for (int u = 0; u < kRowTok; ++u) {
-    key8[u] = 0ull;
-    if (!(r8[u] < 1.0f)) continue;
-    const int i = row_pos(c, u);
-    const Terms t = token_terms_w(w8[u], r8[u], betaf, p.est);
-    key8[u] = make_key(token_gain(t, i, rs, af, lf), i);
-    if (key8[u] >= lo_key) ++cnt;
+  for (int it = 0; it < kSelIt; ++it) {
+    if (!(r8[it] < 1.0f)) continue;
+    if (key8[it] >= lo) emit(pos_of(it), r8[it], s8[it], key8[it]);
+    else below = max(below, rb8[it]);
+  }
+  for (int it = kSelIt; it < iters; ++it) {
+    const int i = pos_of(it);
+    if (i >= n) continue;
+    const float ri = rr[i];
+    if (!(ri < 1.0f)) continue;
+    const float si = sh[i];
+    Terms t;
+    const unsigned long long key = key_of(i, ri, si, t);
+    if (key >= lo) emit(i, ri, si, key);
     else below = max(below, __float_as_uint(t.rb));
   }
-  uint32_t total;
-  const uint32_t off = block_exclusive_scan(cnt, s_scan, &total);
-  if (threadIdx.x == 0) s_base = total ? atomicAdd(p.ccount + row, total) : 0u;
   below = blk_max<uint32_t, kBlock>(below);
-  if (threadIdx.x == 0) p.rpart[(size_t)row * p.nrc + c] = below;
-  const uint32_t base = s_base + off;
-  if (cnt == 0u) return;
-  const int eb = rs.eb, ev = rs.ev;
-  uint32_t k = 0u;
-#pragma unroll
-  for (int u = 0; u < kRowTok; ++u) {
-    if (!(r8[u] < 1.0f) || key8[u] < lo_key) continue;
-    const uint32_t slot = base + k++;
-    if (slot >= (uint32_t)kCandMax) continue;
-    const Terms t = token_terms_w(w8[u], r8[u], betaf, p.est);
-    const size_t at = (size_t)row * kCandMax + slot;
-    p.candk[at] = key8[u];
-    p.candb[at] = to_fx(t.bi, eb);
-    p.candv[at] = to_fx(t.vi, ev);
-    p.candr[at] = __float_as_uint(t.rb);
+  if (threadIdx.x == 0) {
+    const size_t at = (size_t)row * kSelWG + s;
+    p.ccount[at] = min(s_cnt, (uint32_t)kCandWG);
+    p.clo[at] = lo;
+    p.rpart[at] = below;
+    p.tpart[2 * at] = tx[0];
+    p.tpart[2 * at + 1] = tx[1];
   }
 }
 
@@ -1548,16 +1541,25 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rwalk(DParams p) {
   __shared__ WalkLds lds;
   __shared__ RowState rs;
   __shared__ WalkState ws;
-  // every load first: the row, the chunk maxima and all candidate slots
-  // (those past the count are read but not used)
+  __shared__ uint32_t s_wc[kSelWG], s_off[kSelWG];
+  __shared__ unsigned long long s_tot[2], s_lomax;
+  __shared__ uint32_t s_below;
+  __shared__ int s_nc;
+  // every load first: the row, the candidate workgroups' summaries and all
+  // candidate slots (those past a workgroup's count are read but not used)
   constexpr int PT = kCandMax / kPlanThreads;
   const size_t cb0 = (size_t)row * kCandMax;
   if (threadIdx.x == 0) rs = p.rows[row];
-  const SelState ss = p.sel[row];
-  const uint32_t ncount = p.ccount[row];
-  uint32_t below = 0u;
-  for (int s = threadIdx.x; s < p.nrc; s += kPlanThreads)
-    below = max(below, p.rpart[(size_t)row * p.nrc + s]);
+  uint32_t wc = 0u, wbelow = 0u;
+  unsigned long long wlo = 0ull, wtb = 0ull, wtv = 0ull;
+  if (threadIdx.x < kSelWG) {
+    const size_t at = (size_t)row * kSelWG + threadIdx.x;
+    wc = p.ccount[at];
+    wlo = p.clo[at];
+    wbelow = p.rpart[at];
+    wtb = p.tpart[2 * at];
+    wtv = p.tpart[2 * at + 1];
+  }
   unsigned long long ck[PT], cbx[PT], cvx[PT];
   uint32_t crb[PT];
 #pragma unroll
@@ -1570,41 +1572,59 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rwalk(DParams p) {
   }
   __syncthreads();
   if (!rs.fetch) return;
-  const int nc = (int)min(ncount, (uint32_t)kCandMax);
-  const double a = p.a_delta, l = p.l_delta;
-  const double sbs = ldexp(1.0, -rs.eb), svs = ldexp(1.0, -rs.ev);
-  below = plan_max<uint32_t>(below);
-  unsigned long long cs[2] = {0ull, 0ull};
-#pragma unroll
-  for (int q = 0; q < PT; ++q) {
-    if ((int)threadIdx.x + q * kPlanThreads < nc) {
-      cs[0] += cbx[q];
-      cs[1] += cvx[q];
+  // the workgroups' summaries: offsets of their candidates, totals over L,
+  // the max of b_i over every token not written, the largest local bound
+  if (wave == 0) {
+    const uint32_t incl = wave_incl_scan<uint32_t>(wc, lane);
+    if (lane < kSelWG) {
+      s_wc[lane] = wc;
+      s_off[lane] = incl - wc;
+    }
+    const unsigned long long tb = wave_sum(wtb), tv = wave_sum(wtv);
+    const uint32_t bl = wave_max(wbelow);
+    const unsigned long long lm = wave_max(wlo);
+    if (lane == kWave - 1) s_nc = (int)incl;
+    if (lane == 0) {
+      s_tot[0] = tb;
+      s_tot[1] = tv;
+      s_below = bl;
+      s_lomax = lm;
     }
   }
+  __syncthreads();
+  const int nc = s_nc;
+  const unsigned long long tot_b = s_tot[0], tot_v = s_tot[1];
+  const uint32_t below = s_below;
+  const double a = p.a_delta, l = p.l_delta;
+  const double sbs = ldexp(1.0, -rs.eb), svs = ldexp(1.0, -rs.ev);
+  unsigned long long cs[2] = {0ull, 0ull};
+  unsigned long long kmin = ~0ull, kmax = 0ull;
+#pragma unroll
+  for (int q = 0; q < PT; ++q) {
+    const int idx = (int)threadIdx.x + q * kPlanThreads;
+    const int sw = idx / kCandWG, slot = idx % kCandWG;
+    if (slot >= (int)s_wc[sw]) continue;
+    const int k = (int)s_off[sw] + slot;
+    lds.c.key[k] = ck[q];
+    lds.c.bfx[k] = cbx[q];
+    lds.c.vfx[k] = cvx[q];
+    lds.c.rb[k] = crb[q];
+    cs[0] += cbx[q];
+    cs[1] += cvx[q];
+    kmin = min(kmin, ck[q]);
+    kmax = max(kmax, ck[q]);
+  }
   plan_reduce<unsigned long long, 2>(cs);
-  // fetching every candidate leaves exactly the tokens below lo
+  // fetching every candidate leaves exactly the tokens not written
   const double e_below =
-      eps_of((double)(ss.tot_b - cs[0]) * sbs, (double)(ss.tot_v - cs[1]) * svs,
+      eps_of((double)(tot_b - cs[0]) * sbs, (double)(tot_v - cs[1]) * svs,
              (double)__uint_as_float(below), rs.dnorm, a, l);
-  if (!(e_below < (double)p.eps) || ncount != ss.take || nc == 0) {
+  if (!(e_below < (double)p.eps) || nc == 0) {
     __syncthreads();
     select_row(p, row, bg, rs, lds.sel);
     __syncthreads();
     if (threadIdx.x == 0) p.rows[row] = rs;
     return;
-  }
-  unsigned long long kmin = ~0ull, kmax = 0ull;
-#pragma unroll
-  for (int q = 0; q < PT; ++q) {
-    const int k = (int)threadIdx.x + q * kPlanThreads;
-    if (k >= nc) continue;
-    lds.c.key[k] = ck[q];
-    lds.c.bfx[k] = cbx[q];
-    lds.c.vfx[k] = cvx[q];
-    lds.c.rb[k] = crb[q];
-    kmin = min(kmin, ck[q]);
-    kmax = max(kmax, ck[q]);
   }
   kmax = plan_max<unsigned long long>(kmax);
   kmin = ~plan_max<unsigned long long>(~kmin);
@@ -1680,8 +1700,8 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rwalk(DParams p) {
           fv += x.vsum;
           uint32_t mb = mlow;
           for (int q2 = 0; q2 < q; ++q2) mb = max(mb, lds.c.bin[lane * PER + q2].bmax);
-          const double e = eps_of((double)(ss.tot_b - fb) * sbs,
-                                  (double)(ss.tot_v - fv) * svs,
+          const double e = eps_of((double)(tot_b - fb) * sbs,
+                                  (double)(tot_v - fv) * svs,
                                   (double)__uint_as_float(mb), rs.dnorm, a, l);
           if (x.cnt > 0u && e < (double)p.eps) best = lane * PER + q;
         }
@@ -1703,8 +1723,8 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rwalk(DParams p) {
         for (int q2 = 0; q2 < q; ++q2) mb = max(mb, lds.c.bin[lane * PER + q2].bmax);
         const WalkBin &x = lds.c.bin[top];
         if (x.cnt <= 1u || off == 0) {
-          const double e = eps_of((double)(ss.tot_b - fb - x.bsum) * sbs,
-                                  (double)(ss.tot_v - fv - x.vsum) * svs,
+          const double e = eps_of((double)(tot_b - fb - x.bsum) * sbs,
+                                  (double)(tot_v - fv - x.vsum) * svs,
                                   (double)__uint_as_float(mb), rs.dnorm, a, l);
           ws.kstar = (int)(ws.ac + c + x.cnt);
           ws.eps1 = (float)e;
@@ -1734,12 +1754,23 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rwalk(DParams p) {
   }
   __syncthreads();
   const unsigned long long T = ws.T;
+  if (T < s_lomax) {
+    // a candidate workgroup may hold keys in [T, its bound) that it did not
+    // write: the candidates cannot decide this row
+    __syncthreads();
+    select_row(p, row, bg, rs, lds.sel);
+    __syncthreads();
+    if (threadIdx.x == 0) p.rows[row] = rs;
+    return;
+  }
   const uint32_t *rbits = p.resbits + (size_t)bg * p.nwords;
   uint32_t *fbm = p.fbits + (size_t)bg * p.nwords;
+  uint32_t *hb = p.hbits + (size_t)row * p.nwords;
   for (int k = threadIdx.x; k < nc; k += kPlanThreads) {
     const unsigned long long key = lds.c.key[k];
     if (key < T) continue;
     const int pos = (int)(0xFFFFFFu - (uint32_t)(key & 0xFFFFFFull));
+    atomicOr(hb + pos / 32, 1u << (pos % 32));
     if (!((rbits[pos / 32] >> (pos % 32)) & 1u)) atomicOr(fbm + pos / 32, 1u << (pos % 32));
   }
   if (threadIdx.x == 0) {
@@ -1751,21 +1782,36 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rwalk(DParams p) {
 }
 
 // ------------------------------------------------------------ fetch
-// Workgroups per KV head that copy fetched rows: enough host loads in
-// flight for the link, few enough that most compute units stay free for the
+// Workgroups per KV head that read fetched rows: enough host loads in flight
+// for the link, few enough that most compute units stay free for the
 // attention over the resident rows running in the same launch (host loads
 // queued in a compute unit delay every other load issued there).
 constexpr int kGatherWG = 8;
+constexpr int kGatherBatch = 4;   // rows per half-wave with loads in flight
 
-// Gather by workgroup j of a KV head: chunks [j nch / kGatherWG, (j + 1) nch
-// / kGatherWG) of the fetch bitmap in order; for each, its part of the
-// ascending fetch list and its rows, copied from pinned host memory by GPU
-// loads (zero-copy) into device staging.
-__device__ __forceinline__ void gather_part(const DParams &p, int j, int g,
-                                            int b) {
+// Gather and attention over the fetched rows by workgroup j of a KV head:
+// chunks [j nch / kGatherWG, (j + 1) nch / kGatherWG) of the fetch bitmap in
+// order. For each chunk it writes its part of the ascending fetch list and
+// reads its rows from pinned host memory by GPU loads (zero-copy), 32 lanes
+// (16-byte units, K then V) per row. The K lanes form the exact logits of
+// the row for the KV head's query heads; for each head that fetches the row
+// (F_h), the half-wave folds exp(logit) and the V row into a running
+// softmax (shift, sum of weights, weighted sum of V). The eight half-waves
+// are merged at the end into the workgroup's partial, index ncr + j.
+template <int GRP>
+__device__ __forceinline__ void gather_attend(const DParams &p, int j, int g,
+                                              int b) {
   const int bg = b * p.G + g;
+  const int hw = threadIdx.x / 32;          // half-wave: one row at a time
+  const int unit = threadIdx.x % 32;        // 16-byte unit of the row
+  const bool is_v = unit >= 16;
+  const int dim0 = (unit & 15) * 8;
+  constexpr int HW = kBlock / 32;
   __shared__ int s_pos[4096];
+  __shared__ uint8_t s_msk[4096];
   __shared__ uint32_t s_red[kBlock / kWave + 1];
+  __shared__ float s_m[HW][GRP], s_d[HW][GRP];
+  __shared__ float s_o[HW][GRP][kHeadDim];
   int c0, c1;
   split_range(p.nch, kGatherWG, j, c0, c1);
   const int wpc = p.chunk / 32;
@@ -1774,9 +1820,23 @@ __device__ __forceinline__ void gather_part(const DParams &p, int j, int g,
   uint32_t before = 0;
   for (int i = threadIdx.x; i < c0 * wpc && i < p.nwords; i += kBlock)
     before += (uint32_t)__popc(fb[i]);
+  float qv[GRP][8];
+#pragma unroll
+  for (int h = 0; h < GRP; ++h) {
+    const uint4 raw = *reinterpret_cast<const uint4 *>(
+        p.q + (size_t)row_of(p, b, g, h, GRP) * kHeadDim + dim0);
+    unpack8(raw, qv[h]);
+  }
   uint32_t offset = block_sum<uint32_t>(before, s_red);
+  float mrun[GRP], dsum[GRP], acc[GRP][8];
+#pragma unroll
+  for (int h = 0; h < GRP; ++h) {
+    mrun[h] = -INFINITY;
+    dsum[h] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[h][k] = 0.0f;
+  }
   const uint16_t *src_base = p.host_kv + (size_t)bg * p.n * 2 * kHeadDim;
-  uint16_t *dst_base = p.staging + (size_t)bg * p.fetch_cap * 2 * kHeadDim;
   int32_t *fidx = p.fidx + (size_t)bg * p.fetch_cap;
   for (int c = c0; c < c1; ++c) {
     const int w0 = c * wpc;
@@ -1793,34 +1853,89 @@ __device__ __forceinline__ void gather_part(const DParams &p, int j, int g,
       }
     }
     __syncthreads();
-    for (uint32_t k = threadIdx.x; k < total; k += kBlock) {
-      const uint32_t slot = offset + k;
-      if (slot < (uint32_t)p.fetch_cap) fidx[slot] = s_pos[k];
+    // rows past fetch_cap are neither listed nor read (the status says so)
+    const uint32_t nrow = min(total, (uint32_t)p.fetch_cap > offset
+                                         ? (uint32_t)p.fetch_cap - offset : 0u);
+    for (uint32_t k = threadIdx.x; k < nrow; k += kBlock) {
+      const int pos = s_pos[k];
+      fidx[offset + k] = pos;
+      uint32_t msk = 0u;
+#pragma unroll
+      for (int h = 0; h < GRP; ++h)
+        msk |= ((p.hbits[(size_t)row_of(p, b, g, h, GRP) * p.nwords + pos / 32] >> (pos % 32)) & 1u) << h;
+      s_msk[k] = (uint8_t)msk;
     }
-    // rows (K then V, 512 bytes) in 16-byte units, four in flight per lane
-    const uint32_t lim = min(total * 32u, ((uint32_t)p.fetch_cap > offset
-                                               ? ((uint32_t)p.fetch_cap - offset) * 32u
-                                               : 0u));
-    auto src_of = [&](uint32_t u) {
-      return reinterpret_cast<const uint4 *>(
-          src_base + (size_t)s_pos[u >> 5] * 2 * kHeadDim + (u & 31u) * 8);
-    };
-    auto dst_of = [&](uint32_t u) {
-      return reinterpret_cast<uint4 *>(
-          dst_base + (size_t)(offset + (u >> 5)) * 2 * kHeadDim + (u & 31u) * 8);
-    };
-    uint32_t u = threadIdx.x;
-    for (; u + 3 * kBlock < lim; u += 4 * kBlock) {
-      const uint4 v0 = *src_of(u), v1 = *src_of(u + kBlock),
-                  v2 = *src_of(u + 2 * kBlock), v3 = *src_of(u + 3 * kBlock);
-      *dst_of(u) = v0;
-      *dst_of(u + kBlock) = v1;
-      *dst_of(u + 2 * kBlock) = v2;
-      *dst_of(u + 3 * kBlock) = v3;
+    __syncthreads();
+    for (uint32_t r0 = 0; r0 < nrow; r0 += HW * kGatherBatch) {
+      uint4 raw[kGatherBatch];
+#pragma unroll
+      for (int it = 0; it < kGatherBatch; ++it) {
+        const uint32_t rk = r0 + it * HW + hw;
+        if (rk < nrow)
+          raw[it] = *reinterpret_cast<const uint4 *>(
+              src_base + (size_t)s_pos[rk] * 2 * kHeadDim + unit * 8);
+      }
+#pragma unroll
+      for (int it = 0; it < kGatherBatch; ++it) {
+        const uint32_t rk = r0 + it * HW + hw;
+        if (rk >= nrow) continue;  // (uniform over the half-wave)
+        float x[8];
+        unpack8(raw[it], x);
+        const uint32_t msk = s_msk[rk];
+#pragma unroll
+        for (int h = 0; h < GRP; ++h) {
+          float dp = 0.0f;
+          if (!is_v) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) dp = __builtin_fmaf(qv[h][k], x[k], dp);
+          }
+          dp = group_sum<16>(dp);
+          // the V lanes take the logit from the K lanes of their row
+          const float lg = __shfl(dp, (int)(threadIdx.x % kWave) & ~16, kWave) * kInvSqrtD;
+          if (!((msk >> h) & 1u)) continue;
+          const float mn = fmaxf(mrun[h], lg);
+          const float sc = expf(mrun[h] - mn);
+          const float wgt = expf(lg - mn);
+          dsum[h] = dsum[h] * sc + wgt;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) acc[h][k] = __builtin_fmaf(wgt, x[k], acc[h][k] * sc);
+          mrun[h] = mn;
+        }
+      }
     }
-    for (; u < lim; u += kBlock) *dst_of(u) = *src_of(u);
     offset += total;
-    __syncthreads();  // s_pos is rewritten by the next chunk
+    __syncthreads();  // s_pos and s_msk are rewritten by the next chunk
+  }
+  // merge the half-waves' running sums into the workgroup's partial
+  if (unit == 16) {
+#pragma unroll
+    for (int h = 0; h < GRP; ++h) {
+      s_m[hw][h] = mrun[h];
+      s_d[hw][h] = dsum[h];
+    }
+  }
+  if (is_v) {
+#pragma unroll
+    for (int h = 0; h < GRP; ++h)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) s_o[hw][h][dim0 + k] = acc[h][k];
+  }
+  __syncthreads();
+  const int x = p.ncr + j, np = p.ncr + p.ncf;
+  for (int i = threadIdx.x; i < GRP * kHeadDim; i += kBlock) {
+    const int h = i / kHeadDim, e = i % kHeadDim;
+    float mx = -INFINITY;
+    for (int s = 0; s < HW; ++s) mx = fmaxf(mx, s_d[s][h] > 0.0f ? s_m[s][h] : -INFINITY);
+    float o = 0.0f, d = 0.0f;
+    for (int s = 0; s < HW; ++s) {
+      if (!(s_d[s][h] > 0.0f)) continue;
+      const float sc = expf(s_m[s][h] - mx);
+      o += s_o[s][h][e] * sc;
+      d += s_d[s][h] * sc;
+    }
+    const int row = row_of(p, b, g, h, GRP);
+    p.aparto[((size_t)row * kHeadDim + e) * p.npad + x] = o;
+    if (e == 0) p.apart[(size_t)row * np + x] = make_float2(mx, d);
   }
   if (j == kGatherWG - 1 && threadIdx.x == 0) {
     p.fcount[bg] = (int32_t)offset;
@@ -1831,28 +1946,26 @@ __device__ __forceinline__ void gather_part(const DParams &p, int j, int g,
 }
 
 // ------------------------------------------------------------ attention
-constexpr int kMaxFetchRowsPerBlock = 512;
+// Whether position pos is in F_h of this row (the planning marked it).
+__device__ __forceinline__ bool in_fetch(const DParams &p, int row, int pos) {
+  return (p.hbits[(size_t)row * p.nwords + pos / 32] >> (pos % 32)) & 1u;
+}
 
 // Coefficient of one resident row for one head: w on H and on F_h, and
 // lambda w / r on S \ F_h.
 template <int GRP>
 __device__ __forceinline__ float resident_alpha(const DParams &p,
                                                 const RowState &rs, int row,
-                                                int pos, float ri, float ell,
-                                                float a, float l) {
+                                                int pos, float ri, float ell) {
   const float w = expf(ell - rs.m);
-  if (ri >= 1.0f) return w;
+  if (ri >= 1.0f || in_fetch(p, row, pos)) return w;
   const Terms t = token_terms(p.shat[(size_t)row * p.n + pos], ri, rs.m,
                               (float)rs.beta, p.est);
-  if (rs.fetch && rs.kstar > 0 &&
-      is_member(make_key(token_gain(t, pos, rs, a, l), pos), rs))
-    return w;
   return t.lam * w / ri;
 }
 
-// Partial x of a KV head's attention: x < ncr covers a share of the resident
-// rows, x >= ncr a share of the fetched rows; each writes a partial (shift,
-// sum of weights, weighted sum of V) per head.
+// Partial x < ncr of a KV head's attention: a share of the resident rows,
+// written as (shift, sum of weights, weighted sum of V) per head.
 template <int GRP>
 __device__ __forceinline__ void attn_part(const DParams &p, int x, int g,
                                           int b) {
@@ -1861,13 +1974,10 @@ __device__ __forceinline__ void attn_part(const DParams &p, int x, int g,
   const int u = lane % 16;             // 8 dims per lane
   const int slot = threadIdx.x / 16;   // row slot within an iteration
   __shared__ RowState s_rs[GRP];
-  __shared__ float s_lg[GRP][kMaxFetchRowsPerBlock];
   __shared__ float s_o[kBlock / kWave][GRP][kHeadDim];
   __shared__ float s_d[kBlock / kWave][GRP];
-  __shared__ float s_red[kBlock / kWave];
   if (threadIdx.x < GRP) s_rs[threadIdx.x] = p.rows[row_of(p, b, g, threadIdx.x, GRP)];
   __syncthreads();
-  const float a = (float)p.a_delta, l = (float)p.l_delta;
   const float *rr = p.r + (size_t)bg * p.n;
   float acc[GRP][8], dsum[GRP], mloc[GRP];
 #pragma unroll
@@ -1896,92 +2006,10 @@ __device__ __forceinline__ void attn_part(const DParams &p, int x, int g,
       for (int h = 0; h < GRP; ++h) {
         const int row = row_of(p, b, g, h, GRP);
         const float alpha = resident_alpha<GRP>(
-            p, s_rs[h], row, pos, ri, p.ell[(size_t)row * p.cap + j], a, l);
+            p, s_rs[h], row, pos, ri, p.ell[(size_t)row * p.cap + j]);
         dsum[h] += alpha;
 #pragma unroll
         for (int k = 0; k < 8; ++k) acc[h][k] = __builtin_fmaf(alpha, vv[k], acc[h][k]);
-      }
-    }
-  } else {
-    const int fc = max(0, min(p.fcount[bg], p.fetch_cap));
-    int lo, hi;
-    split_range(fc, p.ncf, x - p.ncr, lo, hi);
-    const int32_t *fidx = p.fidx + (size_t)bg * p.fetch_cap;
-    const uint16_t *st = p.staging + (size_t)bg * p.fetch_cap * 2 * kHeadDim;
-    if (lo < hi) {
-      float qv[GRP][8];
-#pragma unroll
-      for (int h = 0; h < GRP; ++h) {
-        const uint4 raw = *reinterpret_cast<const uint4 *>(
-            p.q + (size_t)row_of(p, b, g, h, GRP) * kHeadDim + u * 8);
-        unpack8(raw, qv[h]);
-      }
-      // sub-blocks of at most kMaxFetchRowsPerBlock rows; the running shift
-      // only grows, and earlier sums are rescaled when it does
-      for (int sub = lo; sub < hi; sub += kMaxFetchRowsPerBlock) {
-        const int shi = min(sub + kMaxFetchRowsPerBlock, hi);
-        float mb[GRP];
-#pragma unroll
-        for (int h = 0; h < GRP; ++h) mb[h] = -INFINITY;
-        // pass 1: exact logits of the fetched rows that belong to F_h
-        for (int j0 = sub; j0 < shi; j0 += kBlock / 16) {
-          const int j = j0 + slot;
-          if (j >= shi) continue;
-          const int pos = fidx[j];
-          const float ri = rr[pos];
-          const uint4 raw =
-              *reinterpret_cast<const uint4 *>(st + (size_t)j * 2 * kHeadDim + u * 8);
-          float kk[8];
-          unpack8(raw, kk);
-#pragma unroll
-          for (int h = 0; h < GRP; ++h) {
-            float accd = 0.0f;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) accd = __builtin_fmaf(qv[h][k], kk[k], accd);
-            const float lg = group_sum<16>(accd) * kInvSqrtD;
-            const RowState &rs = s_rs[h];
-            bool member = false;
-            if (rs.fetch && rs.kstar > 0) {
-              const int row = row_of(p, b, g, h, GRP);
-              const Terms t = token_terms(p.shat[(size_t)row * p.n + pos], ri, rs.m,
-                                          (float)rs.beta, p.est);
-              member = is_member(make_key(token_gain(t, pos, rs, a, l), pos), rs);
-            }
-            const float v = member ? lg : -INFINITY;
-            if (u == 0) s_lg[h][j - sub] = v;
-            mb[h] = fmaxf(mb[h], v);
-          }
-        }
-#pragma unroll
-        for (int h = 0; h < GRP; ++h) {
-          const float m2 = fmaxf(mloc[h], block_max<float>(mb[h], s_red));
-          if (m2 > mloc[h]) {
-            const float sc = expf(mloc[h] - m2);
-            dsum[h] *= sc;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) acc[h][k] *= sc;
-            mloc[h] = m2;
-          }
-        }
-        __syncthreads();
-        // pass 2: weights and values
-        for (int j0 = sub; j0 < shi; j0 += kBlock / 16) {
-          const int j = j0 + slot;
-          if (j >= shi) continue;
-          const uint4 raw = *reinterpret_cast<const uint4 *>(
-              st + (size_t)j * 2 * kHeadDim + kHeadDim + u * 8);
-          float vv[8];
-          unpack8(raw, vv);
-#pragma unroll
-          for (int h = 0; h < GRP; ++h) {
-            const float lg = s_lg[h][j - sub];
-            const float alpha = lg == -INFINITY ? 0.0f : expf(lg - mloc[h]);
-            dsum[h] += alpha;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) acc[h][k] = __builtin_fmaf(alpha, vv[k], acc[h][k]);
-          }
-        }
-        __syncthreads();
       }
     }
   }
@@ -2083,17 +2111,13 @@ template <int GRP>
 __global__ __launch_bounds__(kBlock) void dk_fetch(DParams p) {
   const int x = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   if (x < p.ncr) attn_part<GRP>(p, x, g, b);
-  else gather_part(p, x - p.ncr, g, b);
+  else gather_attend<GRP>(p, x - p.ncr, g, b);
 }
 
-// The fetched rows' share of the attention, then the merge by the last
-// block of each KV head.
+// The merge of each KV head's partials. Grid (G, B).
 template <int GRP>
 __global__ __launch_bounds__(kBlock) void dk_attn(DParams p) {
-  const int g = blockIdx.y, b = blockIdx.z;
-  attn_part<GRP>(p, p.ncr + (int)blockIdx.x, g, b);
-  if (!last_block_arrive(&p.groups[b * p.G + g].arrive[ARR_ATTN], gridDim.x)) return;
-  attn_merge<GRP>(p, g, b);
+  attn_merge<GRP>(p, (int)blockIdx.x, (int)blockIdx.y);
 }
 
 // Records the timing event after kernel `k` when the caller asked for it.
@@ -2130,24 +2154,20 @@ hipError_t run(const DParams &p, hipStream_t s, int sd, void **events) {
   }
   dk_rcert<GRP><<<grow, blk, 0, s>>>(p);
   mark(k++);
-  dk_rcount<GRP><<<grow, blk, 0, s>>>(p);
-  mark(k++);
-  dk_rresolve<GRP><<<gone, dim3(kPlanThreads), 0, s>>>(p);
-  mark(k++);
-  dk_rcollect<GRP><<<grow, blk, 0, s>>>(p);
+  dk_rcand<GRP><<<dim3((unsigned)kSelWG, (unsigned)p.Hq, (unsigned)p.B), blk, 0, s>>>(p);
   mark(k++);
   dk_rwalk<GRP><<<gone, dim3(kPlanThreads), 0, s>>>(p);
   mark(k++);
   dk_fetch<GRP><<<dim3((unsigned)(p.ncr + kGatherWG), (unsigned)p.G, (unsigned)p.B), blk, 0, s>>>(p);
   mark(k++);
-  dk_attn<GRP><<<dim3((unsigned)p.ncf, (unsigned)p.G, (unsigned)p.B), blk, 0, s>>>(p);
+  dk_attn<GRP><<<dim3((unsigned)p.G, (unsigned)p.B), blk, 0, s>>>(p);
   mark(k++);
   return hipGetLastError();
 }
 
 const char *const kPhaseNames[] = {
     "scan",  "resident", "beta0",   "beta1",   "beta2", "beta3", "beta4",
-    "cert",  "count",    "resolve", "collect", "walk",  "fetch", "attn"};
+    "cert",  "cand",     "walk",    "fetch", "attn"};
 
 }  // namespace
 
@@ -2171,7 +2191,7 @@ DecodeLayout decode_layout(const vkv_decode_args &a) {
   const int rmax = a.cap < a.n_tokens ? a.cap : a.n_tokens;
   // (each at most 32, so the merge sees at most 64 partial sums)
   L.ncr = std::max(1, std::min(std::min(target, 32), (rmax + 63) / 64));
-  L.ncf = std::max(1, std::min(std::min(target, 32), (a.fetch_cap + 63) / 64));
+  L.ncf = kGatherWG;
   L.npad = (L.ncr + L.ncf + 3) / 4 * 4;
   L.nwords = (a.n_tokens + 31) / 32;
   const size_t B = (size_t)a.batch, Hq = (size_t)a.n_q_heads,
@@ -2184,6 +2204,7 @@ DecodeLayout decode_layout(const vkv_decode_args &a) {
   L.ell = c.take<float>(rows * (size_t)a.cap);
   L.resbits = c.take<uint32_t>(groups * L.nwords);
   L.fbits = c.take<uint32_t>(groups * L.nwords);
+  L.hbits = c.take<uint32_t>(rows * L.nwords);
   L.pmax = c.take<float>(rows * (L.nch + L.ncr));
   L.hpart = c.take<uint32_t>(groups * (L.nch + L.ncr));  // H counts per chunk
   L.nrc = (a.n_tokens + kRowChunk - 1) / kRowChunk;
@@ -2191,18 +2212,16 @@ DecodeLayout decode_layout(const vkv_decode_args &a) {
   L.bstate = c.take<BetaState>(2 * rows);
   L.rbeta = c.take<double>(2 * rows);
   L.cpart = c.take<CertPart>(rows * L.nrc);
-  L.khist = c.take<uint32_t>(rows * L.nrc * (size_t)kSelBinsP);
-  L.tpart = c.take<unsigned long long>(rows * L.nrc * 2);
-  L.sel = c.take<SelState>(rows);
-  L.ccount = c.take<uint32_t>(rows);
+  L.ccount = c.take<uint32_t>(rows * kSelWG);
+  L.clo = c.take<unsigned long long>(rows * kSelWG);
+  L.tpart = c.take<unsigned long long>(rows * kSelWG * 2);
   L.candk = c.take<unsigned long long>(rows * (size_t)kCandMax);
   L.candb = c.take<unsigned long long>(rows * (size_t)kCandMax);
   L.candv = c.take<unsigned long long>(rows * (size_t)kCandMax);
   L.candr = c.take<uint32_t>(rows * (size_t)kCandMax);
-  L.rpart = c.take<uint32_t>(rows * L.nrc);
+  L.rpart = c.take<uint32_t>(rows * kSelWG);
   L.apart = c.take<float2>(rows * (L.ncr + L.ncf));
   L.aparto = c.take<float>(rows * kHeadDim * (size_t)L.npad);
-  L.staging = c.take<uint16_t>(groups * (size_t)a.fetch_cap * 2 * kHeadDim);
   L.total = (c.off + 255) & ~size_t(255);
   return L;
 }
@@ -2236,16 +2255,16 @@ hipError_t launch_decode(const vkv_decode_args &a, const DecodeLayout &L,
   p.ell = at<float>(w, L.ell);
   p.resbits = at<uint32_t>(w, L.resbits);
   p.fbits = at<uint32_t>(w, L.fbits);
+  p.hbits = at<uint32_t>(w, L.hbits);
   p.pmax = at<float>(w, L.pmax);
   p.hpart = at<uint32_t>(w, L.hpart);
   p.bpart = at<double>(w, L.bpart);
   p.bstate = at<BetaState>(w, L.bstate);
   p.rbeta = at<double>(w, L.rbeta);
   p.cpart = at<CertPart>(w, L.cpart);
-  p.khist = at<uint32_t>(w, L.khist);
-  p.tpart = at<unsigned long long>(w, L.tpart);
-  p.sel = at<SelState>(w, L.sel);
   p.ccount = at<uint32_t>(w, L.ccount);
+  p.clo = at<unsigned long long>(w, L.clo);
+  p.tpart = at<unsigned long long>(w, L.tpart);
   p.candk = at<unsigned long long>(w, L.candk);
   p.candb = at<unsigned long long>(w, L.candb);
   p.candv = at<unsigned long long>(w, L.candv);
@@ -2255,7 +2274,6 @@ hipError_t launch_decode(const vkv_decode_args &a, const DecodeLayout &L,
   p.apart = at<float2>(w, L.apart);
   p.aparto = at<float>(w, L.aparto);
   p.npad = L.npad;
-  p.staging = at<uint16_t>(w, L.staging);
   p.B = a.batch;
   p.Hq = a.n_q_heads;
   p.G = a.n_kv_heads;

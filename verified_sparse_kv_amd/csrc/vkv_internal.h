@@ -54,9 +54,10 @@ hipError_t launch_compress(const vkv_compress_args &a, const CompressLayout &L,
 // ------------------------------------------------------------ decoding
 struct DecodeLayout {
   int grp, nch, ncr, ncf, npad, nwords, chunk, nrc;
-  size_t shat, ell, hpart, resbits, fbits, pmax, rows, groups, bpart, bstate,
-      rbeta, cpart, khist, tpart, sel, ccount, candk, candb, candv, candr,
-      rpart, apart, aparto, staging, total;
+  size_t shat, ell, hpart, resbits, fbits, hbits, pmax, rows, groups, bpart,
+      bstate,
+      rbeta, cpart, ccount, clo, tpart, candk, candb, candv, candr,
+      rpart, apart, aparto, total;
 };
 
 DecodeLayout decode_layout(const vkv_decode_args &a);
