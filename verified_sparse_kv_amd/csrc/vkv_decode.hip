@@ -5,12 +5,15 @@
 // ("rows"). Kernels, in launch order:
 //
 //  dk_scan      sketch logits s_i = <P_g^T q, sk_i>/sqrt(d) for every token and
-//               the GRP heads at once (one sketch row serves all of them).
+//               the GRP heads at once (one sketch row serves all of them),
+//               and per chunk the pass-0 sums of the beta* iteration with the
+//               chunk's own shift.
 //  dk_resident  exact logits l_j = <q, k_j>/sqrt(d) on the resident rows,
-//               residency bitmap, common shift m = max(max_R l, max_L s).
-//  dk_rbeta x5  D~ = sum_H w + sum_L w~, then the Definition 2 fixed point
-//               beta* by a bracketed Newton iteration on a convex piecewise-
-//               linear function (one launch per pass).
+//               residency bitmap, per part the shift and sum_H exp(l).
+//  dk_rbeta x4  common shift m = max(max_R l, max_L s), D~ = sum_H w + sum_L
+//               w~, then the Definition 2 fixed point beta* by a bracketed
+//               Newton iteration on a convex piecewise-linear function (one
+//               launch per pass).
 //  dk_rcert     lambda_i, beta(L), V(L) and the top two b_i per chunk
 //               (Lemma 1, eq. 7).
 //  dk_rcand     eps^(L) and, for a row that must fetch, the gain keys (eq. 9)
@@ -24,8 +27,7 @@
 //
 // Passes over a row's tokens run as many workgroups per row; every
 // workgroup combines the partial records of the previous launch itself, so
-// no workgroup waits for another. dk_resident alone ends in a "last block
-// done" step per group.
+// no workgroup waits for another.
 //
 // All per-token recomputations (weights, lambda, certificate terms, gains)
 // go through the same inline functions and the library is built with
@@ -60,9 +62,6 @@ struct RowState {
   float eps1;             // eps^(L') after fetching
 };
 
-struct GroupState {
-  uint32_t arrive[8];
-};
 
 // State of a row's beta* iteration between launches.
 struct BetaState {
@@ -81,7 +80,6 @@ struct CertPart {
 };
 
 
-enum { ARR_RES = 0 };
 
 struct DParams {
   const uint16_t *q, *rkv, *sketch, *host_kv;
@@ -95,10 +93,11 @@ struct DParams {
   float *shat, *ell;
   uint32_t *resbits, *fbits;
   uint32_t *hbits;   // [row][nwords] F_h of each row
-  float *pmax;
+  float *pmax;       // [row][nch + ncr] shift of each scan chunk / resident part
+  double *p0part;    // [row][nch + ncr][4] pass-0 sums of each scan chunk
+  double *hres;      // [row][ncr] sum over H of exp(l - shift) per part
   uint32_t *hpart;
   RowState *rows;
-  GroupState *groups;
   double *bpart;     // [2][row][nrc][kBetaRec] beta pass records
   BetaState *bstate; // [2][row]
   double *rbeta;     // [row][2] beta*, D~
@@ -208,366 +207,9 @@ __device__ __forceinline__ T wave_incl_scan(T v, int lane) {
   return v;
 }
 
-// ------------------------------------------------------------ dk_scan
-template <int GRP, int SD>
-__global__ __launch_bounds__(kBlock) void dk_scan(DParams p) {
-  constexpr int LPT = SD / 8;           // lanes per token (16 bytes each)
-  constexpr int TPI = kBlock / LPT;     // tokens per block iteration
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int bg = b * p.G + g;
-  const int lane = threadIdx.x % kWave;
-  __shared__ float s_qp[GRP][SD];
-  __shared__ float s_red[kBlock / kWave];
-  __shared__ uint32_t s_ured[kBlock / kWave];
-
-  // step-start initialisation of this group's state (no other block of
-  // this launch touches it)
-  if (c == 0) {
-    if (threadIdx.x < 8) p.groups[bg].arrive[threadIdx.x] = 0u;
-    for (int h = 0; h < GRP; ++h) {
-      const int row = row_of(p, b, g, h, GRP);
-      if (threadIdx.x == 0) {
-        RowState z{};
-        z.amax = -1;
-        z.T = ~0ull;
-        p.rows[row] = z;
-      }
-    }
-    if (bg == 0 && threadIdx.x == 0) {
-      *p.status = 0u;
-      *p.host_bytes = 0ull;
-    }
-  }
-  // clear this chunk's bitmap words
-  {
-    const int w0 = c * p.chunk / 32, nw = p.chunk / 32;
-    for (int w = threadIdx.x; w < nw; w += kBlock) {
-      if (w0 + w < p.nwords) {
-        p.resbits[(size_t)bg * p.nwords + w0 + w] = 0u;
-        p.fbits[(size_t)bg * p.nwords + w0 + w] = 0u;
-        for (int h = 0; h < GRP; ++h)
-          p.hbits[(size_t)row_of(p, b, g, h, GRP) * p.nwords + w0 + w] = 0u;
-      }
-    }
-  }
-  // projected, pre-scaled queries: stage q and P_g in LDS, then one output
-  // per thread
-  {
-    __shared__ float s_proj[kHeadDim * SD];
-    __shared__ float s_q[GRP][kHeadDim];
-    const float4 *P4 =
-        reinterpret_cast<const float4 *>(p.proj + (size_t)g * kHeadDim * SD);
-    for (int i = threadIdx.x; i < kHeadDim * SD / 4; i += kBlock)
-      reinterpret_cast<float4 *>(s_proj)[i] = P4[i];
-    for (int i = threadIdx.x; i < GRP * kHeadDim; i += kBlock) {
-      const int h = i / kHeadDim, e = i % kHeadDim;
-      s_q[h][e] = __uint_as_float(
-          (uint32_t)p.q[(size_t)row_of(p, b, g, h, GRP) * kHeadDim + e] << 16);
-    }
-    __syncthreads();
-    if (threadIdx.x < GRP * SD) {
-      const int h = threadIdx.x / SD, j = threadIdx.x % SD;
-      float acc = 0.0f;
-      for (int e = 0; e < kHeadDim; ++e)
-        acc = __builtin_fmaf(s_proj[e * SD + j], s_q[h][e], acc);
-      s_qp[h][j] = acc * kInvSqrtD;
-    }
-    __syncthreads();
-  }
-  const int u = lane % LPT;
-  float qv[GRP][8];
-#pragma unroll
-  for (int h = 0; h < GRP; ++h)
-#pragma unroll
-    for (int k = 0; k < 8; ++k) qv[h][k] = s_qp[h][u * 8 + k];
-
-  float mx[GRP];
-#pragma unroll
-  for (int h = 0; h < GRP; ++h) mx[h] = -INFINITY;
-  uint32_t n_h = 0;
-  bool bad = false;
-  const uint16_t *sk = p.sketch + (size_t)bg * p.n * SD;
-  const float *rr = p.r + (size_t)bg * p.n;
-  const int base = c * p.chunk;
-  const int lim = min(base + p.chunk, p.n);
-  constexpr int UNR = 4;  // sketch rows in flight per lane
-  for (int i0 = base; i0 < lim; i0 += TPI * UNR) {
-    uint4 raw[UNR];
-    float rv[UNR];
-#pragma unroll
-    for (int k = 0; k < UNR; ++k) {
-      const int i = i0 + k * TPI + threadIdx.x / LPT;
-      if (i < lim) {
-        raw[k] = *reinterpret_cast<const uint4 *>(sk + (size_t)i * SD + u * 8);
-        rv[k] = rr[i];
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < UNR; ++k) {
-      const int i = i0 + k * TPI + threadIdx.x / LPT;
-      if (i >= lim) continue;
-      float f[8];
-      unpack8(raw[k], f);
-      float dot[GRP];
-#pragma unroll
-      for (int h = 0; h < GRP; ++h) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(qv[h][e], f[e], acc);
-        dot[h] = group_sum<LPT>(acc);
-      }
-      const float ri = rv[k];
-      if (!(ri > 0.0f && ri <= 1.0f)) bad = true;
-      const bool in_l = ri < 1.0f;
-      if (u == 0 && !in_l) ++n_h;
-#pragma unroll
-      for (int h = 0; h < GRP; ++h) {
-        if (h % LPT == u)
-          p.shat[(size_t)row_of(p, b, g, h, GRP) * p.n + i] = dot[h];
-        if (in_l) mx[h] = fmaxf(mx[h], dot[h]);
-      }
-    }
-  }
-  if (bad) atomicOr(p.status, VKV_STATUS_BAD_R);
-#pragma unroll
-  for (int h = 0; h < GRP; ++h) {
-    const float v = block_max<float>(mx[h], s_red);
-    if (threadIdx.x == 0)
-      p.pmax[(size_t)row_of(p, b, g, h, GRP) * (p.nch + p.ncr) + c] = v;
-  }
-  const uint32_t th = block_sum<uint32_t>(n_h, s_ured);
-  if (threadIdx.x == 0) p.hpart[(size_t)bg * (p.nch + p.ncr) + c] = th;
-}
-
-// Same outputs with exact keys read from the host cache (perfect sketch).
-template <int GRP>
-__global__ __launch_bounds__(kBlock) void dk_scan_exact(DParams p) {
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int bg = b * p.G + g;
-  const int lane = threadIdx.x % kWave;
-  __shared__ float s_red[kBlock / kWave];
-  __shared__ uint32_t s_ured[kBlock / kWave];
-  if (c == 0) {
-    if (threadIdx.x < 8) p.groups[bg].arrive[threadIdx.x] = 0u;
-    for (int h = 0; h < GRP; ++h) {
-      const int row = row_of(p, b, g, h, GRP);
-      if (threadIdx.x == 0) {
-        RowState z{};
-        z.amax = -1;
-        z.T = ~0ull;
-        p.rows[row] = z;
-      }
-    }
-    if (bg == 0 && threadIdx.x == 0) {
-      *p.status = 0u;
-      *p.host_bytes = 0ull;
-    }
-  }
-  {
-    const int w0 = c * p.chunk / 32, nw = p.chunk / 32;
-    for (int w = threadIdx.x; w < nw; w += kBlock) {
-      if (w0 + w < p.nwords) {
-        p.resbits[(size_t)bg * p.nwords + w0 + w] = 0u;
-        p.fbits[(size_t)bg * p.nwords + w0 + w] = 0u;
-        for (int h = 0; h < GRP; ++h)
-          p.hbits[(size_t)row_of(p, b, g, h, GRP) * p.nwords + w0 + w] = 0u;
-      }
-    }
-  }
-  const int u = lane % 16;
-  float qv[GRP][8];
-#pragma unroll
-  for (int h = 0; h < GRP; ++h) {
-    const uint4 raw = *reinterpret_cast<const uint4 *>(
-        p.q + (size_t)row_of(p, b, g, h, GRP) * kHeadDim + u * 8);
-    unpack8(raw, qv[h]);
-  }
-  float mx[GRP];
-#pragma unroll
-  for (int h = 0; h < GRP; ++h) mx[h] = -INFINITY;
-  uint32_t n_h = 0;
-  bool bad = false;
-  const float *rr = p.r + (size_t)bg * p.n;
-  const int base = c * p.chunk;
-  const int lim = min(base + p.chunk, p.n);
-  for (int i0 = base; i0 < lim; i0 += kBlock / 16) {
-    const int i = i0 + threadIdx.x / 16;
-    if (i < lim) {
-      const float ri = rr[i];
-      if (!(ri > 0.0f && ri <= 1.0f)) bad = true;
-      const bool in_l = ri < 1.0f;
-      if (u == 0 && !in_l) ++n_h;
-      float dot[GRP];
-      if (in_l) {
-        const uint4 raw = *reinterpret_cast<const uint4 *>(
-            p.host_kv + ((size_t)bg * p.n + i) * 2 * kHeadDim + u * 8);
-        float f[8];
-        unpack8(raw, f);
-#pragma unroll
-        for (int h = 0; h < GRP; ++h) {
-          float acc = 0.0f;
-#pragma unroll
-          for (int k = 0; k < 8; ++k) acc = __builtin_fmaf(qv[h][k], f[k], acc);
-          dot[h] = group_sum<16>(acc) * kInvSqrtD;
-          mx[h] = fmaxf(mx[h], dot[h]);
-        }
-      } else {
-#pragma unroll
-        for (int h = 0; h < GRP; ++h) dot[h] = 0.0f;
-      }
-#pragma unroll
-      for (int h = 0; h < GRP; ++h)
-        if (u == h) p.shat[(size_t)row_of(p, b, g, h, GRP) * p.n + i] = dot[h];
-    }
-  }
-  if (bad) atomicOr(p.status, VKV_STATUS_BAD_R);
-#pragma unroll
-  for (int h = 0; h < GRP; ++h) {
-    const float v = block_max<float>(mx[h], s_red);
-    if (threadIdx.x == 0)
-      p.pmax[(size_t)row_of(p, b, g, h, GRP) * (p.nch + p.ncr) + c] = v;
-  }
-  const uint32_t th = block_sum<uint32_t>(n_h, s_ured);
-  if (threadIdx.x == 0) p.hpart[(size_t)bg * (p.nch + p.ncr) + c] = th;
-}
-
-// ------------------------------------------------------------ dk_resident
-// The group's resident rows are split evenly over gridDim.x workgroups.
-template <int GRP>
-__global__ __launch_bounds__(kBlock) void dk_resident(DParams p) {
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int bg = b * p.G + g;
-  const int lane = threadIdx.x % kWave;
-  const int u = lane % 16;
-  __shared__ float s_red[kBlock / kWave];
-  __shared__ uint32_t s_ured[kBlock / kWave];
-  float qv[GRP][8];
-#pragma unroll
-  for (int h = 0; h < GRP; ++h) {
-    const uint4 raw = *reinterpret_cast<const uint4 *>(
-        p.q + (size_t)row_of(p, b, g, h, GRP) * kHeadDim + u * 8);
-    unpack8(raw, qv[h]);
-  }
-  int cnt = p.rcount[bg];
-  bool bad = cnt < 0 || cnt > p.cap;
-  cnt = max(0, min(cnt, p.cap));
-  const int32_t *ridx = p.ridx + (size_t)bg * p.cap;
-  const float *rr = p.r + (size_t)bg * p.n;
-  float mx[GRP];
-#pragma unroll
-  for (int h = 0; h < GRP; ++h) mx[h] = -INFINITY;
-  uint32_t n_h = 0;
-  int lo, hi;
-  split_range(cnt, gridDim.x, c, lo, hi);
-  for (int j0 = lo; j0 < hi; j0 += kBlock / 16) {
-    const int j = j0 + threadIdx.x / 16;
-    if (j < hi) {
-      const int pos = ridx[j];
-      const bool ok = pos >= 0 && pos < p.n && (j == 0 || ridx[j - 1] < pos);
-      const uint4 raw = *reinterpret_cast<const uint4 *>(
-          p.rkv + ((size_t)bg * p.cap + j) * 2 * kHeadDim + u * 8);
-      float f[8];
-      unpack8(raw, f);
-#pragma unroll
-      for (int h = 0; h < GRP; ++h) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) acc = __builtin_fmaf(qv[h][k], f[k], acc);
-        const float dot = group_sum<16>(acc) * kInvSqrtD;
-        if (u == h) p.ell[(size_t)row_of(p, b, g, h, GRP) * p.cap + j] = dot;
-        mx[h] = fmaxf(mx[h], dot);
-      }
-      if (u == 0) {
-        if (ok) {
-          atomicOr(p.resbits + (size_t)bg * p.nwords + pos / 32,
-                   1u << (pos % 32));
-          if (rr[pos] >= 1.0f) ++n_h;
-        } else {
-          bad = true;
-        }
-      }
-    }
-  }
-  if (bad) atomicOr(p.status, VKV_STATUS_BAD_RESIDENT);
-  const int np = p.nch + p.ncr;
-#pragma unroll
-  for (int h = 0; h < GRP; ++h) {
-    const float v = block_max<float>(mx[h], s_red);
-    if (threadIdx.x == 0)
-      p.pmax[(size_t)row_of(p, b, g, h, GRP) * np + p.nch + c] = v;
-  }
-  const uint32_t th = block_sum<uint32_t>(n_h, s_ured);
-  if (threadIdx.x == 0) p.hpart[(size_t)bg * np + p.nch + c] = th;
-  if (!last_block_arrive(&p.groups[bg].arrive[ARR_RES], gridDim.x)) return;
-  // shift per row (one wave per head); every token with r == 1 must be resident
-  const int wave = threadIdx.x / kWave;
-  for (int h = wave; h < GRP; h += kBlock / kWave) {
-    const int row = row_of(p, b, g, h, GRP);
-    float m = -INFINITY;
-    for (int i = lane; i < np; i += kWave) m = fmaxf(m, p.pmax[(size_t)row * np + i]);
-    m = wave_max(m);
-    if (lane == 0) p.rows[row].m = m;
-  }
-  if (wave == 0) {
-    uint32_t all_h = 0, res_h = 0;
-    for (int i = lane; i < p.nch; i += kWave) all_h += p.hpart[(size_t)bg * np + i];
-    for (int i = lane; i < p.ncr; i += kWave) res_h += p.hpart[(size_t)bg * np + p.nch + i];
-    all_h = wave_sum(all_h);
-    res_h = wave_sum(res_h);
-    if (lane == 0 && all_h != res_h) atomicOr(p.status, VKV_STATUS_BAD_RESIDENT);
-  }
-}
-
-// ------------------------------------------------------------ planning
-// The plan of Algorithm 2 for every (request, query head) ("row"):
-//   D~ -> beta* -> certificate (Lemma 1, eq. 7) -> k* (eq. 10) -> F_h.
-// Data-parallel passes over a row's tokens run as launches of kBlock-thread
-// workgroups, one per chunk of kRowChunk tokens of a row; each writes a
-// partial record, and every workgroup of the next launch combines the
-// records of its row itself (in one fixed order, so all of them get
-// bit-identical results). No workgroup ever waits for another.
-//
-// beta*: at the root, beta* >= max_i w~_i (1 - r_i) (below that the heaviest
-// token alone would give more than beta), so every token is at or above its
-// lower clip and the Definition 2 fixed point is also the unique root of
-//     h(beta) = sum_i max(0, w~_i - beta rho_i) - beta,  rho_i = r_i/(1-r_i),
-// a convex, decreasing, piecewise-linear function. Pass 0 gives the sums at
-// beta = 0 and the lower bound above; each later pass evaluates, at
-// kBetaPts points of the bracket [lo, hi], the sums of w~ and rho over the
-// active set A(beta) = {w~_i > beta rho_i} and its size. The Newton step
-// from a point with h >= 0, beta' = sum_A w~ / (1 + sum_A rho), never
-// overshoots the root (convexity); it is the root itself when no breakpoint
-// lies between the point and the next evaluated point (equal active counts)
-// or when the next pass finds the same active set at beta'. Since h' <= -1,
-// beta + h(beta) bounds the root from above. A row still open after the
-// last Newton launch finishes in the certificate launch, where each of its
-// workgroups iterates over the whole row (rare; same arithmetic).
-//
-// Selection: keys (gain bits, inverted position) order L as L_g
-// (descending). Each of kSelWG workgroups per row takes a block-cyclic
-// share of the row's tokens and writes its keys at or above a local bound
-// lo_s (at most kCandWG of them) with their fixed-point beta_i and v_i and
-// range term b_i. One workgroup per row then runs the stopping rule on the
-// union to the exact k* and threshold T; that is the answer whenever T >=
-// max_s lo_s (every key >= T was written). Otherwise, or when fetching every
-// candidate cannot certify the row, it runs the streaming selection below
-// instead. All sums of the selection are fixed-point integers, so a rest's
-// sum is the total minus the fetched part exactly.
+// ------------------------------------------------------------ reductions
 constexpr int kPlanThreads = 1024;  // row-level workgroups
 constexpr int kPlanWaves = kPlanThreads / kWave;
-constexpr int kSelUnroll = 4;       // streamed tokens per thread in flight
-constexpr int kRowChunk = 2048;     // tokens per workgroup in row passes
-constexpr int kRowTok = kRowChunk / kBlock;
-constexpr int kBetaPts = 4;         // points of h per Newton pass
-constexpr int kBetaRec = 3 * kBetaPts;
-constexpr int kBetaLaunches = 5;    // pass 0 and four Newton passes
-constexpr int kBetaPassMax = 96;    // never reached: the bracket shrinks >= 2x
-constexpr int kCandMax = 4096;      // candidates sorted by the walk
-constexpr int kSelDigit = 11;
-constexpr int kSelBinsP = 1 << kSelDigit;
-constexpr int kSelLevels = 5;       // five 11-bit digits cover the 55-bit key
-constexpr unsigned long long kKeyEnd = 1ull << 55;  // above every key
-__device__ __forceinline__ int sel_off(int d) { return 44 - kSelDigit * d; }
 
 // rho = r / (1 - r); the same expression in every pass.
 __device__ __forceinline__ float plan_rho(float r) {
@@ -682,6 +324,420 @@ __device__ __forceinline__ void blk_top2(float &x1, int &p1, float &x2) {
   x2 = b2[THREADS + 16];
   p1 = bp[THREADS + 16];
 }
+
+// ------------------------------------------------------------ dk_scan
+// End of a scan chunk: the per-head maxima over L of the chunk's logits
+// (sd[h][t], r in sr[t], cnt tokens, staged in LDS), then pass 0 of the
+// beta* iteration with the chunk's own shift mL: sum_L w~, sum rho over w~ >
+// 0, their count, and max w~ (1 - r). The planning rescales them to the
+// common shift.
+template <int GRP>
+__device__ __forceinline__ void scan_finish(const DParams &p, int b, int g,
+                                            int c, int cnt, float (&mx)[GRP],
+                                            float (*sd)[kChunk],
+                                            const float *sr) {
+  const int np = p.nch + p.ncr;
+  blk_combine<float, GRP, kBlock, OpMax<float>>(mx);
+  constexpr int HG = GRP < 4 ? GRP : 4;  // heads per reduction
+#pragma unroll
+  for (int h0 = 0; h0 < GRP; h0 += HG) {
+    double v0[3 * HG], lbm[HG];
+#pragma unroll
+    for (int k = 0; k < 3 * HG; ++k) v0[k] = 0.0;
+#pragma unroll
+    for (int k = 0; k < HG; ++k) lbm[k] = 0.0;
+    for (int t = threadIdx.x; t < cnt; t += kBlock) {
+      const float ri = sr[t];
+      if (!(ri < 1.0f)) continue;
+      const float rho = plan_rho(ri);
+#pragma unroll
+      for (int k = 0; k < HG; ++k) {
+        const float wt = expf(sd[h0 + k][t] - mx[h0 + k]);
+        v0[3 * k] += (double)wt;
+        if (wt > 0.0f) {
+          v0[3 * k + 1] += (double)rho;
+          v0[3 * k + 2] += 1.0;
+          lbm[k] = fmax(lbm[k], (double)(wt * (1.0f - ri)));
+        }
+      }
+    }
+    blk_reduce<double, 3 * HG, kBlock>(v0);
+    blk_combine<double, HG, kBlock, OpMax<double>>(lbm);
+    if (threadIdx.x == 0) {
+#pragma unroll
+      for (int k = 0; k < HG; ++k) {
+        const int row = row_of(p, b, g, h0 + k, GRP);
+        p.pmax[(size_t)row * np + c] = mx[h0 + k];
+        double *rec = p.p0part + ((size_t)row * np + c) * 4;
+        rec[0] = v0[3 * k];
+        rec[1] = v0[3 * k + 1];
+        rec[2] = v0[3 * k + 2];
+        rec[3] = lbm[k];
+      }
+    }
+  }
+}
+
+template <int GRP, int SD>
+__global__ __launch_bounds__(kBlock) void dk_scan(DParams p) {
+  constexpr int LPT = SD / 8;           // lanes per token (16 bytes each)
+  constexpr int TPI = kBlock / LPT;     // tokens per block iteration
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int bg = b * p.G + g;
+  const int lane = threadIdx.x % kWave;
+  __shared__ float s_qp[GRP][SD];
+  __shared__ uint32_t s_ured[kBlock / kWave];
+
+  // step-start initialisation of this group's state (no other block of
+  // this launch touches it)
+  if (c == 0) {
+    for (int h = 0; h < GRP; ++h) {
+      const int row = row_of(p, b, g, h, GRP);
+      if (threadIdx.x == 0) {
+        RowState z{};
+        z.amax = -1;
+        z.T = ~0ull;
+        p.rows[row] = z;
+      }
+    }
+    if (bg == 0 && threadIdx.x == 0) {
+      *p.status = 0u;
+      *p.host_bytes = 0ull;
+    }
+  }
+  // clear this chunk's bitmap words
+  {
+    const int w0 = c * p.chunk / 32, nw = p.chunk / 32;
+    for (int w = threadIdx.x; w < nw; w += kBlock) {
+      if (w0 + w < p.nwords) {
+        p.resbits[(size_t)bg * p.nwords + w0 + w] = 0u;
+        p.fbits[(size_t)bg * p.nwords + w0 + w] = 0u;
+        for (int h = 0; h < GRP; ++h)
+          p.hbits[(size_t)row_of(p, b, g, h, GRP) * p.nwords + w0 + w] = 0u;
+      }
+    }
+  }
+  // projected, pre-scaled queries: stage q and P_g in LDS, then one output
+  // per thread
+  {
+    __shared__ float s_proj[kHeadDim * SD];
+    __shared__ float s_q[GRP][kHeadDim];
+    const float4 *P4 =
+        reinterpret_cast<const float4 *>(p.proj + (size_t)g * kHeadDim * SD);
+    for (int i = threadIdx.x; i < kHeadDim * SD / 4; i += kBlock)
+      reinterpret_cast<float4 *>(s_proj)[i] = P4[i];
+    for (int i = threadIdx.x; i < GRP * kHeadDim; i += kBlock) {
+      const int h = i / kHeadDim, e = i % kHeadDim;
+      s_q[h][e] = __uint_as_float(
+          (uint32_t)p.q[(size_t)row_of(p, b, g, h, GRP) * kHeadDim + e] << 16);
+    }
+    __syncthreads();
+    if (threadIdx.x < GRP * SD) {
+      const int h = threadIdx.x / SD, j = threadIdx.x % SD;
+      float acc = 0.0f;
+      for (int e = 0; e < kHeadDim; ++e)
+        acc = __builtin_fmaf(s_proj[e * SD + j], s_q[h][e], acc);
+      s_qp[h][j] = acc * kInvSqrtD;
+    }
+    __syncthreads();
+  }
+  const int u = lane % LPT;
+  float qv[GRP][8];
+#pragma unroll
+  for (int h = 0; h < GRP; ++h)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) qv[h][k] = s_qp[h][u * 8 + k];
+
+  float mx[GRP];
+#pragma unroll
+  for (int h = 0; h < GRP; ++h) mx[h] = -INFINITY;
+  uint32_t n_h = 0;
+  bool bad = false;
+  const uint16_t *sk = p.sketch + (size_t)bg * p.n * SD;
+  const float *rr = p.r + (size_t)bg * p.n;
+  const int base = c * p.chunk;
+  const int lim = min(base + p.chunk, p.n);
+  constexpr int UNR = 4;  // sketch rows in flight per lane
+  constexpr int NIT = kChunk / (TPI * UNR);
+  __shared__ float s_dot[GRP][kChunk];  // the chunk's logits and r, for pass 0
+  __shared__ float s_r[kChunk];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int i0 = base + it * TPI * UNR;
+    uint4 raw[UNR];
+    float rv[UNR];
+#pragma unroll
+    for (int k = 0; k < UNR; ++k) {
+      const int i = i0 + k * TPI + threadIdx.x / LPT;
+      if (i < lim) {
+        raw[k] = *reinterpret_cast<const uint4 *>(sk + (size_t)i * SD + u * 8);
+        rv[k] = rr[i];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < UNR; ++k) {
+      const int i = i0 + k * TPI + threadIdx.x / LPT;
+      if (i >= lim) continue;
+      float f[8];
+      unpack8(raw[k], f);
+      float dot[GRP];
+#pragma unroll
+      for (int h = 0; h < GRP; ++h) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(qv[h][e], f[e], acc);
+        dot[h] = group_sum<LPT>(acc);
+      }
+      const float ri = rv[k];
+      if (!(ri > 0.0f && ri <= 1.0f)) bad = true;
+      const bool in_l = ri < 1.0f;
+      if (u == 0 && !in_l) ++n_h;
+      if (u == 0) s_r[i - base] = ri;
+#pragma unroll
+      for (int h = 0; h < GRP; ++h) {
+        if (h % LPT == u) {
+          p.shat[(size_t)row_of(p, b, g, h, GRP) * p.n + i] = dot[h];
+          s_dot[h][i - base] = dot[h];
+        }
+        if (in_l) mx[h] = fmaxf(mx[h], dot[h]);
+      }
+    }
+  }
+  if (bad) atomicOr(p.status, VKV_STATUS_BAD_R);
+  const int np = p.nch + p.ncr;
+  scan_finish<GRP>(p, b, g, c, lim - base, mx, s_dot, s_r);
+  const uint32_t th = block_sum<uint32_t>(n_h, s_ured);
+  if (threadIdx.x == 0) p.hpart[(size_t)bg * np + c] = th;
+}
+
+// Same outputs with exact keys read from the host cache (perfect sketch).
+template <int GRP>
+__global__ __launch_bounds__(kBlock) void dk_scan_exact(DParams p) {
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int bg = b * p.G + g;
+  const int lane = threadIdx.x % kWave;
+  __shared__ uint32_t s_ured[kBlock / kWave];
+  if (c == 0) {
+    for (int h = 0; h < GRP; ++h) {
+      const int row = row_of(p, b, g, h, GRP);
+      if (threadIdx.x == 0) {
+        RowState z{};
+        z.amax = -1;
+        z.T = ~0ull;
+        p.rows[row] = z;
+      }
+    }
+    if (bg == 0 && threadIdx.x == 0) {
+      *p.status = 0u;
+      *p.host_bytes = 0ull;
+    }
+  }
+  {
+    const int w0 = c * p.chunk / 32, nw = p.chunk / 32;
+    for (int w = threadIdx.x; w < nw; w += kBlock) {
+      if (w0 + w < p.nwords) {
+        p.resbits[(size_t)bg * p.nwords + w0 + w] = 0u;
+        p.fbits[(size_t)bg * p.nwords + w0 + w] = 0u;
+        for (int h = 0; h < GRP; ++h)
+          p.hbits[(size_t)row_of(p, b, g, h, GRP) * p.nwords + w0 + w] = 0u;
+      }
+    }
+  }
+  const int u = lane % 16;
+  float qv[GRP][8];
+#pragma unroll
+  for (int h = 0; h < GRP; ++h) {
+    const uint4 raw = *reinterpret_cast<const uint4 *>(
+        p.q + (size_t)row_of(p, b, g, h, GRP) * kHeadDim + u * 8);
+    unpack8(raw, qv[h]);
+  }
+  float mx[GRP];
+#pragma unroll
+  for (int h = 0; h < GRP; ++h) mx[h] = -INFINITY;
+  uint32_t n_h = 0;
+  bool bad = false;
+  const float *rr = p.r + (size_t)bg * p.n;
+  const int base = c * p.chunk;
+  const int lim = min(base + p.chunk, p.n);
+  __shared__ float s_dot[GRP][kChunk];  // the chunk's logits and r, for pass 0
+  __shared__ float s_r[kChunk];
+  for (int i0 = base; i0 < lim; i0 += kBlock / 16) {
+    const int i = i0 + threadIdx.x / 16;
+    if (i < lim) {
+      const float ri = rr[i];
+      if (!(ri > 0.0f && ri <= 1.0f)) bad = true;
+      const bool in_l = ri < 1.0f;
+      if (u == 0 && !in_l) ++n_h;
+      float dot[GRP];
+      if (u == 0) s_r[i - base] = ri;
+      if (in_l) {
+        const uint4 raw = *reinterpret_cast<const uint4 *>(
+            p.host_kv + ((size_t)bg * p.n + i) * 2 * kHeadDim + u * 8);
+        float f[8];
+        unpack8(raw, f);
+#pragma unroll
+        for (int h = 0; h < GRP; ++h) {
+          float acc = 0.0f;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) acc = __builtin_fmaf(qv[h][k], f[k], acc);
+          dot[h] = group_sum<16>(acc) * kInvSqrtD;
+          mx[h] = fmaxf(mx[h], dot[h]);
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < GRP; ++h) dot[h] = 0.0f;
+      }
+#pragma unroll
+      for (int h = 0; h < GRP; ++h) {
+        if (u == h) p.shat[(size_t)row_of(p, b, g, h, GRP) * p.n + i] = dot[h];
+        if (u == 0) s_dot[h][i - base] = dot[h];
+      }
+    }
+  }
+  if (bad) atomicOr(p.status, VKV_STATUS_BAD_R);
+  scan_finish<GRP>(p, b, g, c, lim - base, mx, s_dot, s_r);
+  const uint32_t th = block_sum<uint32_t>(n_h, s_ured);
+  if (threadIdx.x == 0) p.hpart[(size_t)bg * (p.nch + p.ncr) + c] = th;
+}
+
+// ------------------------------------------------------------ dk_resident
+// The group's resident rows are split evenly over gridDim.x workgroups.
+template <int GRP>
+__global__ __launch_bounds__(kBlock) void dk_resident(DParams p) {
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int bg = b * p.G + g;
+  const int lane = threadIdx.x % kWave;
+  const int u = lane % 16;
+  __shared__ uint32_t s_ured[kBlock / kWave];
+  float qv[GRP][8];
+#pragma unroll
+  for (int h = 0; h < GRP; ++h) {
+    const uint4 raw = *reinterpret_cast<const uint4 *>(
+        p.q + (size_t)row_of(p, b, g, h, GRP) * kHeadDim + u * 8);
+    unpack8(raw, qv[h]);
+  }
+  int cnt = p.rcount[bg];
+  bool bad = cnt < 0 || cnt > p.cap;
+  cnt = max(0, min(cnt, p.cap));
+  const int32_t *ridx = p.ridx + (size_t)bg * p.cap;
+  const float *rr = p.r + (size_t)bg * p.n;
+  float mx[GRP];
+  float hm[GRP];   // running shift and sum over this thread's H rows
+  double hsum[GRP];
+#pragma unroll
+  for (int h = 0; h < GRP; ++h) {
+    mx[h] = -INFINITY;
+    hm[h] = -INFINITY;
+    hsum[h] = 0.0;
+  }
+  uint32_t n_h = 0;
+  int lo, hi;
+  split_range(cnt, gridDim.x, c, lo, hi);
+  for (int j0 = lo; j0 < hi; j0 += kBlock / 16) {
+    const int j = j0 + threadIdx.x / 16;
+    if (j < hi) {
+      const int pos = ridx[j];
+      const bool ok = pos >= 0 && pos < p.n && (j == 0 || ridx[j - 1] < pos);
+      const uint4 raw = *reinterpret_cast<const uint4 *>(
+          p.rkv + ((size_t)bg * p.cap + j) * 2 * kHeadDim + u * 8);
+      const bool in_h = ok && rr[pos] >= 1.0f;
+      float f[8];
+      unpack8(raw, f);
+#pragma unroll
+      for (int h = 0; h < GRP; ++h) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc = __builtin_fmaf(qv[h][k], f[k], acc);
+        const float dot = group_sum<16>(acc) * kInvSqrtD;
+        if (u == h) p.ell[(size_t)row_of(p, b, g, h, GRP) * p.cap + j] = dot;
+        mx[h] = fmaxf(mx[h], dot);
+        if (u == 0 && in_h) {  // sum over H of exp(l), with a running shift
+          if (dot > hm[h]) {
+            hsum[h] = hsum[h] * (double)expf(hm[h] - dot) + 1.0;
+            hm[h] = dot;
+          } else {
+            hsum[h] += (double)expf(dot - hm[h]);
+          }
+        }
+      }
+      if (u == 0) {
+        if (ok) {
+          atomicOr(p.resbits + (size_t)bg * p.nwords + pos / 32,
+                   1u << (pos % 32));
+          if (in_h) ++n_h;
+        } else {
+          bad = true;
+        }
+      }
+    }
+  }
+  if (bad) atomicOr(p.status, VKV_STATUS_BAD_RESIDENT);
+  const int np = p.nch + p.ncr;
+  blk_combine<float, GRP, kBlock, OpMax<float>>(mx);
+#pragma unroll
+  for (int h = 0; h < GRP; ++h)
+    hsum[h] = hsum[h] > 0.0 ? hsum[h] * (double)expf(hm[h] - mx[h]) : 0.0;
+  blk_reduce<double, GRP, kBlock>(hsum);
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int h = 0; h < GRP; ++h) {
+      const int row = row_of(p, b, g, h, GRP);
+      p.pmax[(size_t)row * np + p.nch + c] = mx[h];
+      p.hres[(size_t)row * p.ncr + c] = hsum[h];
+    }
+  }
+  const uint32_t th = block_sum<uint32_t>(n_h, s_ured);
+  if (threadIdx.x == 0) p.hpart[(size_t)bg * np + p.nch + c] = th;
+}
+
+// ------------------------------------------------------------ planning
+// The plan of Algorithm 2 for every (request, query head) ("row"):
+//   D~ -> beta* -> certificate (Lemma 1, eq. 7) -> k* (eq. 10) -> F_h.
+// Data-parallel passes over a row's tokens run as launches of kBlock-thread
+// workgroups, one per chunk of kRowChunk tokens of a row; each writes a
+// partial record, and every workgroup of the next launch combines the
+// records of its row itself (in one fixed order, so all of them get
+// bit-identical results). No workgroup ever waits for another.
+//
+// beta*: at the root, beta* >= max_i w~_i (1 - r_i) (below that the heaviest
+// token alone would give more than beta), so every token is at or above its
+// lower clip and the Definition 2 fixed point is also the unique root of
+//     h(beta) = sum_i max(0, w~_i - beta rho_i) - beta,  rho_i = r_i/(1-r_i),
+// a convex, decreasing, piecewise-linear function. Pass 0 gives the sums at
+// beta = 0 and the lower bound above; each later pass evaluates, at
+// kBetaPts points of the bracket [lo, hi], the sums of w~ and rho over the
+// active set A(beta) = {w~_i > beta rho_i} and its size. The Newton step
+// from a point with h >= 0, beta' = sum_A w~ / (1 + sum_A rho), never
+// overshoots the root (convexity); it is the root itself when no breakpoint
+// lies between the point and the next evaluated point (equal active counts)
+// or when the next pass finds the same active set at beta'. Since h' <= -1,
+// beta + h(beta) bounds the root from above. A row still open after the
+// last Newton launch finishes in the certificate launch, where each of its
+// workgroups iterates over the whole row (rare; same arithmetic).
+//
+// Selection: keys (gain bits, inverted position) order L as L_g
+// (descending). Each of kSelWG workgroups per row takes a block-cyclic
+// share of the row's tokens and writes its keys at or above a local bound
+// lo_s (at most kCandWG of them) with their fixed-point beta_i and v_i and
+// range term b_i. One workgroup per row then runs the stopping rule on the
+// union to the exact k* and threshold T; that is the answer whenever T >=
+// max_s lo_s (every key >= T was written). Otherwise, or when fetching every
+// candidate cannot certify the row, it runs the streaming selection below
+// instead. All sums of the selection are fixed-point integers, so a rest's
+// sum is the total minus the fetched part exactly.
+constexpr int kSelUnroll = 4;       // streamed tokens per thread in flight
+constexpr int kRowChunk = 2048;     // tokens per workgroup in row passes
+constexpr int kRowTok = kRowChunk / kBlock;
+constexpr int kBetaPts = 4;         // points of h per Newton pass
+constexpr int kBetaRec = 3 * kBetaPts;
+constexpr int kBetaLaunches = 4;    // Newton passes (pass 0 is in the scan)
+constexpr int kBetaPassMax = 96;    // never reached: the bracket shrinks >= 2x
+constexpr int kCandMax = 4096;      // candidates sorted by the walk
+constexpr int kSelDigit = 11;
+constexpr int kSelBinsP = 1 << kSelDigit;
+constexpr int kSelLevels = 5;       // five 11-bit digits cover the 55-bit key
+constexpr unsigned long long kKeyEnd = 1ull << 55;  // above every key
+__device__ __forceinline__ int sel_off(int d) { return 44 - kSelDigit * d; }
 
 // LDS of the streaming selection: the count histogram, then the collected
 // candidates.
@@ -1138,8 +1194,51 @@ __device__ __forceinline__ void beta_rec_total(double (&v)[kBetaRec]) {
   if (LB) v[3] = blk_max<double, kBlock>(mx);
 }
 
-// Pass `pass` of the beta* iteration: 0 is pass 0, later ones are Newton
-// passes. Grid (chunks, Hq, B).
+// The row's common shift m = max(max_R l, max_L s) and the pass-0 sums
+// rescaled to it, as this thread's share: slots 0-2 sum_L w~, sum rho over
+// w~ > 0 and their count, slot 3 max w~ (1 - r) (combined by maximum), slot
+// 4 sum_H w. Workgroup 0 of the row stores m; with `check`, it also checks
+// that every token with r == 1 of the KV head is resident.
+__device__ __forceinline__ float row_pass0(const DParams &p, int row, int bg,
+                                           int c, bool check,
+                                           double (&v)[kBetaRec]) {
+  const int np = p.nch + p.ncr;
+  float pm[1] = {-INFINITY};
+  for (int t = threadIdx.x; t < np; t += kBlock)
+    pm[0] = fmaxf(pm[0], p.pmax[(size_t)row * np + t]);
+  blk_combine<float, 1, kBlock, OpMax<float>>(pm);
+  const float m = pm[0];
+#pragma unroll
+  for (int k = 0; k < kBetaRec; ++k) v[k] = 0.0;
+  for (int t = threadIdx.x; t < p.nch; t += kBlock) {
+    const double *rec = p.p0part + ((size_t)row * np + t) * 4;
+    if (!(rec[0] > 0.0)) continue;
+    const double f = exp((double)p.pmax[(size_t)row * np + t] - (double)m);
+    v[0] += rec[0] * f;
+    v[1] += rec[1];
+    v[2] += rec[2];
+    v[3] = fmax(v[3], rec[3] * f);
+  }
+  for (int t = threadIdx.x; t < p.ncr; t += kBlock) {
+    const double hs = p.hres[(size_t)row * p.ncr + t];
+    if (hs > 0.0) v[4] += hs * exp((double)p.pmax[(size_t)row * np + p.nch + t] - (double)m);
+  }
+  if (c == 0) {
+    if (threadIdx.x == 0) p.rows[row].m = m;
+    if (check) {
+      uint32_t hc[2] = {0u, 0u};  // tokens with r == 1: all, resident
+      for (int t = threadIdx.x; t < np; t += kBlock)
+        hc[t < p.nch ? 0 : 1] += p.hpart[(size_t)bg * np + t];
+      blk_reduce<uint32_t, 2, kBlock>(hc);
+      if (threadIdx.x == 0 && hc[0] != hc[1]) atomicOr(p.status, VKV_STATUS_BAD_RESIDENT);
+    }
+  }
+  return m;
+}
+
+// Newton pass `pass` (>= 1) of the beta* iteration; pass 1 starts from the
+// pass-0 sums that the scan and resident-logit kernels left per chunk and
+// part. Grid (chunks, Hq, B).
 template <int GRP>
 __global__ __launch_bounds__(kBlock) void dk_rbeta(DParams p, int pass) {
   const int c = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
@@ -1147,57 +1246,26 @@ __global__ __launch_bounds__(kBlock) void dk_rbeta(DParams p, int pass) {
   const size_t rows = (size_t)p.B * p.Hq;
   float w8[kRowTok], r8[kRowTok], s8[kRowTok];
   row_load(p, row, bg, c, r8, s8);
-  const float m = p.rows[row].m;
   // the previous pass: this thread's share of the records, and the state
   const int q = (pass - 1) & 1;
   double rv[kBetaRec];
   BetaState st{};
-  if (pass >= 1) {
-    const double *rec = p.bpart + ((size_t)q * rows + row) * p.nrc * kBetaRec;
-    if (pass == 1) beta_rec_load<true>(rec, p.nrc, rv);
-    else beta_rec_load<false>(rec, p.nrc, rv);
-    if (pass >= 2) st = p.bstate[(size_t)q * rows + row];
+  float m;
+  if (pass == 1) {
+    m = row_pass0(p, row, bg, c, hq % GRP == 0, rv);
+    beta_rec_total<true>(rv);
+    st = beta_init(rv, p.est);
+  } else {
+    m = p.rows[row].m;
+    beta_rec_load<false>(p.bpart + ((size_t)q * rows + row) * p.nrc * kBetaRec, p.nrc, rv);
+    st = p.bstate[(size_t)q * rows + row];
   }
   row_weights(m, r8, s8, w8);
   double v[kBetaRec];
 #pragma unroll
   for (int k = 0; k < kBetaRec; ++k) v[k] = 0.0;
   double *out = p.bpart + (((size_t)(pass & 1) * rows + row) * p.nrc + c) * kBetaRec;
-  if (pass == 0) {
-    double lb = 0.0;
-#pragma unroll
-    for (int u = 0; u < kRowTok; ++u) {
-      if (!(r8[u] < 1.0f)) continue;
-      v[0] += (double)w8[u];
-      if (w8[u] > 0.0f) {
-        v[1] += (double)plan_rho(r8[u]);
-        v[2] += 1.0;
-        lb = fmax(lb, (double)(w8[u] * (1.0f - r8[u])));
-      }
-    }
-    if (c == 0) {  // H part of D~ from the exact resident logits
-      const float *rr = p.r + (size_t)bg * p.n;
-      const int cnt = max(0, min(p.rcount[bg], p.cap));
-      const int32_t *ridx = p.ridx + (size_t)bg * p.cap;
-      const float *el = p.ell + (size_t)row * p.cap;
-      for (int j = threadIdx.x; j < cnt; j += kBlock) {
-        const int pos = ridx[j];
-        const float e = el[j];
-        if (pos >= 0 && pos < p.n && rr[pos] >= 1.0f) v[4] += (double)expf(e - m);
-      }
-    }
-    blk_reduce<double, kBetaRec, kBlock>(v);
-    lb = blk_max<double, kBlock>(lb);
-    if (threadIdx.x == 0) {
-#pragma unroll
-      for (int k = 0; k < kBetaRec; ++k) out[k] = k == 3 ? lb : v[k];
-    }
-    return;
-  }
-  if (pass == 1) {
-    beta_rec_total<true>(rv);
-    st = beta_init(rv, p.est);
-  } else if (!st.done) {
+  if (pass >= 2 && !st.done) {
     beta_rec_total<false>(rv);
     st = beta_advance(st, rv);
   }
@@ -1224,7 +1292,7 @@ __global__ __launch_bounds__(kBlock) void dk_rcert(DParams p) {
   float w8[kRowTok], r8[kRowTok], s8[kRowTok];
   row_load(p, row, bg, c, r8, s8);
   const float m = p.rows[row].m;
-  const int q = (kBetaLaunches - 1) & 1;
+  const int q = kBetaLaunches & 1;
   double rv[kBetaRec];
   beta_rec_load<false>(p.bpart + ((size_t)q * rows + row) * p.nrc * kBetaRec,
                        p.nrc, rv);
@@ -2052,54 +2120,68 @@ __device__ __forceinline__ void attn_part(const DParams &p, int x, int g,
   }
 }
 
-// Merge of a KV head's partial softmax sums by log-sum-exp (one wave per
-// head): at most 64 partials, one per lane, and each output dimension reads
-// its partials as consecutive 16-byte vectors.
-template <int GRP>
-__device__ __forceinline__ void attn_merge(const DParams &p, int g, int b) {
+// Merge of one row's partial softmax sums by log-sum-exp. Each thread takes
+// one output dimension and half of the partials; a dimension's partials are
+// consecutive and read as 16-byte vectors, all loads issued first. Partial
+// slots past ncr + ncf (padding) are never read into the sum.
+__device__ __forceinline__ void attn_merge_row(const DParams &p, int row) {
+  const int np = p.ncr + p.ncf;  // at most 64 (32 resident, kGatherWG fetched)
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int np = p.ncr + p.ncf;
-  __shared__ float s_scale[kBlock / kWave][kWave];  // ncr + ncf <= 64
-  for (int h = wave; h < GRP; h += kBlock / kWave) {
-    const int row = row_of(p, b, g, h, GRP);
-    const float2 md = lane < np ? p.apart[(size_t)row * np + lane] : make_float2(0.0f, 0.0f);
+  __shared__ float s_sc[64];
+  __shared__ float s_half[kHeadDim];
+  __shared__ float s_md[2];
+  const int e = threadIdx.x % kHeadDim, half = threadIdx.x / kHeadDim;
+  const int nq = p.npad / 4, per = (nq + 1) / 2, q0 = half * per;
+  const float4 *src = reinterpret_cast<const float4 *>(
+      p.aparto + ((size_t)row * kHeadDim + e) * p.npad);
+  float4 v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    v[k] = (k < per && q0 + k < nq) ? src[q0 + k] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  const float2 md = (int)threadIdx.x < np ? p.apart[(size_t)row * np + threadIdx.x]
+                                          : make_float2(0.0f, 0.0f);
+  if (wave == 0) {
     const float M = wave_max(md.y > 0.0f ? md.x : -INFINITY);
     const float sc = md.y > 0.0f ? expf(md.x - M) : 0.0f;
     const float D = wave_sum(md.y * sc);
-    s_scale[wave][lane] = sc;
-    __builtin_amdgcn_wave_barrier();
-    for (int e = lane; e < kHeadDim; e += kWave) {
-      const float4 *src = reinterpret_cast<const float4 *>(
-          p.aparto + ((size_t)row * kHeadDim + e) * p.npad);
-      float o = 0.0f;
-      for (int q4 = 0; q4 < p.npad / 4; ++q4) {
-        const float4 v = src[q4];
-        const float *sp = &s_scale[wave][q4 * 4];
-        o += sp[0] != 0.0f ? v.x * sp[0] : 0.0f;
-        o += sp[1] != 0.0f ? v.y * sp[1] : 0.0f;
-        o += sp[2] != 0.0f ? v.z * sp[2] : 0.0f;
-        o += sp[3] != 0.0f ? v.w * sp[3] : 0.0f;
-      }
-      p.out[(size_t)row * kHeadDim + e] = o / D;
-    }
+    s_sc[lane] = sc;
     if (lane == 0) {
-      const RowState &rs = p.rows[row];
-      p.d_hat[row] = D;
-      p.log_shift[row] = M;
-      p.eps_hat0[row] = (float)rs.eps0;
-      p.eps_hat[row] = rs.fetch ? rs.eps1 : (float)rs.eps0;
-      p.k_star[row] = rs.fetch ? rs.kstar : 0;
-      if (p.row_stats) {
-        double *sr = p.row_stats + (size_t)row * 8;
-        sr[0] = rs.m;
-        sr[1] = rs.dnorm;
-        sr[2] = rs.beta;
-        sr[3] = rs.betaL;
-        sr[4] = rs.VL;
-        sr[5] = rs.b1;
-        sr[6] = rs.eps0;
-        sr[7] = rs.fetch ? rs.eps1 : rs.eps0;
-      }
+      s_md[0] = M;
+      s_md[1] = D;
+    }
+  }
+  __syncthreads();
+  float o = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    if (!(k < per && q0 + k < nq)) continue;
+    const float *sp = &s_sc[(q0 + k) * 4];
+    o += sp[0] != 0.0f ? v[k].x * sp[0] : 0.0f;
+    o += sp[1] != 0.0f ? v[k].y * sp[1] : 0.0f;
+    o += sp[2] != 0.0f ? v[k].z * sp[2] : 0.0f;
+    o += sp[3] != 0.0f ? v[k].w * sp[3] : 0.0f;
+  }
+  if (half == 1) s_half[e] = o;
+  __syncthreads();
+  const float M = s_md[0], D = s_md[1];
+  if (half == 0) p.out[(size_t)row * kHeadDim + e] = (o + s_half[e]) / D;
+  if (threadIdx.x == 0) {
+    const RowState &rs = p.rows[row];
+    p.d_hat[row] = D;
+    p.log_shift[row] = M;
+    p.eps_hat0[row] = (float)rs.eps0;
+    p.eps_hat[row] = rs.fetch ? rs.eps1 : (float)rs.eps0;
+    p.k_star[row] = rs.fetch ? rs.kstar : 0;
+    if (p.row_stats) {
+      double *sr = p.row_stats + (size_t)row * 8;
+      sr[0] = rs.m;
+      sr[1] = rs.dnorm;
+      sr[2] = rs.beta;
+      sr[3] = rs.betaL;
+      sr[4] = rs.VL;
+      sr[5] = rs.b1;
+      sr[6] = rs.eps0;
+      sr[7] = rs.fetch ? rs.eps1 : rs.eps0;
     }
   }
 }
@@ -2114,10 +2196,9 @@ __global__ __launch_bounds__(kBlock) void dk_fetch(DParams p) {
   else gather_attend<GRP>(p, x - p.ncr, g, b);
 }
 
-// The merge of each KV head's partials. Grid (G, B).
-template <int GRP>
+// The merge of each row's partials. Grid (Hq, B).
 __global__ __launch_bounds__(kBlock) void dk_attn(DParams p) {
-  attn_merge<GRP>(p, (int)blockIdx.x, (int)blockIdx.y);
+  attn_merge_row(p, (int)blockIdx.y * p.Hq + (int)blockIdx.x);
 }
 
 // Records the timing event after kernel `k` when the caller asked for it.
@@ -2148,7 +2229,7 @@ hipError_t run(const DParams &p, hipStream_t s, int sd, void **events) {
   mark(k++);
   const dim3 grow((unsigned)p.nrc, (unsigned)p.Hq, (unsigned)p.B);
   const dim3 gone((unsigned)p.Hq, (unsigned)p.B);
-  for (int j = 0; j < kBetaLaunches; ++j) {
+  for (int j = 1; j <= kBetaLaunches; ++j) {
     dk_rbeta<GRP><<<grow, blk, 0, s>>>(p, j);
     mark(k++);
   }
@@ -2160,13 +2241,13 @@ hipError_t run(const DParams &p, hipStream_t s, int sd, void **events) {
   mark(k++);
   dk_fetch<GRP><<<dim3((unsigned)(p.ncr + kGatherWG), (unsigned)p.G, (unsigned)p.B), blk, 0, s>>>(p);
   mark(k++);
-  dk_attn<GRP><<<dim3((unsigned)p.G, (unsigned)p.B), blk, 0, s>>>(p);
+  dk_attn<<<dim3((unsigned)p.Hq, (unsigned)p.B), blk, 0, s>>>(p);
   mark(k++);
   return hipGetLastError();
 }
 
 const char *const kPhaseNames[] = {
-    "scan",  "resident", "beta0",   "beta1",   "beta2", "beta3", "beta4",
+    "scan",  "resident", "beta1",   "beta2",   "beta3", "beta4",
     "cert",  "cand",     "walk",    "fetch", "attn"};
 
 }  // namespace
@@ -2199,13 +2280,14 @@ DecodeLayout decode_layout(const vkv_decode_args &a) {
   const size_t rows = B * Hq, groups = B * G;
   Carve c;
   L.rows = c.take<RowState>(rows);
-  L.groups = c.take<GroupState>(groups);
   L.shat = c.take<float>(rows * n);
   L.ell = c.take<float>(rows * (size_t)a.cap);
   L.resbits = c.take<uint32_t>(groups * L.nwords);
   L.fbits = c.take<uint32_t>(groups * L.nwords);
   L.hbits = c.take<uint32_t>(rows * L.nwords);
   L.pmax = c.take<float>(rows * (L.nch + L.ncr));
+  L.p0part = c.take<double>(rows * (L.nch + L.ncr) * 4);
+  L.hres = c.take<double>(rows * L.ncr);
   L.hpart = c.take<uint32_t>(groups * (L.nch + L.ncr));  // H counts per chunk
   L.nrc = (a.n_tokens + kRowChunk - 1) / kRowChunk;
   L.bpart = c.take<double>(2 * rows * L.nrc * (size_t)kBetaRec);
@@ -2250,13 +2332,14 @@ hipError_t launch_decode(const vkv_decode_args &a, const DecodeLayout &L,
   p.status = a.status;
   void *w = a.workspace;
   p.rows = at<RowState>(w, L.rows);
-  p.groups = at<GroupState>(w, L.groups);
   p.shat = at<float>(w, L.shat);
   p.ell = at<float>(w, L.ell);
   p.resbits = at<uint32_t>(w, L.resbits);
   p.fbits = at<uint32_t>(w, L.fbits);
   p.hbits = at<uint32_t>(w, L.hbits);
   p.pmax = at<float>(w, L.pmax);
+  p.p0part = at<double>(w, L.p0part);
+  p.hres = at<double>(w, L.hres);
   p.hpart = at<uint32_t>(w, L.hpart);
   p.bpart = at<double>(w, L.bpart);
   p.bstate = at<BetaState>(w, L.bstate);
