@@ -76,6 +76,37 @@ def algorithmic_bytes(w, counts, fetching_rows, host_bytes):
                 + B * Hq * d * (2 + 4), kernels=per)
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_c2_traffic.md")
+DECODE_SOURCES = ("verified_sparse_kv_amd/csrc/vkv_decode.hip",
+                  "verified_sparse_kv_amd/csrc/vkv_common.h",
+                  "verified_sparse_kv_amd/csrc/vkv_internal.h")
+
+
+def measured_traffic(config, kernel):
+    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE /
+    WRITE_SIZE counter summary, or None when there is none for this workload
+    or the decode sources changed since the counters were taken."""
+    import hashlib
+    if config != "c2" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals, want = {}, None
+    for line in open(TRAFFIC_FILE):
+        if " = " not in line:
+            continue
+        k, v = (x.strip() for x in line.split(" = ", 1))
+        if k == "source_sha256":
+            want = v
+        elif k.startswith("traffic."):
+            vals[k[len("traffic."):]] = float(v)
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if want != h.hexdigest():
+        return None
+    return vals.get(kernel)
+
+
 def cpu_baseline(w, seconds):
     """The oracle (never tuned) decoding KV-head groups of the same layer until
     `seconds` of CPU work have been spent."""
@@ -277,7 +308,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dom, "kernel_us": t_dom * 1e6,
                      "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(args.config, dom),
                      "algorithmic_bytes": cand[dom]},
     }
     if not args.no_cpu_baseline:
