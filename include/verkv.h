@@ -120,7 +120,8 @@ typedef struct {
  * One KVFetch decode step for one layer: every request and every query head.
  *
  * Shapes: B = batch, Hq query heads over G KV heads (Hq/G in {1,2,4,8}),
- * head_dim d = 128, n tokens, sketch_dim s in {16, 32}.
+ * head_dim d = 128, n tokens (1 <= n <= 2^17; larger n returns
+ * VKV_EUNSUPPORTED), sketch_dim s in {16, 32}.
  * q            dev [B][Hq][d] bf16.
  * resident_kv  dev [B][G][cap][2][d] bf16 (rows of H u S, K then V), with
  * resident_idx dev [B][G][cap] i32 ascending positions and

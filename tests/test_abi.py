@@ -139,6 +139,7 @@ def test_compress_validation(kw, code, frag):
     (dict(fetch_cap=0), vk.VKV_EINVAL, "fetch_cap"),
     (dict(fetch_cap=5000), vk.VKV_EINVAL, "fetch_cap"),
     (dict(n_tokens=1 << 24), vk.VKV_EINVAL, "n_tokens"),
+    (dict(n_tokens=(1 << 17) + 1, fetch_cap=1 << 17), vk.VKV_EUNSUPPORTED, "2^17"),
     (dict(estimator=7), vk.VKV_EINVAL, "estimator"),
     (dict(weights=3), vk.VKV_EINVAL, "weights"),
     (dict(sketch=None), vk.VKV_EINVAL, "sketch"),

@@ -64,6 +64,8 @@ vkv_status check_decode_shapes(const vkv_decode_args *a) {
   REQUIRE(a->head_dim == vkv::kHeadDim, "decode: head_dim must be 128");
   REQUIRE(a->n_tokens >= 1 && a->n_tokens < (1 << 24),
           "decode: n_tokens must be in [1, 2^24)");
+  if (a->n_tokens > (1 << 17))
+    return fail(VKV_EUNSUPPORTED, "decode: n_tokens %d (supported: up to 2^17)", a->n_tokens);
   if (!(a->sketch_dim == 16 || a->sketch_dim == 32))
     return fail(VKV_EUNSUPPORTED, "decode: sketch_dim %d (supported: 16, 32)", a->sketch_dim);
   REQUIRE(a->cap >= 1, "decode: cap must be >= 1");

@@ -228,11 +228,11 @@ __device__ __forceinline__ void top2_merge(float &x1, int &p1, float &x2,
 }
 
 // Block-wide combination of NV values per thread for THREADS threads, in a
-// fixed order, through LDS only (cross-lane shuffles are slow on this path):
-// every thread stores its values, 16 threads per value fold a sixteenth each
-// (stride 16, so a wave reads consecutive words), and NV threads fold the
-// sixteen partials. Every thread gets the results; the same inputs give the
-// same bits in every workgroup.
+// fixed order (the same inputs give the same bits in every workgroup), and
+// every thread gets the results. Within a wave the values move by DPP row
+// operations (no LDS): quad exchanges and row rotations leave each 16-lane
+// row's total in all of its lanes, and the four row totals are read from
+// lanes 0, 16, 32 and 48 and folded in that order; across waves through LDS.
 template <typename T>
 struct OpSum {
   __device__ static T f(T a, T b) { return a + b; }
@@ -241,32 +241,78 @@ template <typename T>
 struct OpMax {
   __device__ static T f(T a, T b) { return a > b ? a : b; }
 };
+
+// DPP move of a 32- or 64-bit value (64-bit values move as two halves).
+template <int CTRL, typename T>
+__device__ __forceinline__ T dpp_mov(T v) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "dpp");
+  if constexpr (sizeof(T) == 4) {
+    int x;
+    __builtin_memcpy(&x, &v, 4);
+    x = __builtin_amdgcn_update_dpp(x, x, CTRL, 0xF, 0xF, false);
+    T r;
+    __builtin_memcpy(&r, &x, 4);
+    return r;
+  } else {
+    int x[2];
+    __builtin_memcpy(x, &v, 8);
+    x[0] = __builtin_amdgcn_update_dpp(x[0], x[0], CTRL, 0xF, 0xF, false);
+    x[1] = __builtin_amdgcn_update_dpp(x[1], x[1], CTRL, 0xF, 0xF, false);
+    T r;
+    __builtin_memcpy(&r, x, 8);
+    return r;
+  }
+}
+template <typename T>
+__device__ __forceinline__ T lane_read(T v, int lane) {
+  if constexpr (sizeof(T) == 4) {
+    int x;
+    __builtin_memcpy(&x, &v, 4);
+    x = __builtin_amdgcn_readlane(x, lane);
+    T r;
+    __builtin_memcpy(&r, &x, 4);
+    return r;
+  } else {
+    int x[2];
+    __builtin_memcpy(x, &v, 8);
+    x[0] = __builtin_amdgcn_readlane(x[0], lane);
+    x[1] = __builtin_amdgcn_readlane(x[1], lane);
+    T r;
+    __builtin_memcpy(&r, x, 8);
+    return r;
+  }
+}
+// The wave's total, the same in every lane (all 64 lanes must be active).
+template <typename T, typename OP>
+__device__ __forceinline__ T wave_fold(T v) {
+  constexpr int kXor1 = 0xB1, kXor2 = 0x4E;    // quad_perm [1,0,3,2], [2,3,0,1]
+  constexpr int kRor4 = 0x124, kRor8 = 0x128;  // row_ror:4, row_ror:8
+  v = OP::f(v, dpp_mov<kXor1>(v));
+  v = OP::f(v, dpp_mov<kXor2>(v));
+  v = OP::f(v, dpp_mov<kRor4>(v));
+  v = OP::f(v, dpp_mov<kRor8>(v));
+  return OP::f(OP::f(lane_read(v, 0), lane_read(v, 16)),
+               OP::f(lane_read(v, 32), lane_read(v, 48)));
+}
 template <typename T, int NV, int THREADS, typename OP>
 __device__ __forceinline__ void blk_combine(T (&v)[NV]) {
-  static_assert(NV * 16 <= THREADS && THREADS % 16 == 0, "shape");
-  constexpr int LD = THREADS + 8;  // pitch between values: spreads the banks
-  __shared__ T buf[NV * LD + NV * 16 + NV];
-  T *part = buf + NV * LD;
-  T *tot = part + NV * 16;
-  __syncthreads();  // an earlier call may still be reading tot
+  constexpr int W = THREADS / kWave;
+  __shared__ T buf[W * NV];
 #pragma unroll
-  for (int k = 0; k < NV; ++k) buf[k * LD + threadIdx.x] = v[k];
-  __syncthreads();
-  if (threadIdx.x < NV * 16) {
-    const int k = threadIdx.x / 16, j = threadIdx.x % 16;
-    T acc = buf[k * LD + j];
-    for (int i = 1; i < THREADS / 16; ++i) acc = OP::f(acc, buf[k * LD + i * 16 + j]);
-    part[k * 16 + j] = acc;
-  }
-  __syncthreads();
-  if (threadIdx.x < NV) {
-    T acc = part[threadIdx.x * 16];
-    for (int j = 1; j < 16; ++j) acc = OP::f(acc, part[threadIdx.x * 16 + j]);
-    tot[threadIdx.x] = acc;
+  for (int k = 0; k < NV; ++k) v[k] = wave_fold<T, OP>(v[k]);
+  __syncthreads();  // an earlier call may still be reading buf
+  if (threadIdx.x % kWave == 0) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) buf[(threadIdx.x / kWave) * NV + k] = v[k];
   }
   __syncthreads();
 #pragma unroll
-  for (int k = 0; k < NV; ++k) v[k] = tot[k];
+  for (int k = 0; k < NV; ++k) {
+    T acc = buf[k];
+#pragma unroll
+    for (int w = 1; w < W; ++w) acc = OP::f(acc, buf[w * NV + k]);
+    v[k] = acc;
+  }
 }
 template <typename T, int NV, int THREADS>
 __device__ __forceinline__ void blk_reduce(T (&v)[NV]) {
@@ -387,6 +433,23 @@ __global__ __launch_bounds__(kBlock) void dk_scan(DParams p) {
   const int lane = threadIdx.x % kWave;
   __shared__ float s_qp[GRP][SD];
   __shared__ uint32_t s_ured[kBlock / kWave];
+  // the chunk's sketch rows and r first, all in flight while q is projected
+  const int u = lane % LPT;
+  const uint16_t *sk = p.sketch + (size_t)bg * p.n * SD;
+  const float *rr = p.r + (size_t)bg * p.n;
+  const int base = c * p.chunk;
+  const int lim = min(base + p.chunk, p.n);
+  constexpr int UNR = kChunk / TPI;
+  uint4 raw[UNR];
+  float rv[UNR];
+#pragma unroll
+  for (int k = 0; k < UNR; ++k) {
+    const int i = base + k * TPI + threadIdx.x / LPT;
+    if (i < lim) {
+      raw[k] = *reinterpret_cast<const uint4 *>(sk + (size_t)i * SD + u * 8);
+      rv[k] = rr[i];
+    }
+  }
 
   // step-start initialisation of this group's state (no other block of
   // this launch touches it)
@@ -441,7 +504,6 @@ __global__ __launch_bounds__(kBlock) void dk_scan(DParams p) {
     }
     __syncthreads();
   }
-  const int u = lane % LPT;
   float qv[GRP][8];
 #pragma unroll
   for (int h = 0; h < GRP; ++h)
@@ -453,30 +515,12 @@ __global__ __launch_bounds__(kBlock) void dk_scan(DParams p) {
   for (int h = 0; h < GRP; ++h) mx[h] = -INFINITY;
   uint32_t n_h = 0;
   bool bad = false;
-  const uint16_t *sk = p.sketch + (size_t)bg * p.n * SD;
-  const float *rr = p.r + (size_t)bg * p.n;
-  const int base = c * p.chunk;
-  const int lim = min(base + p.chunk, p.n);
-  constexpr int UNR = 4;  // sketch rows in flight per lane
-  constexpr int NIT = kChunk / (TPI * UNR);
   __shared__ float s_dot[GRP][kChunk];  // the chunk's logits and r, for pass 0
   __shared__ float s_r[kChunk];
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int i0 = base + it * TPI * UNR;
-    uint4 raw[UNR];
-    float rv[UNR];
+  {
 #pragma unroll
     for (int k = 0; k < UNR; ++k) {
-      const int i = i0 + k * TPI + threadIdx.x / LPT;
-      if (i < lim) {
-        raw[k] = *reinterpret_cast<const uint4 *>(sk + (size_t)i * SD + u * 8);
-        rv[k] = rr[i];
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < UNR; ++k) {
-      const int i = i0 + k * TPI + threadIdx.x / LPT;
+      const int i = base + k * TPI + threadIdx.x / LPT;
       if (i >= lim) continue;
       float f[8];
       unpack8(raw[k], f);
@@ -1855,17 +1899,23 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rwalk(DParams p) {
 // attention over the resident rows running in the same launch (host loads
 // queued in a compute unit delay every other load issued there).
 constexpr int kGatherWG = 8;
-constexpr int kGatherBatch = 4;   // rows per half-wave with loads in flight
+constexpr int kGatherBatch = 8;   // rows per half-wave with loads in flight
 
 // Gather and attention over the fetched rows by workgroup j of a KV head:
-// chunks [j nch / kGatherWG, (j + 1) nch / kGatherWG) of the fetch bitmap in
-// order. For each chunk it writes its part of the ascending fetch list and
-// reads its rows from pinned host memory by GPU loads (zero-copy), 32 lanes
-// (16-byte units, K then V) per row. The K lanes form the exact logits of
-// the row for the KV head's query heads; for each head that fetches the row
-// (F_h), the half-wave folds exp(logit) and the V row into a running
-// softmax (shift, sum of weights, weighted sum of V). The eight half-waves
-// are merged at the end into the workgroup's partial, index ncr + j.
+// rows [j R / kGatherWG, (j + 1) R / kGatherWG) of the KV head's ascending
+// fetch list (R rows in all), so every workgroup reads the same number of
+// rows wherever they lie. It lists its positions (up to kGatherSeg at a
+// time) with, per position, which of the KV head's query heads fetch it,
+// writes its part of the fetch list, and reads the rows from pinned host
+// memory by GPU loads (zero-copy), 32 lanes (16-byte units, K then V) per
+// row, the next batch of rows always in flight while one is used. The K
+// lanes form the exact logits of the row for the query heads; for each head
+// that fetches the row (F_h) the half-wave folds exp(logit) and the V row
+// into a running softmax (shift, sum of weights, weighted sum of V). The
+// half-waves are merged at the end into the workgroup's partial, index
+// ncr + j.
+constexpr int kGatherSeg = 4096;   // listed positions held at a time
+constexpr int kGatherWPT = 16;     // bitmap words per thread: n <= 2^17
 template <int GRP>
 __device__ __forceinline__ void gather_attend(const DParams &p, int j, int g,
                                               int b) {
@@ -1875,19 +1925,23 @@ __device__ __forceinline__ void gather_attend(const DParams &p, int j, int g,
   const bool is_v = unit >= 16;
   const int dim0 = (unit & 15) * 8;
   constexpr int HW = kBlock / 32;
-  __shared__ int s_pos[4096];
-  __shared__ uint8_t s_msk[4096];
+  constexpr int STEP = HW * kGatherBatch;   // rows per batch of the workgroup
+  __shared__ int s_pos[kGatherSeg];
+  __shared__ uint8_t s_msk[kGatherSeg];
   __shared__ uint32_t s_red[kBlock / kWave + 1];
   __shared__ float s_m[HW][GRP], s_d[HW][GRP];
   __shared__ float s_o[HW][GRP][kHeadDim];
-  int c0, c1;
-  split_range(p.nch, kGatherWG, j, c0, c1);
-  const int wpc = p.chunk / 32;
+  // this thread's bitmap words [w0, w0 + wpt) and their counts
+  const int wpt = (p.nwords + kBlock - 1) / kBlock;  // <= kGatherWPT (host check)
+  const int w0 = (int)threadIdx.x * wpt;
   const uint32_t *fb = p.fbits + (size_t)bg * p.nwords;
-  // rows fetched before the first chunk: population count of earlier words
-  uint32_t before = 0;
-  for (int i = threadIdx.x; i < c0 * wpc && i < p.nwords; i += kBlock)
-    before += (uint32_t)__popc(fb[i]);
+  uint32_t words[kGatherWPT];
+  uint32_t mine = 0;
+#pragma unroll
+  for (int k = 0; k < kGatherWPT; ++k) {
+    words[k] = (k < wpt && w0 + k < p.nwords) ? fb[w0 + k] : 0u;
+    mine += (uint32_t)__popc(words[k]);
+  }
   float qv[GRP][8];
 #pragma unroll
   for (int h = 0; h < GRP; ++h) {
@@ -1895,7 +1949,14 @@ __device__ __forceinline__ void gather_attend(const DParams &p, int j, int g,
         p.q + (size_t)row_of(p, b, g, h, GRP) * kHeadDim + dim0);
     unpack8(raw, qv[h]);
   }
-  uint32_t offset = block_sum<uint32_t>(before, s_red);
+  uint32_t total = 0;
+  const uint32_t before = block_exclusive_scan<uint32_t>(mine, s_red, &total);
+  // this workgroup's share of the list, within fetch_cap (rows past it are
+  // neither listed nor read; the status says so)
+  int lo_i, hi_i;
+  split_range((int)total, kGatherWG, j, lo_i, hi_i);
+  const uint32_t lo = (uint32_t)lo_i;
+  const uint32_t hi = min((uint32_t)hi_i, (uint32_t)p.fetch_cap);
   float mrun[GRP], dsum[GRP], acc[GRP][8];
 #pragma unroll
   for (int h = 0; h < GRP; ++h) {
@@ -1906,49 +1967,60 @@ __device__ __forceinline__ void gather_attend(const DParams &p, int j, int g,
   }
   const uint16_t *src_base = p.host_kv + (size_t)bg * p.n * 2 * kHeadDim;
   int32_t *fidx = p.fidx + (size_t)bg * p.fetch_cap;
-  for (int c = c0; c < c1; ++c) {
-    const int w0 = c * wpc;
-    // chunk sizes are at most 4096 tokens (128 words)
-    uint32_t word = 0, total = 0;
-    if ((int)threadIdx.x < wpc && w0 + (int)threadIdx.x < p.nwords) word = fb[w0 + threadIdx.x];
-    const uint32_t at0 = block_exclusive_scan<uint32_t>((uint32_t)__popc(word), s_red, &total);
+  auto row_ptr = [&](int pos) {
+    return reinterpret_cast<const uint4 *>(src_base + (size_t)pos * 2 * kHeadDim + unit * 8);
+  };
+  for (uint32_t seg = lo; seg < hi; seg += kGatherSeg) {
+    const uint32_t seg_hi = min(hi, seg + (uint32_t)kGatherSeg);
+    // ---- list the positions with list index in [seg, seg_hi)
     {
-      uint32_t w = word, o = at0;
-      while (w) {
-        const int bit = __ffs(w) - 1;
-        s_pos[o++] = (w0 + (int)threadIdx.x) * 32 + bit;
-        w &= w - 1;
+      uint32_t gi = before;
+#pragma unroll
+      for (int k = 0; k < kGatherWPT; ++k) {
+        uint32_t x = words[k];
+        const uint32_t cnt = (uint32_t)__popc(x);
+        if (gi + cnt > seg && gi < seg_hi) {
+          while (x) {
+            const int bit = __ffs(x) - 1;
+            if (gi >= seg && gi < seg_hi) {
+              const int wi = w0 + k;
+              uint32_t msk = 0u;
+#pragma unroll
+              for (int h = 0; h < GRP; ++h)
+                msk |= ((p.hbits[(size_t)row_of(p, b, g, h, GRP) * p.nwords + wi] >> bit) & 1u) << h;
+              s_pos[gi - seg] = wi * 32 + bit;
+              s_msk[gi - seg] = (uint8_t)msk;
+            }
+            ++gi;
+            x &= x - 1;
+          }
+        } else {
+          gi += cnt;
+        }
       }
     }
     __syncthreads();
-    // rows past fetch_cap are neither listed nor read (the status says so)
-    const uint32_t nrow = min(total, (uint32_t)p.fetch_cap > offset
-                                         ? (uint32_t)p.fetch_cap - offset : 0u);
-    for (uint32_t k = threadIdx.x; k < nrow; k += kBlock) {
-      const int pos = s_pos[k];
-      fidx[offset + k] = pos;
-      uint32_t msk = 0u;
+    const uint32_t nrow = seg_hi - seg;
+    for (uint32_t k = threadIdx.x; k < nrow; k += kBlock) fidx[seg + k] = s_pos[k];
+    // ---- rows: batch r0 in use while batch r0 + STEP is in flight
+    uint4 cur[kGatherBatch], nxt[kGatherBatch];
 #pragma unroll
-      for (int h = 0; h < GRP; ++h)
-        msk |= ((p.hbits[(size_t)row_of(p, b, g, h, GRP) * p.nwords + pos / 32] >> (pos % 32)) & 1u) << h;
-      s_msk[k] = (uint8_t)msk;
+    for (int it = 0; it < kGatherBatch; ++it) {
+      const uint32_t rk = it * HW + hw;
+      if (rk < nrow) cur[it] = *row_ptr(s_pos[rk]);
     }
-    __syncthreads();
-    for (uint32_t r0 = 0; r0 < nrow; r0 += HW * kGatherBatch) {
-      uint4 raw[kGatherBatch];
+    for (uint32_t r0 = 0; r0 < nrow; r0 += STEP) {
 #pragma unroll
       for (int it = 0; it < kGatherBatch; ++it) {
-        const uint32_t rk = r0 + it * HW + hw;
-        if (rk < nrow)
-          raw[it] = *reinterpret_cast<const uint4 *>(
-              src_base + (size_t)s_pos[rk] * 2 * kHeadDim + unit * 8);
+        const uint32_t rk = r0 + STEP + it * HW + hw;
+        if (rk < nrow) nxt[it] = *row_ptr(s_pos[rk]);
       }
 #pragma unroll
       for (int it = 0; it < kGatherBatch; ++it) {
         const uint32_t rk = r0 + it * HW + hw;
         if (rk >= nrow) continue;  // (uniform over the half-wave)
         float x[8];
-        unpack8(raw[it], x);
+        unpack8(cur[it], x);
         const uint32_t msk = s_msk[rk];
 #pragma unroll
         for (int h = 0; h < GRP; ++h) {
@@ -1970,9 +2042,10 @@ __device__ __forceinline__ void gather_attend(const DParams &p, int j, int g,
           mrun[h] = mn;
         }
       }
+#pragma unroll
+      for (int it = 0; it < kGatherBatch; ++it) cur[it] = nxt[it];
     }
-    offset += total;
-    __syncthreads();  // s_pos and s_msk are rewritten by the next chunk
+    __syncthreads();  // s_pos and s_msk are rewritten by the next segment
   }
   // merge the half-waves' running sums into the workgroup's partial
   if (unit == 16) {
@@ -2006,9 +2079,9 @@ __device__ __forceinline__ void gather_attend(const DParams &p, int j, int g,
     if (e == 0) p.apart[(size_t)row * np + x] = make_float2(mx, d);
   }
   if (j == kGatherWG - 1 && threadIdx.x == 0) {
-    p.fcount[bg] = (int32_t)offset;
-    if (offset > (uint32_t)p.fetch_cap) atomicOr(p.status, VKV_STATUS_FETCH_OVERFLOW);
-    const uint32_t moved = min(offset, (uint32_t)p.fetch_cap);
+    p.fcount[bg] = (int32_t)total;
+    if (total > (uint32_t)p.fetch_cap) atomicOr(p.status, VKV_STATUS_FETCH_OVERFLOW);
+    const uint32_t moved = min(total, (uint32_t)p.fetch_cap);
     atomicAdd(p.host_bytes, (unsigned long long)moved * 2ull * kHeadDim * 2ull);
   }
 }
@@ -2271,7 +2344,11 @@ DecodeLayout decode_layout(const vkv_decode_args &a) {
   const int target = (int)((2048 + groups_ll - 1) / groups_ll);
   const int rmax = a.cap < a.n_tokens ? a.cap : a.n_tokens;
   // (each at most 32, so the merge sees at most 64 partial sums)
-  L.ncr = std::max(1, std::min(std::min(target, 32), (rmax + 63) / 64));
+  // (and with the gather workgroups of the same launch, at most one
+  // workgroup per compute unit where the batch allows)
+  const int fit = (int)(256 / std::max<long long>(1, groups_ll)) - kGatherWG;
+  L.ncr = std::max(1, std::min(std::min(std::min(target, 32), std::max(fit, 8)),
+                               (rmax + 63) / 64));
   L.ncf = kGatherWG;
   L.npad = (L.ncr + L.ncf + 3) / 4 * 4;
   L.nwords = (a.n_tokens + 31) / 32;
