@@ -163,7 +163,7 @@ def main():
     import torch
 
     from verified_sparse_kv_amd import verkv as vk
-    from workloads import c3_shift_queries, make_decode_workload
+    from workloads import c3_shift_queries, make_decode_workload, resident_cap
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -176,7 +176,7 @@ def main():
         w["host_kv"][:, :, :, 0, :]).view(np.int16)).to(dev)
     t_v = torch.from_numpy(np.ascontiguousarray(
         w["host_kv"][:, :, :, 1, :]).view(np.int16)).to(dev)
-    cap = int(w["budget"] + 8 * math.sqrt(w["budget"]) + 64)
+    cap = resident_cap(w["budget"])
     comp = vk.compress(t_tau, t_k, t_v, w["budget"], w["n_sink"], w["n_local"],
                        w["seed"], cap)
     rc, bits = vk.vkv_check_status(vk._ptr(comp["status"]), vk._stream(None))

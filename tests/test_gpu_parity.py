@@ -9,7 +9,7 @@ import pytest
 from oracle import compress as oc
 from oracle import decode as od
 from tests import gpu_cases as gc
-from workloads import bf16_bits, bf16_to_f32, make_c5_tau
+from workloads import CONFIGS, bf16_bits, bf16_to_f32, make_c5_tau, resident_cap
 
 pytestmark = pytest.mark.gpu
 
@@ -166,6 +166,20 @@ def test_decode_c4_reduced():
     w, gpu, heads, unions, eps = _decode_case("c4", n=20000, G=2, B=2)
     s = gc.compare(w, gpu, heads, unions, eps)
     gc.say(f"  {s}")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg", ["c2", "c3", "c4"])
+def test_decode_full_size(cfg):
+    """Every row at the configuration's full size, with the resident capacity
+    and fetch capacity the benchmark uses (so the same launch shapes)."""
+    p = CONFIGS[cfg]
+    kw = dict(shift_from=p["shift_from"]) if "shift_from" in p else {}
+    w, gpu, heads, unions, eps = _decode_case(
+        cfg, cap=resident_cap(p["budget"]), **kw)
+    s = gc.compare(w, gpu, heads, unions, eps)
+    gc.say(f"  {s}")
+    assert s["fetched"] > 0
 
 
 def test_decode_fetch_all_is_exact_attention():

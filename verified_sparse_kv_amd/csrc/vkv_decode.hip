@@ -57,6 +57,7 @@ struct RowState {
   float b1, b2;           // largest and second largest b_i (with multiplicity)
   int32_t amax;           // position of the unique argmax of b_i, else -1
   int32_t eb, ev;         // fixed-point exponents for beta_i and v_i
+  double capb, capv;      // caps of beta_i and v_i in the fixed-point sums
   int32_t kstar;
   unsigned long long T;   // F_h = {i in L : key_i >= T}
   float eps1;             // eps^(L') after fetching
@@ -108,8 +109,9 @@ struct DParams {
   unsigned long long *clo;
   uint32_t *rpart;
   unsigned long long *tpart;
-  unsigned long long *candk, *candb, *candv;
-  uint32_t *candr;
+  unsigned long long *candk;
+  float *candw, *candq;  // w~ and r of each candidate
+  double *dpart;         // [row][kSelWG][2] float64 sums below the bound
   float2 *apart;     // [row][ncr + ncf] (shift, sum of weights)
   float *aparto;     // [row][d][npad] weighted sums of V, part index fastest
   int B, Hq, G, n, cap, fetch_cap, nch, ncr, ncf, npad, nwords, chunk, nrc;
@@ -120,7 +122,7 @@ struct DParams {
 
 // ------------------------------------------------------------ shared math
 struct Terms {
-  float wt, lam, bi, vi, rb;
+  float wt, lam, bi, vi, rb, qr;  // qr = (1 - r) / r
 };
 
 // lambda (Definition 2) and the three certificate terms of Lemma 1 for one
@@ -137,9 +139,20 @@ __device__ __forceinline__ Terms token_terms_w(float wt, float r, float beta,
   t.lam = lam;
   t.bi = wt * (1.0f - lam);
   const float lw = lam * wt;
-  t.vi = lw * lw * (1.0f - r) / r;
+  t.qr = (1.0f - r) / r;
+  t.vi = lw * lw * t.qr;
   t.rb = lw * fmaxf(r, 1.0f - r) / r;
   return t;
+}
+
+// beta_i and v_i in float64 for the sums that give eps^(L') itself: v_i is
+// squared in float64, so that the terms of tiny weights (a rest after the
+// dominant tokens are fetched) do not underflow.
+__device__ __forceinline__ void direct_terms(const Terms &t, double &bd,
+                                             double &vd) {
+  bd = (double)t.bi;
+  const double lw = (double)t.lam * (double)t.wt;
+  vd = lw * lw * (double)t.qr;
 }
 
 // The same from the planning logit s and the shift m (w~ = exp(s - m)).
@@ -182,6 +195,18 @@ __device__ __forceinline__ unsigned long long make_key(float gain, int pos) {
 
 __device__ __forceinline__ unsigned long long to_fx(float x, int e) {
   return (unsigned long long)__double2ull_rn(ldexp((double)x, e));
+}
+
+// A term of the selection's fixed-point sums: min(x, cap) 2^e, rounded. The
+// caps are c = 2 eps D~ for beta_i and c^2 / (2 l) for v_i: a rest holding a
+// term above its cap has eps^ >= 2 eps whether the term is capped or not, so
+// capping never changes a stopping decision, while a rest that can stop
+// holds only exact terms. The scale follows eps D~ (cap 2^e < 2^40), not the
+// largest term, so rests near the stopping point keep ~40 bits however
+// heavy the fetched tokens are; with at most 2^17 tokens no sum overflows.
+__device__ __forceinline__ unsigned long long sat_fx(float x, double cap,
+                                                     int e) {
+  return (unsigned long long)__double2ull_rn(ldexp(fmin((double)x, cap), e));
 }
 
 __device__ __forceinline__ int row_of(const DParams &p, int b, int g, int h,
@@ -767,16 +792,18 @@ __global__ __launch_bounds__(kBlock) void dk_resident(DParams p) {
 // union to the exact k* and threshold T; that is the answer whenever T >=
 // max_s lo_s (every key >= T was written). Otherwise, or when fetching every
 // candidate cannot certify the row, it runs the streaming selection below
-// instead. All sums of the selection are fixed-point integers, so a rest's
-// sum is the total minus the fetched part exactly.
+// instead. The stopping decisions use fixed-point integer sums of capped
+// terms (sat_fx), so a rest's sum is the total minus the fetched part
+// exactly; the reported eps^(L') is formed from float64 sums over the rest
+// itself, which keep their relative accuracy however small the rest is.
 constexpr int kSelUnroll = 4;       // streamed tokens per thread in flight
 constexpr int kRowChunk = 2048;     // tokens per workgroup in row passes
 constexpr int kRowTok = kRowChunk / kBlock;
 constexpr int kBetaPts = 4;         // points of h per Newton pass
 constexpr int kBetaRec = 3 * kBetaPts;
-constexpr int kBetaLaunches = 4;    // Newton passes (pass 0 is in the scan)
+constexpr int kBetaLaunches = 5;    // Newton passes (pass 0 is in the scan)
 constexpr int kBetaPassMax = 96;    // never reached: the bracket shrinks >= 2x
-constexpr int kCandMax = 4096;      // candidates sorted by the walk
+constexpr int kCandMax = 8192;      // candidates held by the walk
 constexpr int kSelDigit = 11;
 constexpr int kSelBinsP = 1 << kSelDigit;
 constexpr int kSelLevels = 5;       // five 11-bit digits cover the 55-bit key
@@ -800,8 +827,21 @@ union SelLds {
 // many tokens are fetched. It is the fallback of the candidate walk, taken
 // when the collected candidates cannot certify the row; `rs` (LDS) holds the
 // row's certificate and receives k*, T and eps^(L').
-__device__ void select_row(const DParams &p, int row, int bg, RowState &rs,
-                           SelLds &lds) {
+// The parameters the streaming selection reads, passed by value: a
+// reference to the kernel's parameter block would make the caller copy all
+// of it to scratch memory.
+struct SelArgs {
+  const float *r, *shat;
+  const uint32_t *resbits;
+  uint32_t *fbits, *hbits;
+  double a_delta, l_delta;
+  float eps;
+  int n, nwords, est;
+};
+
+__device__ __attribute__((noinline)) void select_row(const SelArgs p, int row,
+                                                     int bg, RowState &rs,
+                                                     SelLds &lds) {
   const int n = p.n;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   __shared__ unsigned long long s_u[kPlanWaves * 4 + 4];
@@ -817,6 +857,7 @@ __device__ void select_row(const DParams &p, int row, int bg, RowState &rs,
   const float af = (float)p.a_delta, lf = (float)p.l_delta;
   const double a = p.a_delta, l = p.l_delta;
   const int eb = rs.eb, ev = rs.ev;
+  const double capb = rs.capb, capv = rs.capv;
   const double sbs = ldexp(1.0, -eb), svs = ldexp(1.0, -ev);
   const uint32_t *rbits = p.resbits + (size_t)bg * p.nwords;
   uint32_t *fb = p.fbits + (size_t)bg * p.nwords;
@@ -866,8 +907,8 @@ __device__ void select_row(const DParams &p, int row, int bg, RowState &rs,
       stream([&](int, bool valid, unsigned long long key, const Terms &t) {
         if (!valid) return;
         if (first && d == 0) {
-          lb_ += to_fx(t.bi, eb);
-          lv_ += to_fx(t.vi, ev);
+          lb_ += sat_fx(t.bi, capb, eb);
+          lv_ += sat_fx(t.vi, capv, ev);
         }
         if (key >= hi_key || (key >> (off + kSelDigit)) != pre) return;
         atomicAdd(&lds.hist[(int)((key >> off) & (kSelBinsP - 1))], 1u);
@@ -950,7 +991,8 @@ __device__ void select_row(const DParams &p, int row, int bg, RowState &rs,
       if (sel) {
         const uint32_t slot =
             slot0 + (uint32_t)__popcll(msk & ((1ull << lane) - 1ull));
-        const unsigned long long bx = to_fx(t.bi, eb), vx = to_fx(t.vi, ev);
+        const unsigned long long bx = sat_fx(t.bi, capb, eb),
+                                 vx = sat_fx(t.vi, capv, ev);
         cb_ += bx;
         cv_ += vx;
         if (slot < (uint32_t)kCand) {
@@ -1056,7 +1098,6 @@ __device__ void select_row(const DParams &p, int row, int bg, RowState &rs,
     after = max(after, below_max);
     unsigned long long cb = base_b + ib - lb2, cvv = base_v + iv - lv2;
     int best = 0x7fffffff;
-    double best_e = 0.0;
 #pragma unroll
     for (int q = 0; q < PT; ++q) {
       const int k = k0 + q;
@@ -1071,7 +1112,6 @@ __device__ void select_row(const DParams &p, int row, int bg, RowState &rs,
                               (double)__uint_as_float(bt), rs.dnorm, a, l);
       if (e < (double)p.eps) {
         best = k;
-        best_e = e;
       }
     }
     int first_k = best;
@@ -1082,13 +1122,11 @@ __device__ void select_row(const DParams &p, int row, int bg, RowState &rs,
     if (best == first_k && best != 0x7fffffff) {
       rs.kstar = (int)(fet_c + (uint32_t)best + 1u);
       rs.T = lds.cand.key[best];
-      rs.eps1 = (float)best_e;
     }
     __syncthreads();
     if (threadIdx.x == 0 && first_k >= nc) {
       rs.kstar = (int)(fet_c + (uint32_t)nc);
       rs.T = nc > 0 ? lds.cand.key[nc - 1] : (hi_key == kKeyEnd ? ~0ull : hi_key);
-      rs.eps1 = (float)e_below;
     }
     // mark the fetched candidates
     for (int c = threadIdx.x; c <= kk; c += kPlanThreads) {
@@ -1099,8 +1137,26 @@ __device__ void select_row(const DParams &p, int row, int bg, RowState &rs,
     __syncthreads();
     break;
   }
+  // eps^(L') from float64 sums over the rest (every token below T), added
+  // directly rather than as the total minus the fetched part
+  const unsigned long long T = rs.T;
+  double dr[2] = {0.0, 0.0};
+  uint32_t bm = 0u;
+  stream([&](int, bool valid, unsigned long long key, const Terms &t) {
+    if (!valid || key >= T) return;
+    double bd, vd;
+    direct_terms(t, bd, vd);
+    dr[0] += bd;
+    dr[1] += vd;
+    bm = max(bm, __float_as_uint(t.rb));
+  });
+  plan_reduce<double, 2>(dr);
+  bm = plan_max<uint32_t>(bm);
+  if (threadIdx.x == 0)
+    rs.eps1 = (float)eps_of(dr[0], dr[1], (double)__uint_as_float(bm), rs.dnorm,
+                            a, l);
+  __syncthreads();
 }
-
 
 // ------------------------------------------------------------ row passes
 // This thread's tokens of chunk c of a row: r and the planning logit s (r = 1
@@ -1288,10 +1344,16 @@ __global__ __launch_bounds__(kBlock) void dk_rbeta(DParams p, int pass) {
   const int c = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
   const int row = b * p.Hq + hq, bg = b * p.G + hq / GRP;
   const size_t rows = (size_t)p.B * p.Hq;
+  const int q = (pass - 1) & 1;
+  if (pass >= 3 && p.bstate[(size_t)q * rows + row].done) {
+    // settled by an earlier pass: carry the state forward, read nothing else
+    if (c == 0 && threadIdx.x == 0)
+      p.bstate[(size_t)(pass & 1) * rows + row] = p.bstate[(size_t)q * rows + row];
+    return;
+  }
   float w8[kRowTok], r8[kRowTok], s8[kRowTok];
   row_load(p, row, bg, c, r8, s8);
   // the previous pass: this thread's share of the records, and the state
-  const int q = (pass - 1) & 1;
   double rv[kBetaRec];
   BetaState st{};
   float m;
@@ -1348,16 +1410,17 @@ __global__ __launch_bounds__(kBlock) void dk_rcert(DParams p) {
   }
   if (!st.done) {
     // rare: more Newton passes, each over the whole row by this workgroup
-    const float *rr = p.r + (size_t)bg * p.n;
-    const float *sh = p.shat + (size_t)row * p.n;
     for (int it = 0; it < kBetaPassMax && !st.done; ++it) {
       double pts[kBetaPts], v[kBetaRec];
       beta_points(st, pts);
 #pragma unroll
       for (int k = 0; k < kBetaRec; ++k) v[k] = 0.0;
-      for (int i = threadIdx.x; i < p.n; i += kBlock) {
-        const float ri = rr[i];
-        if (ri < 1.0f) beta_accumulate(pts, expf(sh[i] - m), ri, v);
+      for (int cc = 0; cc < p.nrc; ++cc) {
+        float fr[kRowTok], fs[kRowTok], fw[kRowTok];
+        row_load(p, row, bg, cc, fr, fs);
+        row_weights(m, fr, fs, fw);
+#pragma unroll
+        for (int u = 0; u < kRowTok; ++u) beta_accumulate(pts, fw[u], fr[u], v);
       }
       blk_reduce<double, kBetaRec, kBlock>(v);
       st = beta_advance(st, v);
@@ -1448,11 +1511,13 @@ __device__ __forceinline__ void row_certificate(const DParams &p, CertShare sh,
     z.kstar = 0;
     z.T = ~0ull;
     z.fetch = e0 < (double)p.eps ? 0 : 1;
+    z.capb = 2.0 * (double)p.eps * dnorm;
+    z.capv = z.capb * z.capb / (2.0 * l);
     int eb = 0, ev = 0;
-    if (tb > 0.0) { (void)frexp(tb, &eb); eb = 61 - eb; }
-    if (tv > 0.0) { (void)frexp(tv, &ev); ev = 61 - ev; }
-    z.eb = eb;
-    z.ev = ev;
+    (void)frexp(z.capb, &eb);
+    (void)frexp(z.capv, &ev);
+    z.eb = 40 - eb;
+    z.ev = 40 - ev;
     rs = z;
   }
   __syncthreads();
@@ -1463,6 +1528,7 @@ __device__ __forceinline__ void row_certificate(const DParams &p, CertShare sh,
 // run of high-gain positions is spread over all of them.
 constexpr int kSelWG = 16;
 constexpr int kCandWG = kCandMax / kSelWG;
+constexpr int kTier0 = kCandWG / 4;  // candidates per workgroup tried first
 constexpr int kSelBlk = 64;
 constexpr int kSelIt = 8;  // tokens per thread whose keys stay in registers
 
@@ -1480,7 +1546,8 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
   __shared__ RowState rs;
   __shared__ uint32_t s_hist[kSelBinsP];
   __shared__ uint32_t s_cnt;
-  __shared__ int s_j0;
+  __shared__ int s_j0, s_j1;
+  __shared__ uint32_t s_c0, s_cnt1;
   const float *rr = p.r + (size_t)bg * p.n;
   const float *sh = p.shat + (size_t)row * p.n;
   const int n = p.n;
@@ -1503,103 +1570,168 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
   const CertShare cs = cert_rec_load(p, row);
   const double beta = p.rbeta[2 * row], dnorm = p.rbeta[2 * row + 1];
   for (int i = threadIdx.x; i < kSelBinsP; i += kBlock) s_hist[i] = 0u;
-  if (threadIdx.x == 0) s_cnt = 0u;
+  if (threadIdx.x == 0) {
+    s_cnt = 0u;
+    s_cnt1 = 0u;
+  }
   row_certificate(p, cs, m, beta, dnorm, rs);
   if (s == 0 && threadIdx.x == 0) p.rows[row] = rs;
   if (!rs.fetch) return;
   const float betaf = (float)rs.beta;
   const float af = (float)p.a_delta, lf = (float)p.l_delta;
   const int eb = rs.eb, ev = rs.ev;
+  const double capb = rs.capb, capv = rs.capv;
   auto key_of = [&](int i, float ri, float si, Terms &t) {
     t = token_terms_w(expf(si - m), ri, betaf, p.est);
     return make_key(token_gain(t, i, rs, af, lf), i);
   };
   // ---- keys: histogram and totals
   unsigned long long key8[kSelIt];
-  uint32_t rb8[kSelIt];
   unsigned long long tx[2] = {0ull, 0ull};
 #pragma unroll
   for (int it = 0; it < kSelIt; ++it) {
     key8[it] = 0ull;
-    rb8[it] = 0u;
     if (!(r8[it] < 1.0f)) continue;
     Terms t;
     key8[it] = key_of(pos_of(it), r8[it], s8[it], t);
-    rb8[it] = __float_as_uint(t.rb);
     atomicAdd(&s_hist[(int)(key8[it] >> sel_off(0))], 1u);
-    tx[0] += to_fx(t.bi, eb);
-    tx[1] += to_fx(t.vi, ev);
+    tx[0] += sat_fx(t.bi, capb, eb);
+    tx[1] += sat_fx(t.vi, capv, ev);
   }
-  for (int it = kSelIt; it < iters; ++it) {  // long rows: recomputed below
-    const int i = pos_of(it);
-    if (i >= n) continue;
-    const float ri = rr[i];
-    if (!(ri < 1.0f)) continue;
-    Terms t;
-    const unsigned long long key = key_of(i, ri, sh[i], t);
-    atomicAdd(&s_hist[(int)(key >> sel_off(0))], 1u);
-    tx[0] += to_fx(t.bi, eb);
-    tx[1] += to_fx(t.vi, ev);
+  // long rows: the rest in batches of kSelIt tokens (recomputed below)
+  auto load_batch = [&](int it0, float (&rb)[kSelIt], float (&sb)[kSelIt]) {
+#pragma unroll
+    for (int k = 0; k < kSelIt; ++k) {
+      const int i = pos_of(it0 + k);
+      const bool ok = it0 + k < iters && i < n;
+      rb[k] = ok ? rr[i] : 1.0f;
+      sb[k] = ok ? sh[i] : 0.0f;
+    }
+  };
+  for (int it0 = kSelIt; it0 < iters; it0 += kSelIt) {
+    float rb[kSelIt], sb[kSelIt];
+    load_batch(it0, rb, sb);
+#pragma unroll
+    for (int k = 0; k < kSelIt; ++k) {
+      if (!(rb[k] < 1.0f)) continue;
+      Terms t;
+      const unsigned long long key = key_of(pos_of(it0 + k), rb[k], sb[k], t);
+      atomicAdd(&s_hist[(int)(key >> sel_off(0))], 1u);
+      tx[0] += sat_fx(t.bi, capb, eb);
+      tx[1] += sat_fx(t.vi, capv, ev);
+    }
   }
   blk_reduce<unsigned long long, 2, kBlock>(tx);
-  // ---- local bound: lane owns bins [lane * 32, lane * 32 + 32)
+  // ---- local bounds: lane owns bins [lane * 32, lane * 32 + 32). Tier 0
+  // is the smallest bin edge with at most kTier0 keys at or above it, tier 1
+  // the same for kCandWG; c0 = keys at or above the tier-0 edge.
   if (wave == 0) {
     constexpr int PER = kSelBinsP / kWave;
     uint32_t lc = 0u;
     for (int k = 0; k < PER; ++k) lc += s_hist[lane * PER + k];
     const uint32_t incl = wave_incl_scan<uint32_t>(lc, lane);
-    uint32_t c = __shfl(incl, kWave - 1, kWave) - incl;  // keys in lanes above
-    int j = kSelBinsP;
-    if (c <= (uint32_t)kCandWG) {
-      for (int k = PER - 1; k >= 0; --k) {
-        c += s_hist[lane * PER + k];
-        if (c > (uint32_t)kCandWG) break;
-        j = lane * PER + k;
+    const uint32_t above = __shfl(incl, kWave - 1, kWave) - incl;
+    auto edge = [&](uint32_t cap, uint32_t &cnt) {
+      uint32_t c = above, cj = 0u;
+      int j = kSelBinsP;
+      if (c <= cap) {
+        for (int k = PER - 1; k >= 0; --k) {
+          c += s_hist[lane * PER + k];
+          if (c > cap) break;
+          j = lane * PER + k;
+          cj = c;
+        }
       }
+      int jm = j;
+      for (int o = 32; o >= 1; o >>= 1) jm = min(jm, __shfl_xor(jm, o, kWave));
+      cnt = wave_max(j == jm ? cj : 0u);  // one lane owns bin jm
+      return jm;
+    };
+    uint32_t c0, c1;
+    const int j0 = edge((uint32_t)kTier0, c0);
+    const int j1 = edge((uint32_t)kCandWG, c1);
+    if (lane == 0) {
+      s_j0 = j0;
+      s_j1 = j1;
+      s_c0 = c0;
     }
-    for (int o = 32; o >= 1; o >>= 1) j = min(j, __shfl_xor(j, o, kWave));
-    if (lane == 0) s_j0 = j;
   }
   __syncthreads();
-  const unsigned long long lo =
+  const unsigned long long lo0 =
       s_j0 < kSelBinsP ? ((unsigned long long)s_j0 << sel_off(0)) : kKeyEnd;
-  // ---- the keys at or above lo, and the max of b_i below it
+  const unsigned long long lo =
+      s_j1 < kSelBinsP ? ((unsigned long long)s_j1 << sel_off(0)) : kKeyEnd;
+  const uint32_t c0 = s_c0;
+  // ---- the keys at or above lo (with w~ and r), tier 0 first; for the
+  // keys below lo and for those of tier 1 alone, the max of b_i and the
+  // float64 sums of beta_i and v_i
   const size_t seg = ((size_t)row * kSelWG + s) * kCandWG;
-  uint32_t below = 0u;
-  auto emit = [&](int i, float ri, float si, unsigned long long key) {
-    const uint32_t slot = atomicAdd(&s_cnt, 1u);
-    Terms t;
-    key_of(i, ri, si, t);
+  uint32_t below = 0u, below1 = 0u;
+  double dsum[4] = {0.0, 0.0, 0.0, 0.0};
+  auto emit = [&](float ri, float si, unsigned long long key) {
+    uint32_t slot;
+    if (key >= lo0) {
+      slot = atomicAdd(&s_cnt, 1u);
+    } else {
+      slot = c0 + atomicAdd(&s_cnt1, 1u);
+      const Terms t = token_terms_w(expf(si - m), ri, betaf, p.est);
+      double bd, vd;
+      direct_terms(t, bd, vd);
+      dsum[2] += bd;
+      dsum[3] += vd;
+      below1 = max(below1, __float_as_uint(t.rb));
+    }
     if (slot < (uint32_t)kCandWG) {
       p.candk[seg + slot] = key;
-      p.candb[seg + slot] = to_fx(t.bi, eb);
-      p.candv[seg + slot] = to_fx(t.vi, ev);
-      p.candr[seg + slot] = __float_as_uint(t.rb);
+      p.candw[seg + slot] = expf(si - m);
+      p.candq[seg + slot] = ri;
     }
+  };
+  auto rest = [&](const Terms &t) {
+    double bd, vd;
+    direct_terms(t, bd, vd);
+    dsum[0] += bd;
+    dsum[1] += vd;
+    below = max(below, __float_as_uint(t.rb));
   };
 #pragma unroll
   for (int it = 0; it < kSelIt; ++it) {
     if (!(r8[it] < 1.0f)) continue;
-    if (key8[it] >= lo) emit(pos_of(it), r8[it], s8[it], key8[it]);
-    else below = max(below, rb8[it]);
+    if (key8[it] >= lo) {
+      emit(r8[it], s8[it], key8[it]);
+    } else {
+      rest(token_terms_w(expf(s8[it] - m), r8[it], betaf, p.est));
+    }
   }
-  for (int it = kSelIt; it < iters; ++it) {
-    const int i = pos_of(it);
-    if (i >= n) continue;
-    const float ri = rr[i];
-    if (!(ri < 1.0f)) continue;
-    const float si = sh[i];
-    Terms t;
-    const unsigned long long key = key_of(i, ri, si, t);
-    if (key >= lo) emit(i, ri, si, key);
-    else below = max(below, __float_as_uint(t.rb));
+  for (int it0 = kSelIt; it0 < iters; it0 += kSelIt) {
+    float rb[kSelIt], sb[kSelIt];
+    load_batch(it0, rb, sb);
+#pragma unroll
+    for (int k = 0; k < kSelIt; ++k) {
+      if (!(rb[k] < 1.0f)) continue;
+      Terms t;
+      const unsigned long long key = key_of(pos_of(it0 + k), rb[k], sb[k], t);
+      if (key >= lo) emit(rb[k], sb[k], key);
+      else rest(t);
+    }
   }
   below = blk_max<uint32_t, kBlock>(below);
+  below1 = blk_max<uint32_t, kBlock>(below1);
+  blk_reduce<double, 4, kBlock>(dsum);
   if (threadIdx.x == 0) {
+    // per tier: candidates, bound, and over the tokens not written in that
+    // tier the max of b_i and the float64 sums
     const size_t at = (size_t)row * kSelWG + s;
-    p.ccount[at] = min(s_cnt, (uint32_t)kCandWG);
-    p.clo[at] = lo;
-    p.rpart[at] = below;
+    p.ccount[2 * at] = min(s_cnt, c0);
+    p.ccount[2 * at + 1] = min(c0 + s_cnt1, (uint32_t)kCandWG);
+    p.clo[2 * at] = lo0;
+    p.clo[2 * at + 1] = lo;
+    p.rpart[2 * at] = max(below, below1);
+    p.rpart[2 * at + 1] = below;
+    p.dpart[4 * at] = dsum[0] + dsum[2];
+    p.dpart[4 * at + 1] = dsum[1] + dsum[3];
+    p.dpart[4 * at + 2] = dsum[0];
+    p.dpart[4 * at + 3] = dsum[1];
     p.tpart[2 * at] = tx[0];
     p.tpart[2 * at + 1] = tx[1];
   }
@@ -1616,9 +1748,8 @@ struct WalkBin {
 union WalkLds {
   struct {
     unsigned long long key[kCandMax];
-    unsigned long long bfx[kCandMax];
-    unsigned long long vfx[kCandMax];
-    uint32_t rb[kCandMax];
+    float w[kCandMax];  // w~ and r: every term is recomputed from them
+    float r[kCandMax];
     WalkBin bin[kWalkBins];
   } c;
   SelLds sel;
@@ -1633,7 +1764,6 @@ struct WalkState {
   uint32_t bmax;              // max b_i certainly left in the rest
   int32_t off, w;             // current digit: key bits [off, off + w)
   int32_t done, kstar;
-  float eps1;
 };
 
 // One 1024-thread workgroup per fetching row: the stopping rule (eq. 10)
@@ -1656,241 +1786,283 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rwalk(DParams p) {
   __shared__ uint32_t s_wc[kSelWG], s_off[kSelWG];
   __shared__ unsigned long long s_tot[2], s_lomax;
   __shared__ uint32_t s_below;
+  __shared__ double s_dsum[2];
   __shared__ int s_nc;
-  // every load first: the row, the candidate workgroups' summaries and all
-  // candidate slots (those past a workgroup's count are read but not used)
-  constexpr int PT = kCandMax / kPlanThreads;
+  // the row and the candidate workgroups' summaries of both tiers
   const size_t cb0 = (size_t)row * kCandMax;
   if (threadIdx.x == 0) rs = p.rows[row];
-  uint32_t wc = 0u, wbelow = 0u;
-  unsigned long long wlo = 0ull, wtb = 0ull, wtv = 0ull;
+  __shared__ uint32_t s_pc[2][kSelWG], s_pb[2][kSelWG];
+  __shared__ unsigned long long s_plo[2][kSelWG], s_pt[2][kSelWG];
+  __shared__ double s_pd[4][kSelWG];
   if (threadIdx.x < kSelWG) {
-    const size_t at = (size_t)row * kSelWG + threadIdx.x;
-    wc = p.ccount[at];
-    wlo = p.clo[at];
-    wbelow = p.rpart[at];
-    wtb = p.tpart[2 * at];
-    wtv = p.tpart[2 * at + 1];
-  }
-  unsigned long long ck[PT], cbx[PT], cvx[PT];
-  uint32_t crb[PT];
+    const int j = threadIdx.x;
+    const size_t at = (size_t)row * kSelWG + j;
 #pragma unroll
-  for (int q = 0; q < PT; ++q) {
-    const size_t at = cb0 + threadIdx.x + (size_t)q * kPlanThreads;
-    ck[q] = p.candk[at];
-    cbx[q] = p.candb[at];
-    cvx[q] = p.candv[at];
-    crb[q] = p.candr[at];
+    for (int t = 0; t < 2; ++t) {
+      s_pc[t][j] = p.ccount[2 * at + t];
+      s_plo[t][j] = p.clo[2 * at + t];
+      s_pb[t][j] = p.rpart[2 * at + t];
+      s_pt[t][j] = p.tpart[2 * at + t];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) s_pd[k][j] = p.dpart[4 * at + k];
   }
   __syncthreads();
   if (!rs.fetch) return;
-  // the workgroups' summaries: offsets of their candidates, totals over L,
-  // the max of b_i over every token not written, the largest local bound
-  if (wave == 0) {
-    const uint32_t incl = wave_incl_scan<uint32_t>(wc, lane);
-    if (lane < kSelWG) {
-      s_wc[lane] = wc;
-      s_off[lane] = incl - wc;
-    }
-    const unsigned long long tb = wave_sum(wtb), tv = wave_sum(wtv);
-    const uint32_t bl = wave_max(wbelow);
-    const unsigned long long lm = wave_max(wlo);
-    if (lane == kWave - 1) s_nc = (int)incl;
-    if (lane == 0) {
-      s_tot[0] = tb;
-      s_tot[1] = tv;
-      s_below = bl;
-      s_lomax = lm;
-    }
-  }
-  __syncthreads();
-  const int nc = s_nc;
-  const unsigned long long tot_b = s_tot[0], tot_v = s_tot[1];
-  const uint32_t below = s_below;
   const double a = p.a_delta, l = p.l_delta;
-  const double sbs = ldexp(1.0, -rs.eb), svs = ldexp(1.0, -rs.ev);
-  unsigned long long cs[2] = {0ull, 0ull};
-  unsigned long long kmin = ~0ull, kmax = 0ull;
-#pragma unroll
-  for (int q = 0; q < PT; ++q) {
-    const int idx = (int)threadIdx.x + q * kPlanThreads;
-    const int sw = idx / kCandWG, slot = idx % kCandWG;
-    if (slot >= (int)s_wc[sw]) continue;
-    const int k = (int)s_off[sw] + slot;
-    lds.c.key[k] = ck[q];
-    lds.c.bfx[k] = cbx[q];
-    lds.c.vfx[k] = cvx[q];
-    lds.c.rb[k] = crb[q];
-    cs[0] += cbx[q];
-    cs[1] += cvx[q];
-    kmin = min(kmin, ck[q]);
-    kmax = max(kmax, ck[q]);
-  }
-  plan_reduce<unsigned long long, 2>(cs);
-  // fetching every candidate leaves exactly the tokens not written
-  const double e_below =
-      eps_of((double)(tot_b - cs[0]) * sbs, (double)(tot_v - cs[1]) * svs,
-             (double)__uint_as_float(below), rs.dnorm, a, l);
-  if (!(e_below < (double)p.eps) || nc == 0) {
-    __syncthreads();
-    select_row(p, row, bg, rs, lds.sel);
-    __syncthreads();
-    if (threadIdx.x == 0) p.rows[row] = rs;
-    return;
-  }
-  kmax = plan_max<unsigned long long>(kmax);
-  kmin = ~plan_max<unsigned long long>(~kmin);
-  if (threadIdx.x == 0) {
-    // the first digit starts where the candidates' keys start to differ
-    const int span = kmax == kmin ? 0 : 64 - __clzll((long long)(kmax ^ kmin));
-    WalkState z{};
-    z.off = max(0, span - 8);
-    z.w = max(1, span - z.off);
-    z.pre = kmax >> (z.off + z.w);
-    z.bmax = below;
-    ws = z;
-  }
-  __syncthreads();
-  for (int level = 0; level < 10; ++level) {  // at most 7 eight-bit digits
-    if (threadIdx.x < kWalkBins) lds.c.bin[threadIdx.x] = WalkBin{0u, 0u, 0ull, 0ull};
-    __syncthreads();
-    const int off = ws.off, w = ws.w;
-    const unsigned long long pre = ws.pre;
-    for (int k = threadIdx.x; k < nc; k += kPlanThreads) {
-      const unsigned long long key = lds.c.key[k];
-      if ((key >> (off + w)) != pre) continue;
-      WalkBin &x = lds.c.bin[(int)((key >> off) & ((1ull << w) - 1ull))];
-      atomicAdd(&x.cnt, 1u);
-      atomicAdd(&x.bsum, lds.c.bfx[k]);
-      atomicAdd(&x.vsum, lds.c.vfx[k]);
-      atomicMax(&x.bmax, lds.c.rb[k]);
+  const int eb = rs.eb, ev = rs.ev;
+  const double capb = rs.capb, capv = rs.capv;
+  const double sbs = ldexp(1.0, -eb), svs = ldexp(1.0, -ev);
+  const float betaf = (float)rs.beta;
+  const int est = p.est;
+  // Tier 0 holds each workgroup's top kTier0 keys, tier 1 all kCandWG; the
+  // larger set is only walked when the smaller one cannot decide the row.
+#pragma unroll 1
+  for (int tier = 0; tier < 2; ++tier) {
+    const int cap = tier == 0 ? kTier0 : kCandWG;
+    if (wave == 0) {
+      const bool on = lane < kSelWG;
+      const int j = on ? lane : 0;
+      const uint32_t c = on ? s_pc[tier][j] : 0u;
+      const uint32_t incl = wave_incl_scan<uint32_t>(c, lane);
+      if (on) {
+        s_wc[lane] = c;
+        s_off[lane] = incl - c;
+      }
+      const unsigned long long tb = wave_sum(on ? s_pt[0][j] : 0ull),
+                               tv = wave_sum(on ? s_pt[1][j] : 0ull);
+      const double db = wave_sum(on ? s_pd[2 * tier][j] : 0.0),
+                   dv = wave_sum(on ? s_pd[2 * tier + 1][j] : 0.0);
+      const uint32_t bl = wave_max(on ? s_pb[tier][j] : 0u);
+      const unsigned long long lm = wave_max(on ? s_plo[tier][j] : 0ull);
+      if (lane == kWave - 1) s_nc = (int)incl;
+      if (lane == 0) {
+        s_tot[0] = tb;
+        s_tot[1] = tv;
+        s_below = bl;
+        s_lomax = lm;
+        s_dsum[0] = db;
+        s_dsum[1] = dv;
+      }
     }
     __syncthreads();
-    if (wave == 0) {
-      // lane owns bins 4 lane .. 4 lane + 3
-      constexpr int PER = kWalkBins / kWave;
-      uint32_t lc = 0u, lmx = 0u;
-      unsigned long long lb = 0ull, lv = 0ull;
+    const int nc = s_nc;
+    const unsigned long long tot_b = s_tot[0], tot_v = s_tot[1];
+    const uint32_t below = s_below;
+    // the tier's candidates into LDS (loads first), their fixed-point sums
+    unsigned long long cs[2] = {0ull, 0ull};
+    unsigned long long kmin = ~0ull, kmax = 0ull;
+    for (int q0 = 0; q0 < kSelWG * cap; q0 += kPlanThreads * 2) {
+      unsigned long long ck[2];
+      float cw[2], cq[2];
+      int dst[2];
 #pragma unroll
-      for (int q = 0; q < PER; ++q) {
-        const WalkBin &x = lds.c.bin[lane * PER + q];
-        lc += x.cnt;
-        lb += x.bsum;
-        lv += x.vsum;
-        lmx = max(lmx, x.bmax);
-      }
-      // sums over the lanes above, max over the lanes below
-      uint32_t sc = lc;
-      unsigned long long sb = lb, sv = lv;
-      for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t xc = __shfl_down(sc, o, kWave);
-        const unsigned long long xb = __shfl_down(sb, o, kWave), xv = __shfl_down(sv, o, kWave);
-        if (lane + o < kWave) {
-          sc += xc;
-          sb += xb;
-          sv += xv;
+      for (int u = 0; u < 2; ++u) {
+        const int idx = q0 + u * kPlanThreads + (int)threadIdx.x;
+        const int sw = idx / cap, slot = idx % cap;
+        dst[u] = -1;
+        if (idx < kSelWG * cap && slot < (int)s_wc[sw]) {
+          const size_t at = cb0 + (size_t)sw * kCandWG + slot;
+          ck[u] = p.candk[at];
+          cw[u] = p.candw[at];
+          cq[u] = p.candq[at];
+          dst[u] = (int)s_off[sw] + slot;
         }
       }
-      sc -= lc;
-      sb -= lb;
-      sv -= lv;
-      uint32_t pm = lmx;
-      for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t x = __shfl_up(pm, o, kWave);
-        if (lane >= o) pm = max(pm, x);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if (dst[u] < 0) continue;
+        lds.c.key[dst[u]] = ck[u];
+        lds.c.w[dst[u]] = cw[u];
+        lds.c.r[dst[u]] = cq[u];
+        const Terms t = token_terms_w(cw[u], cq[u], betaf, est);
+        cs[0] += sat_fx(t.bi, capb, eb);
+        cs[1] += sat_fx(t.vi, capv, ev);
+        kmin = min(kmin, ck[u]);
+        kmax = max(kmax, ck[u]);
       }
-      uint32_t mlow = __shfl_up(pm, 1, kWave);
-      if (lane == 0) mlow = 0u;
-      mlow = max(mlow, ws.bmax);
-      // the lane's highest bin whose fetched-through eps^ is below eps
-      int best = -1;
-      {
-        unsigned long long fb = ws.ab + sb, fv = ws.av + sv;
-        for (int q = PER - 1; q >= 0 && best < 0; --q) {
+    }
+    plan_reduce<unsigned long long, 2>(cs);
+    // fetching every candidate leaves exactly the tokens not written
+    const double e_below =
+        eps_of((double)(tot_b - cs[0]) * sbs, (double)(tot_v - cs[1]) * svs,
+               (double)__uint_as_float(below), rs.dnorm, a, l);
+    if (!(e_below < (double)p.eps) || nc == 0) {
+      __syncthreads();
+      continue;
+    }
+    kmax = plan_max<unsigned long long>(kmax);
+    kmin = ~plan_max<unsigned long long>(~kmin);
+    if (threadIdx.x == 0) {
+      // the first digit starts where the candidates' keys start to differ
+      const int span = kmax == kmin ? 0 : 64 - __clzll((long long)(kmax ^ kmin));
+      WalkState z{};
+      z.off = max(0, span - 8);
+      z.w = max(1, span - z.off);
+      z.pre = kmax >> (z.off + z.w);
+      z.bmax = below;
+      ws = z;
+    }
+    __syncthreads();
+    for (int level = 0; level < 10; ++level) {  // at most 7 eight-bit digits
+      if (threadIdx.x < kWalkBins) lds.c.bin[threadIdx.x] = WalkBin{0u, 0u, 0ull, 0ull};
+      __syncthreads();
+      const int off = ws.off, w = ws.w;
+      const unsigned long long pre = ws.pre;
+      for (int k = threadIdx.x; k < nc; k += kPlanThreads) {
+        const unsigned long long key = lds.c.key[k];
+        if ((key >> (off + w)) != pre) continue;
+        WalkBin &x = lds.c.bin[(int)((key >> off) & ((1ull << w) - 1ull))];
+        const Terms t = token_terms_w(lds.c.w[k], lds.c.r[k], betaf, est);
+        atomicAdd(&x.cnt, 1u);
+        atomicAdd(&x.bsum, sat_fx(t.bi, capb, eb));
+        atomicAdd(&x.vsum, sat_fx(t.vi, capv, ev));
+        atomicMax(&x.bmax, __float_as_uint(t.rb));
+      }
+      __syncthreads();
+      if (wave == 0) {
+        // lane owns bins 4 lane .. 4 lane + 3
+        constexpr int PER = kWalkBins / kWave;
+        uint32_t lc = 0u, lmx = 0u;
+        unsigned long long lb = 0ull, lv = 0ull;
+  #pragma unroll
+        for (int q = 0; q < PER; ++q) {
           const WalkBin &x = lds.c.bin[lane * PER + q];
-          fb += x.bsum;
-          fv += x.vsum;
+          lc += x.cnt;
+          lb += x.bsum;
+          lv += x.vsum;
+          lmx = max(lmx, x.bmax);
+        }
+        // sums over the lanes above, max over the lanes below
+        uint32_t sc = lc;
+        unsigned long long sb = lb, sv = lv;
+        for (int o = 1; o < kWave; o <<= 1) {
+          const uint32_t xc = __shfl_down(sc, o, kWave);
+          const unsigned long long xb = __shfl_down(sb, o, kWave), xv = __shfl_down(sv, o, kWave);
+          if (lane + o < kWave) {
+            sc += xc;
+            sb += xb;
+            sv += xv;
+          }
+        }
+        sc -= lc;
+        sb -= lb;
+        sv -= lv;
+        uint32_t pm = lmx;
+        for (int o = 1; o < kWave; o <<= 1) {
+          const uint32_t x = __shfl_up(pm, o, kWave);
+          if (lane >= o) pm = max(pm, x);
+        }
+        uint32_t mlow = __shfl_up(pm, 1, kWave);
+        if (lane == 0) mlow = 0u;
+        mlow = max(mlow, ws.bmax);
+        // the lane's highest bin whose fetched-through eps^ is below eps
+        int best = -1;
+        {
+          unsigned long long fb = ws.ab + sb, fv = ws.av + sv;
+          for (int q = PER - 1; q >= 0 && best < 0; --q) {
+            const WalkBin &x = lds.c.bin[lane * PER + q];
+            fb += x.bsum;
+            fv += x.vsum;
+            uint32_t mb = mlow;
+            for (int q2 = 0; q2 < q; ++q2) mb = max(mb, lds.c.bin[lane * PER + q2].bmax);
+            const double e = eps_of((double)(tot_b - fb) * sbs,
+                                    (double)(tot_v - fv) * svs,
+                                    (double)__uint_as_float(mb), rs.dnorm, a, l);
+            if (x.cnt > 0u && e < (double)p.eps) best = lane * PER + q;
+          }
+        }
+        int top = best;
+        for (int o = 32; o >= 1; o >>= 1) top = max(top, __shfl_xor(top, o, kWave));
+        if (top < 0) top = 0;  // unreachable: fetching every candidate certifies
+        if (lane == top / PER) {
+          const int q = top % PER;
+          uint32_t c = sc;
+          unsigned long long fb = ws.ab + sb, fv = ws.av + sv;
+          for (int q2 = PER - 1; q2 > q; --q2) {
+            const WalkBin &x = lds.c.bin[lane * PER + q2];
+            c += x.cnt;
+            fb += x.bsum;
+            fv += x.vsum;
+          }
           uint32_t mb = mlow;
           for (int q2 = 0; q2 < q; ++q2) mb = max(mb, lds.c.bin[lane * PER + q2].bmax);
-          const double e = eps_of((double)(tot_b - fb) * sbs,
-                                  (double)(tot_v - fv) * svs,
-                                  (double)__uint_as_float(mb), rs.dnorm, a, l);
-          if (x.cnt > 0u && e < (double)p.eps) best = lane * PER + q;
+          const WalkBin &x = lds.c.bin[top];
+          if (x.cnt <= 1u || off == 0) {
+            ws.kstar = (int)(ws.ac + c + x.cnt);
+            ws.pre = (pre << w) | (unsigned long long)top;  // the last key's digits
+            ws.done = 1;
+          } else {
+            ws.ac += c;
+            ws.ab = fb;
+            ws.av = fv;
+            ws.bmax = mb;
+            ws.pre = (pre << w) | (unsigned long long)top;
+            const int noff = max(0, off - 8);
+            ws.w = off - noff;
+            ws.off = noff;
+          }
         }
       }
-      int top = best;
-      for (int o = 32; o >= 1; o >>= 1) top = max(top, __shfl_xor(top, o, kWave));
-      if (top < 0) top = 0;  // unreachable: fetching every candidate certifies
-      if (lane == top / PER) {
-        const int q = top % PER;
-        uint32_t c = sc;
-        unsigned long long fb = ws.ab + sb, fv = ws.av + sv;
-        for (int q2 = PER - 1; q2 > q; --q2) {
-          const WalkBin &x = lds.c.bin[lane * PER + q2];
-          c += x.cnt;
-          fb += x.bsum;
-          fv += x.vsum;
-        }
-        uint32_t mb = mlow;
-        for (int q2 = 0; q2 < q; ++q2) mb = max(mb, lds.c.bin[lane * PER + q2].bmax);
-        const WalkBin &x = lds.c.bin[top];
-        if (x.cnt <= 1u || off == 0) {
-          const double e = eps_of((double)(tot_b - fb - x.bsum) * sbs,
-                                  (double)(tot_v - fv - x.vsum) * svs,
-                                  (double)__uint_as_float(mb), rs.dnorm, a, l);
-          ws.kstar = (int)(ws.ac + c + x.cnt);
-          ws.eps1 = (float)e;
-          ws.pre = (pre << w) | (unsigned long long)top;  // the last key's digits
-          ws.done = 1;
-        } else {
-          ws.ac += c;
-          ws.ab = fb;
-          ws.av = fv;
-          ws.bmax = mb;
-          ws.pre = (pre << w) | (unsigned long long)top;
-          const int noff = max(0, off - 8);
-          ws.w = off - noff;
-          ws.off = noff;
-        }
-      }
+      __syncthreads();
+      if (ws.done) break;
+    }
+    // the last fetched key: the one candidate whose bits above `off` are pre
+    {
+      const int off = ws.off;
+      const unsigned long long pre = ws.pre;
+      for (int k = threadIdx.x; k < nc; k += kPlanThreads)
+        if ((lds.c.key[k] >> off) == pre) ws.T = lds.c.key[k];
     }
     __syncthreads();
-    if (ws.done) break;
-  }
-  // the last fetched key: the one candidate whose bits above `off` are pre
-  {
-    const int off = ws.off;
-    const unsigned long long pre = ws.pre;
-    for (int k = threadIdx.x; k < nc; k += kPlanThreads)
-      if ((lds.c.key[k] >> off) == pre) ws.T = lds.c.key[k];
-  }
-  __syncthreads();
-  const unsigned long long T = ws.T;
-  if (T < s_lomax) {
+    const unsigned long long T = ws.T;
     // a candidate workgroup may hold keys in [T, its bound) that it did not
-    // write: the candidates cannot decide this row
-    __syncthreads();
-    select_row(p, row, bg, rs, lds.sel);
-    __syncthreads();
-    if (threadIdx.x == 0) p.rows[row] = rs;
+    // write: then this tier cannot decide the row
+    if (T < s_lomax) {
+      __syncthreads();
+      continue;
+    }
+    // mark F_h; eps^(L') from float64 sums over the rest (the candidates
+    // below T and the tokens not written), added directly rather than as the
+    // total minus the fetched part
+    const uint32_t *rbits = p.resbits + (size_t)bg * p.nwords;
+    uint32_t *fbm = p.fbits + (size_t)bg * p.nwords;
+    uint32_t *hb = p.hbits + (size_t)row * p.nwords;
+    double dr[2] = {0.0, 0.0};
+    uint32_t bm = 0u;
+    for (int k = threadIdx.x; k < nc; k += kPlanThreads) {
+      const unsigned long long key = lds.c.key[k];
+      if (key < T) {
+        const Terms t = token_terms_w(lds.c.w[k], lds.c.r[k], betaf, est);
+        double bd, vd;
+        direct_terms(t, bd, vd);
+        dr[0] += bd;
+        dr[1] += vd;
+        bm = max(bm, __float_as_uint(t.rb));
+        continue;
+      }
+      const int pos = (int)(0xFFFFFFu - (uint32_t)(key & 0xFFFFFFull));
+      atomicOr(hb + pos / 32, 1u << (pos % 32));
+      if (!((rbits[pos / 32] >> (pos % 32)) & 1u)) atomicOr(fbm + pos / 32, 1u << (pos % 32));
+    }
+    plan_reduce<double, 2>(dr);
+    bm = plan_max<uint32_t>(max(bm, below));
+    if (threadIdx.x == 0) {
+      rs.kstar = ws.kstar;
+      rs.T = T;
+      rs.eps1 = (float)eps_of(dr[0] + s_dsum[0], dr[1] + s_dsum[1],
+                              (double)__uint_as_float(bm), rs.dnorm, a, l);
+      p.rows[row] = rs;
+    }
     return;
   }
-  const uint32_t *rbits = p.resbits + (size_t)bg * p.nwords;
-  uint32_t *fbm = p.fbits + (size_t)bg * p.nwords;
-  uint32_t *hb = p.hbits + (size_t)row * p.nwords;
-  for (int k = threadIdx.x; k < nc; k += kPlanThreads) {
-    const unsigned long long key = lds.c.key[k];
-    if (key < T) continue;
-    const int pos = (int)(0xFFFFFFu - (uint32_t)(key & 0xFFFFFFull));
-    atomicOr(hb + pos / 32, 1u << (pos % 32));
-    if (!((rbits[pos / 32] >> (pos % 32)) & 1u)) atomicOr(fbm + pos / 32, 1u << (pos % 32));
-  }
-  if (threadIdx.x == 0) {
-    rs.kstar = ws.kstar;
-    rs.T = T;
-    rs.eps1 = ws.eps1;
-    p.rows[row] = rs;
-  }
+  // neither tier decides the row: the streaming selection
+  __syncthreads();
+  const SelArgs sa{p.r, p.shat, p.resbits, p.fbits, p.hbits, p.a_delta,
+                   p.l_delta, p.eps, p.n, p.nwords, p.est};
+  select_row(sa, row, bg, rs, lds.sel);
+  __syncthreads();
+  if (threadIdx.x == 0) p.rows[row] = rs;
 }
 
 // ------------------------------------------------------------ fetch
@@ -2321,7 +2493,7 @@ hipError_t run(const DParams &p, hipStream_t s, int sd, void **events) {
 
 const char *const kPhaseNames[] = {
     "scan",  "resident", "beta1",   "beta2",   "beta3", "beta4",
-    "cert",  "cand",     "walk",    "fetch", "attn"};
+    "beta5", "cert",     "cand",    "walk",    "fetch", "attn"};
 
 }  // namespace
 
@@ -2371,14 +2543,14 @@ DecodeLayout decode_layout(const vkv_decode_args &a) {
   L.bstate = c.take<BetaState>(2 * rows);
   L.rbeta = c.take<double>(2 * rows);
   L.cpart = c.take<CertPart>(rows * L.nrc);
-  L.ccount = c.take<uint32_t>(rows * kSelWG);
-  L.clo = c.take<unsigned long long>(rows * kSelWG);
+  L.ccount = c.take<uint32_t>(rows * kSelWG * 2);
+  L.clo = c.take<unsigned long long>(rows * kSelWG * 2);
   L.tpart = c.take<unsigned long long>(rows * kSelWG * 2);
   L.candk = c.take<unsigned long long>(rows * (size_t)kCandMax);
-  L.candb = c.take<unsigned long long>(rows * (size_t)kCandMax);
-  L.candv = c.take<unsigned long long>(rows * (size_t)kCandMax);
-  L.candr = c.take<uint32_t>(rows * (size_t)kCandMax);
-  L.rpart = c.take<uint32_t>(rows * kSelWG);
+  L.candw = c.take<float>(rows * (size_t)kCandMax);
+  L.candq = c.take<float>(rows * (size_t)kCandMax);
+  L.dpart = c.take<double>(rows * (size_t)kSelWG * 4);
+  L.rpart = c.take<uint32_t>(rows * kSelWG * 2);
   L.apart = c.take<float2>(rows * (L.ncr + L.ncf));
   L.aparto = c.take<float>(rows * kHeadDim * (size_t)L.npad);
   L.total = (c.off + 255) & ~size_t(255);
@@ -2426,9 +2598,9 @@ hipError_t launch_decode(const vkv_decode_args &a, const DecodeLayout &L,
   p.clo = at<unsigned long long>(w, L.clo);
   p.tpart = at<unsigned long long>(w, L.tpart);
   p.candk = at<unsigned long long>(w, L.candk);
-  p.candb = at<unsigned long long>(w, L.candb);
-  p.candv = at<unsigned long long>(w, L.candv);
-  p.candr = at<uint32_t>(w, L.candr);
+  p.candw = at<float>(w, L.candw);
+  p.candq = at<float>(w, L.candq);
+  p.dpart = at<double>(w, L.dpart);
   p.rpart = at<uint32_t>(w, L.rpart);
   p.nrc = L.nrc;
   p.apart = at<float2>(w, L.apart);

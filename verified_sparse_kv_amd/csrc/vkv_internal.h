@@ -57,7 +57,7 @@ struct DecodeLayout {
   size_t shat, ell, hpart, resbits, fbits, hbits, pmax, p0part, hres, rows,
       bpart,
       bstate,
-      rbeta, cpart, ccount, clo, tpart, candk, candb, candv, candr,
+      rbeta, cpart, ccount, clo, tpart, candk, candw, candq, dpart,
       rpart, apart, aparto, total;
 };
 

@@ -177,6 +177,12 @@ def c3_shift_queries(w, resident_masks, r, step=0):
     return bf16_bits(z)
 
 
+def resident_cap(budget):
+    """Resident-row capacity for a budget: the budget plus eight standard
+    deviations of a Poisson sample's size, plus 64."""
+    return int(budget + 8 * math.sqrt(budget) + 64)
+
+
 def make_c5_tau(seed=0, layers=None, G=None, n=None):
     """Beta(0.5, 5) scores for the compression pass: [layers][G][n] f32."""
     L = C5["layers"] if layers is None else layers
