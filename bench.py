@@ -52,10 +52,10 @@ def algorithmic_bytes(w, counts, fetching_rows, host_bytes):
     Step: sketch + r for every (request, KV head, token), the resident K and V
     rows with their positions, and q in / out (17 + 129 eta bytes per q-head
     x token at s = 32, d = 128, 4 query heads per KV head).
-    Per kernel: the sketch scan reads the sketch and r and writes the fp32
-    sketch logit of every (query head, token); the resident-logit kernel
-    reads the resident K rows and positions and writes one logit per
-    (query head, row); every planning pass over the tokens (beta passes,
+    Per kernel: the first launch scans the sketch (reads the sketch and r,
+    writes the fp32 sketch logit of every (query head, token)) and, in the
+    same launch, forms the resident logits (reads the resident K rows and
+    positions, writes one logit per (query head, row)); every planning pass over the tokens (beta passes,
     certificate, candidate keys) reads the sketch logits of its rows and r of
     their KV heads (the candidate pass only for the rows that fetch). The gather is bound by the host link and
     reported separately (it runs in one launch with the attention over the
@@ -69,8 +69,8 @@ def algorithmic_bytes(w, counts, fetching_rows, host_bytes):
     rows = int(counts.sum())
     tok = B * Hq * n * 4 + B * G * n * 4
     ftok = fetching_rows * n * 4 + min(fetching_rows, B * G) * n * 4
-    per = {"scan": B * G * n * (2 * s + 4) + B * Hq * n * 4,
-           "resident": rows * (2 * d + 4) + rows * grp * 4,
+    per = {"scan": B * G * n * (2 * s + 4) + B * Hq * n * 4
+           + rows * (2 * d + 4) + rows * grp * 4,
            "beta1": tok, "cert": tok, "cand": ftok}
     return dict(step=B * G * n * (2 * s + 4) + rows * (4 * d + 4)
                 + B * Hq * d * (2 + 4), kernels=per)

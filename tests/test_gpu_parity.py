@@ -235,6 +235,16 @@ def test_decode_bad_resident_list_reported():
     assert gpu["bits"] & vk.STATUS_BAD_RESIDENT
 
 
+def test_decode_bad_r_reported():
+    w = gc.build_case("c1")
+    dev = gc.device_inputs(w)
+    dev["r"][0, 0, 700] = 0.0  # outside (0, 1]
+    gc.say("decode with r = 0 at one token")
+    gpu = gc.run_library(w, dev, 0.1, w["delta"])
+    assert gpu["rc"] == vk.VKV_EDATA
+    assert gpu["bits"] & vk.STATUS_BAD_R
+
+
 def test_decode_deterministic():
     w = gc.build_case("c2", n=4000, G=2)
     dev = gc.device_inputs(w)

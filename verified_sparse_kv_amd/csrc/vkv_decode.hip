@@ -42,6 +42,9 @@ namespace vkv {
 namespace {
 
 constexpr int kChunk = 512;      // tokens per workgroup in token passes
+constexpr int kMaxTokens = 1 << 17;  // context length the decode kernels take
+constexpr int kRowChunk = 2048;  // tokens per workgroup in row passes
+constexpr int kRowTok = kRowChunk / kBlock;
 constexpr int kCand = 2048;      // candidates per round of the streaming selection
 constexpr float kInvSqrtD = 0.08838834764831845f;  // 1/sqrt(128)
 
@@ -92,8 +95,9 @@ struct DParams {
   double *row_stats;
   uint32_t *status;
   float *shat, *ell;
-  uint32_t *resbits, *fbits;
+  uint32_t *fbits;
   uint32_t *hbits;   // [row][nwords] F_h of each row
+  uint32_t *fstat;   // [B][G][nch + ncr] input-check bits of the front launch
   float *pmax;       // [row][nch + ncr] shift of each scan chunk / resident part
   double *p0part;    // [row][nch + ncr][4] pass-0 sums of each scan chunk
   double *hres;      // [row][ncr] sum over H of exp(l - shift) per part
@@ -450,10 +454,10 @@ __device__ __forceinline__ void scan_finish(const DParams &p, int b, int g,
 }
 
 template <int GRP, int SD>
-__global__ __launch_bounds__(kBlock) void dk_scan(DParams p) {
+__device__ __forceinline__ void scan_body(const DParams &p, int c, int g,
+                                          int b) {
   constexpr int LPT = SD / 8;           // lanes per token (16 bytes each)
   constexpr int TPI = kBlock / LPT;     // tokens per block iteration
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int bg = b * p.G + g;
   const int lane = threadIdx.x % kWave;
   __shared__ float s_qp[GRP][SD];
@@ -498,7 +502,6 @@ __global__ __launch_bounds__(kBlock) void dk_scan(DParams p) {
     const int w0 = c * p.chunk / 32, nw = p.chunk / 32;
     for (int w = threadIdx.x; w < nw; w += kBlock) {
       if (w0 + w < p.nwords) {
-        p.resbits[(size_t)bg * p.nwords + w0 + w] = 0u;
         p.fbits[(size_t)bg * p.nwords + w0 + w] = 0u;
         for (int h = 0; h < GRP; ++h)
           p.hbits[(size_t)row_of(p, b, g, h, GRP) * p.nwords + w0 + w] = 0u;
@@ -572,8 +575,11 @@ __global__ __launch_bounds__(kBlock) void dk_scan(DParams p) {
       }
     }
   }
-  if (bad) atomicOr(p.status, VKV_STATUS_BAD_R);
   const int np = p.nch + p.ncr;
+  {
+    const int any = __syncthreads_or((int)bad);
+    if (threadIdx.x == 0) p.fstat[(size_t)bg * np + c] = any ? VKV_STATUS_BAD_R : 0u;
+  }
   scan_finish<GRP>(p, b, g, c, lim - base, mx, s_dot, s_r);
   const uint32_t th = block_sum<uint32_t>(n_h, s_ured);
   if (threadIdx.x == 0) p.hpart[(size_t)bg * np + c] = th;
@@ -581,8 +587,8 @@ __global__ __launch_bounds__(kBlock) void dk_scan(DParams p) {
 
 // Same outputs with exact keys read from the host cache (perfect sketch).
 template <int GRP>
-__global__ __launch_bounds__(kBlock) void dk_scan_exact(DParams p) {
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+__device__ __forceinline__ void scan_exact_body(const DParams &p, int c,
+                                                int g, int b) {
   const int bg = b * p.G + g;
   const int lane = threadIdx.x % kWave;
   __shared__ uint32_t s_ured[kBlock / kWave];
@@ -605,7 +611,6 @@ __global__ __launch_bounds__(kBlock) void dk_scan_exact(DParams p) {
     const int w0 = c * p.chunk / 32, nw = p.chunk / 32;
     for (int w = threadIdx.x; w < nw; w += kBlock) {
       if (w0 + w < p.nwords) {
-        p.resbits[(size_t)bg * p.nwords + w0 + w] = 0u;
         p.fbits[(size_t)bg * p.nwords + w0 + w] = 0u;
         for (int h = 0; h < GRP; ++h)
           p.hbits[(size_t)row_of(p, b, g, h, GRP) * p.nwords + w0 + w] = 0u;
@@ -663,7 +668,11 @@ __global__ __launch_bounds__(kBlock) void dk_scan_exact(DParams p) {
       }
     }
   }
-  if (bad) atomicOr(p.status, VKV_STATUS_BAD_R);
+  {
+    const int any = __syncthreads_or((int)bad);
+    if (threadIdx.x == 0)
+      p.fstat[(size_t)bg * (p.nch + p.ncr) + c] = any ? VKV_STATUS_BAD_R : 0u;
+  }
   scan_finish<GRP>(p, b, g, c, lim - base, mx, s_dot, s_r);
   const uint32_t th = block_sum<uint32_t>(n_h, s_ured);
   if (threadIdx.x == 0) p.hpart[(size_t)bg * (p.nch + p.ncr) + c] = th;
@@ -672,8 +681,8 @@ __global__ __launch_bounds__(kBlock) void dk_scan_exact(DParams p) {
 // ------------------------------------------------------------ dk_resident
 // The group's resident rows are split evenly over gridDim.x workgroups.
 template <int GRP>
-__global__ __launch_bounds__(kBlock) void dk_resident(DParams p) {
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+__device__ __forceinline__ void resident_body(const DParams &p, int c, int g,
+                                              int b) {
   const int bg = b * p.G + g;
   const int lane = threadIdx.x % kWave;
   const int u = lane % 16;
@@ -701,7 +710,7 @@ __global__ __launch_bounds__(kBlock) void dk_resident(DParams p) {
   }
   uint32_t n_h = 0;
   int lo, hi;
-  split_range(cnt, gridDim.x, c, lo, hi);
+  split_range(cnt, p.ncr, c, lo, hi);
   for (int j0 = lo; j0 < hi; j0 += kBlock / 16) {
     const int j = j0 + threadIdx.x / 16;
     if (j < hi) {
@@ -731,8 +740,6 @@ __global__ __launch_bounds__(kBlock) void dk_resident(DParams p) {
       }
       if (u == 0) {
         if (ok) {
-          atomicOr(p.resbits + (size_t)bg * p.nwords + pos / 32,
-                   1u << (pos % 32));
           if (in_h) ++n_h;
         } else {
           bad = true;
@@ -740,8 +747,12 @@ __global__ __launch_bounds__(kBlock) void dk_resident(DParams p) {
       }
     }
   }
-  if (bad) atomicOr(p.status, VKV_STATUS_BAD_RESIDENT);
   const int np = p.nch + p.ncr;
+  {
+    const int any = __syncthreads_or((int)bad);
+    if (threadIdx.x == 0)
+      p.fstat[(size_t)bg * np + p.nch + c] = any ? VKV_STATUS_BAD_RESIDENT : 0u;
+  }
   blk_combine<float, GRP, kBlock, OpMax<float>>(mx);
 #pragma unroll
   for (int h = 0; h < GRP; ++h)
@@ -757,6 +768,26 @@ __global__ __launch_bounds__(kBlock) void dk_resident(DParams p) {
   }
   const uint32_t th = block_sum<uint32_t>(n_h, s_ured);
   if (threadIdx.x == 0) p.hpart[(size_t)bg * np + p.nch + c] = th;
+}
+
+// ------------------------------------------------------------ front launch
+// Sketch scan (blockIdx.x < nch) and resident logits (the rest) in one
+// launch: they read disjoint inputs and write disjoint outputs.
+template <int GRP, int SD>
+__global__ __launch_bounds__(kBlock) void dk_front(DParams p) {
+  const int x = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  if (x < p.nch)
+    scan_body<GRP, SD>(p, x, g, b);
+  else
+    resident_body<GRP>(p, x - p.nch, g, b);
+}
+template <int GRP>
+__global__ __launch_bounds__(kBlock) void dk_front_exact(DParams p) {
+  const int x = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  if (x < p.nch)
+    scan_exact_body<GRP>(p, x, g, b);
+  else
+    resident_body<GRP>(p, x - p.nch, g, b);
 }
 
 // ------------------------------------------------------------ planning
@@ -797,8 +828,6 @@ __global__ __launch_bounds__(kBlock) void dk_resident(DParams p) {
 // exactly; the reported eps^(L') is formed from float64 sums over the rest
 // itself, which keep their relative accuracy however small the rest is.
 constexpr int kSelUnroll = 4;       // streamed tokens per thread in flight
-constexpr int kRowChunk = 2048;     // tokens per workgroup in row passes
-constexpr int kRowTok = kRowChunk / kBlock;
 constexpr int kBetaPts = 4;         // points of h per Newton pass
 constexpr int kBetaRec = 3 * kBetaPts;
 constexpr int kBetaLaunches = 5;    // Newton passes (pass 0 is in the scan)
@@ -832,7 +861,7 @@ union SelLds {
 // of it to scratch memory.
 struct SelArgs {
   const float *r, *shat;
-  const uint32_t *resbits;
+  const uint32_t *resbits;  // the KV head's resident bitmap (in LDS)
   uint32_t *fbits, *hbits;
   double a_delta, l_delta;
   float eps;
@@ -859,7 +888,7 @@ __device__ __attribute__((noinline)) void select_row(const SelArgs p, int row,
   const int eb = rs.eb, ev = rs.ev;
   const double capb = rs.capb, capv = rs.capv;
   const double sbs = ldexp(1.0, -eb), svs = ldexp(1.0, -ev);
-  const uint32_t *rbits = p.resbits + (size_t)bg * p.nwords;
+  const uint32_t *rbits = p.resbits;
   uint32_t *fb = p.fbits + (size_t)bg * p.nwords;
   uint32_t *hb = p.hbits + (size_t)row * p.nwords;
 
@@ -1326,11 +1355,21 @@ __device__ __forceinline__ float row_pass0(const DParams &p, int row, int bg,
   if (c == 0) {
     if (threadIdx.x == 0) p.rows[row].m = m;
     if (check) {
-      uint32_t hc[2] = {0u, 0u};  // tokens with r == 1: all, resident
-      for (int t = threadIdx.x; t < np; t += kBlock)
+      // the front launch's input checks (its workgroups cannot touch the
+      // status word, which that launch clears), and the H counts: tokens
+      // with r == 1, all of them and the resident ones
+      uint32_t hc[2] = {0u, 0u};
+      uint32_t fs = 0u;
+      for (int t = threadIdx.x; t < np; t += kBlock) {
         hc[t < p.nch ? 0 : 1] += p.hpart[(size_t)bg * np + t];
+        fs |= p.fstat[(size_t)bg * np + t];
+      }
       blk_reduce<uint32_t, 2, kBlock>(hc);
-      if (threadIdx.x == 0 && hc[0] != hc[1]) atomicOr(p.status, VKV_STATUS_BAD_RESIDENT);
+      uint32_t bits = 0u;
+      if (__syncthreads_or((int)(fs & VKV_STATUS_BAD_R))) bits |= VKV_STATUS_BAD_R;
+      if (__syncthreads_or((int)(fs & VKV_STATUS_BAD_RESIDENT)) || hc[0] != hc[1])
+        bits |= VKV_STATUS_BAD_RESIDENT;
+      if (threadIdx.x == 0 && bits) atomicOr(p.status, bits);
     }
   }
   return m;
@@ -1794,6 +1833,10 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rwalk(DParams p) {
   __shared__ uint32_t s_pc[2][kSelWG], s_pb[2][kSelWG];
   __shared__ unsigned long long s_plo[2][kSelWG], s_pt[2][kSelWG];
   __shared__ double s_pd[4][kSelWG];
+  // the KV head's resident positions as a bitmap (for F_h minus S), built
+  // while the candidates are loaded
+  __shared__ uint32_t s_res[kMaxTokens / 32];
+  for (int i = threadIdx.x; i < p.nwords; i += kPlanThreads) s_res[i] = 0u;
   if (threadIdx.x < kSelWG) {
     const int j = threadIdx.x;
     const size_t at = (size_t)row * kSelWG + j;
@@ -1809,6 +1852,14 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rwalk(DParams p) {
   }
   __syncthreads();
   if (!rs.fetch) return;
+  {
+    const int cnt = max(0, min(p.rcount[bg], p.cap));
+    const int32_t *ridx = p.ridx + (size_t)bg * p.cap;
+    for (int j = threadIdx.x; j < cnt; j += kPlanThreads) {
+      const int pos = ridx[j];
+      if (pos >= 0 && pos < p.n) atomicOr(&s_res[pos / 32], 1u << (pos % 32));
+    }
+  }
   const double a = p.a_delta, l = p.l_delta;
   const int eb = rs.eb, ev = rs.ev;
   const double capb = rs.capb, capv = rs.capv;
@@ -2025,7 +2076,7 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rwalk(DParams p) {
     // mark F_h; eps^(L') from float64 sums over the rest (the candidates
     // below T and the tokens not written), added directly rather than as the
     // total minus the fetched part
-    const uint32_t *rbits = p.resbits + (size_t)bg * p.nwords;
+    const uint32_t *rbits = s_res;
     uint32_t *fbm = p.fbits + (size_t)bg * p.nwords;
     uint32_t *hb = p.hbits + (size_t)row * p.nwords;
     double dr[2] = {0.0, 0.0};
@@ -2058,7 +2109,7 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rwalk(DParams p) {
   }
   // neither tier decides the row: the streaming selection
   __syncthreads();
-  const SelArgs sa{p.r, p.shat, p.resbits, p.fbits, p.hbits, p.a_delta,
+  const SelArgs sa{p.r, p.shat, s_res, p.fbits, p.hbits, p.a_delta,
                    p.l_delta, p.eps, p.n, p.nwords, p.est};
   select_row(sa, row, bg, rs, lds.sel);
   __syncthreads();
@@ -2458,19 +2509,16 @@ struct PhaseMark {
 template <int GRP>
 hipError_t run(const DParams &p, hipStream_t s, int sd, void **events) {
   const dim3 blk(kBlock);
-  const dim3 gch((unsigned)p.nch, (unsigned)p.G, (unsigned)p.B);
-  const dim3 gres((unsigned)p.ncr, (unsigned)p.G, (unsigned)p.B);
+  const dim3 gfront((unsigned)(p.nch + p.ncr), (unsigned)p.G, (unsigned)p.B);
   const PhaseMark mark{events, s};
   int k = 0;
   mark(k++);
   if (p.weights == VKV_W_PERFECT)
-    dk_scan_exact<GRP><<<gch, blk, 0, s>>>(p);
+    dk_front_exact<GRP><<<gfront, blk, 0, s>>>(p);
   else if (sd == 32)
-    dk_scan<GRP, 32><<<gch, blk, 0, s>>>(p);
+    dk_front<GRP, 32><<<gfront, blk, 0, s>>>(p);
   else
-    dk_scan<GRP, 16><<<gch, blk, 0, s>>>(p);
-  mark(k++);
-  dk_resident<GRP><<<gres, blk, 0, s>>>(p);
+    dk_front<GRP, 16><<<gfront, blk, 0, s>>>(p);
   mark(k++);
   const dim3 grow((unsigned)p.nrc, (unsigned)p.Hq, (unsigned)p.B);
   const dim3 gone((unsigned)p.Hq, (unsigned)p.B);
@@ -2492,8 +2540,8 @@ hipError_t run(const DParams &p, hipStream_t s, int sd, void **events) {
 }
 
 const char *const kPhaseNames[] = {
-    "scan",  "resident", "beta1",   "beta2",   "beta3", "beta4",
-    "beta5", "cert",     "cand",    "walk",    "fetch", "attn"};
+    "scan", "beta1", "beta2", "beta3", "beta4", "beta5",
+    "cert", "cand",  "walk",  "fetch", "attn"};
 
 }  // namespace
 
@@ -2524,6 +2572,7 @@ DecodeLayout decode_layout(const vkv_decode_args &a) {
   L.ncf = kGatherWG;
   L.npad = (L.ncr + L.ncf + 3) / 4 * 4;
   L.nwords = (a.n_tokens + 31) / 32;
+  L.nrc = (a.n_tokens + kRowChunk - 1) / kRowChunk;
   const size_t B = (size_t)a.batch, Hq = (size_t)a.n_q_heads,
                G = (size_t)a.n_kv_heads, n = (size_t)a.n_tokens;
   const size_t rows = B * Hq, groups = B * G;
@@ -2531,14 +2580,13 @@ DecodeLayout decode_layout(const vkv_decode_args &a) {
   L.rows = c.take<RowState>(rows);
   L.shat = c.take<float>(rows * n);
   L.ell = c.take<float>(rows * (size_t)a.cap);
-  L.resbits = c.take<uint32_t>(groups * L.nwords);
+  L.fstat = c.take<uint32_t>(groups * (L.nch + L.ncr));
   L.fbits = c.take<uint32_t>(groups * L.nwords);
   L.hbits = c.take<uint32_t>(rows * L.nwords);
   L.pmax = c.take<float>(rows * (L.nch + L.ncr));
   L.p0part = c.take<double>(rows * (L.nch + L.ncr) * 4);
   L.hres = c.take<double>(rows * L.ncr);
   L.hpart = c.take<uint32_t>(groups * (L.nch + L.ncr));  // H counts per chunk
-  L.nrc = (a.n_tokens + kRowChunk - 1) / kRowChunk;
   L.bpart = c.take<double>(2 * rows * L.nrc * (size_t)kBetaRec);
   L.bstate = c.take<BetaState>(2 * rows);
   L.rbeta = c.take<double>(2 * rows);
@@ -2583,7 +2631,7 @@ hipError_t launch_decode(const vkv_decode_args &a, const DecodeLayout &L,
   p.rows = at<RowState>(w, L.rows);
   p.shat = at<float>(w, L.shat);
   p.ell = at<float>(w, L.ell);
-  p.resbits = at<uint32_t>(w, L.resbits);
+  p.fstat = at<uint32_t>(w, L.fstat);
   p.fbits = at<uint32_t>(w, L.fbits);
   p.hbits = at<uint32_t>(w, L.hbits);
   p.pmax = at<float>(w, L.pmax);
