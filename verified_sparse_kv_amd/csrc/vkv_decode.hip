@@ -104,6 +104,7 @@ struct DParams {
   uint32_t *hpart;
   RowState *rows;
   double *bpart;     // [2][row][nrc][kBetaRec] beta pass records
+  float2 *band;      // [2][row][nrc][kBandChunk] (w~, rho) of band tokens
   BetaState *bstate; // [2][row]
   double *rbeta;     // [row][2] beta*, D~
   CertPart *cpart;   // [row][nrc]
@@ -829,8 +830,11 @@ __global__ __launch_bounds__(kBlock) void dk_front_exact(DParams p) {
 // itself, which keep their relative accuracy however small the rest is.
 constexpr int kSelUnroll = 4;       // streamed tokens per thread in flight
 constexpr int kBetaPts = 4;         // points of h per Newton pass
-constexpr int kBetaRec = 3 * kBetaPts;
-constexpr int kBetaLaunches = 5;    // Newton passes (pass 0 is in the scan)
+constexpr int kBetaRec = 3 * kBetaPts + 1;  // + the band count
+constexpr int kBetaLaunches = 2;    // Newton passes (pass 0 is in the scan)
+constexpr int kBandChunk = 512;     // band tokens a chunk may store
+constexpr int kBandMax = 1024;      // band tokens a row may be settled from
+constexpr int kMaxChunks = kMaxTokens / kRowChunk;
 constexpr int kBetaPassMax = 96;    // never reached: the bracket shrinks >= 2x
 constexpr int kCandMax = 8192;      // candidates held by the walk
 constexpr int kSelDigit = 11;
@@ -1375,6 +1379,109 @@ __device__ __forceinline__ float row_pass0(const DParams &p, int row, int bg,
   return m;
 }
 
+// The band of a bracket [lo, hi]: the tokens active at lo and not at hi,
+// the only ones whose share of h can change inside it. Each pass stores its
+// chunk's band (when it fits) in token order and counts it in the record.
+__device__ __forceinline__ bool in_band(const BetaState &st, float wt, float ri) {
+  if (!(wt > 0.0f)) return false;
+  const double w = (double)wt, rh = (double)plan_rho(ri);
+  return w - st.lo * rh > 0.0 && !(w - st.hi * rh > 0.0);
+}
+__device__ __forceinline__ uint32_t band_collect(const BetaState &st,
+                                                 const float (&w8)[kRowTok],
+                                                 const float (&r8)[kRowTok],
+                                                 float2 *dst) {
+  __shared__ uint32_t s_bs[kBlock / kWave + 1];
+  uint32_t mine = 0u;
+#pragma unroll
+  for (int u = 0; u < kRowTok; ++u) mine += in_band(st, w8[u], r8[u]) ? 1u : 0u;
+  uint32_t total;
+  uint32_t k = block_exclusive_scan<uint32_t>(mine, s_bs, &total);
+  if (total <= (uint32_t)kBandChunk) {
+#pragma unroll
+    for (int u = 0; u < kRowTok; ++u)
+      if (in_band(st, w8[u], r8[u])) dst[k++] = make_float2(w8[u], plan_rho(r8[u]));
+  }
+  return total;
+}
+
+// The state after a pass whose combined records are v: one bracketed Newton
+// step; then, when the pass's band was small enough to keep, the iteration
+// goes on over the band alone in LDS (the tokens outside it have the same
+// status at every point of the new, narrower bracket: their sums are those
+// at lo minus the band's), to the root. Every workgroup of the row gets the
+// same state (same data, same order).
+__device__ __forceinline__ BetaState beta_settle(const DParams &p, BetaState st,
+                                                 const double (&v)[kBetaRec],
+                                                 int row, int parity) {
+  __shared__ float s_bw[kBandMax], s_br[kBandMax];
+  __shared__ int s_bo[kMaxChunks + 1];
+  __shared__ int s_bok;
+  st = beta_advance(st, v);
+  if (st.done || !(v[kBetaRec - 1] <= (double)kBandMax)) return st;
+  const size_t rows = (size_t)p.B * p.Hq;
+  const double *rec = p.bpart + ((size_t)parity * rows + row) * p.nrc * kBetaRec;
+  const float2 *band = p.band + ((size_t)parity * rows + row) * p.nrc * kBandChunk;
+  if (threadIdx.x < kWave) {  // one wave: nrc <= 64 chunk counts
+    const int t = threadIdx.x;
+    const int k = t < p.nrc ? (int)rec[(size_t)t * kBetaRec + kBetaRec - 1] : 0;
+    const int incl = wave_incl_scan<int>(k, t);
+    // a chunk over its capacity stored nothing
+    const int bad = wave_max<int>(k > kBandChunk ? 1 : 0);
+    if (t < p.nrc) s_bo[t] = incl - k;
+    if (t == kWave - 1) {
+      s_bo[p.nrc] = incl;
+      s_bok = !bad;
+    }
+  }
+  __syncthreads();
+  if (!s_bok) return st;
+  const int nb = s_bo[p.nrc];
+  double bs[3] = {0.0, 0.0, 0.0};  // the band's sums of w~ and rho, its size
+  for (int k = threadIdx.x; k < nb; k += kBlock) {
+    int lo = 0, hi = p.nrc;  // the chunk holding entry k
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) / 2;
+      if (s_bo[mid] <= k) lo = mid; else hi = mid;
+    }
+    const float2 e = band[(size_t)lo * kBandChunk + (k - s_bo[lo])];
+    s_bw[k] = e.x;
+    s_br[k] = e.y;
+    bs[0] += (double)e.x;
+    bs[1] += (double)e.y;
+    bs[2] += 1.0;
+  }
+  blk_reduce<double, 3, kBlock>(bs);
+  // the tokens active at every point of the bracket (v holds the sums at lo)
+  const double aw = v[0] - bs[0], ar = v[1] - bs[1], ac = v[2] - bs[2];
+  for (int it = 0; it < kBetaPassMax && !st.done; ++it) {
+    double pts[kBetaPts], u[kBetaRec];
+    beta_points(st, pts);
+#pragma unroll
+    for (int k = 0; k < kBetaRec; ++k) u[k] = 0.0;
+    for (int k = threadIdx.x; k < nb; k += kBlock) {
+      const double w = (double)s_bw[k], rh = (double)s_br[k];
+#pragma unroll
+      for (int j = 0; j < kBetaPts; ++j) {
+        if (w - pts[j] * rh > 0.0) {
+          u[3 * j] += w;
+          u[3 * j + 1] += rh;
+          u[3 * j + 2] += 1.0;
+        }
+      }
+    }
+    blk_reduce<double, kBetaRec, kBlock>(u);
+#pragma unroll
+    for (int j = 0; j < kBetaPts; ++j) {
+      u[3 * j] += aw;
+      u[3 * j + 1] += ar;
+      u[3 * j + 2] += ac;
+    }
+    st = beta_advance(st, u);
+  }
+  return st;
+}
+
 // Newton pass `pass` (>= 1) of the beta* iteration; pass 1 starts from the
 // pass-0 sums that the scan and resident-logit kernels left per chunk and
 // part. Grid (chunks, Hq, B).
@@ -1412,7 +1519,7 @@ __global__ __launch_bounds__(kBlock) void dk_rbeta(DParams p, int pass) {
   double *out = p.bpart + (((size_t)(pass & 1) * rows + row) * p.nrc + c) * kBetaRec;
   if (pass >= 2 && !st.done) {
     beta_rec_total<false>(rv);
-    st = beta_advance(st, rv);
+    st = beta_settle(p, st, rv, row, q);
   }
   if (c == 0 && threadIdx.x == 0) p.bstate[(size_t)(pass & 1) * rows + row] = st;
   if (st.done) return;
@@ -1420,10 +1527,14 @@ __global__ __launch_bounds__(kBlock) void dk_rbeta(DParams p, int pass) {
   beta_points(st, pts);
 #pragma unroll
   for (int u = 0; u < kRowTok; ++u) beta_accumulate(pts, w8[u], r8[u], v);
+  const uint32_t nband = band_collect(
+      st, w8, r8,
+      p.band + (((size_t)(pass & 1) * rows + row) * p.nrc + c) * kBandChunk);
   blk_reduce<double, kBetaRec, kBlock>(v);
   if (threadIdx.x == 0) {
 #pragma unroll
-    for (int k = 0; k < kBetaRec; ++k) out[k] = v[k];
+    for (int k = 0; k < kBetaRec - 1; ++k) out[k] = v[k];
+    out[kBetaRec - 1] = (double)nband;
   }
 }
 
@@ -1445,10 +1556,11 @@ __global__ __launch_bounds__(kBlock) void dk_rcert(DParams p) {
   row_weights(m, r8, s8, w8);
   if (!st.done) {
     beta_rec_total<false>(rv);
-    st = beta_advance(st, rv);
+    st = beta_settle(p, st, rv, row, q);
   }
   if (!st.done) {
-    // rare: more Newton passes, each over the whole row by this workgroup
+    // rare (a band too large to keep): more Newton passes, each over the
+    // whole row by this workgroup
     for (int it = 0; it < kBetaPassMax && !st.done; ++it) {
       double pts[kBetaPts], v[kBetaRec];
       beta_points(st, pts);
@@ -2540,8 +2652,7 @@ hipError_t run(const DParams &p, hipStream_t s, int sd, void **events) {
 }
 
 const char *const kPhaseNames[] = {
-    "scan", "beta1", "beta2", "beta3", "beta4", "beta5",
-    "cert", "cand",  "walk",  "fetch", "attn"};
+    "scan", "beta1", "beta2", "cert", "cand", "walk", "fetch", "attn"};
 
 }  // namespace
 
@@ -2588,6 +2699,7 @@ DecodeLayout decode_layout(const vkv_decode_args &a) {
   L.hres = c.take<double>(rows * L.ncr);
   L.hpart = c.take<uint32_t>(groups * (L.nch + L.ncr));  // H counts per chunk
   L.bpart = c.take<double>(2 * rows * L.nrc * (size_t)kBetaRec);
+  L.band = c.take<float2>(2 * rows * L.nrc * (size_t)kBandChunk);
   L.bstate = c.take<BetaState>(2 * rows);
   L.rbeta = c.take<double>(2 * rows);
   L.cpart = c.take<CertPart>(rows * L.nrc);
@@ -2639,6 +2751,7 @@ hipError_t launch_decode(const vkv_decode_args &a, const DecodeLayout &L,
   p.hres = at<double>(w, L.hres);
   p.hpart = at<uint32_t>(w, L.hpart);
   p.bpart = at<double>(w, L.bpart);
+  p.band = at<float2>(w, L.band);
   p.bstate = at<BetaState>(w, L.bstate);
   p.rbeta = at<double>(w, L.rbeta);
   p.cpart = at<CertPart>(w, L.cpart);

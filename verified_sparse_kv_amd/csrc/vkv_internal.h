@@ -55,7 +55,7 @@ hipError_t launch_compress(const vkv_compress_args &a, const CompressLayout &L,
 struct DecodeLayout {
   int grp, nch, ncr, ncf, npad, nwords, chunk, nrc;
   size_t shat, ell, hpart, fstat, fbits, hbits, pmax, p0part, hres, rows,
-      bpart,
+      bpart, band,
       bstate,
       rbeta, cpart, ccount, clo, tpart, candk, candw, candq, dpart,
       rpart, apart, aparto, total;
