@@ -31,12 +31,26 @@ __device__ __forceinline__ T shfl_xor(T v, int m) {
   return __shfl_xor(v, m, kWave);
 }
 
-// Sum over aligned groups of W lanes (W a power of two <= 64); every lane of
-// the group receives the same total, combined in a fixed order.
+// Lane exchange within rows of 16 lanes by DPP (no LDS): CTRL is a DPP
+// control (quad_perm, row_half_mirror, row_mirror).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(
+      __float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of W lanes (W in {1, 2, 4, 8, 16}); every lane of
+// the group receives the same total: pairs, then pairs of pairs (quad
+// permutes), then the two quads of each half-row (half mirror), then the
+// two halves of the row (mirror) -- each step adds two equal partial sums
+// in either order, so all lanes agree bit for bit.
 template <int W>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int m = 1; m < W; m <<= 1) v += shfl_xor(v, m);
+  static_assert(W == 1 || W == 2 || W == 4 || W == 8 || W == 16, "group");
+  if constexpr (W >= 2) v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+  if constexpr (W >= 4) v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  if constexpr (W >= 8) v += dpp_f<0x141>(v);  // row_half_mirror
+  if constexpr (W >= 16) v += dpp_f<0x140>(v); // row_mirror
   return v;
 }
 

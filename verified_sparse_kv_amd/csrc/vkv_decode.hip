@@ -271,6 +271,10 @@ template <typename T>
 struct OpMax {
   __device__ static T f(T a, T b) { return a > b ? a : b; }
 };
+template <typename T>
+struct OpMin {
+  __device__ static T f(T a, T b) { return a < b ? a : b; }
+};
 
 // DPP move of a 32- or 64-bit value (64-bit values move as two halves).
 template <int CTRL, typename T>
@@ -407,35 +411,64 @@ __device__ __forceinline__ void blk_top2(float &x1, int &p1, float &x2) {
 // beta* iteration with the chunk's own shift mL: sum_L w~, sum rho over w~ >
 // 0, their count, and max w~ (1 - r). The planning rescales them to the
 // common shift.
+// Pass-0 sums of one query head over a thread's tokens of L, with a running
+// shift: w~ = exp(s - m) against the largest logit seen so far, the sums
+// rescaled when it grows. A token counts in sum rho and |A(0)| when its w~
+// is nonzero against that shift, a superset of the tokens nonzero against
+// any larger shift, so the Newton step from 0 stays below the root.
+struct P0Acc {
+  float m, sw, sr, cnt, lb;  // shift, sum w~, sum rho, |A(0)|, max w~ (1 - r)
+};
+__device__ __forceinline__ void p0_init(P0Acc &a) {
+  a.m = -INFINITY;
+  a.sw = a.sr = a.cnt = a.lb = 0.0f;
+}
+// Raises the shift to mx (>= a.m) first, then adds the token (s, r).
+__device__ __forceinline__ void p0_shift(P0Acc &a, float mx) {
+  if (mx > a.m) {
+    const float f = expf(a.m - mx);  // 0 while a.m is -inf
+    a.sw *= f;
+    a.lb *= f;
+    a.m = mx;
+  }
+}
+__device__ __forceinline__ void p0_add(P0Acc &a, float s, float r) {
+  const float wt = expf(s - a.m);
+  a.sw += wt;
+  if (wt > 0.0f) {
+    a.sr += plan_rho(r);
+    a.cnt += 1.0f;
+    a.lb = fmaxf(a.lb, wt * (1.0f - r));
+  }
+}
+
+// The workgroup's pass-0 record of each query head (chunk c): the chunk's
+// shift (the largest logit of L) and the sums rescaled to it, combined in a
+// fixed order; and the chunk's count of tokens with r == 1.
 template <int GRP>
-__device__ __forceinline__ void scan_finish(const DParams &p, int b, int g,
-                                            int c, int cnt, float (&mx)[GRP],
-                                            float (*sd)[kChunk],
-                                            const float *sr) {
+__device__ __forceinline__ void p0_finish(const DParams &p, int b, int g,
+                                          int c, P0Acc (&acc)[GRP],
+                                          uint32_t n_h) {
   const int np = p.nch + p.ncr;
+  const int bg = b * p.G + g;
+  float mx[GRP];
+#pragma unroll
+  for (int h = 0; h < GRP; ++h) mx[h] = acc[h].m;
   blk_combine<float, GRP, kBlock, OpMax<float>>(mx);
   constexpr int HG = GRP < 4 ? GRP : 4;  // heads per reduction
+  uint32_t nh[1] = {n_h};
+  blk_reduce<uint32_t, 1, kBlock>(nh);
 #pragma unroll
   for (int h0 = 0; h0 < GRP; h0 += HG) {
     double v0[3 * HG], lbm[HG];
 #pragma unroll
-    for (int k = 0; k < 3 * HG; ++k) v0[k] = 0.0;
-#pragma unroll
-    for (int k = 0; k < HG; ++k) lbm[k] = 0.0;
-    for (int t = threadIdx.x; t < cnt; t += kBlock) {
-      const float ri = sr[t];
-      if (!(ri < 1.0f)) continue;
-      const float rho = plan_rho(ri);
-#pragma unroll
-      for (int k = 0; k < HG; ++k) {
-        const float wt = expf(sd[h0 + k][t] - mx[h0 + k]);
-        v0[3 * k] += (double)wt;
-        if (wt > 0.0f) {
-          v0[3 * k + 1] += (double)rho;
-          v0[3 * k + 2] += 1.0;
-          lbm[k] = fmax(lbm[k], (double)(wt * (1.0f - ri)));
-        }
-      }
+    for (int k = 0; k < HG; ++k) {
+      const P0Acc &a = acc[h0 + k];
+      const float f = expf(a.m - mx[h0 + k]);  // 0 for a thread without L
+      v0[3 * k] = (double)(a.sw * f);
+      v0[3 * k + 1] = (double)a.sr;
+      v0[3 * k + 2] = (double)a.cnt;
+      lbm[k] = (double)(a.lb * f);
     }
     blk_reduce<double, 3 * HG, kBlock>(v0);
     blk_combine<double, HG, kBlock, OpMax<double>>(lbm);
@@ -452,6 +485,7 @@ __device__ __forceinline__ void scan_finish(const DParams &p, int b, int g,
       }
     }
   }
+  if (threadIdx.x == 0) p.hpart[(size_t)bg * np + c] = nh[0];
 }
 
 template <int GRP, int SD>
@@ -462,24 +496,32 @@ __device__ __forceinline__ void scan_body(const DParams &p, int c, int g,
   const int bg = b * p.G + g;
   const int lane = threadIdx.x % kWave;
   __shared__ float s_qp[GRP][SD];
-  __shared__ uint32_t s_ured[kBlock / kWave];
   // the chunk's sketch rows and r first, all in flight while q is projected
   const int u = lane % LPT;
   const uint16_t *sk = p.sketch + (size_t)bg * p.n * SD;
   const float *rr = p.r + (size_t)bg * p.n;
   const int base = c * p.chunk;
   const int lim = min(base + p.chunk, p.n);
-  constexpr int UNR = kChunk / TPI;
-  uint4 raw[UNR];
-  float rv[UNR];
+  // sub-batches of SUB tokens, UNR per thread (LPT lanes per token); the
+  // next sub-batch is loaded while one is used
+  constexpr int UNR = 4;
+  constexpr int SUB = UNR * TPI;
+  static_assert(kChunk % SUB == 0, "chunk");
+  uint4 raw[UNR], nraw[UNR];
+  float rv[UNR], nrv[UNR];
+  auto load_sub = [&](int sb, uint4 (&ra)[UNR], float (&ro)[UNR]) {
 #pragma unroll
-  for (int k = 0; k < UNR; ++k) {
-    const int i = base + k * TPI + threadIdx.x / LPT;
-    if (i < lim) {
-      raw[k] = *reinterpret_cast<const uint4 *>(sk + (size_t)i * SD + u * 8);
-      rv[k] = rr[i];
+    for (int k = 0; k < UNR; ++k) {
+      const int i = sb + k * TPI + (int)threadIdx.x / LPT;
+      if (i < lim) {
+        ra[k] = *reinterpret_cast<const uint4 *>(sk + (size_t)i * SD + u * 8);
+        ro[k] = rr[i];
+      } else {
+        ro[k] = 1.0f;
+      }
     }
-  }
+  };
+  load_sub(base, raw, rv);
 
   // step-start initialisation of this group's state (no other block of
   // this launch touches it)
@@ -539,51 +581,68 @@ __device__ __forceinline__ void scan_body(const DParams &p, int c, int g,
 #pragma unroll
     for (int k = 0; k < 8; ++k) qv[h][k] = s_qp[h][u * 8 + k];
 
-  float mx[GRP];
+  // lane u of a token keeps the heads u, u + LPT, ... (NH of them)
+  constexpr int NH = (GRP + LPT - 1) / LPT;
+  P0Acc acc[NH];
 #pragma unroll
-  for (int h = 0; h < GRP; ++h) mx[h] = -INFINITY;
+  for (int k = 0; k < NH; ++k) p0_init(acc[k]);
   uint32_t n_h = 0;
   bool bad = false;
-  __shared__ float s_dot[GRP][kChunk];  // the chunk's logits and r, for pass 0
-  __shared__ float s_r[kChunk];
-  {
+  for (int sb = base; sb < lim; sb += SUB) {
+    if (sb + SUB < lim) load_sub(sb + SUB, nraw, nrv);
 #pragma unroll
     for (int k = 0; k < UNR; ++k) {
-      const int i = base + k * TPI + threadIdx.x / LPT;
-      if (i >= lim) continue;
+      const int i = sb + k * TPI + (int)threadIdx.x / LPT;
       float f[8];
       unpack8(raw[k], f);
       float dot[GRP];
 #pragma unroll
       for (int h = 0; h < GRP; ++h) {
-        float acc = 0.0f;
+        float a = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(qv[h][e], f[e], acc);
-        dot[h] = group_sum<LPT>(acc);
+        for (int e = 0; e < 8; ++e) a = __builtin_fmaf(qv[h][e], f[e], a);
+        dot[h] = group_sum<LPT>(a);
       }
+      if (i >= lim) continue;
       const float ri = rv[k];
       if (!(ri > 0.0f && ri <= 1.0f)) bad = true;
       const bool in_l = ri < 1.0f;
       if (u == 0 && !in_l) ++n_h;
-      if (u == 0) s_r[i - base] = ri;
 #pragma unroll
-      for (int h = 0; h < GRP; ++h) {
-        if (h % LPT == u) {
-          p.shat[(size_t)row_of(p, b, g, h, GRP) * p.n + i] = dot[h];
-          s_dot[h][i - base] = dot[h];
+      for (int kk = 0; kk < NH; ++kk) {
+        // this lane's head h = u + LPT kk and its logit
+        float val = dot[kk * LPT];
+#pragma unroll
+        for (int j = 1; j < LPT; ++j)
+          if (kk * LPT + j < GRP && u == j) val = dot[kk * LPT + j];
+        const int h = u + LPT * kk;
+        if (h >= GRP) continue;
+        p.shat[(size_t)row_of(p, b, g, h, GRP) * p.n + i] = val;
+        if (in_l) {
+          p0_shift(acc[kk], val);
+          p0_add(acc[kk], val, ri);
         }
-        if (in_l) mx[h] = fmaxf(mx[h], dot[h]);
       }
     }
+#pragma unroll
+    for (int k = 0; k < UNR; ++k) {
+      raw[k] = nraw[k];
+      rv[k] = nrv[k];
+    }
+  }
+  // each head's accumulator, from the lanes that keep it
+  P0Acc hacc[GRP];
+#pragma unroll
+  for (int h = 0; h < GRP; ++h) {
+    p0_init(hacc[h]);
+    if (h % LPT == u) hacc[h] = acc[h / LPT];
   }
   const int np = p.nch + p.ncr;
   {
     const int any = __syncthreads_or((int)bad);
     if (threadIdx.x == 0) p.fstat[(size_t)bg * np + c] = any ? VKV_STATUS_BAD_R : 0u;
   }
-  scan_finish<GRP>(p, b, g, c, lim - base, mx, s_dot, s_r);
-  const uint32_t th = block_sum<uint32_t>(n_h, s_ured);
-  if (threadIdx.x == 0) p.hpart[(size_t)bg * np + c] = th;
+  p0_finish<GRP>(p, b, g, c, hacc, n_h);
 }
 
 // Same outputs with exact keys read from the host cache (perfect sketch).
@@ -592,7 +651,6 @@ __device__ __forceinline__ void scan_exact_body(const DParams &p, int c,
                                                 int g, int b) {
   const int bg = b * p.G + g;
   const int lane = threadIdx.x % kWave;
-  __shared__ uint32_t s_ured[kBlock / kWave];
   if (c == 0) {
     for (int h = 0; h < GRP; ++h) {
       const int row = row_of(p, b, g, h, GRP);
@@ -626,16 +684,14 @@ __device__ __forceinline__ void scan_exact_body(const DParams &p, int c,
         p.q + (size_t)row_of(p, b, g, h, GRP) * kHeadDim + u * 8);
     unpack8(raw, qv[h]);
   }
-  float mx[GRP];
+  P0Acc acc[GRP];  // lane h keeps head h
 #pragma unroll
-  for (int h = 0; h < GRP; ++h) mx[h] = -INFINITY;
+  for (int h = 0; h < GRP; ++h) p0_init(acc[h]);
   uint32_t n_h = 0;
   bool bad = false;
   const float *rr = p.r + (size_t)bg * p.n;
   const int base = c * p.chunk;
   const int lim = min(base + p.chunk, p.n);
-  __shared__ float s_dot[GRP][kChunk];  // the chunk's logits and r, for pass 0
-  __shared__ float s_r[kChunk];
   for (int i0 = base; i0 < lim; i0 += kBlock / 16) {
     const int i = i0 + threadIdx.x / 16;
     if (i < lim) {
@@ -644,7 +700,6 @@ __device__ __forceinline__ void scan_exact_body(const DParams &p, int c,
       const bool in_l = ri < 1.0f;
       if (u == 0 && !in_l) ++n_h;
       float dot[GRP];
-      if (u == 0) s_r[i - base] = ri;
       if (in_l) {
         const uint4 raw = *reinterpret_cast<const uint4 *>(
             p.host_kv + ((size_t)bg * p.n + i) * 2 * kHeadDim + u * 8);
@@ -652,11 +707,14 @@ __device__ __forceinline__ void scan_exact_body(const DParams &p, int c,
         unpack8(raw, f);
 #pragma unroll
         for (int h = 0; h < GRP; ++h) {
-          float acc = 0.0f;
+          float dp = 0.0f;
 #pragma unroll
-          for (int k = 0; k < 8; ++k) acc = __builtin_fmaf(qv[h][k], f[k], acc);
-          dot[h] = group_sum<16>(acc) * kInvSqrtD;
-          mx[h] = fmaxf(mx[h], dot[h]);
+          for (int k = 0; k < 8; ++k) dp = __builtin_fmaf(qv[h][k], f[k], dp);
+          dot[h] = group_sum<16>(dp) * kInvSqrtD;
+          if (u == h) {
+            p0_shift(acc[h], dot[h]);
+            p0_add(acc[h], dot[h], ri);
+          }
         }
       } else {
 #pragma unroll
@@ -665,7 +723,6 @@ __device__ __forceinline__ void scan_exact_body(const DParams &p, int c,
 #pragma unroll
       for (int h = 0; h < GRP; ++h) {
         if (u == h) p.shat[(size_t)row_of(p, b, g, h, GRP) * p.n + i] = dot[h];
-        if (u == 0) s_dot[h][i - base] = dot[h];
       }
     }
   }
@@ -674,9 +731,7 @@ __device__ __forceinline__ void scan_exact_body(const DParams &p, int c,
     if (threadIdx.x == 0)
       p.fstat[(size_t)bg * (p.nch + p.ncr) + c] = any ? VKV_STATUS_BAD_R : 0u;
   }
-  scan_finish<GRP>(p, b, g, c, lim - base, mx, s_dot, s_r);
-  const uint32_t th = block_sum<uint32_t>(n_h, s_ured);
-  if (threadIdx.x == 0) p.hpart[(size_t)bg * (p.nch + p.ncr) + c] = th;
+  p0_finish<GRP>(p, b, g, c, acc, n_h);
 }
 
 // ------------------------------------------------------------ dk_resident
@@ -712,21 +767,45 @@ __device__ __forceinline__ void resident_body(const DParams &p, int c, int g,
   uint32_t n_h = 0;
   int lo, hi;
   split_range(cnt, p.ncr, c, lo, hi);
-  for (int j0 = lo; j0 < hi; j0 += kBlock / 16) {
-    const int j = j0 + threadIdx.x / 16;
-    if (j < hi) {
-      const int pos = ridx[j];
-      const bool ok = pos >= 0 && pos < p.n && (j == 0 || ridx[j - 1] < pos);
-      const uint4 raw = *reinterpret_cast<const uint4 *>(
-          p.rkv + ((size_t)bg * p.cap + j) * 2 * kHeadDim + u * 8);
-      const bool in_h = ok && rr[pos] >= 1.0f;
+  // RB rows per 16-lane slot at a time: their positions and K rows are
+  // loaded together, then r at those positions
+  constexpr int RB = 4, SLOTS = kBlock / 16;
+  for (int j0 = lo; j0 < hi; j0 += RB * SLOTS) {
+    int pos[RB], prv[RB];
+    uint4 raw[RB];
+#pragma unroll
+    for (int k = 0; k < RB; ++k) {
+      const int j = j0 + k * SLOTS + (int)threadIdx.x / 16;
+      pos[k] = -1;
+      prv[k] = -1;
+      if (j < hi) {
+        pos[k] = ridx[j];
+        if (j > 0) prv[k] = ridx[j - 1];
+        raw[k] = *reinterpret_cast<const uint4 *>(
+            p.rkv + ((size_t)bg * p.cap + j) * 2 * kHeadDim + u * 8);
+      }
+    }
+    bool okk[RB];
+    float rk[RB];
+#pragma unroll
+    for (int k = 0; k < RB; ++k) {
+      const int j = j0 + k * SLOTS + (int)threadIdx.x / 16;
+      okk[k] = j < hi && pos[k] >= 0 && pos[k] < p.n && (j == 0 || prv[k] < pos[k]);
+      rk[k] = okk[k] ? rr[pos[k]] : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < RB; ++k) {
+      const int j = j0 + k * SLOTS + (int)threadIdx.x / 16;
+      if (j >= hi) continue;  // (uniform over the 16-lane slot)
+      const bool ok = okk[k];
+      const bool in_h = ok && rk[k] >= 1.0f;
       float f[8];
-      unpack8(raw, f);
+      unpack8(raw[k], f);
 #pragma unroll
       for (int h = 0; h < GRP; ++h) {
         float acc = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) acc = __builtin_fmaf(qv[h][k], f[k], acc);
+        for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(qv[h][e], f[e], acc);
         const float dot = group_sum<16>(acc) * kInvSqrtD;
         if (u == h) p.ell[(size_t)row_of(p, b, g, h, GRP) * p.cap + j] = dot;
         mx[h] = fmaxf(mx[h], dot);
@@ -1306,6 +1385,11 @@ __device__ __forceinline__ void beta_accumulate(const double (&pts)[kBetaPts],
 
 // This thread's share (records t, t + kBlock, ...) of a row's S chunk
 // records; with LB, slot 3 (the lower bound of pass 0) combines by maximum.
+// The per-chunk band counts of the records last loaded (LDS).
+__device__ __forceinline__ int *band_counts() {
+  __shared__ int s_cnt[kMaxChunks];
+  return s_cnt;
+}
 template <bool LB>
 __device__ __forceinline__ void beta_rec_load(const double *rec, int S,
                                               double (&v)[kBetaRec]) {
@@ -1317,6 +1401,7 @@ __device__ __forceinline__ void beta_rec_load(const double *rec, int S,
       const double x = rec[(size_t)t * kBetaRec + k];
       v[k] = (LB && k == 3) ? fmax(v[k], x) : v[k] + x;
     }
+    if (!LB) band_counts()[t] = (int)rec[(size_t)t * kBetaRec + kBetaRec - 1];
   }
 }
 // Fixed-order totals of the shares: the same in every workgroup.
@@ -1420,11 +1505,10 @@ __device__ __forceinline__ BetaState beta_settle(const DParams &p, BetaState st,
   st = beta_advance(st, v);
   if (st.done || !(v[kBetaRec - 1] <= (double)kBandMax)) return st;
   const size_t rows = (size_t)p.B * p.Hq;
-  const double *rec = p.bpart + ((size_t)parity * rows + row) * p.nrc * kBetaRec;
   const float2 *band = p.band + ((size_t)parity * rows + row) * p.nrc * kBandChunk;
   if (threadIdx.x < kWave) {  // one wave: nrc <= 64 chunk counts
     const int t = threadIdx.x;
-    const int k = t < p.nrc ? (int)rec[(size_t)t * kBetaRec + kBetaRec - 1] : 0;
+    const int k = t < p.nrc ? band_counts()[t] : 0;
     const int incl = wave_incl_scan<int>(k, t);
     // a chunk over its capacity stored nothing
     const int bad = wave_max<int>(k > kBandChunk ? 1 : 0);
@@ -1454,6 +1538,7 @@ __device__ __forceinline__ BetaState beta_settle(const DParams &p, BetaState st,
   blk_reduce<double, 3, kBlock>(bs);
   // the tokens active at every point of the bracket (v holds the sums at lo)
   const double aw = v[0] - bs[0], ar = v[1] - bs[1], ac = v[2] - bs[2];
+  // Newton steps over the band in LDS
   for (int it = 0; it < kBetaPassMax && !st.done; ++it) {
     double pts[kBetaPts], u[kBetaRec];
     beta_points(st, pts);
@@ -1696,9 +1781,8 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   __shared__ RowState rs;
   __shared__ uint32_t s_hist[kSelBinsP];
-  __shared__ uint32_t s_cnt;
   __shared__ int s_j0, s_j1;
-  __shared__ uint32_t s_c0, s_cnt1;
+  __shared__ uint32_t s_c0;
   const float *rr = p.r + (size_t)bg * p.n;
   const float *sh = p.shat + (size_t)row * p.n;
   const int n = p.n;
@@ -1721,10 +1805,6 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
   const CertShare cs = cert_rec_load(p, row);
   const double beta = p.rbeta[2 * row], dnorm = p.rbeta[2 * row + 1];
   for (int i = threadIdx.x; i < kSelBinsP; i += kBlock) s_hist[i] = 0u;
-  if (threadIdx.x == 0) {
-    s_cnt = 0u;
-    s_cnt1 = 0u;
-  }
   row_certificate(p, cs, m, beta, dnorm, rs);
   if (s == 0 && threadIdx.x == 0) p.rows[row] = rs;
   if (!rs.fetch) return;
@@ -1773,39 +1853,40 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
     }
   }
   blk_reduce<unsigned long long, 2, kBlock>(tx);
-  // ---- local bounds: lane owns bins [lane * 32, lane * 32 + 32). Tier 0
-  // is the smallest bin edge with at most kTier0 keys at or above it, tier 1
-  // the same for kCandWG; c0 = keys at or above the tier-0 edge.
-  if (wave == 0) {
-    constexpr int PER = kSelBinsP / kWave;
-    uint32_t lc = 0u;
-    for (int k = 0; k < PER; ++k) lc += s_hist[lane * PER + k];
-    const uint32_t incl = wave_incl_scan<uint32_t>(lc, lane);
-    const uint32_t above = __shfl(incl, kWave - 1, kWave) - incl;
-    auto edge = [&](uint32_t cap, uint32_t &cnt) {
-      uint32_t c = above, cj = 0u;
-      int j = kSelBinsP;
-      if (c <= cap) {
-        for (int k = PER - 1; k >= 0; --k) {
-          c += s_hist[lane * PER + k];
-          if (c > cap) break;
-          j = lane * PER + k;
-          cj = c;
-        }
-      }
-      int jm = j;
-      for (int o = 32; o >= 1; o >>= 1) jm = min(jm, __shfl_xor(jm, o, kWave));
-      cnt = wave_max(j == jm ? cj : 0u);  // one lane owns bin jm
-      return jm;
-    };
-    uint32_t c0, c1;
-    const int j0 = edge((uint32_t)kTier0, c0);
-    const int j1 = edge((uint32_t)kCandWG, c1);
-    if (lane == 0) {
-      s_j0 = j0;
-      s_j1 = j1;
-      s_c0 = c0;
+  // ---- local bounds: thread t owns bins [8 t, 8 t + 8). Tier 0 is the
+  // smallest bin edge with at most kTier0 keys at or above it, tier 1 the
+  // same for kCandWG; c0 = keys at or above the tier-0 edge.
+  __shared__ uint32_t s_scan[kBlock / kWave + 1];
+  {
+    constexpr int PB = kSelBinsP / kBlock;
+    uint32_t hc[PB], own = 0u;
+#pragma unroll
+    for (int k = 0; k < PB; ++k) {
+      hc[k] = s_hist[threadIdx.x * PB + k];
+      own += hc[k];
     }
+    uint32_t all;
+    const uint32_t excl = block_exclusive_scan<uint32_t>(own, s_scan, &all);
+    uint32_t c = all - excl - own;  // keys in the bins of later threads
+    int jb[2] = {kSelBinsP, kSelBinsP};
+    uint32_t cj0 = 0u;
+#pragma unroll
+    for (int k = PB - 1; k >= 0; --k) {
+      c += hc[k];
+      if (c <= (uint32_t)kTier0) {
+        jb[0] = (int)threadIdx.x * PB + k;
+        cj0 = c;
+      }
+      if (c <= (uint32_t)kCandWG) jb[1] = (int)threadIdx.x * PB + k;
+    }
+    const int my0 = jb[0];
+    blk_combine<int, 2, kBlock, OpMin<int>>(jb);
+    if (threadIdx.x == 0) {
+      s_j0 = jb[0];
+      s_j1 = jb[1];
+      if (jb[0] == kSelBinsP) s_c0 = 0u;
+    }
+    if (my0 == jb[0] && my0 < kSelBinsP) s_c0 = cj0;  // the owner of that bin
   }
   __syncthreads();
   const unsigned long long lo0 =
@@ -1813,58 +1894,70 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
   const unsigned long long lo =
       s_j1 < kSelBinsP ? ((unsigned long long)s_j1 << sel_off(0)) : kKeyEnd;
   const uint32_t c0 = s_c0;
-  // ---- the keys at or above lo (with w~ and r), tier 0 first; for the
-  // keys below lo and for those of tier 1 alone, the max of b_i and the
-  // float64 sums of beta_i and v_i
+  // ---- the keys at or above lo (with w~ and r), tier 0 first, each tier in
+  // token order (slots from a block scan); for the keys below lo and for
+  // those of tier 1 alone, the max of b_i and the float64 sums of beta_i
+  // and v_i
   const size_t seg = ((size_t)row * kSelWG + s) * kCandWG;
   uint32_t below = 0u, below1 = 0u;
   double dsum[4] = {0.0, 0.0, 0.0, 0.0};
-  auto emit = [&](float ri, float si, unsigned long long key) {
-    uint32_t slot;
-    if (key >= lo0) {
-      slot = atomicAdd(&s_cnt, 1u);
-    } else {
-      slot = c0 + atomicAdd(&s_cnt1, 1u);
-      const Terms t = token_terms_w(expf(si - m), ri, betaf, p.est);
-      double bd, vd;
-      direct_terms(t, bd, vd);
-      dsum[2] += bd;
-      dsum[3] += vd;
-      below1 = max(below1, __float_as_uint(t.rb));
-    }
-    if (slot < (uint32_t)kCandWG) {
-      p.candk[seg + slot] = key;
-      p.candw[seg + slot] = expf(si - m);
-      p.candq[seg + slot] = ri;
-    }
-  };
-  auto rest = [&](const Terms &t) {
-    double bd, vd;
-    direct_terms(t, bd, vd);
-    dsum[0] += bd;
-    dsum[1] += vd;
-    below = max(below, __float_as_uint(t.rb));
-  };
-#pragma unroll
-  for (int it = 0; it < kSelIt; ++it) {
-    if (!(r8[it] < 1.0f)) continue;
-    if (key8[it] >= lo) {
-      emit(r8[it], s8[it], key8[it]);
-    } else {
-      rest(token_terms_w(expf(s8[it] - m), r8[it], betaf, p.est));
-    }
-  }
-  for (int it0 = kSelIt; it0 < iters; it0 += kSelIt) {
-    float rb[kSelIt], sb[kSelIt];
-    load_batch(it0, rb, sb);
+  uint32_t o0 = 0u, o1 = 0u;  // slots taken by earlier batches, per tier
+  auto emit_batch = [&](const unsigned long long (&kb)[kSelIt],
+                        const float (&rb)[kSelIt], const float (&sb)[kSelIt]) {
+    uint32_t n0 = 0u, n1 = 0u;
 #pragma unroll
     for (int k = 0; k < kSelIt; ++k) {
       if (!(rb[k] < 1.0f)) continue;
-      Terms t;
-      const unsigned long long key = key_of(pos_of(it0 + k), rb[k], sb[k], t);
-      if (key >= lo) emit(rb[k], sb[k], key);
-      else rest(t);
+      if (kb[k] >= lo0) ++n0;
+      else if (kb[k] >= lo) ++n1;
     }
+    uint32_t tot;
+    const uint32_t ex = block_exclusive_scan<uint32_t>(n0 | (n1 << 16), s_scan, &tot);
+    uint32_t a0 = o0 + (ex & 0xFFFFu), a1 = c0 + o1 + (ex >> 16);
+#pragma unroll
+    for (int k = 0; k < kSelIt; ++k) {
+      if (!(rb[k] < 1.0f)) continue;
+      uint32_t slot;
+      if (kb[k] >= lo0) {
+        slot = a0++;
+      } else {
+        const Terms t = token_terms_w(expf(sb[k] - m), rb[k], betaf, p.est);
+        double bd, vd;
+        direct_terms(t, bd, vd);
+        if (kb[k] >= lo) {
+          dsum[2] += bd;
+          dsum[3] += vd;
+          below1 = max(below1, __float_as_uint(t.rb));
+          slot = a1++;
+        } else {
+          dsum[0] += bd;
+          dsum[1] += vd;
+          below = max(below, __float_as_uint(t.rb));
+          continue;
+        }
+      }
+      if (slot < (uint32_t)kCandWG) {
+        p.candk[seg + slot] = kb[k];
+        p.candw[seg + slot] = expf(sb[k] - m);
+        p.candq[seg + slot] = rb[k];
+      }
+    }
+    o0 += tot & 0xFFFFu;
+    o1 += tot >> 16;
+  };
+  emit_batch(key8, r8, s8);
+  for (int it0 = kSelIt; it0 < iters; it0 += kSelIt) {
+    float rb[kSelIt], sb[kSelIt];
+    unsigned long long kb[kSelIt];
+    load_batch(it0, rb, sb);
+#pragma unroll
+    for (int k = 0; k < kSelIt; ++k) {
+      kb[k] = 0ull;
+      if (!(rb[k] < 1.0f)) continue;
+      Terms t;
+      kb[k] = key_of(pos_of(it0 + k), rb[k], sb[k], t);
+    }
+    emit_batch(kb, rb, sb);
   }
   below = blk_max<uint32_t, kBlock>(below);
   below1 = blk_max<uint32_t, kBlock>(below1);
@@ -1873,8 +1966,8 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
     // per tier: candidates, bound, and over the tokens not written in that
     // tier the max of b_i and the float64 sums
     const size_t at = (size_t)row * kSelWG + s;
-    p.ccount[2 * at] = min(s_cnt, c0);
-    p.ccount[2 * at + 1] = min(c0 + s_cnt1, (uint32_t)kCandWG);
+    p.ccount[2 * at] = min(o0, c0);
+    p.ccount[2 * at + 1] = min(c0 + o1, (uint32_t)kCandWG);
     p.clo[2 * at] = lo0;
     p.clo[2 * at + 1] = lo;
     p.rpart[2 * at] = max(below, below1);
@@ -2667,12 +2760,23 @@ const char *decode_phase_name(int i) {
 DecodeLayout decode_layout(const vkv_decode_args &a) {
   DecodeLayout L{};
   L.grp = a.n_q_heads / a.n_kv_heads;
-  L.chunk = kChunk;
+  // tokens per scan workgroup: kChunk, or up to 16x more while the launch
+  // keeps about 512 workgroups (large batches), so that each workgroup's
+  // fixed costs (the projected query, the reductions) cover more tokens
+  {
+    const long long groups = (long long)a.batch * a.n_kv_heads;
+    int mult = 1;
+    while (mult < 16 &&
+           groups * ((a.n_tokens + 2 * mult * kChunk - 1) / (2 * mult * kChunk)) >= 512)
+      mult *= 2;
+    L.chunk = kChunk * mult;
+  }
   L.nch = (a.n_tokens + L.chunk - 1) / L.chunk;
   // workgroups per group for the resident rows and for the fetched rows:
-  // about 2048 workgroups per launch in total, at least 64 rows each
+  // about 512 resident-row workgroups per launch in total, at least 64 rows
+  // each
   const long long groups_ll = (long long)a.batch * a.n_kv_heads;
-  const int target = (int)((2048 + groups_ll - 1) / groups_ll);
+  const int target = (int)((512 + groups_ll - 1) / groups_ll);
   const int rmax = a.cap < a.n_tokens ? a.cap : a.n_tokens;
   // (each at most 32, so the merge sees at most 64 partial sums)
   // (and with the gather workgroups of the same launch, at most one
