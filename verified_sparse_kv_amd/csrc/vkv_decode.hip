@@ -103,6 +103,8 @@ struct DParams {
   double *hres;      // [row][ncr] sum over H of exp(l - shift) per part
   uint32_t *hpart;
   RowState *rows;
+  int nsub, rsub;    // kRowChunk sub-chunks per row, and per row workgroup
+  int nsel;          // candidate workgroups per row
   double *bpart;     // [2][row][nrc][kBetaRec] beta pass records
   float2 *band;      // [2][row][nrc][kBandChunk] (w~, rho) of band tokens
   BetaState *bstate; // [2][row]
@@ -896,10 +898,10 @@ __global__ __launch_bounds__(kBlock) void dk_front_exact(DParams p) {
 // workgroups iterates over the whole row (rare; same arithmetic).
 //
 // Selection: keys (gain bits, inverted position) order L as L_g
-// (descending). Each of kSelWG workgroups per row takes a block-cyclic
-// share of the row's tokens and writes its keys at or above a local bound
-// lo_s (at most kCandWG of them) with their fixed-point beta_i and v_i and
-// range term b_i. One workgroup per row then runs the stopping rule on the
+// (descending). Each of nsel workgroups per row takes a block-cyclic share of the row's tokens and writes its keys at or
+// above a local bound lo_s (at most kCandMax / nsel of them, the top
+// quarter first) with their w~ and r; the terms of Lemma 1 are recomputed
+// from those. One workgroup per row then runs the stopping rule on the
 // union to the exact k* and threshold T; that is the answer whenever T >=
 // max_s lo_s (every key >= T was written). Otherwise, or when fetching every
 // candidate cannot certify the row, it runs the streaming selection below
@@ -1466,30 +1468,13 @@ __device__ __forceinline__ float row_pass0(const DParams &p, int row, int bg,
 
 // The band of a bracket [lo, hi]: the tokens active at lo and not at hi,
 // the only ones whose share of h can change inside it. Each pass stores its
-// chunk's band (when it fits) in token order and counts it in the record.
+// workgroup's band (when it fits) in a fixed order and counts it in the
+// record.
 __device__ __forceinline__ bool in_band(const BetaState &st, float wt, float ri) {
   if (!(wt > 0.0f)) return false;
   const double w = (double)wt, rh = (double)plan_rho(ri);
   return w - st.lo * rh > 0.0 && !(w - st.hi * rh > 0.0);
 }
-__device__ __forceinline__ uint32_t band_collect(const BetaState &st,
-                                                 const float (&w8)[kRowTok],
-                                                 const float (&r8)[kRowTok],
-                                                 float2 *dst) {
-  __shared__ uint32_t s_bs[kBlock / kWave + 1];
-  uint32_t mine = 0u;
-#pragma unroll
-  for (int u = 0; u < kRowTok; ++u) mine += in_band(st, w8[u], r8[u]) ? 1u : 0u;
-  uint32_t total;
-  uint32_t k = block_exclusive_scan<uint32_t>(mine, s_bs, &total);
-  if (total <= (uint32_t)kBandChunk) {
-#pragma unroll
-    for (int u = 0; u < kRowTok; ++u)
-      if (in_band(st, w8[u], r8[u])) dst[k++] = make_float2(w8[u], plan_rho(r8[u]));
-  }
-  return total;
-}
-
 // The state after a pass whose combined records are v: one bracketed Newton
 // step; then, when the pass's band was small enough to keep, the iteration
 // goes on over the band alone in LDS (the tokens outside it have the same
@@ -1582,8 +1567,10 @@ __global__ __launch_bounds__(kBlock) void dk_rbeta(DParams p, int pass) {
       p.bstate[(size_t)(pass & 1) * rows + row] = p.bstate[(size_t)q * rows + row];
     return;
   }
+  // sub-chunks [cc0, cc1) of kRowChunk tokens; the first in flight now
+  const int cc0 = c * p.rsub, cc1 = min(cc0 + p.rsub, p.nsub);
   float w8[kRowTok], r8[kRowTok], s8[kRowTok];
-  row_load(p, row, bg, c, r8, s8);
+  row_load(p, row, bg, cc0, r8, s8);
   // the previous pass: this thread's share of the records, and the state
   double rv[kBetaRec];
   BetaState st{};
@@ -1597,7 +1584,6 @@ __global__ __launch_bounds__(kBlock) void dk_rbeta(DParams p, int pass) {
     beta_rec_load<false>(p.bpart + ((size_t)q * rows + row) * p.nrc * kBetaRec, p.nrc, rv);
     st = p.bstate[(size_t)q * rows + row];
   }
-  row_weights(m, r8, s8, w8);
   double v[kBetaRec];
 #pragma unroll
   for (int k = 0; k < kBetaRec; ++k) v[k] = 0.0;
@@ -1610,11 +1596,42 @@ __global__ __launch_bounds__(kBlock) void dk_rbeta(DParams p, int pass) {
   if (st.done) return;
   double pts[kBetaPts];
   beta_points(st, pts);
+  // the band: which of this thread's tokens are in it (bit 8 j + u for
+  // sub-chunk cc0 + j), stored once all are seen, in (thread, token) order
+  static_assert(kRowTok * 8 <= 64, "band mask");
+  unsigned long long bmask = 0ull;
+  for (int cc = cc0; cc < cc1; ++cc) {
+    float nr[kRowTok], ns[kRowTok];
+    if (cc + 1 < cc1) row_load(p, row, bg, cc + 1, nr, ns);  // next in flight
+    row_weights(m, r8, s8, w8);
 #pragma unroll
-  for (int u = 0; u < kRowTok; ++u) beta_accumulate(pts, w8[u], r8[u], v);
-  const uint32_t nband = band_collect(
-      st, w8, r8,
-      p.band + (((size_t)(pass & 1) * rows + row) * p.nrc + c) * kBandChunk);
+    for (int u = 0; u < kRowTok; ++u) {
+      beta_accumulate(pts, w8[u], r8[u], v);
+      if (in_band(st, w8[u], r8[u])) bmask |= 1ull << ((cc - cc0) * kRowTok + u);
+    }
+#pragma unroll
+    for (int u = 0; u < kRowTok; ++u) {
+      r8[u] = nr[u];
+      s8[u] = ns[u];
+    }
+  }
+  uint32_t nband;
+  {
+    __shared__ uint32_t s_bs[kBlock / kWave + 1];
+    uint32_t k = block_exclusive_scan<uint32_t>((uint32_t)__popcll(bmask), s_bs, &nband);
+    if (nband <= (uint32_t)kBandChunk) {
+      float2 *bdst = p.band + (((size_t)(pass & 1) * rows + row) * p.nrc + c) * kBandChunk;
+      const float *rr = p.r + (size_t)bg * p.n;
+      const float *sh = p.shat + (size_t)row * p.n;
+      while (bmask) {
+        const int bit = __ffsll((long long)bmask) - 1;
+        bmask &= bmask - 1ull;
+        const int i = row_pos(cc0 + bit / kRowTok, bit % kRowTok);
+        const float ri = rr[i];
+        bdst[k++] = make_float2(expf(sh[i] - m), plan_rho(ri));
+      }
+    }
+  }
   blk_reduce<double, kBetaRec, kBlock>(v);
   if (threadIdx.x == 0) {
 #pragma unroll
@@ -1630,15 +1647,15 @@ __global__ __launch_bounds__(kBlock) void dk_rcert(DParams p) {
   const int c = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
   const int row = b * p.Hq + hq, bg = b * p.G + hq / GRP;
   const size_t rows = (size_t)p.B * p.Hq;
+  const int cc0 = c * p.rsub, cc1 = min(cc0 + p.rsub, p.nsub);
   float w8[kRowTok], r8[kRowTok], s8[kRowTok];
-  row_load(p, row, bg, c, r8, s8);
+  row_load(p, row, bg, cc0, r8, s8);
   const float m = p.rows[row].m;
   const int q = kBetaLaunches & 1;
   double rv[kBetaRec];
   beta_rec_load<false>(p.bpart + ((size_t)q * rows + row) * p.nrc * kBetaRec,
                        p.nrc, rv);
   BetaState st = p.bstate[(size_t)q * rows + row];
-  row_weights(m, r8, s8, w8);
   if (!st.done) {
     beta_rec_total<false>(rv);
     st = beta_settle(p, st, rv, row, q);
@@ -1651,7 +1668,7 @@ __global__ __launch_bounds__(kBlock) void dk_rcert(DParams p) {
       beta_points(st, pts);
 #pragma unroll
       for (int k = 0; k < kBetaRec; ++k) v[k] = 0.0;
-      for (int cc = 0; cc < p.nrc; ++cc) {
+      for (int cc = 0; cc < p.nsub; ++cc) {
         float fr[kRowTok], fs[kRowTok], fw[kRowTok];
         row_load(p, row, bg, cc, fr, fs);
         row_weights(m, fr, fs, fw);
@@ -1672,13 +1689,23 @@ __global__ __launch_bounds__(kBlock) void dk_rcert(DParams p) {
   double cv[2] = {0.0, 0.0};
   float x1 = 0.0f, x2 = 0.0f;
   int p1 = 0x7fffffff;
+  for (int cc = cc0; cc < cc1; ++cc) {
+    float nr[kRowTok], ns[kRowTok];
+    if (cc + 1 < cc1) row_load(p, row, bg, cc + 1, nr, ns);  // next in flight
+    row_weights(m, r8, s8, w8);
 #pragma unroll
-  for (int u = 0; u < kRowTok; ++u) {
-    if (!(r8[u] < 1.0f)) continue;
-    const Terms t = token_terms_w(w8[u], r8[u], betaf, p.est);
-    cv[0] += (double)t.bi;
-    cv[1] += (double)t.vi;
-    top2_merge(x1, p1, x2, t.rb, row_pos(c, u), 0.0f);
+    for (int u = 0; u < kRowTok; ++u) {
+      if (!(r8[u] < 1.0f)) continue;
+      const Terms t = token_terms_w(w8[u], r8[u], betaf, p.est);
+      cv[0] += (double)t.bi;
+      cv[1] += (double)t.vi;
+      top2_merge(x1, p1, x2, t.rb, row_pos(cc, u), 0.0f);
+    }
+#pragma unroll
+    for (int u = 0; u < kRowTok; ++u) {
+      r8[u] = nr[u];
+      s8[u] = ns[u];
+    }
   }
   blk_reduce<double, 2, kBlock>(cv);
   blk_top2<kBlock>(x1, p1, x2);
@@ -1762,23 +1789,25 @@ __device__ __forceinline__ void row_certificate(const DParams &p, CertShare sh,
 // Candidate workgroups per row and the candidates each may write. Their
 // tokens are split block-cyclically (blocks of kSelBlk positions), so that a
 // run of high-gain positions is spread over all of them.
-constexpr int kSelWG = 16;
-constexpr int kCandWG = kCandMax / kSelWG;
-constexpr int kTier0 = kCandWG / 4;  // candidates per workgroup tried first
+constexpr int kSelWG = 16;           // at most; p.nsel per row at run time
+// Per workgroup of a row's p.nsel: kCandMax / nsel candidates, the top
+// quarter of them tried first.
+__device__ __forceinline__ int cand_cap(const DParams &p) { return kCandMax / p.nsel; }
 constexpr int kSelBlk = 64;
 constexpr int kSelIt = 8;  // tokens per thread whose keys stay in registers
 
 // Certificate of the row (workgroup 0 stores it), then for a row that
 // fetches: this workgroup's keys, their count histogram over the top 11 key
 // bits and the fixed-point totals of beta_i and v_i; its local bound lo_s,
-// the smallest bin edge with at most kCandWG of its keys at or above it; and
+// the smallest bin edge with at most kCandMax / nsel of its keys at or
+// above it; and
 // those keys, written with their fixed-point beta_i, v_i and b_i. Keys below
 // lo_s are not written; their largest b_i is.
 template <int GRP>
 __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
   const int s = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
   const int row = b * p.Hq + hq, bg = b * p.G + hq / GRP;
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int nsel = p.nsel, capw = cand_cap(p);
   __shared__ RowState rs;
   __shared__ uint32_t s_hist[kSelBinsP];
   __shared__ int s_j0, s_j1;
@@ -1788,11 +1817,11 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
   const int n = p.n;
   // token of iteration it for this thread
   auto pos_of = [&](int it) {
-    return ((it * (kBlock / kSelBlk) + (int)threadIdx.x / kSelBlk) * kSelWG + s) * kSelBlk +
+    return ((it * (kBlock / kSelBlk) + (int)threadIdx.x / kSelBlk) * nsel + s) * kSelBlk +
            (int)threadIdx.x % kSelBlk;
   };
   const int nblk = (n + kSelBlk - 1) / kSelBlk;
-  const int iters = ((nblk + kSelWG - 1) / kSelWG + kBlock / kSelBlk - 1) / (kBlock / kSelBlk);
+  const int iters = ((nblk + nsel - 1) / nsel + kBlock / kSelBlk - 1) / (kBlock / kSelBlk);
   // loads first: the first kSelIt tokens, the certificate records
   float r8[kSelIt], s8[kSelIt];
 #pragma unroll
@@ -1854,8 +1883,8 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
   }
   blk_reduce<unsigned long long, 2, kBlock>(tx);
   // ---- local bounds: thread t owns bins [8 t, 8 t + 8). Tier 0 is the
-  // smallest bin edge with at most kTier0 keys at or above it, tier 1 the
-  // same for kCandWG; c0 = keys at or above the tier-0 edge.
+  // smallest bin edge with at most capw / 4 keys at or above it, tier 1 the
+  // same for capw; c0 = keys at or above the tier-0 edge.
   __shared__ uint32_t s_scan[kBlock / kWave + 1];
   {
     constexpr int PB = kSelBinsP / kBlock;
@@ -1873,11 +1902,11 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
 #pragma unroll
     for (int k = PB - 1; k >= 0; --k) {
       c += hc[k];
-      if (c <= (uint32_t)kTier0) {
+      if (c <= (uint32_t)(capw / 4)) {
         jb[0] = (int)threadIdx.x * PB + k;
         cj0 = c;
       }
-      if (c <= (uint32_t)kCandWG) jb[1] = (int)threadIdx.x * PB + k;
+      if (c <= (uint32_t)capw) jb[1] = (int)threadIdx.x * PB + k;
     }
     const int my0 = jb[0];
     blk_combine<int, 2, kBlock, OpMin<int>>(jb);
@@ -1898,7 +1927,7 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
   // token order (slots from a block scan); for the keys below lo and for
   // those of tier 1 alone, the max of b_i and the float64 sums of beta_i
   // and v_i
-  const size_t seg = ((size_t)row * kSelWG + s) * kCandWG;
+  const size_t seg = (size_t)row * kCandMax + (size_t)s * capw;
   uint32_t below = 0u, below1 = 0u;
   double dsum[4] = {0.0, 0.0, 0.0, 0.0};
   uint32_t o0 = 0u, o1 = 0u;  // slots taken by earlier batches, per tier
@@ -1936,7 +1965,7 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
           continue;
         }
       }
-      if (slot < (uint32_t)kCandWG) {
+      if (slot < (uint32_t)capw) {
         p.candk[seg + slot] = kb[k];
         p.candw[seg + slot] = expf(sb[k] - m);
         p.candq[seg + slot] = rb[k];
@@ -1967,7 +1996,7 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
     // tier the max of b_i and the float64 sums
     const size_t at = (size_t)row * kSelWG + s;
     p.ccount[2 * at] = min(o0, c0);
-    p.ccount[2 * at + 1] = min(c0 + o1, (uint32_t)kCandWG);
+    p.ccount[2 * at + 1] = min(c0 + o1, (uint32_t)capw);
     p.clo[2 * at] = lo0;
     p.clo[2 * at + 1] = lo;
     p.rpart[2 * at] = max(below, below1);
@@ -2042,7 +2071,8 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rwalk(DParams p) {
   // while the candidates are loaded
   __shared__ uint32_t s_res[kMaxTokens / 32];
   for (int i = threadIdx.x; i < p.nwords; i += kPlanThreads) s_res[i] = 0u;
-  if (threadIdx.x < kSelWG) {
+  const int nsel = p.nsel, capw = cand_cap(p);
+  if (threadIdx.x < nsel) {
     const int j = threadIdx.x;
     const size_t at = (size_t)row * kSelWG + j;
 #pragma unroll
@@ -2071,13 +2101,13 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rwalk(DParams p) {
   const double sbs = ldexp(1.0, -eb), svs = ldexp(1.0, -ev);
   const float betaf = (float)rs.beta;
   const int est = p.est;
-  // Tier 0 holds each workgroup's top kTier0 keys, tier 1 all kCandWG; the
+  // Tier 0 holds each workgroup's top capw / 4 keys, tier 1 all capw; the
   // larger set is only walked when the smaller one cannot decide the row.
 #pragma unroll 1
   for (int tier = 0; tier < 2; ++tier) {
-    const int cap = tier == 0 ? kTier0 : kCandWG;
+    const int cap = tier == 0 ? capw / 4 : capw;
     if (wave == 0) {
-      const bool on = lane < kSelWG;
+      const bool on = lane < nsel;
       const int j = on ? lane : 0;
       const uint32_t c = on ? s_pc[tier][j] : 0u;
       const uint32_t incl = wave_incl_scan<uint32_t>(c, lane);
@@ -2108,7 +2138,7 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rwalk(DParams p) {
     // the tier's candidates into LDS (loads first), their fixed-point sums
     unsigned long long cs[2] = {0ull, 0ull};
     unsigned long long kmin = ~0ull, kmax = 0ull;
-    for (int q0 = 0; q0 < kSelWG * cap; q0 += kPlanThreads * 2) {
+    for (int q0 = 0; q0 < nsel * cap; q0 += kPlanThreads * 2) {
       unsigned long long ck[2];
       float cw[2], cq[2];
       int dst[2];
@@ -2117,8 +2147,8 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rwalk(DParams p) {
         const int idx = q0 + u * kPlanThreads + (int)threadIdx.x;
         const int sw = idx / cap, slot = idx % cap;
         dst[u] = -1;
-        if (idx < kSelWG * cap && slot < (int)s_wc[sw]) {
-          const size_t at = cb0 + (size_t)sw * kCandWG + slot;
+        if (idx < nsel * cap && slot < (int)s_wc[sw]) {
+          const size_t at = cb0 + (size_t)sw * capw + slot;
           ck[u] = p.candk[at];
           cw[u] = p.candw[at];
           cq[u] = p.candq[at];
@@ -2733,7 +2763,7 @@ hipError_t run(const DParams &p, hipStream_t s, int sd, void **events) {
   }
   dk_rcert<GRP><<<grow, blk, 0, s>>>(p);
   mark(k++);
-  dk_rcand<GRP><<<dim3((unsigned)kSelWG, (unsigned)p.Hq, (unsigned)p.B), blk, 0, s>>>(p);
+  dk_rcand<GRP><<<dim3((unsigned)p.nsel, (unsigned)p.Hq, (unsigned)p.B), blk, 0, s>>>(p);
   mark(k++);
   dk_rwalk<GRP><<<gone, dim3(kPlanThreads), 0, s>>>(p);
   mark(k++);
@@ -2787,7 +2817,19 @@ DecodeLayout decode_layout(const vkv_decode_args &a) {
   L.ncf = kGatherWG;
   L.npad = (L.ncr + L.ncf + 3) / 4 * 4;
   L.nwords = (a.n_tokens + 31) / 32;
-  L.nrc = (a.n_tokens + kRowChunk - 1) / kRowChunk;
+  // row passes: kRowChunk-token sub-chunks, several per workgroup while a
+  // launch keeps about 1024 workgroups (large batches)
+  L.nsub = (a.n_tokens + kRowChunk - 1) / kRowChunk;
+  {
+    const long long rows_ll = (long long)a.batch * a.n_q_heads;
+    int rs = 1;
+    while (rs < 8 && rows_ll * ((L.nsub + 2 * rs - 1) / (2 * rs)) >= 1024) rs *= 2;
+    L.rsub = rs;
+  }
+  L.nrc = (L.nsub + L.rsub - 1) / L.rsub;
+  // candidate workgroups per row (fewer, with more tokens each, measured
+  // slower at every batch size: the gain arithmetic per token dominates)
+  L.nsel = kSelWG;
   const size_t B = (size_t)a.batch, Hq = (size_t)a.n_q_heads,
                G = (size_t)a.n_kv_heads, n = (size_t)a.n_tokens;
   const size_t rows = B * Hq, groups = B * G;
@@ -2868,6 +2910,9 @@ hipError_t launch_decode(const vkv_decode_args &a, const DecodeLayout &L,
   p.dpart = at<double>(w, L.dpart);
   p.rpart = at<uint32_t>(w, L.rpart);
   p.nrc = L.nrc;
+  p.nsub = L.nsub;
+  p.rsub = L.rsub;
+  p.nsel = L.nsel;
   p.apart = at<float2>(w, L.apart);
   p.aparto = at<float>(w, L.aparto);
   p.npad = L.npad;
