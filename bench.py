@@ -305,6 +305,13 @@ def main():
         "host_fetch_gbs": host_bytes / t_gather / 1e9 if t_gather > 0 else None,
         "decisions_fetching_pct": 100.0 * float(np.mean(ks > 0)),
         "kernel_us_profiled": {k: round(float(v), 2) for k, v in zip(names, ph_us)},
+        # every HBM-bound kernel: algorithmic bytes over its profiled time
+        "kernels_hbm": {k: {"us": round(float(ph_us[names.index(k)]), 2),
+                            "bytes": int(v),
+                            "gbs": round(v / (ph_us[names.index(k)] * 1e-6) / 1e9, 1),
+                            "frac": round(v / (ph_us[names.index(k)] * 1e-6)
+                                          / (HBM_PEAK_GBS * 1e9), 4)}
+                        for k, v in cand.items()},
         "roofline": {"bound": "hbm", "kernel": dom, "kernel_us": t_dom * 1e6,
                      "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
