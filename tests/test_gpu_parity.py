@@ -182,6 +182,16 @@ def test_decode_full_size(cfg):
     assert s["fetched"] > 0
 
 
+@pytest.mark.parametrize("grp,s", [(1, 32), (2, 32), (8, 32), (4, 16), (8, 16)])
+def test_decode_head_groups_and_sketch_dims(grp, s):
+    """Every supported query-heads-per-KV-head count and sketch width (the
+    kernels are instantiated per pair)."""
+    w, gpu, heads, unions, eps = _decode_case("c2", n=4000, G=2, grp=grp, s=s)
+    st = gc.compare(w, gpu, heads, unions, eps)
+    gc.say(f"  {st}")
+    assert st["fetched"] > 0
+
+
 def test_decode_fetch_all_is_exact_attention():
     """eps -> 0: every L token is fetched and the output is exact attention."""
     w, gpu, heads, unions, eps = _decode_case("c2", eps=1e-30, n=3000, G=1)

@@ -770,23 +770,27 @@ __device__ __forceinline__ void resident_body(const DParams &p, int c, int g,
   int lo, hi;
   split_range(cnt, p.ncr, c, lo, hi);
   // RB rows per 16-lane slot at a time: their positions and K rows are
-  // loaded together, then r at those positions
+  // loaded together, then r at those positions; the next batch's positions
+  // and K rows load while this one's r arrives and is used
   constexpr int RB = 4, SLOTS = kBlock / 16;
-  for (int j0 = lo; j0 < hi; j0 += RB * SLOTS) {
-    int pos[RB], prv[RB];
-    uint4 raw[RB];
+  int pos[RB], prv[RB], npos[RB], nprv[RB];
+  uint4 raw[RB], nraw[RB];
+  auto load_rows = [&](int j0, int (&ps)[RB], int (&pv)[RB], uint4 (&ra)[RB]) {
 #pragma unroll
     for (int k = 0; k < RB; ++k) {
       const int j = j0 + k * SLOTS + (int)threadIdx.x / 16;
-      pos[k] = -1;
-      prv[k] = -1;
+      ps[k] = -1;
+      pv[k] = -1;
       if (j < hi) {
-        pos[k] = ridx[j];
-        if (j > 0) prv[k] = ridx[j - 1];
-        raw[k] = *reinterpret_cast<const uint4 *>(
+        ps[k] = ridx[j];
+        if (j > 0) pv[k] = ridx[j - 1];
+        ra[k] = *reinterpret_cast<const uint4 *>(
             p.rkv + ((size_t)bg * p.cap + j) * 2 * kHeadDim + u * 8);
       }
     }
+  };
+  if (lo < hi) load_rows(lo, pos, prv, raw);
+  for (int j0 = lo; j0 < hi; j0 += RB * SLOTS) {
     bool okk[RB];
     float rk[RB];
 #pragma unroll
@@ -795,6 +799,7 @@ __device__ __forceinline__ void resident_body(const DParams &p, int c, int g,
       okk[k] = j < hi && pos[k] >= 0 && pos[k] < p.n && (j == 0 || prv[k] < pos[k]);
       rk[k] = okk[k] ? rr[pos[k]] : 0.0f;
     }
+    if (j0 + RB * SLOTS < hi) load_rows(j0 + RB * SLOTS, npos, nprv, nraw);
 #pragma unroll
     for (int k = 0; k < RB; ++k) {
       const int j = j0 + k * SLOTS + (int)threadIdx.x / 16;
@@ -827,6 +832,12 @@ __device__ __forceinline__ void resident_body(const DParams &p, int c, int g,
           bad = true;
         }
       }
+    }
+#pragma unroll
+    for (int k = 0; k < RB; ++k) {
+      pos[k] = npos[k];
+      prv[k] = nprv[k];
+      raw[k] = nraw[k];
     }
   }
   const int np = p.nch + p.ncr;

@@ -84,8 +84,9 @@ def _obs_tau(rng, k, n_q):
 
 
 def make_decode_workload(cfg, seed=0, n=None, B=None, G=None, budget=None,
-                         alpha=None, with_queries=True):
-    """Draw one decode workload; optional overrides shrink it for tests.
+                         alpha=None, with_queries=True, grp=None, s=None):
+    """Draw one decode workload; optional overrides shrink or reshape it for
+    tests (``grp`` query heads per KV head, ``s`` sketch dimension).
 
     Returns a dict of numpy arrays: tau [B][G][n] f32, host_kv [B][G][n][2][d]
     bf16 bits, sketch [B][G][n][s] bf16 bits, proj [G][d][s] f32,
@@ -109,6 +110,10 @@ def make_decode_workload(cfg, seed=0, n=None, B=None, G=None, budget=None,
         p["G"] = G
     if alpha is not None:
         p["alpha"] = alpha
+    if grp is not None:  # query heads per KV head
+        p["Hq"] = p["G"] * grp
+    if s is not None:  # sketch dimension
+        p["s"] = s
     Bn, Hq, Gn, d, nn, s = p["B"], p["Hq"], p["G"], p["d"], p["n"], p["s"]
     grp = Hq // Gn
     cid = _CFG_ID[cfg]
