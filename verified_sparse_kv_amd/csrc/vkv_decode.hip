@@ -1814,7 +1814,7 @@ constexpr int kSelIt = 8;  // tokens per thread whose keys stay in registers
 // above it; and
 // those keys, written with their fixed-point beta_i, v_i and b_i. Keys below
 // lo_s are not written; their largest b_i is.
-template <int GRP>
+template <int GRP, bool KEEP>
 __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
   const int s = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
   const int row = b * p.Hq + hq, bg = b * p.G + hq / GRP;
@@ -1856,8 +1856,11 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
     t = token_terms_w(expf(si - m), ri, betaf, p.est);
     return make_key(token_gain(t, i, rs, af, lf), i);
   };
-  // ---- keys: histogram and totals
+  // ---- keys: histogram and totals (the register tokens keep their terms)
+  // (KEEP: a launch small enough to fit at the lower occupancy the extra
+  // registers cost)
   unsigned long long key8[kSelIt];
+  float bi8[KEEP ? kSelIt : 1], lw8[KEEP ? kSelIt : 1], rb8[KEEP ? kSelIt : 1];
   unsigned long long tx[2] = {0ull, 0ull};
 #pragma unroll
   for (int it = 0; it < kSelIt; ++it) {
@@ -1865,6 +1868,11 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
     if (!(r8[it] < 1.0f)) continue;
     Terms t;
     key8[it] = key_of(pos_of(it), r8[it], s8[it], t);
+    if constexpr (KEEP) {
+      bi8[it] = t.bi;
+      lw8[it] = t.lam * t.wt;
+      rb8[it] = t.rb;
+    }
     atomicAdd(&s_hist[(int)(key8[it] >> sel_off(0))], 1u);
     tx[0] += sat_fx(t.bi, capb, eb);
     tx[1] += sat_fx(t.vi, capv, ev);
@@ -1943,7 +1951,8 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
   double dsum[4] = {0.0, 0.0, 0.0, 0.0};
   uint32_t o0 = 0u, o1 = 0u;  // slots taken by earlier batches, per tier
   auto emit_batch = [&](const unsigned long long (&kb)[kSelIt],
-                        const float (&rb)[kSelIt], const float (&sb)[kSelIt]) {
+                        const float (&rb)[kSelIt], const float (&sb)[kSelIt],
+                        const float *kbi, const float *klw, const float *krb) {
     uint32_t n0 = 0u, n1 = 0u;
 #pragma unroll
     for (int k = 0; k < kSelIt; ++k) {
@@ -1961,18 +1970,27 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
       if (kb[k] >= lo0) {
         slot = a0++;
       } else {
-        const Terms t = token_terms_w(expf(sb[k] - m), rb[k], betaf, p.est);
+        // the token's float64 terms (v_i squared in float64) and b_i
         double bd, vd;
-        direct_terms(t, bd, vd);
+        float tb;
+        if (kbi) {
+          bd = (double)kbi[k];
+          vd = (double)klw[k] * (double)klw[k] * (double)((1.0f - rb[k]) / rb[k]);
+          tb = krb[k];
+        } else {
+          const Terms t = token_terms_w(expf(sb[k] - m), rb[k], betaf, p.est);
+          direct_terms(t, bd, vd);
+          tb = t.rb;
+        }
         if (kb[k] >= lo) {
           dsum[2] += bd;
           dsum[3] += vd;
-          below1 = max(below1, __float_as_uint(t.rb));
+          below1 = max(below1, __float_as_uint(tb));
           slot = a1++;
         } else {
           dsum[0] += bd;
           dsum[1] += vd;
-          below = max(below, __float_as_uint(t.rb));
+          below = max(below, __float_as_uint(tb));
           continue;
         }
       }
@@ -1985,7 +2003,10 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
     o0 += tot & 0xFFFFu;
     o1 += tot >> 16;
   };
-  emit_batch(key8, r8, s8);
+  if constexpr (KEEP)
+    emit_batch(key8, r8, s8, bi8, lw8, rb8);
+  else
+    emit_batch(key8, r8, s8, nullptr, nullptr, nullptr);
   for (int it0 = kSelIt; it0 < iters; it0 += kSelIt) {
     float rb[kSelIt], sb[kSelIt];
     unsigned long long kb[kSelIt];
@@ -1997,10 +2018,14 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
       Terms t;
       kb[k] = key_of(pos_of(it0 + k), rb[k], sb[k], t);
     }
-    emit_batch(kb, rb, sb);
+    emit_batch(kb, rb, sb, nullptr, nullptr, nullptr);
   }
-  below = blk_max<uint32_t, kBlock>(below);
-  below1 = blk_max<uint32_t, kBlock>(below1);
+  {
+    uint32_t bm[2] = {below, below1};
+    blk_combine<uint32_t, 2, kBlock, OpMax<uint32_t>>(bm);
+    below = bm[0];
+    below1 = bm[1];
+  }
   blk_reduce<double, 4, kBlock>(dsum);
   if (threadIdx.x == 0) {
     // per tier: candidates, bound, and over the tokens not written in that
@@ -2774,7 +2799,15 @@ hipError_t run(const DParams &p, hipStream_t s, int sd, void **events) {
   }
   dk_rcert<GRP><<<grow, blk, 0, s>>>(p);
   mark(k++);
-  dk_rcand<GRP><<<dim3((unsigned)p.nsel, (unsigned)p.Hq, (unsigned)p.B), blk, 0, s>>>(p);
+  {
+    // the register-heavy variant only while its grid fits in one round at
+    // three waves per SIMD (768 workgroups)
+    const dim3 gc((unsigned)p.nsel, (unsigned)p.Hq, (unsigned)p.B);
+    if ((long long)p.nsel * p.Hq * p.B <= 768)
+      dk_rcand<GRP, true><<<gc, blk, 0, s>>>(p);
+    else
+      dk_rcand<GRP, false><<<gc, blk, 0, s>>>(p);
+  }
   mark(k++);
   dk_rwalk<GRP><<<gone, dim3(kPlanThreads), 0, s>>>(p);
   mark(k++);
