@@ -40,13 +40,21 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4"])
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--estimator", default="clip",
+                    choices=["clip", "unbiased", "binary"],
+                    help="clipped shrinkage (Definition 2, the default), the "
+                         "unbiased lambda = 1 estimator, or binary shrinkage "
+                         "(Appendix A.2)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU work budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
 
 
-def algorithmic_bytes(w, counts, fetching_rows, host_bytes):
+ESTIMATORS = {"clip": 0, "unbiased": 1, "binary": 2}
+
+
+def algorithmic_bytes(w, counts, fetching_rows, host_bytes, est="clip"):
     """Compulsory HBM bytes of one step and of each HBM-bound kernel.
 
     Step: sketch + r for every (request, KV head, token), the resident K and V
@@ -57,7 +65,9 @@ def algorithmic_bytes(w, counts, fetching_rows, host_bytes):
     same launch, forms the resident logits (reads the resident K rows and
     positions, writes one logit per (query head, row)); every planning pass over the tokens (beta passes,
     certificate, candidate keys) reads the sketch logits of its rows and r of
-    their KV heads (the candidate pass only for the rows that fetch). The gather is bound by the host link and
+    their KV heads (the candidate pass only for the rows that fetch; binary
+    shrinkage adds one workgroup per row that reads them twice: a digit
+    histogram and the gather of the top keys). The gather is bound by the host link and
     reported separately (it runs in one launch with the attention over the
     resident rows, which hides behind it); the resolve and walk steps touch
     only per-row summaries. The gather workgroups also form the attention
@@ -72,6 +82,8 @@ def algorithmic_bytes(w, counts, fetching_rows, host_bytes):
     per = {"scan": B * G * n * (2 * s + 4) + B * Hq * n * 4
            + rows * (2 * d + 4) + rows * grp * 4,
            "beta1": tok, "cert": tok, "cand": ftok}
+    if est == "binary":
+        per["shrink"] = 2 * tok
     return dict(step=B * G * n * (2 * s + 4) + rows * (4 * d + 4)
                 + B * Hq * d * (2 + 4), kernels=per)
 
@@ -82,12 +94,12 @@ DECODE_SOURCES = ("verified_sparse_kv_amd/csrc/vkv_decode.hip",
                   "verified_sparse_kv_amd/csrc/vkv_internal.h")
 
 
-def measured_traffic(config, kernel):
+def measured_traffic(config, kernel, estimator="clip"):
     """HBM bytes per launch of `kernel` from the committed FETCH_SIZE /
     WRITE_SIZE counter summary, or None when there is none for this workload
     or the decode sources changed since the counters were taken."""
     import hashlib
-    if config != "c2" or not os.path.exists(TRAFFIC_FILE):
+    if config != "c2" or not os.path.exists(TRAFFIC_FILE) or estimator != "clip":
         return None
     vals, want = {}, None
     for line in open(TRAFFIC_FILE):
@@ -107,7 +119,7 @@ def measured_traffic(config, kernel):
     return vals.get(kernel)
 
 
-def cpu_baseline(w, seconds):
+def cpu_baseline(w, seconds, est=0):
     """The oracle (never tuned) decoding KV-head groups of the same layer until
     `seconds` of CPU work have been spent."""
     import numpy as np
@@ -138,7 +150,7 @@ def cpu_baseline(w, seconds):
                         [b, g * grp:(g + 1) * grp])
         t0 = time.perf_counter()
         od.decode_group(q, res_kv, idx, sk, w["proj"][g], r, kv, w["eps"],
-                        w["delta"])
+                        w["delta"], est)
         spent += time.perf_counter() - t0
         units += grp * n
         groups += 1
@@ -207,7 +219,7 @@ def main():
     step = vk.DecodeStep(B, Hq, G, n, s, cap, n, dev)
     step.bind(t_qs[0], comp["resident_kv"], comp["resident_idx"],
               comp["resident_count"], sketch, proj, comp["r"], host_kv,
-              w["eps"], w["delta"])
+              w["eps"], w["delta"], ESTIMATORS[args.estimator])
     names = vk.decode_phase_names()
     P = len(names)
 
@@ -239,7 +251,7 @@ def main():
     out = step.out
     ks = out["k_star"].cpu().numpy()
     ab = algorithmic_bytes(w, counts, int(np.sum(ks > 0)),
-                           int(out["host_bytes"][0]))
+                           int(out["host_bytes"][0]), args.estimator)
     cand = ab["kernels"]
     dom = max(cand, key=lambda k: ph_us[names.index(k)])
     di = names.index(dom)
@@ -297,7 +309,8 @@ def main():
             "batch": B, "q_heads": Hq, "kv_heads": G, "head_dim": d,
             "ctx_tokens": n, "budget": w["budget"], "sketch_dim": s,
             "n_sink": w["n_sink"], "n_local": w["n_local"], "eps": w["eps"],
-            "delta": w["delta"], "parallelism": "none (1 GPU)"},
+            "delta": w["delta"], "estimator": args.estimator,
+            "parallelism": "none (1 GPU)"},
         "steps_per_s": 1e3 / ms,
         "hbm_peak_pct": 100.0 * ab["step"] / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "fetch_pct": fetch_pct,
@@ -316,11 +329,13 @@ def main():
                      "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(args.config, dom),
+                     "traffic": measured_traffic(args.config, dom,
+                                                 args.estimator),
                      "algorithmic_bytes": cand[dom]},
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds,
+                                           ESTIMATORS[args.estimator])
     print(json.dumps(res), flush=True)
 
 

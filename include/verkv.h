@@ -59,9 +59,13 @@ typedef enum {
 #define VKV_STATUS_BAD_RESIDENT 0x8u      /* decode: resident list malformed, */
                                           /* or a token with r = 1 missing   */
 
-/* Estimators for the L part (Definition 2): clipped shrinkage, or the
- * unbiased lambda = 1 estimator (the PoissonComp-only baseline). */
-enum { VKV_EST_CLIP = 0, VKV_EST_UNBIASED = 1 };
+/* Estimators for the L part: clipped shrinkage (Definition 2, eq. 5), the
+ * unbiased lambda = 1 estimator (the PoissonComp-only baseline), or binary
+ * shrinkage (Appendix A.2, Figure 2): lambda_i in {1, r_i}, with the tokens
+ * of L taken by w~ (1 - r) / r descending (ties: position ascending) and set
+ * to lambda = r while that value exceeds twice the bias w~ (1 - r) of the
+ * tokens set before them. */
+enum { VKV_EST_CLIP = 0, VKV_EST_UNBIASED = 1, VKV_EST_BINARY = 2 };
 /* Planning weights on L: from the key sketch (what a deployment does), or
  * the exact weights (the "perfect sketch" of section 4.2; reads every key of
  * L from host memory, so it is a slow test mode). */
@@ -133,8 +137,8 @@ typedef struct {
  *              (hipHostMalloc); rows chosen for fetching are read from it.
  * eps, delta   tolerance (eps > 0, 0 < delta < 1) of the (eps, delta)
  *              guarantee on the attention denominator.
- * estimator    VKV_EST_CLIP or VKV_EST_UNBIASED; weights VKV_W_SKETCH or
- *              VKV_W_PERFECT.
+ * estimator    VKV_EST_CLIP, VKV_EST_UNBIASED or VKV_EST_BINARY; weights
+ *              VKV_W_SKETCH or VKV_W_PERFECT.
  * fetch_cap    most rows read from host_kv per (request, KV head) (1..n); rows
  *              of a larger union are neither listed nor read, and the status
  *              word gets VKV_STATUS_FETCH_OVERFLOW.
@@ -145,7 +149,8 @@ typedef struct {
  * (the union over its query heads, minus S); fetch_count [B][G] i32 (true
  * count, see VKV_STATUS_FETCH_OVERFLOW); host_bytes u64 [1] bytes read from
  * host_kv this step; row_stats (may be NULL) [B][Hq][8] f64 =
- * {m, D~ (scaled by exp(-m)), beta*, beta(L), V(L), b(L), eps^(L), eps^(L')}.
+ * {m, D~ (scaled by exp(-m)), beta*, beta(L), V(L), b(L), eps^(L), eps^(L')}
+ * (with VKV_EST_BINARY, beta* is the bias of the tokens set to lambda = r).
  * status   dev u32 [1], cleared at the start of the call.
  * phase_events  optional timing hook: NULL, or vkv_decode_phase_count() + 1
  *          hipEvent_t handles (created by the caller); event 0 is recorded on

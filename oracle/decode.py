@@ -15,6 +15,10 @@ oracle computes, in float64, in the order of Algorithm 2:
    lambda_i(beta) = clip_[r_i,1](beta r_i / (w~_i (1 - r_i))); bisection in
    float64 (reading R8; Theorem 1 makes it the unique minimiser of eq. 6).
 4. Lemma 1 / eq. 7: beta(L), V(L), b(L) and the certificate eps^(L).
+   With the binary estimator of Appendix A.2 the coefficients are instead
+   lambda_i in {1, r_i}: L is visited in decreasing w~_i (1 - r_i) / r_i
+   and a token moves to lambda_i = r_i while that value exceeds twice the
+   bias already accumulated.
 5. If eps^(L) < eps: no fetch (reading R10: strict).
 6. Otherwise gains g_i = eps^(L) - eps^(L \\ {i}) (eq. 9) in the
    cancellation-free closed form (reading R11), order L by (g desc,
@@ -32,6 +36,7 @@ import numpy as np
 
 EST_CLIP = 0
 EST_UNBIASED = 1
+EST_BINARY = 2
 W_SKETCH = 0
 W_PERFECT = 1
 
@@ -84,6 +89,34 @@ def shrinkage_beta(w, r, max_iter=200):
         if hi - lo <= 2.0 ** -52 * hi:
             break
     return 0.5 * (lo + hi)
+
+
+def binary_lambdas(w, r, pos):
+    """Binary shrinkage (Appendix A.2, Figure 2): lambda_i in {1, r_i}.
+
+    Moving token i from lambda_i = 1 to r_i adds the bias a_i = w_i (1 - r_i)
+    and changes the MSE (eq. 6) by a_i (2 beta - w_i (1 - r_i) / r_i), beta
+    being the bias of the tokens moved before it. Tokens are visited by
+    kappa_i = w_i (1 - r_i) / r_i descending, ties by ascending position
+    (reading: the order of equal kappa is left open; positions make it
+    unique, as for the gain order), and moved while kappa_i > 2 beta
+    (strict: a move that leaves the MSE unchanged is not made). Along the
+    order kappa falls and beta grows, so the first token that fails ends the
+    moves. Returns (lambda, beta, number moved).
+    """
+    w = np.asarray(w, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    kappa = w * (1.0 - r) / r
+    lam = np.ones_like(w)
+    beta = 0.0
+    moved = 0
+    for i in np.lexsort((np.asarray(pos), -kappa)):
+        if not kappa[i] > 2.0 * beta:
+            break
+        lam[i] = r[i]
+        beta += w[i] * (1.0 - r[i])
+        moved += 1
+    return lam, beta, moved
 
 
 def mse(lam, w, r):
@@ -202,13 +235,16 @@ def plan_row(wt, r, pos, dnorm, eps, delta, estimator=EST_CLIP):
     if estimator == EST_CLIP:
         beta_star = shrinkage_beta(wt, r)
         lam = lambdas(wt, r, beta_star)
+    elif estimator == EST_BINARY:
+        lam, beta_star, _ = binary_lambdas(wt, r, pos)
     else:
         beta_star = 0.0
         lam = np.ones_like(wt)
     beta_i, v_i, b_i = cert_terms(wt, r, lam)
     b1 = float(b_i.max()) if b_i.size else 0.0
     e0 = float(eps_hat(beta_i.sum(), v_i.sum(), b1, dnorm, delta))
-    out = dict(beta_star=beta_star, lam=lam, beta_i=beta_i, v_i=v_i, b_i=b_i,
+    out = dict(beta_star=beta_star, lam=lam, wt=wt, beta_i=beta_i, v_i=v_i,
+               b_i=b_i,
                beta_L=float(beta_i.sum()), V_L=float(v_i.sum()), b_L=b1,
                eps_hat0=e0)
     if e0 < eps:

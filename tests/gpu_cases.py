@@ -47,10 +47,14 @@ def torch_mod():
     return torch
 
 
-def build_case(cfg, seed=0, cap_slack=64, shift_from=None, cap=None, **kw):
+def build_case(cfg, seed=0, cap_slack=64, shift_from=None, cap=None,
+               mutate=None, **kw):
     """Workload + oracle compression (decode inputs shared by both sides).
-    The resident capacity is the largest count plus `cap_slack`, or `cap`."""
+    The resident capacity is the largest count plus `cap_slack`, or `cap`.
+    `mutate(w)` may edit the generated arrays before compression."""
     w = make_decode_workload(cfg, seed=seed, with_queries=True, **kw)
+    if mutate is not None:
+        mutate(w)
     if shift_from is not None:
         w["shift_from"] = shift_from
     B, G = w["B"], w["G"]
@@ -129,6 +133,27 @@ def _rel(a, b):
     return abs(a - b) / max(abs(b), 1e-300)
 
 
+def binary_tie(w, b, h, hd, beta_gpu):
+    """Binary shrinkage: the library moved a different number of tokens than
+    the oracle. Accepted as a tie when every token whose decision differs is
+    a near tie of the stopping test in the oracle's own numbers,
+    |kappa - 2 beta| <= 1e-5 kappa (the library decides on fp32 weights)."""
+    g = h // (w["Hq"] // w["G"])
+    lpos = hd["lpos"]
+    r = w["r_all"][b, g][lpos].astype(np.float64)
+    wt = hd["wt"]
+    kappa = wt * (1.0 - r) / r
+    order = np.lexsort((lpos, -kappa))
+    pre = np.concatenate([[0.0], np.cumsum((wt * (1.0 - r))[order])])
+    ko = int(np.sum(hd["lam"] != 1.0))
+    kg = int(np.argmin(np.abs(pre - beta_gpu)))
+    if abs(pre[kg] - beta_gpu) > TOL_BETA * max(beta_gpu, 1e-300):
+        return False
+    ks = np.arange(min(ko, kg), max(ko, kg))
+    kap = kappa[order][ks]
+    return bool(ks.size) and bool(np.all(np.abs(kap - 2.0 * pre[ks]) <= TIE * kap))
+
+
 def compare(w, gpu, heads, unions, eps, est=0, max_tie_frac=0.01):
     """Apply the parity rules; returns a summary dict. Every violation is
     collected and reported together."""
@@ -155,6 +180,18 @@ def compare(w, gpu, heads, unions, eps, est=0, max_tie_frac=0.01):
                 check("beta", _rel(st[2], hd["beta_star"]), TOL_BETA, where)
                 check("fixed_point", abs(st[3] - st[2]) / st[1], TOL_FIXED_POINT,
                       where)
+            if est == od.EST_BINARY:
+                # the moved tokens' bias; beta(L) from the certificate pass
+                # must be the same sum (both passes apply one rule)
+                check("fixed_point", abs(st[3] - st[2]) / st[1], TOL_FIXED_POINT,
+                      where)
+                bo = hd["beta_star"]
+                eb = 0.0 if bo == st[2] == 0.0 else _rel(st[2], bo)
+                if not eb <= TOL_BETA and binary_tie(w, b, h, hd, float(st[2])):
+                    ties += 1
+                    tie_rows.add((b, h))
+                    continue
+                check("beta", eb, TOL_BETA, where)
             check("eps0", _rel(float(gpu["eps_hat0"][b, h]), hd["eps_hat0"]),
                   TOL_EPS, where)
             kg, ko = int(gpu["k_star"][b, h]), hd["k_star"]

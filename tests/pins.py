@@ -137,6 +137,49 @@ def check_kkt(w, r):
     assert m <= od_mse_plain(r, w, r) * (1 + 1e-12)
 
 
+def check_binary_prefix(w, r, pos=None):
+    """Binary shrinkage (Appendix A.2, Figure 2), in exact rationals: the
+    moved tokens (lambda = r) are a prefix of the order by w (1 - r) / r
+    descending (positions ascending on ties); that prefix is the first
+    minimum of the MSE (eq. 6) over every prefix of the order; each move
+    changes the MSE by a_i (2 beta - w_i (1 - r_i) / r_i) with a_i =
+    w_i (1 - r_i) and beta the bias before it; and the result lies between
+    the clipped minimiser of Theorem 1 and the two endpoints lambda = 1 and
+    lambda = r."""
+    n = len(w)
+    pos = np.arange(n) if pos is None else np.asarray(pos)
+    lam, beta, moved = od.binary_lambdas(w, r, pos)
+    W = [Fraction(float(x)) for x in w]
+    R = [Fraction(float(x)) for x in r]
+    kap = [W[i] * (1 - R[i]) / R[i] for i in range(n)]
+    order = sorted(range(n), key=lambda i: (-kap[i], int(pos[i])))
+
+    def mse_of(k):
+        S = set(order[:k])
+        bias = sum((W[i] * (1 - R[i]) for i in S), Fraction(0))
+        var = sum(((R[i] if i in S else 1) ** 2 * W[i] ** 2 * (1 - R[i]) / R[i]
+                   for i in range(n)), Fraction(0))
+        return bias * bias + var
+
+    curve = [mse_of(k) for k in range(n + 1)]
+    best = min(curve)
+    assert moved == curve.index(best), (moved, curve.index(best))
+    assert sorted(np.nonzero(lam != 1.0)[0].tolist()) == sorted(order[:moved])
+    assert np.all(lam[order[:moved]] == np.asarray(r, np.float64)[order[:moved]])
+    bias = Fraction(0)
+    for k, i in enumerate(order):
+        a = W[i] * (1 - R[i])
+        assert curve[k + 1] - curve[k] == a * (2 * bias - kap[i])
+        bias += a
+    assert abs(beta - float(sum((W[i] * (1 - R[i]) for i in order[:moved]),
+                                Fraction(0)))) <= 1e-12 * max(beta, 1e-300)
+    m_bin = od_mse_plain(lam, w, r)
+    assert m_bin <= od_mse_plain(np.ones(n), w, r) * (1 + 1e-12)
+    assert m_bin <= od_mse_plain(np.asarray(r, np.float64), w, r) * (1 + 1e-12)
+    lam_c = od.lambdas(w, r, od.shrinkage_beta(w, r))
+    assert od_mse_plain(lam_c, w, r) <= m_bin * (1 + 1e-12)
+
+
 # ---------------------------------------------------------------- certificate
 def check_bernstein_root(V, b, delta):
     """Lemma 1's proof: t = D * (eps^ - beta/D) is the positive root of

@@ -148,6 +148,45 @@ def test_decode_c1_unbiased(weights):
     gc.say(f"  {s}")
 
 
+@pytest.mark.parametrize("weights", [0, 1])
+def test_decode_c1_binary(weights):
+    w, gpu, heads, unions, eps = _decode_case("c1", est=2, weights=weights)
+    s = gc.compare(w, gpu, heads, unions, eps, est=2)
+    gc.say(f"  {s}")
+    assert s["ties"] == 0
+
+
+@pytest.mark.parametrize("cfg,kw", [
+    ("c2", dict(n=5000, G=2)),
+    ("c3", dict(n=6000, G=2, B=4, seed=1, shift_from=2)),
+    ("c4", dict(n=20000, G=2, B=2)),
+])
+def test_decode_binary_reduced(cfg, kw):
+    """Binary shrinkage (lambda in {1, r}) on reduced shapes of each layer."""
+    w, gpu, heads, unions, eps = _decode_case(cfg, est=2, **kw)
+    s = gc.compare(w, gpu, heads, unions, eps, est=2)
+    gc.say(f"  {s}")
+    assert s["fetched"] > 0
+
+
+def _uniform_planning(w):
+    # every sketch row of a KV head equal and tau constant: every token of L
+    # has the same planning weight and inclusion probability, so the binary
+    # order and the gain order are decided by position alone
+    w["sketch"][...] = w["sketch"][:, :, :1, :]
+    w["tau"][...] = np.float32(0.5)
+
+
+@pytest.mark.parametrize("est", [0, 2])
+def test_decode_uniform_planning_weights(est):
+    """The degenerate case of all-equal keys of the order: positions break
+    every tie, on both sides."""
+    w, gpu, heads, unions, eps = _decode_case("c2", est=est, n=3000, G=1,
+                                              mutate=_uniform_planning)
+    s = gc.compare(w, gpu, heads, unions, eps, est=est)
+    gc.say(f"  {s}")
+
+
 def test_decode_c2_reduced():
     w, gpu, heads, unions, eps = _decode_case("c2", n=5000, G=2)
     s = gc.compare(w, gpu, heads, unions, eps)
@@ -178,6 +217,18 @@ def test_decode_full_size(cfg):
     w, gpu, heads, unions, eps = _decode_case(
         cfg, cap=resident_cap(p["budget"]), **kw)
     s = gc.compare(w, gpu, heads, unions, eps)
+    gc.say(f"  {s}")
+    assert s["fetched"] > 0
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg", ["c2", "c4"])
+def test_decode_binary_full_size(cfg):
+    """Binary shrinkage at full size, in the benchmark's launch shapes."""
+    p = CONFIGS[cfg]
+    w, gpu, heads, unions, eps = _decode_case(
+        cfg, est=2, cap=resident_cap(p["budget"]))
+    s = gc.compare(w, gpu, heads, unions, eps, est=2)
     gc.say(f"  {s}")
     assert s["fetched"] > 0
 

@@ -74,6 +74,48 @@ def test_shrinkage_heavy_tokens(seed):
     pins.check_range_bound(w, r)
 
 
+def test_binary_golden():
+    with open(os.path.join(GOLDEN, "binary_small.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        w, r = np.array(c["w"], float), np.array(c["r"], float)
+        lam, beta, moved = od.binary_lambdas(w, r, np.array(c["pos"]))
+        assert lam.tolist() == c["lam"]
+        assert (beta, moved) == (c["beta"], c["moved"])
+        assert od.mse(lam, w, r) == c["mse"]
+        assert od.mse(np.ones_like(r), w, r) == c["mse_unbiased"]
+        pins.check_binary_prefix(w, r, np.array(c["pos"]))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_binary_is_prefix_minimum(seed):
+    rng = np.random.default_rng(300 + seed)
+    n = int(rng.integers(1, 40))
+    w, r = _rand_lr(rng, n) if seed % 2 else _heavy(rng, n)
+    pins.check_binary_prefix(w, r, rng.permutation(n))
+
+
+def test_binary_equal_tokens_closed_form():
+    """n equal tokens with r = 1/m: token k (1-based) moves iff
+    (1 - r)/r > 2 (k - 1)(1 - r), i.e. k - 1 < m / 2, so min(n, ceil(m / 2))
+    move (exact in binary floating point for m a power of two)."""
+    for m in (2, 4, 8, 16, 64):
+        for n in (1, 3, 40):
+            w = np.full(n, 0.75)
+            r = np.full(n, 1.0 / m)
+            lam, beta, moved = od.binary_lambdas(w, r, np.arange(n))
+            assert moved == min(n, math.ceil(m / 2))
+            assert np.all(lam[:moved] == 1.0 / m) and np.all(lam[moved:] == 1.0)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_binary_exact_enumeration(seed):
+    rng = np.random.default_rng(400 + seed)
+    w, r = _heavy(rng, 10)
+    pins.check_enumeration(np.exp(rng.normal(0, 1, 3)), w, r, 0.1,
+                           od.EST_BINARY)
+
+
 @pytest.mark.parametrize("seed", range(6))
 def test_kkt_large(seed):
     rng = np.random.default_rng(200 + seed)

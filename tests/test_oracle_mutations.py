@@ -54,7 +54,18 @@ def run_pins():
     tau = rng.beta(0.5, 5, size=3000).astype(np.float32)
     attempt("rates", lambda: pins.check_rates_sum(tau, 300, 4, 16))
     attempt("golden_wf", _golden_wf)
+    wb, rb = _w_r(10, 30)
+    attempt("binary", lambda: pins.check_binary_prefix(wb, rb))
+    attempt("binary_heavy", lambda: pins.check_binary_prefix(*_heavy(11, 30)))
+    attempt("golden_binary", _golden_binary)
     return failed
+
+
+def _golden_binary():
+    # ten equal tokens with r = 1/8: four move, the fifth is an exact tie
+    lam, beta, moved = od.binary_lambdas(np.ones(10), np.full(10, 0.125),
+                                         np.arange(10))
+    assert (moved, beta) == (4, 3.5)
 
 
 def _heavy(seed, n):
@@ -165,6 +176,29 @@ def _beta_upper(w, r, max_iter=200):
     return float(np.sum(w * (1.0 - r)))
 
 
+def _binary_variant(key, stop, add):
+    """binary_lambdas with the order key, stop test or bias term replaced."""
+    def f(w, r, pos):
+        w = np.asarray(w, np.float64)
+        r = np.asarray(r, np.float64)
+        kappa = key(w, r)
+        lam = np.ones_like(w)
+        beta = 0.0
+        moved = 0
+        for i in np.lexsort((np.asarray(pos), -kappa)):
+            if not stop(kappa[i], beta):
+                break
+            lam[i] = r[i]
+            beta += add(w[i], r[i])
+            moved += 1
+        return lam, beta, moved
+    return f
+
+
+_bin_ok_key = lambda w, r: w * (1 - r) / r
+_bin_ok_stop = lambda k, b: k > 2 * b
+_bin_ok_add = lambda w, r: w * (1 - r)
+
 _orig_wl = oc.water_level
 _orig_rates = oc.rates
 
@@ -181,6 +215,16 @@ MUTATIONS = [
     ("water level one saturated token short", oc, "water_level", _wl_offbyone),
     ("exact saturation left in L", oc, "rates", _rates_strict),
     ("beta* is the bracket's upper end", od, "shrinkage_beta", _beta_upper),
+    ("binary order ascending", od, "binary_lambdas",
+     _binary_variant(lambda w, r: -w * (1 - r) / r, _bin_ok_stop, _bin_ok_add)),
+    ("binary order by w / r", od, "binary_lambdas",
+     _binary_variant(lambda w, r: w / r, _bin_ok_stop, _bin_ok_add)),
+    ("binary stop compares with beta, not 2 beta", od, "binary_lambdas",
+     _binary_variant(_bin_ok_key, lambda k, b: k > b, _bin_ok_add)),
+    ("binary stop not strict", od, "binary_lambdas",
+     _binary_variant(_bin_ok_key, lambda k, b: k >= 2 * b, _bin_ok_add)),
+    ("binary bias accumulates w", od, "binary_lambdas",
+     _binary_variant(_bin_ok_key, _bin_ok_stop, lambda w, r: w)),
 ]
 
 

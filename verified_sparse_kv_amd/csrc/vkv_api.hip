@@ -125,7 +125,8 @@ vkv_status vkv_decode_step(const vkv_decode_args *a, void *stream) {
   if (st != VKV_OK) return st;
   REQUIRE(a->eps > 0.0f && isfinite(a->eps), "decode: eps must be > 0");
   REQUIRE(a->delta > 0.0f && a->delta < 1.0f, "decode: delta must be in (0, 1)");
-  REQUIRE(a->estimator == VKV_EST_CLIP || a->estimator == VKV_EST_UNBIASED,
+  REQUIRE(a->estimator == VKV_EST_CLIP || a->estimator == VKV_EST_UNBIASED ||
+              a->estimator == VKV_EST_BINARY,
           "decode: unknown estimator %d", a->estimator);
   REQUIRE(a->weights == VKV_W_SKETCH || a->weights == VKV_W_PERFECT,
           "decode: unknown weights mode %d", a->weights);

@@ -63,6 +63,7 @@ struct RowState {
   double capb, capv;      // caps of beta_i and v_i in the fixed-point sums
   int32_t kstar;
   unsigned long long T;   // F_h = {i in L : key_i >= T}
+  unsigned long long bkey;  // binary shrinkage: lambda = r for keys >= bkey
   float eps1;             // eps^(L') after fetching
 };
 
@@ -74,6 +75,13 @@ struct BetaState {
   double beta;          // beta* once done
   double dnorm;         // D~ * exp(-m)
   int32_t done, pad;
+};
+
+// Binary shrinkage of a row (Appendix A.2): the tokens whose binary key is
+// at least `key` have lambda = r; `beta` is their bias sum w~ (1 - r).
+struct BinState {
+  unsigned long long key;  // ~0: no token moved
+  double beta;
 };
 
 // Certificate terms of one chunk of a row.
@@ -109,6 +117,7 @@ struct DParams {
   float2 *band;      // [2][row][nrc][kBandChunk] (w~, rho) of band tokens
   BetaState *bstate; // [2][row]
   double *rbeta;     // [row][2] beta*, D~
+  BinState *binst;   // [row] binary shrinkage: last moved key, its bias
   CertPart *cpart;   // [row][nrc]
   // candidate workgroups: [row][kSelWG] counts, local bounds, max b_i of
   // the keys not written, fixed-point totals; candidates [row][kCandMax]
@@ -132,21 +141,58 @@ struct Terms {
   float wt, lam, bi, vi, rb, qr;  // qr = (1 - r) / r
 };
 
-// lambda (Definition 2) and the three certificate terms of Lemma 1 for one
-// token of L with planning weight wt.
-__device__ __forceinline__ Terms token_terms_w(float wt, float r, float beta,
-                                               int est) {
+// Descending key order = value descending, then position ascending (the
+// gain order of eq. 10 and the binary-shrinkage order of Appendix A.2).
+__device__ __forceinline__ unsigned long long make_key(float v, int pos) {
+  return ((unsigned long long)__float_as_uint(v) << 24) |
+         (unsigned long long)(0xFFFFFFu - (uint32_t)pos);
+}
+__device__ __forceinline__ int key_pos(unsigned long long key) {
+  return (int)(0xFFFFFFu - (uint32_t)(key & 0xFFFFFFull));
+}
+// Binary-shrinkage key of a token of L: kappa = w~ (1 - r) / r (qr =
+// (1 - r) / r), clamped to >= 0 so that malformed r cannot leave the key
+// range.
+__device__ __forceinline__ unsigned long long bin_key(float wt, float qr, int pos) {
+  return make_key(fmaxf(wt * qr, 0.0f), pos);
+}
+
+// How lambda is formed: the clipped fixed point at beta (Definition 2), the
+// binary rule of Appendix A.2 (lambda = r for the tokens whose binary key
+// is at least bkey, 1 for the rest), or 1 (the unbiased estimator).
+struct LamRule {
+  float beta;
+  int est;
+  unsigned long long bkey;
+};
+__device__ __forceinline__ LamRule lam_rule(float beta, int est,
+                                            unsigned long long bkey) {
+  LamRule q;
+  q.beta = beta;
+  q.est = est;
+  q.bkey = bkey;
+  return q;
+}
+
+// lambda and the three certificate terms of Lemma 1 for the token of L at
+// `pos` with planning weight wt.
+__device__ __forceinline__ Terms token_terms_w(float wt, float r,
+                                               const LamRule &lr, int pos) {
   Terms t;
   t.wt = wt;
+  t.qr = (1.0f - r) / r;
   float lam = 1.0f;
-  if (est == VKV_EST_CLIP && wt > 0.0f) {
-    const float x = beta * r / (wt * (1.0f - r));
-    lam = fminf(1.0f, fmaxf(r, x));
+  if (lr.est == VKV_EST_CLIP) {
+    if (wt > 0.0f) {
+      const float x = lr.beta * r / (wt * (1.0f - r));
+      lam = fminf(1.0f, fmaxf(r, x));
+    }
+  } else if (lr.est == VKV_EST_BINARY) {
+    if (bin_key(wt, t.qr, pos) >= lr.bkey) lam = r;
   }
   t.lam = lam;
   t.bi = wt * (1.0f - lam);
   const float lw = lam * wt;
-  t.qr = (1.0f - r) / r;
   t.vi = lw * lw * t.qr;
   t.rb = lw * fmaxf(r, 1.0f - r) / r;
   return t;
@@ -164,8 +210,8 @@ __device__ __forceinline__ void direct_terms(const Terms &t, double &bd,
 
 // The same from the planning logit s and the shift m (w~ = exp(s - m)).
 __device__ __forceinline__ Terms token_terms(float s, float r, float m,
-                                             float beta, int est) {
-  return token_terms_w(expf(s - m), r, beta, est);
+                                             const LamRule &lr, int pos) {
+  return token_terms_w(expf(s - m), r, lr, pos);
 }
 
 // eq. 7 in float64.
@@ -192,12 +238,6 @@ __device__ __forceinline__ float token_gain(const Terms &t, int pos,
   const float den = rs.s_full_f + sp;
   const float frac = den > 0.0f ? num / den : 0.0f;
   return t.bi + a * (b1 - bp) + frac;
-}
-
-// Descending key order = gain descending, then position ascending.
-__device__ __forceinline__ unsigned long long make_key(float gain, int pos) {
-  return ((unsigned long long)__float_as_uint(gain) << 24) |
-         (unsigned long long)(0xFFFFFFu - (uint32_t)pos);
 }
 
 __device__ __forceinline__ unsigned long long to_fx(float x, int e) {
@@ -978,7 +1018,7 @@ __device__ __attribute__((noinline)) void select_row(const SelArgs p, int row,
   const float *rr = p.r + (size_t)bg * n;
   const float *sh = p.shat + (size_t)row * n;
   const float m = rs.m;
-  const float betaf = (float)rs.beta;
+  const LamRule lr = lam_rule((float)rs.beta, p.est, rs.bkey);
   const float af = (float)p.a_delta, lf = (float)p.l_delta;
   const double a = p.a_delta, l = p.l_delta;
   const int eb = rs.eb, ev = rs.ev;
@@ -1005,7 +1045,7 @@ __device__ __attribute__((noinline)) void select_row(const SelArgs p, int row,
         Terms t{};
         unsigned long long key = 0ull;
         if (valid) {
-          t = token_terms_w(expf(s8[u] - m), r8[u], betaf, p.est);
+          t = token_terms_w(expf(s8[u] - m), r8[u], lr, i);
           key = make_key(token_gain(t, i, rs, af, lf), i);
         }
         g(i, valid, key, t);
@@ -1651,6 +1691,208 @@ __global__ __launch_bounds__(kBlock) void dk_rbeta(DParams p, int pass) {
   }
 }
 
+// ------------------------------------------------------------ binary shrinkage
+// Appendix A.2: lambda_i in {1, r_i}. The tokens of L are visited by binary
+// key (kappa = w~ (1 - r) / r descending, then position ascending) and
+// moved to lambda = r while kappa exceeds twice the bias w~ (1 - r) of the
+// tokens moved before them. Kappa falls and the bias grows along the order,
+// so the first token that fails ends the moves, and only the top of the
+// order matters (tens of tokens move in the workloads measured). One
+// 1024-thread workgroup per row takes the keys in rounds of at most kBinCap,
+// largest first: count histograms of 11-bit key digits give the round's
+// lower key bound (a second digit only while the round would hold fewer
+// than kBinCap / 4 keys), the round's keys and biases are gathered into
+// LDS and sorted, and float64 prefix sums of the biases in that order, in a
+// fixed tree order, find the first token that stops the moves. A round that
+// moves all of its tokens passes its bias total on to the next. The result
+// is the key of the last token moved (~0 for none) and the moved tokens'
+// bias; every later pass recomputes lambda from it.
+constexpr int kBinCap = 2048;
+
+template <int GRP>
+__global__ __launch_bounds__(kPlanThreads) void dk_rbin(DParams p) {
+  const int hq = blockIdx.x, b = blockIdx.y;
+  const int row = b * p.Hq + hq, bg = b * p.G + hq / GRP;
+  const int n = p.n;
+  const float *rr = p.r + (size_t)bg * n;
+  const float *sh = p.shat + (size_t)row * n;
+  const float m = p.rows[row].m;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  __shared__ uint32_t s_hist[kSelBinsP];
+  __shared__ unsigned long long s_key[kBinCap];
+  __shared__ float s_a[kBinCap];
+  __shared__ double s_wsum[kPlanWaves];
+  __shared__ unsigned long long s_pre, s_lo;
+  __shared__ uint32_t s_room, s_cnt;
+  __shared__ int s_more, s_stop;
+  __shared__ double s_excl;
+
+  // f(binary key, bias w~ (1 - r)) for this thread's tokens of L
+  auto stream = [&](auto &&f) {
+    constexpr int U = 8;
+    for (int base = 0; base < n; base += U * kPlanThreads) {
+      float ru[U], su[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = base + u * kPlanThreads + (int)threadIdx.x;
+        ru[u] = i < n ? rr[i] : 1.0f;
+        su[u] = i < n ? sh[i] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (!(ru[u] < 1.0f)) continue;
+        const float wt = expf(su[u] - m);
+        const float qr = (1.0f - ru[u]) / ru[u];
+        f(bin_key(wt, qr, base + u * kPlanThreads + (int)threadIdx.x),
+          wt * (1.0f - ru[u]));
+      }
+    }
+  };
+
+  unsigned long long hi = kKeyEnd;  // the keys at or above hi are decided
+  unsigned long long last = ~0ull;  // key of the last token moved
+  double beta = 0.0;                // bias of the tokens moved
+  for (;;) {
+    // ---- the round's lower key bound, digit by digit from the top
+    if (threadIdx.x == 0) {
+      s_pre = 0ull;
+      s_room = (uint32_t)kBinCap;
+    }
+    unsigned long long lo = 0ull;
+    for (int d = 0; d < kSelLevels; ++d) {
+      const int off = sel_off(d);
+      for (int k = threadIdx.x; k < kSelBinsP; k += kPlanThreads) s_hist[k] = 0u;
+      __syncthreads();
+      const unsigned long long pre = s_pre;
+      stream([&](unsigned long long key, float) {
+        if (key < hi && (key >> (off + kSelDigit)) == pre)
+          atomicAdd(&s_hist[(int)((key >> off) & (kSelBinsP - 1))], 1u);
+      });
+      __syncthreads();
+      if (wave == 0) {
+        // j0 = the smallest bin j whose keys and those of the bins above it
+        // fit in the room left; cnt = their number
+        constexpr int per = kSelBinsP / kWave;
+        const uint32_t room = s_room;
+        uint32_t tot = 0u;
+        for (int k = 0; k < per; ++k) tot += s_hist[lane * per + k];
+        const uint32_t incl = wave_incl_scan<uint32_t>(tot, lane);
+        uint32_t cum = __shfl(incl, kWave - 1, kWave) - incl;  // bins above
+        int jf = kSelBinsP;
+        for (int k = per - 1; k >= 0; --k) {
+          cum += s_hist[lane * per + k];
+          if (cum > room) break;
+          jf = lane * per + k;
+        }
+        const int j0 = -wave_max<int>(-jf);
+        uint32_t part = 0u;
+        for (int k = 0; k < per; ++k)
+          if (lane * per + k >= j0) part += s_hist[lane * per + k];
+        const uint32_t cnt = wave_sum<uint32_t>(part);
+        if (lane == 0) {
+          const bool more = j0 > 0 && cnt < (uint32_t)(kBinCap / 4) &&
+                            d + 1 < kSelLevels;
+          if (more) {
+            s_pre = (pre << kSelDigit) | (unsigned long long)(j0 - 1);
+            s_room = room - cnt;
+          } else {
+            s_lo = ((pre << kSelDigit) | (unsigned long long)j0) << off;
+          }
+          s_more = more ? 1 : 0;
+        }
+      }
+      __syncthreads();
+      if (!s_more) {
+        lo = s_lo;
+        break;
+      }
+    }
+    // ---- gather the round's keys [lo, hi) and sort them, descending
+    if (threadIdx.x == 0) s_cnt = 0u;
+    __syncthreads();
+    stream([&](unsigned long long key, float a) {
+      if (key >= lo && key < hi) {
+        const uint32_t slot = atomicAdd(&s_cnt, 1u);
+        if (slot < (uint32_t)kBinCap) {
+          s_key[slot] = key;
+          s_a[slot] = a;
+        }
+      }
+    });
+    __syncthreads();
+    const int cnt = (int)min(s_cnt, (uint32_t)kBinCap);
+    int np2 = 1;
+    while (np2 < cnt) np2 <<= 1;
+    for (int k = cnt + (int)threadIdx.x; k < np2; k += kPlanThreads) {
+      s_key[k] = 0ull;  // below every key of L
+      s_a[k] = 0.0f;
+    }
+    __syncthreads();
+    for (int k = 2; k <= np2; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int t = threadIdx.x; t < np2 / 2; t += kPlanThreads) {
+          const int i = 2 * t - (t & (j - 1)), ix = i + j;
+          const unsigned long long x = s_key[i], y = s_key[ix];
+          if (((i & k) == 0) ? (x < y) : (x > y)) {
+            s_key[i] = y;
+            s_key[ix] = x;
+            const float ta = s_a[i];
+            s_a[i] = s_a[ix];
+            s_a[ix] = ta;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    // ---- prefix sums of the bias in key order (two entries per thread)
+    const int e0 = 2 * (int)threadIdx.x;
+    const double a0 = e0 < cnt ? (double)s_a[e0] : 0.0;
+    const double a1 = e0 + 1 < cnt ? (double)s_a[e0 + 1] : 0.0;
+    const double winc = wave_incl_scan<double>(a0 + a1, lane);
+    if (lane == kWave - 1) s_wsum[wave] = winc;
+    if (threadIdx.x == 0) s_excl = 0.0;
+    __syncthreads();
+    double ex = winc - (a0 + a1);
+    double total = 0.0;
+    for (int w = 0; w < kPlanWaves; ++w) {
+      if (w < wave) ex += s_wsum[w];
+      total += s_wsum[w];
+    }
+    // the first entry that does not move: kappa <= 2 (beta + bias before it)
+    int kf = cnt;
+    for (int u = 1; u >= 0; --u) {
+      const int e = e0 + u;
+      if (e >= cnt) continue;
+      const double kap = (double)__uint_as_float((uint32_t)(s_key[e] >> 24));
+      const double before = beta + (u ? ex + a0 : ex);
+      if (!(kap > 2.0 * before)) kf = e;
+    }
+    int kv[1] = {kf};
+    blk_combine<int, 1, kPlanThreads, OpMin<int>>(kv);
+    kf = kv[0];
+    if (kf < cnt) {
+      // the bias of the entries before kf
+      if (e0 == kf) s_excl = ex;
+      if (e0 + 1 == kf) s_excl = ex + a0;
+      __syncthreads();
+      if (kf > 0) last = s_key[kf - 1];
+      beta += s_excl;
+      break;
+    }
+    if (cnt > 0) last = s_key[cnt - 1];
+    beta += total;
+    if (lo == 0ull) break;  // every token of L moved
+    hi = lo;
+    __syncthreads();  // LDS reuse by the next round
+  }
+  if (threadIdx.x == 0) {
+    BinState bs;
+    bs.key = last;
+    bs.beta = beta;
+    p.binst[row] = bs;
+  }
+}
+
 // Certificate terms (Lemma 1) at beta*. Settles beta* from the last Newton
 // pass first; a row still open iterates here over all of its tokens.
 template <int GRP>
@@ -1691,12 +1933,14 @@ __global__ __launch_bounds__(kBlock) void dk_rcert(DParams p) {
     }
     if (!st.done) st.beta = st.lo;
   }
-  const double beta = st.beta;
+  // (binary shrinkage: beta is the bias of the moved tokens)
+  const bool bin = p.est == VKV_EST_BINARY;
+  const double beta = bin ? p.binst[row].beta : st.beta;
+  const LamRule lr = lam_rule((float)beta, p.est, bin ? p.binst[row].key : ~0ull);
   if (c == 0 && threadIdx.x == 0) {
     p.rbeta[2 * row] = beta;
     p.rbeta[2 * row + 1] = st.dnorm;
   }
-  const float betaf = (float)beta;
   double cv[2] = {0.0, 0.0};
   float x1 = 0.0f, x2 = 0.0f;
   int p1 = 0x7fffffff;
@@ -1707,7 +1951,7 @@ __global__ __launch_bounds__(kBlock) void dk_rcert(DParams p) {
 #pragma unroll
     for (int u = 0; u < kRowTok; ++u) {
       if (!(r8[u] < 1.0f)) continue;
-      const Terms t = token_terms_w(w8[u], r8[u], betaf, p.est);
+      const Terms t = token_terms_w(w8[u], r8[u], lr, row_pos(cc, u));
       cv[0] += (double)t.bi;
       cv[1] += (double)t.vi;
       top2_merge(x1, p1, x2, t.rb, row_pos(cc, u), 0.0f);
@@ -1756,7 +2000,9 @@ __device__ __forceinline__ CertShare cert_rec_load(const DParams &p, int row) {
 // `sh`): every workgroup of the row computes the same RowState.
 __device__ __forceinline__ void row_certificate(const DParams &p, CertShare sh,
                                                 float m, double beta,
-                                                double dnorm, RowState &rs) {
+                                                double dnorm,
+                                                unsigned long long bkey,
+                                                RowState &rs) {
   double cv[2] = {sh.cv[0], sh.cv[1]};
   float x1 = sh.x1, x2 = sh.x2;
   int p1 = sh.p1;
@@ -1771,6 +2017,7 @@ __device__ __forceinline__ void row_certificate(const DParams &p, CertShare sh,
     z.m = m;
     z.dnorm = dnorm;
     z.beta = beta;
+    z.bkey = bkey;
     z.betaL = tb;
     z.VL = tv;
     z.b1 = y1;
@@ -1845,15 +2092,16 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
   const CertShare cs = cert_rec_load(p, row);
   const double beta = p.rbeta[2 * row], dnorm = p.rbeta[2 * row + 1];
   for (int i = threadIdx.x; i < kSelBinsP; i += kBlock) s_hist[i] = 0u;
-  row_certificate(p, cs, m, beta, dnorm, rs);
+  row_certificate(p, cs, m, beta, dnorm,
+                  p.est == VKV_EST_BINARY ? p.binst[row].key : ~0ull, rs);
   if (s == 0 && threadIdx.x == 0) p.rows[row] = rs;
   if (!rs.fetch) return;
-  const float betaf = (float)rs.beta;
+  const LamRule lr = lam_rule((float)rs.beta, p.est, rs.bkey);
   const float af = (float)p.a_delta, lf = (float)p.l_delta;
   const int eb = rs.eb, ev = rs.ev;
   const double capb = rs.capb, capv = rs.capv;
   auto key_of = [&](int i, float ri, float si, Terms &t) {
-    t = token_terms_w(expf(si - m), ri, betaf, p.est);
+    t = token_terms_w(expf(si - m), ri, lr, i);
     return make_key(token_gain(t, i, rs, af, lf), i);
   };
   // ---- keys: histogram and totals (the register tokens keep their terms)
@@ -1978,7 +2226,7 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
           vd = (double)klw[k] * (double)klw[k] * (double)((1.0f - rb[k]) / rb[k]);
           tb = krb[k];
         } else {
-          const Terms t = token_terms_w(expf(sb[k] - m), rb[k], betaf, p.est);
+          const Terms t = token_terms_w(expf(sb[k] - m), rb[k], lr, key_pos(kb[k]));
           direct_terms(t, bd, vd);
           tb = t.rb;
         }
@@ -2135,8 +2383,7 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rwalk(DParams p) {
   const int eb = rs.eb, ev = rs.ev;
   const double capb = rs.capb, capv = rs.capv;
   const double sbs = ldexp(1.0, -eb), svs = ldexp(1.0, -ev);
-  const float betaf = (float)rs.beta;
-  const int est = p.est;
+  const LamRule lr = lam_rule((float)rs.beta, p.est, rs.bkey);
   // Tier 0 holds each workgroup's top capw / 4 keys, tier 1 all capw; the
   // larger set is only walked when the smaller one cannot decide the row.
 #pragma unroll 1
@@ -2197,7 +2444,7 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rwalk(DParams p) {
         lds.c.key[dst[u]] = ck[u];
         lds.c.w[dst[u]] = cw[u];
         lds.c.r[dst[u]] = cq[u];
-        const Terms t = token_terms_w(cw[u], cq[u], betaf, est);
+        const Terms t = token_terms_w(cw[u], cq[u], lr, key_pos(ck[u]));
         cs[0] += sat_fx(t.bi, capb, eb);
         cs[1] += sat_fx(t.vi, capv, ev);
         kmin = min(kmin, ck[u]);
@@ -2235,7 +2482,7 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rwalk(DParams p) {
         const unsigned long long key = lds.c.key[k];
         if ((key >> (off + w)) != pre) continue;
         WalkBin &x = lds.c.bin[(int)((key >> off) & ((1ull << w) - 1ull))];
-        const Terms t = token_terms_w(lds.c.w[k], lds.c.r[k], betaf, est);
+        const Terms t = token_terms_w(lds.c.w[k], lds.c.r[k], lr, key_pos(key));
         atomicAdd(&x.cnt, 1u);
         atomicAdd(&x.bsum, sat_fx(t.bi, capb, eb));
         atomicAdd(&x.vsum, sat_fx(t.vi, capv, ev));
@@ -2355,7 +2602,7 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rwalk(DParams p) {
     for (int k = threadIdx.x; k < nc; k += kPlanThreads) {
       const unsigned long long key = lds.c.key[k];
       if (key < T) {
-        const Terms t = token_terms_w(lds.c.w[k], lds.c.r[k], betaf, est);
+        const Terms t = token_terms_w(lds.c.w[k], lds.c.r[k], lr, key_pos(key));
         double bd, vd;
         direct_terms(t, bd, vd);
         dr[0] += bd;
@@ -2595,7 +2842,7 @@ __device__ __forceinline__ float resident_alpha(const DParams &p,
   const float w = expf(ell - rs.m);
   if (ri >= 1.0f || in_fetch(p, row, pos)) return w;
   const Terms t = token_terms(p.shat[(size_t)row * p.n + pos], ri, rs.m,
-                              (float)rs.beta, p.est);
+                              lam_rule((float)rs.beta, p.est, rs.bkey), pos);
   return t.lam * w / ri;
 }
 
@@ -2797,6 +3044,8 @@ hipError_t run(const DParams &p, hipStream_t s, int sd, void **events) {
     dk_rbeta<GRP><<<grow, blk, 0, s>>>(p, j);
     mark(k++);
   }
+  if (p.est == VKV_EST_BINARY) dk_rbin<GRP><<<gone, dim3(kPlanThreads), 0, s>>>(p);
+  mark(k++);
   dk_rcert<GRP><<<grow, blk, 0, s>>>(p);
   mark(k++);
   {
@@ -2819,7 +3068,7 @@ hipError_t run(const DParams &p, hipStream_t s, int sd, void **events) {
 }
 
 const char *const kPhaseNames[] = {
-    "scan", "beta1", "beta2", "cert", "cand", "walk", "fetch", "attn"};
+    "scan", "beta1", "beta2", "shrink", "cert", "cand", "walk", "fetch", "attn"};
 
 }  // namespace
 
@@ -2892,6 +3141,7 @@ DecodeLayout decode_layout(const vkv_decode_args &a) {
   L.band = c.take<float2>(2 * rows * L.nrc * (size_t)kBandChunk);
   L.bstate = c.take<BetaState>(2 * rows);
   L.rbeta = c.take<double>(2 * rows);
+  L.binst = c.take<BinState>(rows);
   L.cpart = c.take<CertPart>(rows * L.nrc);
   L.ccount = c.take<uint32_t>(rows * kSelWG * 2);
   L.clo = c.take<unsigned long long>(rows * kSelWG * 2);
@@ -2944,6 +3194,7 @@ hipError_t launch_decode(const vkv_decode_args &a, const DecodeLayout &L,
   p.band = at<float2>(w, L.band);
   p.bstate = at<BetaState>(w, L.bstate);
   p.rbeta = at<double>(w, L.rbeta);
+  p.binst = at<BinState>(w, L.binst);
   p.cpart = at<CertPart>(w, L.cpart);
   p.ccount = at<uint32_t>(w, L.ccount);
   p.clo = at<unsigned long long>(w, L.clo);

@@ -57,7 +57,7 @@ struct DecodeLayout {
   size_t shat, ell, hpart, fstat, fbits, hbits, pmax, p0part, hres, rows,
       bpart, band,
       bstate,
-      rbeta, cpart, ccount, clo, tpart, candk, candw, candq, dpart,
+      rbeta, binst, cpart, ccount, clo, tpart, candk, candw, candq, dpart,
       rpart, apart, aparto, total;
 };
 

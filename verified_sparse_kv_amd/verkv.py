@@ -26,7 +26,7 @@ STATUS_RESIDENT_OVERFLOW = 0x1
 STATUS_FETCH_OVERFLOW = 0x2
 STATUS_BAD_R = 0x4
 STATUS_BAD_RESIDENT = 0x8
-EST_CLIP, EST_UNBIASED = 0, 1
+EST_CLIP, EST_UNBIASED, EST_BINARY = 0, 1, 2
 W_SKETCH, W_PERFECT = 0, 1
 
 EXPORTS = ("vkv_compress_workspace_bytes", "vkv_decode_workspace_bytes",
