@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU work budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the Dense (resident) / Dense (offload) baselines")
     return ap.parse_args()
 
 
@@ -161,6 +163,47 @@ def cpu_baseline(w, seconds, est=0):
                       f"heads, {n} tokens, fresh query each) of the same "
                       f"layer, fp64 numpy, {spent:.1f} s; "
                       f"host cores available: {len(os.sched_getaffinity(0))}"}
+
+
+def dense_baselines(w, t_qs, host_kv, dev, steps, verkv_ms):
+    """The pages' Dense baselines on this GPU: exact attention over the whole
+    cache, held in HBM (resident) or read from pinned host memory at every
+    step (offload), for the same queries; with VerKV's speedup over each."""
+    import torch
+
+    from verified_sparse_kv_amd import verkv as vk
+    B, Hq, G, n = w["B"], w["Hq"], w["G"], w["n"]
+    cache = B * G * n * ROW_BYTES
+    out = {}
+    kv_dev = host_kv.to(dev)
+    k = max(1, min(steps, 10))
+    for name, kv in (("resident", kv_dev), ("offload", host_kv)):
+        run = vk.DenseAttention(B, Hq, G, n, dev).bind(t_qs[0], kv)
+        for i in range(2):
+            run.launch()
+        # each call between two events on the stream: the GPU time of its
+        # two kernels (the host-side call costs more than the resident
+        # kernels themselves, so wall-clock would time the host)
+        evs = [(torch.cuda.Event(enable_timing=True),
+                torch.cuda.Event(enable_timing=True)) for _ in range(k)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(k):
+            run.args.q = vk._ptr(t_qs[i % len(t_qs)])
+            evs[i][0].record()
+            run.launch()
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / k
+        ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / k
+        out[name] = {"ms_per_step": ms, "wall_ms_per_step": wall,
+                     "value": B * Hq * n / (ms * 1e-3),
+                     "cache_read_gbs": cache / (ms * 1e-3) / 1e9, "steps": k}
+    del kv_dev
+    out["cache_bytes"] = cache
+    out["verkv_speedup_vs_offload"] = out["offload"]["ms_per_step"] / verkv_ms
+    out["verkv_speedup_vs_resident"] = out["resident"]["ms_per_step"] / verkv_ms
+    return out
 
 
 def main():
@@ -333,6 +376,9 @@ def main():
                                                  args.estimator),
                      "algorithmic_bytes": cand[dom]},
     }
+    if not args.no_dense:
+        res["dense_baselines"] = dense_baselines(w, t_qs, host_kv, dev,
+                                                 args.steps, ms)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds,
                                            ESTIMATORS[args.estimator])

@@ -186,15 +186,46 @@ typedef struct {
   size_t workspace_bytes;
 } vkv_decode_args;
 
+/*
+ * Exact decode attention over the whole cache, eq. 1 (section 3): the Dense
+ * baselines of section 5. Dense (resident) passes a cache in device memory;
+ * Dense (offload) passes it in pinned host memory (hipHostMalloc), and every
+ * row is then read over the host link at every call (no device staging).
+ *
+ * Shapes: B = batch, Hq query heads over G KV heads (Hq/G in {1,2,4,8}),
+ * d = 128, 1 <= n <= 2^24 tokens.
+ * q       dev [B][Hq][d] bf16.
+ * kv      [B][G][n][2][d] bf16 (K row then V row per token), device memory or
+ *         pinned host memory.
+ * Outputs (dev): out [B][Hq][d] f32, o = sum_i w_i v_i / sum_i w_i with
+ * w_i = exp(<q, k_i>/sqrt(d)); log_d [B][Hq] f32, the natural log of
+ * sum_i w_i.
+ * Pageable host memory returns VKV_ENOTPINNED; bad shapes VKV_EINVAL.
+ */
+typedef struct {
+  int32_t batch, n_q_heads, n_kv_heads, head_dim, n_tokens;
+  const uint16_t *q;
+  const uint16_t *kv;
+  float *out;
+  float *log_d;
+  void *workspace;
+  size_t workspace_bytes;
+} vkv_dense_args;
+
 /* Workspace sizes in bytes for these arguments (0 if the shapes are invalid). */
 size_t vkv_compress_workspace_bytes(const vkv_compress_args *a);
 size_t vkv_decode_workspace_bytes(const vkv_decode_args *a);
+size_t vkv_dense_workspace_bytes(const vkv_dense_args *a);
 
 /* Enqueue one PoissonComp pass (see vkv_compress_args). */
 vkv_status vkv_compress(const vkv_compress_args *a, void *stream);
 
 /* Enqueue one KVFetch decode step (see vkv_decode_args). */
 vkv_status vkv_decode_step(const vkv_decode_args *a, void *stream);
+
+/* Enqueue one exact decode attention over the whole cache (see
+ * vkv_dense_args). */
+vkv_status vkv_dense_attention(const vkv_dense_args *a, void *stream);
 
 /* Synchronise `stream`, read the device status word and map it to a status:
  * VKV_OK, VKV_EOVERFLOW (capacity bits) or VKV_EDATA (data bits). The word

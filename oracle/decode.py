@@ -364,6 +364,24 @@ def decode_step(q, res_kv, res_idx, sketch, proj, r, host_kv, eps, delta,
     return heads, unions
 
 
+def dense_step(q, kv):
+    """The Dense baselines of section 5: exact attention (eq. 1) of every
+    query head over every token of its KV head. q [B][Hq][d], kv
+    [B][G][n][2][d]; returns (o [B][Hq][d], log D [B][Hq])."""
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, d = q.shape
+    G = kv.shape[1]
+    grp = Hq // G
+    o = np.zeros((B, Hq, d))
+    logd = np.zeros((B, Hq))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // grp
+            o[b, h], logd[b, h] = exact_attention(q[b, h], kv[b, g, :, 0, :],
+                                                  kv[b, g, :, 1, :])
+    return o, logd
+
+
 def exact_attention(q, k, v):
     """Textbook softmax attention o = sum w v / sum w, w = exp(<k,q>/sqrt(d))
     (§3, eq. 1), float64; returns (o, log D)."""

@@ -180,6 +180,21 @@ def check_binary_prefix(w, r, pos=None):
     assert od_mse_plain(lam_c, w, r) <= m_bin * (1 + 1e-12)
 
 
+def check_exact_attention_mp(q, k, v):
+    """eq. 1 term by term at 50 digits: w_i = exp(<q, k_i>/sqrt(d)),
+    o = sum w_i v_i / sum w_i, log D = log sum w_i."""
+    o, logd = od.exact_attention(q, k, v)
+    d = len(q)
+    sd = mpmath.sqrt(d)
+    ws = [mpmath.exp(mpmath.fsum(mpmath.mpf(float(a)) * mpmath.mpf(float(b))
+                                 for a, b in zip(q, ki)) / sd) for ki in k]
+    D = mpmath.fsum(ws)
+    assert abs(logd - float(mpmath.log(D))) <= 1e-12 * max(1.0, abs(logd))
+    for c in range(v.shape[1]):
+        oc = mpmath.fsum(wi * mpmath.mpf(float(vi[c])) for wi, vi in zip(ws, v)) / D
+        assert abs(o[c] - float(oc)) <= 1e-12 * (1 + abs(float(oc)))
+
+
 # ---------------------------------------------------------------- certificate
 def check_bernstein_root(V, b, delta):
     """Lemma 1's proof: t = D * (eps^ - beta/D) is the positive root of

@@ -52,7 +52,8 @@ def _c_layout(struct, fields):
 
 
 @pytest.mark.parametrize("cls,cname", [(vk.CompressArgs, "vkv_compress_args"),
-                                       (vk.DecodeArgs, "vkv_decode_args")])
+                                       (vk.DecodeArgs, "vkv_decode_args"),
+                                       (vk.DenseArgs, "vkv_dense_args")])
 def test_struct_layout_matches_c(cls, cname):
     fields = [f for f, _ in cls._fields_]
     size, offs = _c_layout(cname, fields)
@@ -173,3 +174,41 @@ def test_phase_names():
     assert names[0] == "scan" and names[-1] == "attn"
     assert vk.vkv_decode_phase_name(len(names)) is None
     assert vk.vkv_decode_phase_name(-1) is None
+
+
+def _dense_args(**kw):
+    a = vk.DenseArgs(batch=2, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                     n_tokens=4096)
+    fake = ctypes.c_void_p(0x1000)
+    for f in ("q", "kv", "out", "log_d"):
+        setattr(a, f, fake)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_dense_workspace_sizes():
+    w = vk.vkv_dense_workspace_bytes(_dense_args())
+    assert w > 0 and w % 256 == 0
+    assert vk.vkv_dense_workspace_bytes(_dense_args(n_q_heads=20)) == 0
+    assert vk.vkv_dense_workspace_bytes(_dense_args(n_tokens=1)) > 0
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(n_q_heads=20), "multiple"),
+    (dict(n_q_heads=24), "1, 2, 4 or 8"),
+    (dict(head_dim=64), "head_dim"),
+    (dict(n_tokens=0), "n_tokens"),
+    (dict(n_tokens=(1 << 24) + 1), "n_tokens"),
+    (dict(kv=None), "required"),
+    (dict(log_d=None), "required"),
+    (dict(workspace=None), "workspace"),
+])
+def test_dense_validation(kw, frag):
+    a = _dense_args(**kw)
+    if "workspace" not in kw:
+        a.workspace = ctypes.c_void_p(0x1000)
+        a.workspace_bytes = 1 << 40
+    assert vk.vkv_dense_attention(a, None) == vk.VKV_EINVAL
+    msg = vk.vkv_last_error()
+    assert frag in msg, msg

@@ -116,6 +116,38 @@ def test_binary_exact_enumeration(seed):
                            od.EST_BINARY)
 
 
+@pytest.mark.parametrize("seed", range(3))
+def test_exact_attention_mp(seed):
+    rng = np.random.default_rng(500 + seed)
+    n, d = int(rng.integers(1, 12)), 16
+    q, k, v = (rng.normal(0, 2, (d,)), rng.normal(0, 2, (n, d)),
+               rng.normal(0, 1, (n, 3)))
+    pins.check_exact_attention_mp(q, k, v)
+
+
+def test_exact_attention_two_keys():
+    """Logits 1 and 0 (d = 4, q = (2, 0, 0, 0)): o = (e v1 + v2)/(e + 1)."""
+    q = np.array([2.0, 0, 0, 0])
+    k = np.array([[1.0, 0, 0, 0], [0, 0, 0, 0]])
+    v = np.array([[1.0, 0.0], [0.0, 1.0]])
+    o, logd = od.exact_attention(q, k, v)
+    e = math.e
+    assert np.allclose(o, [e / (e + 1), 1 / (e + 1)], rtol=1e-15, atol=0)
+    assert logd == pytest.approx(math.log(e + 1), rel=1e-15)
+
+
+def test_dense_step_layout():
+    """dense_step maps query head h to KV head h // (Hq/G)."""
+    rng = np.random.default_rng(7)
+    q = rng.normal(size=(2, 4, 8))
+    kv = rng.normal(size=(2, 2, 5, 2, 8))
+    o, logd = od.dense_step(q, kv)
+    for b in range(2):
+        for h in range(4):
+            oo, ll = od.exact_attention(q[b, h], kv[b, h // 2, :, 0], kv[b, h // 2, :, 1])
+            assert np.array_equal(o[b, h], oo) and logd[b, h] == ll
+
+
 @pytest.mark.parametrize("seed", range(6))
 def test_kkt_large(seed):
     rng = np.random.default_rng(200 + seed)

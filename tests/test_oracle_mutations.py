@@ -58,6 +58,9 @@ def run_pins():
     attempt("binary", lambda: pins.check_binary_prefix(wb, rb))
     attempt("binary_heavy", lambda: pins.check_binary_prefix(*_heavy(11, 30)))
     attempt("golden_binary", _golden_binary)
+    rng = np.random.default_rng(12)
+    attempt("attention_mp", lambda: pins.check_exact_attention_mp(
+        rng.normal(0, 2, 16), rng.normal(0, 2, (6, 16)), rng.normal(0, 1, (6, 3))))
     return failed
 
 
@@ -199,6 +202,14 @@ _bin_ok_key = lambda w, r: w * (1 - r) / r
 _bin_ok_stop = lambda k, b: k > 2 * b
 _bin_ok_add = lambda w, r: w * (1 - r)
 
+def _attention_no_scale(q, k, v):
+    q = np.asarray(q, np.float64)
+    lg = np.asarray(k, np.float64) @ q
+    m = lg.max()
+    w = np.exp(lg - m)
+    return (w @ np.asarray(v, np.float64)) / w.sum(), math.log(w.sum()) + m
+
+
 _orig_wl = oc.water_level
 _orig_rates = oc.rates
 
@@ -225,6 +236,8 @@ MUTATIONS = [
      _binary_variant(_bin_ok_key, lambda k, b: k >= 2 * b, _bin_ok_add)),
     ("binary bias accumulates w", od, "binary_lambdas",
      _binary_variant(_bin_ok_key, _bin_ok_stop, lambda w, r: w)),
+    ("attention logits not scaled by 1/sqrt(d)", od, "exact_attention",
+     _attention_no_scale),
 ]
 
 

@@ -51,6 +51,24 @@ vkv_status check_compress_shapes(const vkv_compress_args *a) {
   return VKV_OK;
 }
 
+vkv_status check_dense_shapes(const vkv_dense_args *a) {
+  REQUIRE(a != nullptr, "dense: args is NULL");
+  REQUIRE(a->batch >= 1 && a->batch <= 65535, "dense: batch must be in [1, 65535]");
+  REQUIRE(a->n_kv_heads >= 1 && a->n_kv_heads <= 65535,
+          "dense: n_kv_heads must be in [1, 65535]");
+  REQUIRE(a->n_q_heads >= a->n_kv_heads && a->n_q_heads % a->n_kv_heads == 0,
+          "dense: n_q_heads must be a multiple of n_kv_heads");
+  const int grp = a->n_q_heads / a->n_kv_heads;
+  REQUIRE(grp == 1 || grp == 2 || grp == 4 || grp == 8,
+          "dense: n_q_heads / n_kv_heads must be 1, 2, 4 or 8");
+  REQUIRE((int64_t)a->batch * a->n_q_heads <= 65535,
+          "dense: batch * n_q_heads must be <= 65535");
+  REQUIRE(a->head_dim == vkv::kHeadDim, "dense: head_dim must be 128");
+  REQUIRE(a->n_tokens >= 1 && a->n_tokens <= (1 << 24),
+          "dense: n_tokens must be in [1, 2^24]");
+  return VKV_OK;
+}
+
 vkv_status check_decode_shapes(const vkv_decode_args *a) {
   REQUIRE(a != nullptr, "decode: args is NULL");
   REQUIRE(a->batch >= 1 && a->batch <= 65535, "decode: batch must be in [1, 65535]");
@@ -94,6 +112,11 @@ size_t vkv_compress_workspace_bytes(const vkv_compress_args *a) {
 size_t vkv_decode_workspace_bytes(const vkv_decode_args *a) {
   if (check_decode_shapes(a) != VKV_OK) return 0;
   return vkv::decode_layout(*a).total;
+}
+
+size_t vkv_dense_workspace_bytes(const vkv_dense_args *a) {
+  if (check_dense_shapes(a) != VKV_OK) return 0;
+  return vkv::dense_layout(*a).total;
 }
 
 vkv_status vkv_compress(const vkv_compress_args *a, void *stream) {
@@ -153,6 +176,32 @@ vkv_status vkv_decode_step(const vkv_decode_args *a, void *stream) {
   const uint16_t *hkv = static_cast<const uint16_t *>(attr.devicePointer);
   e = vkv::launch_decode(*a, L, hkv, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return VKV_OK;
+}
+
+vkv_status vkv_dense_attention(const vkv_dense_args *a, void *stream) {
+  vkv_status st = check_dense_shapes(a);
+  if (st != VKV_OK) return st;
+  REQUIRE(a->q && a->kv && a->out && a->log_d, "dense: q, kv, out and log_d are required");
+  const vkv::DenseLayout L = vkv::dense_layout(*a);
+  REQUIRE(a->workspace != nullptr && a->workspace_bytes >= L.total,
+          "dense: workspace of %zu bytes needed", L.total);
+  // device memory as it is; host memory only when pinned and mapped
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, a->kv);
+  const uint16_t *kv = nullptr;
+  if (e == hipSuccess && attr.type == hipMemoryTypeDevice) {
+    kv = a->kv;
+  } else if (e == hipSuccess && attr.type == hipMemoryTypeHost && attr.devicePointer) {
+    kv = static_cast<const uint16_t *>(attr.devicePointer);
+  } else {
+    (void)hipGetLastError();
+    return fail(VKV_ENOTPINNED,
+                "dense: kv is neither device memory nor device-accessible pinned host memory (%s)",
+                e != hipSuccess ? hipGetErrorString(e) : "wrong memory type");
+  }
+  e = vkv::launch_dense(*a, L, kv, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "dense launch");
   return VKV_OK;
 }
 

@@ -4,16 +4,19 @@
 // A "group" is one (request b, KV head g) with its GRP = Hq/G query heads
 // ("rows"). Kernels, in launch order:
 //
-//  dk_scan      sketch logits s_i = <P_g^T q, sk_i>/sqrt(d) for every token and
-//               the GRP heads at once (one sketch row serves all of them),
-//               and per chunk the pass-0 sums of the beta* iteration with the
-//               chunk's own shift.
-//  dk_resident  exact logits l_j = <q, k_j>/sqrt(d) on the resident rows,
-//               residency bitmap, per part the shift and sum_H exp(l).
-//  dk_rbeta x4  common shift m = max(max_R l, max_L s), D~ = sum_H w + sum_L
-//               w~, then the Definition 2 fixed point beta* by a bracketed
-//               Newton iteration on a convex piecewise-linear function (one
-//               launch per pass).
+//  dk_front     one launch of two kinds of workgroups. Scan workgroups: the
+//               sketch logits s_i = <P_g^T q, sk_i>/sqrt(d) of every token for
+//               the GRP heads at once (one sketch row serves all of them), and
+//               per chunk the pass-0 sums of the beta* iteration against the
+//               chunk's running shift. Resident workgroups: the exact logits
+//               l_j = <q, k_j>/sqrt(d) on the resident rows, and per part the
+//               shift and sum_H exp(l).
+//  dk_rbeta x2  common shift m = max(max_R l, max_L s), D~ = sum_H w + sum_L
+//               w~, then the Definition 2 fixed point beta* by bracketed
+//               Newton passes on a convex piecewise-linear function, settled
+//               from the band of undecided tokens (one launch per pass).
+//  dk_rbin      binary shrinkage only (Appendix A.2): the tokens set to
+//               lambda = r, one workgroup per row.
 //  dk_rcert     lambda_i, beta(L), V(L) and the top two b_i per chunk
 //               (Lemma 1, eq. 7).
 //  dk_rcand     eps^(L) and, for a row that must fetch, the gain keys (eq. 9)
@@ -47,6 +50,10 @@ constexpr int kRowChunk = 2048;  // tokens per workgroup in row passes
 constexpr int kRowTok = kRowChunk / kBlock;
 constexpr int kCand = 2048;      // candidates per round of the streaming selection
 constexpr float kInvSqrtD = 0.08838834764831845f;  // 1/sqrt(128)
+constexpr int kSelDigit = 11;    // radix digit of the selections' keys
+constexpr int kSelBinsP = 1 << kSelDigit;
+constexpr int kBinCap = 256;     // keys per round of the binary shrinkage
+static_assert(kBinCap <= 4 * kWave, "one wave sorts a round");
 
 struct RowState {
   float m;                // common shift of the planning and resident logits
@@ -118,6 +125,13 @@ struct DParams {
   BetaState *bstate; // [2][row]
   double *rbeta;     // [row][2] beta*, D~
   BinState *binst;   // [row] binary shrinkage: last moved key, its bias
+  // binary shrinkage's first round, gathered by the beta launches: the
+  // row's histogram of the top key digit, then per row workgroup its keys at
+  // or above the round's bound (count, keys, biases)
+  uint32_t *bhist;   // [row][kSelBinsP]
+  uint32_t *bcnt;    // [row][nrc]
+  unsigned long long *bkeys;  // [row][nrc][kBinCap]
+  float *bav;        // [row][nrc][kBinCap]
   CertPart *cpart;   // [row][nrc]
   // candidate workgroups: [row][kSelWG] counts, local bounds, max b_i of
   // the keys not written, fixed-point totals; candidates [row][kCandMax]
@@ -530,6 +544,19 @@ __device__ __forceinline__ void p0_finish(const DParams &p, int b, int g,
   if (threadIdx.x == 0) p.hpart[(size_t)bg * np + c] = nh[0];
 }
 
+// Binary shrinkage: scan chunk c of group (b, g) clears its share of the
+// group's rows' key-digit histograms (added to by the first beta launch).
+template <int GRP>
+__device__ __forceinline__ void clear_bin_hist(const DParams &p, int c, int b,
+                                               int g) {
+  if (p.est != VKV_EST_BINARY) return;
+  const int total = GRP * kSelBinsP;
+  int lo, hi;
+  split_range(total, p.nch, c, lo, hi);
+  uint32_t *h0 = p.bhist + (size_t)row_of(p, b, g, 0, GRP) * kSelBinsP;
+  for (int t = lo + (int)threadIdx.x; t < hi; t += kBlock) h0[t] = 0u;
+}
+
 template <int GRP, int SD>
 __device__ __forceinline__ void scan_body(const DParams &p, int c, int g,
                                           int b) {
@@ -582,6 +609,7 @@ __device__ __forceinline__ void scan_body(const DParams &p, int c, int g,
       *p.host_bytes = 0ull;
     }
   }
+  clear_bin_hist<GRP>(p, c, b, g);
   // clear this chunk's bitmap words
   {
     const int w0 = c * p.chunk / 32, nw = p.chunk / 32;
@@ -708,6 +736,7 @@ __device__ __forceinline__ void scan_exact_body(const DParams &p, int c,
       *p.host_bytes = 0ull;
     }
   }
+  clear_bin_hist<GRP>(p, c, b, g);
   {
     const int w0 = c * p.chunk / 32, nw = p.chunk / 32;
     for (int w = threadIdx.x; w < nw; w += kBlock) {
@@ -969,8 +998,6 @@ constexpr int kBandMax = 1024;      // band tokens a row may be settled from
 constexpr int kMaxChunks = kMaxTokens / kRowChunk;
 constexpr int kBetaPassMax = 96;    // never reached: the bracket shrinks >= 2x
 constexpr int kCandMax = 8192;      // candidates held by the walk
-constexpr int kSelDigit = 11;
-constexpr int kSelBinsP = 1 << kSelDigit;
 constexpr int kSelLevels = 5;       // five 11-bit digits cover the 55-bit key
 constexpr unsigned long long kKeyEnd = 1ull << 55;  // above every key
 __device__ __forceinline__ int sel_off(int d) { return 44 - kSelDigit * d; }
@@ -1603,6 +1630,146 @@ __device__ __forceinline__ BetaState beta_settle(const DParams &p, BetaState st,
   return st;
 }
 
+// ------------------------------------------------------------ binary shrinkage,
+// first round (in the beta launches, which binary shrinkage leaves idle)
+// The first round's lower key bound from a row's top-digit histogram (LDS),
+// by the calling wave: the smallest bin j0 whose keys, with those of the
+// bins above it, fit in kBinCap. It is usable (ok) unless a finer digit
+// would be taken, i.e. j0 > 0 with fewer than kBinCap / 4 keys above it --
+// the same decision as the first digit of the streaming rounds below.
+__device__ __forceinline__ void bin_bound(const uint32_t *hist, int lane,
+                                          unsigned long long &lo, int &ok) {
+  constexpr int per = kSelBinsP / kWave;
+  uint32_t tot = 0u;
+  for (int k = 0; k < per; ++k) tot += hist[lane * per + k];
+  const uint32_t incl = wave_incl_scan<uint32_t>(tot, lane);
+  uint32_t cum = __shfl(incl, kWave - 1, kWave) - incl;  // bins above
+  int jf = kSelBinsP;
+  for (int k = per - 1; k >= 0; --k) {
+    cum += hist[lane * per + k];
+    if (cum > (uint32_t)kBinCap) break;
+    jf = lane * per + k;
+  }
+  const int j0 = -wave_max<int>(-jf);
+  uint32_t part = 0u;
+  for (int k = 0; k < per; ++k)
+    if (lane * per + k >= j0) part += hist[lane * per + k];
+  const uint32_t cnt = wave_sum<uint32_t>(part);
+  ok = (j0 > 0 && cnt < (uint32_t)(kBinCap / 4)) ? 0 : 1;
+  lo = (unsigned long long)j0 << sel_off(0);
+}
+
+// The histogram buffer both beta launches use (LDS).
+__device__ __forceinline__ uint32_t *bin_lds_hist() {
+  __shared__ uint32_t s_h[kSelBinsP];
+  return s_h;
+}
+
+// First beta launch: this workgroup's tokens of L counted by the top digit
+// of their binary key, added to the row's histogram (integer atomics: the
+// same counts in any order).
+__device__ __forceinline__ void bin_hist_pass(const DParams &p, int row, int bg,
+                                              int cc0, int cc1, float m,
+                                              float (&r8)[kRowTok],
+                                              float (&s8)[kRowTok]) {
+  uint32_t *s_h = bin_lds_hist();
+  for (int k = threadIdx.x; k < kSelBinsP; k += kBlock) s_h[k] = 0u;
+  __syncthreads();
+  for (int cc = cc0; cc < cc1; ++cc) {
+    float nr[kRowTok], ns[kRowTok];
+    if (cc + 1 < cc1) row_load(p, row, bg, cc + 1, nr, ns);  // next in flight
+#pragma unroll
+    for (int u = 0; u < kRowTok; ++u) {
+      if (!(r8[u] < 1.0f)) continue;
+      const float wt = expf(s8[u] - m);
+      const float qr = (1.0f - r8[u]) / r8[u];
+      atomicAdd(&s_h[(int)(bin_key(wt, qr, row_pos(cc, u)) >> sel_off(0))], 1u);
+    }
+#pragma unroll
+    for (int u = 0; u < kRowTok; ++u) {
+      r8[u] = nr[u];
+      s8[u] = ns[u];
+    }
+  }
+  __syncthreads();
+  uint32_t *gh = p.bhist + (size_t)row * kSelBinsP;
+  for (int k = threadIdx.x; k < kSelBinsP; k += kBlock)
+    if (s_h[k]) atomicAdd(&gh[k], s_h[k]);
+}
+
+// Second beta launch: the first round's bound from the row's histogram and,
+// when it is usable, this workgroup's keys at or above it (with their
+// biases) in its own segment; a count of 0 otherwise.
+__device__ __forceinline__ void bin_collect_pass(const DParams &p, int row,
+                                                 int bg, int c, int cc0,
+                                                 int cc1, float m,
+                                                 float (&r8)[kRowTok],
+                                                 float (&s8)[kRowTok]) {
+  uint32_t *s_h = bin_lds_hist();
+  __shared__ unsigned long long s_lo;
+  __shared__ int s_ok;
+  __shared__ uint32_t s_n;
+  const int lane = threadIdx.x % kWave;
+  for (int k = threadIdx.x; k < kSelBinsP; k += kBlock)
+    s_h[k] = p.bhist[(size_t)row * kSelBinsP + k];
+  if (threadIdx.x == 0) s_n = 0u;
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    unsigned long long l0;
+    int ok;
+    bin_bound(s_h, lane, l0, ok);
+    if (lane == 0) {
+      s_lo = l0;
+      s_ok = ok;
+    }
+  }
+  __syncthreads();
+  const size_t seg = (size_t)row * p.nrc + c;
+  if (!s_ok) {
+    if (threadIdx.x == 0) p.bcnt[seg] = 0u;
+    return;
+  }
+  const unsigned long long lo = s_lo;
+  for (int cc = cc0; cc < cc1; ++cc) {
+    float nr[kRowTok], ns[kRowTok];
+    if (cc + 1 < cc1) row_load(p, row, bg, cc + 1, nr, ns);  // next in flight
+#pragma unroll
+    for (int u = 0; u < kRowTok; ++u) {
+      bool take = false;
+      unsigned long long key = 0ull;
+      float a = 0.0f;
+      if (r8[u] < 1.0f) {
+        const float wt = expf(s8[u] - m);
+        const float qr = (1.0f - r8[u]) / r8[u];
+        key = bin_key(wt, qr, row_pos(cc, u));
+        a = wt * (1.0f - r8[u]);
+        take = key >= lo;
+      }
+      // one LDS atomic per wave: the wave's takers get consecutive slots
+      const unsigned long long bal = __ballot(take);
+      if (bal == 0ull) continue;
+      const int leader = __ffsll((long long)bal) - 1;
+      uint32_t base = 0u;
+      if (lane == leader) base = atomicAdd(&s_n, (uint32_t)__popcll(bal));
+      base = __shfl(base, leader, kWave);
+      if (take) {
+        const uint32_t slot = base + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+        if (slot < (uint32_t)kBinCap) {
+          p.bkeys[seg * kBinCap + slot] = key;
+          p.bav[seg * kBinCap + slot] = a;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kRowTok; ++u) {
+      r8[u] = nr[u];
+      s8[u] = ns[u];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) p.bcnt[seg] = min(s_n, (uint32_t)kBinCap);
+}
+
 // Newton pass `pass` (>= 1) of the beta* iteration; pass 1 starts from the
 // pass-0 sums that the scan and resident-logit kernels left per chunk and
 // part. Grid (chunks, Hq, B).
@@ -1644,6 +1811,11 @@ __global__ __launch_bounds__(kBlock) void dk_rbeta(DParams p, int pass) {
     st = beta_settle(p, st, rv, row, q);
   }
   if (c == 0 && threadIdx.x == 0) p.bstate[(size_t)(pass & 1) * rows + row] = st;
+  if (p.est == VKV_EST_BINARY) {  // (st.done: no beta* to find)
+    if (pass == 1) bin_hist_pass(p, row, bg, cc0, cc1, m, r8, s8);
+    else if (pass == 2) bin_collect_pass(p, row, bg, c, cc0, cc1, m, r8, s8);
+    return;
+  }
   if (st.done) return;
   double pts[kBetaPts];
   beta_points(st, pts);
@@ -1702,12 +1874,12 @@ __global__ __launch_bounds__(kBlock) void dk_rbeta(DParams p, int pass) {
 // largest first: count histograms of 11-bit key digits give the round's
 // lower key bound (a second digit only while the round would hold fewer
 // than kBinCap / 4 keys), the round's keys and biases are gathered into
-// LDS and sorted, and float64 prefix sums of the biases in that order, in a
+// LDS (slots by wave, in wave order of arrival; the sort fixes the order)
+// and sorted, and float64 prefix sums of the biases in that order, in a
 // fixed tree order, find the first token that stops the moves. A round that
 // moves all of its tokens passes its bias total on to the next. The result
 // is the key of the last token moved (~0 for none) and the moved tokens'
 // bias; every later pass recomputes lambda from it.
-constexpr int kBinCap = 2048;
 
 template <int GRP>
 __global__ __launch_bounds__(kPlanThreads) void dk_rbin(DParams p) {
@@ -1752,13 +1924,58 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rbin(DParams p) {
   unsigned long long hi = kKeyEnd;  // the keys at or above hi are decided
   unsigned long long last = ~0ull;  // key of the last token moved
   double beta = 0.0;                // bias of the tokens moved
+  // the first round as the beta launches gathered it: its bound from the
+  // row's top-digit histogram (the same decision they took) and their keys
+  bool pre;
+  {
+    for (int k = threadIdx.x; k < kSelBinsP; k += kPlanThreads)
+      s_hist[k] = p.bhist[(size_t)row * kSelBinsP + k];
+    __syncthreads();
+    if (wave == 0) {
+      unsigned long long l0;
+      int ok;
+      bin_bound(s_hist, lane, l0, ok);
+      if (lane == 0) {
+        s_lo = l0;
+        s_more = ok;
+      }
+    }
+    __syncthreads();
+    pre = s_more != 0;
+  }
   for (;;) {
+    unsigned long long lo = 0ull;
+    if (pre) {
+      __shared__ uint32_t s_off[kMaxChunks + 1];
+      lo = s_lo;
+      if (wave == 0) {  // nrc <= 64 segment counts, one per lane
+        const uint32_t k = lane < p.nrc ? p.bcnt[(size_t)row * p.nrc + lane] : 0u;
+        const uint32_t incl = wave_incl_scan<uint32_t>(k, lane);
+        if (lane < p.nrc) s_off[lane] = incl - k;
+        if (lane == kWave - 1) {
+          s_off[p.nrc] = incl;
+          s_cnt = incl;
+        }
+      }
+      __syncthreads();
+      const int tot = (int)min(s_off[p.nrc], (uint32_t)kBinCap);
+      for (int e = threadIdx.x; e < tot; e += kPlanThreads) {
+        int a0 = 0, a1 = p.nrc;  // the segment holding entry e
+        while (a1 - a0 > 1) {
+          const int mid = (a0 + a1) / 2;
+          if ((int)s_off[mid] <= e) a0 = mid; else a1 = mid;
+        }
+        const size_t at = ((size_t)row * p.nrc + a0) * kBinCap + (e - (int)s_off[a0]);
+        s_key[e] = p.bkeys[at];
+        s_a[e] = p.bav[at];
+      }
+      __syncthreads();
+    } else {
     // ---- the round's lower key bound, digit by digit from the top
     if (threadIdx.x == 0) {
       s_pre = 0ull;
       s_room = (uint32_t)kBinCap;
     }
-    unsigned long long lo = 0ull;
     for (int d = 0; d < kSelLevels; ++d) {
       const int off = sel_off(d);
       for (int k = threadIdx.x; k < kSelBinsP; k += kPlanThreads) s_hist[k] = 0u;
@@ -1811,8 +2028,17 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rbin(DParams p) {
     if (threadIdx.x == 0) s_cnt = 0u;
     __syncthreads();
     stream([&](unsigned long long key, float a) {
-      if (key >= lo && key < hi) {
-        const uint32_t slot = atomicAdd(&s_cnt, 1u);
+      const bool take = key >= lo && key < hi;
+      // one LDS atomic per wave: the wave's takers get consecutive slots
+      const unsigned long long bal = __ballot(take);
+      if (bal == 0ull) return;
+      const int leader = __ffsll((long long)bal) - 1;
+      uint32_t base = 0u;
+      if (lane == leader) base = atomicAdd(&s_cnt, (uint32_t)__popcll(bal));
+      base = __shfl(base, leader, kWave);
+      if (take) {
+        const uint32_t slot =
+            base + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
         if (slot < (uint32_t)kBinCap) {
           s_key[slot] = key;
           s_a[slot] = a;
@@ -1820,6 +2046,8 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rbin(DParams p) {
       }
     });
     __syncthreads();
+    }
+    pre = false;
     const int cnt = (int)min(s_cnt, (uint32_t)kBinCap);
     int np2 = 1;
     while (np2 < cnt) np2 <<= 1;
@@ -1828,22 +2056,29 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rbin(DParams p) {
       s_a[k] = 0.0f;
     }
     __syncthreads();
-    for (int k = 2; k <= np2; k <<= 1) {
-      for (int j = k >> 1; j > 0; j >>= 1) {
-        for (int t = threadIdx.x; t < np2 / 2; t += kPlanThreads) {
-          const int i = 2 * t - (t & (j - 1)), ix = i + j;
-          const unsigned long long x = s_key[i], y = s_key[ix];
-          if (((i & k) == 0) ? (x < y) : (x > y)) {
-            s_key[i] = y;
-            s_key[ix] = x;
-            const float ta = s_a[i];
-            s_a[i] = s_a[ix];
-            s_a[ix] = ta;
+    // bitonic sort by the first wave alone (at most 256 entries: two
+    // compare-exchanges per lane and step), its LDS accesses ordered by a
+    // wavefront fence between steps instead of workgroup barriers
+    if (wave == 0) {
+      for (int k = 2; k <= np2; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+          for (int t = lane; t < np2 / 2; t += kWave) {
+            const int i = 2 * t - (t & (j - 1)), ix = i + j;
+            const unsigned long long x = s_key[i], y = s_key[ix];
+            if (((i & k) == 0) ? (x < y) : (x > y)) {
+              s_key[i] = y;
+              s_key[ix] = x;
+              const float ta = s_a[i];
+              s_a[i] = s_a[ix];
+              s_a[ix] = ta;
+            }
           }
+          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+          __builtin_amdgcn_wave_barrier();
         }
-        __syncthreads();
       }
     }
+    __syncthreads();
     // ---- prefix sums of the bias in key order (two entries per thread)
     const int e0 = 2 * (int)threadIdx.x;
     const double a0 = e0 < cnt ? (double)s_a[e0] : 0.0;
@@ -3142,6 +3377,10 @@ DecodeLayout decode_layout(const vkv_decode_args &a) {
   L.bstate = c.take<BetaState>(2 * rows);
   L.rbeta = c.take<double>(2 * rows);
   L.binst = c.take<BinState>(rows);
+  L.bhist = c.take<uint32_t>(rows * (size_t)kSelBinsP);
+  L.bcnt = c.take<uint32_t>(rows * (size_t)L.nrc);
+  L.bkeys = c.take<unsigned long long>(rows * (size_t)L.nrc * kBinCap);
+  L.bav = c.take<float>(rows * (size_t)L.nrc * kBinCap);
   L.cpart = c.take<CertPart>(rows * L.nrc);
   L.ccount = c.take<uint32_t>(rows * kSelWG * 2);
   L.clo = c.take<unsigned long long>(rows * kSelWG * 2);
@@ -3195,6 +3434,10 @@ hipError_t launch_decode(const vkv_decode_args &a, const DecodeLayout &L,
   p.bstate = at<BetaState>(w, L.bstate);
   p.rbeta = at<double>(w, L.rbeta);
   p.binst = at<BinState>(w, L.binst);
+  p.bhist = at<uint32_t>(w, L.bhist);
+  p.bcnt = at<uint32_t>(w, L.bcnt);
+  p.bkeys = at<unsigned long long>(w, L.bkeys);
+  p.bav = at<float>(w, L.bav);
   p.cpart = at<CertPart>(w, L.cpart);
   p.ccount = at<uint32_t>(w, L.ccount);
   p.clo = at<unsigned long long>(w, L.clo);

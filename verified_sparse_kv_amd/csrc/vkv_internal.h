@@ -2,6 +2,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -57,7 +59,7 @@ struct DecodeLayout {
   size_t shat, ell, hpart, fstat, fbits, hbits, pmax, p0part, hres, rows,
       bpart, band,
       bstate,
-      rbeta, binst, cpart, ccount, clo, tpart, candk, candw, candq, dpart,
+      rbeta, binst, bhist, bcnt, bkeys, bav, cpart, ccount, clo, tpart, candk, candw, candq, dpart,
       rpart, apart, aparto, total;
 };
 
@@ -66,5 +68,15 @@ int decode_phase_count();
 const char *decode_phase_name(int i);
 hipError_t launch_decode(const vkv_decode_args &a, const DecodeLayout &L,
                          const uint16_t *host_kv_dev, hipStream_t s);
+
+// ------------------------------------------------------------ dense baselines
+struct DenseLayout {
+  int parts;
+  size_t pm, pd, po, total;
+};
+
+DenseLayout dense_layout(const vkv_dense_args &a);
+hipError_t launch_dense(const vkv_dense_args &a, const DenseLayout &L,
+                        const uint16_t *kv_dev, hipStream_t s);
 
 }  // namespace vkv

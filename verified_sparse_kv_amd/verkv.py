@@ -32,7 +32,8 @@ W_SKETCH, W_PERFECT = 0, 1
 EXPORTS = ("vkv_compress_workspace_bytes", "vkv_decode_workspace_bytes",
            "vkv_compress", "vkv_decode_step", "vkv_check_status",
            "vkv_last_error", "vkv_version", "vkv_decode_phase_count",
-           "vkv_decode_phase_name")
+           "vkv_decode_phase_name", "vkv_dense_workspace_bytes",
+           "vkv_dense_attention")
 
 _p = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -63,6 +64,13 @@ class DecodeArgs(ctypes.Structure):
                 ("fetch_count", _p), ("host_bytes", _p), ("row_stats", _p),
                 ("status", _p), ("phase_events", _p), ("workspace", _p),
                 ("workspace_bytes", ctypes.c_size_t)]
+
+
+class DenseArgs(ctypes.Structure):
+    _fields_ = [("batch", _i32), ("n_q_heads", _i32), ("n_kv_heads", _i32),
+                ("head_dim", _i32), ("n_tokens", _i32),
+                ("q", _p), ("kv", _p), ("out", _p), ("log_d", _p),
+                ("workspace", _p), ("workspace_bytes", ctypes.c_size_t)]
 
 
 class VerKVError(RuntimeError):
@@ -98,6 +106,10 @@ def _load():
     lib.vkv_decode_phase_count.restype = ctypes.c_int32
     lib.vkv_decode_phase_name.argtypes = [ctypes.c_int32]
     lib.vkv_decode_phase_name.restype = ctypes.c_char_p
+    lib.vkv_dense_workspace_bytes.argtypes = [ctypes.POINTER(DenseArgs)]
+    lib.vkv_dense_workspace_bytes.restype = ctypes.c_size_t
+    lib.vkv_dense_attention.argtypes = [ctypes.POINTER(DenseArgs), _p]
+    lib.vkv_dense_attention.restype = ctypes.c_int
     return lib
 
 
@@ -119,6 +131,14 @@ def vkv_compress(args, stream=None):
 
 def vkv_decode_step(args, stream=None):
     return int(LIB.vkv_decode_step(ctypes.byref(args), stream))
+
+
+def vkv_dense_workspace_bytes(args):
+    return int(LIB.vkv_dense_workspace_bytes(ctypes.byref(args)))
+
+
+def vkv_dense_attention(args, stream=None):
+    return int(LIB.vkv_dense_attention(ctypes.byref(args), stream))
 
 
 def vkv_check_status(status_ptr, stream=None):
@@ -320,3 +340,38 @@ def decode_step(q, resident_kv, resident_idx, resident_count, sketch, proj, r,
     step.bind(q, resident_kv, resident_idx, resident_count, sketch, proj, r,
               host_kv, eps, delta, estimator, weights)
     return step.launch(stream)
+
+
+class DenseAttention:
+    """Reusable launcher of the exact whole-cache attention (the Dense
+    baselines): `kv` [B][G][n][2][d] int16 (bf16 bits) either on the device
+    (Dense resident) or in pinned host memory (Dense offload)."""
+
+    def __init__(self, B, Hq, G, n, device, d=128):
+        torch = _torch()
+        self.shape = (B, Hq, G, n)
+        self.out = dict(
+            out=torch.empty((B, Hq, d), dtype=torch.float32, device=device),
+            log_d=torch.empty((B, Hq), dtype=torch.float32, device=device))
+        self.args = DenseArgs(batch=B, n_q_heads=Hq, n_kv_heads=G, head_dim=d,
+                              n_tokens=n, out=_ptr(self.out["out"]),
+                              log_d=_ptr(self.out["log_d"]))
+        nbytes = vkv_dense_workspace_bytes(self.args)
+        if nbytes == 0:
+            raise VerKVError(VKV_EINVAL, vkv_last_error())
+        self.workspace = torch.empty((nbytes,), dtype=torch.uint8, device=device)
+        self.args.workspace = _ptr(self.workspace)
+        self.args.workspace_bytes = nbytes
+
+    def bind(self, q, kv):
+        torch = _torch()
+        B, Hq, G, n = self.shape
+        _need(q, torch.int16, (B, Hq, 128), "q")
+        _need(kv, torch.int16, (B, G, n, 2, 128), "kv", device=kv.is_cuda)
+        self.args.q, self.args.kv = _ptr(q), _ptr(kv)
+        self._keep = (q, kv)
+        return self
+
+    def launch(self, stream=None):
+        _check(vkv_dense_attention(self.args, _stream(stream)))
+        return self.out
