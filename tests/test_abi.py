@@ -212,3 +212,13 @@ def test_dense_validation(kw, frag):
     assert vk.vkv_dense_attention(a, None) == vk.VKV_EINVAL
     msg = vk.vkv_last_error()
     assert frag in msg, msg
+
+
+def test_one_hip_runtime_in_process():
+    """The binding loads torch (when installed) before the library, so the
+    process maps a single HIP runtime: the library's pointers and torch's
+    must belong to the same one."""
+    pytest.importorskip("torch")
+    maps = open("/proc/self/maps").read().splitlines()
+    hip = {l.split()[-1] for l in maps if "libamdhip64" in l}
+    assert len(hip) == 1, hip

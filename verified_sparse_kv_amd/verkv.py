@@ -84,6 +84,14 @@ def _load():
         raise ImportError(
             f"{LIB_PATH} is missing: build it with "
             "`python -m verified_sparse_kv_amd.build` (there is no fallback)")
+    # torch first when it is installed: its bundled HIP runtime then
+    # satisfies the library's dependency (same soname), so the process holds
+    # one HIP runtime; loading the library first would map the system
+    # runtime beside torch's, and pointers of one are unknown to the other
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     for name in EXPORTS:
         if not hasattr(lib, name):
