@@ -187,6 +187,47 @@ def test_decode_uniform_planning_weights(est):
     gc.say(f"  {s}")
 
 
+def _forced(n_sink, n_local, budget):
+    def f(w):
+        w["n_sink"], w["n_local"], w["budget"] = n_sink, n_local, budget
+    return f
+
+
+@pytest.mark.parametrize("n,sink,local,budget,est", [
+    (1, 64, 64, 129, 0),       # one token, forced: L empty
+    (100, 64, 64, 129, 0),     # every token forced: L empty
+    (300, 4, 4, 40, 0),        # a short context
+    (300, 4, 4, 40, 2),
+    (513, 4, 8, 60, 0),        # one token past a scan chunk
+    (2049, 16, 16, 160, 0),    # one token past a row sub-chunk
+    (2049, 16, 16, 160, 2),
+])
+def test_decode_short_and_ragged_contexts(n, sink, local, budget, est):
+    """Contexts shorter than a chunk or one token past one, and the empty L
+    of a fully forced context (then nothing is estimated or fetched and the
+    output is exact attention)."""
+    w, gpu, heads, unions, eps = _decode_case("c2", est=est, n=n, G=2, B=2,
+                                              mutate=_forced(sink, local, budget))
+    s_ = gc.compare(w, gpu, heads, unions, eps, est=est)
+    gc.say(f"  {s_}")
+    if sink + local >= n:
+        assert s_["fetched"] == 0 and np.all(gpu["eps_hat0"] == 0.0)
+        for b in range(w["B"]):
+            for h in range(w["Hq"]):
+                kv = bf16_to_f32(w["host_kv"][b, h // (w["Hq"] // w["G"])])
+                o_ref, _ = od.exact_attention(bf16_to_f32(w["q"][b, h]),
+                                              kv[:, 0], kv[:, 1])
+                err = np.linalg.norm(gpu["out"][b, h] - o_ref) / np.linalg.norm(o_ref)
+                assert err <= gc.TOL_O, (b, h, err)
+
+
+def test_decode_three_kv_heads_three_requests():
+    """Request and KV-head counts that are not powers of two."""
+    w, gpu, heads, unions, eps = _decode_case("c2", n=3000, G=3, B=3)
+    s_ = gc.compare(w, gpu, heads, unions, eps)
+    gc.say(f"  {s_}")
+
+
 def test_decode_c2_reduced():
     w, gpu, heads, unions, eps = _decode_case("c2", n=5000, G=2)
     s = gc.compare(w, gpu, heads, unions, eps)

@@ -14,7 +14,7 @@
 //             weighted sum of V); the sixteen lane groups merge in LDS into
 //             the workgroup's partial.
 //   dd_merge  grid (query heads, requests): the log-sum-exp merge of the
-//             partials into o and log D, in a fixed order.
+//             partials into o and log D, in a fixed order (float64 sums).
 
 #include <math.h>
 
@@ -175,14 +175,30 @@ __global__ __launch_bounds__(kHeadDim) void dd_merge(DenseParams p) {
   const size_t row = (size_t)b * p.Hq + h;
   const float *pm = p.pm + row * p.P;
   const float *pd = p.pd + row * p.P;
-  float mx = -INFINITY;
-  for (int j = 0; j < p.P; ++j)
-    if (pd[j] > 0.0f) mx = fmaxf(mx, pm[j]);
+  // the partials' shifts and sums in LDS (P <= 64), one load per thread
+  __shared__ float s_m[64], s_d[64], s_f[64];
+  __shared__ float s_mx;
+  if (k < p.P) {
+    s_m[k] = pm[k];
+    s_d[k] = pd[k];
+  }
+  __syncthreads();
+  if (k == 0) {
+    float mx = -INFINITY;
+    for (int j = 0; j < p.P; ++j)
+      if (s_d[j] > 0.0f) mx = fmaxf(mx, s_m[j]);
+    s_mx = mx;
+  }
+  __syncthreads();
+  const float mx = s_mx;
+  if (k < p.P) s_f[k] = s_d[k] > 0.0f ? expf(s_m[k] - mx) : 0.0f;
+  __syncthreads();
+  // fixed order over the partials; their weighted V sums are independent
+  // loads, all in flight at once
   double dd = 0.0, oo = 0.0;
   for (int j = 0; j < p.P; ++j) {
-    if (!(pd[j] > 0.0f)) continue;
-    const double f = exp((double)pm[j] - (double)mx);
-    dd += (double)pd[j] * f;
+    const double f = (double)s_f[j];
+    dd += (double)s_d[j] * f;
     oo += (double)p.po[(row * p.P + j) * kHeadDim + k] * f;
   }
   p.out[row * kHeadDim + k] = (float)(oo / dd);
@@ -197,7 +213,7 @@ DenseLayout dense_layout(const vkv_dense_args &a) {
   // about 1024 workgroups (enough host loads in flight for the link), at
   // least 256 rows each, at most 64 parts per KV head
   long long P = (1024 + groups - 1) / groups;
-  P = std::min<long long>(P, 64);
+  P = std::min<long long>(P, 64);  // (the merge holds 64 partials in LDS)
   P = std::min<long long>(P, (a.n_tokens + 255) / 256);
   L.parts = (int)std::max<long long>(P, 1);
   const size_t rows = (size_t)a.batch * a.n_q_heads;
