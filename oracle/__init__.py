@@ -14,8 +14,9 @@ Compression for LLM Inference" (Jha, Kumar, Chowdhury, Agrawal, Desai):
   1, 2, 3", SC'11).
 * ``oracle.compress`` -- PoissonComp (Algorithm 1, §4.1, eq. 3).
 * ``oracle.decode``   -- KVFetch (Algorithm 2, §4.2: Definition 2 / eq. 5,
-  Theorem 1 / eq. 6, Lemma 1 / eq. 7, eqs. 9-10, Theorem 2) and the
-  corrected attention output (§3, eq. 1).
+  Theorem 1 / eq. 6, Lemma 1 / eq. 7, eqs. 9-10, Theorem 2), the binary
+  shrinkage of Appendix A.2, the corrected attention output (§3, eq. 1) and
+  the Dense baselines of §5 (exact attention over the whole cache).
 
 Parity status of each function is stated in its docstring; every function is
 pinned by ``tests/test_oracle_*.py`` against closed forms, brute force or

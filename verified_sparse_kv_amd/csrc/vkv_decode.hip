@@ -188,17 +188,26 @@ __device__ __forceinline__ LamRule lam_rule(float beta, int est,
   return q;
 }
 
+// (1 - r) / r with the hardware reciprocal (within 2 ulp): the same
+// expression in every pass that forms it, so all passes agree bit for bit.
+__device__ __forceinline__ float qr_of(float r) {
+  return (1.0f - r) * __builtin_amdgcn_rcpf(r);
+}
+
 // lambda and the three certificate terms of Lemma 1 for the token of L at
-// `pos` with planning weight wt.
+// `pos` with planning weight wt. Divisions and the square root of the gain
+// use the hardware reciprocal and square root (~1 ulp each): the terms only
+// order tokens and feed float64 sums checked to 1e-4, and every pass uses
+// these same functions.
 __device__ __forceinline__ Terms token_terms_w(float wt, float r,
                                                const LamRule &lr, int pos) {
   Terms t;
   t.wt = wt;
-  t.qr = (1.0f - r) / r;
+  t.qr = qr_of(r);
   float lam = 1.0f;
   if (lr.est == VKV_EST_CLIP) {
     if (wt > 0.0f) {
-      const float x = lr.beta * r / (wt * (1.0f - r));
+      const float x = lr.beta * r * __builtin_amdgcn_rcpf(wt * (1.0f - r));
       lam = fminf(1.0f, fmaxf(r, x));
     }
   } else if (lr.est == VKV_EST_BINARY) {
@@ -208,7 +217,7 @@ __device__ __forceinline__ Terms token_terms_w(float wt, float r,
   t.bi = wt * (1.0f - lam);
   const float lw = lam * wt;
   t.vi = lw * lw * t.qr;
-  t.rb = lw * fmaxf(r, 1.0f - r) / r;
+  t.rb = lw * fmaxf(r, 1.0f - r) * __builtin_amdgcn_rcpf(r);
   return t;
 }
 
@@ -247,10 +256,10 @@ __device__ __forceinline__ float token_gain(const Terms &t, int pos,
   const float b1 = rs.b1;
   const float bp = (pos == rs.amax) ? rs.b2 : b1;
   const float vp = (float)fmax(rs.VL - (double)t.vi, 0.0);
-  const float sp = sqrtf(a * a * bp * bp + 2.0f * vp * l);
+  const float sp = __builtin_amdgcn_sqrtf(a * a * bp * bp + 2.0f * vp * l);
   const float num = a * a * (b1 - bp) * (b1 + bp) + 2.0f * t.vi * l;
   const float den = rs.s_full_f + sp;
-  const float frac = den > 0.0f ? num / den : 0.0f;
+  const float frac = den > 0.0f ? num * __builtin_amdgcn_rcpf(den) : 0.0f;
   return t.bi + a * (b1 - bp) + frac;
 }
 
@@ -993,8 +1002,8 @@ constexpr int kSelUnroll = 4;       // streamed tokens per thread in flight
 constexpr int kBetaPts = 4;         // points of h per Newton pass
 constexpr int kBetaRec = 3 * kBetaPts + 1;  // + the band count
 constexpr int kBetaLaunches = 2;    // Newton passes (pass 0 is in the scan)
-constexpr int kBandChunk = 512;     // band tokens a chunk may store
-constexpr int kBandMax = 1024;      // band tokens a row may be settled from
+constexpr int kBandChunk = 1024;    // band tokens a chunk may store
+constexpr int kBandMax = 2048;      // band tokens a row may be settled from
 constexpr int kMaxChunks = kMaxTokens / kRowChunk;
 constexpr int kBetaPassMax = 96;    // never reached: the bracket shrinks >= 2x
 constexpr int kCandMax = 8192;      // candidates held by the walk
@@ -1682,7 +1691,7 @@ __device__ __forceinline__ void bin_hist_pass(const DParams &p, int row, int bg,
     for (int u = 0; u < kRowTok; ++u) {
       if (!(r8[u] < 1.0f)) continue;
       const float wt = expf(s8[u] - m);
-      const float qr = (1.0f - r8[u]) / r8[u];
+      const float qr = qr_of(r8[u]);
       atomicAdd(&s_h[(int)(bin_key(wt, qr, row_pos(cc, u)) >> sel_off(0))], 1u);
     }
 #pragma unroll
@@ -1740,7 +1749,7 @@ __device__ __forceinline__ void bin_collect_pass(const DParams &p, int row,
       float a = 0.0f;
       if (r8[u] < 1.0f) {
         const float wt = expf(s8[u] - m);
-        const float qr = (1.0f - r8[u]) / r8[u];
+        const float qr = qr_of(r8[u]);
         key = bin_key(wt, qr, row_pos(cc, u));
         a = wt * (1.0f - r8[u]);
         take = key >= lo;
@@ -1914,7 +1923,7 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rbin(DParams p) {
       for (int u = 0; u < U; ++u) {
         if (!(ru[u] < 1.0f)) continue;
         const float wt = expf(su[u] - m);
-        const float qr = (1.0f - ru[u]) / ru[u];
+        const float qr = qr_of(ru[u]);
         f(bin_key(wt, qr, base + u * kPlanThreads + (int)threadIdx.x),
           wt * (1.0f - ru[u]));
       }
@@ -2260,7 +2269,7 @@ __device__ __forceinline__ void row_certificate(const DParams &p, CertShare sh,
     z.amax = (y2 < y1) ? yq : -1;
     z.s_full = sqrt(a * a * (double)y1 * (double)y1 + 2.0 * tv * l);
     const float af = (float)a, lf = (float)l;
-    z.s_full_f = sqrtf(af * af * y1 * y1 + 2.0f * (float)tv * lf);
+    z.s_full_f = __builtin_amdgcn_sqrtf(af * af * y1 * y1 + 2.0f * (float)tv * lf);
     const double e0 = (tb + a * (double)y1 + z.s_full) / dnorm;
     z.eps0 = e0;
     z.eps1 = (float)e0;
@@ -2458,7 +2467,7 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
         float tb;
         if (kbi) {
           bd = (double)kbi[k];
-          vd = (double)klw[k] * (double)klw[k] * (double)((1.0f - rb[k]) / rb[k]);
+          vd = (double)klw[k] * (double)klw[k] * (double)qr_of(rb[k]);
           tb = krb[k];
         } else {
           const Terms t = token_terms_w(expf(sb[k] - m), rb[k], lr, key_pos(kb[k]));
