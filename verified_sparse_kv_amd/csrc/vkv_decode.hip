@@ -569,7 +569,11 @@ __device__ __forceinline__ void clear_bin_hist(const DParams &p, int c, int b,
 template <int GRP, int SD>
 __device__ __forceinline__ void scan_body(const DParams &p, int c, int g,
                                           int b) {
-  constexpr int LPT = SD / 8;           // lanes per token (16 bytes each)
+  // 16 sketch dimensions (32 bytes) per lane: two lanes per token at
+  // s = 32, one at s = 16 (fewer cross-lane sums and selects per token than
+  // narrower lanes; the FMAs are the same)
+  constexpr int DPL = 16;
+  constexpr int LPT = SD / DPL;         // lanes per token
   constexpr int TPI = kBlock / LPT;     // tokens per block iteration
   const int bg = b * p.G + g;
   const int lane = threadIdx.x % kWave;
@@ -581,18 +585,22 @@ __device__ __forceinline__ void scan_body(const DParams &p, int c, int g,
   const int base = c * p.chunk;
   const int lim = min(base + p.chunk, p.n);
   // sub-batches of SUB tokens, UNR per thread (LPT lanes per token); the
-  // next sub-batch is loaded while one is used
-  constexpr int UNR = 4;
+  // next sub-batch is loaded while one is used (one token per lane: the
+  // registers of a second would cost the launch's resident workgroups a
+  // wave per SIMD)
+  constexpr int UNR = 1;
   constexpr int SUB = UNR * TPI;
   static_assert(kChunk % SUB == 0, "chunk");
-  uint4 raw[UNR], nraw[UNR];
+  uint4 raw[UNR][2], nraw[UNR][2];
   float rv[UNR], nrv[UNR];
-  auto load_sub = [&](int sb, uint4 (&ra)[UNR], float (&ro)[UNR]) {
+  auto load_sub = [&](int sb, uint4 (&ra)[UNR][2], float (&ro)[UNR]) {
 #pragma unroll
     for (int k = 0; k < UNR; ++k) {
       const int i = sb + k * TPI + (int)threadIdx.x / LPT;
       if (i < lim) {
-        ra[k] = *reinterpret_cast<const uint4 *>(sk + (size_t)i * SD + u * 8);
+        const uint4 *src = reinterpret_cast<const uint4 *>(sk + (size_t)i * SD + u * DPL);
+        ra[k][0] = src[0];
+        ra[k][1] = src[1];
         ro[k] = rr[i];
       } else {
         ro[k] = 1.0f;
@@ -654,11 +662,11 @@ __device__ __forceinline__ void scan_body(const DParams &p, int c, int g,
     }
     __syncthreads();
   }
-  float qv[GRP][8];
+  float qv[GRP][DPL];
 #pragma unroll
   for (int h = 0; h < GRP; ++h)
 #pragma unroll
-    for (int k = 0; k < 8; ++k) qv[h][k] = s_qp[h][u * 8 + k];
+    for (int k = 0; k < DPL; ++k) qv[h][k] = s_qp[h][u * DPL + k];
 
   // lane u of a token keeps the heads u, u + LPT, ... (NH of them)
   constexpr int NH = (GRP + LPT - 1) / LPT;
@@ -672,14 +680,15 @@ __device__ __forceinline__ void scan_body(const DParams &p, int c, int g,
 #pragma unroll
     for (int k = 0; k < UNR; ++k) {
       const int i = sb + k * TPI + (int)threadIdx.x / LPT;
-      float f[8];
-      unpack8(raw[k], f);
+      float f[DPL];
+      unpack8(raw[k][0], f);
+      unpack8(raw[k][1], f + 8);
       float dot[GRP];
 #pragma unroll
       for (int h = 0; h < GRP; ++h) {
         float a = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a = __builtin_fmaf(qv[h][e], f[e], a);
+        for (int e = 0; e < DPL; ++e) a = __builtin_fmaf(qv[h][e], f[e], a);
         dot[h] = group_sum<LPT>(a);
       }
       if (i >= lim) continue;
@@ -705,7 +714,8 @@ __device__ __forceinline__ void scan_body(const DParams &p, int c, int g,
     }
 #pragma unroll
     for (int k = 0; k < UNR; ++k) {
-      raw[k] = nraw[k];
+      raw[k][0] = nraw[k][0];
+      raw[k][1] = nraw[k][1];
       rv[k] = nrv[k];
     }
   }
