@@ -1,0 +1,25 @@
+"""bench.py's command line on the CPU: asking for more than one GPU exits
+with a message before anything touches a device."""
+
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_bench_refuses_several_gpus():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_bench_help_lists_the_options():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--help"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0
+    for opt in ("--steps", "--warmup", "--config", "--estimator", "--no-dense",
+                "--no-cpu-baseline"):
+        assert opt in r.stdout, opt
