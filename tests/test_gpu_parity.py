@@ -9,7 +9,8 @@ import pytest
 from oracle import compress as oc
 from oracle import decode as od
 from tests import gpu_cases as gc
-from workloads import CONFIGS, bf16_bits, bf16_to_f32, make_c5_tau, resident_cap
+from workloads import (CONFIGS, bf16_bits, bf16_to_f32, make_c5_tau,
+                       make_decode_workload, resident_cap)
 
 pytestmark = pytest.mark.gpu
 
@@ -354,3 +355,39 @@ def test_decode_deterministic():
     b = gc.run_library(w, dev, w["eps"], w["delta"])
     for key in ("k_star", "fetch_count", "fetch_idx", "eps_hat0"):
         assert np.array_equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("est", [0, 2])
+def test_decode_certificate_coverage_on_gpu(est):
+    """Theorem 2 on the library's own outputs: over 400 fresh Poisson samples
+    (Philox seeds) of the tiny layer, planned with exact weights, the
+    estimate stays within eps^(L') of the true denominator with frequency
+    >= 1 - delta (3 sigma slack)."""
+    w = make_decode_workload("c1", seed=0)
+    dev = torch.device("cuda")
+    kb = w["host_kv"][:, :, :, 0, :]
+    vb = w["host_kv"][:, :, :, 1, :]
+    t_tau = torch.from_numpy(w["tau"]).to(dev)
+    t_k = torch.from_numpy(np.ascontiguousarray(kb).view(np.int16)).to(dev)
+    t_v = torch.from_numpy(np.ascontiguousarray(vb).view(np.int16)).to(dev)
+    host_kv = torch.from_numpy(w["host_kv"].view(np.int16)).pin_memory()
+    q = torch.from_numpy(w["q"].view(np.int16)).to(dev)
+    sk = torch.from_numpy(w["sketch"].view(np.int16)).to(dev)
+    proj = torch.from_numpy(w["proj"]).to(dev)
+    kv = bf16_to_f32(w["host_kv"][0, 0])
+    _, logd = od.exact_attention(bf16_to_f32(w["q"][0, 0]), kv[:, 0], kv[:, 1])
+    cap = 512
+    delta, eps = w["delta"], 0.1
+    n_trials, fails = 400, 0
+    for s in range(n_trials):
+        comp = vk.compress(t_tau, t_k, t_v, w["budget"], w["n_sink"],
+                           w["n_local"], 5000 + s, cap)
+        out = vk.decode_step(q, comp["resident_kv"], comp["resident_idx"],
+                             comp["resident_count"], sk, proj, comp["r"],
+                             host_kv, eps, delta, estimator=est, weights=1)
+        torch.cuda.synchronize()
+        dh = float(out["d_hat"][0, 0]) * math.exp(float(out["log_shift"][0, 0]))
+        err = abs(dh / math.exp(logd) - 1.0)
+        fails += err > float(out["eps_hat"][0, 0])
+    gc.say(f"  coverage failures {fails} of {n_trials} (delta {delta})")
+    assert fails <= delta * n_trials + 3 * math.sqrt(delta * n_trials)
