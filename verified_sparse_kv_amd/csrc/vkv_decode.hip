@@ -826,107 +826,132 @@ __device__ __forceinline__ void scan_exact_body(const DParams &p, int c,
 
 // ------------------------------------------------------------ dk_resident
 // The group's resident rows are split evenly over gridDim.x workgroups.
+// Exact logits of the resident rows by matrix cores: per wave, tiles of 16
+// rows times the group's query heads (padded to 16 columns) with
+// v_mfma_f32_16x16x16_bf16 over eight 16-dimension slices of d. The inputs
+// are the bf16 K rows and q as stored, and products of bf16 values are exact
+// in fp32, so the logits match a vector dot product up to the order of the
+// fp32 additions. The k index of the product is permuted so that each lane
+// reads 64 contiguous bytes of its row: lane (g, i) of a wave (g = lane / 16,
+// i = lane % 16) loads dimensions 32 g .. 32 g + 31 of row i of the tile, and
+// slice c takes dimensions 32 g + 4 c .. 32 g + 4 c + 3 from each lane group;
+// q is read with the same permutation. Lane (g, j) then holds the logits of
+// rows 4 g .. 4 g + 3 of the tile for query head j.
+typedef short vkv_short4 __attribute__((ext_vector_type(4)));
+typedef float vkv_float4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ vkv_short4 mfma_slice(const uint4 (&w)[4], int c) {
+  // bf16 elements 4c .. 4c + 3 of the lane's 32 (words 2c and 2c + 1)
+  const uint32_t *x = reinterpret_cast<const uint32_t *>(w);
+  const uint32_t lo = x[2 * c], hi = x[2 * c + 1];
+  vkv_short4 r;
+  r[0] = (short)(lo & 0xFFFFu);
+  r[1] = (short)(lo >> 16);
+  r[2] = (short)(hi & 0xFFFFu);
+  r[3] = (short)(hi >> 16);
+  return r;
+}
+
 template <int GRP>
 __device__ __forceinline__ void resident_body(const DParams &p, int c, int g,
                                               int b) {
+  static_assert(GRP <= 16, "heads per MFMA tile");
   const int bg = b * p.G + g;
-  const int lane = threadIdx.x % kWave;
-  const int u = lane % 16;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int lg = lane / 16, li = lane % 16;  // lane group, row / head index
   __shared__ uint32_t s_ured[kBlock / kWave];
-  float qv[GRP][8];
+  // B operand: q of head li (zero for the padding columns), permuted slices
+  vkv_short4 bq[8];
+  {
+    uint4 w[4];
 #pragma unroll
-  for (int h = 0; h < GRP; ++h) {
-    const uint4 raw = *reinterpret_cast<const uint4 *>(
-        p.q + (size_t)row_of(p, b, g, h, GRP) * kHeadDim + u * 8);
-    unpack8(raw, qv[h]);
+    for (int k = 0; k < 4; ++k) w[k] = make_uint4(0u, 0u, 0u, 0u);
+    if (li < GRP) {
+      const uint4 *src = reinterpret_cast<const uint4 *>(
+          p.q + (size_t)row_of(p, b, g, li, GRP) * kHeadDim + 32 * lg);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w[k] = src[k];
+    }
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) bq[cc] = mfma_slice(w, cc);
   }
   int cnt = p.rcount[bg];
   bool bad = cnt < 0 || cnt > p.cap;
   cnt = max(0, min(cnt, p.cap));
   const int32_t *ridx = p.ridx + (size_t)bg * p.cap;
   const float *rr = p.r + (size_t)bg * p.n;
-  float mx[GRP];
-  float hm[GRP];   // running shift and sum over this thread's H rows
-  double hsum[GRP];
-#pragma unroll
-  for (int h = 0; h < GRP; ++h) {
-    mx[h] = -INFINITY;
-    hm[h] = -INFINITY;
-    hsum[h] = 0.0;
-  }
+  const int hl = li < GRP ? li : 0;  // this lane's head (lanes li >= GRP idle)
+  float mx = -INFINITY, hm = -INFINITY;  // this lane's head: max, H shift
+  double hsum = 0.0;
   uint32_t n_h = 0;
   int lo, hi;
   split_range(cnt, p.ncr, c, lo, hi);
-  // RB rows per 16-lane slot at a time: their positions and K rows are
-  // loaded together, then r at those positions; the next batch's positions
-  // and K rows load while this one's r arrives and is used
-  constexpr int RB = 4, SLOTS = kBlock / 16;
-  int pos[RB], prv[RB], npos[RB], nprv[RB];
-  uint4 raw[RB], nraw[RB];
-  auto load_rows = [&](int j0, int (&ps)[RB], int (&pv)[RB], uint4 (&ra)[RB]) {
+  constexpr int WV = kBlock / kWave;
+  auto load_tile = [&](int t0, uint4 (&w)[4]) {
+    const int j = t0 + li;
+    if (j < hi) {
+      const uint4 *src = reinterpret_cast<const uint4 *>(
+          p.rkv + ((size_t)bg * p.cap + j) * 2 * kHeadDim + 32 * lg);
 #pragma unroll
-    for (int k = 0; k < RB; ++k) {
-      const int j = j0 + k * SLOTS + (int)threadIdx.x / 16;
-      ps[k] = -1;
-      pv[k] = -1;
-      if (j < hi) {
-        ps[k] = ridx[j];
-        if (j > 0) pv[k] = ridx[j - 1];
-        ra[k] = *reinterpret_cast<const uint4 *>(
-            p.rkv + ((size_t)bg * p.cap + j) * 2 * kHeadDim + u * 8);
-      }
+      for (int k = 0; k < 4; ++k) w[k] = src[k];
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w[k] = make_uint4(0u, 0u, 0u, 0u);
     }
   };
-  if (lo < hi) load_rows(lo, pos, prv, raw);
-  for (int j0 = lo; j0 < hi; j0 += RB * SLOTS) {
-    bool okk[RB];
-    float rk[RB];
+  uint4 cur[4], nxt[4];
+  int t0 = lo + 16 * wave;
+  if (t0 < hi) load_tile(t0, cur);
+  for (; t0 < hi; t0 += 16 * WV) {
+    if (t0 + 16 * WV < hi) load_tile(t0 + 16 * WV, nxt);  // next tile in flight
+    // the rows this lane post-processes: 4 lg .. 4 lg + 3 of the tile
+    int pos[4];
+    bool okr[4];
+    float rk[4];
 #pragma unroll
-    for (int k = 0; k < RB; ++k) {
-      const int j = j0 + k * SLOTS + (int)threadIdx.x / 16;
-      okk[k] = j < hi && pos[k] >= 0 && pos[k] < p.n && (j == 0 || prv[k] < pos[k]);
-      rk[k] = okk[k] ? rr[pos[k]] : 0.0f;
+    for (int t = 0; t < 4; ++t) {
+      const int j = t0 + 4 * lg + t;
+      pos[t] = -1;
+      okr[t] = false;
+      if (li < GRP && j < hi) {
+        pos[t] = ridx[j];
+        const int pv = j > 0 ? ridx[j - 1] : -1;
+        okr[t] = pos[t] >= 0 && pos[t] < p.n && (j == 0 || pv < pos[t]);
+      }
+      rk[t] = okr[t] ? rr[pos[t]] : 0.0f;
     }
-    if (j0 + RB * SLOTS < hi) load_rows(j0 + RB * SLOTS, npos, nprv, nraw);
+    vkv_float4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int k = 0; k < RB; ++k) {
-      const int j = j0 + k * SLOTS + (int)threadIdx.x / 16;
-      if (j >= hi) continue;  // (uniform over the 16-lane slot)
-      const bool ok = okk[k];
-      const bool in_h = ok && rk[k] >= 1.0f;
-      float f[8];
-      unpack8(raw[k], f);
+    for (int cc = 0; cc < 8; ++cc)
+      acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(mfma_slice(cur, cc), bq[cc],
+                                                     acc, 0, 0, 0);
+    if (li < GRP) {
 #pragma unroll
-      for (int h = 0; h < GRP; ++h) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(qv[h][e], f[e], acc);
-        const float dot = group_sum<16>(acc) * kInvSqrtD;
-        if (u == h) p.ell[(size_t)row_of(p, b, g, h, GRP) * p.cap + j] = dot;
-        mx[h] = fmaxf(mx[h], dot);
-        if (u == 0 && in_h) {  // sum over H of exp(l), with a running shift
-          if (dot > hm[h]) {
-            hsum[h] = hsum[h] * (double)expf(hm[h] - dot) + 1.0;
-            hm[h] = dot;
+      for (int t = 0; t < 4; ++t) {
+        const int j = t0 + 4 * lg + t;
+        if (j >= hi) continue;
+        const float dot = acc[t] * kInvSqrtD;
+        p.ell[(size_t)row_of(p, b, g, hl, GRP) * p.cap + j] = dot;
+        mx = fmaxf(mx, dot);
+        const bool in_h = okr[t] && rk[t] >= 1.0f;
+        if (in_h) {  // sum over H of exp(l), with a running shift
+          if (dot > hm) {
+            hsum = hsum * (double)expf(hm - dot) + 1.0;
+            hm = dot;
           } else {
-            hsum[h] += (double)expf(dot - hm[h]);
+            hsum += (double)expf(dot - hm);
+          }
+        }
+        if (li == 0) {
+          if (okr[t]) {
+            if (in_h) ++n_h;
+          } else {
+            bad = true;
           }
         }
       }
-      if (u == 0) {
-        if (ok) {
-          if (in_h) ++n_h;
-        } else {
-          bad = true;
-        }
-      }
     }
 #pragma unroll
-    for (int k = 0; k < RB; ++k) {
-      pos[k] = npos[k];
-      prv[k] = nprv[k];
-      raw[k] = nraw[k];
-    }
+    for (int k = 0; k < 4; ++k) cur[k] = nxt[k];
   }
   const int np = p.nch + p.ncr;
   {
@@ -934,17 +959,21 @@ __device__ __forceinline__ void resident_body(const DParams &p, int c, int g,
     if (threadIdx.x == 0)
       p.fstat[(size_t)bg * np + p.nch + c] = any ? VKV_STATUS_BAD_RESIDENT : 0u;
   }
-  blk_combine<float, GRP, kBlock, OpMax<float>>(mx);
+  float mxv[GRP];
+#pragma unroll
+  for (int h = 0; h < GRP; ++h) mxv[h] = (li < GRP && h == hl) ? mx : -INFINITY;
+  blk_combine<float, GRP, kBlock, OpMax<float>>(mxv);
+  double hsv[GRP];
 #pragma unroll
   for (int h = 0; h < GRP; ++h)
-    hsum[h] = hsum[h] > 0.0 ? hsum[h] * (double)expf(hm[h] - mx[h]) : 0.0;
-  blk_reduce<double, GRP, kBlock>(hsum);
+    hsv[h] = (li < GRP && h == hl && hsum > 0.0) ? hsum * (double)expf(hm - mxv[h]) : 0.0;
+  blk_reduce<double, GRP, kBlock>(hsv);
   if (threadIdx.x == 0) {
 #pragma unroll
     for (int h = 0; h < GRP; ++h) {
       const int row = row_of(p, b, g, h, GRP);
-      p.pmax[(size_t)row * np + p.nch + c] = mx[h];
-      p.hres[(size_t)row * p.ncr + c] = hsum[h];
+      p.pmax[(size_t)row * np + p.nch + c] = mxv[h];
+      p.hres[(size_t)row * p.ncr + c] = hsv[h];
     }
   }
   const uint32_t th = block_sum<uint32_t>(n_h, s_ured);
