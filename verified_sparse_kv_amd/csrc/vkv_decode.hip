@@ -1632,7 +1632,6 @@ __device__ __forceinline__ BetaState beta_settle(const DParams &p, BetaState st,
   __syncthreads();
   if (!s_bok) return st;
   const int nb = s_bo[p.nrc];
-  double bs[3] = {0.0, 0.0, 0.0};  // the band's sums of w~ and rho, its size
   for (int k = threadIdx.x; k < nb; k += kBlock) {
     int lo = 0, hi = p.nrc;  // the chunk holding entry k
     while (hi - lo > 1) {
@@ -1642,40 +1641,54 @@ __device__ __forceinline__ BetaState beta_settle(const DParams &p, BetaState st,
     const float2 e = band[(size_t)lo * kBandChunk + (k - s_bo[lo])];
     s_bw[k] = e.x;
     s_br[k] = e.y;
-    bs[0] += (double)e.x;
-    bs[1] += (double)e.y;
-    bs[2] += 1.0;
   }
-  blk_reduce<double, 3, kBlock>(bs);
-  // the tokens active at every point of the bracket (v holds the sums at lo)
-  const double aw = v[0] - bs[0], ar = v[1] - bs[1], ac = v[2] - bs[2];
-  // Newton steps over the band in LDS
-  for (int it = 0; it < kBetaPassMax && !st.done; ++it) {
-    double pts[kBetaPts], u[kBetaRec];
-    beta_points(st, pts);
+  __syncthreads();
+  // the band's sums and the Newton steps over it by the first wave alone
+  // (its sums fold by DPP: no workgroup barrier per step); the result goes
+  // to the other waves through LDS
+  __shared__ BetaState s_st;
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    double bs[3] = {0.0, 0.0, 0.0};  // the band's sums of w~ and rho, its size
+    for (int k = lane; k < nb; k += kWave) {
+      bs[0] += (double)s_bw[k];
+      bs[1] += (double)s_br[k];
+      bs[2] += 1.0;
+    }
 #pragma unroll
-    for (int k = 0; k < kBetaRec; ++k) u[k] = 0.0;
-    for (int k = threadIdx.x; k < nb; k += kBlock) {
-      const double w = (double)s_bw[k], rh = (double)s_br[k];
+    for (int k = 0; k < 3; ++k) bs[k] = wave_fold<double, OpSum<double>>(bs[k]);
+    // the tokens active at every point of the bracket (v: the sums at lo)
+    const double aw = v[0] - bs[0], ar = v[1] - bs[1], ac = v[2] - bs[2];
+    for (int it = 0; it < kBetaPassMax && !st.done; ++it) {
+      double pts[kBetaPts], u[kBetaRec];
+      beta_points(st, pts);
 #pragma unroll
-      for (int j = 0; j < kBetaPts; ++j) {
-        if (w - pts[j] * rh > 0.0) {
-          u[3 * j] += w;
-          u[3 * j + 1] += rh;
-          u[3 * j + 2] += 1.0;
+      for (int k = 0; k < kBetaRec; ++k) u[k] = 0.0;
+      for (int k = lane; k < nb; k += kWave) {
+        const double w = (double)s_bw[k], rh = (double)s_br[k];
+#pragma unroll
+        for (int j = 0; j < kBetaPts; ++j) {
+          if (w - pts[j] * rh > 0.0) {
+            u[3 * j] += w;
+            u[3 * j + 1] += rh;
+            u[3 * j + 2] += 1.0;
+          }
         }
       }
-    }
-    blk_reduce<double, kBetaRec, kBlock>(u);
 #pragma unroll
-    for (int j = 0; j < kBetaPts; ++j) {
-      u[3 * j] += aw;
-      u[3 * j + 1] += ar;
-      u[3 * j + 2] += ac;
+      for (int k = 0; k < 3 * kBetaPts; ++k) u[k] = wave_fold<double, OpSum<double>>(u[k]);
+#pragma unroll
+      for (int j = 0; j < kBetaPts; ++j) {
+        u[3 * j] += aw;
+        u[3 * j + 1] += ar;
+        u[3 * j + 2] += ac;
+      }
+      st = beta_advance(st, u);
     }
-    st = beta_advance(st, u);
+    if (lane == 0) s_st = st;
   }
-  return st;
+  __syncthreads();
+  return s_st;
 }
 
 // ------------------------------------------------------------ binary shrinkage,
