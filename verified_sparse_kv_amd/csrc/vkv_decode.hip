@@ -1511,37 +1511,41 @@ __device__ __forceinline__ void beta_accumulate(const double (&pts)[kBetaPts],
   }
 }
 
-// This thread's share (records t, t + kBlock, ...) of a row's S chunk
-// records; with LB, slot 3 (the lower bound of pass 0) combines by maximum.
 // The per-chunk band counts of the records last loaded (LDS).
 __device__ __forceinline__ int *band_counts() {
   __shared__ int s_cnt[kMaxChunks];
   return s_cnt;
 }
+// Wave-level totals: every wave folds its lanes' shares by DPP on its own.
+// With shares taken by lane (records lane, lane + 64, ... in order) every
+// wave, and every workgroup of the row, gets the same bits without a
+// workgroup barrier.
 template <bool LB>
-__device__ __forceinline__ void beta_rec_load(const double *rec, int S,
+__device__ __forceinline__ void beta_rec_fold(double (&v)[kBetaRec]) {
+#pragma unroll
+  for (int k = 0; k < kBetaRec; ++k)
+    v[k] = (LB && k == 3) ? wave_fold<double, OpMax<double>>(v[k])
+                          : wave_fold<double, OpSum<double>>(v[k]);
+}
+// A row's S <= 64 chunk records combined by every wave (see beta_rec_fold);
+// the first wave also keeps the per-chunk band counts in LDS.
+__device__ __forceinline__ void beta_rec_wave(const double *rec, int S,
                                               double (&v)[kBetaRec]) {
+  const int lane = threadIdx.x % kWave;
 #pragma unroll
   for (int k = 0; k < kBetaRec; ++k) v[k] = 0.0;
-  for (int t = threadIdx.x; t < S; t += kBlock) {
+  for (int t = lane; t < S; t += kWave) {
 #pragma unroll
-    for (int k = 0; k < kBetaRec; ++k) {
-      const double x = rec[(size_t)t * kBetaRec + k];
-      v[k] = (LB && k == 3) ? fmax(v[k], x) : v[k] + x;
-    }
-    if (!LB) band_counts()[t] = (int)rec[(size_t)t * kBetaRec + kBetaRec - 1];
+    for (int k = 0; k < kBetaRec; ++k) v[k] += rec[(size_t)t * kBetaRec + k];
+    if (threadIdx.x < kWave)
+      band_counts()[t] = (int)rec[(size_t)t * kBetaRec + kBetaRec - 1];
   }
-}
-// Fixed-order totals of the shares: the same in every workgroup.
-template <bool LB>
-__device__ __forceinline__ void beta_rec_total(double (&v)[kBetaRec]) {
-  const double mx = v[3];
-  blk_reduce<double, kBetaRec, kBlock>(v);
-  if (LB) v[3] = blk_max<double, kBlock>(mx);
+  beta_rec_fold<false>(v);
 }
 
 // The row's common shift m = max(max_R l, max_L s) and the pass-0 sums
-// rescaled to it, as this thread's share: slots 0-2 sum_L w~, sum rho over
+// rescaled to it, as this lane's share (beta_rec_fold totals them): slots
+// 0-2 sum_L w~, sum rho over
 // w~ > 0 and their count, slot 3 max w~ (1 - r) (combined by maximum), slot
 // 4 sum_H w. Workgroup 0 of the row stores m; with `check`, it also checks
 // that every token with r == 1 of the KV head is resident.
@@ -1549,14 +1553,15 @@ __device__ __forceinline__ float row_pass0(const DParams &p, int row, int bg,
                                            int c, bool check,
                                            double (&v)[kBetaRec]) {
   const int np = p.nch + p.ncr;
-  float pm[1] = {-INFINITY};
-  for (int t = threadIdx.x; t < np; t += kBlock)
-    pm[0] = fmaxf(pm[0], p.pmax[(size_t)row * np + t]);
-  blk_combine<float, 1, kBlock, OpMax<float>>(pm);
-  const float m = pm[0];
+  const int lane = threadIdx.x % kWave;
+  // (every wave on its own: lane-strided shares folded by DPP)
+  float pm = -INFINITY;
+  for (int t = lane; t < np; t += kWave)
+    pm = fmaxf(pm, p.pmax[(size_t)row * np + t]);
+  const float m = wave_fold<float, OpMax<float>>(pm);
 #pragma unroll
   for (int k = 0; k < kBetaRec; ++k) v[k] = 0.0;
-  for (int t = threadIdx.x; t < p.nch; t += kBlock) {
+  for (int t = lane; t < p.nch; t += kWave) {
     const double *rec = p.p0part + ((size_t)row * np + t) * 4;
     if (!(rec[0] > 0.0)) continue;
     const double f = exp((double)p.pmax[(size_t)row * np + t] - (double)m);
@@ -1565,7 +1570,7 @@ __device__ __forceinline__ float row_pass0(const DParams &p, int row, int bg,
     v[2] += rec[2];
     v[3] = fmax(v[3], rec[3] * f);
   }
-  for (int t = threadIdx.x; t < p.ncr; t += kBlock) {
+  for (int t = lane; t < p.ncr; t += kWave) {
     const double hs = p.hres[(size_t)row * p.ncr + t];
     if (hs > 0.0) v[4] += hs * exp((double)p.pmax[(size_t)row * np + p.nch + t] - (double)m);
   }
@@ -1856,21 +1861,19 @@ __global__ __launch_bounds__(kBlock) void dk_rbeta(DParams p, int pass) {
   float m;
   if (pass == 1) {
     m = row_pass0(p, row, bg, c, hq % GRP == 0, rv);
-    beta_rec_total<true>(rv);
+    beta_rec_fold<true>(rv);
     st = beta_init(rv, p.est);
   } else {
     m = p.rows[row].m;
-    beta_rec_load<false>(p.bpart + ((size_t)q * rows + row) * p.nrc * kBetaRec, p.nrc, rv);
     st = p.bstate[(size_t)q * rows + row];
+    if (!st.done)
+      beta_rec_wave(p.bpart + ((size_t)q * rows + row) * p.nrc * kBetaRec, p.nrc, rv);
   }
   double v[kBetaRec];
 #pragma unroll
   for (int k = 0; k < kBetaRec; ++k) v[k] = 0.0;
   double *out = p.bpart + (((size_t)(pass & 1) * rows + row) * p.nrc + c) * kBetaRec;
-  if (pass >= 2 && !st.done) {
-    beta_rec_total<false>(rv);
-    st = beta_settle(p, st, rv, row, q);
-  }
+  if (pass >= 2 && !st.done) st = beta_settle(p, st, rv, row, q);
   if (c == 0 && threadIdx.x == 0) p.bstate[(size_t)(pass & 1) * rows + row] = st;
   if (p.est == VKV_EST_BINARY) {  // (st.done: no beta* to find)
     if (pass == 1) bin_hist_pass(p, row, bg, cc0, cc1, m, r8, s8);
@@ -2201,12 +2204,10 @@ __global__ __launch_bounds__(kBlock) void dk_rcert(DParams p) {
   row_load(p, row, bg, cc0, r8, s8);
   const float m = p.rows[row].m;
   const int q = kBetaLaunches & 1;
-  double rv[kBetaRec];
-  beta_rec_load<false>(p.bpart + ((size_t)q * rows + row) * p.nrc * kBetaRec,
-                       p.nrc, rv);
   BetaState st = p.bstate[(size_t)q * rows + row];
-  if (!st.done) {
-    beta_rec_total<false>(rv);
+  if (!st.done) {  // (uniform: the same state in every workgroup)
+    double rv[kBetaRec];
+    beta_rec_wave(p.bpart + ((size_t)q * rows + row) * p.nrc * kBetaRec, p.nrc, rv);
     st = beta_settle(p, st, rv, row, q);
   }
   if (!st.done) {
@@ -2283,7 +2284,7 @@ __device__ __forceinline__ CertShare cert_rec_load(const DParams &p, int row) {
   z.cv[0] = z.cv[1] = 0.0;
   z.x1 = z.x2 = 0.0f;
   z.p1 = 0x7fffffff;
-  for (int t = threadIdx.x; t < p.nrc; t += kBlock) {
+  for (int t = threadIdx.x % kWave; t < p.nrc; t += kWave) {
     const CertPart cp = p.cpart[(size_t)row * p.nrc + t];
     z.cv[0] += cp.tb;
     z.cv[1] += cp.tv;
@@ -2299,11 +2300,18 @@ __device__ __forceinline__ void row_certificate(const DParams &p, CertShare sh,
                                                 double dnorm,
                                                 unsigned long long bkey,
                                                 RowState &rs) {
-  double cv[2] = {sh.cv[0], sh.cv[1]};
+  // (every wave folds the lane-strided shares on its own: sums by DPP, the
+  // top two by a butterfly of exact merges, the same in every lane)
+  double cv[2] = {wave_fold<double, OpSum<double>>(sh.cv[0]),
+                  wave_fold<double, OpSum<double>>(sh.cv[1])};
   float x1 = sh.x1, x2 = sh.x2;
   int p1 = sh.p1;
-  blk_reduce<double, 2, kBlock>(cv);
-  blk_top2<kBlock>(x1, p1, x2);
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const float y1 = __shfl_xor(x1, o, kWave), y2 = __shfl_xor(x2, o, kWave);
+    const int q1 = __shfl_xor(p1, o, kWave);
+    top2_merge(x1, p1, x2, y1, q1, y2);
+  }
   if (threadIdx.x == 0) {
     const float y1 = x1, y2 = x2;
     const int yq = p1;
