@@ -12,8 +12,9 @@ from pinned host memory and corrected attention -- for a fresh query.
 Prints one JSON line. ``value`` is q-head x context tokens per second over
 the timed steps (inputs resident in HBM, full cache in pinned host memory).
 The ``roofline`` object covers the longest-running HBM-bound kernel, timed
-with HIP events recorded by the library on its own stream inside the timed
-region; ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample.
+with a pair of HIP events that the kernel's own dispatch records on the
+library's stream, over as many steps as the timed region;
+``cpu_baseline`` times the fp64 CPU oracle on a bounded sample.
 """
 
 import argparse
@@ -314,8 +315,8 @@ def main():
     rc, bits = step.check_status()
     assert rc == 0, (rc, bits, vk.vkv_last_error())
     ms = (t1 - t0) * 1e3 / max(args.steps, 1)
-    # the same steps again with events around the dominant kernel only: its
-    # average duration on the library's stream
+    # the same steps again with events on the dominant kernel only (recorded
+    # by its dispatch): its average duration on the library's stream
     pairs = [timed_events(2) for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):

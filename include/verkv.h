@@ -156,7 +156,11 @@ typedef struct {
  *          hipEvent_t handles (created by the caller); event 0 is recorded on
  *          `stream` before the first kernel and event i + 1 after kernel i.
  *          NULL entries are skipped, so a caller can time one kernel without
- *          putting a record between every pair of kernels.
+ *          putting a record between every pair of kernels. When exactly the
+ *          two entries i and i + 1 are non-NULL, kernel i's own dispatch
+ *          records them (hipExtLaunchKernel): the span of that kernel alone,
+ *          as a kernel trace reports it. Phase 3 has no kernel unless the
+ *          estimator is VKV_EST_BINARY; its events are then plain records.
  */
 typedef struct {
   int32_t batch, n_q_heads, n_kv_heads, head_dim, n_tokens, sketch_dim, cap;

@@ -38,6 +38,8 @@
 
 #include <algorithm>
 
+#include <hip/hip_ext.h>
+
 #include "vkv_common.h"
 #include "vkv_internal.h"
 
@@ -3319,12 +3321,42 @@ __global__ __launch_bounds__(kBlock) void dk_attn(DParams p) {
   attn_merge_row(p, (int)blockIdx.y * p.Hq + (int)blockIdx.x);
 }
 
-// Records the timing event after kernel `k` when the caller asked for it.
+// The caller's timing events: entry k is recorded before the kernel of
+// phase k and entry k + 1 after it. When only the two entries of one phase
+// are given, its kernel's own dispatch records them (the span of that
+// kernel alone, with no marker packets around it).
 struct PhaseMark {
   void **ev;
   hipStream_t s;
+  int solo;  // the phase whose two entries alone are given, else -1
+  PhaseMark(void **e, hipStream_t st, int n) : ev(e), s(st), solo(-1) {
+    if (!ev) return;
+    int first = -1, count = 0;
+    for (int i = 0; i <= n; ++i)
+      if (ev[i]) {
+        if (first < 0) first = i;
+        ++count;
+      }
+    if (count == 2 && first < n && ev[first + 1]) solo = first;
+  }
   void operator()(int k) const {
-    if (ev && ev[k]) (void)hipEventRecord(static_cast<hipEvent_t>(ev[k]), s);
+    if (ev && ev[k] && k != solo && k != solo + 1)
+      (void)hipEventRecord(static_cast<hipEvent_t>(ev[k]), s);
+  }
+  // a phase with no kernel in this mode: its events as markers
+  void empty(int k) const {
+    if (k == solo) {
+      (void)hipEventRecord(static_cast<hipEvent_t>(ev[k]), s);
+      (void)hipEventRecord(static_cast<hipEvent_t>(ev[k + 1]), s);
+    }
+  }
+  template <typename... A>
+  void launch(int k, void (*f)(A...), dim3 g, dim3 b, A... args) const {
+    if (k == solo)
+      hipExtLaunchKernelGGL(f, g, b, 0, s, static_cast<hipEvent_t>(ev[k]),
+                            static_cast<hipEvent_t>(ev[k + 1]), 0u, args...);
+    else
+      hipLaunchKernelGGL(f, g, b, 0, s, args...);
   }
 };
 
@@ -3332,47 +3364,54 @@ template <int GRP>
 hipError_t run(const DParams &p, hipStream_t s, int sd, void **events) {
   const dim3 blk(kBlock);
   const dim3 gfront((unsigned)(p.nch + p.ncr), (unsigned)p.G, (unsigned)p.B);
-  const PhaseMark mark{events, s};
+  constexpr int kPhases = 9;  // the entries of kPhaseNames
+  const PhaseMark mark(events, s, kPhases);
   int k = 0;
-  mark(k++);
+  mark(k);
   if (p.weights == VKV_W_PERFECT)
-    dk_front_exact<GRP><<<gfront, blk, 0, s>>>(p);
+    mark.launch(k, dk_front_exact<GRP>, gfront, blk, p);
   else if (sd == 32)
-    dk_front<GRP, 32><<<gfront, blk, 0, s>>>(p);
+    mark.launch(k, dk_front<GRP, 32>, gfront, blk, p);
   else
-    dk_front<GRP, 16><<<gfront, blk, 0, s>>>(p);
-  mark(k++);
+    mark.launch(k, dk_front<GRP, 16>, gfront, blk, p);
+  mark(++k);
   const dim3 grow((unsigned)p.nrc, (unsigned)p.Hq, (unsigned)p.B);
   const dim3 gone((unsigned)p.Hq, (unsigned)p.B);
   for (int j = 1; j <= kBetaLaunches; ++j) {
-    dk_rbeta<GRP><<<grow, blk, 0, s>>>(p, j);
-    mark(k++);
+    mark.launch(k, dk_rbeta<GRP>, grow, blk, p, j);
+    mark(++k);
   }
-  if (p.est == VKV_EST_BINARY) dk_rbin<GRP><<<gone, dim3(kPlanThreads), 0, s>>>(p);
-  mark(k++);
-  dk_rcert<GRP><<<grow, blk, 0, s>>>(p);
-  mark(k++);
+  if (p.est == VKV_EST_BINARY)
+    mark.launch(k, dk_rbin<GRP>, gone, dim3(kPlanThreads), p);
+  else
+    mark.empty(k);
+  mark(++k);
+  mark.launch(k, dk_rcert<GRP>, grow, blk, p);
+  mark(++k);
   {
     // the register-heavy variant only while its grid fits in one round at
     // three waves per SIMD (768 workgroups)
     const dim3 gc((unsigned)p.nsel, (unsigned)p.Hq, (unsigned)p.B);
     if ((long long)p.nsel * p.Hq * p.B <= 768)
-      dk_rcand<GRP, true><<<gc, blk, 0, s>>>(p);
+      mark.launch(k, dk_rcand<GRP, true>, gc, blk, p);
     else
-      dk_rcand<GRP, false><<<gc, blk, 0, s>>>(p);
+      mark.launch(k, dk_rcand<GRP, false>, gc, blk, p);
   }
-  mark(k++);
-  dk_rwalk<GRP><<<gone, dim3(kPlanThreads), 0, s>>>(p);
-  mark(k++);
-  dk_fetch<GRP><<<dim3((unsigned)(p.ncr + kGatherWG), (unsigned)p.G, (unsigned)p.B), blk, 0, s>>>(p);
-  mark(k++);
-  dk_attn<<<dim3((unsigned)p.Hq, (unsigned)p.B), blk, 0, s>>>(p);
-  mark(k++);
+  mark(++k);
+  mark.launch(k, dk_rwalk<GRP>, gone, dim3(kPlanThreads), p);
+  mark(++k);
+  mark.launch(k, dk_fetch<GRP>,
+              dim3((unsigned)(p.ncr + kGatherWG), (unsigned)p.G, (unsigned)p.B), blk, p);
+  mark(++k);
+  mark.launch(k, dk_attn, dim3((unsigned)p.Hq, (unsigned)p.B), blk, p);
+  mark(++k);
   return hipGetLastError();
 }
 
 const char *const kPhaseNames[] = {
     "scan", "beta1", "beta2", "shrink", "cert", "cand", "walk", "fetch", "attn"};
+static_assert(sizeof(kPhaseNames) / sizeof(kPhaseNames[0]) == 9,
+              "one name per phase of run()");
 
 }  // namespace
 
