@@ -888,38 +888,50 @@ __device__ __forceinline__ void resident_body(const DParams &p, int c, int g,
   int lo, hi;
   split_range(cnt, p.ncr, c, lo, hi);
   constexpr int WV = kBlock / kWave;
+  // Loads are branch-free (indices past the range read its last row; the
+  // results for them are never used), so that the loop waits only for what
+  // it uses: the K tile one tile ahead, the resident positions two tiles
+  // ahead and their r one tile ahead.
   auto load_tile = [&](int t0, uint4 (&w)[4]) {
-    const int j = t0 + li;
-    if (j < hi) {
-      const uint4 *src = reinterpret_cast<const uint4 *>(
-          p.rkv + ((size_t)bg * p.cap + j) * 2 * kHeadDim + 32 * lg);
+    const int j = min(t0 + li, hi - 1);
+    const uint4 *src = reinterpret_cast<const uint4 *>(
+        p.rkv + ((size_t)bg * p.cap + j) * 2 * kHeadDim + 32 * lg);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) w[k] = src[k];
-    } else {
+    for (int k = 0; k < 4; ++k) w[k] = src[k];
+  };
+  // positions of rows t0 + 4 lg - 1 .. t0 + 4 lg + 3 (the row before first)
+  auto load_idx = [&](int t0, int (&pi)[5]) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) w[k] = make_uint4(0u, 0u, 0u, 0u);
-    }
+    for (int u = 0; u < 5; ++u)
+      pi[u] = ridx[min(max(t0 + 4 * lg + u - 1, 0), hi - 1)];
+  };
+  auto load_r = [&](const int (&pi)[5], float (&rk)[4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) rk[t] = rr[min(max(pi[t + 1], 0), p.n - 1)];
   };
   uint4 cur[4], nxt[4];
+  int ia[5], ib[5], ic[5];
+  float ra[4], rb[4];
   int t0 = lo + 16 * wave;
-  if (t0 < hi) load_tile(t0, cur);
+  if (t0 < hi) {
+    load_tile(t0, cur);
+    load_idx(t0, ia);
+    load_idx(t0 + 16 * WV, ib);
+    load_r(ia, ra);
+  }
   for (; t0 < hi; t0 += 16 * WV) {
-    if (t0 + 16 * WV < hi) load_tile(t0 + 16 * WV, nxt);  // next tile in flight
+    load_tile(t0 + 16 * WV, nxt);  // next tile in flight
+    load_r(ib, rb);
+    load_idx(t0 + 32 * WV, ic);
     // the rows this lane post-processes: 4 lg .. 4 lg + 3 of the tile
     int pos[4];
     bool okr[4];
-    float rk[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int j = t0 + 4 * lg + t;
-      pos[t] = -1;
-      okr[t] = false;
-      if (li < GRP && j < hi) {
-        pos[t] = ridx[j];
-        const int pv = j > 0 ? ridx[j - 1] : -1;
-        okr[t] = pos[t] >= 0 && pos[t] < p.n && (j == 0 || pv < pos[t]);
-      }
-      rk[t] = okr[t] ? rr[pos[t]] : 0.0f;
+      pos[t] = ia[t + 1];
+      okr[t] = li < GRP && j < hi && pos[t] >= 0 && pos[t] < p.n &&
+               (j == 0 || ia[t] < pos[t]);
     }
     vkv_float4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -934,7 +946,7 @@ __device__ __forceinline__ void resident_body(const DParams &p, int c, int g,
         const float dot = acc[t] * kInvSqrtD;
         p.ell[(size_t)row_of(p, b, g, hl, GRP) * p.cap + j] = dot;
         mx = fmaxf(mx, dot);
-        const bool in_h = okr[t] && rk[t] >= 1.0f;
+        const bool in_h = okr[t] && ra[t] >= 1.0f;
         if (in_h) {  // sum over H of exp(l), with a running shift
           if (dot > hm) {
             hsum = hsum * (double)expf(hm - dot) + 1.0;
@@ -954,6 +966,13 @@ __device__ __forceinline__ void resident_body(const DParams &p, int c, int g,
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) cur[k] = nxt[k];
+#pragma unroll
+    for (int u = 0; u < 5; ++u) {
+      ia[u] = ib[u];
+      ib[u] = ic[u];
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) ra[t] = rb[t];
   }
   const int np = p.nch + p.ncr;
   {
@@ -3340,7 +3359,8 @@ struct PhaseMark {
     if (count == 2 && first < n && ev[first + 1]) solo = first;
   }
   void operator()(int k) const {
-    if (ev && ev[k] && k != solo && k != solo + 1)
+    const bool own = solo >= 0 && (k == solo || k == solo + 1);
+    if (ev && ev[k] && !own)
       (void)hipEventRecord(static_cast<hipEvent_t>(ev[k]), s);
   }
   // a phase with no kernel in this mode: its events as markers
