@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the Dense (resident) / Dense (offload) baselines")
+    ap.add_argument("--no-compress", action="store_true",
+                    help="skip the compression pass over the 36-layer, "
+                         "128K-token workload")
     return ap.parse_args()
 
 
@@ -164,6 +167,62 @@ def cpu_baseline(w, seconds, est=0):
                       f"heads, {n} tokens, fresh query each) of the same "
                       f"layer, fp64 numpy, {spent:.1f} s; "
                       f"host cores available: {len(os.sched_getaffinity(0))}"}
+
+
+def compress_pass(dev, steps):
+    """PoissonComp over a whole model's prefill cache: 36 layers x 8 KV heads
+    x 131072 tokens, tau ~ Beta(0.5, 5), 4 sinks + 256 local tokens, at
+    eta = 1/8, 1/16, 1/32 (K and V random bf16 on the device). Per eta: the
+    GPU span of one call (events on the stream around it), its algorithmic
+    HBM bytes (tau read, r written, the resident positions written, each
+    resident K/V row read and written) as GB/s, and the time per (layer,
+    KV head) slice."""
+    import torch
+
+    from verified_sparse_kv_amd import verkv as vk
+    from workloads import C5, make_c5_tau, resident_cap
+    L, G, n = C5["layers"], C5["G"], C5["n"]
+    t_tau = torch.from_numpy(make_c5_tau(seed=0)).to(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    kv = [torch.randn((L, G, n, 128), dtype=torch.bfloat16, device=dev,
+                      generator=gen).view(torch.int16) for _ in range(2)]
+    out = {"workload": f"{L} layers x {G} KV heads x {n} tokens, tau ~ "
+                       f"Beta(0.5, 5), {C5['n_sink']} sinks + "
+                       f"{C5['n_local']} local", "per_eta": {}}
+    k = max(1, min(steps, 10))
+    for eta in C5["etas"]:
+        budget = int(round(eta * n))
+        cap = resident_cap(budget)
+        ws = None
+        for _ in range(2):
+            res = vk.compress(t_tau, kv[0], kv[1], budget, C5["n_sink"],
+                              C5["n_local"], 0, cap, workspace=ws)
+            ws = res["workspace"]
+        evs = [(torch.cuda.Event(enable_timing=True),
+                torch.cuda.Event(enable_timing=True)) for _ in range(k)]
+        torch.cuda.synchronize()
+        for i in range(k):
+            evs[i][0].record()
+            res = vk.compress(t_tau, kv[0], kv[1], budget, C5["n_sink"],
+                              C5["n_local"], 0, cap, workspace=ws)
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        rc, bits = vk.vkv_check_status(vk._ptr(res["status"]), vk._stream(None))
+        assert rc == 0, (rc, bits, vk.vkv_last_error())
+        ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / k
+        rows = int(res["resident_count"].sum().item())
+        nbytes = 8 * L * G * n + rows * (4 + 2 * ROW_BYTES)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out["per_eta"][f"1/{round(1 / eta)}"] = {
+            "ms": ms, "algorithmic_bytes": nbytes, "gbs": gbs,
+            "frac_hbm_peak": gbs / HBM_PEAK_GBS,
+            "us_per_slice": ms * 1e3 / (L * G), "resident_rows": rows,
+            "calls": k}
+        del res
+    del kv, t_tau
+    torch.cuda.empty_cache()
+    return out
 
 
 def dense_baselines(w, t_qs, host_kv, dev, steps, verkv_ms):
@@ -383,6 +442,8 @@ def main():
     if not args.no_dense:
         res["dense_baselines"] = dense_baselines(w, t_qs, host_kv, dev,
                                                  args.steps, ms)
+    if not args.no_compress:
+        res["compress_c5"] = compress_pass(dev, args.steps)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds,
                                            ESTIMATORS[args.estimator])

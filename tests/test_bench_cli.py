@@ -21,5 +21,5 @@ def test_bench_help_lists_the_options():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 0
     for opt in ("--steps", "--warmup", "--config", "--estimator", "--no-dense",
-                "--no-cpu-baseline"):
+                "--no-cpu-baseline", "--no-compress"):
         assert opt in r.stdout, opt

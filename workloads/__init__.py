@@ -6,6 +6,6 @@ arithmetic, and imports neither the oracle nor the library.
 """
 
 from .gen import (  # noqa: F401
-    CONFIGS, bf16_bits, bf16_to_f32, make_decode_workload, make_c5_tau,
+    C5, CONFIGS, bf16_bits, bf16_to_f32, make_decode_workload, make_c5_tau,
     c3_shift_queries, resident_cap,
 )
