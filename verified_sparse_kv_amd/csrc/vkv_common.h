@@ -120,28 +120,6 @@ __device__ __forceinline__ T block_exclusive_scan(T v, T *scratch, T *total) {
   return base + incl - v;
 }
 
-// "Last block done": every block of a group calls this after its global
-// writes; exactly one (the last to arrive) gets true. Arrival is a release at
-// device scope (the block's writes become visible before the counter moves)
-// and the last block acquires before it reads the others' writes. No block
-// ever waits for another. The counter must start at 0; the last block resets
-// it.
-__device__ __forceinline__ bool last_block_arrive(uint32_t *counter,
-                                                  uint32_t blocks) {
-  __shared__ int s_last;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const uint32_t prev = __hip_atomic_fetch_add(
-        counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (prev == blocks - 1);
-    if (s_last) *counter = 0;
-  }
-  __syncthreads();
-  if (s_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return s_last != 0;
-}
-
 // ---------------------------------------------------------------- Philox
 // Philox4x32-10 (Salmon et al., SC'11): 10 rounds of the 4x32 bijection with
 // multipliers M0, M1 and Weyl key increments W0, W1. Returns the first of

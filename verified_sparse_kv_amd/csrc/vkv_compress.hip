@@ -64,16 +64,14 @@ __global__ __launch_bounds__(kBlock) void ck_zero(uint32_t *buf, size_t words,
 }
 
 // One radix level: histogram of the 11-bit digit at `shift` among free tokens
-// whose higher digits match the slice's bracket; the last block of the slice
-// picks the bin holding e* and narrows the bracket.
+// whose higher digits match the slice's bracket, added to the slice's global
+// histogram (ck_pick then picks the bin holding e* and narrows the bracket).
 __global__ __launch_bounds__(kBlock) void ck_hist(CParams p, int level) {
   const int slice = blockIdx.y, chunk = blockIdx.x;
   CompressSlice *st = p.slices + slice;
   if (st->done) return;
   __shared__ uint32_t s_cnt[kCompBins];
   __shared__ unsigned long long s_sum[kCompBins];
-  __shared__ unsigned long long s_red[kBlock / kWave + 1];
-  __shared__ int s_best;
   for (int b = threadIdx.x; b < kCompBins; b += kBlock) {
     s_cnt[b] = 0u;
     s_sum[b] = 0ull;
@@ -103,9 +101,24 @@ __global__ __launch_bounds__(kBlock) void ck_hist(CParams p, int level) {
       atomicAdd(gs + b, s_sum[b]);
     }
   }
-  if (!last_block_arrive(&st->arrive, gridDim.x)) return;
+}
 
-  // ---- last block of the slice: locate the bin that holds e*.
+// One workgroup per slice, after each histogram level: locate the bin that
+// holds e* from the slice's global histogram (complete once the level's
+// launch has ended), narrow the bracket or settle c, and zero the histogram
+// for the next level. (A separate launch instead of a last-arriving
+// workgroup: no workgroup of the histogram launch needs a device-scope
+// fence.)
+__global__ __launch_bounds__(kBlock) void ck_pick(CParams p, int level) {
+  const int slice = blockIdx.x;
+  CompressSlice *st = p.slices + slice;
+  if (st->done) return;
+  __shared__ unsigned long long s_red[kBlock / kWave + 1];
+  __shared__ int s_best;
+  const int shift = level == 0 ? 22 : (level == 1 ? 11 : 0);
+  const uint64_t lo = st->lo;
+  uint32_t *gc = p.hcnt + (size_t)slice * kCompBins;
+  unsigned long long *gs = p.hsum + (size_t)slice * kCompBins;
   constexpr int PER = kCompBins / kBlock;  // 8 bins per thread
   uint64_t c[PER], s[PER];
   uint64_t my_c = 0, my_s = 0;
@@ -340,8 +353,10 @@ hipError_t launch_compress(const vkv_compress_args &a, const CompressLayout &L,
             dim3(kBlock), 0, s>>>(static_cast<uint32_t *>(a.workspace),
                                   zero_words, a.status);
   const dim3 grid((unsigned)L.ncc, (unsigned)L.n_slices);
-  for (int level = 0; level < 3; ++level)
+  for (int level = 0; level < 3; ++level) {
     ck_hist<<<grid, dim3(kBlock), 0, s>>>(p, level);
+    ck_pick<<<dim3((unsigned)L.n_slices), dim3(kBlock), 0, s>>>(p, level);
+  }
   ck_rate<<<grid, dim3(kBlock), 0, s>>>(p);
   ck_compact<<<grid, dim3(kBlock), 0, s>>>(p);
   return hipGetLastError();

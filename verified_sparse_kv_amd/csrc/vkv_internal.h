@@ -40,8 +40,7 @@ struct CompressSlice {
   uint32_t n_free;    // free (non-forced) tokens
   int32_t done;       // water level known
   int32_t all_sat;    // every free token saturates (L empty)
-  uint32_t arrive;    // last-block counter
-  uint32_t pad[3];
+  uint32_t pad[4];
 };
 
 struct CompressLayout {
