@@ -83,10 +83,18 @@ __global__ __launch_bounds__(kBlock) void ck_hist(CParams p, int level) {
   const uint64_t pref = lo >> hshift;
   const float *tau = p.tau + (size_t)slice * p.n;
   const int base = chunk * kCompChunk;
-  for (int k = 0; k < kCompChunk / kBlock; ++k) {
+  // the thread's scores first, all in flight together (indices past the
+  // slice read its last score, which is not used)
+  constexpr int PT = kCompChunk / kBlock;
+  float tv[PT];
+#pragma unroll
+  for (int k = 0; k < PT; ++k)
+    tv[k] = tau[min(base + k * kBlock + (int)threadIdx.x, p.n - 1)];
+#pragma unroll
+  for (int k = 0; k < PT; ++k) {
     const int i = base + k * kBlock + threadIdx.x;
     if (i >= p.n || is_forced(p, i)) continue;
-    const uint64_t v = tau_q(tau[i]);
+    const uint64_t v = tau_q(tv[k]);
     if (level > 0 && (v >> hshift) != pref) continue;
     const int d = (int)((v >> shift) & (kCompBins - 1));
     atomicAdd(&s_cnt[d], 1u);
@@ -213,8 +221,16 @@ __global__ __launch_bounds__(kBlock) void ck_rate(CParams p) {
   uint32_t *bits = p.bits + (size_t)slice * p.nwords;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int base = chunk * kCompChunk;
+  // the thread's scores first, all in flight together (indices past the
+  // slice read its last score, which is not used)
+  constexpr int PT = kCompChunk / kBlock;
+  float tv[PT];
+#pragma unroll
+  for (int k = 0; k < PT; ++k)
+    tv[k] = tau[min(base + k * kBlock + (int)threadIdx.x, p.n - 1)];
   uint32_t count = 0;
-  for (int k = 0; k < kCompChunk / kBlock; ++k) {
+#pragma unroll
+  for (int k = 0; k < PT; ++k) {
     const int i = base + k * kBlock + threadIdx.x;
     bool res = false;
     if (i < p.n) {
@@ -222,7 +238,7 @@ __global__ __launch_bounds__(kBlock) void ck_rate(CParams p) {
       if (is_forced(p, i) || all_sat) {
         res = true;
       } else {
-        const uint64_t prod = num * tau_q(tau[i]);
+        const uint64_t prod = num * tau_q(tv[k]);
         if (prod >= den) {
           res = true;
         } else {
