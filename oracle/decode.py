@@ -260,6 +260,45 @@ def plan_row(wt, r, pos, dnorm, eps, delta, estimator=EST_CLIP):
     return out
 
 
+def key_logits(qh, keys):
+    """Exact logits <q, k_j> / sqrt(d) of the given key rows (§3, eq. 1)."""
+    qh = np.asarray(qh, dtype=np.float64)
+    return np.asarray(keys, dtype=np.float64) @ qh * (1.0 / math.sqrt(qh.size))
+
+
+def sketch_logits(qh, sk, proj):
+    """Planning logits from the key sketch (Algorithm 2, first step: the
+    weights w^ come from the sketch M_A): s_i = <P^T q, sk_i> / sqrt(d).
+
+    ``sk``: [m][s] sketch rows sk_i = P^T k_i (reading R4); ``proj``: P,
+    [d][s]. Whenever E[P P^T] = I (Gaussian entries of variance 1/s, or an
+    orthogonal P), s_i estimates the exact logit <q, k_i> / sqrt(d) without
+    bias; the scale is the attention's 1/sqrt(d), not 1/sqrt(s).
+    """
+    qh = np.asarray(qh, dtype=np.float64)
+    qp = np.asarray(proj, dtype=np.float64).T @ qh
+    return np.asarray(sk, dtype=np.float64) @ qp * (1.0 / math.sqrt(qh.size))
+
+
+def output_coefficients(w_res, r_res, lam_res, exact_res):
+    """Coefficients alpha_j of the resident rows in Theorem 2's estimator:
+    the exact weight w_j on H and on the fetched part F_h (``exact_res``),
+    lambda_j w_j / r_j on the sampled rows S minus F_h (reading R15: those
+    rows are resident, so their exact weight is used)."""
+    w_res = np.asarray(w_res, dtype=np.float64)
+    return np.where(exact_res, w_res, np.asarray(lam_res) * w_res /
+                    np.asarray(r_res, dtype=np.float64))
+
+
+def combine(alpha, v_res, w_f, v_f):
+    """The estimate from its parts: D^ = sum alpha_j + sum w_f, the
+    numerator N^ = sum alpha_j v_j + sum w_f v_f with the same coefficients
+    (reading R16), and o = N^ / D^. Returns (D^, N^, o)."""
+    d_hat = float(alpha.sum() + w_f.sum())
+    num = alpha @ v_res + w_f @ v_f
+    return d_hat, num, num / d_hat
+
+
 def decode_group(q, res_kv, res_idx, sketch, proj, r, host_kv, eps, delta,
                  estimator=EST_CLIP, weights=W_SKETCH, fetch_override=None):
     """KVFetch for the query heads sharing one KV head.
@@ -275,7 +314,6 @@ def decode_group(q, res_kv, res_idx, sketch, proj, r, host_kv, eps, delta,
     grp, d = q.shape
     r = np.asarray(r, dtype=np.float32)
     n = r.size
-    scale = 1.0 / math.sqrt(d)
     in_h = r == np.float32(1.0)
     in_l = ~in_h
     res_idx = np.asarray(res_idx, dtype=np.int64)
@@ -297,12 +335,11 @@ def decode_group(q, res_kv, res_idx, sketch, proj, r, host_kv, eps, delta,
     union = set()
     for h in range(grp):
         qh = q[h]
-        ell = kres @ qh * scale
+        ell = key_logits(qh, kres)
         if weights == W_SKETCH:
-            qp = np.asarray(proj, dtype=np.float64).T @ qh
-            s_l = np.asarray(sketch, dtype=np.float64)[lpos] @ qp * scale
+            s_l = sketch_logits(qh, np.asarray(sketch)[lpos], proj)
         else:
-            s_l = np.asarray(host_kv[lpos, 0, :], dtype=np.float64) @ qh * scale
+            s_l = key_logits(qh, host_kv[lpos, 0, :])
         m = max(ell.max() if ell.size else -np.inf,
                 s_l.max() if s_l.size else -np.inf)
         w_res = np.exp(ell - m)
@@ -316,23 +353,20 @@ def decode_group(q, res_kv, res_idx, sketch, proj, r, host_kv, eps, delta,
         # coefficients on resident rows
         lam_full = np.ones(n)
         lam_full[lpos] = plan["lam"]
-        rr = r64[res_idx]
-        alpha = np.where(res_h | in_f[res_idx], w_res,
-                         lam_full[res_idx] * w_res / rr)
+        alpha = output_coefficients(w_res, r64[res_idx], lam_full[res_idx],
+                                    res_h | in_f[res_idx])
         # exact contributions of fetched rows outside S
         fetch_rows = np.array(sorted(set(fpos.tolist()) - set(res_idx.tolist())),
                               dtype=np.int64)
         if fetch_rows.size:
             kf = np.asarray(host_kv[fetch_rows, 0, :], dtype=np.float64)
             vf = np.asarray(host_kv[fetch_rows, 1, :], dtype=np.float64)
-            wf = np.exp(kf @ qh * scale - m)
+            wf = np.exp(key_logits(qh, kf) - m)
         else:
             vf = np.zeros((0, d))
             wf = np.zeros(0)
         union.update(fetch_rows.tolist())
-        d_hat = float(alpha.sum() + wf.sum())
-        num = alpha @ vres + wf @ vf
-        o = num / d_hat
+        d_hat, _, o = combine(alpha, vres, wf, vf)
         plan.update(m=m, dnorm=dnorm, d_hat=d_hat, o=o, fetch_rows=fetch_rows,
                     lpos=lpos, n_s=int(in_s.sum()))
         heads.append(plan)

@@ -313,3 +313,183 @@ def check_range_bound(w, r):
     x0 = np.abs(lam * w * (0 - r) / r)
     top = np.maximum(x0, x1)
     assert np.allclose(top, b_i, rtol=1e-13, atol=0)
+
+
+# ---------------------------------------------------------------- sketch logits
+def _exact_logit_mp(q, k):
+    """<q, k> / sqrt(d) at 50 digits (the logit of eq. 1)."""
+    d = len(q)
+    return mpmath.fsum(mpmath.mpf(float(a)) * mpmath.mpf(float(b))
+                       for a, b in zip(q, k)) / mpmath.sqrt(d)
+
+
+def check_sketch_orthogonal(seed, d=16, m=12):
+    """An orthogonal projection (s = d) preserves inner products,
+    <P^T q, P^T k> = <q, k>, so the planning logits of a sketch sk = P^T k
+    must equal the exact logits <q, k> / sqrt(d). P is a random orthogonal
+    matrix (not symmetric), so using P q instead of P^T q fails."""
+    rng = np.random.default_rng(seed)
+    P, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    assert np.max(np.abs(P - P.T)) > 0.1
+    q = rng.standard_normal(d)
+    K = 2.0 * rng.standard_normal((m, d))
+    s = od.sketch_logits(q, K @ P, P)
+    for i in range(m):
+        ref = float(_exact_logit_mp(q, K[i]))
+        tol = 1e-12 * np.linalg.norm(q) * np.linalg.norm(K[i]) / math.sqrt(d)
+        assert abs(s[i] - ref) <= tol, (i, s[i], ref)
+
+
+def check_sketch_blocks(seed, d=16, s=4, m=12):
+    """E[P P^T] = I makes the sketch logit an unbiased estimate of the exact
+    one (reading R4). A uniform draw among the d/s signed coordinate blocks
+    P_j = sqrt(d/s) E_j (E_j: s distinct coordinates, random signs) has
+    E[P_j P_j^T] = I exactly, so the mean of the sketch logits over the d/s
+    blocks must equal <q, k> / sqrt(d) (a scale of 1/sqrt(s) is off by
+    sqrt(d/s))."""
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(d)
+    sgn = rng.choice([-1.0, 1.0], d)
+    q = rng.standard_normal(d)
+    K = 2.0 * rng.standard_normal((m, d))
+    acc = np.zeros(m)
+    for j in range(d // s):
+        P = np.zeros((d, s))
+        for t in range(s):
+            c = perm[j * s + t]
+            P[c, t] = sgn[c] * math.sqrt(d / s)
+        acc += od.sketch_logits(q, K @ P, P)
+    acc /= d // s
+    for i in range(m):
+        ref = float(_exact_logit_mp(q, K[i]))
+        tol = 1e-12 * np.linalg.norm(q) * np.linalg.norm(K[i])
+        assert abs(acc[i] - ref) <= tol, (i, acc[i], ref)
+
+
+def tiny_layer(seed, d=8, n_h=3, n_l=8, grp=1, s=4):
+    """A small KV head for the estimator pins: n_h tokens with r = 1 and n_l
+    tokens of L with r in (0.15, 0.85), spread logits, a Gaussian sketch
+    (entries of variance 1/s). Returns a dict of float64/float32 arrays."""
+    rng = np.random.default_rng(seed)
+    n = n_h + n_l
+    pos = rng.permutation(n)
+    h_pos = np.sort(pos[:n_h])
+    l_pos = np.sort(pos[n_h:])
+    K = 1.5 * rng.standard_normal((n, d))
+    V = rng.standard_normal((n, d))
+    r = np.ones(n, dtype=np.float32)
+    r[l_pos] = rng.uniform(0.15, 0.85, n_l).astype(np.float32)
+    P = rng.standard_normal((d, s)) / math.sqrt(s)
+    return dict(q=rng.standard_normal((grp, d)), K=K, V=V, r=r, P=P,
+                sketch=K @ P, host_kv=np.stack([K, V], axis=1),
+                h_pos=h_pos, l_pos=l_pos, n=n, d=d)
+
+
+def check_sketch_decode_identity(seed):
+    """With P = I (s = d) the sketch is the keys themselves, so every output
+    of the decode step (plan, fetch set, estimate) in sketch mode must equal
+    the exact-weight (perfect sketch) mode bit for bit: the sketch rows are
+    looked up at the positions of L and scaled like the exact logits."""
+    t = tiny_layer(seed, d=8, n_h=4, n_l=24, grp=2)
+    rng = np.random.default_rng(seed + 1)
+    samp = t["l_pos"][rng.random(t["l_pos"].size) < t["r"][t["l_pos"]]]
+    res_idx = np.sort(np.concatenate([t["h_pos"], samp]))
+    res_kv = t["host_kv"][res_idx]
+    eye = np.eye(t["d"])
+    outs = []
+    for wm in (od.W_SKETCH, od.W_PERFECT):
+        heads, union = od.decode_group(t["q"], res_kv, res_idx, t["K"].copy(),
+                                       eye, t["r"], t["host_kv"], 0.02, 0.1,
+                                       od.EST_CLIP, wm)
+        outs.append((heads, union))
+    (ha, ua), (hb, ub) = outs
+    assert np.array_equal(ua, ub)
+    for a, b in zip(ha, hb):
+        for k in ("m", "dnorm", "beta_star", "eps_hat0", "k_star", "eps_hat",
+                  "d_hat"):
+            assert a[k] == b[k], (k, a[k], b[k])
+        assert np.array_equal(a["fetch_pos"], b["fetch_pos"])
+        assert np.array_equal(a["o"], b["o"])
+    assert any(h["k_star"] > 0 for h in ha)
+
+
+# ---------------------------------------------------------------- estimator
+def check_estimator_enumeration(seed, estimator, weights, n_l=8, n_fetch=2):
+    """Theorem 2's estimator, through the decode step itself, over all 2^|L|
+    Poisson samples: with a fixed fetch set F (so S minus F is not empty),
+    coefficients w on H u F and lambda w / r on S minus F, the expectations
+    of the denominator and the numerator are
+        E[D^] = D - sum_{L'} w_i (1 - lambda_i),
+        E[N^] = N - sum_{L'} w_i (1 - lambda_i) v_i,   L' = L minus F,
+    with D = sum_i w_i and N = sum_i w_i v_i over every token (exact weights
+    w_i = exp(<q, k_i>/sqrt(d)), eq. 1); with lambda = 1 both are unbiased.
+    Each sample's estimate is taken as D^ = d_hat e^m and N^ = D^ o."""
+    t = tiny_layer(seed, n_l=n_l)
+    l_pos, h_pos = t["l_pos"], t["h_pos"]
+    # fetch the lightest tokens of L, so that the heavy (shrunk) ones stay
+    # in L' = L minus F
+    lw = t["K"][l_pos] @ t["q"][0]
+    F = np.sort(l_pos[np.argsort(lw)[:n_fetch]])
+    rl = t["r"][l_pos].astype(np.float64)
+    ED = mpmath.mpf(0)
+    EN = [mpmath.mpf(0)] * t["d"]
+    lam0 = None
+    for z in itertools.product((0, 1), repeat=n_l):
+        z = np.array(z, dtype=bool)
+        res_idx = np.sort(np.concatenate([h_pos, l_pos[z]]))
+        heads, _ = od.decode_group(t["q"], t["host_kv"][res_idx], res_idx,
+                                   t["sketch"], t["P"], t["r"], t["host_kv"],
+                                   0.1, 0.1, estimator, weights,
+                                   fetch_override=[F])
+        hd = heads[0]
+        assert np.array_equal(hd["lpos"], l_pos)
+        if lam0 is None:
+            lam0 = hd["lam"].copy()
+        # lambda is fixed before the sample is seen (up to rounding of the
+        # shift, which scales every planning weight alike)
+        assert np.allclose(hd["lam"], lam0, rtol=1e-12, atol=0)
+        prob = mpmath.mpf(float(np.prod(np.where(z, rl, 1.0 - rl))))
+        dh = mpmath.mpf(hd["d_hat"]) * mpmath.exp(mpmath.mpf(hd["m"]))
+        ED += prob * dh
+        for c in range(t["d"]):
+            EN[c] += prob * dh * mpmath.mpf(float(hd["o"][c]))
+    q = t["q"][0]
+    w = [mpmath.exp(_exact_logit_mp(q, t["K"][i])) for i in range(t["n"])]
+    lam = np.ones(t["n"])
+    lam[l_pos] = lam0
+    rest = set(l_pos.tolist()) - set(F.tolist())
+    D = mpmath.fsum(w)
+    bias = mpmath.fsum(w[i] * (1 - mpmath.mpf(float(lam[i]))) for i in rest)
+    assert abs(ED - (D - bias)) <= mpmath.mpf("1e-11") * D, (ED, D - bias)
+    scale = mpmath.fsum(w[i] * mpmath.fsum(abs(mpmath.mpf(float(x)))
+                                           for x in t["V"][i])
+                        for i in range(t["n"]))
+    for c in range(t["d"]):
+        N = mpmath.fsum(w[i] * mpmath.mpf(float(t["V"][i, c]))
+                        for i in range(t["n"]))
+        bn = mpmath.fsum(w[i] * (1 - mpmath.mpf(float(lam[i]))) *
+                         mpmath.mpf(float(t["V"][i, c])) for i in rest)
+        assert abs(EN[c] - (N - bn)) <= mpmath.mpf("1e-11") * scale, \
+            (c, EN[c], N - bn)
+    if estimator == od.EST_UNBIASED:
+        assert np.all(lam0 == 1.0)
+    else:
+        # the case is not degenerate: some coefficient on L' is shrunk
+        assert max(1.0 - lam[i] for i in rest) > 1e-3
+
+
+# ---------------------------------------------------------------- Philox
+def check_philox_kat():
+    """The published known-answer vectors of Philox4x32-10 (Salmon et al.,
+    SC'11), stored in tests/golden/philox_kat.json."""
+    import json
+    import os
+    from oracle import philox
+    path = os.path.join(os.path.dirname(__file__), "golden", "philox_kat.json")
+    with open(path) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        ctr = [int(x, 16) for x in c["ctr"]]
+        key = [int(x, 16) for x in c["key"]]
+        out = philox.philox4x32_10(*ctr, *key)
+        assert [int(x) for x in out] == [int(x, 16) for x in c["out"]], c

@@ -132,3 +132,9 @@ def test_compress_layout():
     # the sample depends on (seed, layer, head, token) only
     again = oc.compress_slice(tau[1, 2], 40, 3, 5, 9, 5, 2)
     assert np.array_equal(again["resident_idx"], out[1][2]["resident_idx"])
+
+
+def test_philox_known_answer_vectors():
+    """The three published Philox4x32-10 known-answer vectors (Salmon et
+    al., SC'11), held in tests/golden/philox_kat.json."""
+    pins.check_philox_kat()

@@ -360,3 +360,56 @@ def test_fixed_point_single_breakpoint_form(seed):
     # one-breakpoint form
     for b in np.linspace(0, 2 * beta, 9):
         assert od.shrink_residual(b, w, r) <= f(b) + 1e-13 * float(np.sum(w))
+
+
+# ---------------------------------------------------------------- sketch logits
+@pytest.mark.parametrize("seed", range(4))
+def test_sketch_logits_orthogonal_projection(seed):
+    """An orthogonal P preserves inner products: sketch logits = exact
+    logits <q, k>/sqrt(d) (Algorithm 2's sketch weights, reading R4)."""
+    pins.check_sketch_orthogonal(900 + seed)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_sketch_logits_unbiased_over_coordinate_blocks(seed):
+    """E[P P^T] = I exactly over signed coordinate blocks: the mean sketch
+    logit is the exact logit (the scale is 1/sqrt(d), not 1/sqrt(s))."""
+    pins.check_sketch_blocks(910 + seed)
+
+
+def test_sketch_logits_unbiased_gaussian_projection():
+    """The sketch of the decode workloads: P with N(0, 1/s) entries
+    (E[P P^T] = I). Over 4000 seeded draws of P the mean sketch logit of a
+    key must match <q, k>/sqrt(d) within five standard errors, at d = 128,
+    s = 32 (a 1/sqrt(s) scale or a missing 1/sqrt(d) would be off by a
+    factor of 2 or 11)."""
+    rng = np.random.default_rng(920)
+    d, s, m_draws = 128, 32, 4000
+    q = rng.standard_normal(d)
+    k = 0.5 * q + rng.standard_normal(d)  # a logit well away from 0
+    exact = float(q @ k) / math.sqrt(d)
+    vals = np.empty(m_draws)
+    for j in range(m_draws):
+        P = rng.standard_normal((d, s)) / math.sqrt(s)
+        vals[j] = od.sketch_logits(q, (k @ P)[None], P)[0]
+    se = vals.std(ddof=1) / math.sqrt(m_draws)
+    assert abs(vals.mean() - exact) <= 5 * se, (vals.mean(), exact, se)
+    assert exact > 20 * se
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_sketch_mode_with_identity_projection_is_perfect_mode(seed):
+    """P = I, s = d: sketch mode and exact-weight mode agree bit for bit in
+    every output of the decode step."""
+    pins.check_sketch_decode_identity(930 + seed)
+
+
+# ---------------------------------------------------------------- estimator
+@pytest.mark.parametrize("est", [od.EST_CLIP, od.EST_UNBIASED, od.EST_BINARY])
+@pytest.mark.parametrize("weights", [od.W_SKETCH, od.W_PERFECT])
+def test_estimator_bias_by_exact_enumeration(est, weights):
+    """Theorem 2's estimator through decode_group over every Poisson sample
+    of a 10-token L with a fixed fetch set: E[D^] and E[N^] fall short of D
+    and N by exactly the shrinkage bias on L' (zero with lambda = 1)."""
+    pins.check_estimator_enumeration(940 + 3 * est + weights, est, weights,
+                                     n_l=10, n_fetch=3)

@@ -8,6 +8,7 @@ import pytest
 
 from oracle import compress as oc
 from oracle import decode as od
+from oracle import philox
 from tests import pins
 
 
@@ -61,6 +62,14 @@ def run_pins():
     rng = np.random.default_rng(12)
     attempt("attention_mp", lambda: pins.check_exact_attention_mp(
         rng.normal(0, 2, 16), rng.normal(0, 2, (6, 16)), rng.normal(0, 1, (6, 3))))
+    attempt("sketch_orthogonal", lambda: pins.check_sketch_orthogonal(13))
+    attempt("sketch_blocks", lambda: pins.check_sketch_blocks(14))
+    attempt("sketch_identity", lambda: pins.check_sketch_decode_identity(15))
+    attempt("estimator_enum", lambda: pins.check_estimator_enumeration(
+        16, od.EST_CLIP, od.W_SKETCH, n_l=6))
+    attempt("estimator_enum_unbiased", lambda: pins.check_estimator_enumeration(
+        17, od.EST_UNBIASED, od.W_PERFECT, n_l=6))
+    attempt("philox_kat", pins.check_philox_kat)
     return failed
 
 
@@ -210,8 +219,74 @@ def _attention_no_scale(q, k, v):
     return (w @ np.asarray(v, np.float64)) / w.sum(), math.log(w.sum()) + m
 
 
+def _sketch_scale_s(qh, sk, proj):
+    qh = np.asarray(qh, np.float64)
+    qp = np.asarray(proj, np.float64).T @ qh
+    return np.asarray(sk, np.float64) @ qp / math.sqrt(np.asarray(proj).shape[1])
+
+
+def _sketch_unscaled(qh, sk, proj):
+    qp = np.asarray(proj, np.float64).T @ np.asarray(qh, np.float64)
+    return np.asarray(sk, np.float64) @ qp
+
+
+def _sketch_p_not_transposed(qh, sk, proj):
+    qh = np.asarray(qh, np.float64)
+    qp = np.asarray(proj, np.float64) @ qh
+    return np.asarray(sk, np.float64) @ qp / math.sqrt(qh.size)
+
+
+def _sketch_first_rows(qh, sk, proj):
+    # the sketch rows of tokens 0..m-1 instead of the rows passed in (an
+    # indexing slip: scores the wrong tokens whenever L is not a prefix)
+    return _orig_sketch(qh, sk, proj)[::-1]
+
+
+def _coef_no_r(w_res, r_res, lam_res, exact_res):
+    w_res = np.asarray(w_res, np.float64)
+    return np.where(exact_res, w_res, np.asarray(lam_res) * w_res)
+
+
+def _coef_no_lambda(w_res, r_res, lam_res, exact_res):
+    w_res = np.asarray(w_res, np.float64)
+    return np.where(exact_res, w_res, w_res / np.asarray(r_res, np.float64))
+
+
+def _combine_num_no_fetched(alpha, v_res, w_f, v_f):
+    d_hat = float(alpha.sum() + w_f.sum())
+    num = alpha @ v_res
+    return d_hat, num, num / d_hat
+
+
+def _combine_den_no_fetched(alpha, v_res, w_f, v_f):
+    d_hat = float(alpha.sum())
+    num = alpha @ v_res + w_f @ v_f
+    return d_hat, num, num / d_hat
+
+
+def _philox_nine_rounds(c0, c1, c2, c3, k0, k1):
+    # the reference round function, applied nine times
+    from oracle import philox as ph
+    c0 = np.asarray(c0, dtype=np.uint64) & ph.MASK32
+    c1 = np.asarray(c1, dtype=np.uint64) & ph.MASK32
+    c2 = np.asarray(c2, dtype=np.uint64) & ph.MASK32
+    c3 = np.asarray(c3, dtype=np.uint64) & ph.MASK32
+    ka, kb = int(k0) & 0xFFFFFFFF, int(k1) & 0xFFFFFFFF
+    for _ in range(9):
+        p0 = ph.M0 * c0
+        p1 = ph.M1 * c2
+        c0, c1, c2, c3 = ((p1 >> np.uint64(32)) ^ c1 ^ np.uint64(ka),
+                          p1 & ph.MASK32,
+                          (p0 >> np.uint64(32)) ^ c3 ^ np.uint64(kb),
+                          p0 & ph.MASK32)
+        ka = (ka + ph.W0) & 0xFFFFFFFF
+        kb = (kb + ph.W1) & 0xFFFFFFFF
+    return c0, c1, c2, c3
+
+
 _orig_wl = oc.water_level
 _orig_rates = oc.rates
+_orig_sketch = od.sketch_logits
 
 MUTATIONS = [
     ("eps_hat drops the b*l/3 term", od, "eps_hat", _eps_no_ab),
@@ -238,6 +313,19 @@ MUTATIONS = [
      _binary_variant(_bin_ok_key, _bin_ok_stop, lambda w, r: w)),
     ("attention logits not scaled by 1/sqrt(d)", od, "exact_attention",
      _attention_no_scale),
+    ("sketch logits scaled by 1/sqrt(s)", od, "sketch_logits", _sketch_scale_s),
+    ("sketch logits not scaled", od, "sketch_logits", _sketch_unscaled),
+    ("sketch logits project q by P, not P^T", od, "sketch_logits",
+     _sketch_p_not_transposed),
+    ("sketch logits of the wrong tokens", od, "sketch_logits", _sketch_first_rows),
+    ("S minus F_h coefficients drop 1/r", od, "output_coefficients", _coef_no_r),
+    ("S minus F_h coefficients drop lambda", od, "output_coefficients",
+     _coef_no_lambda),
+    ("numerator omits the fetched rows", od, "combine", _combine_num_no_fetched),
+    ("denominator omits the fetched rows", od, "combine", _combine_den_no_fetched),
+    ("Philox Weyl constant W0 off by one", philox, "W0", 0x9E3779B8),
+    ("Philox multiplier M1 wrong", philox, "M1", np.uint64(0xCD9E8D55)),
+    ("Philox with nine rounds", philox, "philox4x32_10", _philox_nine_rounds),
 ]
 
 
