@@ -54,44 +54,52 @@ def parse():
     ap.add_argument("--no-compress", action="store_true",
                     help="skip the compression pass over the 36-layer, "
                          "128K-token workload")
+    ap.add_argument("--also", nargs="*", default=["c3"],
+                    choices=["c2", "c3", "c4"],
+                    help="other decode workloads measured after the headline "
+                         "one, each reported as its own block (default: c3, "
+                         "batch 16 with fetching active); none with --also")
     return ap.parse_args()
 
 
 ESTIMATORS = {"clip": 0, "unbiased": 1, "binary": 2}
 
 
-def algorithmic_bytes(w, counts, fetching_rows, host_bytes, est="clip"):
-    """Compulsory HBM bytes of one step and of each HBM-bound kernel.
+def algorithmic_bytes(w, counts, fetching_rows, est="clip"):
+    """Algorithmic HBM bytes of one step and of each HBM-bound kernel, each
+    input counted once; intermediates the design writes and reads back are
+    reported apart and are not in the fractions.
 
-    Step: sketch + r for every (request, KV head, token), the resident K and V
-    rows with their positions, and q in / out (17 + 129 eta bytes per q-head
-    x token at s = 32, d = 128, 4 query heads per KV head).
-    Per kernel: the first launch scans the sketch (reads the sketch and r,
-    writes the fp32 sketch logit of every (query head, token)) and, in the
-    same launch, forms the resident logits (reads the resident K rows and
-    positions, writes one logit per (query head, row)); every planning pass over the tokens (beta passes,
-    certificate, candidate keys) reads the sketch logits of its rows and r of
-    their KV heads (the candidate pass only for the rows that fetch; binary
-    shrinkage adds one workgroup per row that reads them twice: a digit
-    histogram and the gather of the top keys). The gather is bound by the host link and
-    reported separately (it runs in one launch with the attention over the
-    resident rows, which hides behind it); the resolve and walk steps touch
-    only per-row summaries. The gather workgroups also form the attention
-    over the rows they read; the last launch only merges per-KV-head partial
-    sums and writes the outputs.
+    Step (compulsory): sketch + r for every (request, KV head, token), the
+    resident K and V rows with their positions, q in and the output out
+    (17 + 129 eta bytes per q-head x token at s = 32, d = 128, 4 query heads
+    per KV head).
+    Per kernel:
+      scan   the sketch and r of every token, the resident K rows and their
+             positions, q (the a5/a6 inputs). Intermediate: the fp32 sketch
+             logit of every (query head, token) and the resident logits.
+      beta1, cert   the estimator phases' own figure: the sketch logit of
+             every (query head, token) read once and r once per KV head
+             (5 B per q-head x token at 4 query heads per KV head).
+      cand   the same for the rows that fetch.
+      shrink (binary shrinkage) two reads of the same.
+    The gather is bound by the host link and reported separately (it runs in
+    one launch with the attention over the resident rows, which hides
+    behind it); the resolve and walk steps touch only per-row summaries.
     """
     B, Hq, G, n, s, d = w["B"], w["Hq"], w["G"], w["n"], w["s"], w["d"]
     grp = Hq // G
     rows = int(counts.sum())
     tok = B * Hq * n * 4 + B * G * n * 4
     ftok = fetching_rows * n * 4 + min(fetching_rows, B * G) * n * 4
-    per = {"scan": B * G * n * (2 * s + 4) + B * Hq * n * 4
-           + rows * (2 * d + 4) + rows * grp * 4,
+    per = {"scan": B * G * n * (2 * s + 4) + rows * (2 * d + 4)
+           + B * Hq * d * 2,
            "beta1": tok, "cert": tok, "cand": ftok}
+    inter = {"scan": B * Hq * n * 4 + rows * grp * 4}
     if est == "binary":
         per["shrink"] = 2 * tok
     return dict(step=B * G * n * (2 * s + 4) + rows * (4 * d + 4)
-                + B * Hq * d * (2 + 4), kernels=per)
+                + B * Hq * d * (2 + 4), kernels=per, intermediate=inter)
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_c2_traffic.md")
@@ -163,10 +171,23 @@ def cpu_baseline(w, seconds, est=0):
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     return {"value": units / spent, "unit": "q-head*ctx-tokens/s",
             "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{groups} decisions-groups (one KV head, {grp} query "
                       f"heads, {n} tokens, fresh query each) of the same "
                       f"layer, fp64 numpy, {spent:.1f} s; "
                       f"host cores available: {len(os.sched_getaffinity(0))}"}
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def compress_pass(dev, steps):
@@ -266,23 +287,22 @@ def dense_baselines(w, t_qs, host_kv, dev, steps, verkv_ms):
     return out
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for {args.gpus}); the "
-              "decode step shards by request and KV head with no exchange, "
-              "so per-GPU throughput is the figure to scale.", file=sys.stderr)
-        sys.exit(2)
+WORKLOADS = {"c2": "Qwen3-4B-shaped decode layer, 32K context",
+             "c3": "Qwen3-4B-shaped decode layer, batch 16, 32K, fetch active",
+             "c4": "Ministral-8B-shaped decode layer, 128K context"}
 
+
+def measure(config, args, dev, headline):
+    """Compress one workload's cache with the library, then time decode
+    steps on it. Returns (the measurement dict, the workload, the step)."""
     import numpy as np
     import torch
 
     from verified_sparse_kv_amd import verkv as vk
-    from workloads import c3_shift_queries, make_decode_workload, resident_cap
+    from workloads import (bf16_bits, c3_shift_queries, make_decode_workload,
+                           resident_cap)
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
-    w = make_decode_workload(args.config, seed=args.seed, with_queries=False)
+    w = make_decode_workload(config, seed=args.seed, with_queries=False)
     B, Hq, G, n, s, d = w["B"], w["Hq"], w["G"], w["n"], w["s"], w["d"]
 
     # ---- PoissonComp by the library (prefill time, untimed)
@@ -302,10 +322,9 @@ def main():
     # ---- queries: a fresh one per step
     nq = max(args.steps, 1)
     rng = np.random.default_rng([2, args.seed, 4242])
-    qs = [rng.standard_normal((B, Hq, d), dtype=np.float32) for _ in range(nq)]
-    from workloads import bf16_bits
-    qs = [bf16_bits(q) for q in qs]
-    if args.config == "c3":
+    qs = [bf16_bits(rng.standard_normal((B, Hq, d), dtype=np.float32))
+          for _ in range(nq)]
+    if config == "c3":
         r_np = comp["r"].cpu().numpy()
         ridx = comp["resident_idx"].cpu().numpy()
         masks = np.zeros((B, G, n), dtype=bool)
@@ -353,13 +372,10 @@ def main():
     ph_us = ph * 1e3 / nprof
     out = step.out
     ks = out["k_star"].cpu().numpy()
-    ab = algorithmic_bytes(w, counts, int(np.sum(ks > 0)),
-                           int(out["host_bytes"][0]), args.estimator)
+    ab = algorithmic_bytes(w, counts, int(np.sum(ks > 0)), args.estimator)
     cand = ab["kernels"]
-    # the roofline object covers the longest-running HBM-bound kernel; the
-    # candidate pass is listed with the others but is bound by its per-token
-    # gain arithmetic (eq. 9 for every token of a fetching row), not HBM
-    dom = max((k for k in cand if k != "cand"), key=lambda k: ph_us[names.index(k)])
+    # the roofline object covers the longest-running HBM-bound kernel
+    dom = max(cand, key=lambda k: ph_us[names.index(k)])
     di = names.index(dom)
 
     # timed steps, no events: the step time
@@ -388,60 +404,99 @@ def main():
     t_dom = sum(e0.elapsed_time(e1) for e0, e1 in pairs) * 1e-3 / max(args.steps, 1)
     host_bytes = int(out["host_bytes"][0])
     ks = out["k_star"].cpu().numpy()
+    paths = np.bincount(out["row_path"].cpu().numpy().ravel(), minlength=4)
     fetch_pct = 100.0 * host_bytes / (B * G * n * ROW_BYTES)
     units = B * Hq * n
-    value = units / (ms * 1e-3)
     achieved = cand[dom] / t_dom / 1e9
     t_gather = ph_us[names.index("fetch")] * 1e-6
+
+    def hbm(k, v):
+        t = ph_us[names.index(k)] * 1e-6
+        e = {"us": round(float(t * 1e6), 2), "bytes": int(v),
+             "gbs": round(v / t / 1e9, 1),
+             "frac": round(v / t / (HBM_PEAK_GBS * 1e9), 4)}
+        if k in ab["intermediate"]:
+            e["intermediate_bytes"] = int(ab["intermediate"][k])
+        return e
+
+    res = {
+        "ms_per_step": ms,
+        "value": units / (ms * 1e-3),
+        "steps_per_s": 1e3 / ms,
+        "config": {
+            "workload": WORKLOADS[config],
+            "batch": B, "q_heads": Hq, "kv_heads": G, "head_dim": d,
+            "ctx_tokens": n, "budget": w["budget"], "sketch_dim": s,
+            "n_sink": w["n_sink"], "n_local": w["n_local"], "eps": w["eps"],
+            "delta": w["delta"], "estimator": args.estimator},
+        "step_compulsory_bytes": int(ab["step"]),
+        "hbm_peak_pct": 100.0 * ab["step"] / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        "fetch_pct": fetch_pct,
+        "host_bytes_per_step": host_bytes,
+        "host_bytes_per_request": host_bytes / B,
+        "host_fetch_gbs": host_bytes / t_gather / 1e9 if t_gather > 0 else None,
+        "decisions_fetching_pct": 100.0 * float(np.mean(ks > 0)),
+        "decision_paths": {"no_fetch": int(paths[0]), "top_candidates": int(paths[1]),
+                           "all_candidates": int(paths[2]),
+                           "streaming": int(paths[3])},
+        "kernel_us_profiled": {k: round(float(v), 2) for k, v in zip(names, ph_us)},
+        # every HBM-bound kernel: algorithmic bytes over its profiled time
+        "kernels_hbm": {k: hbm(k, v) for k, v in cand.items()},
+        "roofline": {"bound": "hbm", "kernel": dom, "kernel_us": t_dom * 1e6,
+                     "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(config, dom, args.estimator),
+                     "algorithmic_bytes": cand[dom]},
+    }
+    res["_t_qs"], res["_host_kv"] = t_qs, host_kv
+    return res, w
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); the "
+              "decode step shards by request and KV head with no exchange, "
+              "so per-GPU throughput is the figure to scale.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    m, w = measure(args.config, args, dev, True)
+    t_qs, host_kv = m.pop("_t_qs"), m.pop("_host_kv")
     res = {
         "metric": METRIC,
-        "value": value,
+        "value": m["value"],
         "unit": "q-head*ctx-tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms,
+        "ms_per_step": m["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {
-            "workload": {"c2": "Qwen3-4B-shaped decode layer, 32K context",
-                         "c3": "Qwen3-4B-shaped decode layer, batch 16, 32K, "
-                               "fetch active",
-                         "c4": "Ministral-8B-shaped decode layer, 128K "
-                               "context"}[args.config],
-            "batch": B, "q_heads": Hq, "kv_heads": G, "head_dim": d,
-            "ctx_tokens": n, "budget": w["budget"], "sketch_dim": s,
-            "n_sink": w["n_sink"], "n_local": w["n_local"], "eps": w["eps"],
-            "delta": w["delta"], "estimator": args.estimator,
-            "parallelism": "none (1 GPU)"},
-        "steps_per_s": 1e3 / ms,
-        "hbm_peak_pct": 100.0 * ab["step"] / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
-        "fetch_pct": fetch_pct,
-        "host_bytes_per_step": host_bytes,
-        "host_fetch_gbs": host_bytes / t_gather / 1e9 if t_gather > 0 else None,
-        "decisions_fetching_pct": 100.0 * float(np.mean(ks > 0)),
-        "kernel_us_profiled": {k: round(float(v), 2) for k, v in zip(names, ph_us)},
-        # every HBM-bound kernel: algorithmic bytes over its profiled time
-        "kernels_hbm": {k: {"us": round(float(ph_us[names.index(k)]), 2),
-                            "bytes": int(v),
-                            "gbs": round(v / (ph_us[names.index(k)] * 1e-6) / 1e9, 1),
-                            "frac": round(v / (ph_us[names.index(k)] * 1e-6)
-                                          / (HBM_PEAK_GBS * 1e9), 4)}
-                        for k, v in cand.items()},
-        "roofline": {"bound": "hbm", "kernel": dom, "kernel_us": t_dom * 1e6,
-                     "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(args.config, dom,
-                                                 args.estimator),
-                     "algorithmic_bytes": cand[dom]},
+        "config": dict(m["config"], parallelism="none (1 GPU)"),
     }
+    for k, v in m.items():
+        if k not in ("value", "ms_per_step", "config"):
+            res[k] = v
     if not args.no_dense:
         res["dense_baselines"] = dense_baselines(w, t_qs, host_kv, dev,
-                                                 args.steps, ms)
+                                                 args.steps, m["ms_per_step"])
+    del t_qs, host_kv
+    for extra in args.also:
+        if extra == args.config:
+            continue
+        e, _ = measure(extra, args, dev, False)
+        e.pop("_t_qs")
+        e.pop("_host_kv")
+        res[extra] = e
+        torch.cuda.empty_cache()
     if not args.no_compress:
         res["compress_c5"] = compress_pass(dev, args.steps)
     if not args.no_cpu_baseline:

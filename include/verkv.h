@@ -59,6 +59,17 @@ typedef enum {
 #define VKV_STATUS_BAD_RESIDENT 0x8u      /* decode: resident list malformed, */
                                           /* or a token with r = 1 missing   */
 
+/* How the fetch count k* of a row was decided (row_path output): no fetch
+ * (eps^(L) < eps), from the top-tier gain candidates, from all gain
+ * candidates, or by the streaming selection over every token of L (taken
+ * when the candidates cannot decide the row, e.g. k* above 8192). */
+enum {
+  VKV_PATH_NO_FETCH = 0,
+  VKV_PATH_TOP_CANDIDATES = 1,
+  VKV_PATH_ALL_CANDIDATES = 2,
+  VKV_PATH_STREAMING = 3
+};
+
 /* Estimators for the L part: clipped shrinkage (Definition 2, eq. 5), the
  * unbiased lambda = 1 estimator (the PoissonComp-only baseline), or binary
  * shrinkage (Appendix A.2, Figure 2): lambda_i in {1, r_i}, with the tokens
@@ -150,7 +161,8 @@ typedef struct {
  * count, see VKV_STATUS_FETCH_OVERFLOW); host_bytes u64 [1] bytes read from
  * host_kv this step; row_stats (may be NULL) [B][Hq][8] f64 =
  * {m, D~ (scaled by exp(-m)), beta*, beta(L), V(L), b(L), eps^(L), eps^(L')}
- * (with VKV_EST_BINARY, beta* is the bias of the tokens set to lambda = r).
+ * (with VKV_EST_BINARY, beta* is the bias of the tokens set to lambda = r);
+ * row_path (may be NULL) [B][Hq] i32, how k* was decided (VKV_PATH_*).
  * status   dev u32 [1], cleared at the start of the call.
  * phase_events  optional timing hook: NULL, or vkv_decode_phase_count() + 1
  *          hipEvent_t handles (created by the caller); event 0 is recorded on
@@ -184,6 +196,7 @@ typedef struct {
   int32_t *fetch_count;
   uint64_t *host_bytes;
   double *row_stats;
+  int32_t *row_path;
   uint32_t *status;
   void **phase_events;
   void *workspace;

@@ -91,7 +91,7 @@ def shrinkage_beta(w, r, max_iter=200):
     return 0.5 * (lo + hi)
 
 
-def binary_lambdas(w, r, pos):
+def binary_lambdas(w, r, pos, moves=None):
     """Binary shrinkage (Appendix A.2, Figure 2): lambda_i in {1, r_i}.
 
     Moving token i from lambda_i = 1 to r_i adds the bias a_i = w_i (1 - r_i)
@@ -103,6 +103,10 @@ def binary_lambdas(w, r, pos):
     (strict: a move that leaves the MSE unchanged is not made). Along the
     order kappa falls and beta grows, so the first token that fails ends the
     moves. Returns (lambda, beta, number moved).
+
+    ``moves``: when given, exactly the first ``moves`` tokens of the order
+    are moved instead of applying the stopping test (to evaluate the plan
+    under another implementation's decision).
     """
     w = np.asarray(w, dtype=np.float64)
     r = np.asarray(r, dtype=np.float64)
@@ -111,7 +115,8 @@ def binary_lambdas(w, r, pos):
     beta = 0.0
     moved = 0
     for i in np.lexsort((np.asarray(pos), -kappa)):
-        if not kappa[i] > 2.0 * beta:
+        if (moves is None and not kappa[i] > 2.0 * beta) or \
+                (moves is not None and moved >= moves):
             break
         lam[i] = r[i]
         beta += w[i] * (1.0 - r[i])
@@ -224,11 +229,13 @@ def first_below(e, eps):
     return k
 
 
-def plan_row(wt, r, pos, dnorm, eps, delta, estimator=EST_CLIP):
+def plan_row(wt, r, pos, dnorm, eps, delta, estimator=EST_CLIP,
+             binary_moves=None):
     """Plan one decision over L: beta*, lambda, certificate, gains, k*.
 
     ``wt``: planning weights on L (shifted), ``r``: their inclusion
     probabilities, ``pos``: their positions, ``dnorm``: D~.
+    ``binary_moves``: see ``binary_lambdas(moves=...)``.
     """
     wt = np.asarray(wt, dtype=np.float64)
     r = np.asarray(r, dtype=np.float64)
@@ -236,7 +243,7 @@ def plan_row(wt, r, pos, dnorm, eps, delta, estimator=EST_CLIP):
         beta_star = shrinkage_beta(wt, r)
         lam = lambdas(wt, r, beta_star)
     elif estimator == EST_BINARY:
-        lam, beta_star, _ = binary_lambdas(wt, r, pos)
+        lam, beta_star, _ = binary_lambdas(wt, r, pos, binary_moves)
     else:
         beta_star = 0.0
         lam = np.ones_like(wt)
@@ -300,14 +307,17 @@ def combine(alpha, v_res, w_f, v_f):
 
 
 def decode_group(q, res_kv, res_idx, sketch, proj, r, host_kv, eps, delta,
-                 estimator=EST_CLIP, weights=W_SKETCH, fetch_override=None):
+                 estimator=EST_CLIP, weights=W_SKETCH, fetch_override=None,
+                 binary_moves=None):
     """KVFetch for the query heads sharing one KV head.
 
     q: [grp][d]; res_kv: [count][2][d]; res_idx: [count] ascending positions;
     sketch: [n][s]; proj: [d][s]; r: [n] float32; host_kv: [n][2][d] (full
     cache, only rows outside R and PERFECT planning read it).
-    ``fetch_override``: optional list (per head) of fetch sets F_h to use
-    instead of the planned ones (to evaluate the output of another plan).
+    ``fetch_override``: optional list (per head, None = the plan's own) of
+    fetch sets F_h to use instead of the planned ones (to evaluate the
+    output of another plan); ``binary_moves``: optional list (per head,
+    None = the stopping test) of how many tokens binary shrinkage moves.
     Returns (list of per-head dicts, union of fetched positions).
     """
     q = np.asarray(q, dtype=np.float64)
@@ -345,8 +355,10 @@ def decode_group(q, res_kv, res_idx, sketch, proj, r, host_kv, eps, delta,
         w_res = np.exp(ell - m)
         wt = np.exp(s_l - m)
         dnorm = float(np.sum(w_res[res_h]) + np.sum(wt))
-        plan = plan_row(wt, rl, lpos, dnorm, eps, delta, estimator)
-        fpos = plan["fetch_pos"] if fetch_override is None \
+        plan = plan_row(wt, rl, lpos, dnorm, eps, delta, estimator,
+                        None if binary_moves is None else binary_moves[h])
+        fpos = plan["fetch_pos"] \
+            if fetch_override is None or fetch_override[h] is None \
             else np.asarray(fetch_override[h], dtype=np.int64)
         in_f = np.zeros(n, dtype=bool)
         in_f[fpos] = True

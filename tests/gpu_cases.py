@@ -137,7 +137,9 @@ def binary_tie(w, b, h, hd, beta_gpu):
     """Binary shrinkage: the library moved a different number of tokens than
     the oracle. Accepted as a tie when every token whose decision differs is
     a near tie of the stopping test in the oracle's own numbers,
-    |kappa - 2 beta| <= 1e-5 kappa (the library decides on fp32 weights)."""
+    |kappa - 2 beta| <= 1e-5 kappa (the library decides on fp32 weights).
+    Returns the library's move count (the prefix of the oracle's order whose
+    bias matches the library's), or None when it is not a tie."""
     g = h // (w["Hq"] // w["G"])
     lpos = hd["lpos"]
     r = w["r_all"][b, g][lpos].astype(np.float64)
@@ -148,22 +150,68 @@ def binary_tie(w, b, h, hd, beta_gpu):
     ko = int(np.sum(hd["lam"] != 1.0))
     kg = int(np.argmin(np.abs(pre - beta_gpu)))
     if abs(pre[kg] - beta_gpu) > TOL_BETA * max(beta_gpu, 1e-300):
-        return False
+        return None
     ks = np.arange(min(ko, kg), max(ko, kg))
     kap = kappa[order][ks]
-    return bool(ks.size) and bool(np.all(np.abs(kap - 2.0 * pre[ks]) <= TIE * kap))
+    ok = bool(ks.size) and bool(np.all(np.abs(kap - 2.0 * pre[ks]) <= TIE * kap))
+    return kg if ok else None
 
 
-def compare(w, gpu, heads, unions, eps, est=0, max_tie_frac=0.01):
+def kstar_tie(hd, kg, eps):
+    """The library's k* differs from the oracle's. A tie when the oracle's
+    own certificate is within 1e-5 relative of eps wherever the two
+    stopping decisions differ (at kg when the library stops first, else at
+    kg - 1: the oracle's eps^_k fall with k, so that is the farthest), or
+    when every token between the two cut points has a gain within 1e-5 of
+    the gain at the oracle's k*. Returns (tie, the tokens whose membership
+    in F_h the tie leaves open)."""
+    ko = hd["k_star"]
+    if hd["order"] is None or kg <= 0 or kg > hd["order"].size:
+        return False, None
+    suf = hd["suffix"]
+    kd = kg if kg < ko else kg - 1
+    if kd < suf.size and abs(suf[kd] - eps) <= TIE * eps:
+        return True, np.zeros(0, dtype=np.int64)
+    lo_k, hi_k = min(kg, ko), max(kg, ko)
+    g = hd["gains"][hd["order"]]
+    gk = g[max(ko - 1, 0)]
+    band = np.abs(g - gk) <= TIE * gk
+    if np.all(band[max(lo_k - 1, 0):hi_k]):
+        return True, np.sort(hd["lpos"][hd["order"][band]])
+    return False, None
+
+
+def rerun_group(w, b, g, eps, est, weights, binary_moves=None,
+                fetch_override=None):
+    """The oracle for one (request, KV head) under the given overrides."""
+    grp = w["Hq"] // w["G"]
+    sl = w["cm"][b][g]
+    return od.decode_group(bf16_to_f32(w["q"][b, g * grp:(g + 1) * grp]),
+                           sl["resident_kv"], sl["resident_idx"],
+                           bf16_to_f32(w["sketch"][b, g]), w["proj"][g],
+                           w["r_all"][b, g], bf16_to_f32(w["host_kv"][b, g]),
+                           eps, w["delta"], est, weights,
+                           fetch_override=fetch_override,
+                           binary_moves=binary_moves)
+
+
+def compare(w, gpu, heads, unions, eps, est=0, weights=0, max_tie_frac=0.01):
     """Apply the parity rules; returns a summary dict. Every violation is
-    collected and reported together."""
+    collected and reported together.
+
+    A tie-accepted row is not skipped: the oracle is run again for its KV
+    head under the library's decision (binary shrinkage: the library's move
+    count; k*: the oracle's own gain order cut at the library's k*), and
+    eps^(L), eps^(L'), D^, the output and the fetch union are checked
+    against that run at the same tolerances. At most floor(1% of the rows)
+    may be tie-accepted."""
     B, Hq, G = w["B"], w["Hq"], w["G"]
     grp = Hq // G
     bad = []
     if gpu["rc"] != 0:
         bad.append(f"status rc={gpu['rc']} bits={gpu['bits']:#x}")
     ties = 0
-    tie_rows = set()
+    tie_rows = []
     worst = dict(beta=0.0, fixed_point=0.0, eps0=0.0, eps1=0.0, dhat=0.0, o=0.0)
 
     def check(name, err, tol, where):
@@ -171,80 +219,99 @@ def compare(w, gpu, heads, unions, eps, est=0, max_tie_frac=0.01):
         if not err <= tol:
             bad.append(f"{name} {where}: {err:.3e} > {tol:.0e}")
 
-    for b in range(B):
-        for h in range(Hq):
-            hd = heads[b][h]
-            st = gpu["row_stats"][b, h]
-            where = f"(b={b},h={h})"
-            if est == od.EST_CLIP and hd["beta_star"] > 0:
-                check("beta", _rel(st[2], hd["beta_star"]), TOL_BETA, where)
-                check("fixed_point", abs(st[3] - st[2]) / st[1], TOL_FIXED_POINT,
-                      where)
-            if est == od.EST_BINARY:
-                # the moved tokens' bias; beta(L) from the certificate pass
-                # must be the same sum (both passes apply one rule)
-                check("fixed_point", abs(st[3] - st[2]) / st[1], TOL_FIXED_POINT,
-                      where)
-                bo = hd["beta_star"]
-                eb = 0.0 if bo == st[2] == 0.0 else _rel(st[2], bo)
-                if not eb <= TOL_BETA and binary_tie(w, b, h, hd, float(st[2])):
-                    ties += 1
-                    tie_rows.add((b, h))
-                    continue
-                check("beta", eb, TOL_BETA, where)
-            check("eps0", _rel(float(gpu["eps_hat0"][b, h]), hd["eps_hat0"]),
-                  TOL_EPS, where)
-            kg, ko = int(gpu["k_star"][b, h]), hd["k_star"]
-            if kg != ko:
-                ok = hd["order"] is not None and kg > 0
-                if ok:
-                    # the stopping decisions differ at kg when the library
-                    # stops first, and at every k in [ko, kg) otherwise (the
-                    # oracle's eps^_k fall with k, so kg - 1 is the farthest)
-                    suf = hd["suffix"]
-                    kd = kg if kg < ko else kg - 1
-                    near = kd < suf.size and abs(suf[kd] - eps) <= TIE * eps
-                    lo_k, hi_k = min(kg, ko), max(kg, ko)
-                    g = hd["gains"][hd["order"]]
-                    gk = g[max(ko - 1, 0)]
-                    gap = bool(np.all(np.abs(g[max(lo_k - 1, 0):hi_k] - gk)
-                                      <= TIE * gk))
-                    ok = near or gap
-                if not ok:
-                    bad.append(f"k* {where}: gpu {kg} oracle {ko} (not a tie)")
-                ties += 1
-                tie_rows.add((b, h))
-                continue
-            check("eps1", _rel(float(gpu["eps_hat"][b, h]), hd["eps_hat"]),
-                  TOL_EPS, where)
-            logd_g = math.log(max(float(gpu["d_hat"][b, h]), 1e-300)) + \
-                float(gpu["log_shift"][b, h])
-            logd_o = math.log(hd["d_hat"]) + hd["m"]
-            check("dhat", abs(math.expm1(logd_g - logd_o)), TOL_D, where)
-            o_g = gpu["out"][b, h].astype(np.float64)
-            check("o", float(np.linalg.norm(o_g - hd["o"]) /
-                             np.linalg.norm(hd["o"])), TOL_O, where)
-    n_rows = B * Hq
-    if ties > max(1, max_tie_frac * n_rows):
-        bad.append(f"{ties} tie-accepted rows of {n_rows}")
     fetched = 0
     for b in range(B):
         for g in range(G):
+            hs = [heads[b][g * grp + j] for j in range(grp)]
+            union = unions[b][g]
+            # binary shrinkage: beta (the moved tokens' bias) and ties of
+            # the move count
+            moves = [None] * grp
+            for j in range(grp):
+                h = g * grp + j
+                hd, st, where = hs[j], gpu["row_stats"][b, h], f"(b={b},h={h})"
+                if est == od.EST_CLIP and hd["beta_star"] > 0:
+                    check("beta", _rel(st[2], hd["beta_star"]), TOL_BETA, where)
+                    check("fixed_point", abs(st[3] - st[2]) / st[1],
+                          TOL_FIXED_POINT, where)
+                if est == od.EST_BINARY:
+                    # beta(L) from the certificate pass must be the same sum
+                    # (both passes apply one rule)
+                    check("fixed_point", abs(st[3] - st[2]) / st[1],
+                          TOL_FIXED_POINT, where)
+                    bo = hd["beta_star"]
+                    eb = 0.0 if bo == st[2] == 0.0 else _rel(st[2], bo)
+                    if not eb <= TOL_BETA:
+                        kg = binary_tie(w, b, h, hd, float(st[2]))
+                        if kg is None:
+                            check("beta", eb, TOL_BETA, where)
+                        else:
+                            moves[j] = kg
+                            tie_rows.append((b, h, "binary"))
+            if any(m is not None for m in moves):
+                hs, union = rerun_group(w, b, g, eps, est, weights,
+                                        binary_moves=moves)
+            # k*: exact, or a tie scored under the library's k*
+            over = [None] * grp
+            open_tokens = []
+            for j in range(grp):
+                h = g * grp + j
+                kg, ko = int(gpu["k_star"][b, h]), hs[j]["k_star"]
+                if kg == ko:
+                    continue
+                tie, toks = kstar_tie(hs[j], kg, eps)
+                if not tie:
+                    bad.append(f"k* (b={b},h={h}): gpu {kg} oracle {ko} "
+                               f"(not a tie)")
+                    continue
+                over[j] = hs[j]["lpos"][hs[j]["order"][:kg]]
+                open_tokens.append(toks)
+                tie_rows.append((b, h, "k*"))
+            kset = [None] * grp
+            if any(o is not None for o in over):
+                kset = [hs[j]["suffix"][int(gpu["k_star"][b, g * grp + j])]
+                        if over[j] is not None else None for j in range(grp)]
+                hs, union = rerun_group(w, b, g, eps, est, weights,
+                                        binary_moves=moves,
+                                        fetch_override=over)
+            for j in range(grp):
+                h = g * grp + j
+                hd, where = hs[j], f"(b={b},h={h})"
+                check("eps0", _rel(float(gpu["eps_hat0"][b, h]), hd["eps_hat0"]),
+                      TOL_EPS, where)
+                e1 = hd["eps_hat"] if kset[j] is None else kset[j]
+                check("eps1", _rel(float(gpu["eps_hat"][b, h]), e1), TOL_EPS,
+                      where)
+                logd_g = math.log(max(float(gpu["d_hat"][b, h]), 1e-300)) + \
+                    float(gpu["log_shift"][b, h])
+                logd_o = math.log(hd["d_hat"]) + hd["m"]
+                check("dhat", abs(math.expm1(logd_g - logd_o)), TOL_D, where)
+                o_g = gpu["out"][b, h].astype(np.float64)
+                check("o", float(np.linalg.norm(o_g - hd["o"]) /
+                                 np.linalg.norm(hd["o"])), TOL_O, where)
             cnt = int(gpu["fetch_count"][b, g])
             got = gpu["fetch_idx"][b, g, :cnt]
             if not np.all(np.diff(got) > 0):
                 bad.append(f"fetch list (b={b},g={g}) not ascending")
             fetched += cnt
-            if any((b, g * grp + j) in tie_rows for j in range(grp)):
-                continue
-            if not np.array_equal(got, unions[b][g]):
+            diff = set(got.tolist()) ^ set(union.tolist())
+            allowed = set(np.concatenate(open_tokens).tolist()) \
+                if open_tokens else set()
+            if diff - allowed:
                 bad.append(f"fetch union (b={b},g={g}): gpu {cnt} oracle "
-                           f"{unions[b][g].size}, sym diff "
-                           f"{len(set(got.tolist()) ^ set(unions[b][g].tolist()))}")
+                           f"{union.size}, sym diff {len(diff)} "
+                           f"({len(diff - allowed)} outside gain ties)")
+    n_rows = B * Hq
+    ties = len(tie_rows)
+    if ties > int(max_tie_frac * n_rows):
+        bad.append(f"{ties} tie-accepted rows of {n_rows}: {tie_rows}")
     if int(gpu["host_bytes"][0]) != fetched * 512:
         bad.append(f"host_bytes {int(gpu['host_bytes'][0])} != {fetched * 512}")
-    summary = dict(ties=ties, rows=n_rows, fetched=fetched, worst=worst,
-                   fetch_frac=fetched / (B * G * w["n"]),
+    summary = dict(ties=ties, tie_rows=tie_rows, rows=n_rows, fetched=fetched,
+                   worst=worst, fetch_frac=fetched / (B * G * w["n"]),
                    kstar_mean=float(np.mean(gpu["k_star"])))
+    if "row_path" in gpu:
+        summary["paths"] = np.bincount(gpu["row_path"].ravel(),
+                                       minlength=4).tolist()
     assert not bad, "\n".join(bad[:40] + [f"... {len(bad)} problems", str(summary)])
     return summary

@@ -137,7 +137,7 @@ def _decode_case(cfg, eps=None, est=0, weights=0, seed=0, fetch_cap=None,
 @pytest.mark.parametrize("weights", [0, 1])
 def test_decode_c1(weights):
     w, gpu, heads, unions, eps = _decode_case("c1", weights=weights)
-    s = gc.compare(w, gpu, heads, unions, eps)
+    s = gc.compare(w, gpu, heads, unions, eps, weights=weights)
     gc.say(f"  {s}")
     assert s["ties"] == 0  # the tiny case must match exactly
 
@@ -145,14 +145,14 @@ def test_decode_c1(weights):
 @pytest.mark.parametrize("weights", [0, 1])
 def test_decode_c1_unbiased(weights):
     w, gpu, heads, unions, eps = _decode_case("c1", est=1, weights=weights)
-    s = gc.compare(w, gpu, heads, unions, eps, est=1)
+    s = gc.compare(w, gpu, heads, unions, eps, est=1, weights=weights)
     gc.say(f"  {s}")
 
 
 @pytest.mark.parametrize("weights", [0, 1])
 def test_decode_c1_binary(weights):
     w, gpu, heads, unions, eps = _decode_case("c1", est=2, weights=weights)
-    s = gc.compare(w, gpu, heads, unions, eps, est=2)
+    s = gc.compare(w, gpu, heads, unions, eps, est=2, weights=weights)
     gc.say(f"  {s}")
     assert s["ties"] == 0
 
@@ -348,13 +348,47 @@ def test_decode_bad_r_reported():
     assert gpu["bits"] & vk.STATUS_BAD_R
 
 
-def test_decode_deterministic():
-    w = gc.build_case("c2", n=4000, G=2)
+@pytest.mark.parametrize("cfg,kw", [
+    ("c2", dict(n=4000, G=2)),
+    ("c3", dict(n=6000, G=2, B=4, seed=1, shift_from=2)),
+])
+@pytest.mark.parametrize("est", [0, 2])
+def test_decode_deterministic(cfg, kw, est):
+    """Two runs of the same step give bit-identical outputs: every reduction
+    runs in a fixed order and no result depends on the scheduling of
+    workgroups (no float atomics)."""
+    w = gc.build_case(cfg, **kw)
     dev = gc.device_inputs(w)
-    a = gc.run_library(w, dev, w["eps"], w["delta"])
-    b = gc.run_library(w, dev, w["eps"], w["delta"])
-    for key in ("k_star", "fetch_count", "fetch_idx", "eps_hat0"):
-        assert np.array_equal(a[key], b[key]), key
+    gc.say(f"decode determinism {cfg} est={est}")
+    a = gc.run_library(w, dev, w["eps"], w["delta"], est)
+    b = gc.run_library(w, dev, w["eps"], w["delta"], est)
+    assert a["rc"] == b["rc"] == 0
+    for key in ("out", "d_hat", "log_shift", "eps_hat0", "eps_hat", "k_star",
+                "fetch_count", "host_bytes", "row_stats", "row_path"):
+        assert a[key].tobytes() == b[key].tobytes(), key
+    for bb in range(w["B"]):
+        for g in range(w["G"]):
+            c = int(a["fetch_count"][bb, g])
+            assert np.array_equal(a["fetch_idx"][bb, g, :c],
+                                  b["fetch_idx"][bb, g, :c])
+    assert int(a["host_bytes"][0]) > 0
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("eps", [1e-30, 2e-4])
+def test_decode_streaming_selection(eps):
+    """The streaming selection over every token of L, the fallback taken
+    when the gain candidates (at most 8192 per row) cannot decide a row: a
+    full-length 32K layer (one KV head, ~30K tokens in L) with eps small
+    enough that k* exceeds the candidates, over several rounds of the
+    selection. The row_path output shows that the fallback decided every
+    row, and every output matches the oracle (the decide kernel's full-row
+    re-solve, "Verify Before You Fetch", Appendix A.3)."""
+    w, gpu, heads, unions, eps = _decode_case("c2", eps=eps, G=1)
+    s = gc.compare(w, gpu, heads, unions, eps)
+    gc.say(f"  {s}")
+    assert np.all(gpu["row_path"] == vk.PATH_STREAMING), gpu["row_path"]
+    assert np.all(gpu["k_star"] > 8192), gpu["k_star"]
 
 
 @pytest.mark.parametrize("est", [0, 2])
@@ -391,3 +425,17 @@ def test_decode_certificate_coverage_on_gpu(est):
         fails += err > float(out["eps_hat"][0, 0])
     gc.say(f"  coverage failures {fails} of {n_trials} (delta {delta})")
     assert fails <= delta * n_trials + 3 * math.sqrt(delta * n_trials)
+
+
+@pytest.mark.timeout(600)
+def test_decode_all_candidates_tier():
+    """k* between the top tier (2048 candidates per row) and all candidates
+    (8192): a full-length 32K layer at eps = 0.01 (oracle k* of 2.3K-6K).
+    Every row is decided by the larger candidate tier or the streaming
+    selection, at least one by the candidates, and every output matches."""
+    w, gpu, heads, unions, eps = _decode_case("c2", eps=0.01, G=1)
+    s = gc.compare(w, gpu, heads, unions, eps)
+    gc.say(f"  {s}")
+    paths = gpu["row_path"].ravel()
+    assert np.all((paths == vk.PATH_ALL_CANDIDATES) | (paths == vk.PATH_STREAMING))
+    assert np.any(paths == vk.PATH_ALL_CANDIDATES)

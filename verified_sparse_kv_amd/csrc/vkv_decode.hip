@@ -74,6 +74,7 @@ struct RowState {
   unsigned long long T;   // F_h = {i in L : key_i >= T}
   unsigned long long bkey;  // binary shrinkage: lambda = r for keys >= bkey
   float eps1;             // eps^(L') after fetching
+  int32_t path;           // how k* was decided (VKV_PATH_*)
 };
 
 
@@ -110,6 +111,7 @@ struct DParams {
   int32_t *k_star, *fidx, *fcount;
   unsigned long long *host_bytes;
   double *row_stats;
+  int32_t *row_path;
   uint32_t *status;
   float *shat, *ell;
   uint32_t *fbits;
@@ -2946,6 +2948,7 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rwalk(DParams p) {
       rs.T = T;
       rs.eps1 = (float)eps_of(dr[0] + s_dsum[0], dr[1] + s_dsum[1],
                               (double)__uint_as_float(bm), rs.dnorm, a, l);
+      rs.path = tier == 0 ? VKV_PATH_TOP_CANDIDATES : VKV_PATH_ALL_CANDIDATES;
       p.rows[row] = rs;
     }
     return;
@@ -2956,7 +2959,10 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rwalk(DParams p) {
                    p.l_delta, p.eps, p.n, p.nwords, p.est};
   select_row(sa, row, bg, rs, lds.sel);
   __syncthreads();
-  if (threadIdx.x == 0) p.rows[row] = rs;
+  if (threadIdx.x == 0) {
+    rs.path = VKV_PATH_STREAMING;
+    p.rows[row] = rs;
+  }
 }
 
 // ------------------------------------------------------------ fetch
@@ -3312,6 +3318,7 @@ __device__ __forceinline__ void attn_merge_row(const DParams &p, int row) {
     p.eps_hat0[row] = (float)rs.eps0;
     p.eps_hat[row] = rs.fetch ? rs.eps1 : (float)rs.eps0;
     p.k_star[row] = rs.fetch ? rs.kstar : 0;
+    if (p.row_path) p.row_path[row] = rs.fetch ? rs.path : VKV_PATH_NO_FETCH;
     if (p.row_stats) {
       double *sr = p.row_stats + (size_t)row * 8;
       sr[0] = rs.m;
@@ -3551,6 +3558,7 @@ hipError_t launch_decode(const vkv_decode_args &a, const DecodeLayout &L,
   p.fcount = a.fetch_count;
   p.host_bytes = reinterpret_cast<unsigned long long *>(a.host_bytes);
   p.row_stats = a.row_stats;
+  p.row_path = a.row_path;
   p.status = a.status;
   void *w = a.workspace;
   p.rows = at<RowState>(w, L.rows);

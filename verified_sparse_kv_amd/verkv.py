@@ -27,6 +27,8 @@ STATUS_FETCH_OVERFLOW = 0x2
 STATUS_BAD_R = 0x4
 STATUS_BAD_RESIDENT = 0x8
 EST_CLIP, EST_UNBIASED, EST_BINARY = 0, 1, 2
+PATH_NO_FETCH, PATH_TOP_CANDIDATES, PATH_ALL_CANDIDATES, PATH_STREAMING = \
+    0, 1, 2, 3
 W_SKETCH, W_PERFECT = 0, 1
 
 EXPORTS = ("vkv_compress_workspace_bytes", "vkv_decode_workspace_bytes",
@@ -62,7 +64,8 @@ class DecodeArgs(ctypes.Structure):
                 ("out", _p), ("d_hat", _p), ("log_shift", _p), ("eps_hat0", _p),
                 ("eps_hat", _p), ("k_star", _p), ("fetch_idx", _p),
                 ("fetch_count", _p), ("host_bytes", _p), ("row_stats", _p),
-                ("status", _p), ("phase_events", _p), ("workspace", _p),
+                ("row_path", _p), ("status", _p), ("phase_events", _p),
+                ("workspace", _p),
                 ("workspace_bytes", ctypes.c_size_t)]
 
 
@@ -276,13 +279,14 @@ class DecodeStep:
             host_bytes=torch.zeros((1,), dtype=torch.int64, device=device),
             row_stats=torch.empty((B, Hq, 8), dtype=torch.float64,
                                   device=device),
+            row_path=torch.empty((B, Hq), dtype=torch.int32, device=device),
             status=torch.zeros((1,), dtype=torch.int32, device=device))
         self.args = DecodeArgs(batch=B, n_q_heads=Hq, n_kv_heads=G, head_dim=d,
                                n_tokens=n, sketch_dim=s, cap=cap,
                                fetch_cap=fetch_cap)
         for key in ("out", "d_hat", "log_shift", "eps_hat0", "eps_hat", "k_star",
                     "fetch_idx", "fetch_count", "host_bytes", "row_stats",
-                    "status"):
+                    "row_path", "status"):
             setattr(self.args, key, _ptr(self.out[key]))
         nbytes = vkv_decode_workspace_bytes(self.args)
         if nbytes == 0:
