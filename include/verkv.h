@@ -240,6 +240,26 @@ vkv_status vkv_compress(const vkv_compress_args *a, void *stream);
 /* Enqueue one KVFetch decode step (see vkv_decode_args). */
 vkv_status vkv_decode_step(const vkv_decode_args *a, void *stream);
 
+/* Size of the library's own decode workspace (128 MiB per GPU), used by
+ * vkv_decode_step_noalloc. */
+#define VKV_NOALLOC_WORKSPACE_BYTES (128u << 20)
+
+/* vkv_decode_step for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same step and outputs, with the workspace taken from a
+ * buffer the library holds on each GPU (VKV_NOALLOC_WORKSPACE_BYTES,
+ * placed when the library's code is loaded on that GPU and held until the
+ * process ends). a->workspace must be NULL and a->workspace_bytes 0; the
+ * caller still passes every input and output. Shapes whose workspace
+ * (vkv_decode_workspace_bytes) exceeds the buffer return VKV_EUNSUPPORTED
+ * (for example: batch 1 fits up to 128K tokens at 32 query heads over 8
+ * KV heads; batch 16 at 32K does not). The call allocates nothing and
+ * needs the buffer cleared by nobody: the kernels initialise what they
+ * read. Every call on one GPU shares that GPU's buffer, which keeps the
+ * last call's contents: calls that overlap on one GPU (other streams,
+ * other threads) race, and the caller must order them. */
+vkv_status vkv_decode_step_noalloc(const vkv_decode_args *a, void *stream);
+
 /* Enqueue one exact decode attention over the whole cache (see
  * vkv_dense_args). */
 vkv_status vkv_dense_attention(const vkv_dense_args *a, void *stream);

@@ -222,3 +222,17 @@ def test_one_hip_runtime_in_process():
     maps = open("/proc/self/maps").read().splitlines()
     hip = {l.split()[-1] for l in maps if "libamdhip64" in l}
     assert len(hip) == 1, hip
+
+
+def test_noalloc_validation_before_any_launch():
+    """The no-allocation decode entry point checks its arguments on the host:
+    a caller workspace is refused, and shapes whose workspace exceeds the
+    library's buffer return VKV_EUNSUPPORTED, both before touching a GPU."""
+    a = _decode_args(batch=16, n_tokens=32768, cap=4700, fetch_cap=32768)
+    assert vk.vkv_decode_workspace_bytes(a) > vk.NOALLOC_WORKSPACE_BYTES
+    assert vk.vkv_decode_step_noalloc(a, None) == vk.VKV_EUNSUPPORTED
+    assert "buffer" in vk.vkv_last_error()
+    a = _decode_args()
+    a.workspace, a.workspace_bytes = ctypes.c_void_p(0x1000), 1 << 20
+    assert vk.vkv_decode_step_noalloc(a, None) == vk.VKV_EINVAL
+    assert "NULL" in vk.vkv_last_error()

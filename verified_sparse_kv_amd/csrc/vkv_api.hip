@@ -5,6 +5,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "vkv_common.h"
 #include "vkv_internal.h"
 
@@ -92,6 +94,82 @@ vkv_status check_decode_shapes(const vkv_decode_args *a) {
   return VKV_OK;
 }
 
+// The workspace of vkv_decode_step_noalloc: one library-owned device buffer
+// per GPU (the loader places it when the code object is loaded on that GPU;
+// it is held until the process ends). In host code `scratch` names a
+// host-side stand-in, not the device buffer: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+static __device__ __align__(256) unsigned char scratch[VKV_NOALLOC_WORKSPACE_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (looked up on the first call
+// on that device, with the device current).
+vkv_status scratch_for_current_device(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "decode_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(VKV_EUNSUPPORTED, "decode_noalloc: device %d (supported: 0..%d)",
+                dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                      "decode_noalloc: hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return VKV_OK;
+}
+
+// Argument checks of a decode step that need no workspace and no GPU.
+vkv_status check_decode_args(const vkv_decode_args *a) {
+  vkv_status st = check_decode_shapes(a);
+  if (st != VKV_OK) return st;
+  REQUIRE(a->eps > 0.0f && isfinite(a->eps), "decode: eps must be > 0");
+  REQUIRE(a->delta > 0.0f && a->delta < 1.0f, "decode: delta must be in (0, 1)");
+  REQUIRE(a->estimator == VKV_EST_CLIP || a->estimator == VKV_EST_UNBIASED ||
+              a->estimator == VKV_EST_BINARY,
+          "decode: unknown estimator %d", a->estimator);
+  REQUIRE(a->weights == VKV_W_SKETCH || a->weights == VKV_W_PERFECT,
+          "decode: unknown weights mode %d", a->weights);
+  REQUIRE(a->q && a->resident_kv && a->resident_idx && a->resident_count && a->r &&
+              a->host_kv,
+          "decode: q, resident_kv, resident_idx, resident_count, r and host_kv are required");
+  REQUIRE(a->weights == VKV_W_PERFECT || (a->sketch && a->proj),
+          "decode: sketch and proj are required in sketch mode");
+  REQUIRE(a->out && a->d_hat && a->log_shift && a->eps_hat0 && a->eps_hat &&
+              a->k_star && a->fetch_idx && a->fetch_count && a->host_bytes && a->status,
+          "decode: every output pointer except row_stats and row_path is required");
+  return VKV_OK;
+}
+
+// The pinned-memory check and the launch, with the workspace `ws`.
+vkv_status decode_launch(const vkv_decode_args *a, const vkv::DecodeLayout &L,
+                         void *ws, void *stream) {
+  // host_kv must be pinned host memory the GPU can read
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, a->host_kv);
+  if (e != hipSuccess || attr.type != hipMemoryTypeHost || attr.devicePointer == nullptr) {
+    (void)hipGetLastError();
+    return fail(VKV_ENOTPINNED,
+                "decode: host_kv is not device-accessible pinned host memory (%s)",
+                e != hipSuccess ? hipGetErrorString(e) : "wrong memory type");
+  }
+  const uint16_t *hkv = static_cast<const uint16_t *>(attr.devicePointer);
+  vkv_decode_args b = *a;
+  b.workspace = ws;
+  b.workspace_bytes = L.total;
+  e = vkv::launch_decode(b, L, hkv, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return VKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -144,39 +222,31 @@ vkv_status vkv_compress(const vkv_compress_args *a, void *stream) {
 }
 
 vkv_status vkv_decode_step(const vkv_decode_args *a, void *stream) {
-  vkv_status st = check_decode_shapes(a);
+  vkv_status st = check_decode_args(a);
   if (st != VKV_OK) return st;
-  REQUIRE(a->eps > 0.0f && isfinite(a->eps), "decode: eps must be > 0");
-  REQUIRE(a->delta > 0.0f && a->delta < 1.0f, "decode: delta must be in (0, 1)");
-  REQUIRE(a->estimator == VKV_EST_CLIP || a->estimator == VKV_EST_UNBIASED ||
-              a->estimator == VKV_EST_BINARY,
-          "decode: unknown estimator %d", a->estimator);
-  REQUIRE(a->weights == VKV_W_SKETCH || a->weights == VKV_W_PERFECT,
-          "decode: unknown weights mode %d", a->weights);
-  REQUIRE(a->q && a->resident_kv && a->resident_idx && a->resident_count && a->r &&
-              a->host_kv,
-          "decode: q, resident_kv, resident_idx, resident_count, r and host_kv are required");
-  REQUIRE(a->weights == VKV_W_PERFECT || (a->sketch && a->proj),
-          "decode: sketch and proj are required in sketch mode");
-  REQUIRE(a->out && a->d_hat && a->log_shift && a->eps_hat0 && a->eps_hat &&
-              a->k_star && a->fetch_idx && a->fetch_count && a->host_bytes && a->status,
-          "decode: every output pointer except row_stats is required");
   const vkv::DecodeLayout L = vkv::decode_layout(*a);
   REQUIRE(a->workspace != nullptr && a->workspace_bytes >= L.total,
           "decode: workspace of %zu bytes needed", L.total);
-  // host_kv must be pinned host memory the GPU can read
-  hipPointerAttribute_t attr;
-  hipError_t e = hipPointerGetAttributes(&attr, a->host_kv);
-  if (e != hipSuccess || attr.type != hipMemoryTypeHost || attr.devicePointer == nullptr) {
-    (void)hipGetLastError();
-    return fail(VKV_ENOTPINNED,
-                "decode: host_kv is not device-accessible pinned host memory (%s)",
-                e != hipSuccess ? hipGetErrorString(e) : "wrong memory type");
-  }
-  const uint16_t *hkv = static_cast<const uint16_t *>(attr.devicePointer);
-  e = vkv::launch_decode(*a, L, hkv, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "decode launch");
-  return VKV_OK;
+  return decode_launch(a, L, a->workspace, stream);
+}
+
+vkv_status vkv_decode_step_noalloc(const vkv_decode_args *a, void *stream) {
+  vkv_status st = check_decode_args(a);
+  if (st != VKV_OK) return st;
+  REQUIRE(a->workspace == nullptr && a->workspace_bytes == 0,
+          "decode_noalloc: workspace must be NULL with workspace_bytes 0 (the "
+          "library's own buffer is used)");
+  const vkv::DecodeLayout L = vkv::decode_layout(*a);
+  if (L.total > (size_t)VKV_NOALLOC_WORKSPACE_BYTES)
+    return fail(VKV_EUNSUPPORTED,
+                "decode_noalloc: these shapes need a workspace of %zu bytes, "
+                "above the library's buffer of %zu bytes (use vkv_decode_step "
+                "with a caller workspace)",
+                L.total, (size_t)VKV_NOALLOC_WORKSPACE_BYTES);
+  void *ws = nullptr;
+  st = scratch_for_current_device(&ws);
+  if (st != VKV_OK) return st;
+  return decode_launch(a, L, ws, stream);
 }
 
 vkv_status vkv_dense_attention(const vkv_dense_args *a, void *stream) {

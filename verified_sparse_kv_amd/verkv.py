@@ -35,7 +35,8 @@ EXPORTS = ("vkv_compress_workspace_bytes", "vkv_decode_workspace_bytes",
            "vkv_compress", "vkv_decode_step", "vkv_check_status",
            "vkv_last_error", "vkv_version", "vkv_decode_phase_count",
            "vkv_decode_phase_name", "vkv_dense_workspace_bytes",
-           "vkv_dense_attention")
+           "vkv_dense_attention", "vkv_decode_step_noalloc")
+NOALLOC_WORKSPACE_BYTES = 128 << 20
 
 _p = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -107,6 +108,8 @@ def _load():
     lib.vkv_compress.restype = ctypes.c_int
     lib.vkv_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _p]
     lib.vkv_decode_step.restype = ctypes.c_int
+    lib.vkv_decode_step_noalloc.argtypes = [ctypes.POINTER(DecodeArgs), _p]
+    lib.vkv_decode_step_noalloc.restype = ctypes.c_int
     lib.vkv_check_status.argtypes = [_p, _p, ctypes.POINTER(ctypes.c_uint32)]
     lib.vkv_check_status.restype = ctypes.c_int
     lib.vkv_last_error.argtypes = []
@@ -142,6 +145,10 @@ def vkv_compress(args, stream=None):
 
 def vkv_decode_step(args, stream=None):
     return int(LIB.vkv_decode_step(ctypes.byref(args), stream))
+
+
+def vkv_decode_step_noalloc(args, stream=None):
+    return int(LIB.vkv_decode_step_noalloc(ctypes.byref(args), stream))
 
 
 def vkv_dense_workspace_bytes(args):
