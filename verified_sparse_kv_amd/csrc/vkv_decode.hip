@@ -209,13 +209,11 @@ __device__ __forceinline__ Terms token_terms_w(float wt, float r,
   t.wt = wt;
   t.qr = qr_of(r);
   float lam = 1.0f;
-  if (lr.est == VKV_EST_CLIP) {
-    if (wt > 0.0f) {
-      const float x = lr.beta * r * __builtin_amdgcn_rcpf(wt * (1.0f - r));
-      lam = fminf(1.0f, fmaxf(r, x));
-    }
+  if (lr.est == VKV_EST_CLIP) {  // (uniform; the rest selects, no branches)
+    const float x = lr.beta * r * __builtin_amdgcn_rcpf(wt * (1.0f - r));
+    lam = wt > 0.0f ? fminf(1.0f, fmaxf(r, x)) : 1.0f;
   } else if (lr.est == VKV_EST_BINARY) {
-    if (bin_key(wt, t.qr, pos) >= lr.bkey) lam = r;
+    lam = bin_key(wt, t.qr, pos) >= lr.bkey ? r : 1.0f;
   }
   t.lam = lam;
   t.bi = wt * (1.0f - lam);
@@ -267,20 +265,30 @@ __device__ __forceinline__ float token_gain(const Terms &t, int pos,
   return t.bi + a * (b1 - bp) + frac;
 }
 
-__device__ __forceinline__ unsigned long long to_fx(float x, int e) {
-  return (unsigned long long)__double2ull_rn(ldexp((double)x, e));
+// A term of the selection's fixed-point sums: min(x, cap) 2^e, truncated to
+// an integer, formed from the fp32 bits of x >= 0 (the significand shifted
+// by the exponent; values below 2^-e become 0), with no float64 arithmetic.
+// The caps are c = 2 eps D~ for beta_i and c^2 / (2 l) for v_i (compared in
+// fp32): a rest holding a term at its cap has eps^ >= 2 eps (to within the
+// cap's fp32 rounding) whether the term is capped or not, so capping never
+// changes a stopping decision, while a rest that can stop holds only exact
+// terms. The scale follows eps D~ (cap 2^e < 2^40), not the largest term,
+// so rests near the stopping point keep ~40 bits however heavy the fetched
+// tokens are; with at most 2^17 tokens no sum overflows. Every pass forms
+// the terms with this one function, so all passes agree bit for bit.
+__device__ __forceinline__ unsigned long long fx_bits(float x, int e) {
+  const uint32_t u = __float_as_uint(x);
+  const int E = (int)(u >> 23);
+  const unsigned long long m = (unsigned long long)((u & 0x7FFFFFu) | 0x800000u);
+  const int sh = E - 150 + e;
+  const unsigned long long up = m << (sh > 0 ? sh : 0);
+  const unsigned long long dn = m >> (sh < 0 ? min(-sh, 63) : 0);
+  return (E == 0 || sh <= -24) ? 0ull : (sh >= 0 ? up : dn);
 }
-
-// A term of the selection's fixed-point sums: min(x, cap) 2^e, rounded. The
-// caps are c = 2 eps D~ for beta_i and c^2 / (2 l) for v_i: a rest holding a
-// term above its cap has eps^ >= 2 eps whether the term is capped or not, so
-// capping never changes a stopping decision, while a rest that can stop
-// holds only exact terms. The scale follows eps D~ (cap 2^e < 2^40), not the
-// largest term, so rests near the stopping point keep ~40 bits however
-// heavy the fetched tokens are; with at most 2^17 tokens no sum overflows.
 __device__ __forceinline__ unsigned long long sat_fx(float x, double cap,
                                                      int e) {
-  return (unsigned long long)__double2ull_rn(ldexp(fmin((double)x, cap), e));
+  const float cf = (float)cap;
+  return fx_bits(x < cf ? x : cf, e);
 }
 
 __device__ __forceinline__ int row_of(const DParams &p, int b, int g, int h,
