@@ -28,17 +28,25 @@ oracle computes, in float64, in the order of Algorithm 2:
 7. Fetch F_h = L_g[:k*] minus S; the output uses exact weights on H u F_h and
    lambda_i w_i / r_i on S \\ F_h (Theorem 2's estimator; reading R15), with
    the same coefficients in the numerator (reading R16).
+
+With the pages' deployed sketch (SKETCH2: 2-bit keys over 16 RoPE channel
+pairs and an exact shortlist, Appendix A.1; oracle.sketch2), step 1 plans
+with exact logits on S and on the shortlist and with the 2-bit sketch's
+logits on the rest of L.
 """
 
 import math
 
 import numpy as np
 
+from oracle import sketch2 as sk2
+
 EST_CLIP = 0
 EST_UNBIASED = 1
 EST_BINARY = 2
 W_SKETCH = 0
 W_PERFECT = 1
+W_SKETCH2 = 2
 
 
 def bernstein_consts(delta):
@@ -308,7 +316,8 @@ def combine(alpha, v_res, w_f, v_f):
 
 def decode_group(q, res_kv, res_idx, sketch, proj, r, host_kv, eps, delta,
                  estimator=EST_CLIP, weights=W_SKETCH, fetch_override=None,
-                 binary_moves=None):
+                 binary_moves=None, sketch2=None, n_short=128,
+                 shortlist_override=None):
     """KVFetch for the query heads sharing one KV head.
 
     q: [grp][d]; res_kv: [count][2][d]; res_idx: [count] ascending positions;
@@ -318,6 +327,9 @@ def decode_group(q, res_kv, res_idx, sketch, proj, r, host_kv, eps, delta,
     fetch sets F_h to use instead of the planned ones (to evaluate the
     output of another plan); ``binary_moves``: optional list (per head,
     None = the stopping test) of how many tokens binary shrinkage moves.
+    With ``weights`` == W_SKETCH2, ``sketch2`` is the 2-bit sketch of this
+    KV head (oracle.sketch2.build) and ``n_short`` the shortlist size;
+    ``shortlist_override`` replaces the selected shortlist (positions).
     Returns (list of per-head dicts, union of fetched positions).
     """
     q = np.asarray(q, dtype=np.float64)
@@ -343,11 +355,26 @@ def decode_group(q, res_kv, res_idx, sketch, proj, r, host_kv, eps, delta,
     host_kv = None if host_kv is None else np.asarray(host_kv)
     heads = []
     union = set()
+    short = np.zeros(0, dtype=np.int64)
+    if weights == W_SKETCH2:
+        s2 = [sk2.sketch_logits(q[h], sketch2) for h in range(grp)]
+        if shortlist_override is not None:
+            short = np.sort(np.asarray(shortlist_override, dtype=np.int64))
+        else:
+            short = sk2.shortlist(np.array(s2).astype(np.float32),
+                                  in_l & ~resident, n_short)
     for h in range(grp):
         qh = q[h]
         ell = key_logits(qh, kres)
         if weights == W_SKETCH:
             s_l = sketch_logits(qh, np.asarray(sketch)[lpos], proj)
+        elif weights == W_SKETCH2:
+            # exact logits on S and on the shortlist, the sketch's elsewhere
+            s_all = s2[h].copy()
+            s_all[res_idx] = ell
+            if short.size:
+                s_all[short] = key_logits(qh, host_kv[short, 0, :])
+            s_l = s_all[lpos]
         else:
             s_l = key_logits(qh, host_kv[lpos, 0, :])
         m = max(ell.max() if ell.size else -np.inf,
@@ -380,18 +407,19 @@ def decode_group(q, res_kv, res_idx, sketch, proj, r, host_kv, eps, delta,
         union.update(fetch_rows.tolist())
         d_hat, _, o = combine(alpha, vres, wf, vf)
         plan.update(m=m, dnorm=dnorm, d_hat=d_hat, o=o, fetch_rows=fetch_rows,
-                    lpos=lpos, n_s=int(in_s.sum()))
+                    lpos=lpos, n_s=int(in_s.sum()), shortlist=short)
         heads.append(plan)
     return heads, np.array(sorted(union), dtype=np.int64)
 
 
 def decode_step(q, res_kv, res_idx, sketch, proj, r, host_kv, eps, delta,
-                estimator=EST_CLIP, weights=W_SKETCH):
+                estimator=EST_CLIP, weights=W_SKETCH, sketch2=None, n_short=128):
     """All requests and KV heads of one layer.
 
     q: [B][Hq][d]; res_kv[b][g]: [count][2][d]; res_idx[b][g]: [count];
     sketch: [B][G][n][s]; proj: [G][d][s]; r: [B][G][n]; host_kv:
-    [B][G][n][2][d]. Returns (heads[b][h] dicts, unions[b][g]).
+    [B][G][n][2][d]; sketch2[b][g]: 2-bit sketches (W_SKETCH2 only).
+    Returns (heads[b][h] dicts, unions[b][g]).
     """
     B, Hq, _ = q.shape
     G = r.shape[1]
@@ -401,9 +429,13 @@ def decode_step(q, res_kv, res_idx, sketch, proj, r, host_kv, eps, delta,
     for b in range(B):
         for g in range(G):
             hs, un = decode_group(q[b, g * grp:(g + 1) * grp], res_kv[b][g],
-                                  res_idx[b][g], sketch[b, g], proj[g],
+                                  res_idx[b][g],
+                                  None if sketch is None else sketch[b, g],
+                                  None if proj is None else proj[g],
                                   r[b, g], host_kv[b, g], eps, delta,
-                                  estimator, weights)
+                                  estimator, weights,
+                                  sketch2=None if sketch2 is None else sketch2[b][g],
+                                  n_short=n_short)
             for j, hd in enumerate(hs):
                 heads[b][g * grp + j] = hd
             unions[b][g] = un

@@ -16,6 +16,7 @@ from scipy.optimize import brentq, minimize
 
 from oracle import compress as oc
 from oracle import decode as od
+from oracle import sketch2 as sk2
 
 mpmath.mp.dps = 50
 
@@ -493,3 +494,179 @@ def check_philox_kat():
         key = [int(x, 16) for x in c["key"]]
         out = philox.philox4x32_10(*ctr, *key)
         assert [int(x) for x in out] == [int(x, 16) for x in c["out"]], c
+
+
+# ---------------------------------------------------------------- 2-bit sketch
+# "Verify Before You Fetch", Appendix A.1 (Key Sketch) and section 5.1.
+
+def _levels_keys(seed, n=300, d=128, planted=None):
+    """Keys whose planted pairs (j, j + d/2) take, per 128-token group and
+    channel, exactly the four levels z + k s (k = 0..3, each present), with z
+    and s exact in fp16; every other channel is small noise. Returns
+    (keys float32 [n][d], planted pairs, z [ngroups][d], s [ngroups][d],
+    level index [n][d])."""
+    rng = np.random.default_rng(seed)
+    if planted is None:
+        planted = np.sort(rng.choice(d // 2, sk2.N_PAIRS, replace=False))
+    chan = sk2.kept_channels(planted, d)
+    keys = (0.05 * rng.standard_normal((n, d))).astype(np.float32)
+    ng = (n + sk2.GROUP - 1) // sk2.GROUP
+    z = np.zeros((ng, d), dtype=np.float32)
+    s = np.zeros((ng, d), dtype=np.float32)
+    lev = np.zeros((n, d), dtype=np.int64)
+    for gi in range(ng):
+        lo, hi = gi * sk2.GROUP, min(n, (gi + 1) * sk2.GROUP)
+        m = hi - lo
+        for c in chan:
+            zz = -float(rng.integers(8, 64)) / 8.0       # exact in fp16
+            ss = float(rng.integers(16, 64)) / 16.0      # exact in fp16
+            k = rng.integers(0, 4, m)
+            k[:4] = rng.permutation(4)                   # every level present
+            keys[lo:hi, c] = zz + k * ss
+            z[gi, c], s[gi, c] = zz, ss
+            lev[lo:hi, c] = k
+    return keys, np.asarray(planted), z, s, lev
+
+
+def check_sketch2_levels(seed, n=300):
+    """Quantisation closed form: a channel that holds exactly four equally
+    spaced levels between its group minimum and maximum is stored without
+    loss. The zero point is the minimum, the scale a third of the range, the
+    code the level index, and dequantisation returns every key bit for bit.
+    The pairs of largest energy are the planted ones."""
+    keys, planted, z, s, lev = _levels_keys(seed, n)
+    sk = sk2.build(keys)
+    assert np.array_equal(sk["pairs"], planted), (sk["pairs"], planted)
+    chan = sk["chan"]
+    assert np.array_equal(chan, np.sort(np.concatenate([planted, planted + 64])))
+    assert np.array_equal(sk["zero"], z[:, chan])
+    assert np.array_equal(sk["scale"], s[:, chan])
+    assert np.array_equal(sk["codes"], lev[:, chan])
+    assert np.array_equal(sk2.dequantize(sk), keys[:, chan])
+
+
+def check_sketch2_error(seed, n=700, d=128):
+    """Uniform 2-bit quantisation between the group's minimum and maximum:
+    codes in 0..3, and every dequantised key within half a step (plus the
+    fp16 rounding of zero and scale) of the key."""
+    rng = np.random.default_rng(seed)
+    keys = (rng.standard_normal((n, d)) * rng.uniform(0.2, 4.0, d)).astype(np.float32)
+    sk = sk2.build(keys)
+    chan = sk["chan"]
+    assert sk["codes"].max() <= 3
+    kh = sk2.dequantize(sk)
+    for gi in range(sk["zero"].shape[0]):
+        lo, hi = gi * sk2.GROUP, min(n, (gi + 1) * sk2.GROUP)
+        v = keys[lo:hi][:, chan].astype(np.float64)
+        step = (v.max(axis=0) - v.min(axis=0)) / 3.0
+        slack = 2.0 ** -10 * (np.abs(v).max(axis=0) + step) * 4
+        err = np.abs(kh[lo:hi].astype(np.float64) - v)
+        assert np.all(err <= step / 2 + slack), float((err - step / 2 - slack).max())
+        # the codes of each group's extremes
+        assert np.all(sk["codes"][lo:hi][v.argmin(axis=0), np.arange(chan.size)] == 0)
+        assert np.all(sk["codes"][lo:hi][v.argmax(axis=0), np.arange(chan.size)] == 3)
+
+
+def check_sketch2_rotation(seed, n=400, d=128):
+    """RoPE rotates the two channels of a pair together, so a pair's energy,
+    and with it the choice of pairs, does not change when every token's key
+    is rotated within each pair (j, j + d/2) by any angle. The pairs chosen
+    are the planted high-energy ones."""
+    rng = np.random.default_rng(seed)
+    planted = np.sort(rng.choice(d // 2, sk2.N_PAIRS, replace=False))
+    amp = np.ones(d // 2)
+    amp[planted] = 3.0
+    keys = rng.standard_normal((n, d))
+    keys[:, :d // 2] *= amp
+    keys[:, d // 2:] *= amp
+    ang = rng.uniform(0, 2 * np.pi, (n, d // 2))
+    a, b = keys[:, :d // 2], keys[:, d // 2:]
+    rot = np.concatenate([a * np.cos(ang) - b * np.sin(ang),
+                          a * np.sin(ang) + b * np.cos(ang)], axis=1)
+    e0 = sk2.pair_energy(keys.astype(np.float32))
+    e1 = sk2.pair_energy(rot.astype(np.float32))
+    assert np.allclose(e0, e1, rtol=1e-5)
+    assert np.array_equal(sk2.build(keys.astype(np.float32))["pairs"], planted)
+    assert np.array_equal(sk2.build(rot.astype(np.float32))["pairs"], planted)
+
+
+def check_sketch2_cost():
+    """The pages' cost figure: the sketch holds 1.76% of the full bf16 K/V
+    cache (2 bits for a quarter of the key channels, with an fp16 zero point
+    and scale per channel and 128-token group)."""
+    rng = np.random.default_rng(0)
+    for n in (32768, 131072):
+        d = 128
+        keys = np.zeros((n, d), dtype=np.float32)
+        keys[:, :] = rng.standard_normal(d).astype(np.float32)  # cheap content
+        sk = sk2.build(keys[:sk2.GROUP * 2])
+        # scale the stored sizes of a two-group build to n tokens
+        per_token = sk["codes"].shape[1] * 2 / 8
+        per_group = (sk["zero"].shape[1] + sk["scale"].shape[1]) * 2
+        total = n * per_token + (n // sk2.GROUP) * per_group
+        assert sk2.storage_bytes(sk) == 2 * sk2.GROUP * per_token + 2 * per_group
+        assert sk["codes"].shape[1] == d // 4
+        assert round(100.0 * total / (n * 2 * d * 2), 2) == 1.76
+
+
+def check_sketch2_logit_identity(seed, n=300, d=128):
+    """With keys the sketch stores without loss (four levels per group and
+    kept channel) and a query that is zero outside the kept channels, the
+    sketch logit is the exact logit <q, k> / sqrt(d) of every token."""
+    keys, planted, _, _, _ = _levels_keys(seed, n)
+    sk = sk2.build(keys)
+    rng = np.random.default_rng(seed + 7)
+    q = np.zeros(d)
+    q[sk["chan"]] = rng.standard_normal(sk["chan"].size)
+    s = sk2.sketch_logits(q, sk)
+    exact = keys.astype(np.float64) @ q / math.sqrt(d)
+    assert np.allclose(s, exact, rtol=1e-12, atol=1e-12)
+    # and a query on the other channels adds nothing
+    q2 = rng.standard_normal(d)
+    q2[sk["chan"]] = 0.0
+    assert np.all(sk2.sketch_logits(q2, sk) == 0.0)
+
+
+def check_shortlist_bruteforce(seed, n=500, grp=4):
+    """Shortlist against a plain sort of (largest score over the heads
+    descending, position ascending) over the eligible tokens, with planted
+    equal scores."""
+    rng = np.random.default_rng(seed)
+    sc = rng.standard_normal((grp, n)).astype(np.float32)
+    sc[:, 50:60] = sc[0, 40]          # ties across positions
+    elig = rng.random(n) < 0.7
+    for ns in (0, 1, 7, 128, int(elig.sum()), int(elig.sum()) + 5):
+        got = sk2.shortlist(sc, elig, ns)
+        cand = [(-max(float(sc[h, i]) for h in range(grp)), i)
+                for i in range(n) if elig[i]]
+        cand.sort()
+        want = sorted(i for _, i in cand[:max(ns, 0)])
+        assert list(got) == want, ns
+
+
+def check_sketch2_full_shortlist(seed):
+    """A shortlist that covers every non-resident token of L makes every
+    planning weight exact, so the plan, fetch set and estimate equal the
+    perfect-sketch mode's."""
+    t = tiny_layer(seed, d=128, n_h=6, n_l=120, grp=2)
+    rng = np.random.default_rng(seed + 1)
+    samp = t["l_pos"][rng.random(t["l_pos"].size) < t["r"][t["l_pos"]]]
+    res_idx = np.sort(np.concatenate([t["h_pos"], samp]))
+    res_kv = t["host_kv"][res_idx]
+    sk = sk2.build(t["K"].astype(np.float32))
+    outs = []
+    for wm, ns in ((od.W_SKETCH2, t["n"]), (od.W_PERFECT, 0)):
+        outs.append(od.decode_group(t["q"], res_kv, res_idx, None, None, t["r"],
+                                    t["host_kv"], 0.02, 0.1, od.EST_CLIP, wm,
+                                    sketch2=sk, n_short=ns))
+    (ha, ua), (hb, ub) = outs
+    assert np.array_equal(ua, ub)
+    for a, b in zip(ha, hb):
+        assert a["k_star"] == b["k_star"]
+        assert np.array_equal(a["fetch_pos"], b["fetch_pos"])
+        for k in ("m", "dnorm", "beta_star", "eps_hat0", "eps_hat", "d_hat"):
+            assert abs(a[k] - b[k]) <= 1e-12 * max(1.0, abs(b[k])), (k, a[k], b[k])
+        assert np.allclose(a["o"], b["o"], rtol=1e-12, atol=1e-12)
+    assert any(h["k_star"] > 0 for h in ha)
+    n_nonres = int(np.sum((t["r"] < 1)) - samp.size)
+    assert ha[0]["shortlist"].size == n_nonres

@@ -9,6 +9,7 @@ import pytest
 from oracle import compress as oc
 from oracle import decode as od
 from oracle import philox
+from oracle import sketch2 as sk2
 from tests import pins
 
 
@@ -70,6 +71,13 @@ def run_pins():
     attempt("estimator_enum_unbiased", lambda: pins.check_estimator_enumeration(
         17, od.EST_UNBIASED, od.W_PERFECT, n_l=6))
     attempt("philox_kat", pins.check_philox_kat)
+    attempt("sketch2_levels", lambda: pins.check_sketch2_levels(18))
+    attempt("sketch2_error", lambda: pins.check_sketch2_error(19))
+    attempt("sketch2_rotation", lambda: pins.check_sketch2_rotation(20))
+    attempt("sketch2_cost", pins.check_sketch2_cost)
+    attempt("sketch2_identity", lambda: pins.check_sketch2_logit_identity(21))
+    attempt("shortlist", lambda: pins.check_shortlist_bruteforce(22))
+    attempt("sketch2_full", lambda: pins.check_sketch2_full_shortlist(23))
     return failed
 
 
@@ -284,6 +292,65 @@ def _philox_nine_rounds(c0, c1, c2, c3, k0, k1):
     return c0, c1, c2, c3
 
 
+def _pairs_interleaved(d):
+    return np.stack([np.arange(0, d, 2), np.arange(1, d, 2)], axis=1)
+
+
+def _channels_interleaved(pairs, d):
+    pairs = np.asarray(pairs, dtype=np.int64)
+    return np.sort(np.concatenate([2 * pairs, 2 * pairs + 1]))
+
+
+def _quant_one_range(vals):
+    # one zero point and scale for the whole group
+    v = np.asarray(vals, dtype=np.float32)
+    z = np.full(v.shape[1], v.min(), dtype=np.float32)
+    s = np.full(v.shape[1], (v.max() - v.min()) / np.float32(3), dtype=np.float32)
+    z = z.astype(np.float16).astype(np.float32)
+    s = s.astype(np.float16).astype(np.float32)
+    c = np.clip(np.rint((v - z) / s), 0, 3).astype(np.uint8)
+    return z, s, c
+
+
+def _quant_floor(vals):
+    # codes truncated instead of rounded
+    v = np.asarray(vals, dtype=np.float32)
+    z, s, _ = _orig_quant(v)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        c = np.clip(np.floor((v - z) / s), 0, 3)
+    return z, s, np.where(s > 0, c, 0).astype(np.uint8)
+
+
+def _sk2_unscaled(qh, sk):
+    return _orig_sk2_logits(qh, sk) * np.sqrt(np.asarray(qh).size)
+
+
+def _sk2_channel_shift(qh, sk):
+    # query entries taken from the pair's other channel
+    qh = np.asarray(qh, dtype=np.float64)
+    d = qh.size
+    sh = np.concatenate([qh[d // 2:], qh[:d // 2]])
+    return _orig_sk2_logits(sh, sk)
+
+
+def _shortlist_min_heads(scores32, eligible, n_short):
+    s = np.asarray(scores32, dtype=np.float32)
+    return _orig_shortlist(np.broadcast_to(s.min(axis=0), s.shape), eligible, n_short)
+
+
+def _shortlist_smallest(scores32, eligible, n_short):
+    return _orig_shortlist(-np.asarray(scores32, dtype=np.float32), eligible, n_short)
+
+
+def _energy_sum_abs(keys):
+    k = np.abs(np.asarray(keys, dtype=np.float64))
+    h = k.shape[1] // 2
+    return k[:, :h].sum(axis=0) + k[:, h:].sum(axis=0) * 0.0
+
+
+_orig_quant = sk2.quantize_group
+_orig_sk2_logits = sk2.sketch_logits
+_orig_shortlist = sk2.shortlist
 _orig_wl = oc.water_level
 _orig_rates = oc.rates
 _orig_sketch = od.sketch_logits
@@ -326,6 +393,22 @@ MUTATIONS = [
     ("Philox Weyl constant W0 off by one", philox, "W0", 0x9E3779B8),
     ("Philox multiplier M1 wrong", philox, "M1", np.uint64(0xCD9E8D55)),
     ("Philox with nine rounds", philox, "philox4x32_10", _philox_nine_rounds),
+    ("RoPE pairs taken as (2j, 2j+1)", sk2, "rope_pairs", _pairs_interleaved),
+    ("kept channels taken as (2j, 2j+1)", sk2, "kept_channels",
+     _channels_interleaved),
+    ("2-bit scale a quarter of the range", sk2, "LEVELS", 4),
+    ("one zero point and scale per group", sk2, "quantize_group", _quant_one_range),
+    ("2-bit codes truncated", sk2, "quantize_group", _quant_floor),
+    ("8 kept pairs instead of 16", sk2, "N_PAIRS", 8),
+    ("groups of 64 tokens", sk2, "GROUP", 64),
+    ("sketch2 logits not scaled", sk2, "sketch_logits", _sk2_unscaled),
+    ("sketch2 query channels of the other half", sk2, "sketch_logits",
+     _sk2_channel_shift),
+    ("shortlist by the smallest score over the heads", sk2, "shortlist",
+     _shortlist_min_heads),
+    ("shortlist of the lowest scores", sk2, "shortlist", _shortlist_smallest),
+    ("pair energy from one channel of the pair", sk2, "pair_energy",
+     _energy_sum_abs),
 ]
 
 
