@@ -59,10 +59,38 @@ def parse():
                     help="other decode workloads measured after the headline "
                          "one, each reported as its own block (default: c3, "
                          "batch 16 with fetching active); none with --also")
+    ap.add_argument("--sketch2", nargs="*", default=["c2", "c3"],
+                    choices=["c2", "c3", "c4"],
+                    help="workloads measured again planning with the pages' "
+                         "2-bit sketch and a 128-token exact shortlist "
+                         "(blocks '<config>_sketch2'); none with --sketch2")
     return ap.parse_args()
 
 
 ESTIMATORS = {"clip": 0, "unbiased": 1, "binary": 2}
+
+
+def algorithmic_bytes_sketch2(w, counts, fetching_rows, est="clip"):
+    """The same with the 2-bit sketch: the scan reads 8 bytes of codes, one
+    byte of zero points and scales (128 bytes per 128-token group) and r per
+    (request, KV head, token), with the resident K rows, positions and q.
+    Intermediates: the fp32 sketch logit of every (query head, token) and
+    the shortlist key of every (KV head, token). The pass-0 launch reads the
+    planning logits once and r once per KV head (5 B per q-head x token at 4
+    query heads per KV head), like the estimator phases."""
+    B, Hq, G, n, d = w["B"], w["Hq"], w["G"], w["n"], w["d"]
+    grp = Hq // G
+    rows = int(counts.sum())
+    tok = B * Hq * n * 4 + B * G * n * 4
+    ftok = fetching_rows * n * 4 + min(fetching_rows, B * G) * n * 4
+    sk = B * G * n * (8 + 1 + 4)
+    per = {"scan": sk + rows * (2 * d + 4) + B * Hq * d * 2,
+           "pass0": tok, "beta1": tok, "cert": tok, "cand": ftok}
+    inter = {"scan": B * Hq * n * 4 + B * G * n * 4 + rows * grp * 4}
+    if est == "binary":
+        per["shrink"] = 2 * tok
+    return dict(step=sk + rows * (4 * d + 4) + B * Hq * d * (2 + 4),
+                kernels=per, intermediate=inter)
 
 
 def algorithmic_bytes(w, counts, fetching_rows, est="clip"):
@@ -292,9 +320,10 @@ WORKLOADS = {"c2": "Qwen3-4B-shaped decode layer, 32K context",
              "c4": "Ministral-8B-shaped decode layer, 128K context"}
 
 
-def measure(config, args, dev, headline):
-    """Compress one workload's cache with the library, then time decode
-    steps on it. Returns (the measurement dict, the workload, the step)."""
+def measure(config, args, dev, headline, weights=0):
+    """Compress one workload's cache with the library (and with the 2-bit
+    sketch, build the sketch), then time decode steps on it. Returns (the
+    measurement dict, the workload)."""
     import numpy as np
     import torch
 
@@ -302,7 +331,9 @@ def measure(config, args, dev, headline):
     from workloads import (bf16_bits, c3_shift_queries, make_decode_workload,
                            resident_cap)
 
-    w = make_decode_workload(config, seed=args.seed, with_queries=False)
+    sk2 = weights == vk.W_SKETCH2
+    w = make_decode_workload(config, seed=args.seed, with_queries=False,
+                             pair_profile=sk2)
     B, Hq, G, n, s, d = w["B"], w["Hq"], w["G"], w["n"], w["s"], w["d"]
 
     # ---- PoissonComp by the library (prefill time, untimed)
@@ -316,6 +347,14 @@ def measure(config, args, dev, headline):
                        w["seed"], cap)
     rc, bits = vk.vkv_check_status(vk._ptr(comp["status"]), vk._stream(None))
     assert rc == 0, (rc, bits)
+    sketch2, build_ms = None, None
+    if sk2:  # the 2-bit sketch, built at prefill time (untimed in the step)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        sketch2 = vk.sketch2_build(t_k)
+        e1.record()
+        torch.cuda.synchronize()
+        build_ms = e0.elapsed_time(e1)
     del t_k, t_v
     counts = comp["resident_count"].cpu().numpy()
 
@@ -338,10 +377,11 @@ def measure(config, args, dev, headline):
     proj = torch.from_numpy(w["proj"]).to(dev)
     host_kv = torch.from_numpy(w["host_kv"].view(np.int16)).pin_memory()
 
-    step = vk.DecodeStep(B, Hq, G, n, s, cap, n, dev)
+    step = vk.DecodeStep(B, Hq, G, n, s, cap, n, dev, n_short=128)
     step.bind(t_qs[0], comp["resident_kv"], comp["resident_idx"],
               comp["resident_count"], sketch, proj, comp["r"], host_kv,
-              w["eps"], w["delta"], ESTIMATORS[args.estimator])
+              w["eps"], w["delta"], ESTIMATORS[args.estimator], weights,
+              sketch2)
     names = vk.decode_phase_names()
     P = len(names)
 
@@ -372,7 +412,8 @@ def measure(config, args, dev, headline):
     ph_us = ph * 1e3 / nprof
     out = step.out
     ks = out["k_star"].cpu().numpy()
-    ab = algorithmic_bytes(w, counts, int(np.sum(ks > 0)), args.estimator)
+    ab = (algorithmic_bytes_sketch2 if sk2 else algorithmic_bytes)(
+        w, counts, int(np.sum(ks > 0)), args.estimator)
     cand = ab["kernels"]
     # the roofline object covers the longest-running HBM-bound kernel
     dom = max(cand, key=lambda k: ph_us[names.index(k)])
@@ -428,7 +469,10 @@ def measure(config, args, dev, headline):
             "batch": B, "q_heads": Hq, "kv_heads": G, "head_dim": d,
             "ctx_tokens": n, "budget": w["budget"], "sketch_dim": s,
             "n_sink": w["n_sink"], "n_local": w["n_local"], "eps": w["eps"],
-            "delta": w["delta"], "estimator": args.estimator},
+            "delta": w["delta"], "estimator": args.estimator,
+            "planning": ("2-bit RoPE-pair sketch + 128-token exact shortlist "
+                         "(keys with uneven pair energy)") if sk2 else
+                        "projected bf16 sketch"},
         "step_compulsory_bytes": int(ab["step"]),
         "hbm_peak_pct": 100.0 * ab["step"] / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "fetch_pct": fetch_pct,
@@ -446,9 +490,14 @@ def measure(config, args, dev, headline):
                      "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(config, dom, args.estimator),
+                     "traffic": None if sk2 else measured_traffic(
+                         config, dom, args.estimator),
                      "algorithmic_bytes": cand[dom]},
     }
+    if sk2:
+        res["sketch_build_ms"] = build_ms
+        res["sketch_bytes"] = int(B * G * (n * 8 + (n + 127) // 128 * 128))
+        del res["config"]["sketch_dim"]
     res["_t_qs"], res["_host_kv"] = t_qs, host_kv
     return res, w
 
@@ -496,6 +545,13 @@ def main():
         e.pop("_t_qs")
         e.pop("_host_kv")
         res[extra] = e
+        torch.cuda.empty_cache()
+    for extra in args.sketch2:
+        from verified_sparse_kv_amd import verkv as vk
+        e, _ = measure(extra, args, dev, False, weights=vk.W_SKETCH2)
+        e.pop("_t_qs")
+        e.pop("_host_kv")
+        res[extra + "_sketch2"] = e
         torch.cuda.empty_cache()
     if not args.no_compress:
         res["compress_c5"] = compress_pass(dev, args.steps)

@@ -77,10 +77,16 @@ enum {
  * to lambda = r while that value exceeds twice the bias w~ (1 - r) of the
  * tokens set before them. */
 enum { VKV_EST_CLIP = 0, VKV_EST_UNBIASED = 1, VKV_EST_BINARY = 2 };
-/* Planning weights on L: from the key sketch (what a deployment does), or
- * the exact weights (the "perfect sketch" of section 4.2; reads every key of
- * L from host memory, so it is a slow test mode). */
-enum { VKV_W_SKETCH = 0, VKV_W_PERFECT = 1 };
+/* Planning weights on L: from the projected key sketch (sketch, proj); the
+ * exact weights (the "perfect sketch" of section 4.2; reads every key of L
+ * from host memory, so it is a slow test mode); or the pages' deployed
+ * sketch ("Verify Before You Fetch", Appendix A.1 and section 5.1): 2-bit
+ * keys over 16 RoPE channel pairs (vkv_sketch2_build) and an exact
+ * shortlist of the n_short non-resident tokens with the largest sketch
+ * logit over the KV head's query heads, whose keys are read from host
+ * memory; the plan then uses exact weights on S and the shortlist and the
+ * sketch's weights on the rest of L. */
+enum { VKV_W_SKETCH = 0, VKV_W_PERFECT = 1, VKV_W_SKETCH2 = 2 };
 
 /*
  * PoissonComp over n_layers x n_kv_heads independent slices of n_tokens.
@@ -146,6 +152,11 @@ typedef struct {
  * r            dev [B][G][n] f32 inclusion probabilities, H <=> r == 1.
  * host_kv      host [B][G][n][2][d] bf16 full cache in pinned memory
  *              (hipHostMalloc); rows chosen for fetching are read from it.
+ * sk2_codes, sk2_zs, sk2_chan  the 2-bit sketch of every (request, KV
+ *              head), as vkv_sketch2_build writes it (VKV_W_SKETCH2 only;
+ *              otherwise ignored and may be NULL).
+ * n_short      shortlist size per (request, KV head), 0..1024 (the pages
+ *              use 128); VKV_W_SKETCH2 only.
  * eps, delta   tolerance (eps > 0, 0 < delta < 1) of the (eps, delta)
  *              guarantee on the attention denominator.
  * estimator    VKV_EST_CLIP, VKV_EST_UNBIASED or VKV_EST_BINARY; weights
@@ -162,7 +173,11 @@ typedef struct {
  * host_kv this step; row_stats (may be NULL) [B][Hq][8] f64 =
  * {m, D~ (scaled by exp(-m)), beta*, beta(L), V(L), b(L), eps^(L), eps^(L')}
  * (with VKV_EST_BINARY, beta* is the bias of the tokens set to lambda = r);
- * row_path (may be NULL) [B][Hq] i32, how k* was decided (VKV_PATH_*).
+ * row_path (may be NULL) [B][Hq] i32, how k* was decided (VKV_PATH_*);
+ * shortlist (may be NULL; VKV_W_SKETCH2 only) [B][G][n_short] i32, the
+ * shortlisted positions ascending, -1 after the last (fewer when fewer
+ * tokens are eligible). With VKV_W_SKETCH2, host_bytes also counts the
+ * 2 d bytes of each shortlisted key.
  * status   dev u32 [1], cleared at the start of the call.
  * phase_events  optional timing hook: NULL, or vkv_decode_phase_count() + 1
  *          hipEvent_t handles (created by the caller); event 0 is recorded on
@@ -184,6 +199,10 @@ typedef struct {
   const float *proj;
   const float *r;
   const uint16_t *host_kv;
+  const uint64_t *sk2_codes;
+  const uint16_t *sk2_zs;
+  const int32_t *sk2_chan;
+  int32_t n_short;
   float eps, delta;
   int32_t estimator, weights, fetch_cap;
   float *out;
@@ -197,6 +216,7 @@ typedef struct {
   uint64_t *host_bytes;
   double *row_stats;
   int32_t *row_path;
+  int32_t *shortlist;
   uint32_t *status;
   void **phase_events;
   void *workspace;
@@ -229,10 +249,52 @@ typedef struct {
   size_t workspace_bytes;
 } vkv_dense_args;
 
+/*
+ * The pages' 2-bit key sketch ("Verify Before You Fetch", Appendix A.1 and
+ * section 5.1), built from the prefill keys of n_slices independent slices
+ * (layers x KV heads, or requests x KV heads) of n_tokens each.
+ *
+ * Per slice: the 16 RoPE channel pairs (j, j + d/2) with the largest key
+ * energy, the sum over tokens of k_j^2 + k_{j+d/2}^2 (ties: lower j), give
+ * the 32 kept channels, listed in increasing channel index in chan. Each
+ * kept channel is quantised per group of 128 tokens (the last group may be
+ * shorter) between the group's minimum and maximum: zero z = fp16(min),
+ * scale s = fp16(fp32(max - min) / 3), both saturated at +-65504, and code
+ * clamp(rint(fp32(fp32(k - z) / s)), 0, 3) (0 when s == 0). The dequantised
+ * key is z + code * s. Bits 2c and 2c + 1 of a token's 64-bit code word
+ * hold the code of kept channel c. Stored size: 8 bytes per token and
+ * 128 bytes per group, 1.76% of the bf16 K/V cache.
+ *
+ * k         dev bf16 keys; token t of slice i at k + i * slice_stride +
+ *           t * key_stride (elements; key_stride >= head_dim, so K rows
+ *           interleaved with V rows can be passed as they are).
+ * codes     out dev [n_slices][n_tokens] u64.
+ * zs        out dev [n_slices][ceil(n_tokens / 128)][2][32] fp16 bits: the
+ *           group's 32 zero points, then its 32 scales.
+ * chan      out dev [n_slices][32] i32.
+ * Supported: head_dim = 128, 1 <= n_tokens <= 2^24, n_slices <= 65535.
+ * The pair choice sums squares in float64; pairs whose energies agree to
+ * rounding may be chosen either way.
+ */
+typedef struct {
+  int32_t n_slices, n_tokens, head_dim;
+  int64_t key_stride, slice_stride;
+  const uint16_t *k;
+  uint64_t *codes;
+  uint16_t *zs;
+  int32_t *chan;
+  void *workspace;
+  size_t workspace_bytes;
+} vkv_sketch2_args;
+
 /* Workspace sizes in bytes for these arguments (0 if the shapes are invalid). */
 size_t vkv_compress_workspace_bytes(const vkv_compress_args *a);
 size_t vkv_decode_workspace_bytes(const vkv_decode_args *a);
 size_t vkv_dense_workspace_bytes(const vkv_dense_args *a);
+size_t vkv_sketch2_workspace_bytes(const vkv_sketch2_args *a);
+
+/* Enqueue the 2-bit sketch build (see vkv_sketch2_args). */
+vkv_status vkv_sketch2_build(const vkv_sketch2_args *a, void *stream);
 
 /* Enqueue one PoissonComp pass (see vkv_compress_args). */
 vkv_status vkv_compress(const vkv_compress_args *a, void *stream);

@@ -10,6 +10,12 @@ compare them by the parity rules:
   decisions differ (the stopping test is a near tie: at the library's k* if
   it stops first, else at its k* - 1) or every token between the two cut
   points has a gain within 1e-5 relative of the gain at k*;
+* 2-bit sketch: the kept channels, zero points, scales and codes bit for
+  bit (pairs whose float64 energies agree to 1e-9 may be chosen either
+  way; the oracle then takes the library's); the shortlist exactly, except
+  for tokens whose sketch score is within 1e-5 of the score magnitude of
+  the oracle's last shortlisted one (fp32 against float64 scores), where the
+  oracle is run again with the library's shortlist;
 * numeric: eps^(L), eps^(L') and D^ within 1e-4 relative and the output
   within 1e-3 relative L2 (the stated tolerances); beta* within 1e-5
   relative of the oracle. That last bound is derived from the arithmetic:
@@ -27,6 +33,7 @@ import numpy as np
 
 from oracle import compress as oc
 from oracle import decode as od
+from oracle import sketch2 as sk2
 from workloads import bf16_to_f32, c3_shift_queries, make_decode_workload
 
 TOL_BETA = 1e-5
@@ -104,29 +111,111 @@ def device_inputs(w):
         host_kv=torch.from_numpy(w["host_kv"].view(np.int16)).pin_memory())
 
 
-def run_library(w, dev, eps, delta, est=0, weights=0, fetch_cap=None):
+def library_sketch2(w, dev):
+    """The library's 2-bit sketch of every (request, KV head), built from a
+    device copy of the cache (K rows interleaved with V rows)."""
+    from verified_sparse_kv_amd import verkv as vk
+    torch = torch_mod()
+    B, G, n, d = w["B"], w["G"], w["n"], w["d"]
+    if "sk2" not in dev:
+        kv = dev["host_kv"].to("cuda").view(B, G, n, 2 * d)
+        dev["sk2"] = vk.sketch2_build(kv)
+        torch.cuda.synchronize()
+    return dev["sk2"]
+
+
+def run_library(w, dev, eps, delta, est=0, weights=0, fetch_cap=None,
+                n_short=128):
     from verified_sparse_kv_amd import verkv as vk
     torch = torch_mod()
     step = vk.DecodeStep(w["B"], w["Hq"], w["G"], w["n"], w["s"], w["cap"],
-                         fetch_cap or w["n"], torch.device("cuda"))
+                         fetch_cap or w["n"], torch.device("cuda"),
+                         n_short=n_short)
+    skt = library_sketch2(w, dev) if weights == od.W_SKETCH2 else None
     step.bind(dev["q"], dev["resident_kv"], dev["resident_idx"],
               dev["resident_count"], dev["sketch"], dev["proj"], dev["r"],
-              dev["host_kv"], eps, delta, est, weights)
+              dev["host_kv"], eps, delta, est, weights, skt)
     out = step.launch()
     rc, bits = step.check_status()
     res = {k: v.cpu().numpy() for k, v in out.items()}
     res["rc"] = rc
     res["bits"] = bits
+    res["n_short"] = n_short
+    if skt is not None:
+        res["sk2"] = {k: v.cpu().numpy() for k, v in skt.items() if k != "_ws"}
     return res
 
 
-def run_oracle(w, eps, delta, est=0, weights=0):
+PAIR_TIE = 1e-9
+
+
+def oracle_sketch2(w, b, g, lib_chan=None):
+    """The oracle's sketch of (b, g). If the library kept other pairs and
+    every pair in the difference has an energy within 1e-9 relative of the
+    oracle's 16th largest, both choices are correct and the oracle takes
+    the library's. Returns (sketch, 'tie' | 'same' | 'differs')."""
+    keys = bf16_to_f32(w["host_kv"][b, g, :, 0, :])
+    sk = sk2.build(keys)
+    if lib_chan is None:
+        return sk, "same"
+    lp = np.sort(np.asarray(lib_chan)[:sk2.N_PAIRS].astype(np.int64))
+    if np.array_equal(lp, sk["pairs"]):
+        return sk, "same"
+    e = sk["energy"]
+    e16 = np.sort(e)[::-1][sk2.N_PAIRS - 1]
+    diff = np.setxor1d(lp, sk["pairs"])
+    if np.all(np.abs(e[diff] - e16) <= PAIR_TIE * e16):
+        return sk2.with_pairs(keys, lp), "tie"
+    return sk, "differs"
+
+
+def oracle_sketches(w, gpu=None):
+    """Oracle sketches of every (b, g) (kept in w for re-runs)."""
+    B, G = w["B"], w["G"]
+    out, states = [], []
+    for b in range(B):
+        row = []
+        for g in range(G):
+            lib = None if gpu is None else gpu["sk2"]["chan"][b, g]
+            sk, st = oracle_sketch2(w, b, g, lib)
+            row.append(sk)
+            states.append(st)
+        out.append(row)
+    w["sk2_oracle"] = out
+    return out, states
+
+
+def run_oracle(w, eps, delta, est=0, weights=0, n_short=128, gpu=None):
     B, G = w["B"], w["G"]
     res_kv = [[w["cm"][b][g]["resident_kv"] for g in range(G)] for b in range(B)]
     res_idx = [[w["cm"][b][g]["resident_idx"] for g in range(G)] for b in range(B)]
+    skt = None
+    if weights == od.W_SKETCH2:
+        skt, _ = oracle_sketches(w, gpu)
+    w["n_short"] = n_short
     return od.decode_step(bf16_to_f32(w["q"]), res_kv, res_idx,
                           bf16_to_f32(w["sketch"]), w["proj"], w["r_all"],
-                          bf16_to_f32(w["host_kv"]), eps, delta, est, weights)
+                          bf16_to_f32(w["host_kv"]), eps, delta, est, weights,
+                          sketch2=skt, n_short=n_short)
+
+
+def shortlist_tie(w, b, g, lib, orc):
+    """The library's shortlist differs from the oracle's: a tie when both
+    have the same size and every token in the difference has an oracle score
+    (largest float64 sketch logit over the group's heads) within 1e-5 of
+    its score magnitude (sum of |q_c k^_c| / sqrt(d)) from the score of the
+    oracle's last shortlisted token."""
+    if lib.size != orc.size:
+        return False
+    grp = w["Hq"] // w["G"]
+    sk = w["sk2_oracle"][b][g]
+    qs = bf16_to_f32(w["q"][b, g * grp:(g + 1) * grp]).astype(np.float64)
+    sc = np.max([sk2.sketch_logits(q, sk) for q in qs], axis=0)
+    kh = np.abs(sk2.dequantize(sk).astype(np.float64))
+    mag = np.max([kh @ np.abs(q[sk["chan"]]) for q in qs], axis=0) / math.sqrt(w["d"])
+    t = sc[orc].min()
+    diff = np.setxor1d(lib, orc)
+    return bool(np.all(np.abs(sc[diff] - t) <= 1e-5 * np.maximum(mag[diff], 1e-30)))
 
 
 def _rel(a, b):
@@ -182,17 +271,20 @@ def kstar_tie(hd, kg, eps):
 
 
 def rerun_group(w, b, g, eps, est, weights, binary_moves=None,
-                fetch_override=None):
+                fetch_override=None, shortlist_override=None):
     """The oracle for one (request, KV head) under the given overrides."""
     grp = w["Hq"] // w["G"]
     sl = w["cm"][b][g]
+    skt = w["sk2_oracle"][b][g] if weights == od.W_SKETCH2 else None
     return od.decode_group(bf16_to_f32(w["q"][b, g * grp:(g + 1) * grp]),
                            sl["resident_kv"], sl["resident_idx"],
                            bf16_to_f32(w["sketch"][b, g]), w["proj"][g],
                            w["r_all"][b, g], bf16_to_f32(w["host_kv"][b, g]),
                            eps, w["delta"], est, weights,
                            fetch_override=fetch_override,
-                           binary_moves=binary_moves)
+                           binary_moves=binary_moves, sketch2=skt,
+                           n_short=w.get("n_short", 128),
+                           shortlist_override=shortlist_override)
 
 
 def compare(w, gpu, heads, unions, eps, est=0, weights=0, max_tie_frac=0.01):
@@ -220,10 +312,32 @@ def compare(w, gpu, heads, unions, eps, est=0, weights=0, max_tie_frac=0.01):
             bad.append(f"{name} {where}: {err:.3e} > {tol:.0e}")
 
     fetched = 0
+    short_keys = 0
+    short_ties = []
     for b in range(B):
         for g in range(G):
             hs = [heads[b][g * grp + j] for j in range(grp)]
             union = unions[b][g]
+            sl_over = None
+            if weights == od.W_SKETCH2:
+                lib = gpu["shortlist"][b, g][:gpu["n_short"]]
+                if np.any(lib[np.cumsum(lib < 0) > 0] >= 0):
+                    bad.append(f"shortlist (b={b},g={g}): -1 before a position")
+                lib = lib[lib >= 0].astype(np.int64)
+                short_keys += lib.size
+                orc = hs[0]["shortlist"]
+                if not np.all(np.diff(lib) > 0):
+                    bad.append(f"shortlist (b={b},g={g}) not ascending")
+                if not np.array_equal(lib, orc):
+                    if shortlist_tie(w, b, g, lib, orc):
+                        sl_over = lib
+                        short_ties.append((b, g))
+                        hs, union = rerun_group(w, b, g, eps, est, weights,
+                                                shortlist_override=sl_over)
+                    else:
+                        bad.append(f"shortlist (b={b},g={g}): library "
+                                   f"{lib.size} oracle {orc.size}, sym diff "
+                                   f"{np.setxor1d(lib, orc).size} (not a tie)")
             # binary shrinkage: beta (the moved tokens' bias) and ties of
             # the move count
             moves = [None] * grp
@@ -250,7 +364,8 @@ def compare(w, gpu, heads, unions, eps, est=0, weights=0, max_tie_frac=0.01):
                             tie_rows.append((b, h, "binary"))
             if any(m is not None for m in moves):
                 hs, union = rerun_group(w, b, g, eps, est, weights,
-                                        binary_moves=moves)
+                                        binary_moves=moves,
+                                        shortlist_override=sl_over)
             # k*: exact, or a tie scored under the library's k*
             over = [None] * grp
             open_tokens = []
@@ -273,7 +388,8 @@ def compare(w, gpu, heads, unions, eps, est=0, weights=0, max_tie_frac=0.01):
                         if over[j] is not None else None for j in range(grp)]
                 hs, union = rerun_group(w, b, g, eps, est, weights,
                                         binary_moves=moves,
-                                        fetch_override=over)
+                                        fetch_override=over,
+                                        shortlist_override=sl_over)
             for j in range(grp):
                 h = g * grp + j
                 hd, where = hs[j], f"(b={b},h={h})"
@@ -305,11 +421,14 @@ def compare(w, gpu, heads, unions, eps, est=0, weights=0, max_tie_frac=0.01):
     ties = len(tie_rows)
     if ties > int(max_tie_frac * n_rows):
         bad.append(f"{ties} tie-accepted rows of {n_rows}: {tie_rows}")
-    if int(gpu["host_bytes"][0]) != fetched * 512:
-        bad.append(f"host_bytes {int(gpu['host_bytes'][0])} != {fetched * 512}")
+    want_bytes = fetched * 512 + short_keys * 256
+    if int(gpu["host_bytes"][0]) != want_bytes:
+        bad.append(f"host_bytes {int(gpu['host_bytes'][0])} != {want_bytes}")
     summary = dict(ties=ties, tie_rows=tie_rows, rows=n_rows, fetched=fetched,
                    worst=worst, fetch_frac=fetched / (B * G * w["n"]),
                    kstar_mean=float(np.mean(gpu["k_star"])))
+    if weights == od.W_SKETCH2:
+        summary.update(short_keys=short_keys, short_ties=short_ties)
     if "row_path" in gpu:
         summary["paths"] = np.bincount(gpu["row_path"].ravel(),
                                        minlength=4).tolist()

@@ -53,7 +53,8 @@ def _c_layout(struct, fields):
 
 @pytest.mark.parametrize("cls,cname", [(vk.CompressArgs, "vkv_compress_args"),
                                        (vk.DecodeArgs, "vkv_decode_args"),
-                                       (vk.DenseArgs, "vkv_dense_args")])
+                                       (vk.DenseArgs, "vkv_dense_args"),
+                                       (vk.Sketch2Args, "vkv_sketch2_args")])
 def test_struct_layout_matches_c(cls, cname):
     fields = [f for f, _ in cls._fields_]
     size, offs = _c_layout(cname, fields)
@@ -146,6 +147,16 @@ def test_compress_validation(kw, code, frag):
     (dict(sketch=None), vk.VKV_EINVAL, "sketch"),
     (dict(k_star=None), vk.VKV_EINVAL, "output"),
     (dict(host_kv=None), vk.VKV_EINVAL, "required"),
+    (dict(weights=2), vk.VKV_EINVAL, "sk2_codes"),
+    (dict(weights=2, sk2_codes=ctypes.c_void_p(0x1000), sk2_zs=ctypes.c_void_p(0x1000),
+          sk2_chan=ctypes.c_void_p(0x1000), n_short=1025), vk.VKV_EINVAL, "n_short"),
+    (dict(weights=2, sk2_codes=ctypes.c_void_p(0x1000), sk2_zs=ctypes.c_void_p(0x1000),
+          sk2_chan=ctypes.c_void_p(0x1000), n_short=-1), vk.VKV_EINVAL, "n_short"),
+    # the projected sketch is neither needed nor checked with the 2-bit one:
+    # validation passes and the pinned-memory check of host_kv is next
+    (dict(weights=2, sketch=None, proj=None, sketch_dim=0,
+          sk2_codes=ctypes.c_void_p(0x1000), sk2_zs=ctypes.c_void_p(0x1000),
+          sk2_chan=ctypes.c_void_p(0x1000), n_short=128), vk.VKV_ENOTPINNED, "host_kv"),
 ])
 def test_decode_validation(kw, code, frag):
     a = _decode_args(**kw)
@@ -236,3 +247,44 @@ def test_noalloc_validation_before_any_launch():
     a.workspace, a.workspace_bytes = ctypes.c_void_p(0x1000), 1 << 20
     assert vk.vkv_decode_step_noalloc(a, None) == vk.VKV_EINVAL
     assert "NULL" in vk.vkv_last_error()
+
+
+def _sketch2_args(**kw):
+    a = vk.Sketch2Args(n_slices=4, n_tokens=1000, head_dim=128, key_stride=256,
+                       slice_stride=256000)
+    fake = ctypes.c_void_p(0x1000)
+    for f in ("k", "codes", "zs", "chan"):
+        setattr(a, f, fake)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_sketch2_workspace_sizes():
+    w = vk.vkv_sketch2_workspace_bytes(_sketch2_args())
+    assert w > 0 and w % 256 == 0
+    assert vk.vkv_sketch2_workspace_bytes(_sketch2_args(n_tokens=100000)) > w
+    assert vk.vkv_sketch2_workspace_bytes(_sketch2_args(head_dim=64)) == 0
+    assert vk.vkv_sketch2_workspace_bytes(_sketch2_args(key_stride=100)) == 0
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(n_slices=0), "n_slices"),
+    (dict(n_tokens=0), "n_tokens"),
+    (dict(n_tokens=(1 << 24) + 1), "n_tokens"),
+    (dict(head_dim=96), "head_dim"),
+    (dict(key_stride=64), "key_stride"),
+    (dict(key_stride=260), "key_stride"),
+    (dict(slice_stride=4), "slice_stride"),
+    (dict(codes=None), "required"),
+    (dict(k=ctypes.c_void_p(0x1008)), "aligned"),
+    (dict(workspace=None), "workspace"),
+])
+def test_sketch2_validation(kw, frag):
+    a = _sketch2_args(**kw)
+    if "workspace" not in kw:
+        a.workspace = ctypes.c_void_p(0x1000)
+        a.workspace_bytes = 1
+    assert vk.vkv_sketch2_build(a, None) == vk.VKV_EINVAL
+    msg = vk.vkv_last_error()
+    assert frag in msg, msg

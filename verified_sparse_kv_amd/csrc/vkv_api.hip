@@ -86,7 +86,7 @@ vkv_status check_decode_shapes(const vkv_decode_args *a) {
           "decode: n_tokens must be in [1, 2^24)");
   if (a->n_tokens > (1 << 17))
     return fail(VKV_EUNSUPPORTED, "decode: n_tokens %d (supported: up to 2^17)", a->n_tokens);
-  if (!(a->sketch_dim == 16 || a->sketch_dim == 32))
+  if (a->weights == VKV_W_SKETCH && !(a->sketch_dim == 16 || a->sketch_dim == 32))
     return fail(VKV_EUNSUPPORTED, "decode: sketch_dim %d (supported: 16, 32)", a->sketch_dim);
   REQUIRE(a->cap >= 1, "decode: cap must be >= 1");
   REQUIRE(a->fetch_cap >= 1 && a->fetch_cap <= a->n_tokens,
@@ -136,16 +136,33 @@ vkv_status check_decode_args(const vkv_decode_args *a) {
   REQUIRE(a->estimator == VKV_EST_CLIP || a->estimator == VKV_EST_UNBIASED ||
               a->estimator == VKV_EST_BINARY,
           "decode: unknown estimator %d", a->estimator);
-  REQUIRE(a->weights == VKV_W_SKETCH || a->weights == VKV_W_PERFECT,
+  REQUIRE(a->weights == VKV_W_SKETCH || a->weights == VKV_W_PERFECT ||
+              a->weights == VKV_W_SKETCH2,
           "decode: unknown weights mode %d", a->weights);
   REQUIRE(a->q && a->resident_kv && a->resident_idx && a->resident_count && a->r &&
               a->host_kv,
           "decode: q, resident_kv, resident_idx, resident_count, r and host_kv are required");
-  REQUIRE(a->weights == VKV_W_PERFECT || (a->sketch && a->proj),
+  REQUIRE(a->weights != VKV_W_SKETCH || (a->sketch && a->proj),
           "decode: sketch and proj are required in sketch mode");
+  REQUIRE(a->weights != VKV_W_SKETCH2 || (a->sk2_codes && a->sk2_zs && a->sk2_chan),
+          "decode: sk2_codes, sk2_zs and sk2_chan are required with the 2-bit sketch");
+  REQUIRE(a->weights != VKV_W_SKETCH2 || (a->n_short >= 0 && a->n_short <= 1024),
+          "decode: n_short must be in [0, 1024]");
   REQUIRE(a->out && a->d_hat && a->log_shift && a->eps_hat0 && a->eps_hat &&
               a->k_star && a->fetch_idx && a->fetch_count && a->host_bytes && a->status,
           "decode: every output pointer except row_stats and row_path is required");
+  return VKV_OK;
+}
+
+vkv_status check_sketch2_args(const vkv_sketch2_args *a) {
+  REQUIRE(a != nullptr, "sketch2: args is NULL");
+  REQUIRE(a->n_slices >= 1 && a->n_slices <= 65535, "sketch2: n_slices must be in [1, 65535]");
+  REQUIRE(a->n_tokens >= 1 && a->n_tokens <= (1 << 24), "sketch2: n_tokens must be in [1, 2^24]");
+  REQUIRE(a->head_dim == vkv::kHeadDim, "sketch2: head_dim must be 128");
+  REQUIRE(a->key_stride >= a->head_dim && a->key_stride % 8 == 0,
+          "sketch2: key_stride must be >= head_dim and a multiple of 8");
+  REQUIRE(a->slice_stride >= 0 && a->slice_stride % 8 == 0,
+          "sketch2: slice_stride must be >= 0 and a multiple of 8");
   return VKV_OK;
 }
 
@@ -190,6 +207,24 @@ size_t vkv_compress_workspace_bytes(const vkv_compress_args *a) {
 size_t vkv_decode_workspace_bytes(const vkv_decode_args *a) {
   if (check_decode_shapes(a) != VKV_OK) return 0;
   return vkv::decode_layout(*a).total;
+}
+
+size_t vkv_sketch2_workspace_bytes(const vkv_sketch2_args *a) {
+  if (check_sketch2_args(a) != VKV_OK) return 0;
+  return vkv::sketch2_layout(*a).total;
+}
+
+vkv_status vkv_sketch2_build(const vkv_sketch2_args *a, void *stream) {
+  vkv_status st = check_sketch2_args(a);
+  if (st != VKV_OK) return st;
+  REQUIRE(a->k && a->codes && a->zs && a->chan, "sketch2: k, codes, zs and chan are required");
+  REQUIRE(((uintptr_t)a->k & 15u) == 0, "sketch2: k must be 16-byte aligned");
+  const vkv::Sketch2Layout L = vkv::sketch2_layout(*a);
+  REQUIRE(a->workspace != nullptr && a->workspace_bytes >= L.total,
+          "sketch2: workspace of %zu bytes needed", L.total);
+  const hipError_t e = vkv::launch_sketch2(*a, L, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "sketch2 launch");
+  return VKV_OK;
 }
 
 size_t vkv_dense_workspace_bytes(const vkv_dense_args *a) {

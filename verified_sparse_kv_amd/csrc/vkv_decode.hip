@@ -105,6 +105,15 @@ struct CertPart {
 
 struct DParams {
   const uint16_t *q, *rkv, *sketch, *host_kv;
+  // 2-bit sketch (Appendix A.1): codes [B][G][n], zero points and scales
+  // [B][G][ceil(n/128)][2][32], kept channels [B][G][32]; the shortlist
+  // size and output; the scan's shortlist keys [B][G][n]
+  const unsigned long long *sk2_codes;
+  const uint16_t *sk2_zs;
+  const int32_t *sk2_chan;
+  int n_short;
+  int32_t *shortlist;
+  uint32_t *skey;
   const int32_t *ridx, *rcount;
   const float *proj, *r;
   float *out, *d_hat, *log_shift, *eps_hat0, *eps_hat;
@@ -578,6 +587,40 @@ __device__ __forceinline__ void clear_bin_hist(const DParams &p, int c, int b,
   for (int t = lo + (int)threadIdx.x; t < hi; t += kBlock) h0[t] = 0u;
 }
 
+// Step-start work of scan chunk c of group (b, g): the group's row states
+// (chunk 0; no other block of the launch touches them), the status word and
+// host byte count (chunk 0 of group 0), and this chunk's share of the
+// bitmaps and histograms the later launches fill.
+template <int GRP>
+__device__ __forceinline__ void scan_setup(const DParams &p, int c, int g,
+                                           int b) {
+  const int bg = b * p.G + g;
+  if (c == 0) {
+    for (int h = 0; h < GRP; ++h) {
+      const int row = row_of(p, b, g, h, GRP);
+      if (threadIdx.x == 0) {
+        RowState z{};
+        z.amax = -1;
+        z.T = ~0ull;
+        p.rows[row] = z;
+      }
+    }
+    if (bg == 0 && threadIdx.x == 0) {
+      *p.status = 0u;
+      *p.host_bytes = 0ull;
+    }
+  }
+  clear_bin_hist<GRP>(p, c, b, g);
+  const int w0 = c * p.chunk / 32, nw = p.chunk / 32;
+  for (int w = threadIdx.x; w < nw; w += kBlock) {
+    if (w0 + w < p.nwords) {
+      p.fbits[(size_t)bg * p.nwords + w0 + w] = 0u;
+      for (int h = 0; h < GRP; ++h)
+        p.hbits[(size_t)row_of(p, b, g, h, GRP) * p.nwords + w0 + w] = 0u;
+    }
+  }
+}
+
 template <int GRP, int SD>
 __device__ __forceinline__ void scan_body(const DParams &p, int c, int g,
                                           int b) {
@@ -620,36 +663,7 @@ __device__ __forceinline__ void scan_body(const DParams &p, int c, int g,
     }
   };
   load_sub(base, raw, rv);
-
-  // step-start initialisation of this group's state (no other block of
-  // this launch touches it)
-  if (c == 0) {
-    for (int h = 0; h < GRP; ++h) {
-      const int row = row_of(p, b, g, h, GRP);
-      if (threadIdx.x == 0) {
-        RowState z{};
-        z.amax = -1;
-        z.T = ~0ull;
-        p.rows[row] = z;
-      }
-    }
-    if (bg == 0 && threadIdx.x == 0) {
-      *p.status = 0u;
-      *p.host_bytes = 0ull;
-    }
-  }
-  clear_bin_hist<GRP>(p, c, b, g);
-  // clear this chunk's bitmap words
-  {
-    const int w0 = c * p.chunk / 32, nw = p.chunk / 32;
-    for (int w = threadIdx.x; w < nw; w += kBlock) {
-      if (w0 + w < p.nwords) {
-        p.fbits[(size_t)bg * p.nwords + w0 + w] = 0u;
-        for (int h = 0; h < GRP; ++h)
-          p.hbits[(size_t)row_of(p, b, g, h, GRP) * p.nwords + w0 + w] = 0u;
-      }
-    }
-  }
+  scan_setup<GRP>(p, c, g, b);
   // projected, pre-scaled queries: stage q and P_g in LDS, then one output
   // per thread
   {
@@ -1029,6 +1043,371 @@ __global__ __launch_bounds__(kBlock) void dk_front_exact(DParams p) {
     scan_exact_body<GRP>(p, x, g, b);
   else
     resident_body<GRP>(p, x - p.nch, g, b);
+}
+
+// ------------------------------------------------------------ 2-bit sketch
+// The pages' deployed sketch ("Verify Before You Fetch", Appendix A.1 and
+// section 5.1): 2-bit codes of 32 kept key channels per token, an fp16 zero
+// point z and scale s per kept channel and 128-token group. With the query
+// entries q_c of the kept channels (scaled by 1/sqrt(d)), the sketch logit
+// of token i is A + sum_c code_ic u_c, where A = sum_c q_c z_c and
+// u_c = q_c s_c are per group and head. The plan then uses exact logits on
+// S and on the shortlist (the n_short tokens of L outside S with the
+// largest sketch logit over the group's heads, whose keys are read from
+// host memory) and these sketch logits on the rest of L.
+constexpr int kSk2Chan = 32;
+constexpr int kSk2Group = 128;
+constexpr int kSk2Sub = 1024;              // tokens per scan sub-batch
+constexpr int kSk2Tok = kSk2Sub / kBlock;  // tokens per thread and sub-batch
+constexpr int kShortMax = 1024;            // largest shortlist
+
+// fp32 -> an unsigned key in the same order (0 is never produced for a
+// finite value, so it marks tokens that are not eligible).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float half_to_float(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// Scan workgroup of the 2-bit sketch: the sketch logits of chunk c for the
+// group's heads into shat, and each token's shortlist key (the largest of
+// them as order_key, 0 for r == 1).
+template <int GRP>
+__device__ __forceinline__ void scan2_body(const DParams &p, int c, int g,
+                                           int b) {
+  const int bg = b * p.G + g;
+  const int base = c * p.chunk, lim = min(base + p.chunk, p.n);
+  const int ngrp = (p.n + kSk2Group - 1) / kSk2Group;
+  __shared__ float s_q[GRP][kSk2Chan];
+  __shared__ float s_u[kSk2Sub / kSk2Group][kSk2Chan][GRP];
+  __shared__ float s_a[kSk2Sub / kSk2Group][GRP];
+  const unsigned long long *codes = p.sk2_codes + (size_t)bg * p.n;
+  const float *rr = p.r + (size_t)bg * p.n;
+  unsigned long long wv[kSk2Tok];
+  float rv[kSk2Tok];
+  auto load = [&](int sb, unsigned long long (&w)[kSk2Tok], float (&r)[kSk2Tok]) {
+#pragma unroll
+    for (int k = 0; k < kSk2Tok; ++k) {
+      const int i = sb + k * kBlock + (int)threadIdx.x;
+      const bool ok = i < lim;
+      w[k] = ok ? codes[i] : 0ull;
+      r[k] = ok ? rr[i] : 1.0f;
+    }
+  };
+  load(base, wv, rv);  // first sub-batch in flight
+  scan_setup<GRP>(p, c, g, b);
+  if (threadIdx.x < GRP * kSk2Chan) {
+    const int h = threadIdx.x / kSk2Chan, cc = threadIdx.x % kSk2Chan;
+    // (a channel outside 0..127 is read as the nearest one)
+    const int ch = min(max(p.sk2_chan[(size_t)bg * kSk2Chan + cc], 0), kHeadDim - 1);
+    s_q[h][cc] = __uint_as_float(
+                     (uint32_t)p.q[(size_t)row_of(p, b, g, h, GRP) * kHeadDim + ch] << 16) *
+                 kInvSqrtD;
+  }
+  bool bad = false;
+  for (int sb = base; sb < lim; sb += kSk2Sub) {
+    __syncthreads();  // s_q written; the previous sub-batch done with s_u
+    const int ng = (min(sb + kSk2Sub, lim) - sb + kSk2Group - 1) / kSk2Group;
+    const uint16_t *zs = p.sk2_zs + ((size_t)bg * ngrp + sb / kSk2Group) * 2 * kSk2Chan;
+    for (int e = threadIdx.x; e < ng * kSk2Chan * GRP; e += kBlock) {
+      const int gi = e / (kSk2Chan * GRP), cc = (e / GRP) % kSk2Chan, h = e % GRP;
+      s_u[gi][cc][h] = s_q[h][cc] * half_to_float(zs[gi * 2 * kSk2Chan + kSk2Chan + cc]);
+    }
+    for (int e = threadIdx.x; e < ng * GRP; e += kBlock) {
+      const int gi = e / GRP, h = e % GRP;
+      float a = 0.0f;
+      for (int cc = 0; cc < kSk2Chan; ++cc)
+        a = __builtin_fmaf(s_q[h][cc], half_to_float(zs[gi * 2 * kSk2Chan + cc]), a);
+      s_a[gi][h] = a;
+    }
+    __syncthreads();
+    unsigned long long nw[kSk2Tok];
+    float nr[kSk2Tok];
+    if (sb + kSk2Sub < lim) load(sb + kSk2Sub, nw, nr);  // next in flight
+#pragma unroll
+    for (int k = 0; k < kSk2Tok; ++k) {
+      const int i = sb + k * kBlock + (int)threadIdx.x;
+      if (i >= lim) continue;
+      const int gi = (k * kBlock + (int)threadIdx.x) / kSk2Group;
+      float acc[GRP];
+#pragma unroll
+      for (int h = 0; h < GRP; ++h) acc[h] = s_a[gi][h];
+      const uint32_t lo = (uint32_t)wv[k], hi = (uint32_t)(wv[k] >> 32);
+#pragma unroll
+      for (int cc = 0; cc < kSk2Chan; ++cc) {
+        const uint32_t w = cc < 16 ? lo : hi;
+        const float cf = (float)((w >> (2 * (cc & 15))) & 3u);
+#pragma unroll
+        for (int h = 0; h < GRP; ++h) acc[h] = __builtin_fmaf(cf, s_u[gi][cc][h], acc[h]);
+      }
+      const float ri = rv[k];
+      if (!(ri > 0.0f && ri <= 1.0f)) bad = true;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int h = 0; h < GRP; ++h) {
+        p.shat[(size_t)row_of(p, b, g, h, GRP) * p.n + i] = acc[h];
+        mx = fmaxf(mx, acc[h]);
+      }
+      p.skey[(size_t)bg * p.n + i] = ri < 1.0f ? order_key(mx) : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < kSk2Tok; ++k) {
+      wv[k] = nw[k];
+      rv[k] = nr[k];
+    }
+  }
+  const int np = p.nch + p.ncr;
+  const int any = __syncthreads_or((int)bad);
+  if (threadIdx.x == 0) p.fstat[(size_t)bg * np + c] = any ? VKV_STATUS_BAD_R : 0u;
+}
+
+template <int GRP>
+__global__ __launch_bounds__(kBlock) void dk_front2(DParams p) {
+  const int x = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  if (x < p.nch)
+    scan2_body<GRP>(p, x, g, b);
+  else
+    resident_body<GRP>(p, x - p.nch, g, b);
+}
+
+// Exclusive prefix sum over the 1024 threads of a row-level workgroup
+// (thread order); the total through *total.
+__device__ __forceinline__ uint32_t plan_excl_scan(uint32_t v, uint32_t *s_w,
+                                                   uint32_t *total) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const uint32_t incl = wave_incl_scan<uint32_t>(v, lane);
+  __syncthreads();
+  if (lane == kWave - 1) s_w[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0u, tot = 0u;
+  for (int w = 0; w < kPlanWaves; ++w) {
+    before += w < wave ? s_w[w] : 0u;
+    tot += s_w[w];
+  }
+  *total = tot;
+  return before + incl - v;
+}
+
+// Shortlist of one (request, KV head), one 1024-thread workgroup: the
+// n_short eligible tokens (L outside S) with the largest keys, equal keys by
+// position, found by an 11/11/10-bit radix select over the scan's keys;
+// their key rows read from host memory and scored exactly for the group's
+// heads, those logits written over the sketch logits, and likewise the
+// resident logits over the sketch logits of S.
+template <int GRP>
+__global__ __launch_bounds__(kPlanThreads) void dk_short(DParams p) {
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int bg = b * p.G + g, n = p.n, tid = threadIdx.x;
+  const int lane = tid % kWave;
+  __shared__ uint32_t s_res[kMaxTokens / 32];
+  __shared__ uint32_t s_hist[kSelBinsP];
+  __shared__ int s_list[kShortMax];
+  __shared__ float s_q[GRP][kHeadDim];
+  __shared__ uint32_t s_w[kPlanWaves];
+  __shared__ uint32_t s_pick[2];
+  const int nw = (n + 31) / 32;
+  for (int w = tid; w < nw; w += kPlanThreads) s_res[w] = 0u;
+  for (int e = tid; e < GRP * kHeadDim; e += kPlanThreads) {
+    const int h = e / kHeadDim, k = e % kHeadDim;
+    s_q[h][k] = __uint_as_float(
+        (uint32_t)p.q[(size_t)row_of(p, b, g, h, GRP) * kHeadDim + k] << 16);
+  }
+  __syncthreads();
+  const int cnt = max(0, min(p.rcount[bg], p.cap));
+  const int32_t *ridx = p.ridx + (size_t)bg * p.cap;
+  for (int j = tid; j < cnt; j += kPlanThreads) {
+    const int pos = ridx[j];
+    if (pos >= 0 && pos < n) atomicOr(&s_res[pos >> 5], 1u << (pos & 31));
+  }
+  __syncthreads();
+  const uint32_t *keys = p.skey + (size_t)bg * n;
+  auto key_at = [&](int i) {
+    const uint32_t k = keys[i];
+    return ((s_res[i >> 5] >> (i & 31)) & 1u) ? 0u : k;
+  };
+  // radix select: after the levels, the chosen tokens are those with key
+  // > T and the first `need` (by position) with key == T
+  uint32_t prefix = 0u, mask = 0u;
+  int need = p.n_short;
+  uint32_t T = 0xFFFFFFFFu;
+  if (need > 0) {
+    bool all = false;
+    for (int lvl = 0; lvl < 3; ++lvl) {
+      // key bits [21, 32), then [10, 21), then [0, 10)
+      const int sh = lvl == 0 ? 21 : (lvl == 1 ? 10 : 0);
+      const int nb = lvl == 2 ? 1 << 10 : 1 << 11;
+      for (int e = tid; e < kSelBinsP; e += kPlanThreads) s_hist[e] = 0u;
+      __syncthreads();
+      for (int i = tid; i < n; i += kPlanThreads) {
+        const uint32_t k = key_at(i);
+        if (k != 0u && (k & mask) == prefix) atomicAdd(&s_hist[(k >> sh) & (nb - 1)], 1u);
+      }
+      __syncthreads();
+      if (tid < kWave) {
+        // lane l owns bins [l * per, (l + 1) * per); counts above each lane
+        const int per = nb / kWave;
+        uint32_t own = 0u;
+        for (int e = 0; e < per; ++e) own += s_hist[lane * per + e];
+        // inclusive suffix sums over the lanes (keys in this lane's bins and
+        // those of higher lanes), by shuffles from above
+        uint32_t suf = own;
+        for (int o = 1; o < kWave; o <<= 1) {
+          const uint32_t v = __shfl_down(suf, o, kWave);
+          if (lane + o < kWave) suf += v;
+        }
+        const uint32_t above = suf - own;
+        const uint32_t total = __shfl(suf, 0, kWave);
+        if (lvl == 0 && total <= (uint32_t)need) {
+          if (lane == 0) {
+            s_pick[0] = 0xFFFFFFFFu;  // every eligible token
+            s_pick[1] = 0u;
+          }
+        } else if (above < (uint32_t)need && (uint32_t)need <= suf) {
+          uint32_t acc = above;
+          int bin = lane * per;
+          for (int e = per - 1; e >= 0; --e) {
+            const uint32_t h = s_hist[lane * per + e];
+            if (acc + h >= (uint32_t)need) {
+              bin = lane * per + e;
+              break;
+            }
+            acc += h;
+          }
+          s_pick[0] = (uint32_t)bin;
+          s_pick[1] = acc;  // keys above the bin
+        }
+      }
+      __syncthreads();
+      const uint32_t bin = s_pick[0], acc = s_pick[1];
+      __syncthreads();
+      if (bin == 0xFFFFFFFFu) {
+        all = true;
+        break;
+      }
+      prefix |= bin << sh;
+      mask |= (uint32_t)(nb - 1) << sh;
+      need -= (int)acc;
+    }
+    if (all) {
+      T = 0u;
+      need = 0;
+    } else {
+      T = prefix;
+    }
+  }
+  // positions in order: thread t takes [t * per, (t + 1) * per)
+  const int per = (n + kPlanThreads - 1) / kPlanThreads;
+  const int i0 = min(n, tid * per), i1 = min(n, i0 + per);
+  uint32_t neq = 0u;
+  for (int i = i0; i < i1; ++i) neq += key_at(i) == T ? 1u : 0u;
+  uint32_t tot;
+  const uint32_t er0 = plan_excl_scan(neq, s_w, &tot);  // equal keys before
+  auto chosen = [&](uint32_t k, uint32_t &er) {
+    if (k > T) return true;
+    return k == T && k != 0u && er++ < (uint32_t)need;
+  };
+  uint32_t nsel = 0u;
+  {
+    uint32_t er = er0;
+    for (int i = i0; i < i1; ++i) nsel += chosen(key_at(i), er) ? 1u : 0u;
+  }
+  uint32_t ns;
+  uint32_t slot = plan_excl_scan(nsel, s_w, &ns);
+  {
+    uint32_t er = er0;
+    for (int i = i0; i < i1; ++i)
+      if (chosen(key_at(i), er) && slot < (uint32_t)kShortMax) s_list[slot++] = i;
+  }
+  __syncthreads();
+  ns = min(ns, (uint32_t)kShortMax);
+  if (p.shortlist)
+    for (int j = tid; j < p.n_short; j += kPlanThreads)
+      p.shortlist[(size_t)bg * p.n_short + j] = j < (int)ns ? s_list[j] : -1;
+  if (tid == 0 && ns > 0)
+    atomicAdd(p.host_bytes, (unsigned long long)ns * kHeadDim * 2ull);
+  // exact logits of the shortlist: 8 threads per token, 16 dimensions each
+  const uint16_t *hk = p.host_kv;
+  for (int j0 = 0; j0 < (int)ns; j0 += kPlanThreads / 8) {
+    const int j = j0 + tid / 8, part = tid % 8;
+    const bool ok = j < (int)ns;
+    const int pos = ok ? s_list[j] : 0;
+    float kf[16];
+    {
+      uint4 w0 = make_uint4(0u, 0u, 0u, 0u), w1 = w0;
+      if (ok) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(
+            hk + ((size_t)bg * n + pos) * 2 * kHeadDim + part * 16);
+        w0 = src[0];
+        w1 = src[1];
+      }
+      unpack8(w0, kf);
+      unpack8(w1, kf + 8);
+    }
+#pragma unroll
+    for (int h = 0; h < GRP; ++h) {
+      float a = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) a = __builtin_fmaf(s_q[h][part * 16 + e], kf[e], a);
+      a = group_sum<8>(a);
+      if (ok && part == 0) p.shat[(size_t)row_of(p, b, g, h, GRP) * n + pos] = a * kInvSqrtD;
+    }
+  }
+  // exact logits of S
+  const float *rr = p.r + (size_t)bg * n;
+  for (int j = tid; j < cnt; j += kPlanThreads) {
+    const int pos = ridx[j];
+    if (pos < 0 || pos >= n || !(rr[pos] < 1.0f)) continue;
+#pragma unroll
+    for (int h = 0; h < GRP; ++h) {
+      const int row = row_of(p, b, g, h, GRP);
+      p.shat[(size_t)row * n + pos] = p.ell[(size_t)row * p.cap + j];
+    }
+  }
+}
+
+// Pass-0 sums of the beta* iteration for the 2-bit sketch, per scan chunk,
+// from the planning logits once S and the shortlist hold exact logits: the
+// records the scan itself writes in the other modes.
+template <int GRP>
+__global__ __launch_bounds__(kBlock) void dk_p0(DParams p) {
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int bg = b * p.G + g;
+  const int base = c * p.chunk, lim = min(base + p.chunk, p.n);
+  const float *rr = p.r + (size_t)bg * p.n;
+  P0Acc acc[GRP];
+#pragma unroll
+  for (int h = 0; h < GRP; ++h) p0_init(acc[h]);
+  uint32_t n_h = 0u;
+  constexpr int U = 4;
+  for (int i0 = base + (int)threadIdx.x; i0 < lim; i0 += kBlock * U) {
+    float rv[U], sv[U][GRP];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * kBlock;
+      const bool ok = i < lim;
+      rv[u] = ok ? rr[i] : 1.0f;
+#pragma unroll
+      for (int h = 0; h < GRP; ++h)
+        sv[u][h] = ok ? p.shat[(size_t)row_of(p, b, g, h, GRP) * p.n + i] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (i0 + u * kBlock >= lim) continue;
+      if (!(rv[u] < 1.0f)) {
+        ++n_h;
+        continue;
+      }
+#pragma unroll
+      for (int h = 0; h < GRP; ++h) {
+        p0_shift(acc[h], sv[u][h]);
+        p0_add(acc[h], sv[u][h], rv[u]);
+      }
+    }
+  }
+  p0_finish<GRP>(p, b, g, c, acc, n_h);
 }
 
 // ------------------------------------------------------------ planning
@@ -3400,16 +3779,32 @@ template <int GRP>
 hipError_t run(const DParams &p, hipStream_t s, int sd, void **events) {
   const dim3 blk(kBlock);
   const dim3 gfront((unsigned)(p.nch + p.ncr), (unsigned)p.G, (unsigned)p.B);
-  constexpr int kPhases = 9;  // the entries of kPhaseNames
+  constexpr int kPhases = 11;  // the entries of kPhaseNames
   const PhaseMark mark(events, s, kPhases);
+  const bool sk2 = p.weights == VKV_W_SKETCH2;
   int k = 0;
   mark(k);
   if (p.weights == VKV_W_PERFECT)
     mark.launch(k, dk_front_exact<GRP>, gfront, blk, p);
+  else if (sk2)
+    mark.launch(k, dk_front2<GRP>, gfront, blk, p);
   else if (sd == 32)
     mark.launch(k, dk_front<GRP, 32>, gfront, blk, p);
   else
     mark.launch(k, dk_front<GRP, 16>, gfront, blk, p);
+  mark(++k);
+  // 2-bit sketch: the shortlist with its exact logits, then pass 0
+  if (sk2)
+    mark.launch(k, dk_short<GRP>, dim3((unsigned)p.G, (unsigned)p.B),
+                dim3(kPlanThreads), p);
+  else
+    mark.empty(k);
+  mark(++k);
+  if (sk2)
+    mark.launch(k, dk_p0<GRP>, dim3((unsigned)p.nch, (unsigned)p.G, (unsigned)p.B),
+                blk, p);
+  else
+    mark.empty(k);
   mark(++k);
   const dim3 grow((unsigned)p.nrc, (unsigned)p.Hq, (unsigned)p.B);
   const dim3 gone((unsigned)p.Hq, (unsigned)p.B);
@@ -3445,8 +3840,9 @@ hipError_t run(const DParams &p, hipStream_t s, int sd, void **events) {
 }
 
 const char *const kPhaseNames[] = {
-    "scan", "beta1", "beta2", "shrink", "cert", "cand", "walk", "fetch", "attn"};
-static_assert(sizeof(kPhaseNames) / sizeof(kPhaseNames[0]) == 9,
+    "scan", "shortlist", "pass0", "beta1", "beta2", "shrink", "cert", "cand",
+    "walk", "fetch", "attn"};
+static_assert(sizeof(kPhaseNames) / sizeof(kPhaseNames[0]) == 11,
               "one name per phase of run()");
 
 }  // namespace
@@ -3541,6 +3937,7 @@ DecodeLayout decode_layout(const vkv_decode_args &a) {
   L.rpart = c.take<uint32_t>(rows * kSelWG * 2);
   L.apart = c.take<float2>(rows * (L.ncr + L.ncf));
   L.aparto = c.take<float>(rows * kHeadDim * (size_t)L.npad);
+  L.skey = c.take<uint32_t>(groups * n);  // (2-bit sketch only)
   L.total = (c.off + 255) & ~size_t(255);
   return L;
 }
@@ -3568,6 +3965,11 @@ hipError_t launch_decode(const vkv_decode_args &a, const DecodeLayout &L,
   p.row_stats = a.row_stats;
   p.row_path = a.row_path;
   p.status = a.status;
+  p.sk2_codes = reinterpret_cast<const unsigned long long *>(a.sk2_codes);
+  p.sk2_zs = a.sk2_zs;
+  p.sk2_chan = a.sk2_chan;
+  p.n_short = a.n_short;
+  p.shortlist = a.shortlist;
   void *w = a.workspace;
   p.rows = at<RowState>(w, L.rows);
   p.shat = at<float>(w, L.shat);
@@ -3603,6 +4005,7 @@ hipError_t launch_decode(const vkv_decode_args &a, const DecodeLayout &L,
   p.nsel = L.nsel;
   p.apart = at<float2>(w, L.apart);
   p.aparto = at<float>(w, L.aparto);
+  p.skey = at<uint32_t>(w, L.skey);
   p.npad = L.npad;
   p.B = a.batch;
   p.Hq = a.n_q_heads;

@@ -59,7 +59,7 @@ struct DecodeLayout {
       bpart, band,
       bstate,
       rbeta, binst, bhist, bcnt, bkeys, bav, cpart, ccount, clo, tpart, candk, candw, candq, dpart,
-      rpart, apart, aparto, total;
+      rpart, apart, aparto, skey, total;
 };
 
 DecodeLayout decode_layout(const vkv_decode_args &a);
@@ -67,6 +67,16 @@ int decode_phase_count();
 const char *decode_phase_name(int i);
 hipError_t launch_decode(const vkv_decode_args &a, const DecodeLayout &L,
                          const uint16_t *host_kv_dev, hipStream_t s);
+
+// ------------------------------------------------------------ 2-bit sketch
+struct Sketch2Layout {
+  int nblk;
+  size_t part, total;
+};
+
+Sketch2Layout sketch2_layout(const vkv_sketch2_args &a);
+hipError_t launch_sketch2(const vkv_sketch2_args &a, const Sketch2Layout &L,
+                          hipStream_t s);
 
 // ------------------------------------------------------------ dense baselines
 struct DenseLayout {

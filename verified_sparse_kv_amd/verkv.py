@@ -29,13 +29,15 @@ STATUS_BAD_RESIDENT = 0x8
 EST_CLIP, EST_UNBIASED, EST_BINARY = 0, 1, 2
 PATH_NO_FETCH, PATH_TOP_CANDIDATES, PATH_ALL_CANDIDATES, PATH_STREAMING = \
     0, 1, 2, 3
-W_SKETCH, W_PERFECT = 0, 1
+W_SKETCH, W_PERFECT, W_SKETCH2 = 0, 1, 2
+SK2_CHANNELS, SK2_GROUP = 32, 128
 
 EXPORTS = ("vkv_compress_workspace_bytes", "vkv_decode_workspace_bytes",
            "vkv_compress", "vkv_decode_step", "vkv_check_status",
            "vkv_last_error", "vkv_version", "vkv_decode_phase_count",
            "vkv_decode_phase_name", "vkv_dense_workspace_bytes",
-           "vkv_dense_attention", "vkv_decode_step_noalloc")
+           "vkv_dense_attention", "vkv_decode_step_noalloc",
+           "vkv_sketch2_workspace_bytes", "vkv_sketch2_build")
 NOALLOC_WORKSPACE_BYTES = 128 << 20
 
 _p = ctypes.c_void_p
@@ -60,12 +62,15 @@ class DecodeArgs(ctypes.Structure):
                 ("q", _p), ("resident_kv", _p), ("resident_idx", _p),
                 ("resident_count", _p), ("sketch", _p), ("proj", _p), ("r", _p),
                 ("host_kv", _p),
+                ("sk2_codes", _p), ("sk2_zs", _p), ("sk2_chan", _p),
+                ("n_short", _i32),
                 ("eps", ctypes.c_float), ("delta", ctypes.c_float),
                 ("estimator", _i32), ("weights", _i32), ("fetch_cap", _i32),
                 ("out", _p), ("d_hat", _p), ("log_shift", _p), ("eps_hat0", _p),
                 ("eps_hat", _p), ("k_star", _p), ("fetch_idx", _p),
                 ("fetch_count", _p), ("host_bytes", _p), ("row_stats", _p),
-                ("row_path", _p), ("status", _p), ("phase_events", _p),
+                ("row_path", _p), ("shortlist", _p), ("status", _p),
+                ("phase_events", _p),
                 ("workspace", _p),
                 ("workspace_bytes", ctypes.c_size_t)]
 
@@ -74,6 +79,13 @@ class DenseArgs(ctypes.Structure):
     _fields_ = [("batch", _i32), ("n_q_heads", _i32), ("n_kv_heads", _i32),
                 ("head_dim", _i32), ("n_tokens", _i32),
                 ("q", _p), ("kv", _p), ("out", _p), ("log_d", _p),
+                ("workspace", _p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class Sketch2Args(ctypes.Structure):
+    _fields_ = [("n_slices", _i32), ("n_tokens", _i32), ("head_dim", _i32),
+                ("key_stride", ctypes.c_int64), ("slice_stride", ctypes.c_int64),
+                ("k", _p), ("codes", _p), ("zs", _p), ("chan", _p),
                 ("workspace", _p), ("workspace_bytes", ctypes.c_size_t)]
 
 
@@ -124,6 +136,10 @@ def _load():
     lib.vkv_dense_workspace_bytes.restype = ctypes.c_size_t
     lib.vkv_dense_attention.argtypes = [ctypes.POINTER(DenseArgs), _p]
     lib.vkv_dense_attention.restype = ctypes.c_int
+    lib.vkv_sketch2_workspace_bytes.argtypes = [ctypes.POINTER(Sketch2Args)]
+    lib.vkv_sketch2_workspace_bytes.restype = ctypes.c_size_t
+    lib.vkv_sketch2_build.argtypes = [ctypes.POINTER(Sketch2Args), _p]
+    lib.vkv_sketch2_build.restype = ctypes.c_int
     return lib
 
 
@@ -157,6 +173,14 @@ def vkv_dense_workspace_bytes(args):
 
 def vkv_dense_attention(args, stream=None):
     return int(LIB.vkv_dense_attention(ctypes.byref(args), stream))
+
+
+def vkv_sketch2_workspace_bytes(args):
+    return int(LIB.vkv_sketch2_workspace_bytes(ctypes.byref(args)))
+
+
+def vkv_sketch2_build(args, stream=None):
+    return int(LIB.vkv_sketch2_build(ctypes.byref(args), stream))
 
 
 def vkv_check_status(status_ptr, stream=None):
@@ -266,13 +290,51 @@ def compress(tau, k, v, budget, n_sink, n_local, seed, cap, layer0=0,
     return out
 
 
+def sketch2_build(k, key_stride=None, stream=None):
+    """The 2-bit key sketch of every slice of ``k`` (a device tensor of bf16
+    bits, int16, shaped [..., n, key_stride] with the key in the first 128
+    elements of each token's row; leading dimensions are the slices).
+    Returns dict(codes [..., n] int64, zs [..., ceil(n/128), 2, 32] int16,
+    chan [..., 32] int32)."""
+    torch = _torch()
+    if k.dtype != torch.int16 or not k.is_cuda or not k.is_contiguous():
+        raise ValueError("k: contiguous int16 device tensor expected")
+    lead = tuple(k.shape[:-2])
+    n, stride = k.shape[-2], k.shape[-1]
+    slices = 1
+    for x in lead:
+        slices *= x
+    ng = (n + SK2_GROUP - 1) // SK2_GROUP
+    dev = k.device
+    out = dict(codes=torch.empty(lead + (n,), dtype=torch.int64, device=dev),
+               zs=torch.empty(lead + (ng, 2, SK2_CHANNELS), dtype=torch.int16,
+                              device=dev),
+               chan=torch.empty(lead + (SK2_CHANNELS,), dtype=torch.int32,
+                                device=dev))
+    a = Sketch2Args(n_slices=slices, n_tokens=n, head_dim=128,
+                    key_stride=stride if key_stride is None else key_stride,
+                    slice_stride=n * stride, k=_ptr(k),
+                    codes=_ptr(out["codes"]), zs=_ptr(out["zs"]),
+                    chan=_ptr(out["chan"]))
+    nbytes = vkv_sketch2_workspace_bytes(a)
+    if nbytes == 0:
+        _check(vkv_sketch2_build(a, _stream(stream)))
+    ws = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
+    a.workspace, a.workspace_bytes = _ptr(ws), nbytes
+    _check(vkv_sketch2_build(a, _stream(stream)))
+    out["_ws"] = ws
+    return out
+
+
 class DecodeStep:
     """Reusable decode-step launcher: outputs and workspace are allocated once
     for a shape, so repeated steps only marshal pointers and launch."""
 
-    def __init__(self, B, Hq, G, n, s, cap, fetch_cap, device, d=128):
+    def __init__(self, B, Hq, G, n, s, cap, fetch_cap, device, d=128,
+                 n_short=128):
         torch = _torch()
         self.shape = (B, Hq, G, n, s, cap, fetch_cap)
+        self.n_short = n_short
         self.out = dict(
             out=torch.empty((B, Hq, d), dtype=torch.float32, device=device),
             d_hat=torch.empty((B, Hq), dtype=torch.float32, device=device),
@@ -287,13 +349,15 @@ class DecodeStep:
             row_stats=torch.empty((B, Hq, 8), dtype=torch.float64,
                                   device=device),
             row_path=torch.empty((B, Hq), dtype=torch.int32, device=device),
+            shortlist=torch.empty((B, G, max(n_short, 1)), dtype=torch.int32,
+                                  device=device),
             status=torch.zeros((1,), dtype=torch.int32, device=device))
         self.args = DecodeArgs(batch=B, n_q_heads=Hq, n_kv_heads=G, head_dim=d,
                                n_tokens=n, sketch_dim=s, cap=cap,
-                               fetch_cap=fetch_cap)
+                               fetch_cap=fetch_cap, n_short=n_short)
         for key in ("out", "d_hat", "log_shift", "eps_hat0", "eps_hat", "k_star",
                     "fetch_idx", "fetch_count", "host_bytes", "row_stats",
-                    "row_path", "status"):
+                    "row_path", "shortlist", "status"):
             setattr(self.args, key, _ptr(self.out[key]))
         nbytes = vkv_decode_workspace_bytes(self.args)
         if nbytes == 0:
@@ -303,7 +367,10 @@ class DecodeStep:
         self.args.workspace_bytes = nbytes
 
     def bind(self, q, resident_kv, resident_idx, resident_count, sketch, proj, r,
-             host_kv, eps, delta, estimator=EST_CLIP, weights=W_SKETCH):
+             host_kv, eps, delta, estimator=EST_CLIP, weights=W_SKETCH,
+             sketch2=None):
+        """``sketch2``: with W_SKETCH2, the dict sketch2_build returns for
+        keys shaped [B][G][n][...] (codes, zs, chan)."""
         torch = _torch()
         B, Hq, G, n, s, cap, _ = self.shape
         d = 128
@@ -317,6 +384,16 @@ class DecodeStep:
             _need(sketch, torch.int16, (B, G, n, s), "sketch")
             _need(proj, torch.float32, (G, d, s), "proj")
         a = self.args
+        if weights == W_SKETCH2:
+            ng = (n + SK2_GROUP - 1) // SK2_GROUP
+            _need(sketch2["codes"], torch.int64, (B, G, n), "sketch2 codes")
+            _need(sketch2["zs"], torch.int16, (B, G, ng, 2, SK2_CHANNELS), "sketch2 zs")
+            _need(sketch2["chan"], torch.int32, (B, G, SK2_CHANNELS), "sketch2 chan")
+            a.sk2_codes = _ptr(sketch2["codes"])
+            a.sk2_zs = _ptr(sketch2["zs"])
+            a.sk2_chan = _ptr(sketch2["chan"])
+        else:
+            a.sk2_codes = a.sk2_zs = a.sk2_chan = None
         a.q, a.resident_kv = _ptr(q), _ptr(resident_kv)
         a.resident_idx, a.resident_count = _ptr(resident_idx), _ptr(resident_count)
         a.sketch, a.proj, a.r = _ptr(sketch), _ptr(proj), _ptr(r)
@@ -324,7 +401,7 @@ class DecodeStep:
         a.eps, a.delta = float(eps), float(delta)
         a.estimator, a.weights = int(estimator), int(weights)
         self._keep = (q, resident_kv, resident_idx, resident_count, sketch, proj,
-                      r, host_kv)
+                      r, host_kv, sketch2)
         return self
 
     def set_phase_events(self, events):
@@ -349,15 +426,16 @@ class DecodeStep:
 
 def decode_step(q, resident_kv, resident_idx, resident_count, sketch, proj, r,
                 host_kv, eps, delta, fetch_cap=None, estimator=EST_CLIP,
-                weights=W_SKETCH, stream=None):
+                weights=W_SKETCH, stream=None, sketch2=None, n_short=128):
     """One KVFetch decode step (allocates outputs and workspace)."""
     B, Hq, _ = q.shape
     _, G, cap = resident_idx.shape
     n = r.shape[-1]
     s = sketch.shape[-1] if sketch is not None else 32
-    step = DecodeStep(B, Hq, G, n, s, cap, fetch_cap or n, q.device)
+    step = DecodeStep(B, Hq, G, n, s, cap, fetch_cap or n, q.device,
+                      n_short=n_short)
     step.bind(q, resident_kv, resident_idx, resident_count, sketch, proj, r,
-              host_kv, eps, delta, estimator, weights)
+              host_kv, eps, delta, estimator, weights, sketch2)
     return step.launch(stream)
 
 

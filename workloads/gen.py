@@ -22,6 +22,12 @@ paper's shapes (32K/128K context, GQA 4:1, head_dim 128, resident fraction
 * c5  compression only: 36 layers x 8 KV heads x n=131072,
       tau ~ Beta(0.5, 5), 4 sinks + 256 local, eta in {1/8, 1/16, 1/32}.
 
+With ``pair_profile`` (the workloads of the 2-bit sketch), key energy is
+spread unevenly over the RoPE channel pairs (j, j + 64), as the pages'
+sketch assumes: per KV head a random ranking of the 64 pairs, and pair j
+scaled by (1 + rank_j)^-1/2 (normalised to unit mean square), so the 16
+strongest pairs hold about 71% of the key energy.
+
 Every array is drawn from numpy PCG64 ``default_rng([config, seed, ...])``;
 K, V, sketches and queries are rounded to bfloat16 (round to nearest even)
 and handed to both the library and the oracle as the same bf16 values.
@@ -83,8 +89,19 @@ def _obs_tau(rng, k, n_q):
     return (tau / tau.max()).astype(np.float32)
 
 
+def _pair_scales(rng, d):
+    """Per-channel scales with uneven RoPE-pair energy (see the module
+    notes): pair j -> channels j and j + d/2."""
+    h = d // 2
+    rank = rng.permutation(h).astype(np.float64)
+    sc = (1.0 + rank) ** -0.5
+    sc /= math.sqrt(np.mean(sc ** 2))
+    return np.concatenate([sc, sc]).astype(np.float32)
+
+
 def make_decode_workload(cfg, seed=0, n=None, B=None, G=None, budget=None,
-                         alpha=None, with_queries=True, grp=None, s=None):
+                         alpha=None, with_queries=True, grp=None, s=None,
+                         pair_profile=False):
     """Draw one decode workload; optional overrides shrink or reshape it for
     tests (``grp`` query heads per KV head, ``s`` sketch dimension).
 
@@ -135,6 +152,8 @@ def make_decode_workload(cfg, seed=0, n=None, B=None, G=None, budget=None,
             else:
                 sig = _zipf_sigma(rng, nn)
                 k = rng.standard_normal((nn, d), dtype=np.float32) * sig[:, None]
+            if pair_profile:
+                k = k * _pair_scales(np.random.default_rng([cid, seed, b, g, 555]), d)
             v = rng.standard_normal((nn, d), dtype=np.float32)
             kb = bf16_bits(k)
             host_kv[b, g, :, 0, :] = kb
@@ -153,7 +172,7 @@ def make_decode_workload(cfg, seed=0, n=None, B=None, G=None, budget=None,
         qrng = np.random.default_rng([cid, seed, 777])
         q = bf16_bits(qrng.standard_normal((Bn, Hq, d), dtype=np.float32))
     p.update(tau=tau, host_kv=host_kv, sketch=sketch, proj=proj, q=q,
-             seed=seed, cfg=cfg)
+             seed=seed, cfg=cfg, pair_profile=pair_profile)
     return p
 
 
