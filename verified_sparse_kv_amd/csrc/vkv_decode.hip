@@ -133,6 +133,7 @@ struct DParams {
   RowState *rows;
   int nsub, rsub;    // kRowChunk sub-chunks per row, and per row workgroup
   int nsel;          // candidate workgroups per row
+  int nbeta;         // Newton launches of the beta* iteration (2 or 3)
   double *bpart;     // [2][row][nrc][kBetaRec] beta pass records
   float2 *band;      // [2][row][nrc][kBandChunk] (w~, rho) of band tokens
   BetaState *bstate; // [2][row]
@@ -1060,6 +1061,8 @@ constexpr int kSk2Group = 128;
 constexpr int kSk2Sub = 1024;              // tokens per scan sub-batch
 constexpr int kSk2Tok = kSk2Sub / kBlock;  // tokens per thread and sub-batch
 constexpr int kShortMax = 1024;            // largest shortlist
+constexpr int kShortKPT = 32;              // shortlist keys per thread and tile
+constexpr int kShortTile = kShortKPT * kPlanThreads;  // positions per tile
 
 // fp32 -> an unsigned key in the same order (0 is never produced for a
 // finite value, so it marks tokens that are not eligible).
@@ -1202,14 +1205,21 @@ __global__ __launch_bounds__(kPlanThreads) void dk_short(DParams p) {
   const int g = blockIdx.x, b = blockIdx.y;
   const int bg = b * p.G + g, n = p.n, tid = threadIdx.x;
   const int lane = tid % kWave;
-  __shared__ uint32_t s_res[kMaxTokens / 32];
+  constexpr int kWords = kMaxTokens / 32;
+  __shared__ uint32_t s_res[kWords];  // resident positions
+  __shared__ uint32_t s_sel[kWords];  // chosen positions
+  __shared__ uint32_t s_eq[kWords];   // positions with key == T (ties only)
   __shared__ uint32_t s_hist[kSelBinsP];
   __shared__ int s_list[kShortMax];
   __shared__ float s_q[GRP][kHeadDim];
   __shared__ uint32_t s_w[kPlanWaves];
-  __shared__ uint32_t s_pick[2];
+  __shared__ uint32_t s_pick[3];
   const int nw = (n + 31) / 32;
-  for (int w = tid; w < nw; w += kPlanThreads) s_res[w] = 0u;
+  for (int w = tid; w < nw; w += kPlanThreads) {
+    s_res[w] = 0u;
+    s_sel[w] = 0u;
+    s_eq[w] = 0u;
+  }
   for (int e = tid; e < GRP * kHeadDim; e += kPlanThreads) {
     const int h = e / kHeadDim, k = e % kHeadDim;
     s_q[h][k] = __uint_as_float(
@@ -1223,16 +1233,47 @@ __global__ __launch_bounds__(kPlanThreads) void dk_short(DParams p) {
     if (pos >= 0 && pos < n) atomicOr(&s_res[pos >> 5], 1u << (pos & 31));
   }
   __syncthreads();
+  // the keys in tiles of kShortKPT per thread (position tile * kShortTile +
+  // k * 1024 + tid), all loads of a tile in flight together; resident
+  // positions read as 0 (not eligible). One tile (n <= 32K) stays in
+  // registers for every pass.
   const uint32_t *keys = p.skey + (size_t)bg * n;
-  auto key_at = [&](int i) {
-    const uint32_t k = keys[i];
-    return ((s_res[i >> 5] >> (i & 31)) & 1u) ? 0u : k;
+  const int ntiles = (n + kShortTile - 1) / kShortTile;
+  uint32_t kr[kShortKPT];
+  auto load_tile = [&](int tile, uint32_t (&kk)[kShortKPT]) {
+#pragma unroll
+    for (int k = 0; k < kShortKPT; ++k) {
+      const int i = tile * kShortTile + k * kPlanThreads + tid;
+      kk[k] = i < n ? keys[i] : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < kShortKPT; ++k) {
+      const int i = tile * kShortTile + k * kPlanThreads + tid;
+      if (i < n && ((s_res[i >> 5] >> (i & 31)) & 1u)) kk[k] = 0u;
+    }
   };
-  // radix select: after the levels, the chosen tokens are those with key
-  // > T and the first `need` (by position) with key == T
-  uint32_t prefix = 0u, mask = 0u;
+  load_tile(0, kr);
+  // fn(position, key) for every position < n
+  auto for_keys = [&](auto fn) {
+    for (int tile = 0; tile < ntiles; ++tile) {
+      uint32_t kt[kShortKPT];
+      if (ntiles == 1) {
+#pragma unroll
+        for (int k = 0; k < kShortKPT; ++k) kt[k] = kr[k];
+      } else {
+        load_tile(tile, kt);
+      }
+#pragma unroll
+      for (int k = 0; k < kShortKPT; ++k) {
+        const int i = tile * kShortTile + k * kPlanThreads + tid;
+        if (i < n) fn(i, kt[k]);
+      }
+    }
+  };
+  // radix select: the chosen tokens are those with key > T and the first
+  // `need` (by position) of the `neq` tokens with key == T
+  uint32_t prefix = 0u, mask = 0u, T = 0xFFFFFFFFu, neq = 0u;
   int need = p.n_short;
-  uint32_t T = 0xFFFFFFFFu;
   if (need > 0) {
     bool all = false;
     for (int lvl = 0; lvl < 3; ++lvl) {
@@ -1241,13 +1282,12 @@ __global__ __launch_bounds__(kPlanThreads) void dk_short(DParams p) {
       const int nb = lvl == 2 ? 1 << 10 : 1 << 11;
       for (int e = tid; e < kSelBinsP; e += kPlanThreads) s_hist[e] = 0u;
       __syncthreads();
-      for (int i = tid; i < n; i += kPlanThreads) {
-        const uint32_t k = key_at(i);
+      for_keys([&](int, uint32_t k) {
         if (k != 0u && (k & mask) == prefix) atomicAdd(&s_hist[(k >> sh) & (nb - 1)], 1u);
-      }
+      });
       __syncthreads();
       if (tid < kWave) {
-        // lane l owns bins [l * per, (l + 1) * per); counts above each lane
+        // lane l owns bins [l * per, (l + 1) * per)
         const int per = nb / kWave;
         uint32_t own = 0u;
         for (int e = 0; e < per; ++e) own += s_hist[lane * per + e];
@@ -1264,6 +1304,7 @@ __global__ __launch_bounds__(kPlanThreads) void dk_short(DParams p) {
           if (lane == 0) {
             s_pick[0] = 0xFFFFFFFFu;  // every eligible token
             s_pick[1] = 0u;
+            s_pick[2] = 0u;
           }
         } else if (above < (uint32_t)need && (uint32_t)need <= suf) {
           uint32_t acc = above;
@@ -1277,11 +1318,12 @@ __global__ __launch_bounds__(kPlanThreads) void dk_short(DParams p) {
             acc += h;
           }
           s_pick[0] = (uint32_t)bin;
-          s_pick[1] = acc;  // keys above the bin
+          s_pick[1] = acc;                  // keys above the bin
+          s_pick[2] = s_hist[bin];          // keys in it
         }
       }
       __syncthreads();
-      const uint32_t bin = s_pick[0], acc = s_pick[1];
+      const uint32_t bin = s_pick[0], acc = s_pick[1], inbin = s_pick[2];
       __syncthreads();
       if (bin == 0xFFFFFFFFu) {
         all = true;
@@ -1290,6 +1332,7 @@ __global__ __launch_bounds__(kPlanThreads) void dk_short(DParams p) {
       prefix |= bin << sh;
       mask |= (uint32_t)(nb - 1) << sh;
       need -= (int)acc;
+      neq = inbin;  // after the last level: the keys equal to T
     }
     if (all) {
       T = 0u;
@@ -1298,28 +1341,47 @@ __global__ __launch_bounds__(kPlanThreads) void dk_short(DParams p) {
       T = prefix;
     }
   }
-  // positions in order: thread t takes [t * per, (t + 1) * per)
-  const int per = (n + kPlanThreads - 1) / kPlanThreads;
-  const int i0 = min(n, tid * per), i1 = min(n, i0 + per);
-  uint32_t neq = 0u;
-  for (int i = i0; i < i1; ++i) neq += key_at(i) == T ? 1u : 0u;
+  // mark the chosen positions; equal keys go to s_eq only when they do not
+  // all fit (then by position below)
+  const bool ties = need > 0 && neq > (uint32_t)need;
+  for_keys([&](int i, uint32_t k) {
+    if (k > T || (k == T && k != 0u && need > 0 && !ties))
+      atomicOr(&s_sel[i >> 5], 1u << (i & 31));
+    else if (ties && k == T)
+      atomicOr(&s_eq[i >> 5], 1u << (i & 31));
+  });
+  __syncthreads();
+  // thread t owns words [t * wpt, (t + 1) * wpt): positions in order
+  const int wpt = (nw + kPlanThreads - 1) / kPlanThreads;
+  const int w0 = min(nw, tid * wpt), w1 = min(nw, w0 + wpt);
   uint32_t tot;
-  const uint32_t er0 = plan_excl_scan(neq, s_w, &tot);  // equal keys before
-  auto chosen = [&](uint32_t k, uint32_t &er) {
-    if (k > T) return true;
-    return k == T && k != 0u && er++ < (uint32_t)need;
-  };
-  uint32_t nsel = 0u;
-  {
-    uint32_t er = er0;
-    for (int i = i0; i < i1; ++i) nsel += chosen(key_at(i), er) ? 1u : 0u;
+  if (ties) {  // (uniform)
+    uint32_t mine = 0u;
+    for (int w = w0; w < w1; ++w) mine += (uint32_t)__popc(s_eq[w]);
+    uint32_t rank = plan_excl_scan(mine, s_w, &tot);
+    for (int w = w0; w < w1; ++w) {
+      uint32_t x = s_eq[w], take = 0u;
+      while (x) {
+        const uint32_t bit = x & (0u - x);
+        if (rank++ < (uint32_t)need) take |= bit;
+        x &= x - 1u;
+      }
+      s_sel[w] |= take;  // (this thread's words only)
+    }
+    __syncthreads();
   }
+  uint32_t mine = 0u;
+  for (int w = w0; w < w1; ++w) mine += (uint32_t)__popc(s_sel[w]);
   uint32_t ns;
-  uint32_t slot = plan_excl_scan(nsel, s_w, &ns);
-  {
-    uint32_t er = er0;
-    for (int i = i0; i < i1; ++i)
-      if (chosen(key_at(i), er) && slot < (uint32_t)kShortMax) s_list[slot++] = i;
+  uint32_t slot = plan_excl_scan(mine, s_w, &ns);
+  for (int w = w0; w < w1; ++w) {
+    uint32_t x = s_sel[w];
+    while (x) {
+      const int bit = __ffs(x) - 1;
+      if (slot < (uint32_t)kShortMax) s_list[slot] = w * 32 + bit;
+      ++slot;
+      x &= x - 1u;
+    }
   }
   __syncthreads();
   ns = min(ns, (uint32_t)kShortMax);
@@ -1450,7 +1512,8 @@ __global__ __launch_bounds__(kBlock) void dk_p0(DParams p) {
 constexpr int kSelUnroll = 4;       // streamed tokens per thread in flight
 constexpr int kBetaPts = 4;         // points of h per Newton pass
 constexpr int kBetaRec = 3 * kBetaPts + 1;  // + the band count
-constexpr int kBetaLaunches = 2;    // Newton passes (pass 0 is in the scan)
+constexpr int kBetaLaunchMax = 4;   // Newton passes (pass 0 is in the scan):
+                                    // p.nbeta of them, 2 to 4
 constexpr int kBandChunk = 1024;    // band tokens a chunk may store
 constexpr int kBandMax = 2048;      // band tokens a row may be settled from
 constexpr int kMaxChunks = kMaxTokens / kRowChunk;
@@ -2613,7 +2676,7 @@ __global__ __launch_bounds__(kBlock) void dk_rcert(DParams p) {
   float w8[kRowTok], r8[kRowTok], s8[kRowTok];
   row_load(p, row, bg, cc0, r8, s8);
   const float m = p.rows[row].m;
-  const int q = kBetaLaunches & 1;
+  const int q = p.nbeta & 1;
   BetaState st = p.bstate[(size_t)q * rows + row];
   if (!st.done) {  // (uniform: the same state in every workgroup)
     double rv[kBetaRec];
@@ -3779,7 +3842,7 @@ template <int GRP>
 hipError_t run(const DParams &p, hipStream_t s, int sd, void **events) {
   const dim3 blk(kBlock);
   const dim3 gfront((unsigned)(p.nch + p.ncr), (unsigned)p.G, (unsigned)p.B);
-  constexpr int kPhases = 11;  // the entries of kPhaseNames
+  constexpr int kPhases = 13;  // the entries of kPhaseNames
   const PhaseMark mark(events, s, kPhases);
   const bool sk2 = p.weights == VKV_W_SKETCH2;
   int k = 0;
@@ -3808,8 +3871,11 @@ hipError_t run(const DParams &p, hipStream_t s, int sd, void **events) {
   mark(++k);
   const dim3 grow((unsigned)p.nrc, (unsigned)p.Hq, (unsigned)p.B);
   const dim3 gone((unsigned)p.Hq, (unsigned)p.B);
-  for (int j = 1; j <= kBetaLaunches; ++j) {
-    mark.launch(k, dk_rbeta<GRP>, grow, blk, p, j);
+  for (int j = 1; j <= kBetaLaunchMax; ++j) {
+    if (j <= p.nbeta)
+      mark.launch(k, dk_rbeta<GRP>, grow, blk, p, j);
+    else
+      mark.empty(k);
     mark(++k);
   }
   if (p.est == VKV_EST_BINARY)
@@ -3840,9 +3906,9 @@ hipError_t run(const DParams &p, hipStream_t s, int sd, void **events) {
 }
 
 const char *const kPhaseNames[] = {
-    "scan", "shortlist", "pass0", "beta1", "beta2", "shrink", "cert", "cand",
-    "walk", "fetch", "attn"};
-static_assert(sizeof(kPhaseNames) / sizeof(kPhaseNames[0]) == 11,
+    "scan", "shortlist", "pass0", "beta1", "beta2", "beta3", "beta4", "shrink",
+    "cert", "cand", "walk", "fetch", "attn"};
+static_assert(sizeof(kPhaseNames) / sizeof(kPhaseNames[0]) == 13,
               "one name per phase of run()");
 
 }  // namespace
@@ -4023,6 +4089,12 @@ hipError_t launch_decode(const vkv_decode_args &a, const DecodeLayout &L,
   p.a_delta = p.l_delta / 3.0;
   p.est = a.estimator;
   p.weights = a.weights;
+  // planning weights that are exact on the sample (and the shortlist) put
+  // far more tokens near the root after one Newton launch than the
+  // projected sketch's do (hundreds to tens of thousands against tens), so
+  // those modes take a third launch before the band settle
+  // (and contexts above 32K tokens one more again)
+  p.nbeta = (a.weights == VKV_W_SKETCH ? 2 : 3) + (a.n_tokens > 32768 ? 1 : 0);
   switch (L.grp) {
     case 1: return run<1>(p, s, a.sketch_dim, a.phase_events);
     case 2: return run<2>(p, s, a.sketch_dim, a.phase_events);
