@@ -91,12 +91,19 @@ enum { VKV_W_SKETCH = 0, VKV_W_PERFECT = 1, VKV_W_SKETCH2 = 2 };
 /*
  * PoissonComp over n_layers x n_kv_heads independent slices of n_tokens.
  *
- * tau      dev [n_layers][n_kv_heads][n_tokens] f32. Importance scores in [0,1]
+ * tau      dev [n_layers][n_kv_heads][ctx_stride] f32. Importance scores in [0,1]
  *          (section 4.1 maps other ranges through a softmax first; that is the
  *          caller's job). They are read on a 2^-32 grid and floored at one
  *          step, so every token gets r > 0; values outside [0,1] are clamped.
- * k, v     dev [n_layers][n_kv_heads][n_tokens][head_dim] bf16 prefill keys and
- *          values; may be NULL when resident_kv is NULL.
+ * k, v     [n_layers][n_kv_heads][n_tokens][head_dim] bf16 prefill keys and
+ *          values, in device memory or pinned host memory (hipHostMalloc);
+ *          may be NULL when resident_kv is NULL. Token t of slice i at
+ *          k + (i * ctx_stride + t) * kv_stride elements (so the interleaved
+ *          K/V rows of a decode cache, k = host_kv and v = host_kv + d with
+ *          kv_stride 2 d, compress again as they are).
+ * ctx_stride  positions per slice in tau, r and k/v (0: n_tokens; else
+ *          >= n_tokens). kv_stride  elements per token in k and v (0:
+ *          head_dim; else >= head_dim and a multiple of 8).
  * budget   expected number of GPU-resident rows per slice (eta * n rounded);
  *          it includes the forced sink/local tokens and must exceed their
  *          count (unless every token is forced).
@@ -105,7 +112,7 @@ enum { VKV_W_SKETCH = 0, VKV_W_PERFECT = 1, VKV_W_SKETCH2 = 2 };
  *          counter (token, head, layer0 + l, 0) so any slice can be redrawn
  *          alone.
  * cap      resident-row capacity per slice (>= 1).
- * Outputs (dev): r [n_layers][n_kv_heads][n_tokens] f32 (exactly 1.0 on H,
+ * Outputs (dev): r [n_layers][n_kv_heads][ctx_stride] f32 (exactly 1.0 on H,
  * below 1 on L); resident_idx [n_layers][n_kv_heads][cap] i32 ascending
  * positions of H u S; resident_count [n_layers][n_kv_heads] i32 (the true
  * count even when it exceeds cap; then only cap rows are written and the
@@ -120,6 +127,8 @@ enum { VKV_W_SKETCH = 0, VKV_W_PERFECT = 1, VKV_W_SKETCH2 = 2 };
 typedef struct {
   int32_t n_layers, n_kv_heads, n_tokens, head_dim;
   int32_t layer0;
+  int32_t ctx_stride;
+  int64_t kv_stride;
   const float *tau;
   const uint16_t *k;
   const uint16_t *v;
@@ -143,6 +152,10 @@ typedef struct {
  * Shapes: B = batch, Hq query heads over G KV heads (Hq/G in {1,2,4,8}),
  * head_dim d = 128, n tokens (1 <= n <= 2^17; larger n returns
  * VKV_EUNSUPPORTED), sketch_dim s in {16, 32}.
+ * ctx_stride   positions allocated per (request, KV head) in r, sketch,
+ *              sk2_codes, sk2_zs (ceil(ctx_stride / 128) groups) and
+ *              host_kv: 0 means n; otherwise n <= ctx_stride <= 2^24, so a
+ *              context can grow in place (vkv_append_token) between steps.
  * q            dev [B][Hq][d] bf16.
  * resident_kv  dev [B][G][cap][2][d] bf16 (rows of H u S, K then V), with
  * resident_idx dev [B][G][cap] i32 ascending positions and
@@ -157,6 +170,23 @@ typedef struct {
  *              otherwise ignored and may be NULL).
  * n_short      shortlist size per (request, KV head), 0..1024 (the pages
  *              use 128); VKV_W_SKETCH2 only.
+ * Reuse of rows staged in earlier steps ("Verify Before You Fetch",
+ * Appendix A.3.2, fetching: a device map keyed by (request, KV head,
+ * position) lets the fetch reuse rows staged before). All four may be NULL
+ * (no staging); the caller alternates two maps and two staging areas:
+ * stage_map_prev dev [B][G][ctx_stride] i32, read only: for each position,
+ *              its row's index in stage_prev, or -1 (as the previous step
+ *              left it in its stage_map_next; a map of -1 to start).
+ * stage_prev   dev [B][G][fetch_cap][2][d] bf16, read only: rows staged by
+ *              the previous step. A fetched row found there is read from
+ *              it instead of from host_kv (and not counted in host_bytes).
+ * stage_map_next, stage_next  the same for this step, written: every row
+ *              fetched this step is staged at its index in fetch_idx, and
+ *              the map holds that index (-1 elsewhere). Both pairs must be
+ *              given together; prev and next must not alias.
+ *              Staging assumes the positions and rows of the cache did not
+ *              change since the previous step (appending keeps them; a new
+ *              compression or a new request starts again from a map of -1).
  * eps, delta   tolerance (eps > 0, 0 < delta < 1) of the (eps, delta)
  *              guarantee on the attention denominator.
  * estimator    VKV_EST_CLIP, VKV_EST_UNBIASED or VKV_EST_BINARY; weights
@@ -191,6 +221,7 @@ typedef struct {
  */
 typedef struct {
   int32_t batch, n_q_heads, n_kv_heads, head_dim, n_tokens, sketch_dim, cap;
+  int32_t ctx_stride;
   const uint16_t *q;
   const uint16_t *resident_kv;
   const int32_t *resident_idx;
@@ -203,6 +234,10 @@ typedef struct {
   const uint16_t *sk2_zs;
   const int32_t *sk2_chan;
   int32_t n_short;
+  const int32_t *stage_map_prev;
+  const uint16_t *stage_prev;
+  int32_t *stage_map_next;
+  uint16_t *stage_next;
   float eps, delta;
   int32_t estimator, weights, fetch_cap;
   float *out;
@@ -265,19 +300,23 @@ typedef struct {
  * hold the code of kept channel c. Stored size: 8 bytes per token and
  * 128 bytes per group, 1.76% of the bf16 K/V cache.
  *
- * k         dev bf16 keys; token t of slice i at k + i * slice_stride +
+ * k         bf16 keys in device memory or device-accessible pinned host
+ *           memory; token t of slice i at k + i * slice_stride +
  *           t * key_stride (elements; key_stride >= head_dim, so K rows
  *           interleaved with V rows can be passed as they are).
- * codes     out dev [n_slices][n_tokens] u64.
- * zs        out dev [n_slices][ceil(n_tokens / 128)][2][32] fp16 bits: the
- *           group's 32 zero points, then its 32 scales.
+ * out_stride  positions per slice in codes and zs (0: n_tokens; else >=
+ *           n_tokens), so a capacity layout can be filled.
+ * codes     out dev [n_slices][out_stride] u64.
+ * zs        out dev [n_slices][ceil(out_stride / 128)][2][32] fp16 bits: the
+ *           group's 32 zero points, then its 32 scales (groups past the
+ *           context are left as they are).
  * chan      out dev [n_slices][32] i32.
  * Supported: head_dim = 128, 1 <= n_tokens <= 2^24, n_slices <= 65535.
  * The pair choice sums squares in float64; pairs whose energies agree to
  * rounding may be chosen either way.
  */
 typedef struct {
-  int32_t n_slices, n_tokens, head_dim;
+  int32_t n_slices, n_tokens, head_dim, out_stride;
   int64_t key_stride, slice_stride;
   const uint16_t *k;
   uint64_t *codes;
@@ -286,6 +325,54 @@ typedef struct {
   void *workspace;
   size_t workspace_bytes;
 } vkv_sketch2_args;
+
+/*
+ * Decode-time maintenance: one generated token joins every (request, KV
+ * head) at position pos ("Verify Before You Fetch", section 3: sinks and
+ * the local window stay resident; Appendix A.3.1: the per-(layer, head)
+ * list of resident positions is extended as tokens are generated and new
+ * tokens are written after the packed region). The token goes to H: its
+ * K/V row is written to host_kv at pos and appended to resident_kv at
+ * resident_count, pos is appended to resident_idx, resident_count grows by
+ * one and r[pos] = 1. When given, its projected sketch row is written
+ * (sketch = bf16(P_g^T k), round to nearest even, P_g^T k summed in fp32
+ * over increasing dimension) and its 2-bit code word is 0, with a group
+ * that starts at pos getting zero points and scales 0 (the sketch of a
+ * token of H is never used while it stays in H; a new compression
+ * rebuilds it). The next decode step then takes n_tokens = pos + 1.
+ *
+ * k_new, v_new  dev [B][G][d] bf16 rows of the new token.
+ * host_kv     host [B][G][ctx_stride][2][d] bf16, pinned (hipHostMalloc).
+ * resident_kv dev [B][G][cap][2][d]; resident_idx dev [B][G][cap];
+ *             resident_count dev [B][G] (updated in place).
+ * r           dev [B][G][ctx_stride] f32.
+ * sketch, proj  dev [B][G][ctx_stride][s] bf16 and [G][d][s] f32, or both
+ *             NULL; sk2_codes dev [B][G][ctx_stride] u64 and sk2_zs dev
+ *             [B][G][ceil(ctx_stride/128)][2][32], or both NULL.
+ * status      dev u32 [1]: VKV_STATUS_RESIDENT_OVERFLOW when a list is at
+ *             cap (that list is left as it is), VKV_STATUS_BAD_RESIDENT
+ *             when pos does not exceed the list's last position.
+ * Requires 0 <= pos < ctx_stride <= 2^24; not cleared: bits accumulate
+ * until the caller clears the word.
+ */
+typedef struct {
+  int32_t batch, n_kv_heads, head_dim, pos, cap, ctx_stride, sketch_dim;
+  const uint16_t *k_new;
+  const uint16_t *v_new;
+  uint16_t *host_kv;
+  uint16_t *resident_kv;
+  int32_t *resident_idx;
+  int32_t *resident_count;
+  float *r;
+  uint16_t *sketch;
+  const float *proj;
+  uint64_t *sk2_codes;
+  uint16_t *sk2_zs;
+  uint32_t *status;
+} vkv_append_args;
+
+/* Enqueue one token's append (see vkv_append_args). */
+vkv_status vkv_append_token(const vkv_append_args *a, void *stream);
 
 /* Workspace sizes in bytes for these arguments (0 if the shapes are invalid). */
 size_t vkv_compress_workspace_bytes(const vkv_compress_args *a);

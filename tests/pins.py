@@ -670,3 +670,67 @@ def check_sketch2_full_shortlist(seed):
     assert any(h["k_star"] > 0 for h in ha)
     n_nonres = int(np.sum((t["r"] < 1)) - samp.size)
     assert ha[0]["shortlist"].size == n_nonres
+
+
+# ---------------------------------------------------------------- maintenance
+# "Verify Before You Fetch", section 3 and Appendix A.3.1-A.3.2.
+
+def check_append_invariants(seed, B=2, G=3, ns=40, n=25, d=128, s=16):
+    """After appending tokens: every resident list stays ascending and ends
+    at the new position, counts grow by one, r = 1 there, the host row is
+    the new K/V, and the projected sketch row is within one bf16 rounding
+    of P^T k evaluated in float64."""
+    from oracle import maintain as om
+    rng = np.random.default_rng(seed)
+    hkv = rng.integers(0, 2 ** 15, (B, G, ns, 2, d)).astype(np.uint16)
+    r = rng.uniform(0.1, 0.9, (B, G, ns)).astype(np.float32)
+    res_idx = [[np.sort(rng.choice(n, 6, replace=False)).astype(np.int64)
+                for _ in range(G)] for _ in range(B)]
+    res_kv = [[hkv[b, g, res_idx[b][g]] for g in range(G)] for b in range(B)]
+    proj = (rng.standard_normal((G, d, s)) / np.sqrt(s)).astype(np.float32)
+    st = dict(host_kv=hkv, r=r, res_idx=res_idx, res_kv=res_kv,
+              sketch=np.zeros((B, G, ns, s), dtype=np.uint16))
+    for pos in (n, n + 1, n + 2):
+        kf = rng.standard_normal((B, G, d)).astype(np.float32)
+        k_new = om.bf16_rne(kf)
+        v_new = om.bf16_rne(rng.standard_normal((B, G, d)).astype(np.float32))
+        before = [[st["res_idx"][b][g].size for g in range(G)] for b in range(B)]
+        om.append_token(st, pos, k_new, v_new, proj)
+        for b in range(B):
+            for g in range(G):
+                idx = st["res_idx"][b][g]
+                assert idx.size == before[b][g] + 1 and idx[-1] == pos
+                assert np.all(np.diff(idx) > 0)
+                assert np.array_equal(st["res_kv"][b][g][-1, 0], k_new[b, g])
+                assert np.array_equal(st["res_kv"][b][g][-1, 1], v_new[b, g])
+                assert st["r"][b, g, pos] == 1.0
+                assert np.array_equal(st["host_kv"][b, g, pos, 0], k_new[b, g])
+                k64 = (k_new[b, g].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+                exact = proj[g].astype(np.float64).T @ k64
+                got = (st["sketch"][b, g, pos].astype(np.uint32) << 16).view(np.float32)
+                # bf16 keeps 8 significant bits: within 2^-8 relative, plus
+                # the fp32 sum's rounding
+                assert np.all(np.abs(got - exact) <= 2.0 ** -8 * np.abs(exact) + 1e-5)
+    # appending out of order is refused
+    try:
+        om.append_token(st, n, k_new, v_new, proj)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("out-of-order append accepted")
+
+
+def check_staged_hits(seed):
+    """Staged rows: the hits are exactly the rows in both unions, so the
+    host bytes of a step with staging plus the saved bytes equal those of
+    the same step without it."""
+    from oracle import maintain as om
+    rng = np.random.default_rng(seed)
+    a = np.sort(rng.choice(1000, 120, replace=False))
+    b = np.sort(rng.choice(1000, 150, replace=False))
+    hits = om.staged_hits(a, b)
+    assert set(hits.tolist()) == set(a.tolist()) & set(b.tolist())
+    miss = np.setdiff1d(b, hits)
+    assert miss.size * 512 + hits.size * 512 == b.size * 512
+    assert om.staged_hits(a, a).size == a.size
+    assert om.staged_hits(a, np.zeros(0, dtype=np.int64)).size == 0

@@ -54,7 +54,8 @@ def _c_layout(struct, fields):
 @pytest.mark.parametrize("cls,cname", [(vk.CompressArgs, "vkv_compress_args"),
                                        (vk.DecodeArgs, "vkv_decode_args"),
                                        (vk.DenseArgs, "vkv_dense_args"),
-                                       (vk.Sketch2Args, "vkv_sketch2_args")])
+                                       (vk.Sketch2Args, "vkv_sketch2_args"),
+                                       (vk.AppendArgs, "vkv_append_args")])
 def test_struct_layout_matches_c(cls, cname):
     fields = [f for f, _ in cls._fields_]
     size, offs = _c_layout(cname, fields)
@@ -118,6 +119,9 @@ def test_workspace_sizes():
     (dict(tau=None), vk.VKV_EINVAL, "required"),
     (dict(resident_kv=ctypes.c_void_p(0x1000)), vk.VKV_EINVAL, "k and v"),
     (dict(workspace=None), vk.VKV_EINVAL, "workspace"),
+    (dict(ctx_stride=4999), vk.VKV_EINVAL, "ctx_stride"),
+    (dict(kv_stride=100), vk.VKV_EINVAL, "kv_stride"),
+    (dict(kv_stride=132), vk.VKV_EINVAL, "kv_stride"),
 ])
 def test_compress_validation(kw, code, frag):
     a = _compress_args(**kw)
@@ -148,6 +152,12 @@ def test_compress_validation(kw, code, frag):
     (dict(k_star=None), vk.VKV_EINVAL, "output"),
     (dict(host_kv=None), vk.VKV_EINVAL, "required"),
     (dict(weights=2), vk.VKV_EINVAL, "sk2_codes"),
+    (dict(ctx_stride=4095), vk.VKV_EINVAL, "ctx_stride"),
+    (dict(stage_map_prev=ctypes.c_void_p(0x1000)), vk.VKV_EINVAL, "pairs"),
+    (dict(stage_map_next=ctypes.c_void_p(0x1000)), vk.VKV_EINVAL, "pairs"),
+    (dict(stage_map_prev=ctypes.c_void_p(0x1000), stage_prev=ctypes.c_void_p(0x2000),
+          stage_map_next=ctypes.c_void_p(0x1000), stage_next=ctypes.c_void_p(0x3000)),
+     vk.VKV_EINVAL, "alias"),
     (dict(weights=2, sk2_codes=ctypes.c_void_p(0x1000), sk2_zs=ctypes.c_void_p(0x1000),
           sk2_chan=ctypes.c_void_p(0x1000), n_short=1025), vk.VKV_EINVAL, "n_short"),
     (dict(weights=2, sk2_codes=ctypes.c_void_p(0x1000), sk2_zs=ctypes.c_void_p(0x1000),
@@ -288,3 +298,44 @@ def test_sketch2_validation(kw, frag):
     assert vk.vkv_sketch2_build(a, None) == vk.VKV_EINVAL
     msg = vk.vkv_last_error()
     assert frag in msg, msg
+
+
+def _append_args(**kw):
+    a = vk.AppendArgs(batch=2, n_kv_heads=8, head_dim=128, pos=100, cap=64,
+                      ctx_stride=200, sketch_dim=0)
+    fake = ctypes.c_void_p(0x1000)
+    for f in ("k_new", "v_new", "host_kv", "resident_kv", "resident_idx",
+              "resident_count", "r", "status"):
+        setattr(a, f, fake)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(batch=0), "batch"),
+    (dict(head_dim=64), "head_dim"),
+    (dict(ctx_stride=0), "ctx_stride"),
+    (dict(pos=200), "pos"),
+    (dict(pos=-1), "pos"),
+    (dict(cap=0), "cap"),
+    (dict(r=None), "required"),
+    (dict(sketch=ctypes.c_void_p(0x1000)), "together"),
+    (dict(sketch=ctypes.c_void_p(0x1000), proj=ctypes.c_void_p(0x1000),
+          sketch_dim=24), "sketch_dim"),
+    (dict(sk2_codes=ctypes.c_void_p(0x1000)), "together"),
+])
+def test_append_validation(kw, frag):
+    a = _append_args(**kw)
+    assert vk.vkv_append_token(a, None) == vk.VKV_EINVAL
+    msg = vk.vkv_last_error()
+    assert frag in msg, msg
+
+
+def test_append_needs_pinned_host_cache():
+    """Valid arguments with a host_kv that is not pinned memory: refused
+    before any launch."""
+    import numpy as np
+    buf = np.zeros(16, dtype=np.uint16)
+    a = _append_args(host_kv=ctypes.c_void_p(buf.ctypes.data))
+    assert vk.vkv_append_token(a, None) == vk.VKV_ENOTPINNED

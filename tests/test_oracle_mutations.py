@@ -9,6 +9,7 @@ import pytest
 from oracle import compress as oc
 from oracle import decode as od
 from oracle import philox
+from oracle import maintain as om
 from oracle import sketch2 as sk2
 from tests import pins
 
@@ -78,6 +79,8 @@ def run_pins():
     attempt("sketch2_identity", lambda: pins.check_sketch2_logit_identity(21))
     attempt("shortlist", lambda: pins.check_shortlist_bruteforce(22))
     attempt("sketch2_full", lambda: pins.check_sketch2_full_shortlist(23))
+    attempt("append", lambda: pins.check_append_invariants(24))
+    attempt("staged", lambda: pins.check_staged_hits(25))
     return failed
 
 
@@ -348,6 +351,21 @@ def _energy_sum_abs(keys):
     return k[:, :h].sum(axis=0) + k[:, h:].sum(axis=0) * 0.0
 
 
+def _bf16_truncate(x):
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    return (u >> 16).astype(np.uint16)
+
+
+def _hits_union(prev_union, union):
+    return np.union1d(np.asarray(prev_union), np.asarray(union)).astype(np.int64)
+
+
+def _sketch_row_fp16(proj_g, k):
+    # the sum kept in half precision
+    acc = (np.asarray(proj_g, dtype=np.float16).T @ np.asarray(k, dtype=np.float16))
+    return om.bf16_rne(acc.astype(np.float32))
+
+
 _orig_quant = sk2.quantize_group
 _orig_sk2_logits = sk2.sketch_logits
 _orig_shortlist = sk2.shortlist
@@ -409,6 +427,9 @@ MUTATIONS = [
     ("shortlist of the lowest scores", sk2, "shortlist", _shortlist_smallest),
     ("pair energy from one channel of the pair", sk2, "pair_energy",
      _energy_sum_abs),
+    ("appended sketch row truncated to bf16", om, "bf16_rne", _bf16_truncate),
+    ("appended sketch row summed in fp16", om, "sketch_row", _sketch_row_fp16),
+    ("staged hits taken as the union", om, "staged_hits", _hits_union),
 ]
 
 

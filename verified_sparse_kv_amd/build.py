@@ -10,7 +10,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libverkv.so")
 SOURCES = ["vkv_api.hip", "vkv_compress.hip", "vkv_decode.hip", "vkv_dense.hip",
-           "vkv_sketch2.hip"]
+           "vkv_sketch2.hip", "vkv_maint.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -50,6 +50,10 @@ vkv_status check_compress_shapes(const vkv_compress_args *a) {
   REQUIRE(a->n_sink >= 0 && a->n_local >= 0,
           "compress: n_sink and n_local must be >= 0");
   REQUIRE(a->cap >= 1, "compress: cap must be >= 1");
+  REQUIRE(a->ctx_stride == 0 || (a->ctx_stride >= a->n_tokens && a->ctx_stride <= (1 << 24)),
+          "compress: ctx_stride must be 0 or in [n_tokens, 2^24]");
+  REQUIRE(a->kv_stride == 0 || (a->kv_stride >= a->head_dim && a->kv_stride % 8 == 0),
+          "compress: kv_stride must be 0 or >= head_dim and a multiple of 8");
   return VKV_OK;
 }
 
@@ -91,6 +95,8 @@ vkv_status check_decode_shapes(const vkv_decode_args *a) {
   REQUIRE(a->cap >= 1, "decode: cap must be >= 1");
   REQUIRE(a->fetch_cap >= 1 && a->fetch_cap <= a->n_tokens,
           "decode: fetch_cap must be in [1, n_tokens]");
+  REQUIRE(a->ctx_stride == 0 || (a->ctx_stride >= a->n_tokens && a->ctx_stride <= (1 << 24)),
+          "decode: ctx_stride must be 0 or in [n_tokens, 2^24]");
   return VKV_OK;
 }
 
@@ -151,7 +157,34 @@ vkv_status check_decode_args(const vkv_decode_args *a) {
   REQUIRE(a->out && a->d_hat && a->log_shift && a->eps_hat0 && a->eps_hat &&
               a->k_star && a->fetch_idx && a->fetch_count && a->host_bytes && a->status,
           "decode: every output pointer except row_stats and row_path is required");
+  REQUIRE((a->stage_map_prev == nullptr) == (a->stage_prev == nullptr) &&
+              (a->stage_map_next == nullptr) == (a->stage_next == nullptr),
+          "decode: stage_map_prev/stage_prev and stage_map_next/stage_next are given in pairs");
+  REQUIRE(a->stage_prev == nullptr ||
+              (a->stage_prev != a->stage_next && a->stage_map_prev != a->stage_map_next),
+          "decode: the previous and next staging must not alias");
   return VKV_OK;
+}
+
+// A device-readable address for p: device memory as it is, pinned host
+// memory (hipHostMalloc) through its device view. Anything else fails.
+bool device_view(const void *p, const void **dev) {
+  hipPointerAttribute_t attr;
+  const hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  if (attr.type == hipMemoryTypeDevice) {
+    *dev = p;
+    return true;
+  }
+  if (attr.type == hipMemoryTypeHost && attr.devicePointer && attr.hostPointer) {
+    *dev = static_cast<const char *>(attr.devicePointer) +
+           (static_cast<const char *>(p) - static_cast<const char *>(attr.hostPointer));
+    return true;
+  }
+  return false;
 }
 
 vkv_status check_sketch2_args(const vkv_sketch2_args *a) {
@@ -163,6 +196,31 @@ vkv_status check_sketch2_args(const vkv_sketch2_args *a) {
           "sketch2: key_stride must be >= head_dim and a multiple of 8");
   REQUIRE(a->slice_stride >= 0 && a->slice_stride % 8 == 0,
           "sketch2: slice_stride must be >= 0 and a multiple of 8");
+  REQUIRE(a->out_stride == 0 || (a->out_stride >= a->n_tokens && a->out_stride <= (1 << 24)),
+          "sketch2: out_stride must be 0 or in [n_tokens, 2^24]");
+  return VKV_OK;
+}
+
+vkv_status check_append_args(const vkv_append_args *a) {
+  REQUIRE(a != nullptr, "append: args is NULL");
+  REQUIRE(a->batch >= 1 && a->batch <= 65535 && a->n_kv_heads >= 1 &&
+              a->n_kv_heads <= 65535,
+          "append: batch and n_kv_heads must be in [1, 65535]");
+  REQUIRE(a->head_dim == vkv::kHeadDim, "append: head_dim must be 128");
+  REQUIRE(a->ctx_stride >= 1 && a->ctx_stride <= (1 << 24),
+          "append: ctx_stride must be in [1, 2^24]");
+  REQUIRE(a->pos >= 0 && a->pos < a->ctx_stride, "append: pos must be in [0, ctx_stride)");
+  REQUIRE(a->cap >= 1, "append: cap must be >= 1");
+  REQUIRE(a->k_new && a->v_new && a->host_kv && a->resident_kv && a->resident_idx &&
+              a->resident_count && a->r && a->status,
+          "append: k_new, v_new, host_kv, resident_kv, resident_idx, "
+          "resident_count, r and status are required");
+  REQUIRE((a->sketch == nullptr) == (a->proj == nullptr),
+          "append: sketch and proj are given together");
+  REQUIRE(a->sketch == nullptr || a->sketch_dim == 16 || a->sketch_dim == 32,
+          "append: sketch_dim must be 16 or 32 with a sketch");
+  REQUIRE((a->sk2_codes == nullptr) == (a->sk2_zs == nullptr),
+          "append: sk2_codes and sk2_zs are given together");
   return VKV_OK;
 }
 
@@ -222,7 +280,12 @@ vkv_status vkv_sketch2_build(const vkv_sketch2_args *a, void *stream) {
   const vkv::Sketch2Layout L = vkv::sketch2_layout(*a);
   REQUIRE(a->workspace != nullptr && a->workspace_bytes >= L.total,
           "sketch2: workspace of %zu bytes needed", L.total);
-  const hipError_t e = vkv::launch_sketch2(*a, L, static_cast<hipStream_t>(stream));
+  vkv_sketch2_args b = *a;
+  const void *kd = nullptr;
+  if (!device_view(a->k, &kd))
+    return fail(VKV_ENOTPINNED, "sketch2: k is neither device memory nor pinned host memory");
+  b.k = static_cast<const uint16_t *>(kd);
+  const hipError_t e = vkv::launch_sketch2(b, L, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "sketch2 launch");
   return VKV_OK;
 }
@@ -250,7 +313,16 @@ vkv_status vkv_compress(const vkv_compress_args *a, void *stream) {
   const vkv::CompressLayout L = vkv::compress_layout(*a);
   REQUIRE(a->workspace != nullptr && a->workspace_bytes >= L.total,
           "compress: workspace of %zu bytes needed", L.total);
-  const hipError_t e = vkv::launch_compress(*a, L, b_free, (int32_t)nf,
+  vkv_compress_args b = *a;
+  if (a->resident_kv) {  // k and v: device memory or pinned host memory
+    const void *kd = nullptr, *vd = nullptr;
+    if (!device_view(a->k, &kd) || !device_view(a->v, &vd))
+      return fail(VKV_ENOTPINNED,
+                  "compress: k and v must be device memory or pinned host memory");
+    b.k = static_cast<const uint16_t *>(kd);
+    b.v = static_cast<const uint16_t *>(vd);
+  }
+  const hipError_t e = vkv::launch_compress(b, L, b_free, (int32_t)nf,
                                             static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "compress launch");
   return VKV_OK;
@@ -282,6 +354,21 @@ vkv_status vkv_decode_step_noalloc(const vkv_decode_args *a, void *stream) {
   st = scratch_for_current_device(&ws);
   if (st != VKV_OK) return st;
   return decode_launch(a, L, ws, stream);
+}
+
+vkv_status vkv_append_token(const vkv_append_args *a, void *stream) {
+  vkv_status st = check_append_args(a);
+  if (st != VKV_OK) return st;
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, a->host_kv);
+  if (e != hipSuccess || attr.type != hipMemoryTypeHost || attr.devicePointer == nullptr) {
+    (void)hipGetLastError();
+    return fail(VKV_ENOTPINNED, "append: host_kv is not device-accessible pinned host memory");
+  }
+  e = vkv::launch_append(*a, static_cast<uint16_t *>(attr.devicePointer),
+                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return VKV_OK;
 }
 
 vkv_status vkv_dense_attention(const vkv_dense_args *a, void *stream) {

@@ -39,6 +39,7 @@ struct CParams {
   uint32_t *ccnt;
   uint32_t *bits;
   int n, n_heads, n_sink, n_local, cap, layer0, ncc, nwords;
+  int64_t ns, kvs;  // positions per slice in tau, r, k, v; elements per token in k, v
   int64_t b_free;
   uint32_t seed_lo, seed_hi;
 };
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(kBlock) void ck_hist(CParams p, int level) {
   const int hshift = shift + 11;
   const uint64_t lo = st->lo;
   const uint64_t pref = lo >> hshift;
-  const float *tau = p.tau + (size_t)slice * p.n;
+  const float *tau = p.tau + (size_t)slice * p.ns;
   const int base = chunk * kCompChunk;
   // the thread's scores first, all in flight together (indices past the
   // slice read its last score, which is not used)
@@ -216,8 +217,8 @@ __global__ __launch_bounds__(kBlock) void ck_rate(CParams p) {
   const uint64_t num = st->num, den = st->den;
   const bool all_sat = st->all_sat != 0;
   const double dden = (double)den;
-  const float *tau = p.tau + (size_t)slice * p.n;
-  float *rr = p.r + (size_t)slice * p.n;
+  const float *tau = p.tau + (size_t)slice * p.ns;
+  float *rr = p.r + (size_t)slice * p.ns;
   uint32_t *bits = p.bits + (size_t)slice * p.nwords;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int base = chunk * kCompChunk;
@@ -302,7 +303,7 @@ __global__ __launch_bounds__(kBlock) void ck_compact(CParams p) {
       if (slot >= (uint32_t)p.cap) continue;
       const size_t pos = (size_t)s_pos[row];
       const uint16_t *src = (part < 16 ? p.k : p.v) +
-                            ((size_t)slice * p.n + pos) * kHeadDim +
+                            ((size_t)slice * p.ns + pos) * p.kvs +
                             (part & 15u) * 8;
       uint16_t *dst = p.rkv + ((size_t)slice * p.cap + slot) * (2 * kHeadDim) +
                       part * 8;
@@ -352,6 +353,8 @@ hipError_t launch_compress(const vkv_compress_args &a, const CompressLayout &L,
   p.ccnt = at<uint32_t>(a.workspace, L.ccnt);
   p.bits = at<uint32_t>(a.workspace, L.bits);
   p.n = a.n_tokens;
+  p.ns = a.ctx_stride > 0 ? a.ctx_stride : a.n_tokens;
+  p.kvs = a.kv_stride > 0 ? a.kv_stride : kHeadDim;
   p.n_heads = a.n_kv_heads;
   p.n_sink = a.n_sink;
   p.n_local = a.n_local;

@@ -133,7 +133,14 @@ struct DParams {
   RowState *rows;
   int nsub, rsub;    // kRowChunk sub-chunks per row, and per row workgroup
   int nsel;          // candidate workgroups per row
-  int nbeta;         // Newton launches of the beta* iteration (2 or 3)
+  int nbeta;         // Newton launches of the beta* iteration (2 to 4)
+  int ns;            // positions per (request, KV head) in r, the sketches
+                     // and host_kv (>= n)
+  // rows staged by the previous step and by this one (NULL: none)
+  const int32_t *smap_prev;
+  const uint16_t *stage_prev;
+  int32_t *smap_next;
+  uint16_t *stage_next;
   double *bpart;     // [2][row][nrc][kBetaRec] beta pass records
   float2 *band;      // [2][row][nrc][kBandChunk] (w~, rho) of band tokens
   BetaState *bstate; // [2][row]
@@ -612,6 +619,11 @@ __device__ __forceinline__ void scan_setup(const DParams &p, int c, int g,
     }
   }
   clear_bin_hist<GRP>(p, c, b, g);
+  if (p.smap_next) {  // this step's staging map starts empty
+    const int i1 = min((c + 1) * p.chunk, p.n);
+    for (int i = c * p.chunk + (int)threadIdx.x; i < i1; i += kBlock)
+      p.smap_next[(size_t)bg * p.ns + i] = -1;
+  }
   const int w0 = c * p.chunk / 32, nw = p.chunk / 32;
   for (int w = threadIdx.x; w < nw; w += kBlock) {
     if (w0 + w < p.nwords) {
@@ -636,8 +648,8 @@ __device__ __forceinline__ void scan_body(const DParams &p, int c, int g,
   __shared__ float s_qp[GRP][SD];
   // the chunk's sketch rows and r first, all in flight while q is projected
   const int u = lane % LPT;
-  const uint16_t *sk = p.sketch + (size_t)bg * p.n * SD;
-  const float *rr = p.r + (size_t)bg * p.n;
+  const uint16_t *sk = p.sketch + (size_t)bg * p.ns * SD;
+  const float *rr = p.r + (size_t)bg * p.ns;
   const int base = c * p.chunk;
   const int lim = min(base + p.chunk, p.n);
   // sub-batches of SUB tokens, UNR per thread (LPT lanes per token); the
@@ -767,32 +779,7 @@ __device__ __forceinline__ void scan_exact_body(const DParams &p, int c,
                                                 int g, int b) {
   const int bg = b * p.G + g;
   const int lane = threadIdx.x % kWave;
-  if (c == 0) {
-    for (int h = 0; h < GRP; ++h) {
-      const int row = row_of(p, b, g, h, GRP);
-      if (threadIdx.x == 0) {
-        RowState z{};
-        z.amax = -1;
-        z.T = ~0ull;
-        p.rows[row] = z;
-      }
-    }
-    if (bg == 0 && threadIdx.x == 0) {
-      *p.status = 0u;
-      *p.host_bytes = 0ull;
-    }
-  }
-  clear_bin_hist<GRP>(p, c, b, g);
-  {
-    const int w0 = c * p.chunk / 32, nw = p.chunk / 32;
-    for (int w = threadIdx.x; w < nw; w += kBlock) {
-      if (w0 + w < p.nwords) {
-        p.fbits[(size_t)bg * p.nwords + w0 + w] = 0u;
-        for (int h = 0; h < GRP; ++h)
-          p.hbits[(size_t)row_of(p, b, g, h, GRP) * p.nwords + w0 + w] = 0u;
-      }
-    }
-  }
+  scan_setup<GRP>(p, c, g, b);
   const int u = lane % 16;
   float qv[GRP][8];
 #pragma unroll
@@ -806,7 +793,7 @@ __device__ __forceinline__ void scan_exact_body(const DParams &p, int c,
   for (int h = 0; h < GRP; ++h) p0_init(acc[h]);
   uint32_t n_h = 0;
   bool bad = false;
-  const float *rr = p.r + (size_t)bg * p.n;
+  const float *rr = p.r + (size_t)bg * p.ns;
   const int base = c * p.chunk;
   const int lim = min(base + p.chunk, p.n);
   for (int i0 = base; i0 < lim; i0 += kBlock / 16) {
@@ -819,7 +806,7 @@ __device__ __forceinline__ void scan_exact_body(const DParams &p, int c,
       float dot[GRP];
       if (in_l) {
         const uint4 raw = *reinterpret_cast<const uint4 *>(
-            p.host_kv + ((size_t)bg * p.n + i) * 2 * kHeadDim + u * 8);
+            p.host_kv + ((size_t)bg * p.ns + i) * 2 * kHeadDim + u * 8);
         float f[8];
         unpack8(raw, f);
 #pragma unroll
@@ -905,7 +892,7 @@ __device__ __forceinline__ void resident_body(const DParams &p, int c, int g,
   bool bad = cnt < 0 || cnt > p.cap;
   cnt = max(0, min(cnt, p.cap));
   const int32_t *ridx = p.ridx + (size_t)bg * p.cap;
-  const float *rr = p.r + (size_t)bg * p.n;
+  const float *rr = p.r + (size_t)bg * p.ns;
   const int hl = li < GRP ? li : 0;  // this lane's head (lanes li >= GRP idle)
   float mx = -INFINITY, hm = -INFINITY;  // this lane's head: max, H shift
   double hsum = 0.0;
@@ -1083,12 +1070,12 @@ __device__ __forceinline__ void scan2_body(const DParams &p, int c, int g,
                                            int b) {
   const int bg = b * p.G + g;
   const int base = c * p.chunk, lim = min(base + p.chunk, p.n);
-  const int ngrp = (p.n + kSk2Group - 1) / kSk2Group;
+  const int ngrp = (p.ns + kSk2Group - 1) / kSk2Group;
   __shared__ float s_q[GRP][kSk2Chan];
   __shared__ float s_u[kSk2Sub / kSk2Group][kSk2Chan][GRP];
   __shared__ float s_a[kSk2Sub / kSk2Group][GRP];
-  const unsigned long long *codes = p.sk2_codes + (size_t)bg * p.n;
-  const float *rr = p.r + (size_t)bg * p.n;
+  const unsigned long long *codes = p.sk2_codes + (size_t)bg * p.ns;
+  const float *rr = p.r + (size_t)bg * p.ns;
   unsigned long long wv[kSk2Tok];
   float rv[kSk2Tok];
   auto load = [&](int sb, unsigned long long (&w)[kSk2Tok], float (&r)[kSk2Tok]) {
@@ -1401,7 +1388,7 @@ __global__ __launch_bounds__(kPlanThreads) void dk_short(DParams p) {
       uint4 w0 = make_uint4(0u, 0u, 0u, 0u), w1 = w0;
       if (ok) {
         const uint4 *src = reinterpret_cast<const uint4 *>(
-            hk + ((size_t)bg * n + pos) * 2 * kHeadDim + part * 16);
+            hk + ((size_t)bg * p.ns + pos) * 2 * kHeadDim + part * 16);
         w0 = src[0];
         w1 = src[1];
       }
@@ -1418,7 +1405,7 @@ __global__ __launch_bounds__(kPlanThreads) void dk_short(DParams p) {
     }
   }
   // exact logits of S
-  const float *rr = p.r + (size_t)bg * n;
+  const float *rr = p.r + (size_t)bg * p.ns;
   for (int j = tid; j < cnt; j += kPlanThreads) {
     const int pos = ridx[j];
     if (pos < 0 || pos >= n || !(rr[pos] < 1.0f)) continue;
@@ -1438,7 +1425,7 @@ __global__ __launch_bounds__(kBlock) void dk_p0(DParams p) {
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int bg = b * p.G + g;
   const int base = c * p.chunk, lim = min(base + p.chunk, p.n);
-  const float *rr = p.r + (size_t)bg * p.n;
+  const float *rr = p.r + (size_t)bg * p.ns;
   P0Acc acc[GRP];
 #pragma unroll
   for (int h = 0; h < GRP; ++h) p0_init(acc[h]);
@@ -1549,7 +1536,7 @@ struct SelArgs {
   uint32_t *fbits, *hbits;
   double a_delta, l_delta;
   float eps;
-  int n, nwords, est;
+  int n, ns, nwords, est;  // (ns: positions per KV head in r)
 };
 
 __device__ __attribute__((noinline)) void select_row(const SelArgs p, int row,
@@ -1563,7 +1550,7 @@ __device__ __attribute__((noinline)) void select_row(const SelArgs p, int row,
   __shared__ unsigned long long s_lo;  // the resolved lower key bound
   __shared__ int s_more;               // another count level is needed
   __shared__ int s_j[kPlanWaves];
-  const float *rr = p.r + (size_t)bg * n;
+  const float *rr = p.r + (size_t)bg * p.ns;
   const float *sh = p.shat + (size_t)row * n;
   const float m = rs.m;
   const LamRule lr = lam_rule((float)rs.beta, p.est, rs.bkey);
@@ -1879,7 +1866,7 @@ __device__ __attribute__((noinline)) void select_row(const SelArgs p, int row,
 __device__ __forceinline__ void row_load(const DParams &p, int row, int bg,
                                          int c, float (&r8)[kRowTok],
                                          float (&s8)[kRowTok]) {
-  const float *rr = p.r + (size_t)bg * p.n;
+  const float *rr = p.r + (size_t)bg * p.ns;
   const float *sh = p.shat + (size_t)row * p.n;
 #pragma unroll
   for (int u = 0; u < kRowTok; ++u) {
@@ -2381,7 +2368,7 @@ __global__ __launch_bounds__(kBlock) void dk_rbeta(DParams p, int pass) {
     uint32_t k = block_exclusive_scan<uint32_t>((uint32_t)__popcll(bmask), s_bs, &nband);
     if (nband <= (uint32_t)kBandChunk) {
       float2 *bdst = p.band + (((size_t)(pass & 1) * rows + row) * p.nrc + c) * kBandChunk;
-      const float *rr = p.r + (size_t)bg * p.n;
+      const float *rr = p.r + (size_t)bg * p.ns;
       const float *sh = p.shat + (size_t)row * p.n;
       while (bmask) {
         const int bit = __ffsll((long long)bmask) - 1;
@@ -2423,7 +2410,7 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rbin(DParams p) {
   const int hq = blockIdx.x, b = blockIdx.y;
   const int row = b * p.Hq + hq, bg = b * p.G + hq / GRP;
   const int n = p.n;
-  const float *rr = p.r + (size_t)bg * n;
+  const float *rr = p.r + (size_t)bg * p.ns;
   const float *sh = p.shat + (size_t)row * n;
   const float m = p.rows[row].m;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
@@ -2847,7 +2834,7 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
   __shared__ uint32_t s_hist[kSelBinsP];
   __shared__ int s_j0, s_j1;
   __shared__ uint32_t s_c0;
-  const float *rr = p.r + (size_t)bg * p.n;
+  const float *rr = p.r + (size_t)bg * p.ns;
   const float *sh = p.shat + (size_t)row * p.n;
   const int n = p.n;
   // token of iteration it for this thread
@@ -3406,7 +3393,7 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rwalk(DParams p) {
   // neither tier decides the row: the streaming selection
   __syncthreads();
   const SelArgs sa{p.r, p.shat, s_res, p.fbits, p.hbits, p.a_delta,
-                   p.l_delta, p.eps, p.n, p.nwords, p.est};
+                   p.l_delta, p.eps, p.n, p.ns, p.nwords, p.est};
   select_row(sa, row, bg, rs, lds.sel);
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -3450,6 +3437,7 @@ __device__ __forceinline__ void gather_attend(const DParams &p, int j, int g,
   constexpr int HW = kBlock / 32;
   constexpr int STEP = HW * kGatherBatch;   // rows per batch of the workgroup
   __shared__ int s_pos[kGatherSeg];
+  __shared__ int s_src[kGatherSeg];  // index in stage_prev, or -1: host
   __shared__ uint8_t s_msk[kGatherSeg];
   __shared__ uint32_t s_red[kBlock / kWave + 1];
   __shared__ float s_m[HW][GRP], s_d[HW][GRP];
@@ -3488,11 +3476,19 @@ __device__ __forceinline__ void gather_attend(const DParams &p, int j, int g,
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc[h][k] = 0.0f;
   }
-  const uint16_t *src_base = p.host_kv + (size_t)bg * p.n * 2 * kHeadDim;
+  const uint16_t *src_base = p.host_kv + (size_t)bg * p.ns * 2 * kHeadDim;
+  const uint16_t *stg_base =
+      p.stage_prev ? p.stage_prev + (size_t)bg * p.fetch_cap * 2 * kHeadDim : nullptr;
   int32_t *fidx = p.fidx + (size_t)bg * p.fetch_cap;
-  auto row_ptr = [&](int pos) {
-    return reinterpret_cast<const uint4 *>(src_base + (size_t)pos * 2 * kHeadDim + unit * 8);
+  // row k of the segment: from the previous step's staging when it holds
+  // it, else from host memory
+  auto row_ptr = [&](uint32_t k) {
+    const int sl = s_src[k];
+    const uint16_t *base = sl >= 0 ? stg_base + (size_t)sl * 2 * kHeadDim
+                                   : src_base + (size_t)s_pos[k] * 2 * kHeadDim;
+    return reinterpret_cast<const uint4 *>(base + unit * 8);
   };
+  uint32_t n_host = 0u;  // rows this thread listed that come from host memory
   for (uint32_t seg = lo; seg < hi; seg += kGatherSeg) {
     const uint32_t seg_hi = min(hi, seg + (uint32_t)kGatherSeg);
     // ---- list the positions with list index in [seg, seg_hi)
@@ -3511,7 +3507,15 @@ __device__ __forceinline__ void gather_attend(const DParams &p, int j, int g,
 #pragma unroll
               for (int h = 0; h < GRP; ++h)
                 msk |= ((p.hbits[(size_t)row_of(p, b, g, h, GRP) * p.nwords + wi] >> bit) & 1u) << h;
-              s_pos[gi - seg] = wi * 32 + bit;
+              const int pos = wi * 32 + bit;
+              int sl = -1;
+              if (p.smap_prev) {
+                sl = p.smap_prev[(size_t)bg * p.ns + pos];
+                if (sl >= p.fetch_cap) sl = -1;
+              }
+              n_host += sl < 0 ? 1u : 0u;
+              s_pos[gi - seg] = pos;
+              s_src[gi - seg] = sl;
               s_msk[gi - seg] = (uint8_t)msk;
             }
             ++gi;
@@ -3524,24 +3528,31 @@ __device__ __forceinline__ void gather_attend(const DParams &p, int j, int g,
     }
     __syncthreads();
     const uint32_t nrow = seg_hi - seg;
-    for (uint32_t k = threadIdx.x; k < nrow; k += kBlock) fidx[seg + k] = s_pos[k];
+    for (uint32_t k = threadIdx.x; k < nrow; k += kBlock) {
+      fidx[seg + k] = s_pos[k];
+      if (p.smap_next) p.smap_next[(size_t)bg * p.ns + s_pos[k]] = (int32_t)(seg + k);
+    }
+    uint16_t *stg_next =
+        p.stage_next ? p.stage_next + (size_t)bg * p.fetch_cap * 2 * kHeadDim : nullptr;
     // ---- rows: batch r0 in use while batch r0 + STEP is in flight
     uint4 cur[kGatherBatch], nxt[kGatherBatch];
 #pragma unroll
     for (int it = 0; it < kGatherBatch; ++it) {
       const uint32_t rk = it * HW + hw;
-      if (rk < nrow) cur[it] = *row_ptr(s_pos[rk]);
+      if (rk < nrow) cur[it] = *row_ptr(rk);
     }
     for (uint32_t r0 = 0; r0 < nrow; r0 += STEP) {
 #pragma unroll
       for (int it = 0; it < kGatherBatch; ++it) {
         const uint32_t rk = r0 + STEP + it * HW + hw;
-        if (rk < nrow) nxt[it] = *row_ptr(s_pos[rk]);
+        if (rk < nrow) nxt[it] = *row_ptr(rk);
       }
 #pragma unroll
       for (int it = 0; it < kGatherBatch; ++it) {
         const uint32_t rk = r0 + it * HW + hw;
         if (rk >= nrow) continue;  // (uniform over the half-wave)
+        if (stg_next)  // this step's staging: the row at its list index
+          reinterpret_cast<uint4 *>(stg_next + (size_t)(seg + rk) * 2 * kHeadDim)[unit] = cur[it];
         float x[8];
         unpack8(cur[it], x);
         const uint32_t msk = s_msk[rk];
@@ -3601,11 +3612,13 @@ __device__ __forceinline__ void gather_attend(const DParams &p, int j, int g,
     p.aparto[((size_t)row * kHeadDim + e) * p.npad + x] = o;
     if (e == 0) p.apart[(size_t)row * np + x] = make_float2(mx, d);
   }
+  // bytes read from host memory: the rows not found in the staging
+  const uint32_t moved = block_sum<uint32_t>(n_host, s_red);
+  if (threadIdx.x == 0 && moved > 0u)
+    atomicAdd(p.host_bytes, (unsigned long long)moved * 2ull * kHeadDim * 2ull);
   if (j == p.ncf - 1 && threadIdx.x == 0) {
     p.fcount[bg] = (int32_t)total;
     if (total > (uint32_t)p.fetch_cap) atomicOr(p.status, VKV_STATUS_FETCH_OVERFLOW);
-    const uint32_t moved = min(total, (uint32_t)p.fetch_cap);
-    atomicAdd(p.host_bytes, (unsigned long long)moved * 2ull * kHeadDim * 2ull);
   }
 }
 
@@ -3642,7 +3655,7 @@ __device__ __forceinline__ void attn_part(const DParams &p, int x, int g,
   __shared__ float s_d[kBlock / kWave][GRP];
   if (threadIdx.x < GRP) s_rs[threadIdx.x] = p.rows[row_of(p, b, g, threadIdx.x, GRP)];
   __syncthreads();
-  const float *rr = p.r + (size_t)bg * p.n;
+  const float *rr = p.r + (size_t)bg * p.ns;
   float acc[GRP][8], dsum[GRP], mloc[GRP];
 #pragma unroll
   for (int h = 0; h < GRP; ++h) {
@@ -4077,6 +4090,11 @@ hipError_t launch_decode(const vkv_decode_args &a, const DecodeLayout &L,
   p.Hq = a.n_q_heads;
   p.G = a.n_kv_heads;
   p.n = a.n_tokens;
+  p.ns = a.ctx_stride > 0 ? a.ctx_stride : a.n_tokens;
+  p.smap_prev = a.stage_map_prev;
+  p.stage_prev = a.stage_prev;
+  p.smap_next = a.stage_map_next;
+  p.stage_next = a.stage_next;
   p.cap = a.cap;
   p.fetch_cap = a.fetch_cap;
   p.nch = L.nch;

@@ -51,6 +51,8 @@ struct CompressLayout {
 CompressLayout compress_layout(const vkv_compress_args &a);
 hipError_t launch_compress(const vkv_compress_args &a, const CompressLayout &L,
                            int64_t b_free, int32_t n_forced, hipStream_t s);
+// (k and v are device-readable addresses: device memory, or pinned host
+// memory's device view)
 
 // ------------------------------------------------------------ decoding
 struct DecodeLayout {
@@ -77,6 +79,10 @@ struct Sketch2Layout {
 Sketch2Layout sketch2_layout(const vkv_sketch2_args &a);
 hipError_t launch_sketch2(const vkv_sketch2_args &a, const Sketch2Layout &L,
                           hipStream_t s);
+
+// ------------------------------------------------------------ maintenance
+hipError_t launch_append(const vkv_append_args &a, uint16_t *host_kv_dev,
+                         hipStream_t s);
 
 // ------------------------------------------------------------ dense baselines
 struct DenseLayout {

@@ -143,7 +143,8 @@ __global__ __launch_bounds__(kSkGroup) void sk_quant(const vkv_sketch2_args a) {
     const float s = fp16_sat((mx - mn) / 3.0f);
     s_z[t] = z;
     s_s[t] = s;
-    const size_t zs = ((size_t)sl * ((a.n_tokens + kSkGroup - 1) / kSkGroup) + grp) * 2 * kSkChan;
+    const int os = a.out_stride > 0 ? a.out_stride : a.n_tokens;
+    const size_t zs = ((size_t)sl * ((os + kSkGroup - 1) / kSkGroup) + grp) * 2 * kSkChan;
     a.zs[zs + t] = __builtin_bit_cast(uint16_t, (_Float16)z);
     a.zs[zs + kSkChan + t] = __builtin_bit_cast(uint16_t, (_Float16)s);
   }
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(kSkGroup) void sk_quant(const vkv_sketch2_args a) {
       const float cf = s > 0.0f ? fminf(fmaxf(rintf(x), 0.0f), 3.0f) : 0.0f;
       word |= (unsigned long long)(uint32_t)cf << (2 * c);
     }
-    a.codes[(size_t)sl * a.n_tokens + t0 + t] = word;
+    a.codes[(size_t)sl * (a.out_stride > 0 ? a.out_stride : a.n_tokens) + t0 + t] = word;
   }
 }
 

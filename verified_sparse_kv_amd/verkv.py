@@ -37,7 +37,8 @@ EXPORTS = ("vkv_compress_workspace_bytes", "vkv_decode_workspace_bytes",
            "vkv_last_error", "vkv_version", "vkv_decode_phase_count",
            "vkv_decode_phase_name", "vkv_dense_workspace_bytes",
            "vkv_dense_attention", "vkv_decode_step_noalloc",
-           "vkv_sketch2_workspace_bytes", "vkv_sketch2_build")
+           "vkv_sketch2_workspace_bytes", "vkv_sketch2_build",
+           "vkv_append_token")
 NOALLOC_WORKSPACE_BYTES = 128 << 20
 
 _p = ctypes.c_void_p
@@ -46,7 +47,8 @@ _i32 = ctypes.c_int32
 
 class CompressArgs(ctypes.Structure):
     _fields_ = [("n_layers", _i32), ("n_kv_heads", _i32), ("n_tokens", _i32),
-                ("head_dim", _i32), ("layer0", _i32),
+                ("head_dim", _i32), ("layer0", _i32), ("ctx_stride", _i32),
+                ("kv_stride", ctypes.c_int64),
                 ("tau", _p), ("k", _p), ("v", _p),
                 ("budget", ctypes.c_int64), ("n_sink", _i32), ("n_local", _i32),
                 ("seed", ctypes.c_uint64), ("cap", _i32),
@@ -58,12 +60,14 @@ class CompressArgs(ctypes.Structure):
 class DecodeArgs(ctypes.Structure):
     _fields_ = [("batch", _i32), ("n_q_heads", _i32), ("n_kv_heads", _i32),
                 ("head_dim", _i32), ("n_tokens", _i32), ("sketch_dim", _i32),
-                ("cap", _i32),
+                ("cap", _i32), ("ctx_stride", _i32),
                 ("q", _p), ("resident_kv", _p), ("resident_idx", _p),
                 ("resident_count", _p), ("sketch", _p), ("proj", _p), ("r", _p),
                 ("host_kv", _p),
                 ("sk2_codes", _p), ("sk2_zs", _p), ("sk2_chan", _p),
                 ("n_short", _i32),
+                ("stage_map_prev", _p), ("stage_prev", _p),
+                ("stage_map_next", _p), ("stage_next", _p),
                 ("eps", ctypes.c_float), ("delta", ctypes.c_float),
                 ("estimator", _i32), ("weights", _i32), ("fetch_cap", _i32),
                 ("out", _p), ("d_hat", _p), ("log_shift", _p), ("eps_hat0", _p),
@@ -84,9 +88,21 @@ class DenseArgs(ctypes.Structure):
 
 class Sketch2Args(ctypes.Structure):
     _fields_ = [("n_slices", _i32), ("n_tokens", _i32), ("head_dim", _i32),
+                ("out_stride", _i32),
                 ("key_stride", ctypes.c_int64), ("slice_stride", ctypes.c_int64),
                 ("k", _p), ("codes", _p), ("zs", _p), ("chan", _p),
                 ("workspace", _p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class AppendArgs(ctypes.Structure):
+    _fields_ = [("batch", _i32), ("n_kv_heads", _i32), ("head_dim", _i32),
+                ("pos", _i32), ("cap", _i32), ("ctx_stride", _i32),
+                ("sketch_dim", _i32),
+                ("k_new", _p), ("v_new", _p), ("host_kv", _p),
+                ("resident_kv", _p), ("resident_idx", _p),
+                ("resident_count", _p), ("r", _p), ("sketch", _p),
+                ("proj", _p), ("sk2_codes", _p), ("sk2_zs", _p),
+                ("status", _p)]
 
 
 class VerKVError(RuntimeError):
@@ -140,6 +156,8 @@ def _load():
     lib.vkv_sketch2_workspace_bytes.restype = ctypes.c_size_t
     lib.vkv_sketch2_build.argtypes = [ctypes.POINTER(Sketch2Args), _p]
     lib.vkv_sketch2_build.restype = ctypes.c_int
+    lib.vkv_append_token.argtypes = [ctypes.POINTER(AppendArgs), _p]
+    lib.vkv_append_token.restype = ctypes.c_int
     return lib
 
 
@@ -181,6 +199,10 @@ def vkv_sketch2_workspace_bytes(args):
 
 def vkv_sketch2_build(args, stream=None):
     return int(LIB.vkv_sketch2_build(ctypes.byref(args), stream))
+
+
+def vkv_append_token(args, stream=None):
+    return int(LIB.vkv_append_token(ctypes.byref(args), stream))
 
 
 def vkv_check_status(status_ptr, stream=None):
@@ -290,30 +312,34 @@ def compress(tau, k, v, budget, n_sink, n_local, seed, cap, layer0=0,
     return out
 
 
-def sketch2_build(k, key_stride=None, stream=None):
-    """The 2-bit key sketch of every slice of ``k`` (a device tensor of bf16
-    bits, int16, shaped [..., n, key_stride] with the key in the first 128
-    elements of each token's row; leading dimensions are the slices).
-    Returns dict(codes [..., n] int64, zs [..., ceil(n/128), 2, 32] int16,
-    chan [..., 32] int32)."""
+def sketch2_build(k, key_stride=None, stream=None, n=None, out=None):
+    """The 2-bit key sketch of every slice of ``k`` (bf16 bits, int16,
+    shaped [..., ns, key_stride] with the key in the first 128 elements of
+    each token's row; leading dimensions are the slices; device memory or
+    pinned host memory). The first ``n`` (default ns) tokens are sketched.
+    Returns (or fills ``out``) dict(codes [..., ns] int64,
+    zs [..., ceil(ns/128), 2, 32] int16, chan [..., 32] int32)."""
     torch = _torch()
-    if k.dtype != torch.int16 or not k.is_cuda or not k.is_contiguous():
-        raise ValueError("k: contiguous int16 device tensor expected")
+    if k.dtype != torch.int16 or not k.is_contiguous() or \
+            not (k.is_cuda or k.is_pinned()):
+        raise ValueError("k: contiguous int16 tensor in device or pinned memory expected")
     lead = tuple(k.shape[:-2])
-    n, stride = k.shape[-2], k.shape[-1]
+    ns, stride = k.shape[-2], k.shape[-1]
+    n = ns if n is None else n
     slices = 1
     for x in lead:
         slices *= x
-    ng = (n + SK2_GROUP - 1) // SK2_GROUP
-    dev = k.device
-    out = dict(codes=torch.empty(lead + (n,), dtype=torch.int64, device=dev),
-               zs=torch.empty(lead + (ng, 2, SK2_CHANNELS), dtype=torch.int16,
-                              device=dev),
-               chan=torch.empty(lead + (SK2_CHANNELS,), dtype=torch.int32,
-                                device=dev))
-    a = Sketch2Args(n_slices=slices, n_tokens=n, head_dim=128,
+    ng = (ns + SK2_GROUP - 1) // SK2_GROUP
+    dev = torch.device("cuda")
+    if out is None:
+        out = dict(codes=torch.empty(lead + (ns,), dtype=torch.int64, device=dev),
+                   zs=torch.empty(lead + (ng, 2, SK2_CHANNELS), dtype=torch.int16,
+                                  device=dev),
+                   chan=torch.empty(lead + (SK2_CHANNELS,), dtype=torch.int32,
+                                    device=dev))
+    a = Sketch2Args(n_slices=slices, n_tokens=n, head_dim=128, out_stride=ns,
                     key_stride=stride if key_stride is None else key_stride,
-                    slice_stride=n * stride, k=_ptr(k),
+                    slice_stride=ns * stride, k=_ptr(k),
                     codes=_ptr(out["codes"]), zs=_ptr(out["zs"]),
                     chan=_ptr(out["chan"]))
     nbytes = vkv_sketch2_workspace_bytes(a)
@@ -326,15 +352,69 @@ def sketch2_build(k, key_stride=None, stream=None):
     return out
 
 
+def append_token(k_new, v_new, pos, host_kv, resident_kv, resident_idx,
+                 resident_count, r, status, sketch=None, proj=None,
+                 sketch2=None, stream=None):
+    """One generated token joins H of every (request, KV head) at ``pos``
+    (see vkv_append_args). k_new/v_new [B][G][d] int16 on the device;
+    host_kv [B][G][ns][2][d] pinned; the resident arrays, r [B][G][ns],
+    the sketches and status on the device, all updated in place."""
+    B, G, ns = host_kv.shape[0], host_kv.shape[1], host_kv.shape[2]
+    cap = resident_idx.shape[-1]
+    a = AppendArgs(batch=B, n_kv_heads=G, head_dim=128, pos=int(pos), cap=cap,
+                   ctx_stride=ns,
+                   sketch_dim=0 if sketch is None else sketch.shape[-1],
+                   k_new=_ptr(k_new), v_new=_ptr(v_new), host_kv=_ptr(host_kv),
+                   resident_kv=_ptr(resident_kv), resident_idx=_ptr(resident_idx),
+                   resident_count=_ptr(resident_count), r=_ptr(r),
+                   sketch=_ptr(sketch), proj=_ptr(proj),
+                   sk2_codes=None if sketch2 is None else _ptr(sketch2["codes"]),
+                   sk2_zs=None if sketch2 is None else _ptr(sketch2["zs"]),
+                   status=_ptr(status))
+    _check(vkv_append_token(a, _stream(stream)))
+
+
+def recompress(tau, host_kv, n, budget, n_sink, n_local, seed, out, layer0=0,
+               stream=None, workspace=None):
+    """PoissonComp again over the first ``n`` tokens of a decode cache held
+    in pinned host memory (host_kv [B][G][ns][2][d]), with fresh scores tau
+    [B][G][ns] (first n read). Fills ``out`` (r [B][G][ns], resident_idx,
+    resident_count, resident_kv, water_level, status: device tensors)."""
+    torch = _torch()
+    B, G, ns = host_kv.shape[0], host_kv.shape[1], host_kv.shape[2]
+    cap = out["resident_idx"].shape[-1]
+    base = host_kv.data_ptr()
+    a = CompressArgs(n_layers=B, n_kv_heads=G, n_tokens=n, head_dim=128,
+                     layer0=layer0, ctx_stride=ns, kv_stride=256,
+                     tau=_ptr(tau), k=ctypes.c_void_p(base),
+                     v=ctypes.c_void_p(base + 256), budget=int(budget),
+                     n_sink=n_sink, n_local=n_local,
+                     seed=int(seed) & 0xFFFFFFFFFFFFFFFF, cap=cap,
+                     r=_ptr(out["r"]), resident_idx=_ptr(out["resident_idx"]),
+                     resident_count=_ptr(out["resident_count"]),
+                     resident_kv=_ptr(out["resident_kv"]),
+                     water_level=_ptr(out["water_level"]),
+                     status=_ptr(out["status"]))
+    nbytes = vkv_compress_workspace_bytes(a)
+    if nbytes == 0:
+        _check(vkv_compress(a, _stream(stream)))
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty((nbytes,), dtype=torch.uint8, device=out["r"].device)
+    a.workspace, a.workspace_bytes = _ptr(workspace), nbytes
+    _check(vkv_compress(a, _stream(stream)))
+    return workspace
+
+
 class DecodeStep:
     """Reusable decode-step launcher: outputs and workspace are allocated once
     for a shape, so repeated steps only marshal pointers and launch."""
 
     def __init__(self, B, Hq, G, n, s, cap, fetch_cap, device, d=128,
-                 n_short=128):
+                 n_short=128, ctx_stride=None):
         torch = _torch()
         self.shape = (B, Hq, G, n, s, cap, fetch_cap)
         self.n_short = n_short
+        self.ns = n if ctx_stride is None else ctx_stride
         self.out = dict(
             out=torch.empty((B, Hq, d), dtype=torch.float32, device=device),
             d_hat=torch.empty((B, Hq), dtype=torch.float32, device=device),
@@ -354,7 +434,8 @@ class DecodeStep:
             status=torch.zeros((1,), dtype=torch.int32, device=device))
         self.args = DecodeArgs(batch=B, n_q_heads=Hq, n_kv_heads=G, head_dim=d,
                                n_tokens=n, sketch_dim=s, cap=cap,
-                               fetch_cap=fetch_cap, n_short=n_short)
+                               ctx_stride=self.ns, fetch_cap=fetch_cap,
+                               n_short=n_short)
         for key in ("out", "d_hat", "log_shift", "eps_hat0", "eps_hat", "k_star",
                     "fetch_idx", "fetch_count", "host_bytes", "row_stats",
                     "row_path", "shortlist", "status"):
@@ -373,20 +454,21 @@ class DecodeStep:
         keys shaped [B][G][n][...] (codes, zs, chan)."""
         torch = _torch()
         B, Hq, G, n, s, cap, _ = self.shape
+        ns = self.ns
         d = 128
         _need(q, torch.int16, (B, Hq, d), "q")
         _need(resident_kv, torch.int16, (B, G, cap, 2, d), "resident_kv")
         _need(resident_idx, torch.int32, (B, G, cap), "resident_idx")
         _need(resident_count, torch.int32, (B, G), "resident_count")
-        _need(r, torch.float32, (B, G, n), "r")
-        _need(host_kv, torch.int16, (B, G, n, 2, d), "host_kv", device=False)
+        _need(r, torch.float32, (B, G, ns), "r")
+        _need(host_kv, torch.int16, (B, G, ns, 2, d), "host_kv", device=False)
         if weights == W_SKETCH:
-            _need(sketch, torch.int16, (B, G, n, s), "sketch")
+            _need(sketch, torch.int16, (B, G, ns, s), "sketch")
             _need(proj, torch.float32, (G, d, s), "proj")
         a = self.args
         if weights == W_SKETCH2:
-            ng = (n + SK2_GROUP - 1) // SK2_GROUP
-            _need(sketch2["codes"], torch.int64, (B, G, n), "sketch2 codes")
+            ng = (ns + SK2_GROUP - 1) // SK2_GROUP
+            _need(sketch2["codes"], torch.int64, (B, G, ns), "sketch2 codes")
             _need(sketch2["zs"], torch.int16, (B, G, ng, 2, SK2_CHANNELS), "sketch2 zs")
             _need(sketch2["chan"], torch.int32, (B, G, SK2_CHANNELS), "sketch2 chan")
             a.sk2_codes = _ptr(sketch2["codes"])
@@ -403,6 +485,32 @@ class DecodeStep:
         self._keep = (q, resident_kv, resident_idx, resident_count, sketch, proj,
                       r, host_kv, sketch2)
         return self
+
+    def set_tokens(self, n):
+        """The context length of the next launch (<= the capacity)."""
+        B, Hq, G, _, s, cap, fetch_cap = self.shape
+        if not 1 <= n <= self.ns or fetch_cap > n:
+            raise ValueError(f"n_tokens {n} outside [fetch_cap, {self.ns}]")
+        self.shape = (B, Hq, G, n, s, cap, fetch_cap)
+        self.args.n_tokens = n
+        nbytes = vkv_decode_workspace_bytes(self.args)
+        if nbytes > self.workspace.numel():
+            torch = _torch()
+            self.workspace = torch.empty((nbytes,), dtype=torch.uint8,
+                                         device=self.workspace.device)
+            self.args.workspace = _ptr(self.workspace)
+        self.args.workspace_bytes = self.workspace.numel()
+
+    def set_staging(self, prev=None, nxt=None):
+        """Rows staged by the previous step (prev = (map, rows)) and this
+        step's staging (nxt = (map, rows)): maps [B][G][ns] int32, rows
+        [B][G][fetch_cap][2][d] int16, device tensors; None for none."""
+        a = self.args
+        a.stage_map_prev = None if prev is None else _ptr(prev[0])
+        a.stage_prev = None if prev is None else _ptr(prev[1])
+        a.stage_map_next = None if nxt is None else _ptr(nxt[0])
+        a.stage_next = None if nxt is None else _ptr(nxt[1])
+        self._stage = (prev, nxt)
 
     def set_phase_events(self, events):
         """Attach phase_count()+1 torch.cuda.Event objects (or None); None
