@@ -59,6 +59,12 @@ def parse():
                     help="other decode workloads measured after the headline "
                          "one, each reported as its own block (default: c3, "
                          "batch 16 with fetching active); none with --also")
+    ap.add_argument("--serving", nargs="*", default=["c3"],
+                    choices=["c2", "c3", "c4"],
+                    help="serving loops (block '<config>_serving'): each step "
+                         "a decode step and the generated token's append, "
+                         "the next query correlated with the last, fetched "
+                         "rows staged for the next step; none with --serving")
     ap.add_argument("--sketch2", nargs="*", default=["c2", "c3"],
                     choices=["c2", "c3", "c4"],
                     help="workloads measured again planning with the pages' "
@@ -272,6 +278,126 @@ def compress_pass(dev, steps):
     del kv, t_tau
     torch.cuda.empty_cache()
     return out
+
+
+def serving_loop(config, args, dev):
+    """A serving loop on one workload: the cache compressed once (from the
+    pinned host cache, into a layout with room to grow), then per step a
+    decode step for the current query and the append of the generated token
+    (a random bf16 K/V row) to every (request, KV head); the next query is
+    0.9 q + 0.44 N(0, I) (consecutive decode queries are correlated). Timed
+    twice over the same sequence: with the fetched rows staged for the next
+    step (hits read from device memory) and without. Reports ms per step
+    (decode + append), host bytes per step and the share of fetched rows
+    found in the staging."""
+    import numpy as np
+    import torch
+
+    from verified_sparse_kv_amd import verkv as vk
+    from workloads import bf16_bits, make_decode_workload, resident_cap
+
+    w = make_decode_workload(config, seed=args.seed, with_queries=False)
+    B, Hq, G, n0, s, d = w["B"], w["Hq"], w["G"], w["n"], w["s"], w["d"]
+    K = max(2, min(args.steps, 20))
+    W = max(1, min(args.warmup, 5))
+    total = W + K
+    ns = n0 + 2 * total + 2
+    cap = resident_cap(w["budget"]) + 2 * total + 2
+    host0 = np.zeros((B, G, ns, 2, d), dtype=np.uint16)
+    host0[:, :, :n0] = w["host_kv"]
+    tau = np.zeros((B, G, ns), dtype=np.float32)
+    tau[:, :, :n0] = w["tau"]
+    sketch0 = np.zeros((B, G, ns, s), dtype=np.uint16)
+    sketch0[:, :, :n0] = w["sketch"]
+    rng = np.random.default_rng([7, args.seed])
+    q0 = bf16_bits(rng.standard_normal((B, Hq, d), dtype=np.float32))
+    new_kv = [(bf16_bits(rng.standard_normal((B, G, d), dtype=np.float32)),
+               bf16_bits(rng.standard_normal((B, G, d), dtype=np.float32)))
+              for _ in range(total)]
+    qs = [q0]
+    for _ in range(total - 1):
+        qf = (qs[-1].astype(np.uint32) << 16).view(np.float32)
+        qs.append(bf16_bits((0.9 * qf + 0.44 * rng.standard_normal(qf.shape))
+                            .astype(np.float32)))
+    t_qs = [torch.from_numpy(q.view(np.int16)).to(dev) for q in qs]
+    t_kv = [(torch.from_numpy(a.view(np.int16)).to(dev),
+             torch.from_numpy(b.view(np.int16)).to(dev)) for a, b in new_kv]
+    proj = torch.from_numpy(w["proj"]).to(dev)
+    host = torch.from_numpy(host0.view(np.int16)).pin_memory()
+    t_tau = torch.from_numpy(tau).to(dev)
+
+    def run(staged, record=False):
+        """Compress, then W + K steps; returns (ms per timed step, host
+        bytes per timed step, fetched rows, rows found in the staging)."""
+        st = dict(r=torch.zeros((B, G, ns), dtype=torch.float32, device=dev),
+                  resident_idx=torch.zeros((B, G, cap), dtype=torch.int32, device=dev),
+                  resident_count=torch.zeros((B, G), dtype=torch.int32, device=dev),
+                  resident_kv=torch.zeros((B, G, cap, 2, d), dtype=torch.int16, device=dev),
+                  water_level=torch.empty((B, G), dtype=torch.float64, device=dev),
+                  status=torch.zeros((1,), dtype=torch.int32, device=dev))
+        host.copy_(torch.from_numpy(host0.view(np.int16)))
+        vk.recompress(t_tau, host, n0, w["budget"], w["n_sink"], w["n_local"],
+                      w["seed"], st)
+        sketch = torch.from_numpy(sketch0.view(np.int16)).to(dev)
+        status = torch.zeros((1,), dtype=torch.int32, device=dev)
+        step = vk.DecodeStep(B, Hq, G, n0, s, cap, n0, dev, ctx_stride=ns)
+        maps = [torch.full((B, G, ns), -1, dtype=torch.int32, device=dev)
+                for _ in range(2)]
+        stages = [torch.empty((B, G, n0, 2, d), dtype=torch.int16, device=dev)
+                  for _ in range(2)]
+        hb, lists = [], []
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(total):
+            if i == W:
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+            n = n0 + i
+            step.set_tokens(n)
+            step.bind(t_qs[i], st["resident_kv"], st["resident_idx"],
+                      st["resident_count"], sketch, proj, st["r"], host,
+                      w["eps"], w["delta"], ESTIMATORS[args.estimator])
+            if staged:
+                step.set_staging(prev=(maps[(i + 1) % 2], stages[(i + 1) % 2]),
+                                 nxt=(maps[i % 2], stages[i % 2]))
+            step.launch()
+            vk.append_token(t_kv[i][0], t_kv[i][1], n, host, st["resident_kv"],
+                            st["resident_idx"], st["resident_count"], st["r"],
+                            status, sketch, proj)
+            if i >= W:
+                hb.append(step.out["host_bytes"].clone())
+                if record:
+                    lists.append((step.out["fetch_idx"].clone(),
+                                  step.out["fetch_count"].clone()))
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        rc, bits = step.check_status()
+        assert rc == 0 and int(status[0]) == 0, (rc, bits)
+        fetched = hits = 0
+        for j in range(1, len(lists)):
+            a1, c1 = (x.cpu().numpy() for x in lists[j])
+            a0, c0 = (x.cpu().numpy() for x in lists[j - 1])
+            for b in range(B):
+                for g in range(G):
+                    u1 = a1[b, g, :c1[b, g]]
+                    fetched += u1.size
+                    hits += np.intersect1d(u1, a0[b, g, :c0[b, g]]).size
+        return ((t1 - t0) * 1e3 / K, float(np.mean([int(x[0]) for x in hb])),
+                fetched, hits)
+
+    ms_s, hb_s, _, _ = run(True)
+    ms_n, hb_n, _, _ = run(False)
+    _, _, fetched, hits = run(True, record=True)
+    return {
+        "workload": WORKLOADS[config] + ", serving loop (decode + append per "
+                    "step, correlated queries)",
+        "steps": K, "ctx_tokens_start": n0,
+        "ms_per_step": ms_s, "ms_per_step_no_staging": ms_n,
+        "host_bytes_per_step": hb_s, "host_bytes_per_step_no_staging": hb_n,
+        "host_bytes_saved_pct": 100.0 * (1.0 - hb_s / hb_n) if hb_n else 0.0,
+        "staged_rows_pct": 100.0 * hits / fetched if fetched else 0.0,
+        "value": B * Hq * (n0 + W + K / 2) / (ms_s * 1e-3),
+    }
 
 
 def dense_baselines(w, t_qs, host_kv, dev, steps, verkv_ms):
@@ -545,6 +671,9 @@ def main():
         e.pop("_t_qs")
         e.pop("_host_kv")
         res[extra] = e
+        torch.cuda.empty_cache()
+    for extra in args.serving:
+        res[extra + "_serving"] = serving_loop(extra, args, dev)
         torch.cuda.empty_cache()
     for extra in args.sketch2:
         from verified_sparse_kv_amd import verkv as vk
