@@ -59,6 +59,10 @@ def parse():
                     help="other decode workloads measured after the headline "
                          "one, each reported as its own block (default: c3, "
                          "batch 16 with fetching active); none with --also")
+    ap.add_argument("--weights", default="sketch", choices=["sketch", "sketch2"],
+                    help="planning weights of the main line: the projected "
+                         "sketch (default) or the pages' 2-bit sketch with "
+                         "a 128-token exact shortlist")
     ap.add_argument("--serving", nargs="*", default=["c3"],
                     choices=["c2", "c3", "c4"],
                     help="serving loops (block '<config>_serving'): each step "
@@ -640,7 +644,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    m, w = measure(args.config, args, dev, True)
+    from verified_sparse_kv_amd import verkv as vk
+    main_w = vk.W_SKETCH2 if args.weights == "sketch2" else vk.W_SKETCH
+    m, w = measure(args.config, args, dev, True, weights=main_w)
     t_qs, host_kv = m.pop("_t_qs"), m.pop("_host_kv")
     res = {
         "metric": METRIC,
@@ -676,7 +682,8 @@ def main():
         res[extra + "_serving"] = serving_loop(extra, args, dev)
         torch.cuda.empty_cache()
     for extra in args.sketch2:
-        from verified_sparse_kv_amd import verkv as vk
+        if extra == args.config and main_w == vk.W_SKETCH2:
+            continue
         e, _ = measure(extra, args, dev, False, weights=vk.W_SKETCH2)
         e.pop("_t_qs")
         e.pop("_host_kv")

@@ -65,6 +65,7 @@ struct RowState {
   double betaL, VL;       // beta(L), V(L) (float64 sums of fp32 terms)
   double s_full;          // sqrt((a b)^2 + 2 V l)
   float s_full_f;         // the same in fp32 (the gain formula's s)
+  float ab1sq;            // ((a a) b1) b1 in fp32: the gain's (a b')^2 when b' = b1
   double eps0;            // eps^(L)
   float b1, b2;           // largest and second largest b_i (with multiplicity)
   int32_t amax;           // position of the unique argmax of b_i, else -1
@@ -273,8 +274,16 @@ __device__ __forceinline__ float token_gain(const Terms &t, int pos,
                                             const RowState &rs, float a,
                                             float l) {
   const float b1 = rs.b1;
-  const float bp = (pos == rs.amax) ? rs.b2 : b1;
   const float vp = (float)fmax(rs.VL - (double)t.vi, 0.0);
+  if (pos != rs.amax) {
+    // b' = b: the terms in b - b' are exact zeros, so the same value as the
+    // general form below with (a b)^2 taken from the row
+    const float sp = __builtin_amdgcn_sqrtf(rs.ab1sq + 2.0f * vp * l);
+    const float den = rs.s_full_f + sp;
+    const float frac = den > 0.0f ? (2.0f * t.vi * l) * __builtin_amdgcn_rcpf(den) : 0.0f;
+    return t.bi + frac;
+  }
+  const float bp = rs.b2;
   const float sp = __builtin_amdgcn_sqrtf(a * a * bp * bp + 2.0f * vp * l);
   const float num = a * a * (b1 - bp) * (b1 + bp) + 2.0f * t.vi * l;
   const float den = rs.s_full_f + sp;
@@ -283,29 +292,25 @@ __device__ __forceinline__ float token_gain(const Terms &t, int pos,
 }
 
 // A term of the selection's fixed-point sums: min(x, cap) 2^e, truncated to
-// an integer, formed from the fp32 bits of x >= 0 (the significand shifted
-// by the exponent; values below 2^-e become 0), with no float64 arithmetic.
-// The caps are c = 2 eps D~ for beta_i and c^2 / (2 l) for v_i (compared in
-// fp32): a rest holding a term at its cap has eps^ >= 2 eps (to within the
-// cap's fp32 rounding) whether the term is capped or not, so capping never
-// changes a stopping decision, while a rest that can stop holds only exact
-// terms. The scale follows eps D~ (cap 2^e < 2^40), not the largest term,
-// so rests near the stopping point keep ~40 bits however heavy the fetched
-// tokens are; with at most 2^17 tokens no sum overflows. Every pass forms
-// the terms with this one function, so all passes agree bit for bit.
-__device__ __forceinline__ unsigned long long fx_bits(float x, int e) {
-  const uint32_t u = __float_as_uint(x);
-  const int E = (int)(u >> 23);
-  const unsigned long long m = (unsigned long long)((u & 0x7FFFFFu) | 0x800000u);
-  const int sh = E - 150 + e;
-  const unsigned long long up = m << (sh > 0 ? sh : 0);
-  const unsigned long long dn = m >> (sh < 0 ? min(-sh, 63) : 0);
-  return (E == 0 || sh <= -24) ? 0ull : (sh >= 0 ? up : dn);
+// an integer. The caps are c = 2 eps D~ for beta_i and c^2 / (2 l) for v_i
+// (compared in fp32): a rest holding a term at its cap has eps^ >= 2 eps (to
+// within the cap's fp32 rounding) whether the term is capped or not, so
+// capping never changes a stopping decision, while a rest that can stop
+// holds only exact terms. The scale follows eps D~ (cap 2^e < 2^40), not the
+// largest term, so rests near the stopping point keep ~40 bits however heavy
+// the fetched tokens are; with at most 2^17 tokens no sum overflows. The
+// term is formed in float64, where x 2^e is exact and below 2^40, so a sum
+// of at most 2^13 terms (one candidate workgroup's share) is still an exact
+// integer in float64; other sums take it as a 64-bit integer. Every pass
+// forms the terms with this one function, so all passes agree bit for bit.
+__device__ __forceinline__ double fx_term(float x, double cap, int e) {
+  const float cf = (float)cap;
+  // (the product is exact in float64 and below 2^40; NaN takes the cap)
+  return trunc(ldexp((double)(x < cf ? x : cf), e));
 }
 __device__ __forceinline__ unsigned long long sat_fx(float x, double cap,
                                                      int e) {
-  const float cf = (float)cap;
-  return fx_bits(x < cf ? x : cf, e);
+  return (unsigned long long)fx_term(x, cap, e);
 }
 
 __device__ __forceinline__ int row_of(const DParams &p, int b, int g, int h,
@@ -2790,6 +2795,7 @@ __device__ __forceinline__ void row_certificate(const DParams &p, CertShare sh,
     z.s_full = sqrt(a * a * (double)y1 * (double)y1 + 2.0 * tv * l);
     const float af = (float)a, lf = (float)l;
     z.s_full_f = __builtin_amdgcn_sqrtf(af * af * y1 * y1 + 2.0f * (float)tv * lf);
+    z.ab1sq = af * af * y1 * y1;
     const double e0 = (tb + a * (double)y1 + z.s_full) / dnorm;
     z.eps0 = e0;
     z.eps1 = (float)e0;
@@ -2871,23 +2877,25 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
   // ---- keys: histogram and totals (the register tokens keep their terms)
   // (KEEP: a launch small enough to fit at the lower occupancy the extra
   // registers cost)
+  // (s8 holds each register token's w~ from here on)
   unsigned long long key8[kSelIt];
   float bi8[KEEP ? kSelIt : 1], lw8[KEEP ? kSelIt : 1], rb8[KEEP ? kSelIt : 1];
-  unsigned long long tx[2] = {0ull, 0ull};
+  double tx[2] = {0.0, 0.0};  // exact integers (fx_term)
 #pragma unroll
   for (int it = 0; it < kSelIt; ++it) {
     key8[it] = 0ull;
     if (!(r8[it] < 1.0f)) continue;
     Terms t;
     key8[it] = key_of(pos_of(it), r8[it], s8[it], t);
+    s8[it] = t.wt;
     if constexpr (KEEP) {
       bi8[it] = t.bi;
       lw8[it] = t.lam * t.wt;
       rb8[it] = t.rb;
     }
     atomicAdd(&s_hist[(int)(key8[it] >> sel_off(0))], 1u);
-    tx[0] += sat_fx(t.bi, capb, eb);
-    tx[1] += sat_fx(t.vi, capv, ev);
+    tx[0] += fx_term(t.bi, capb, eb);
+    tx[1] += fx_term(t.vi, capv, ev);
   }
   // long rows: the rest in batches of kSelIt tokens (recomputed below)
   auto load_batch = [&](int it0, float (&rb)[kSelIt], float (&sb)[kSelIt]) {
@@ -2908,11 +2916,11 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
       Terms t;
       const unsigned long long key = key_of(pos_of(it0 + k), rb[k], sb[k], t);
       atomicAdd(&s_hist[(int)(key >> sel_off(0))], 1u);
-      tx[0] += sat_fx(t.bi, capb, eb);
-      tx[1] += sat_fx(t.vi, capv, ev);
+      tx[0] += fx_term(t.bi, capb, eb);
+      tx[1] += fx_term(t.vi, capv, ev);
     }
   }
-  blk_reduce<unsigned long long, 2, kBlock>(tx);
+  blk_reduce<double, 2, kBlock>(tx);  // (exact: integers below 2^53)
   // ---- local bounds: thread t owns bins [8 t, 8 t + 8). Tier 0 is the
   // smallest bin edge with at most capw / 4 keys at or above it, tier 1 the
   // same for capw; c0 = keys at or above the tier-0 edge.
@@ -2962,8 +2970,9 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
   uint32_t below = 0u, below1 = 0u;
   double dsum[4] = {0.0, 0.0, 0.0, 0.0};
   uint32_t o0 = 0u, o1 = 0u;  // slots taken by earlier batches, per tier
+  // (wb: each token's w~)
   auto emit_batch = [&](const unsigned long long (&kb)[kSelIt],
-                        const float (&rb)[kSelIt], const float (&sb)[kSelIt],
+                        const float (&rb)[kSelIt], const float (&wb)[kSelIt],
                         const float *kbi, const float *klw, const float *krb) {
     uint32_t n0 = 0u, n1 = 0u;
 #pragma unroll
@@ -2990,7 +2999,7 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
           vd = (double)klw[k] * (double)klw[k] * (double)qr_of(rb[k]);
           tb = krb[k];
         } else {
-          const Terms t = token_terms_w(expf(sb[k] - m), rb[k], lr, key_pos(kb[k]));
+          const Terms t = token_terms_w(wb[k], rb[k], lr, key_pos(kb[k]));
           direct_terms(t, bd, vd);
           tb = t.rb;
         }
@@ -3008,7 +3017,7 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
       }
       if (slot < (uint32_t)capw) {
         p.candk[seg + slot] = kb[k];
-        p.candw[seg + slot] = expf(sb[k] - m);
+        p.candw[seg + slot] = wb[k];
         p.candq[seg + slot] = rb[k];
       }
     }
@@ -3029,6 +3038,7 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
       if (!(rb[k] < 1.0f)) continue;
       Terms t;
       kb[k] = key_of(pos_of(it0 + k), rb[k], sb[k], t);
+      sb[k] = t.wt;
     }
     emit_batch(kb, rb, sb, nullptr, nullptr, nullptr);
   }
@@ -3053,8 +3063,8 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
     p.dpart[4 * at + 1] = dsum[1] + dsum[3];
     p.dpart[4 * at + 2] = dsum[0];
     p.dpart[4 * at + 3] = dsum[1];
-    p.tpart[2 * at] = tx[0];
-    p.tpart[2 * at + 1] = tx[1];
+    p.tpart[2 * at] = (unsigned long long)tx[0];
+    p.tpart[2 * at + 1] = (unsigned long long)tx[1];
   }
 }
 
