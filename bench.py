@@ -545,8 +545,27 @@ def measure(config, args, dev, headline, weights=0):
     ab = (algorithmic_bytes_sketch2 if sk2 else algorithmic_bytes)(
         w, counts, int(np.sum(ks > 0)), args.estimator)
     cand = ab["kernels"]
-    # the roofline object covers the longest-running HBM-bound kernel
-    dom = max(cand, key=lambda k: ph_us[names.index(k)])
+
+    def solo_us(k, count):
+        """Average duration of kernel k over `count` steps, from two events
+        recorded by its own dispatch (no other events in those steps)."""
+        j = names.index(k)
+        pairs = [timed_events(2) for _ in range(count)]
+        torch.cuda.synchronize()
+        for i in range(count):
+            step.args.q = vk._ptr(t_qs[i % nq])
+            evl = [None] * (P + 1)
+            evl[j], evl[j + 1] = pairs[i]
+            step.set_phase_events(evl)
+            step.launch()
+        torch.cuda.synchronize()
+        step.set_phase_events(None)
+        return sum(e0.elapsed_time(e1) for e0, e1 in pairs) * 1e3 / count
+
+    # each counted kernel timed alone (events between every kernel add gaps
+    # of their own); the roofline object covers the longest-running one
+    solo = {k: solo_us(k, nprof) for k in cand}
+    dom = max(cand, key=lambda k: solo[k])
     di = names.index(dom)
 
     # timed steps, no events: the step time
@@ -582,7 +601,7 @@ def measure(config, args, dev, headline, weights=0):
     t_gather = ph_us[names.index("fetch")] * 1e-6
 
     def hbm(k, v):
-        t = ph_us[names.index(k)] * 1e-6
+        t = solo[k] * 1e-6
         e = {"us": round(float(t * 1e6), 2), "bytes": int(v),
              "gbs": round(v / t / 1e9, 1),
              "frac": round(v / t / (HBM_PEAK_GBS * 1e9), 4)}
@@ -614,7 +633,8 @@ def measure(config, args, dev, headline, weights=0):
                            "all_candidates": int(paths[2]),
                            "streaming": int(paths[3])},
         "kernel_us_profiled": {k: round(float(v), 2) for k, v in zip(names, ph_us)},
-        # every HBM-bound kernel: algorithmic bytes over its profiled time
+        # every counted kernel: its compulsory bytes over its own duration
+        # (timed alone, like the roofline kernel)
         "kernels_hbm": {k: hbm(k, v) for k, v in cand.items()},
         "roofline": {"bound": "hbm", "kernel": dom, "kernel_us": t_dom * 1e6,
                      "achieved": achieved,
