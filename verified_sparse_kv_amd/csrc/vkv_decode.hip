@@ -550,41 +550,68 @@ __device__ __forceinline__ void p0_finish(const DParams &p, int b, int g,
                                           uint32_t n_h) {
   const int np = p.nch + p.ncr;
   const int bg = b * p.G + g;
+  constexpr int W = kBlock / kWave;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  // two LDS rounds: the shifts (and the H count), then the sums rescaled to
+  // them; each value folded per wave, the waves combined in wave order
+  __shared__ float s_mx[W][GRP];
+  __shared__ uint32_t s_nh[W];
+  __shared__ double s_v[W][4 * GRP];
   float mx[GRP];
 #pragma unroll
-  for (int h = 0; h < GRP; ++h) mx[h] = acc[h].m;
-  blk_combine<float, GRP, kBlock, OpMax<float>>(mx);
-  constexpr int HG = GRP < 4 ? GRP : 4;  // heads per reduction
-  uint32_t nh[1] = {n_h};
-  blk_reduce<uint32_t, 1, kBlock>(nh);
+  for (int h = 0; h < GRP; ++h) mx[h] = wave_fold<float, OpMax<float>>(acc[h].m);
+  const uint32_t nhw = wave_fold<uint32_t, OpSum<uint32_t>>(n_h);
+  if (lane == 0) {
 #pragma unroll
-  for (int h0 = 0; h0 < GRP; h0 += HG) {
-    double v0[3 * HG], lbm[HG];
-#pragma unroll
-    for (int k = 0; k < HG; ++k) {
-      const P0Acc &a = acc[h0 + k];
-      const float f = expf(a.m - mx[h0 + k]);  // 0 for a thread without L
-      v0[3 * k] = (double)(a.sw * f);
-      v0[3 * k + 1] = (double)a.sr;
-      v0[3 * k + 2] = (double)a.cnt;
-      lbm[k] = (double)(a.lb * f);
-    }
-    blk_reduce<double, 3 * HG, kBlock>(v0);
-    blk_combine<double, HG, kBlock, OpMax<double>>(lbm);
-    if (threadIdx.x == 0) {
-#pragma unroll
-      for (int k = 0; k < HG; ++k) {
-        const int row = row_of(p, b, g, h0 + k, GRP);
-        p.pmax[(size_t)row * np + c] = mx[h0 + k];
-        double *rec = p.p0part + ((size_t)row * np + c) * 4;
-        rec[0] = v0[3 * k];
-        rec[1] = v0[3 * k + 1];
-        rec[2] = v0[3 * k + 2];
-        rec[3] = lbm[k];
-      }
-    }
+    for (int h = 0; h < GRP; ++h) s_mx[wave][h] = mx[h];
+    s_nh[wave] = nhw;
   }
-  if (threadIdx.x == 0) p.hpart[(size_t)bg * np + c] = nh[0];
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < GRP; ++h) {
+    float m = s_mx[0][h];
+#pragma unroll
+    for (int w = 1; w < W; ++w) m = OpMax<float>::f(m, s_mx[w][h]);
+    mx[h] = m;
+  }
+  double v[4 * GRP];
+#pragma unroll
+  for (int h = 0; h < GRP; ++h) {
+    const P0Acc &a = acc[h];
+    const float f = expf(a.m - mx[h]);  // 0 for a thread without L
+    v[4 * h] = wave_fold<double, OpSum<double>>((double)(a.sw * f));
+    v[4 * h + 1] = wave_fold<double, OpSum<double>>((double)a.sr);
+    v[4 * h + 2] = wave_fold<double, OpSum<double>>((double)a.cnt);
+    v[4 * h + 3] = wave_fold<double, OpMax<double>>((double)(a.lb * f));
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int k = 0; k < 4 * GRP; ++k) s_v[wave][k] = v[k];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int h = 0; h < GRP; ++h) {
+      double t[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) t[k] = s_v[0][4 * h + k];
+#pragma unroll
+      for (int w = 1; w < W; ++w) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k) t[k] = OpSum<double>::f(t[k], s_v[w][4 * h + k]);
+        t[3] = OpMax<double>::f(t[3], s_v[w][4 * h + 3]);
+      }
+      const int row = row_of(p, b, g, h, GRP);
+      p.pmax[(size_t)row * np + c] = mx[h];
+      double *rec = p.p0part + ((size_t)row * np + c) * 4;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) rec[k] = t[k];
+    }
+    uint32_t nh = s_nh[0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) nh += s_nh[w];
+    p.hpart[(size_t)bg * np + c] = nh;
+  }
 }
 
 // Binary shrinkage: scan chunk c of group (b, g) clears its share of the
@@ -639,7 +666,7 @@ __device__ __forceinline__ void scan_setup(const DParams &p, int c, int g,
   }
 }
 
-template <int GRP, int SD>
+template <int GRP, int SD, int UNR>
 __device__ __forceinline__ void scan_body(const DParams &p, int c, int g,
                                           int b) {
   // 16 sketch dimensions (32 bytes) per lane: two lanes per token at
@@ -658,10 +685,10 @@ __device__ __forceinline__ void scan_body(const DParams &p, int c, int g,
   const int base = c * p.chunk;
   const int lim = min(base + p.chunk, p.n);
   // sub-batches of SUB tokens, UNR per thread (LPT lanes per token); the
-  // next sub-batch is loaded while one is used (one token per lane: the
-  // registers of a second would cost the launch's resident workgroups a
-  // wave per SIMD)
-  constexpr int UNR = 1;
+  // next sub-batch is loaded while one is used. Large launches take one
+  // token per lane (the registers of a second would cost the launch's
+  // resident workgroups a wave per SIMD); a launch of 512-token chunks
+  // loads its whole chunk at once (one round trip instead of four)
   constexpr int SUB = UNR * TPI;
   static_assert(kChunk % SUB == 0, "chunk");
   uint4 raw[UNR][2], nraw[UNR][2];
@@ -683,7 +710,8 @@ __device__ __forceinline__ void scan_body(const DParams &p, int c, int g,
   load_sub(base, raw, rv);
   scan_setup<GRP>(p, c, g, b);
   // projected, pre-scaled queries: stage q and P_g in LDS, then one output
-  // per thread
+  // per thread (loaded after the chunk's rows: measured at batch 1, loading
+  // them first made the launch 2.5 us longer)
   {
     __shared__ float s_proj[kHeadDim * SD];
     __shared__ float s_q[GRP][kHeadDim];
@@ -720,7 +748,8 @@ __device__ __forceinline__ void scan_body(const DParams &p, int c, int g,
   uint32_t n_h = 0;
   bool bad = false;
   for (int sb = base; sb < lim; sb += SUB) {
-    if (sb + SUB < lim) load_sub(sb + SUB, nraw, nrv);
+    // (a sub-batch that covers the chunk has no next one: no second buffer)
+    if (SUB < kChunk && sb + SUB < lim) load_sub(sb + SUB, nraw, nrv);
 #pragma unroll
     for (int k = 0; k < UNR; ++k) {
       const int i = sb + k * TPI + (int)threadIdx.x / LPT;
@@ -756,11 +785,13 @@ __device__ __forceinline__ void scan_body(const DParams &p, int c, int g,
         }
       }
     }
+    if constexpr (SUB < kChunk) {
 #pragma unroll
-    for (int k = 0; k < UNR; ++k) {
-      raw[k][0] = nraw[k][0];
-      raw[k][1] = nraw[k][1];
-      rv[k] = nrv[k];
+      for (int k = 0; k < UNR; ++k) {
+        raw[k][0] = nraw[k][0];
+        raw[k][1] = nraw[k][1];
+        rv[k] = nrv[k];
+      }
     }
   }
   // each head's accumulator, from the lanes that keep it
@@ -1021,11 +1052,11 @@ __device__ __forceinline__ void resident_body(const DParams &p, int c, int g,
 // ------------------------------------------------------------ front launch
 // Sketch scan (blockIdx.x < nch) and resident logits (the rest) in one
 // launch: they read disjoint inputs and write disjoint outputs.
-template <int GRP, int SD>
+template <int GRP, int SD, int UNR>
 __global__ __launch_bounds__(kBlock) void dk_front(DParams p) {
   const int x = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   if (x < p.nch)
-    scan_body<GRP, SD>(p, x, g, b);
+    scan_body<GRP, SD, UNR>(p, x, g, b);
   else
     resident_body<GRP>(p, x - p.nch, g, b);
 }
@@ -2019,14 +2050,37 @@ __device__ __forceinline__ float row_pass0(const DParams &p, int row, int bg,
                                            double (&v)[kBetaRec]) {
   const int np = p.nch + p.ncr;
   const int lane = threadIdx.x % kWave;
-  // (every wave on its own: lane-strided shares folded by DPP)
+  // (every wave on its own: lane-strided shares folded by DPP; the first
+  // kPre shares of each lane, records included, loaded before any is used)
+  constexpr int kPre = 2;
+  float pmv[kPre];
+  double rc[kPre][4];
+#pragma unroll
+  for (int k = 0; k < kPre; ++k) {
+    const int t = lane + k * kWave;
+    pmv[k] = t < np ? p.pmax[(size_t)row * np + t] : -INFINITY;
+    const double *rec = p.p0part + ((size_t)row * np + t) * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rc[k][e] = t < p.nch ? rec[e] : 0.0;
+  }
   float pm = -INFINITY;
-  for (int t = lane; t < np; t += kWave)
+#pragma unroll
+  for (int k = 0; k < kPre; ++k) pm = fmaxf(pm, pmv[k]);
+  for (int t = lane + kPre * kWave; t < np; t += kWave)
     pm = fmaxf(pm, p.pmax[(size_t)row * np + t]);
   const float m = wave_fold<float, OpMax<float>>(pm);
 #pragma unroll
   for (int k = 0; k < kBetaRec; ++k) v[k] = 0.0;
-  for (int t = lane; t < p.nch; t += kWave) {
+#pragma unroll
+  for (int k = 0; k < kPre; ++k) {
+    if (!(lane + k * kWave < p.nch) || !(rc[k][0] > 0.0)) continue;
+    const double f = exp((double)pmv[k] - (double)m);
+    v[0] += rc[k][0] * f;
+    v[1] += rc[k][1];
+    v[2] += rc[k][2];
+    v[3] = fmax(v[3], rc[k][3] * f);
+  }
+  for (int t = lane + kPre * kWave; t < p.nch; t += kWave) {
     const double *rec = p.p0part + ((size_t)row * np + t) * 4;
     if (!(rec[0] > 0.0)) continue;
     const double f = exp((double)p.pmax[(size_t)row * np + t] - (double)m);
@@ -2920,7 +2974,8 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
       tx[1] += fx_term(t.vi, capv, ev);
     }
   }
-  blk_reduce<double, 2, kBlock>(tx);  // (exact: integers below 2^53)
+  // (tx: exact integers below 2^53, summed with the others at the end)
+  __syncthreads();  // the histogram is complete
   // ---- local bounds: thread t owns bins [8 t, 8 t + 8). Tier 0 is the
   // smallest bin edge with at most capw / 4 keys at or above it, tier 1 the
   // same for capw; c0 = keys at or above the tier-0 edge.
@@ -3042,13 +3097,45 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
     }
     emit_batch(kb, rb, sb, nullptr, nullptr, nullptr);
   }
+  // the workgroup's totals in one LDS round (thread 0 writes them): each
+  // value folded per wave, the waves combined in wave order
   {
-    uint32_t bm[2] = {below, below1};
-    blk_combine<uint32_t, 2, kBlock, OpMax<uint32_t>>(bm);
-    below = bm[0];
-    below1 = bm[1];
+    constexpr int W = kBlock / kWave;
+    __shared__ double s_fd[W][6];
+    __shared__ uint32_t s_fb[W][2];
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    double fd[6] = {tx[0], tx[1], dsum[0], dsum[1], dsum[2], dsum[3]};
+#pragma unroll
+    for (int k = 0; k < 6; ++k) fd[k] = wave_fold<double, OpSum<double>>(fd[k]);
+    const uint32_t b0 = wave_fold<uint32_t, OpMax<uint32_t>>(below);
+    const uint32_t b1 = wave_fold<uint32_t, OpMax<uint32_t>>(below1);
+    if (lane == 0) {
+#pragma unroll
+      for (int k = 0; k < 6; ++k) s_fd[wave][k] = fd[k];
+      s_fb[wave][0] = b0;
+      s_fb[wave][1] = b1;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+#pragma unroll
+      for (int k = 0; k < 6; ++k) {
+        fd[k] = s_fd[0][k];
+#pragma unroll
+        for (int w = 1; w < W; ++w) fd[k] = OpSum<double>::f(fd[k], s_fd[w][k]);
+      }
+      below = s_fb[0][0];
+      below1 = s_fb[0][1];
+#pragma unroll
+      for (int w = 1; w < W; ++w) {
+        below = OpMax<uint32_t>::f(below, s_fb[w][0]);
+        below1 = OpMax<uint32_t>::f(below1, s_fb[w][1]);
+      }
+      tx[0] = fd[0];
+      tx[1] = fd[1];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) dsum[k] = fd[2 + k];
+    }
   }
-  blk_reduce<double, 4, kBlock>(dsum);
   if (threadIdx.x == 0) {
     // per tier: candidates, bound, and over the tokens not written in that
     // tier the max of b_i and the float64 sums
@@ -3633,26 +3720,16 @@ __device__ __forceinline__ void gather_attend(const DParams &p, int j, int g,
 }
 
 // ------------------------------------------------------------ attention
-// Whether position pos is in F_h of this row (the planning marked it).
-__device__ __forceinline__ bool in_fetch(const DParams &p, int row, int pos) {
-  return (p.hbits[(size_t)row * p.nwords + pos / 32] >> (pos % 32)) & 1u;
-}
-
-// Coefficient of one resident row for one head: w on H and on F_h, and
-// lambda w / r on S \ F_h.
-template <int GRP>
-__device__ __forceinline__ float resident_alpha(const DParams &p,
-                                                const RowState &rs, int row,
-                                                int pos, float ri, float ell) {
-  const float w = expf(ell - rs.m);
-  if (ri >= 1.0f || in_fetch(p, row, pos)) return w;
-  const Terms t = token_terms(p.shat[(size_t)row * p.n + pos], ri, rs.m,
-                              lam_rule((float)rs.beta, p.est, rs.bkey), pos);
-  return t.lam * w / ri;
-}
-
 // Partial x < ncr of a KV head's attention: a share of the resident rows,
-// written as (shift, sum of weights, weighted sum of V) per head.
+// written as (shift, sum of weights, weighted sum of V) per head. Rows go in
+// batches of kResBatch: first every row's coefficient per head, once (one
+// thread per row, the loads of its rows issued together), into LDS; then
+// the V rows, 16 lanes per row and kResUnroll rows per lane in flight. (A
+// loop that took position, r and the coefficient inside each row's V step
+// waited on three dependent loads per row, and behind host reads when the
+// compute unit also ran a gather.)
+constexpr int kResBatch = 512;
+constexpr int kResUnroll = 4;
 template <int GRP>
 __device__ __forceinline__ void attn_part(const DParams &p, int x, int g,
                                           int b) {
@@ -3660,9 +3737,11 @@ __device__ __forceinline__ void attn_part(const DParams &p, int x, int g,
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int u = lane % 16;             // 8 dims per lane
   const int slot = threadIdx.x / 16;   // row slot within an iteration
+  constexpr int kSlots = kBlock / 16;
   __shared__ RowState s_rs[GRP];
   __shared__ float s_o[kBlock / kWave][GRP][kHeadDim];
   __shared__ float s_d[kBlock / kWave][GRP];
+  __shared__ float s_al[kResBatch][GRP];  // coefficients; -1: row skipped
   if (threadIdx.x < GRP) s_rs[threadIdx.x] = p.rows[row_of(p, b, g, threadIdx.x, GRP)];
   __syncthreads();
   const float *rr = p.r + (size_t)bg * p.ns;
@@ -3679,28 +3758,89 @@ __device__ __forceinline__ void attn_part(const DParams &p, int x, int g,
     int lo, hi;
     split_range(cnt, p.ncr, x, lo, hi);
     const int32_t *ridx = p.ridx + (size_t)bg * p.cap;
-    for (int j0 = lo; j0 < hi; j0 += kBlock / 16) {
-      const int j = j0 + slot;
-      if (j >= hi) continue;
-      const int pos = ridx[j];
-      if (pos < 0 || pos >= p.n) continue;
-      const float ri = rr[pos];
-      const uint4 raw = *reinterpret_cast<const uint4 *>(
-          p.rkv + ((size_t)bg * p.cap + j) * 2 * kHeadDim + kHeadDim + u * 8);
-      float vv[8];
-      unpack8(raw, vv);
+    constexpr int RPT = kResBatch / kBlock;  // rows per thread in a batch
+    for (int c0 = lo; c0 < hi; c0 += kResBatch) {
+      const int c1 = min(c0 + kResBatch, hi);
+      // the coefficients (w on H and on F_h, lambda w / r on S minus F_h):
+      // positions, then r, F_h bits, logits and planning logits of all of
+      // this thread's rows, then the arithmetic
+      int pos[RPT];
 #pragma unroll
-      for (int h = 0; h < GRP; ++h) {
-        const int row = row_of(p, b, g, h, GRP);
-        const float alpha = resident_alpha<GRP>(
-            p, s_rs[h], row, pos, ri, p.ell[(size_t)row * p.cap + j]);
-        dsum[h] += alpha;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) acc[h][k] = __builtin_fmaf(alpha, vv[k], acc[h][k]);
+      for (int k = 0; k < RPT; ++k) {
+        const int j = c0 + k * kBlock + (int)threadIdx.x;
+        pos[k] = j < c1 ? ridx[j] : -1;
       }
+      float ri[RPT], el[RPT][GRP], sv[RPT][GRP];
+      uint32_t fw[RPT][GRP];
+#pragma unroll
+      for (int k = 0; k < RPT; ++k) {
+        const int j = c0 + k * kBlock + (int)threadIdx.x;
+        const bool ok = pos[k] >= 0 && pos[k] < p.n;
+        const int ps = ok ? pos[k] : 0;
+        ri[k] = ok ? rr[ps] : 1.0f;
+#pragma unroll
+        for (int h = 0; h < GRP; ++h) {
+          const int row = row_of(p, b, g, h, GRP);
+          el[k][h] = ok ? p.ell[(size_t)row * p.cap + j] : 0.0f;
+          fw[k][h] = ok ? p.hbits[(size_t)row * p.nwords + ps / 32] : 0u;
+          sv[k][h] = ok ? p.shat[(size_t)row * p.n + ps] : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < RPT; ++k) {
+        const int jj = k * kBlock + (int)threadIdx.x;
+        if (c0 + jj >= c1) continue;
+        const bool ok = pos[k] >= 0 && pos[k] < p.n;
+#pragma unroll
+        for (int h = 0; h < GRP; ++h) {
+          float al = -1.0f;
+          if (ok) {
+            const RowState &rs = s_rs[h];
+            const float w = expf(el[k][h] - rs.m);
+            if (ri[k] >= 1.0f || ((fw[k][h] >> (pos[k] % 32)) & 1u)) {
+              al = w;
+            } else {
+              const Terms t = token_terms(sv[k][h], ri[k], rs.m,
+                                          lam_rule((float)rs.beta, p.est, rs.bkey), pos[k]);
+              al = t.lam * w / ri[k];
+            }
+            dsum[h] += al;
+          }
+          s_al[jj][h] = al;
+        }
+      }
+      __syncthreads();
+      // the V rows: 16 lanes per row, kResUnroll rows per lane in flight
+      const int nb = c1 - c0;
+      for (int q0 = 0; q0 < nb; q0 += kSlots * kResUnroll) {
+        uint4 raw[kResUnroll];
+#pragma unroll
+        for (int k = 0; k < kResUnroll; ++k) {
+          const int jj = q0 + k * kSlots + slot;
+          raw[k] = jj < nb ? *reinterpret_cast<const uint4 *>(
+                                 p.rkv + ((size_t)bg * p.cap + c0 + jj) * 2 * kHeadDim +
+                                 kHeadDim + u * 8)
+                           : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int k = 0; k < kResUnroll; ++k) {
+          const int jj = q0 + k * kSlots + slot;
+          if (jj >= nb || s_al[jj][0] < 0.0f) continue;
+          float vv[8];
+          unpack8(raw[k], vv);
+#pragma unroll
+          for (int h = 0; h < GRP; ++h) {
+            const float alpha = s_al[jj][h];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] = __builtin_fmaf(alpha, vv[e], acc[h][e]);
+          }
+        }
+      }
+      __syncthreads();  // s_al is rewritten by the next batch
     }
   }
-  // reduce the four 16-lane row slots of each wave, then the waves
+  // reduce the four 16-lane row slots of each wave, then the waves (the
+  // weight sums were formed one thread per row: over all 64 lanes)
 #pragma unroll
   for (int h = 0; h < GRP; ++h) {
 #pragma unroll
@@ -3710,10 +3850,7 @@ __device__ __forceinline__ void attn_part(const DParams &p, int x, int g,
       v += shfl_xor(v, 32);
       acc[h][k] = v;
     }
-    float d = dsum[h];
-    d += shfl_xor(d, 16);
-    d += shfl_xor(d, 32);
-    dsum[h] = d;
+    dsum[h] = wave_sum(dsum[h]);
   }
   if (lane < 16) {
 #pragma unroll
@@ -3809,11 +3946,21 @@ __device__ __forceinline__ void attn_merge_row(const DParams &p, int row) {
 // The gather (bound by the host link) and the attention over the resident
 // rows, which does not depend on it, in one launch: blocks x < ncr take a
 // share of the resident rows, the others a share of the fetch bitmap.
+// One launch of both kinds of workgroups, every resident part first in
+// dispatch order: gather workgroups hold their compute-unit slots for the
+// whole transfer, so a resident part queued behind them would start only
+// once a gather has ended (at batch 16 the launch holds three times the
+// workgroups that fit at once).
 template <int GRP>
 __global__ __launch_bounds__(kBlock) void dk_fetch(DParams p) {
-  const int x = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  if (x < p.ncr) attn_part<GRP>(p, x, g, b);
-  else gather_attend<GRP>(p, x - p.ncr, g, b);
+  const int x = (int)blockIdx.x, nres = p.ncr * p.G * p.B;
+  if (x < nres) {
+    const int gb = x / p.ncr;
+    attn_part<GRP>(p, x % p.ncr, gb % p.G, gb / p.G);
+  } else {
+    const int y = x - nres, gb = y / p.ncf;
+    gather_attend<GRP>(p, y % p.ncf, gb % p.G, gb / p.G);
+  }
 }
 
 // The merge of each row's partials. Grid (Hq, B).
@@ -3875,9 +4022,13 @@ hipError_t run(const DParams &p, hipStream_t s, int sd, void **events) {
   else if (sk2)
     mark.launch(k, dk_front2<GRP>, gfront, blk, p);
   else if (sd == 32)
-    mark.launch(k, dk_front<GRP, 32>, gfront, blk, p);
+    mark.launch(k, p.chunk == kChunk ? dk_front<GRP, 32, kChunk / kBlock * 2>
+                                     : dk_front<GRP, 32, 1>,
+                gfront, blk, p);
   else
-    mark.launch(k, dk_front<GRP, 16>, gfront, blk, p);
+    mark.launch(k, p.chunk == kChunk ? dk_front<GRP, 16, kChunk / kBlock>
+                                     : dk_front<GRP, 16, 1>,
+                gfront, blk, p);
   mark(++k);
   // 2-bit sketch: the shortlist with its exact logits, then pass 0
   if (sk2)
@@ -3921,7 +4072,7 @@ hipError_t run(const DParams &p, hipStream_t s, int sd, void **events) {
   mark.launch(k, dk_rwalk<GRP>, gone, dim3(kPlanThreads), p);
   mark(++k);
   mark.launch(k, dk_fetch<GRP>,
-              dim3((unsigned)(p.ncr + p.ncf), (unsigned)p.G, (unsigned)p.B), blk, p);
+              dim3((unsigned)((p.ncr + p.ncf) * p.G * p.B)), blk, p);
   mark(++k);
   mark.launch(k, dk_attn, dim3((unsigned)p.Hq, (unsigned)p.B), blk, p);
   mark(++k);
@@ -3972,9 +4123,18 @@ DecodeLayout decode_layout(const vkv_decode_args &a) {
   // the KV head with the most rows to fetch keeps enough rows in flight
   // at the end (measured: 1.3% faster steps at 8 KV heads, slower at 32
   // and 128)
-  const int ncf = groups_ll <= 8 ? kGatherWGSmall : kGatherWG;
+  // Beyond one workgroup per compute unit, the launch keeps its workgroups
+  // within what runs at once (two per compute unit at the kernel's register
+  // and LDS use): gather workgroups hold their slots for the whole
+  // transfer, so any workgroup past that count starts only when a gather
+  // ends (measured at batch 16: resident parts then ended 190 us after the
+  // gathers).
+  const long long per_head = std::max<long long>(2, 512 / std::max<long long>(1, groups_ll));
+  const int ncf = (int)std::min<long long>(groups_ll <= 8 ? kGatherWGSmall : kGatherWG,
+                                           per_head - 1);
   const int fit = (int)(256 / std::max<long long>(1, groups_ll)) - ncf;
-  L.ncr = std::max(1, std::min(std::min(std::min(target, 32), std::max(fit, 8)),
+  const int room = fit >= 1 ? fit : (int)std::max<long long>(1, per_head - ncf);
+  L.ncr = std::max(1, std::min(std::min(std::min(target, 32), room),
                                (rmax + 63) / 64));
   L.ncf = ncf;
   L.npad = (L.ncr + L.ncf + 3) / 4 * 4;
