@@ -3505,8 +3505,13 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rwalk(DParams p) {
 // attention over the resident rows running in the same launch (host loads
 // queued in a compute unit delay every other load issued there).
 constexpr int kGatherWG = 8;        // gather workgroups per KV head
-constexpr int kGatherWGSmall = 12;  // ... when the launch has <= 8 KV heads
-constexpr int kGatherBatch = 8;   // rows per half-wave with loads in flight
+constexpr int kGatherWGSmall = 24;  // ... when the launch has <= 8 KV heads
+// Rows per half-wave with loads in flight (a batch in use and the next in
+// flight). Measured at 1, 2, 4 and 8: two gave the shortest steps at batch
+// 1, 4 and 16 (the launch keeps enough rows in flight for the host link,
+// and the host loads queued in a compute unit delay less the loads of a
+// resident part sharing it).
+constexpr int kGatherBatch = 2;
 
 // Gather and attention over the fetched rows by workgroup j of a KV head:
 // rows [j R / ncf, (j + 1) R / ncf) of the KV head's ascending
@@ -3881,7 +3886,7 @@ __device__ __forceinline__ void attn_part(const DParams &p, int x, int g,
 // consecutive and read as 16-byte vectors, all loads issued first. Partial
 // slots past ncr + ncf (padding) are never read into the sum.
 __device__ __forceinline__ void attn_merge_row(const DParams &p, int row) {
-  const int np = p.ncr + p.ncf;  // at most 64 (32 resident, <= 12 fetched)
+  const int np = p.ncr + p.ncf;  // at most 56 (32 resident, <= 24 fetched)
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   __shared__ float s_sc[64];
   __shared__ float s_half[kHeadDim];
@@ -4121,8 +4126,8 @@ DecodeLayout decode_layout(const vkv_decode_args &a) {
   // workgroup per compute unit where the batch allows)
   // gather workgroups per KV head: more when the batch is small, so that
   // the KV head with the most rows to fetch keeps enough rows in flight
-  // at the end (measured: 1.3% faster steps at 8 KV heads, slower at 32
-  // and 128)
+  // at the end (measured at 8 KV heads with two rows per half-wave in
+  // flight: 24 per KV head 1% faster steps than 12 or 32)
   // Beyond one workgroup per compute unit, the launch keeps its workgroups
   // within what runs at once (two per compute unit at the kernel's register
   // and LDS use): gather workgroups hold their slots for the whole
