@@ -1086,6 +1086,7 @@ constexpr int kSk2Tok = kSk2Sub / kBlock;  // tokens per thread and sub-batch
 constexpr int kShortMax = 1024;            // largest shortlist
 constexpr int kShortKPT = 32;              // shortlist keys per thread and tile
 constexpr int kShortTile = kShortKPT * kPlanThreads;  // positions per tile
+constexpr int kShortSWG = 4;  // workgroups per KV head writing the logits of S
 
 // fp32 -> an unsigned key in the same order (0 is never produced for a
 // finite value, so it marks tokens that are not eligible).
@@ -1221,12 +1222,33 @@ __device__ __forceinline__ uint32_t plan_excl_scan(uint32_t v, uint32_t *s_w,
 // n_short eligible tokens (L outside S) with the largest keys, equal keys by
 // position, found by an 11/11/10-bit radix select over the scan's keys;
 // their key rows read from host memory and scored exactly for the group's
-// heads, those logits written over the sketch logits, and likewise the
-// resident logits over the sketch logits of S.
+// heads, those logits written over the sketch logits. kShortSWG more
+// workgroups per KV head write the resident logits over the sketch logits
+// of S (disjoint positions).
 template <int GRP>
 __global__ __launch_bounds__(kPlanThreads) void dk_short(DParams p) {
   const int g = blockIdx.x, b = blockIdx.y;
   const int bg = b * p.G + g, n = p.n, tid = threadIdx.x;
+  if (blockIdx.z > 0) {
+    // the exact logits of S over the plan's logits: share blockIdx.z - 1 of
+    // the resident rows, beside the select (its scattered stores would
+    // otherwise follow it on the same compute unit)
+    const int cnt = max(0, min(p.rcount[bg], p.cap));
+    int j0, j1;
+    split_range(cnt, kShortSWG, (int)blockIdx.z - 1, j0, j1);
+    const int32_t *ridx = p.ridx + (size_t)bg * p.cap;
+    const float *rr = p.r + (size_t)bg * p.ns;
+    for (int j = j0 + tid; j < j1; j += kPlanThreads) {
+      const int pos = ridx[j];
+      if (pos < 0 || pos >= n || !(rr[pos] < 1.0f)) continue;
+#pragma unroll
+      for (int h = 0; h < GRP; ++h) {
+        const int row = row_of(p, b, g, h, GRP);
+        p.shat[(size_t)row * n + pos] = p.ell[(size_t)row * p.cap + j];
+      }
+    }
+    return;
+  }
   const int lane = tid % kWave;
   constexpr int kWords = kMaxTokens / 32;
   __shared__ uint32_t s_res[kWords];  // resident positions
@@ -1438,17 +1460,6 @@ __global__ __launch_bounds__(kPlanThreads) void dk_short(DParams p) {
       for (int e = 0; e < 16; ++e) a = __builtin_fmaf(s_q[h][part * 16 + e], kf[e], a);
       a = group_sum<8>(a);
       if (ok && part == 0) p.shat[(size_t)row_of(p, b, g, h, GRP) * n + pos] = a * kInvSqrtD;
-    }
-  }
-  // exact logits of S
-  const float *rr = p.r + (size_t)bg * p.ns;
-  for (int j = tid; j < cnt; j += kPlanThreads) {
-    const int pos = ridx[j];
-    if (pos < 0 || pos >= n || !(rr[pos] < 1.0f)) continue;
-#pragma unroll
-    for (int h = 0; h < GRP; ++h) {
-      const int row = row_of(p, b, g, h, GRP);
-      p.shat[(size_t)row * n + pos] = p.ell[(size_t)row * p.cap + j];
     }
   }
 }
@@ -4037,7 +4048,7 @@ hipError_t run(const DParams &p, hipStream_t s, int sd, void **events) {
   mark(++k);
   // 2-bit sketch: the shortlist with its exact logits, then pass 0
   if (sk2)
-    mark.launch(k, dk_short<GRP>, dim3((unsigned)p.G, (unsigned)p.B),
+    mark.launch(k, dk_short<GRP>, dim3((unsigned)p.G, (unsigned)p.B, 1u + kShortSWG),
                 dim3(kPlanThreads), p);
   else
     mark.empty(k);
