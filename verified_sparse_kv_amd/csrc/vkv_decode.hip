@@ -1550,6 +1550,7 @@ constexpr int kBetaLaunchMax = 4;   // Newton passes (pass 0 is in the scan):
                                     // p.nbeta of them, 2 to 4
 constexpr int kBandChunk = 1024;    // band tokens a chunk may store
 constexpr int kBandMax = 2048;      // band tokens a row may be settled from
+constexpr int kBandWave = 512;      // ... by one wave; the whole workgroup above
 constexpr int kMaxChunks = kMaxTokens / kRowChunk;
 constexpr int kBetaPassMax = 96;    // never reached: the bracket shrinks >= 2x
 constexpr int kCandMax = 8192;      // candidates held by the walk
@@ -2178,9 +2179,51 @@ __device__ __forceinline__ BetaState beta_settle(const DParams &p, BetaState st,
     s_br[k] = e.y;
   }
   __syncthreads();
-  // the band's sums and the Newton steps over it by the first wave alone
-  // (its sums fold by DPP: no workgroup barrier per step); the result goes
-  // to the other waves through LDS
+  if (nb > kBandWave) {
+    // a large band: the Newton steps by the whole workgroup, per-thread sums
+    // over a share of the band folded per wave and combined across the
+    // waves in wave order (every thread gets the same sums and takes the
+    // same steps)
+    double bs[3] = {0.0, 0.0, 0.0};  // the band's sums of w~ and rho, its size
+    for (int k = threadIdx.x; k < nb; k += kBlock) {
+      bs[0] += (double)s_bw[k];
+      bs[1] += (double)s_br[k];
+      bs[2] += 1.0;
+    }
+    blk_reduce<double, 3, kBlock>(bs);
+    // the tokens active at every point of the bracket (v: the sums at lo)
+    const double aw = v[0] - bs[0], ar = v[1] - bs[1], ac = v[2] - bs[2];
+    for (int it = 0; it < kBetaPassMax && !st.done; ++it) {
+      double pts[kBetaPts], t[3 * kBetaPts], u[kBetaRec];
+      beta_points(st, pts);
+#pragma unroll
+      for (int k = 0; k < 3 * kBetaPts; ++k) t[k] = 0.0;
+      for (int k = threadIdx.x; k < nb; k += kBlock) {
+        const double w = (double)s_bw[k], rh = (double)s_br[k];
+#pragma unroll
+        for (int j = 0; j < kBetaPts; ++j) {
+          if (w - pts[j] * rh > 0.0) {
+            t[3 * j] += w;
+            t[3 * j + 1] += rh;
+            t[3 * j + 2] += 1.0;
+          }
+        }
+      }
+      blk_reduce<double, 3 * kBetaPts, kBlock>(t);
+#pragma unroll
+      for (int j = 0; j < kBetaPts; ++j) {
+        u[3 * j] = t[3 * j] + aw;
+        u[3 * j + 1] = t[3 * j + 1] + ar;
+        u[3 * j + 2] = t[3 * j + 2] + ac;
+      }
+      u[kBetaRec - 1] = 0.0;
+      st = beta_advance(st, u);
+    }
+    return st;
+  }
+  // a small band: the Newton steps by the first wave alone (its sums fold
+  // by DPP: no workgroup barrier per step); the result goes to the other
+  // waves through LDS
   __shared__ BetaState s_st;
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
