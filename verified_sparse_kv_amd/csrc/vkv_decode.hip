@@ -465,6 +465,32 @@ template <typename T>
 __device__ __forceinline__ T plan_max(T x) {
   return blk_max<T, kPlanThreads>(x);
 }
+// Two sums and two maxima of 64-bit integers over a plan workgroup in one
+// LDS round: each folded per wave, the waves combined in wave order; every
+// thread gets the results.
+__device__ __forceinline__ void plan_sum2_max2(unsigned long long (&v)[4]) {
+  using U = unsigned long long;
+  __shared__ U buf[kPlanWaves][4];
+  v[0] = wave_fold<U, OpSum<U>>(v[0]);
+  v[1] = wave_fold<U, OpSum<U>>(v[1]);
+  v[2] = wave_fold<U, OpMax<U>>(v[2]);
+  v[3] = wave_fold<U, OpMax<U>>(v[3]);
+  __syncthreads();  // an earlier call may still be reading buf
+  if (threadIdx.x % kWave == 0) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) buf[threadIdx.x / kWave][k] = v[k];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) v[k] = buf[0][k];
+#pragma unroll
+  for (int w = 1; w < kPlanWaves; ++w) {
+    v[0] = OpSum<U>::f(v[0], buf[w][0]);
+    v[1] = OpSum<U>::f(v[1], buf[w][1]);
+    v[2] = OpMax<U>::f(v[2], buf[w][2]);
+    v[3] = OpMax<U>::f(v[3], buf[w][3]);
+  }
+}
 
 // Block-wide top two of (value, position) pairs as top2_merge keeps them
 // (the merge does not depend on order), through LDS.
@@ -574,15 +600,17 @@ __device__ __forceinline__ void p0_finish(const DParams &p, int b, int g,
     for (int w = 1; w < W; ++w) m = OpMax<float>::f(m, s_mx[w][h]);
     mx[h] = m;
   }
+  // (a wave's 64 partial sums folded in fp32, its count as an integer; the
+  // waves combined in float64)
   double v[4 * GRP];
 #pragma unroll
   for (int h = 0; h < GRP; ++h) {
     const P0Acc &a = acc[h];
     const float f = expf(a.m - mx[h]);  // 0 for a thread without L
-    v[4 * h] = wave_fold<double, OpSum<double>>((double)(a.sw * f));
-    v[4 * h + 1] = wave_fold<double, OpSum<double>>((double)a.sr);
-    v[4 * h + 2] = wave_fold<double, OpSum<double>>((double)a.cnt);
-    v[4 * h + 3] = wave_fold<double, OpMax<double>>((double)(a.lb * f));
+    v[4 * h] = (double)wave_fold<float, OpSum<float>>(a.sw * f);
+    v[4 * h + 1] = (double)wave_fold<float, OpSum<float>>(a.sr);
+    v[4 * h + 2] = (double)wave_fold<uint32_t, OpSum<uint32_t>>((uint32_t)a.cnt);
+    v[4 * h + 3] = (double)wave_fold<float, OpMax<float>>(a.lb * f);
   }
   if (lane == 0) {
 #pragma unroll
@@ -3366,7 +3394,14 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rwalk(DParams p) {
         kmax = max(kmax, ck[u]);
       }
     }
-    plan_reduce<unsigned long long, 2>(cs);
+    {  // the candidates' sums and key range in one LDS round
+      unsigned long long red[4] = {cs[0], cs[1], kmax, ~kmin};
+      plan_sum2_max2(red);
+      cs[0] = red[0];
+      cs[1] = red[1];
+      kmax = red[2];
+      kmin = ~red[3];
+    }
     // fetching every candidate leaves exactly the tokens not written
     const double e_below =
         eps_of((double)(tot_b - cs[0]) * sbs, (double)(tot_v - cs[1]) * svs,
@@ -3375,8 +3410,6 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rwalk(DParams p) {
       __syncthreads();
       continue;
     }
-    kmax = plan_max<unsigned long long>(kmax);
-    kmin = ~plan_max<unsigned long long>(~kmin);
     if (threadIdx.x == 0) {
       // the first digit starts where the candidates' keys start to differ
       const int span = kmax == kmin ? 0 : 64 - __clzll((long long)(kmax ^ kmin));
@@ -3529,8 +3562,30 @@ __global__ __launch_bounds__(kPlanThreads) void dk_rwalk(DParams p) {
       atomicOr(hb + pos / 32, 1u << (pos % 32));
       if (!((rbits[pos / 32] >> (pos % 32)) & 1u)) atomicOr(fbm + pos / 32, 1u << (pos % 32));
     }
-    plan_reduce<double, 2>(dr);
-    bm = plan_max<uint32_t>(max(bm, below));
+    {  // the rest's float64 sums and its max b_i in one LDS round, for
+       // thread 0: each folded per wave, the waves combined in wave order
+      __shared__ double s_dr[kPlanWaves][2];
+      __shared__ uint32_t s_bm[kPlanWaves];
+      const double d0 = wave_fold<double, OpSum<double>>(dr[0]);
+      const double d1 = wave_fold<double, OpSum<double>>(dr[1]);
+      const uint32_t m0 = wave_fold<uint32_t, OpMax<uint32_t>>(max(bm, below));
+      if (lane == 0) {
+        s_dr[wave][0] = d0;
+        s_dr[wave][1] = d1;
+        s_bm[wave] = m0;
+      }
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        dr[0] = s_dr[0][0];
+        dr[1] = s_dr[0][1];
+        bm = s_bm[0];
+        for (int w = 1; w < kPlanWaves; ++w) {
+          dr[0] = OpSum<double>::f(dr[0], s_dr[w][0]);
+          dr[1] = OpSum<double>::f(dr[1], s_dr[w][1]);
+          bm = OpMax<uint32_t>::f(bm, s_bm[w]);
+        }
+      }
+    }
     if (threadIdx.x == 0) {
       rs.kstar = ws.kstar;
       rs.T = T;
