@@ -1615,7 +1615,7 @@ struct SelArgs {
   int n, ns, nwords, est;  // (ns: positions per KV head in r)
 };
 
-__device__ __attribute__((noinline)) void select_row(const SelArgs p, int row,
+__device__ __forceinline__ void select_row(const SelArgs p, int row,
                                                      int bg, RowState &rs,
                                                      SelLds &lds) {
   const int n = p.n;
@@ -2014,16 +2014,33 @@ __device__ __forceinline__ BetaState beta_advance(BetaState st,
     st.done = 1;
     return st;
   }
-  const double sw = v[3 * jl], sr = v[3 * jl + 1], c = v[3 * jl + 2];
+  // the point jl and the next one, selected by unrolled compares (an index
+  // computed at run time would put the arrays in scratch memory)
+  double sw = 0.0, sr = 0.0, c = 0.0, pl = 0.0, pn = 0.0, cn = 0.0;
+  bool next = false;
+#pragma unroll
+  for (int j = 0; j < kBetaPts; ++j) {
+    if (j == jl) {
+      sw = v[3 * j];
+      sr = v[3 * j + 1];
+      c = v[3 * j + 2];
+      pl = pts[j];
+    }
+    if (j == jl + 1) {
+      cn = v[3 * j + 2];
+      pn = pts[j];
+      next = true;
+    }
+  }
   const double nb = sw / (1.0 + sr);
-  if (jl + 1 < kBetaPts && v[3 * (jl + 1) + 2] == c) {  // h linear up to there
+  if (next && cn == c) {  // h linear up to there
     st.beta = nb;
     st.done = 1;
     return st;
   }
-  double nhi = fmin(st.hi, pts[jl] + (sw - pts[jl] * (1.0 + sr)));
-  if (jl + 1 < kBetaPts) nhi = fmin(nhi, pts[jl + 1]);
-  st.lo = fmax(nb, pts[jl]);
+  double nhi = fmin(st.hi, pl + (sw - pl * (1.0 + sr)));
+  if (next) nhi = fmin(nhi, pn);
+  st.lo = fmax(nb, pl);
   st.hi = nhi;
   st.prev_cnt = c;
   st.beta = st.lo;
@@ -3108,9 +3125,17 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
   double dsum[4] = {0.0, 0.0, 0.0, 0.0};
   uint32_t o0 = 0u, o1 = 0u;  // slots taken by earlier batches, per tier
   // (wb: each token's w~)
+  // (the batch's results are returned, not written through captures: the
+  // captured counters and maxima were otherwise kept in scratch memory)
+  struct EmitRes {
+    uint32_t t0, t1, bl, bl1;
+    double d[4];
+  };
   auto emit_batch = [&](const unsigned long long (&kb)[kSelIt],
                         const float (&rb)[kSelIt], const float (&wb)[kSelIt],
-                        const float *kbi, const float *klw, const float *krb) {
+                        const float *kbi, const float *klw, const float *krb,
+                        uint32_t o0, uint32_t o1) {
+    EmitRes e{0u, 0u, 0u, 0u, {0.0, 0.0, 0.0, 0.0}};
     uint32_t n0 = 0u, n1 = 0u;
 #pragma unroll
     for (int k = 0; k < kSelIt; ++k) {
@@ -3141,14 +3166,14 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
           tb = t.rb;
         }
         if (kb[k] >= lo) {
-          dsum[2] += bd;
-          dsum[3] += vd;
-          below1 = max(below1, __float_as_uint(tb));
+          e.d[2] += bd;
+          e.d[3] += vd;
+          e.bl1 = OpMax<uint32_t>::f(e.bl1, __float_as_uint(tb));
           slot = a1++;
         } else {
-          dsum[0] += bd;
-          dsum[1] += vd;
-          below = max(below, __float_as_uint(tb));
+          e.d[0] += bd;
+          e.d[1] += vd;
+          e.bl = OpMax<uint32_t>::f(e.bl, __float_as_uint(tb));
           continue;
         }
       }
@@ -3158,13 +3183,22 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
         p.candq[seg + slot] = rb[k];
       }
     }
-    o0 += tot & 0xFFFFu;
-    o1 += tot >> 16;
+    e.t0 = tot & 0xFFFFu;
+    e.t1 = tot >> 16;
+    return e;
+  };
+  auto take = [&](const EmitRes &e) {
+    o0 += e.t0;
+    o1 += e.t1;
+    below = OpMax<uint32_t>::f(below, e.bl);
+    below1 = OpMax<uint32_t>::f(below1, e.bl1);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dsum[k] += e.d[k];
   };
   if constexpr (KEEP)
-    emit_batch(key8, r8, s8, bi8, lw8, rb8);
+    take(emit_batch(key8, r8, s8, bi8, lw8, rb8, o0, o1));
   else
-    emit_batch(key8, r8, s8, nullptr, nullptr, nullptr);
+    take(emit_batch(key8, r8, s8, nullptr, nullptr, nullptr, o0, o1));
   for (int it0 = kSelIt; it0 < iters; it0 += kSelIt) {
     float rb[kSelIt], sb[kSelIt];
     unsigned long long kb[kSelIt];
@@ -3177,7 +3211,7 @@ __global__ __launch_bounds__(kBlock) void dk_rcand(DParams p) {
       kb[k] = key_of(pos_of(it0 + k), rb[k], sb[k], t);
       sb[k] = t.wt;
     }
-    emit_batch(kb, rb, sb, nullptr, nullptr, nullptr);
+    take(emit_batch(kb, rb, sb, nullptr, nullptr, nullptr, o0, o1));
   }
   // the workgroup's totals in one LDS round (thread 0 writes them): each
   // value folded per wave, the waves combined in wave order
