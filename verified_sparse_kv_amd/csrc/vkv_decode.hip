@@ -2075,8 +2075,10 @@ __device__ __forceinline__ int *band_counts() {
 // workgroup barrier.
 template <bool LB>
 __device__ __forceinline__ void beta_rec_fold(double (&v)[kBetaRec]) {
+  // (pass 0's records fill slots 0-4 only; the rest stay 0)
+  constexpr int N = LB ? 5 : kBetaRec;
 #pragma unroll
-  for (int k = 0; k < kBetaRec; ++k)
+  for (int k = 0; k < N; ++k)
     v[k] = (LB && k == 3) ? wave_fold<double, OpMax<double>>(v[k])
                           : wave_fold<double, OpSum<double>>(v[k]);
 }
@@ -2152,21 +2154,27 @@ __device__ __forceinline__ float row_pass0(const DParams &p, int row, int bg,
   }
   if (c == 0) {
     if (threadIdx.x == 0) p.rows[row].m = m;
-    if (check) {
+    if (check && threadIdx.x < kWave) {
       // the front launch's input checks (its workgroups cannot touch the
       // status word, which that launch clears), and the H counts: tokens
-      // with r == 1, all of them and the resident ones
-      uint32_t hc[2] = {0u, 0u};
-      uint32_t fs = 0u;
-      for (int t = threadIdx.x; t < np; t += kBlock) {
-        hc[t < p.nch ? 0 : 1] += p.hpart[(size_t)bg * np + t];
-        fs |= p.fstat[(size_t)bg * np + t];
+      // with r == 1, all of them and the resident ones; by the first wave
+      // alone (lane-strided shares folded by DPP, no workgroup barrier)
+      uint32_t hc0 = 0u, hc1 = 0u, fr = 0u, fh = 0u;
+      for (int t = lane; t < np; t += kWave) {
+        const uint32_t hv = p.hpart[(size_t)bg * np + t];
+        const uint32_t fv = p.fstat[(size_t)bg * np + t];
+        if (t < p.nch) hc0 += hv;
+        else hc1 += hv;
+        fr = OpMax<uint32_t>::f(fr, (fv & VKV_STATUS_BAD_R) ? 1u : 0u);
+        fh = OpMax<uint32_t>::f(fh, (fv & VKV_STATUS_BAD_RESIDENT) ? 1u : 0u);
       }
-      blk_reduce<uint32_t, 2, kBlock>(hc);
+      hc0 = wave_fold<uint32_t, OpSum<uint32_t>>(hc0);
+      hc1 = wave_fold<uint32_t, OpSum<uint32_t>>(hc1);
+      fr = wave_fold<uint32_t, OpMax<uint32_t>>(fr);
+      fh = wave_fold<uint32_t, OpMax<uint32_t>>(fh);
       uint32_t bits = 0u;
-      if (__syncthreads_or((int)(fs & VKV_STATUS_BAD_R))) bits |= VKV_STATUS_BAD_R;
-      if (__syncthreads_or((int)(fs & VKV_STATUS_BAD_RESIDENT)) || hc[0] != hc[1])
-        bits |= VKV_STATUS_BAD_RESIDENT;
+      if (fr) bits |= VKV_STATUS_BAD_R;
+      if (fh || hc0 != hc1) bits |= VKV_STATUS_BAD_RESIDENT;
       if (threadIdx.x == 0 && bits) atomicOr(p.status, bits);
     }
   }
