@@ -806,7 +806,8 @@ __device__ __forceinline__ void scan_body(const DParams &p, int c, int g,
           if (kk * LPT + j < GRP && u == j) val = dot[kk * LPT + j];
         const int h = u + LPT * kk;
         if (h >= GRP) continue;
-        p.shat[(size_t)row_of(p, b, g, h, GRP) * p.n + i] = val;
+        // (non-temporal: the later passes read it from other compute units)
+        __builtin_nontemporal_store(val, &p.shat[(size_t)row_of(p, b, g, h, GRP) * p.n + i]);
         if (in_l) {
           p0_shift(acc[kk], val);
           p0_add(acc[kk], val, ri);
@@ -1203,7 +1204,7 @@ __device__ __forceinline__ void scan2_body(const DParams &p, int c, int g,
       float mx = -INFINITY;
 #pragma unroll
       for (int h = 0; h < GRP; ++h) {
-        p.shat[(size_t)row_of(p, b, g, h, GRP) * p.n + i] = acc[h];
+        __builtin_nontemporal_store(acc[h], &p.shat[(size_t)row_of(p, b, g, h, GRP) * p.n + i]);
         mx = fmaxf(mx, acc[h]);
       }
       p.skey[(size_t)bg * p.n + i] = ri < 1.0f ? order_key(mx) : 0u;
