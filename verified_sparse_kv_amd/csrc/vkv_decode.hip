@@ -126,10 +126,10 @@ struct DParams {
   float *shat, *ell;
   uint32_t *fbits;
   uint32_t *hbits;   // [row][nwords] F_h of each row
-  uint32_t *fstat;   // [B][G][nch + ncr] input-check bits of the front launch
-  float *pmax;       // [row][nch + ncr] shift of each scan chunk / resident part
-  double *p0part;    // [row][nch + ncr][4] pass-0 sums of each scan chunk
-  double *hres;      // [row][ncr] sum over H of exp(l - shift) per part
+  uint32_t *fstat;   // [B][G][nch + nrr] input-check bits of the front launch
+  float *pmax;       // [row][nch + nrr] shift of each scan chunk / resident part
+  double *p0part;    // [row][nch + nrr][4] pass-0 sums of each scan chunk
+  double *hres;      // [row][nrr] sum over H of exp(l - shift) per part
   uint32_t *hpart;
   RowState *rows;
   int nsub, rsub;    // kRowChunk sub-chunks per row, and per row workgroup
@@ -166,7 +166,7 @@ struct DParams {
   double *dpart;         // [row][kSelWG][2] float64 sums below the bound
   float2 *apart;     // [row][ncr + ncf] (shift, sum of weights)
   float *aparto;     // [row][d][npad] weighted sums of V, part index fastest
-  int B, Hq, G, n, cap, fetch_cap, nch, ncr, ncf, npad, nwords, chunk, nrc;
+  int B, Hq, G, n, cap, fetch_cap, nch, nrr, ncr, ncf, npad, nwords, chunk, nrc;
   float eps;
   double l_delta, a_delta;
   int est, weights;
@@ -574,7 +574,7 @@ template <int GRP>
 __device__ __forceinline__ void p0_finish(const DParams &p, int b, int g,
                                           int c, P0Acc (&acc)[GRP],
                                           uint32_t n_h) {
-  const int np = p.nch + p.ncr;
+  const int np = p.nch + p.nrr;
   const int bg = b * p.G + g;
   constexpr int W = kBlock / kWave;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -830,7 +830,7 @@ __device__ __forceinline__ void scan_body(const DParams &p, int c, int g,
     p0_init(hacc[h]);
     if (h % LPT == u) hacc[h] = acc[h / LPT];
   }
-  const int np = p.nch + p.ncr;
+  const int np = p.nch + p.nrr;
   {
     const int any = __syncthreads_or((int)bad);
     if (threadIdx.x == 0) p.fstat[(size_t)bg * np + c] = any ? VKV_STATUS_BAD_R : 0u;
@@ -898,7 +898,7 @@ __device__ __forceinline__ void scan_exact_body(const DParams &p, int c,
   {
     const int any = __syncthreads_or((int)bad);
     if (threadIdx.x == 0)
-      p.fstat[(size_t)bg * (p.nch + p.ncr) + c] = any ? VKV_STATUS_BAD_R : 0u;
+      p.fstat[(size_t)bg * (p.nch + p.nrr) + c] = any ? VKV_STATUS_BAD_R : 0u;
   }
   p0_finish<GRP>(p, b, g, c, acc, n_h);
 }
@@ -963,7 +963,7 @@ __device__ __forceinline__ void resident_body(const DParams &p, int c, int g,
   double hsum = 0.0;
   uint32_t n_h = 0;
   int lo, hi;
-  split_range(cnt, p.ncr, c, lo, hi);
+  split_range(cnt, p.nrr, c, lo, hi);
   constexpr int WV = kBlock / kWave;
   // Loads are branch-free (indices past the range read its last row; the
   // results for them are never used), so that the loop waits only for what
@@ -1051,7 +1051,7 @@ __device__ __forceinline__ void resident_body(const DParams &p, int c, int g,
 #pragma unroll
     for (int t = 0; t < 4; ++t) ra[t] = rb[t];
   }
-  const int np = p.nch + p.ncr;
+  const int np = p.nch + p.nrr;
   {
     const int any = __syncthreads_or((int)bad);
     if (threadIdx.x == 0)
@@ -1071,7 +1071,7 @@ __device__ __forceinline__ void resident_body(const DParams &p, int c, int g,
     for (int h = 0; h < GRP; ++h) {
       const int row = row_of(p, b, g, h, GRP);
       p.pmax[(size_t)row * np + p.nch + c] = mxv[h];
-      p.hres[(size_t)row * p.ncr + c] = hsv[h];
+      p.hres[(size_t)row * p.nrr + c] = hsv[h];
     }
   }
   const uint32_t th = block_sum<uint32_t>(n_h, s_ured);
@@ -1215,7 +1215,7 @@ __device__ __forceinline__ void scan2_body(const DParams &p, int c, int g,
       rv[k] = nr[k];
     }
   }
-  const int np = p.nch + p.ncr;
+  const int np = p.nch + p.nrr;
   const int any = __syncthreads_or((int)bad);
   if (threadIdx.x == 0) p.fstat[(size_t)bg * np + c] = any ? VKV_STATUS_BAD_R : 0u;
 }
@@ -2108,7 +2108,7 @@ __device__ __forceinline__ void beta_rec_wave(const double *rec, int S,
 __device__ __forceinline__ float row_pass0(const DParams &p, int row, int bg,
                                            int c, bool check,
                                            double (&v)[kBetaRec]) {
-  const int np = p.nch + p.ncr;
+  const int np = p.nch + p.nrr;
   const int lane = threadIdx.x % kWave;
   // (every wave on its own: lane-strided shares folded by DPP; the first
   // kPre shares of each lane, records included, loaded before any is used)
@@ -2149,8 +2149,8 @@ __device__ __forceinline__ float row_pass0(const DParams &p, int row, int bg,
     v[2] += rec[2];
     v[3] = fmax(v[3], rec[3] * f);
   }
-  for (int t = lane; t < p.ncr; t += kWave) {
-    const double hs = p.hres[(size_t)row * p.ncr + t];
+  for (int t = lane; t < p.nrr; t += kWave) {
+    const double hs = p.hres[(size_t)row * p.nrr + t];
     if (hs > 0.0) v[4] += hs * exp((double)p.pmax[(size_t)row * np + p.nch + t] - (double)m);
   }
   if (c == 0) {
@@ -4168,7 +4168,7 @@ struct PhaseMark {
 template <int GRP>
 hipError_t run(const DParams &p, hipStream_t s, int sd, void **events) {
   const dim3 blk(kBlock);
-  const dim3 gfront((unsigned)(p.nch + p.ncr), (unsigned)p.G, (unsigned)p.B);
+  const dim3 gfront((unsigned)(p.nch + p.nrr), (unsigned)p.G, (unsigned)p.B);
   constexpr int kPhases = 13;  // the entries of kPhaseNames
   const PhaseMark mark(events, s, kPhases);
   const bool sk2 = p.weights == VKV_W_SKETCH2;
@@ -4293,6 +4293,17 @@ DecodeLayout decode_layout(const vkv_decode_args &a) {
   const int room = fit >= 1 ? fit : (int)std::max<long long>(1, per_head - ncf);
   L.ncr = std::max(1, std::min(std::min(std::min(target, 32), room),
                                (rmax + 63) / 64));
+  // resident parts of the front launch (the resident logits beside the
+  // scan): about 512 per launch, at most 32 per KV head and at least 64
+  // rows each, and up to one workgroup per compute unit beside 12 (at most
+  // 8 KV heads) or 8 other workgroups per KV head where the batch allows
+  // (the front launch's workgroups all run at once at its register use)
+  {
+    const int other = groups_ll <= 8 ? 12 : 8;
+    const int fit_f = (int)(256 / std::max<long long>(1, groups_ll)) - other;
+    L.nrr = std::max(1, std::min(std::min(std::min(target, 32), std::max(fit_f, 8)),
+                                 (rmax + 63) / 64));
+  }
   L.ncf = ncf;
   L.npad = (L.ncr + L.ncf + 3) / 4 * 4;
   L.nwords = (a.n_tokens + 31) / 32;
@@ -4316,13 +4327,13 @@ DecodeLayout decode_layout(const vkv_decode_args &a) {
   L.rows = c.take<RowState>(rows);
   L.shat = c.take<float>(rows * n);
   L.ell = c.take<float>(rows * (size_t)a.cap);
-  L.fstat = c.take<uint32_t>(groups * (L.nch + L.ncr));
+  L.fstat = c.take<uint32_t>(groups * (L.nch + L.nrr));
   L.fbits = c.take<uint32_t>(groups * L.nwords);
   L.hbits = c.take<uint32_t>(rows * L.nwords);
-  L.pmax = c.take<float>(rows * (L.nch + L.ncr));
-  L.p0part = c.take<double>(rows * (L.nch + L.ncr) * 4);
-  L.hres = c.take<double>(rows * L.ncr);
-  L.hpart = c.take<uint32_t>(groups * (L.nch + L.ncr));  // H counts per chunk
+  L.pmax = c.take<float>(rows * (L.nch + L.nrr));
+  L.p0part = c.take<double>(rows * (L.nch + L.nrr) * 4);
+  L.hres = c.take<double>(rows * L.nrr);
+  L.hpart = c.take<uint32_t>(groups * (L.nch + L.nrr));  // H counts per chunk
   L.bpart = c.take<double>(2 * rows * L.nrc * (size_t)kBetaRec);
   L.band = c.take<float2>(2 * rows * L.nrc * (size_t)kBandChunk);
   L.bstate = c.take<BetaState>(2 * rows);
@@ -4425,6 +4436,7 @@ hipError_t launch_decode(const vkv_decode_args &a, const DecodeLayout &L,
   p.cap = a.cap;
   p.fetch_cap = a.fetch_cap;
   p.nch = L.nch;
+  p.nrr = L.nrr;
   p.ncr = L.ncr;
   p.ncf = L.ncf;
   p.nwords = L.nwords;

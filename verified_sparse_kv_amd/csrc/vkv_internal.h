@@ -56,7 +56,7 @@ hipError_t launch_compress(const vkv_compress_args &a, const CompressLayout &L,
 
 // ------------------------------------------------------------ decoding
 struct DecodeLayout {
-  int grp, nch, ncr, ncf, npad, nwords, chunk, nrc, nsub, rsub, nsel;
+  int grp, nch, nrr, ncr, ncf, npad, nwords, chunk, nrc, nsub, rsub, nsel;
   size_t shat, ell, hpart, fstat, fbits, hbits, pmax, p0part, hres, rows,
       bpart, band,
       bstate,
