@@ -140,7 +140,7 @@ def algorithmic_bytes(w, counts, fetching_rows, est="clip"):
                 + B * Hq * d * (2 + 4), kernels=per, intermediate=inter)
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_c2_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_{}_traffic.md")
 DECODE_SOURCES = ("verified_sparse_kv_amd/csrc/vkv_decode.hip",
                   "verified_sparse_kv_amd/csrc/vkv_common.h",
                   "verified_sparse_kv_amd/csrc/vkv_internal.h")
@@ -148,13 +148,14 @@ DECODE_SOURCES = ("verified_sparse_kv_amd/csrc/vkv_decode.hip",
 
 def measured_traffic(config, kernel, estimator="clip"):
     """HBM bytes per launch of `kernel` from the committed FETCH_SIZE /
-    WRITE_SIZE counter summary, or None when there is none for this workload
+    WRITE_SIZE counter summary of this workload, or None when there is none
     or the decode sources changed since the counters were taken."""
     import hashlib
-    if config != "c2" or not os.path.exists(TRAFFIC_FILE) or estimator != "clip":
+    path = TRAFFIC_FILE.format(config)
+    if not os.path.exists(path) or estimator != "clip":
         return None
     vals, want = {}, None
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if " = " not in line:
             continue
         k, v = (x.strip() for x in line.split(" = ", 1))
