@@ -3745,7 +3745,11 @@ __device__ __forceinline__ void gather_attend(const DParams &p, int j, int g,
   uint32_t n_host = 0u;  // rows this thread listed that come from host memory
   for (uint32_t seg = lo; seg < hi; seg += kGatherSeg) {
     const uint32_t seg_hi = min(hi, seg + (uint32_t)kGatherSeg);
-    // ---- list the positions with list index in [seg, seg_hi)
+    // ---- list the positions with list index in [seg, seg_hi): each
+    // thread the set bits of its own words, with no loads; then, one list
+    // entry per thread at a time, which query heads fetch it and whether
+    // the previous step staged it (all those loads issued together, not one
+    // dependent round trip per listed position)
     {
       uint32_t gi = before;
 #pragma unroll
@@ -3755,23 +3759,7 @@ __device__ __forceinline__ void gather_attend(const DParams &p, int j, int g,
         if (gi + cnt > seg && gi < seg_hi) {
           while (x) {
             const int bit = __ffs(x) - 1;
-            if (gi >= seg && gi < seg_hi) {
-              const int wi = w0 + k;
-              uint32_t msk = 0u;
-#pragma unroll
-              for (int h = 0; h < GRP; ++h)
-                msk |= ((p.hbits[(size_t)row_of(p, b, g, h, GRP) * p.nwords + wi] >> bit) & 1u) << h;
-              const int pos = wi * 32 + bit;
-              int sl = -1;
-              if (p.smap_prev) {
-                sl = p.smap_prev[(size_t)bg * p.ns + pos];
-                if (sl >= p.fetch_cap) sl = -1;
-              }
-              n_host += sl < 0 ? 1u : 0u;
-              s_pos[gi - seg] = pos;
-              s_src[gi - seg] = sl;
-              s_msk[gi - seg] = (uint8_t)msk;
-            }
+            if (gi >= seg && gi < seg_hi) s_pos[gi - seg] = (w0 + k) * 32 + bit;
             ++gi;
             x &= x - 1;
           }
@@ -3782,6 +3770,23 @@ __device__ __forceinline__ void gather_attend(const DParams &p, int j, int g,
     }
     __syncthreads();
     const uint32_t nrow = seg_hi - seg;
+    for (uint32_t k = threadIdx.x; k < nrow; k += kBlock) {
+      const int pos = s_pos[k];
+      const int wi = pos / 32, bit = pos % 32;
+      uint32_t msk = 0u;
+#pragma unroll
+      for (int h = 0; h < GRP; ++h)
+        msk |= ((p.hbits[(size_t)row_of(p, b, g, h, GRP) * p.nwords + wi] >> bit) & 1u) << h;
+      int sl = -1;
+      if (p.smap_prev) {
+        sl = p.smap_prev[(size_t)bg * p.ns + pos];
+        if (sl >= p.fetch_cap) sl = -1;
+      }
+      n_host += sl < 0 ? 1u : 0u;
+      s_src[k] = sl;
+      s_msk[k] = (uint8_t)msk;
+    }
+    __syncthreads();
     for (uint32_t k = threadIdx.x; k < nrow; k += kBlock) {
       fidx[seg + k] = s_pos[k];
       if (p.smap_next) p.smap_next[(size_t)bg * p.ns + s_pos[k]] = (int32_t)(seg + k);
