@@ -54,11 +54,12 @@ def parse():
     ap.add_argument("--no-compress", action="store_true",
                     help="skip the compression pass over the 36-layer, "
                          "128K-token workload")
-    ap.add_argument("--also", nargs="*", default=["c3"],
+    ap.add_argument("--also", nargs="*", default=["c3", "c4"],
                     choices=["c2", "c3", "c4"],
                     help="other decode workloads measured after the headline "
                          "one, each reported as its own block (default: c3, "
-                         "batch 16 with fetching active); none with --also")
+                         "batch 16 with fetching active, and c4, 128K at batch "
+                         "4); none with --also")
     ap.add_argument("--weights", default="sketch", choices=["sketch", "sketch2"],
                     help="planning weights of the main line: the projected "
                          "sketch (default) or the pages' 2-bit sketch with "
