@@ -208,6 +208,17 @@ typedef struct {
  * shortlisted positions ascending, -1 after the last (fewer when fewer
  * tokens are eligible). With VKV_W_SKETCH2, host_bytes also counts the
  * 2 d bytes of each shortlisted key.
+ * prefetch_rows  read-ahead: up to this many rows per (request, KV head)
+ *          are copied from host_kv into the workspace on a second stream
+ *          (one per device, owned by the library) while the planning
+ *          kernels run, chosen by their planning weight before k* is known;
+ *          the gather takes a fetched row from there when it was read ahead.
+ *          No output except host_bytes depends on it (host_bytes counts
+ *          the rows read ahead too, fetched or not). 0: none; -1: the
+ *          library's choice for the shapes; otherwise 1..n_tokens. The
+ *          workspace grows by prefetch_rows * 2 d * 2 bytes per (request,
+ *          KV head). Steps on one device that read ahead share its second
+ *          stream and are ordered on it in call order.
  * status   dev u32 [1], cleared at the start of the call.
  * phase_events  optional timing hook: NULL, or vkv_decode_phase_count() + 1
  *          hipEvent_t handles (created by the caller); event 0 is recorded on
@@ -256,6 +267,7 @@ typedef struct {
   void **phase_events;
   void *workspace;
   size_t workspace_bytes;
+  int32_t prefetch_rows;
 } vkv_decode_args;
 
 /*
@@ -406,7 +418,8 @@ vkv_status vkv_decode_step(const vkv_decode_args *a, void *stream);
  * needs the buffer cleared by nobody: the kernels initialise what they
  * read. Every call on one GPU shares that GPU's buffer, which keeps the
  * last call's contents: calls that overlap on one GPU (other streams,
- * other threads) race, and the caller must order them. */
+ * other threads) race, and the caller must order them. It reads no rows
+ * ahead: prefetch_rows is taken as 0. */
 vkv_status vkv_decode_step_noalloc(const vkv_decode_args *a, void *stream);
 
 /* Enqueue one exact decode attention over the whole cache (see

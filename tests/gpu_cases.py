@@ -125,12 +125,12 @@ def library_sketch2(w, dev):
 
 
 def run_library(w, dev, eps, delta, est=0, weights=0, fetch_cap=None,
-                n_short=128):
+                n_short=128, prefetch_rows=0):
     from verified_sparse_kv_amd import verkv as vk
     torch = torch_mod()
     step = vk.DecodeStep(w["B"], w["Hq"], w["G"], w["n"], w["s"], w["cap"],
                          fetch_cap or w["n"], torch.device("cuda"),
-                         n_short=n_short)
+                         n_short=n_short, prefetch_rows=prefetch_rows)
     skt = library_sketch2(w, dev) if weights == od.W_SKETCH2 else None
     step.bind(dev["q"], dev["resident_kv"], dev["resident_idx"],
               dev["resident_count"], dev["sketch"], dev["proj"], dev["r"],

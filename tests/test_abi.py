@@ -104,6 +104,10 @@ def test_workspace_sizes():
     assert vk.vkv_decode_workspace_bytes(_decode_args(n_tokens=1024, fetch_cap=1024)) < dw
     assert vk.vkv_decode_workspace_bytes(_decode_args(cap=300)) < dw
     assert vk.vkv_decode_workspace_bytes(_decode_args(n_q_heads=20)) == 0
+    # the read-ahead area: prefetch_rows rows of 2 d bf16 per KV head
+    pf = vk.vkv_decode_workspace_bytes(_decode_args(prefetch_rows=1000))
+    assert pf >= dw + 2 * 8 * 1000 * 512
+    assert vk.vkv_decode_workspace_bytes(_decode_args(prefetch_rows=-1)) > dw
     # the shapes named in the configs fit easily in 288 GB
     big = _decode_args(batch=16, n_tokens=32768, cap=4600, fetch_cap=32768)
     assert vk.vkv_decode_workspace_bytes(big) < 8 * 2 ** 30
@@ -153,6 +157,8 @@ def test_compress_validation(kw, code, frag):
     (dict(host_kv=None), vk.VKV_EINVAL, "required"),
     (dict(weights=2), vk.VKV_EINVAL, "sk2_codes"),
     (dict(ctx_stride=4095), vk.VKV_EINVAL, "ctx_stride"),
+    (dict(prefetch_rows=-2), vk.VKV_EINVAL, "prefetch_rows"),
+    (dict(prefetch_rows=4097), vk.VKV_EINVAL, "prefetch_rows"),
     (dict(stage_map_prev=ctypes.c_void_p(0x1000)), vk.VKV_EINVAL, "pairs"),
     (dict(stage_map_next=ctypes.c_void_p(0x1000)), vk.VKV_EINVAL, "pairs"),
     (dict(stage_map_prev=ctypes.c_void_p(0x1000), stage_prev=ctypes.c_void_p(0x2000),

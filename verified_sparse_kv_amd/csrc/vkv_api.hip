@@ -93,6 +93,8 @@ vkv_status check_decode_shapes(const vkv_decode_args *a) {
   if (a->weights == VKV_W_SKETCH && !(a->sketch_dim == 16 || a->sketch_dim == 32))
     return fail(VKV_EUNSUPPORTED, "decode: sketch_dim %d (supported: 16, 32)", a->sketch_dim);
   REQUIRE(a->cap >= 1, "decode: cap must be >= 1");
+  REQUIRE(a->prefetch_rows >= -1 && a->prefetch_rows <= a->n_tokens,
+          "decode: prefetch_rows must be -1, 0 or in [1, n_tokens]");
   REQUIRE(a->fetch_cap >= 1 && a->fetch_cap <= a->n_tokens,
           "decode: fetch_cap must be in [1, n_tokens]");
   REQUIRE(a->ctx_stride == 0 || (a->ctx_stride >= a->n_tokens && a->ctx_stride <= (1 << 24)),
@@ -343,6 +345,9 @@ vkv_status vkv_decode_step_noalloc(const vkv_decode_args *a, void *stream) {
   REQUIRE(a->workspace == nullptr && a->workspace_bytes == 0,
           "decode_noalloc: workspace must be NULL with workspace_bytes 0 (the "
           "library's own buffer is used)");
+  vkv_decode_args b = *a;
+  b.prefetch_rows = 0;  // (no read-ahead: its stream is made on first use)
+  a = &b;
   const vkv::DecodeLayout L = vkv::decode_layout(*a);
   if (L.total > (size_t)VKV_NOALLOC_WORKSPACE_BYTES)
     return fail(VKV_EUNSUPPORTED,

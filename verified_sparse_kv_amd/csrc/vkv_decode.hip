@@ -37,6 +37,7 @@
 // floating-point contraction off, so every pass sees identical values.
 
 #include <algorithm>
+#include <mutex>
 
 #include <hip/hip_ext.h>
 
@@ -164,6 +165,16 @@ struct DParams {
   unsigned long long *candk;
   float *candw, *candq;  // w~ and r of each candidate
   double *dpart;         // [row][kSelWG][2] float64 sums below the bound
+  // speculative reads (prefetch): per row m_L + log D~_L; per group the
+  // selection's score bin and its slot counter; per group the bitmap of S,
+  // of the rows read and each word's first slot; the rows [group][spec_m]
+  float *sp_c;
+  int32_t *sp_thr;
+  uint32_t *sp_cnt;
+  uint32_t *sp_res, *sp_bits, *sp_base;
+  int32_t *sp_list;  // [group][spec_m] positions to read, in slot order
+  uint16_t *spec_kv;
+  int spec_m;        // rows per group read ahead (0: none)
   float2 *apart;     // [row][ncr + ncf] (shift, sum of weights)
   float *aparto;     // [row][d][npad] weighted sums of V, part index fastest
   int B, Hq, G, n, cap, fetch_cap, nch, nrr, ncr, ncf, npad, nwords, chunk, nrc;
@@ -3678,6 +3689,19 @@ constexpr int kGatherBatch = 2;
 // into a running softmax (shift, sum of weights, weighted sum of V). The
 // half-waves are merged at the end into the workgroup's partial, index
 // ncr + j.
+// The 16-byte unit `unit` of a listed row: from the previous step's staging
+// (sl >= 0) or this step's read-ahead (sl <= -2) when either holds it, else
+// from host memory (sl == -1).
+__device__ __forceinline__ const uint4 *gather_row(int sl, int pos,
+                                                   const uint16_t *stg,
+                                                   const uint16_t *host,
+                                                   const uint16_t *spec,
+                                                   int unit) {
+  const uint16_t *base = sl >= 0 ? stg + (size_t)sl * 2 * kHeadDim
+                       : sl == -1 ? host + (size_t)pos * 2 * kHeadDim
+                                  : spec + (size_t)(-2 - sl) * 2 * kHeadDim;
+  return reinterpret_cast<const uint4 *>(base + unit * 8);
+}
 constexpr int kGatherSeg = 4096;   // listed positions held at a time
 constexpr int kGatherWPT = 16;     // bitmap words per thread: n <= 2^17
 template <int GRP>
@@ -3691,7 +3715,7 @@ __device__ __forceinline__ void gather_attend(const DParams &p, int j, int g,
   constexpr int HW = kBlock / 32;
   constexpr int STEP = HW * kGatherBatch;   // rows per batch of the workgroup
   __shared__ int s_pos[kGatherSeg];
-  __shared__ int s_src[kGatherSeg];  // index in stage_prev, or -1: host
+  __shared__ int s_src[kGatherSeg];  // index in stage_prev; -1: host; -2 - k: row k read ahead
   __shared__ uint8_t s_msk[kGatherSeg];
   __shared__ uint32_t s_red[kBlock / kWave + 1];
   __shared__ float s_m[HW][GRP], s_d[HW][GRP];
@@ -3733,15 +3757,10 @@ __device__ __forceinline__ void gather_attend(const DParams &p, int j, int g,
   const uint16_t *src_base = p.host_kv + (size_t)bg * p.ns * 2 * kHeadDim;
   const uint16_t *stg_base =
       p.stage_prev ? p.stage_prev + (size_t)bg * p.fetch_cap * 2 * kHeadDim : nullptr;
+  const uint16_t *spec_base =
+      p.spec_m > 0 ? p.spec_kv + (size_t)bg * p.spec_m * 2 * kHeadDim : nullptr;
   int32_t *fidx = p.fidx + (size_t)bg * p.fetch_cap;
-  // row k of the segment: from the previous step's staging when it holds
-  // it, else from host memory
-  auto row_ptr = [&](uint32_t k) {
-    const int sl = s_src[k];
-    const uint16_t *base = sl >= 0 ? stg_base + (size_t)sl * 2 * kHeadDim
-                                   : src_base + (size_t)s_pos[k] * 2 * kHeadDim;
-    return reinterpret_cast<const uint4 *>(base + unit * 8);
-  };
+
   uint32_t n_host = 0u;  // rows this thread listed that come from host memory
   for (uint32_t seg = lo; seg < hi; seg += kGatherSeg) {
     const uint32_t seg_hi = min(hi, seg + (uint32_t)kGatherSeg);
@@ -3780,9 +3799,15 @@ __device__ __forceinline__ void gather_attend(const DParams &p, int j, int g,
       int sl = -1;
       if (p.smap_prev) {
         sl = p.smap_prev[(size_t)bg * p.ns + pos];
-        if (sl >= p.fetch_cap) sl = -1;
+        if (sl < 0 || sl >= p.fetch_cap) sl = -1;
       }
-      n_host += sl < 0 ? 1u : 0u;
+      if (p.spec_m > 0) {  // read ahead this step: slot -2 - sl of spec_kv
+        const uint32_t wb = p.sp_bits[(size_t)bg * p.nwords + wi];
+        const uint32_t w0s = p.sp_base[(size_t)bg * p.nwords + wi];
+        if (sl < 0 && ((wb >> bit) & 1u))
+          sl = -2 - (int)(w0s + (uint32_t)__popc(wb & ((1u << bit) - 1u)));
+      }
+      n_host += sl == -1 ? 1u : 0u;
       s_src[k] = sl;
       s_msk[k] = (uint8_t)msk;
     }
@@ -3798,13 +3823,13 @@ __device__ __forceinline__ void gather_attend(const DParams &p, int j, int g,
 #pragma unroll
     for (int it = 0; it < kGatherBatch; ++it) {
       const uint32_t rk = it * HW + hw;
-      if (rk < nrow) cur[it] = *row_ptr(rk);
+      if (rk < nrow) cur[it] = *gather_row(s_src[rk], s_pos[rk], stg_base, src_base, spec_base, unit);
     }
     for (uint32_t r0 = 0; r0 < nrow; r0 += STEP) {
 #pragma unroll
       for (int it = 0; it < kGatherBatch; ++it) {
         const uint32_t rk = r0 + STEP + it * HW + hw;
-        if (rk < nrow) nxt[it] = *row_ptr(rk);
+        if (rk < nrow) nxt[it] = *gather_row(s_src[rk], s_pos[rk], stg_base, src_base, spec_base, unit);
       }
 #pragma unroll
       for (int it = 0; it < kGatherBatch; ++it) {
@@ -3879,6 +3904,277 @@ __device__ __forceinline__ void gather_attend(const DParams &p, int j, int g,
     p.fcount[bg] = (int32_t)total;
     if (total > (uint32_t)p.fetch_cap) atomicOr(p.status, VKV_STATUS_FETCH_OVERFLOW);
   }
+}
+
+// ------------------------------------------------------------ read-ahead
+// Speculative host reads while the planning passes run (a second stream,
+// joined before the gather). A query head fetches a prefix of its gain
+// order (eqs. 9-10), and a token's gain grows with its share w~_i / D~ of
+// the plug-in denominator and with 1 - r_i (the bias and variance terms of
+// Lemma 1 vanish as r_i -> 1). So the tokens of L outside S with the largest
+//   score_i = max_h (s_hi - m_h - log D~_L,h) + log(1 - r_i),
+// up to spec_m per KV head, are copied from host memory into a device area
+// before the decision; the gather takes a listed row from there when it
+// finds it. A row is the same bytes wherever it is read from, so no output
+// depends on the read-ahead; a row read ahead but not fetched costs only
+// host-link time that the planning leaves idle.
+constexpr int kSpecBins = 1024;         // score histogram: bin = -32 score
+constexpr float kSpecBinScale = 32.0f;  // (bin 1023 takes every score < -32)
+constexpr int kSpecRun = 64;            // tokens sampled per kChunk tokens
+constexpr int kSpecUnroll = 8;          // samples per thread in flight
+constexpr int kSpecMoveUnroll = 8;      // rows per half-wave in flight
+constexpr int kSpecMovers = 64;         // copying workgroups (compute units)
+// dynamic LDS each copying workgroup asks for: with its own few bytes, the
+// 160 KB of a compute unit less less than the smallest planning
+// workgroup's LDS (8.4 KB), so no planning workgroup fits beside it
+constexpr int kSpecMoveLds = 156 * 1024;
+
+__device__ __forceinline__ int spec_bin(float sc) {
+  const float x = fminf(fmaxf(-sc * kSpecBinScale, 0.0f), (float)(kSpecBins - 1));
+  return (int)x;
+}
+
+// Per KV head (one workgroup each): m_L + log D~_L of every query head from
+// the scan chunks' pass-0 records, the bitmap of the resident positions, and
+// from a sample of L (the first kSpecRun tokens of every kChunk) the score
+// bin above which about spec_m tokens lie.
+template <int GRP>
+__global__ __launch_bounds__(kBlock) void sp_pick(DParams p) {
+  const int g = blockIdx.x, b = blockIdx.y, bg = b * p.G + g;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  constexpr int W = kBlock / kWave;
+  const int np = p.nch + p.nrr, nw = p.nwords;
+  __shared__ float s_c[GRP];
+  __shared__ uint32_t s_hist[kSpecBins];
+  __shared__ uint32_t s_res[kMaxTokens / 32];
+  __shared__ uint32_t s_scan[W + 1];
+  __shared__ int s_best[W];
+  for (int i = threadIdx.x; i < kSpecBins; i += kBlock) s_hist[i] = 0u;
+  for (int i = threadIdx.x; i < nw; i += kBlock) s_res[i] = 0u;
+  for (int h = wave; h < GRP; h += W) {
+    const int row = row_of(p, b, g, h, GRP);
+    float m = -INFINITY;
+    for (int t = lane; t < p.nch; t += kWave) m = fmaxf(m, p.pmax[(size_t)row * np + t]);
+    m = wave_fold<float, OpMax<float>>(m);
+    float sw = 0.0f;
+    for (int t = lane; t < p.nch; t += kWave) {
+      const float sv = (float)p.p0part[((size_t)row * np + t) * 4];
+      if (sv > 0.0f) sw += sv * __expf(p.pmax[(size_t)row * np + t] - m);
+    }
+    sw = wave_fold<float, OpSum<float>>(sw);
+    if (lane == 0) {
+      const float c = sw > 0.0f ? m + __logf(sw) : INFINITY;  // inf: no L
+      s_c[h] = c;
+      p.sp_c[row] = c;
+    }
+  }
+  __syncthreads();
+  const int cnt = min(p.rcount[bg], p.cap);
+  const int32_t *ri = p.ridx + (size_t)bg * p.cap;
+  for (int k = threadIdx.x; k < cnt; k += kBlock) {
+    const int pos = ri[k];
+    if (pos >= 0 && pos < p.n) atomicOr(&s_res[pos / 32], 1u << (pos % 32));
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < nw; i += kBlock) p.sp_res[(size_t)bg * nw + i] = s_res[i];
+  float c[GRP];
+#pragma unroll
+  for (int h = 0; h < GRP; ++h) c[h] = s_c[h];
+  const float *rr = p.r + (size_t)bg * p.ns;
+  const int nsamp = (p.n + kChunk - 1) / kChunk * kSpecRun;
+  for (int s0 = 0; s0 < nsamp; s0 += kBlock * kSpecUnroll) {
+    int ii[kSpecUnroll];
+    float rv[kSpecUnroll], sv[kSpecUnroll][GRP];
+#pragma unroll
+    for (int u = 0; u < kSpecUnroll; ++u) {
+      const int sidx = s0 + u * kBlock + (int)threadIdx.x;
+      const int i = (sidx / kSpecRun) * kChunk + sidx % kSpecRun;
+      ii[u] = sidx < nsamp && i < p.n ? i : -1;
+      rv[u] = ii[u] >= 0 ? rr[i] : 1.0f;
+#pragma unroll
+      for (int h = 0; h < GRP; ++h)
+        sv[u][h] = ii[u] >= 0 ? p.shat[(size_t)row_of(p, b, g, h, GRP) * p.n + i] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kSpecUnroll; ++u) {
+      const int i = ii[u];
+      if (i < 0 || !(rv[u] < 1.0f) || ((s_res[i / 32] >> (i % 32)) & 1u)) continue;
+      float sc = -INFINITY;
+#pragma unroll
+      for (int h = 0; h < GRP; ++h) sc = fmaxf(sc, sv[u][h] - c[h]);
+      sc += __logf(1.0f - rv[u]);
+      if (sc == sc) atomicAdd(&s_hist[spec_bin(sc)], 1u);
+    }
+  }
+  __syncthreads();
+  // the last bin (best first) whose cumulative count stays within the
+  // sample's share of spec_m
+  const uint32_t tgt = (uint32_t)(((long long)p.spec_m * kSpecRun) / kChunk);
+  constexpr int BPT = kSpecBins / kBlock;
+  uint32_t loc[BPT], mine = 0u;
+#pragma unroll
+  for (int k = 0; k < BPT; ++k) {
+    loc[k] = s_hist[threadIdx.x * BPT + k];
+    mine += loc[k];
+  }
+  uint32_t tot;
+  uint32_t run = block_exclusive_scan<uint32_t>(mine, s_scan, &tot);
+  int best = -1;
+#pragma unroll
+  for (int k = 0; k < BPT; ++k) {
+    run += loc[k];
+    if (run <= tgt) best = (int)threadIdx.x * BPT + k;
+  }
+  best = wave_fold<int, OpMax<int>>(best);
+  if (lane == 0) s_best[wave] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int bb = s_best[0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) bb = max(bb, s_best[w]);
+    p.sp_thr[bg] = max(bb, 0);
+    p.sp_cnt[bg] = 0u;
+  }
+}
+
+// Per kChunk tokens of a KV head: the tokens of L outside S (and not staged
+// by the previous step) whose score bin is within the threshold take slots
+// of the KV head's area in position order (one slot counter per KV head;
+// tokens past spec_m are dropped); their bits and each word's first slot
+// are written for the gather, and their positions into the KV head's list
+// of rows to read.
+template <int GRP>
+__global__ __launch_bounds__(kBlock) void sp_sel(DParams p) {
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z, bg = b * p.G + g;
+  constexpr int NW = kChunk / 32;
+  constexpr int TPT = kChunk / kBlock;
+  static_assert(TPT * kBlock == kChunk && kBlock == 4 * kWave, "token layout");
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int t0 = c * kChunk, nw = p.nwords;
+  __shared__ uint32_t s_bits[NW], s_keep[NW], s_before[NW];
+  __shared__ int s_list[kChunk];
+  __shared__ uint32_t s_base;
+  const int thr = p.sp_thr[bg];
+  float cc[GRP];
+#pragma unroll
+  for (int h = 0; h < GRP; ++h) cc[h] = p.sp_c[row_of(p, b, g, h, GRP)];
+  const float *rr = p.r + (size_t)bg * p.ns;
+  const uint32_t *res = p.sp_res + (size_t)bg * nw;
+  float rv[TPT], sv[TPT][GRP];
+  uint32_t rw[TPT];
+#pragma unroll
+  for (int k = 0; k < TPT; ++k) {
+    const int i = t0 + k * kBlock + (int)threadIdx.x;
+    const bool in = i < p.n;
+    rv[k] = in ? rr[i] : 1.0f;
+    rw[k] = in ? res[i / 32] : 0u;
+#pragma unroll
+    for (int h = 0; h < GRP; ++h)
+      sv[k][h] = in ? p.shat[(size_t)row_of(p, b, g, h, GRP) * p.n + i] : 0.0f;
+  }
+#pragma unroll
+  for (int k = 0; k < TPT; ++k) {
+    const int i = t0 + k * kBlock + (int)threadIdx.x;
+    bool sel = false;
+    if (i < p.n && rv[k] < 1.0f && !((rw[k] >> (i % 32)) & 1u)) {
+      float sc = -INFINITY;
+#pragma unroll
+      for (int h = 0; h < GRP; ++h) sc = fmaxf(sc, sv[k][h] - cc[h]);
+      sc += __logf(1.0f - rv[k]);
+      sel = sc == sc && spec_bin(sc) <= thr;
+    }
+    if (sel && p.smap_prev) {
+      const int sl = p.smap_prev[(size_t)bg * p.ns + i];
+      sel = !(sl >= 0 && sl < p.fetch_cap);
+    }
+    const unsigned long long m = __ballot(sel);
+    if (lane == 0) {
+      s_bits[k * (kBlock / 32) + 2 * wave] = (uint32_t)m;
+      s_bits[k * (kBlock / 32) + 2 * wave + 1] = (uint32_t)(m >> 32);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t tot = 0u;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) tot += (uint32_t)__popc(s_bits[w]);
+    s_base = tot > 0u ? atomicAdd(&p.sp_cnt[bg], tot) : 0u;
+  }
+  __syncthreads();
+  const uint32_t base = s_base;
+  const uint32_t room = base >= (uint32_t)p.spec_m ? 0u : (uint32_t)p.spec_m - base;
+  if (threadIdx.x < NW) {
+    const int w = threadIdx.x;
+    uint32_t before = 0u;
+    for (int v = 0; v < w; ++v) before += (uint32_t)__popc(s_bits[v]);
+    uint32_t bits = s_bits[w];
+    // (the rows past the KV head's area: the highest positions go first)
+    while (bits != 0u && before + (uint32_t)__popc(bits) > room)
+      bits &= ~(1u << (31 - __clz(bits)));
+    if (before > room) before = room;
+    s_before[w] = before;
+    const int gw = c * NW + w;
+    if (gw < nw) {
+      p.sp_bits[(size_t)bg * nw + gw] = bits;
+      p.sp_base[(size_t)bg * nw + gw] = base + before;
+    }
+    s_keep[w] = bits;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < TPT; ++k) {
+    const int o = k * kBlock + (int)threadIdx.x, w = o / 32, bit = o % 32;
+    const uint32_t wb = s_keep[w];
+    if ((wb >> bit) & 1u)
+      s_list[s_before[w] + (uint32_t)__popc(wb & ((1u << bit) - 1u))] = t0 + o;
+  }
+  const uint32_t kept = s_before[NW - 1] + (uint32_t)__popc(s_keep[NW - 1]);
+  __syncthreads();
+  int32_t *list = p.sp_list + (size_t)bg * p.spec_m + base;
+  for (uint32_t k = threadIdx.x; k < kept; k += kBlock) list[k] = s_list[k];
+}
+
+// The rows of every KV head's list, from host memory into the read-ahead
+// area, by kSpecMovers workgroups that each hold a whole compute unit (they
+// ask for all of its LDS, so no planning workgroup shares a unit with their
+// host loads in flight): 32 lanes per row, kSpecMoveUnroll rows per
+// half-wave in flight, the rows of all KV heads in one grid-strided loop.
+__global__ __launch_bounds__(kBlock) void sp_move(DParams p) {
+  const int hw = threadIdx.x / 32, unit = threadIdx.x % 32;
+  constexpr int HW = kBlock / 32;
+  __shared__ uint32_t s_red[kBlock / kWave];
+  const long long total = (long long)p.B * p.G * p.spec_m;
+  const long long stride = (long long)gridDim.x * HW;
+  uint32_t moved = 0u;
+  for (long long t0 = (long long)blockIdx.x * HW + hw; t0 < total;
+       t0 += stride * kSpecMoveUnroll) {
+    int pos[kSpecMoveUnroll];
+    int bgs[kSpecMoveUnroll];
+#pragma unroll
+    for (int u = 0; u < kSpecMoveUnroll; ++u) {
+      const long long t = t0 + u * stride;
+      const int bg = (int)(t / p.spec_m), k = (int)(t % p.spec_m);
+      const bool ok = t < total && k < (int)min(p.sp_cnt[t < total ? bg : 0], (uint32_t)p.spec_m);
+      pos[u] = ok ? p.sp_list[t] : -1;
+      bgs[u] = bg;
+    }
+    uint4 v[kSpecMoveUnroll];
+#pragma unroll
+    for (int u = 0; u < kSpecMoveUnroll; ++u)
+      if (pos[u] >= 0)
+        v[u] = reinterpret_cast<const uint4 *>(
+            p.host_kv + ((size_t)bgs[u] * p.ns + pos[u]) * 2 * kHeadDim)[unit];
+#pragma unroll
+    for (int u = 0; u < kSpecMoveUnroll; ++u) {
+      if (pos[u] < 0) continue;
+      const long long t = t0 + u * stride;
+      reinterpret_cast<uint4 *>(p.spec_kv + (size_t)t * 2 * kHeadDim)[unit] = v[u];
+      moved += unit == 0 ? 1u : 0u;
+    }
+  }
+  moved = block_sum<uint32_t>(moved, s_red);
+  if (threadIdx.x == 0 && moved > 0u)
+    atomicAdd(p.host_bytes, (unsigned long long)moved * 2ull * kHeadDim * 2ull);
 }
 
 // ------------------------------------------------------------ attention
@@ -4160,6 +4456,18 @@ struct PhaseMark {
       (void)hipEventRecord(static_cast<hipEvent_t>(ev[k + 1]), s);
     }
   }
+  // a launch whose completion also records `done` (when given): through the
+  // dispatch itself, or with the phase timed alone, a record after it
+  template <typename... A>
+  void launch_then(int k, hipEvent_t done, void (*f)(A...), dim3 g, dim3 b,
+                   A... args) const {
+    if (done == nullptr || k == solo) {
+      launch(k, f, g, b, args...);
+      if (done) (void)hipEventRecord(done, s);
+    } else {
+      hipExtLaunchKernelGGL(f, g, b, 0, s, nullptr, done, 0u, args...);
+    }
+  }
   template <typename... A>
   void launch(int k, void (*f)(A...), dim3 g, dim3 b, A... args) const {
     if (k == solo)
@@ -4170,27 +4478,79 @@ struct PhaseMark {
   }
 };
 
+// The second stream of a step that reads ahead and its two events, one set
+// per device, made on the first such step on that device (default
+// priority; non-blocking, so it waits on nothing but its events). The fork
+// event is recorded by the completion of the launch that finishes the
+// pass-0 records (no packet of its own on the caller's stream).
+struct SpecStream {
+  std::mutex mu;
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kSpecDevices = 64;
+std::mutex g_spec_mu;
+SpecStream g_spec[kSpecDevices];
+
+hipError_t spec_stream(SpecStream **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kSpecDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_spec_mu);
+  SpecStream &x = g_spec[dev];
+  if (x.side == nullptr) {
+    int lds = 0;
+    e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (e != hipSuccess) return e;
+    if (lds < kSpecMoveLds + 1024) return hipErrorNotSupported;
+    hipStream_t sd = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    e = hipStreamCreateWithFlags(&sd, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreate(&f);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&j, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      if (j) (void)hipEventDestroy(j);
+      if (f) (void)hipEventDestroy(f);
+      if (sd) (void)hipStreamDestroy(sd);
+      return e;
+    }
+    x.fork = f;
+    x.join = j;
+    x.side = sd;
+  }
+  *out = &x;
+  return hipSuccess;
+}
+
 template <int GRP>
-hipError_t run(const DParams &p, hipStream_t s, int sd, void **events) {
+hipError_t run(const DParams &p, hipStream_t s, int sd, void **events,
+               const SpecStream *sx) {
   const dim3 blk(kBlock);
   const dim3 gfront((unsigned)(p.nch + p.nrr), (unsigned)p.G, (unsigned)p.B);
   constexpr int kPhases = 13;  // the entries of kPhaseNames
   const PhaseMark mark(events, s, kPhases);
   const bool sk2 = p.weights == VKV_W_SKETCH2;
+  // the read-ahead forks once the pass-0 records are written: after the
+  // front launch, or with the 2-bit sketch after the pass-0 launch
+  hipEvent_t fork_front = sx && !sk2 ? sx->fork : nullptr;
+  hipEvent_t fork_p0 = sx && sk2 ? sx->fork : nullptr;
   int k = 0;
   mark(k);
   if (p.weights == VKV_W_PERFECT)
-    mark.launch(k, dk_front_exact<GRP>, gfront, blk, p);
+    mark.launch_then(k, fork_front, dk_front_exact<GRP>, gfront, blk, p);
   else if (sk2)
     mark.launch(k, dk_front2<GRP>, gfront, blk, p);
   else if (sd == 32)
-    mark.launch(k, p.chunk == kChunk ? dk_front<GRP, 32, kChunk / kBlock * 2>
-                                     : dk_front<GRP, 32, 1>,
-                gfront, blk, p);
+    mark.launch_then(k, fork_front,
+                     p.chunk == kChunk ? dk_front<GRP, 32, kChunk / kBlock * 2>
+                                       : dk_front<GRP, 32, 1>,
+                     gfront, blk, p);
   else
-    mark.launch(k, p.chunk == kChunk ? dk_front<GRP, 16, kChunk / kBlock>
-                                     : dk_front<GRP, 16, 1>,
-                gfront, blk, p);
+    mark.launch_then(k, fork_front,
+                     p.chunk == kChunk ? dk_front<GRP, 16, kChunk / kBlock>
+                                       : dk_front<GRP, 16, 1>,
+                     gfront, blk, p);
   mark(++k);
   // 2-bit sketch: the shortlist with its exact logits, then pass 0
   if (sk2)
@@ -4200,39 +4560,59 @@ hipError_t run(const DParams &p, hipStream_t s, int sd, void **events) {
     mark.empty(k);
   mark(++k);
   if (sk2)
-    mark.launch(k, dk_p0<GRP>, dim3((unsigned)p.nch, (unsigned)p.G, (unsigned)p.B),
-                blk, p);
+    mark.launch_then(k, fork_p0, dk_p0<GRP>,
+                     dim3((unsigned)p.nch, (unsigned)p.G, (unsigned)p.B), blk, p);
   else
     mark.empty(k);
   mark(++k);
+  // the read-ahead on the second stream, beside the planning launches; the
+  // gather waits for it
+  if (sx) {
+    hipError_t e = hipStreamWaitEvent(sx->side, sx->fork, 0);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(sp_pick<GRP>, dim3((unsigned)p.G, (unsigned)p.B), blk, 0, sx->side, p);
+    hipLaunchKernelGGL(sp_sel<GRP>,
+                       dim3((unsigned)((p.n + kChunk - 1) / kChunk), (unsigned)p.G,
+                            (unsigned)p.B),
+                       blk, 0, sx->side, p);
+    hipLaunchKernelGGL(sp_move, dim3((unsigned)kSpecMovers), blk,
+                       (size_t)kSpecMoveLds, sx->side, p);
+    e = hipEventRecord(sx->join, sx->side);
+    if (e != hipSuccess) return e;
+  }
+  const PhaseMark &pmark = mark;
   const dim3 grow((unsigned)p.nrc, (unsigned)p.Hq, (unsigned)p.B);
   const dim3 gone((unsigned)p.Hq, (unsigned)p.B);
   for (int j = 1; j <= kBetaLaunchMax; ++j) {
     if (j <= p.nbeta)
-      mark.launch(k, dk_rbeta<GRP>, grow, blk, p, j);
+      pmark.launch(k, dk_rbeta<GRP>, grow, blk, p, j);
     else
-      mark.empty(k);
-    mark(++k);
+      pmark.empty(k);
+    pmark(++k);
   }
   if (p.est == VKV_EST_BINARY)
-    mark.launch(k, dk_rbin<GRP>, gone, dim3(kPlanThreads), p);
+    pmark.launch(k, dk_rbin<GRP>, gone, dim3(kPlanThreads), p);
   else
-    mark.empty(k);
-  mark(++k);
-  mark.launch(k, dk_rcert<GRP>, grow, blk, p);
-  mark(++k);
+    pmark.empty(k);
+  pmark(++k);
+  pmark.launch(k, dk_rcert<GRP>, grow, blk, p);
+  pmark(++k);
   {
     // the register-heavy variant only while its grid fits in one round at
     // three waves per SIMD (768 workgroups)
     const dim3 gc((unsigned)p.nsel, (unsigned)p.Hq, (unsigned)p.B);
     if ((long long)p.nsel * p.Hq * p.B <= 768)
-      mark.launch(k, dk_rcand<GRP, true>, gc, blk, p);
+      pmark.launch(k, dk_rcand<GRP, true>, gc, blk, p);
     else
-      mark.launch(k, dk_rcand<GRP, false>, gc, blk, p);
+      pmark.launch(k, dk_rcand<GRP, false>, gc, blk, p);
   }
-  mark(++k);
-  mark.launch(k, dk_rwalk<GRP>, gone, dim3(kPlanThreads), p);
-  mark(++k);
+  pmark(++k);
+  pmark.launch(k, dk_rwalk<GRP>, gone, dim3(kPlanThreads), p);
+  pmark(++k);
+  if (sx) {
+    const hipError_t e = hipStreamWaitEvent(s, sx->join, 0);
+    if (e != hipSuccess) return e;
+  }
   mark.launch(k, dk_fetch<GRP>,
               dim3((unsigned)((p.ncr + p.ncf) * p.G * p.B)), blk, p);
   mark(++k);
@@ -4255,6 +4635,23 @@ int decode_phase_count() {
 
 const char *decode_phase_name(int i) {
   return (i >= 0 && i < decode_phase_count()) ? kPhaseNames[i] : nullptr;
+}
+
+// Rows per (request, KV head) read ahead: the caller's count, or with -1
+// the library's choice: about as many rows as the host link moves while the
+// planning launches run, which grow less than linearly with the query
+// heads times the context; 6144 * (B Hq n / 2^20)^0.6 rows in all, shared
+// by the B G KV heads, within [64, n / 8] each. (Measured with 64 copying
+// workgroups: the best of 512-896 rows per KV head at 1 x 32 x 32K, of
+// 160-512 at 16 x 32 x 32K and of 768-2048 at 4 x 32 x 128K; the rule
+// gives 768, 255 and 1019.)
+int spec_rows(const vkv_decode_args &a) {
+  if (a.prefetch_rows >= 0) return std::min(a.prefetch_rows, a.n_tokens);
+  const double work = (double)a.batch * a.n_q_heads * a.n_tokens / 1048576.0;
+  const double total = 6144.0 * pow(work, 0.6);
+  const double per = total / ((double)a.batch * a.n_kv_heads);
+  const int hi = std::max(1, a.n_tokens / 8);
+  return std::min(hi, std::max(std::min(64, hi), (int)per));
 }
 
 DecodeLayout decode_layout(const vkv_decode_args &a) {
@@ -4360,6 +4757,17 @@ DecodeLayout decode_layout(const vkv_decode_args &a) {
   L.apart = c.take<float2>(rows * (L.ncr + L.ncf));
   L.aparto = c.take<float>(rows * kHeadDim * (size_t)L.npad);
   L.skey = c.take<uint32_t>(groups * n);  // (2-bit sketch only)
+  L.spec_m = spec_rows(a);
+  if (L.spec_m > 0) {
+    L.sp_c = c.take<float>(rows);
+    L.sp_thr = c.take<int32_t>(groups);
+    L.sp_cnt = c.take<uint32_t>(groups);
+    L.sp_res = c.take<uint32_t>(groups * L.nwords);
+    L.sp_bits = c.take<uint32_t>(groups * L.nwords);
+    L.sp_base = c.take<uint32_t>(groups * L.nwords);
+    L.sp_list = c.take<int32_t>(groups * (size_t)L.spec_m);
+    L.spec_kv = c.take<uint16_t>(groups * (size_t)L.spec_m * 2 * kHeadDim);
+  }
   L.total = (c.off + 255) & ~size_t(255);
   return L;
 }
@@ -4429,6 +4837,17 @@ hipError_t launch_decode(const vkv_decode_args &a, const DecodeLayout &L,
   p.aparto = at<float>(w, L.aparto);
   p.skey = at<uint32_t>(w, L.skey);
   p.npad = L.npad;
+  p.spec_m = L.spec_m;
+  if (L.spec_m > 0) {
+    p.sp_c = at<float>(w, L.sp_c);
+    p.sp_thr = at<int32_t>(w, L.sp_thr);
+    p.sp_cnt = at<uint32_t>(w, L.sp_cnt);
+    p.sp_res = at<uint32_t>(w, L.sp_res);
+    p.sp_bits = at<uint32_t>(w, L.sp_bits);
+    p.sp_base = at<uint32_t>(w, L.sp_base);
+    p.sp_list = at<int32_t>(w, L.sp_list);
+    p.spec_kv = at<uint16_t>(w, L.spec_kv);
+  }
   p.B = a.batch;
   p.Hq = a.n_q_heads;
   p.G = a.n_kv_heads;
@@ -4457,11 +4876,20 @@ hipError_t launch_decode(const vkv_decode_args &a, const DecodeLayout &L,
   // those modes take a third launch before the band settle
   // (and contexts above 32K tokens one more again)
   p.nbeta = (a.weights == VKV_W_SKETCH ? 2 : 3) + (a.n_tokens > 32768 ? 1 : 0);
+  SpecStream *sx = nullptr;
+  std::unique_lock<std::mutex> lock;
+  if (p.spec_m > 0) {
+    const hipError_t e = spec_stream(&sx);
+    if (e != hipSuccess) return e;
+    // (the fork, the read-ahead launches and the join of one step are
+    // enqueued together: the device's second stream and events are shared)
+    lock = std::unique_lock<std::mutex>(sx->mu);
+  }
   switch (L.grp) {
-    case 1: return run<1>(p, s, a.sketch_dim, a.phase_events);
-    case 2: return run<2>(p, s, a.sketch_dim, a.phase_events);
-    case 4: return run<4>(p, s, a.sketch_dim, a.phase_events);
-    case 8: return run<8>(p, s, a.sketch_dim, a.phase_events);
+    case 1: return run<1>(p, s, a.sketch_dim, a.phase_events, sx);
+    case 2: return run<2>(p, s, a.sketch_dim, a.phase_events, sx);
+    case 4: return run<4>(p, s, a.sketch_dim, a.phase_events, sx);
+    case 8: return run<8>(p, s, a.sketch_dim, a.phase_events, sx);
     default: return hipErrorInvalidValue;
   }
 }

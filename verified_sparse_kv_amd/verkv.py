@@ -76,7 +76,8 @@ class DecodeArgs(ctypes.Structure):
                 ("row_path", _p), ("shortlist", _p), ("status", _p),
                 ("phase_events", _p),
                 ("workspace", _p),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t),
+                ("prefetch_rows", _i32)]
 
 
 class DenseArgs(ctypes.Structure):
@@ -410,7 +411,7 @@ class DecodeStep:
     for a shape, so repeated steps only marshal pointers and launch."""
 
     def __init__(self, B, Hq, G, n, s, cap, fetch_cap, device, d=128,
-                 n_short=128, ctx_stride=None):
+                 n_short=128, ctx_stride=None, prefetch_rows=0):
         torch = _torch()
         self.shape = (B, Hq, G, n, s, cap, fetch_cap)
         self.n_short = n_short
@@ -435,7 +436,7 @@ class DecodeStep:
         self.args = DecodeArgs(batch=B, n_q_heads=Hq, n_kv_heads=G, head_dim=d,
                                n_tokens=n, sketch_dim=s, cap=cap,
                                ctx_stride=self.ns, fetch_cap=fetch_cap,
-                               n_short=n_short)
+                               n_short=n_short, prefetch_rows=prefetch_rows)
         for key in ("out", "d_hat", "log_shift", "eps_hat0", "eps_hat", "k_star",
                     "fetch_idx", "fetch_count", "host_bytes", "row_stats",
                     "row_path", "shortlist", "status"):
