@@ -60,6 +60,11 @@ def parse():
                          "one, each reported as its own block (default: c3, "
                          "batch 16 with fetching active, and c4, 128K at batch "
                          "4); none with --also")
+    ap.add_argument("--prefetch-rows", type=int, default=-1,
+                    help="rows per (request, KV head) read from host memory "
+                         "while the planning launches run (-1: the library's "
+                         "choice for the shapes, 0: none); each decode block "
+                         "also times the same steps without it")
     ap.add_argument("--weights", default="sketch", choices=["sketch", "sketch2"],
                     help="planning weights of the main line: the projected "
                          "sketch (default) or the pages' 2-bit sketch with "
@@ -346,7 +351,8 @@ def serving_loop(config, args, dev):
                       w["seed"], st)
         sketch = torch.from_numpy(sketch0.view(np.int16)).to(dev)
         status = torch.zeros((1,), dtype=torch.int32, device=dev)
-        step = vk.DecodeStep(B, Hq, G, n0, s, cap, n0, dev, ctx_stride=ns)
+        step = vk.DecodeStep(B, Hq, G, n0, s, cap, n0, dev, ctx_stride=ns,
+                             prefetch_rows=args.prefetch_rows)
         maps = [torch.full((B, G, ns), -1, dtype=torch.int32, device=dev)
                 for _ in range(2)]
         stages = [torch.empty((B, G, n0, 2, d), dtype=torch.int16, device=dev)
@@ -509,11 +515,16 @@ def measure(config, args, dev, headline, weights=0):
     proj = torch.from_numpy(w["proj"]).to(dev)
     host_kv = torch.from_numpy(w["host_kv"].view(np.int16)).pin_memory()
 
-    step = vk.DecodeStep(B, Hq, G, n, s, cap, n, dev, n_short=128)
-    step.bind(t_qs[0], comp["resident_kv"], comp["resident_idx"],
-              comp["resident_count"], sketch, proj, comp["r"], host_kv,
-              w["eps"], w["delta"], ESTIMATORS[args.estimator], weights,
-              sketch2)
+    def make_step(prefetch_rows):
+        st = vk.DecodeStep(B, Hq, G, n, s, cap, n, dev, n_short=128,
+                           prefetch_rows=prefetch_rows)
+        st.bind(t_qs[0], comp["resident_kv"], comp["resident_idx"],
+                comp["resident_count"], sketch, proj, comp["r"], host_kv,
+                w["eps"], w["delta"], ESTIMATORS[args.estimator], weights,
+                sketch2)
+        return st
+
+    step = make_step(args.prefetch_rows)
     names = vk.decode_phase_names()
     P = len(names)
 
@@ -594,13 +605,50 @@ def measure(config, args, dev, headline, weights=0):
         step.launch()
     torch.cuda.synchronize()
     t_dom = sum(e0.elapsed_time(e1) for e0, e1 in pairs) * 1e-3 / max(args.steps, 1)
+    # (every row read from host memory, the read-ahead included)
     host_bytes = int(out["host_bytes"][0])
+    t_gather = ph_us[names.index("fetch")] * 1e-6
+    # the same steps without read-ahead: its step time, the bytes the method
+    # itself fetches, and the host link's rate on them in the gather
+    ra_rows = vk.vkv_decode_prefetch_rows(step.args)
+    read_ahead = None
+    fetched_bytes, t_gather_f = host_bytes, t_gather
+    if ra_rows > 0:
+        step0 = make_step(0)
+        for i in range(max(2, min(args.warmup, 5))):
+            step0.args.q = vk._ptr(t_qs[i % nq])
+            step0.launch()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step0.args.q = vk._ptr(t_qs[i])
+            step0.launch()
+        torch.cuda.synchronize()
+        ms0 = (time.perf_counter() - t0) * 1e3 / max(args.steps, 1)
+        fetched_bytes = int(step0.out["host_bytes"][0])
+        jf = names.index("fetch")
+        fp = [timed_events(2) for _ in range(nprof)]
+        torch.cuda.synchronize()
+        for i in range(nprof):
+            step0.args.q = vk._ptr(t_qs[i % nq])
+            evl = [None] * (P + 1)
+            evl[jf], evl[jf + 1] = fp[i]
+            step0.set_phase_events(evl)
+            step0.launch()
+        torch.cuda.synchronize()
+        t_gather_f = sum(e0.elapsed_time(e1) for e0, e1 in fp) * 1e-3 / nprof
+        read_ahead = {"rows_per_kv_head": ra_rows,
+                      "ms_per_step_without": ms0,
+                      "host_bytes_per_step_without": fetched_bytes,
+                      "host_bytes_read_ahead_not_fetched": host_bytes - fetched_bytes,
+                      "fetch_us_without": t_gather_f * 1e6,
+                      "fetch_us": t_gather * 1e6}
+        del step0
     ks = out["k_star"].cpu().numpy()
     paths = np.bincount(out["row_path"].cpu().numpy().ravel(), minlength=4)
-    fetch_pct = 100.0 * host_bytes / (B * G * n * ROW_BYTES)
+    fetch_pct = 100.0 * fetched_bytes / (B * G * n * ROW_BYTES)
     units = B * Hq * n
     achieved = cand[dom] / t_dom / 1e9
-    t_gather = ph_us[names.index("fetch")] * 1e-6
 
     def hbm(k, v):
         t = solo[k] * 1e-6
@@ -629,7 +677,9 @@ def measure(config, args, dev, headline, weights=0):
         "fetch_pct": fetch_pct,
         "host_bytes_per_step": host_bytes,
         "host_bytes_per_request": host_bytes / B,
-        "host_fetch_gbs": host_bytes / t_gather / 1e9 if t_gather > 0 else None,
+        # the method's own fetch over the gather's time without read-ahead
+        "host_fetch_gbs": fetched_bytes / t_gather_f / 1e9 if t_gather_f > 0 else None,
+        "read_ahead": read_ahead,
         "decisions_fetching_pct": 100.0 * float(np.mean(ks > 0)),
         "decision_paths": {"no_fetch": int(paths[0]), "top_candidates": int(paths[1]),
                            "all_candidates": int(paths[2]),

@@ -398,6 +398,11 @@ vkv_status vkv_sketch2_build(const vkv_sketch2_args *a, void *stream);
 /* Enqueue one PoissonComp pass (see vkv_compress_args). */
 vkv_status vkv_compress(const vkv_compress_args *a, void *stream);
 
+/* Rows per (request, KV head) that a decode step with these arguments
+ * reads ahead (prefetch_rows resolved: -1 gives the library's choice for
+ * the shapes); -1 when the shapes are invalid. */
+int32_t vkv_decode_prefetch_rows(const vkv_decode_args *a);
+
 /* Enqueue one KVFetch decode step (see vkv_decode_args). */
 vkv_status vkv_decode_step(const vkv_decode_args *a, void *stream);
 

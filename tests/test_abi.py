@@ -108,6 +108,21 @@ def test_workspace_sizes():
     pf = vk.vkv_decode_workspace_bytes(_decode_args(prefetch_rows=1000))
     assert pf >= dw + 2 * 8 * 1000 * 512
     assert vk.vkv_decode_workspace_bytes(_decode_args(prefetch_rows=-1)) > dw
+    assert vk.vkv_decode_prefetch_rows(_decode_args(prefetch_rows=1000)) == 1000
+    assert vk.vkv_decode_prefetch_rows(_decode_args(prefetch_rows=0)) == 0
+    # the library's choice: 6144 (B Hq n / 2^20)^0.6 rows over the B G KV heads
+    assert vk.vkv_decode_prefetch_rows(_decode_args(
+        batch=1, n_tokens=32768, fetch_cap=32768, prefetch_rows=-1)) == 768
+    assert vk.vkv_decode_prefetch_rows(_decode_args(
+        batch=16, n_tokens=32768, fetch_cap=32768, prefetch_rows=-1)) == 253
+    assert vk.vkv_decode_prefetch_rows(_decode_args(
+        batch=4, n_tokens=131072, fetch_cap=131072, prefetch_rows=-1)) == 1013
+    assert vk.vkv_decode_prefetch_rows(_decode_args(n_q_heads=20)) == -1
+    # with the 2-bit sketch, none below 2^23 query-head tokens
+    assert vk.vkv_decode_prefetch_rows(_decode_args(
+        batch=1, n_tokens=32768, fetch_cap=32768, weights=2, prefetch_rows=-1)) == 0
+    assert vk.vkv_decode_prefetch_rows(_decode_args(
+        batch=16, n_tokens=32768, fetch_cap=32768, weights=2, prefetch_rows=-1)) == 253
     # the shapes named in the configs fit easily in 288 GB
     big = _decode_args(batch=16, n_tokens=32768, cap=4600, fetch_cap=32768)
     assert vk.vkv_decode_workspace_bytes(big) < 8 * 2 ** 30

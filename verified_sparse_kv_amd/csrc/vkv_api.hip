@@ -269,6 +269,11 @@ size_t vkv_decode_workspace_bytes(const vkv_decode_args *a) {
   return vkv::decode_layout(*a).total;
 }
 
+int32_t vkv_decode_prefetch_rows(const vkv_decode_args *a) {
+  if (check_decode_shapes(a) != VKV_OK) return -1;
+  return vkv::decode_layout(*a).spec_m;
+}
+
 size_t vkv_sketch2_workspace_bytes(const vkv_sketch2_args *a) {
   if (check_sketch2_args(a) != VKV_OK) return 0;
   return vkv::sketch2_layout(*a).total;

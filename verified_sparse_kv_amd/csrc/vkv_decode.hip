@@ -4644,10 +4644,18 @@ const char *decode_phase_name(int i) {
 // by the B G KV heads, within [64, n / 8] each. (Measured with 64 copying
 // workgroups: the best of 512-896 rows per KV head at 1 x 32 x 32K, of
 // 160-512 at 16 x 32 x 32K and of 768-2048 at 4 x 32 x 128K; the rule
-// gives 768, 255 and 1019.)
+// gives 768, 253 and 1013.)
+// With the 2-bit sketch, the exact shortlist already holds the heaviest
+// tokens and a small batch fetches a few hundred rows per KV head: the
+// fixed cost of the second stream (about 12 us: the fork after the pass-0
+// launch, the join before the gather, the compute units held) is then more
+// than the read-ahead saves (measured at 1 x 32 x 32K: 0.199 ms with 64 rows
+// read ahead against 0.187 ms without; at 16 x 32 x 32K 2.49 against 2.62),
+// so there the library's choice is none below B Hq n = 2^23.
 int spec_rows(const vkv_decode_args &a) {
   if (a.prefetch_rows >= 0) return std::min(a.prefetch_rows, a.n_tokens);
   const double work = (double)a.batch * a.n_q_heads * a.n_tokens / 1048576.0;
+  if (a.weights == VKV_W_SKETCH2 && work < 8.0) return 0;
   const double total = 6144.0 * pow(work, 0.6);
   const double per = total / ((double)a.batch * a.n_kv_heads);
   const int hi = std::max(1, a.n_tokens / 8);

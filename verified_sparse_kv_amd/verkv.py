@@ -38,7 +38,7 @@ EXPORTS = ("vkv_compress_workspace_bytes", "vkv_decode_workspace_bytes",
            "vkv_decode_phase_name", "vkv_dense_workspace_bytes",
            "vkv_dense_attention", "vkv_decode_step_noalloc",
            "vkv_sketch2_workspace_bytes", "vkv_sketch2_build",
-           "vkv_append_token")
+           "vkv_append_token", "vkv_decode_prefetch_rows")
 NOALLOC_WORKSPACE_BYTES = 128 << 20
 
 _p = ctypes.c_void_p
@@ -135,6 +135,8 @@ def _load():
     lib.vkv_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.vkv_compress.argtypes = [ctypes.POINTER(CompressArgs), _p]
     lib.vkv_compress.restype = ctypes.c_int
+    lib.vkv_decode_prefetch_rows.argtypes = [ctypes.POINTER(DecodeArgs)]
+    lib.vkv_decode_prefetch_rows.restype = ctypes.c_int32
     lib.vkv_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _p]
     lib.vkv_decode_step.restype = ctypes.c_int
     lib.vkv_decode_step_noalloc.argtypes = [ctypes.POINTER(DecodeArgs), _p]
@@ -172,6 +174,10 @@ def vkv_compress_workspace_bytes(args):
 
 def vkv_decode_workspace_bytes(args):
     return int(LIB.vkv_decode_workspace_bytes(ctypes.byref(args)))
+
+
+def vkv_decode_prefetch_rows(args):
+    return int(LIB.vkv_decode_prefetch_rows(ctypes.byref(args)))
 
 
 def vkv_compress(args, stream=None):
