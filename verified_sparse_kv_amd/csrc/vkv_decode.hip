@@ -3934,45 +3934,94 @@ __device__ __forceinline__ int spec_bin(float sc) {
   return (int)x;
 }
 
+// kSpecUnroll samples of a thread (sample k is token (k / kSpecRun) kChunk
+// + k % kSpecRun): position (-1: none), r and the group's plan logits.
+template <int GRP>
+__device__ __forceinline__ void spec_samples(const DParams &p, int b, int g,
+                                             int s0, int nsamp,
+                                             int (&ii)[kSpecUnroll],
+                                             float (&rv)[kSpecUnroll],
+                                             float (&sv)[kSpecUnroll][GRP]) {
+  const float *rr = p.r + (size_t)(b * p.G + g) * p.ns;
+#pragma unroll
+  for (int u = 0; u < kSpecUnroll; ++u) {
+    const int sidx = s0 + u * kBlock + (int)threadIdx.x;
+    const int i = (sidx / kSpecRun) * kChunk + sidx % kSpecRun;
+    ii[u] = sidx < nsamp && i < p.n ? i : -1;
+    rv[u] = ii[u] >= 0 ? rr[i] : 1.0f;
+#pragma unroll
+    for (int h = 0; h < GRP; ++h)
+      sv[u][h] = ii[u] >= 0 ? p.shat[(size_t)row_of(p, b, g, h, GRP) * p.n + i] : 0.0f;
+  }
+}
+
 // Per KV head (one workgroup each): m_L + log D~_L of every query head from
 // the scan chunks' pass-0 records, the bitmap of the resident positions, and
 // from a sample of L (the first kSpecRun tokens of every kChunk) the score
-// bin above which about spec_m tokens lie.
+// bin above which about spec_m tokens lie. The first samples, the records
+// and the resident list are all loaded before any of them is used.
+constexpr int kSpecRecPerLane = kMaxTokens / kChunk / kWave;
 template <int GRP>
 __global__ __launch_bounds__(kBlock) void sp_pick(DParams p) {
   const int g = blockIdx.x, b = blockIdx.y, bg = b * p.G + g;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   constexpr int W = kBlock / kWave;
+  constexpr int kResPerThread = 32;  // resident positions loaded at once
   const int np = p.nch + p.nrr, nw = p.nwords;
   __shared__ float s_c[GRP];
   __shared__ uint32_t s_hist[kSpecBins];
   __shared__ uint32_t s_res[kMaxTokens / 32];
   __shared__ uint32_t s_scan[W + 1];
   __shared__ int s_best[W];
+  const int nsamp = (p.n + kChunk - 1) / kChunk * kSpecRun;
+  int ii[kSpecUnroll];
+  float rv[kSpecUnroll], sv[kSpecUnroll][GRP];
+  spec_samples<GRP>(p, b, g, 0, nsamp, ii, rv, sv);
+  // (the records of head `wave`, and of head wave + W, ... in later rounds)
+  float pm[kSpecRecPerLane], pw[kSpecRecPerLane];
+  auto load_rec = [](const DParams &q, int row, int np_, int ln, float (&m_)[kSpecRecPerLane],
+                     float (&w_)[kSpecRecPerLane]) {
+#pragma unroll
+    for (int k = 0; k < kSpecRecPerLane; ++k) {
+      const int t = ln + k * kWave;
+      m_[k] = t < q.nch ? q.pmax[(size_t)row * np_ + t] : -INFINITY;
+      w_[k] = t < q.nch ? (float)q.p0part[((size_t)row * np_ + t) * 4] : 0.0f;
+    }
+  };
+  if (wave < GRP) load_rec(p, row_of(p, b, g, wave, GRP), np, lane, pm, pw);
+  const int cnt = min(p.rcount[bg], p.cap);
+  const int32_t *ri = p.ridx + (size_t)bg * p.cap;
+  int rp[kResPerThread];
+#pragma unroll
+  for (int k = 0; k < kResPerThread; ++k) {
+    const int j = (int)threadIdx.x + k * kBlock;
+    rp[k] = j < cnt ? ri[j] : -1;
+  }
   for (int i = threadIdx.x; i < kSpecBins; i += kBlock) s_hist[i] = 0u;
   for (int i = threadIdx.x; i < nw; i += kBlock) s_res[i] = 0u;
   for (int h = wave; h < GRP; h += W) {
-    const int row = row_of(p, b, g, h, GRP);
+    if (h != wave) load_rec(p, row_of(p, b, g, h, GRP), np, lane, pm, pw);
     float m = -INFINITY;
-    for (int t = lane; t < p.nch; t += kWave) m = fmaxf(m, p.pmax[(size_t)row * np + t]);
+#pragma unroll
+    for (int k = 0; k < kSpecRecPerLane; ++k) m = fmaxf(m, pm[k]);
     m = wave_fold<float, OpMax<float>>(m);
     float sw = 0.0f;
-    for (int t = lane; t < p.nch; t += kWave) {
-      const float sv = (float)p.p0part[((size_t)row * np + t) * 4];
-      if (sv > 0.0f) sw += sv * __expf(p.pmax[(size_t)row * np + t] - m);
-    }
+#pragma unroll
+    for (int k = 0; k < kSpecRecPerLane; ++k)
+      if (pw[k] > 0.0f) sw += pw[k] * __expf(pm[k] - m);
     sw = wave_fold<float, OpSum<float>>(sw);
     if (lane == 0) {
       const float c = sw > 0.0f ? m + __logf(sw) : INFINITY;  // inf: no L
       s_c[h] = c;
-      p.sp_c[row] = c;
+      p.sp_c[row_of(p, b, g, h, GRP)] = c;
     }
   }
-  __syncthreads();
-  const int cnt = min(p.rcount[bg], p.cap);
-  const int32_t *ri = p.ridx + (size_t)bg * p.cap;
-  for (int k = threadIdx.x; k < cnt; k += kBlock) {
-    const int pos = ri[k];
+  __syncthreads();  // s_res cleared, s_c written
+#pragma unroll
+  for (int k = 0; k < kResPerThread; ++k)
+    if (rp[k] >= 0 && rp[k] < p.n) atomicOr(&s_res[rp[k] / 32], 1u << (rp[k] % 32));
+  for (int j = (int)threadIdx.x + kResPerThread * kBlock; j < cnt; j += kBlock) {
+    const int pos = ri[j];
     if (pos >= 0 && pos < p.n) atomicOr(&s_res[pos / 32], 1u << (pos % 32));
   }
   __syncthreads();
@@ -3980,21 +4029,8 @@ __global__ __launch_bounds__(kBlock) void sp_pick(DParams p) {
   float c[GRP];
 #pragma unroll
   for (int h = 0; h < GRP; ++h) c[h] = s_c[h];
-  const float *rr = p.r + (size_t)bg * p.ns;
-  const int nsamp = (p.n + kChunk - 1) / kChunk * kSpecRun;
   for (int s0 = 0; s0 < nsamp; s0 += kBlock * kSpecUnroll) {
-    int ii[kSpecUnroll];
-    float rv[kSpecUnroll], sv[kSpecUnroll][GRP];
-#pragma unroll
-    for (int u = 0; u < kSpecUnroll; ++u) {
-      const int sidx = s0 + u * kBlock + (int)threadIdx.x;
-      const int i = (sidx / kSpecRun) * kChunk + sidx % kSpecRun;
-      ii[u] = sidx < nsamp && i < p.n ? i : -1;
-      rv[u] = ii[u] >= 0 ? rr[i] : 1.0f;
-#pragma unroll
-      for (int h = 0; h < GRP; ++h)
-        sv[u][h] = ii[u] >= 0 ? p.shat[(size_t)row_of(p, b, g, h, GRP) * p.n + i] : 0.0f;
-    }
+    if (s0 > 0) spec_samples<GRP>(p, b, g, s0, nsamp, ii, rv, sv);
 #pragma unroll
     for (int u = 0; u < kSpecUnroll; ++u) {
       const int i = ii[u];
