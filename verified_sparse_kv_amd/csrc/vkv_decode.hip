@@ -56,6 +56,7 @@ constexpr float kInvSqrtD = 0.08838834764831845f;  // 1/sqrt(128)
 constexpr int kSelDigit = 11;    // radix digit of the selections' keys
 constexpr int kSelBinsP = 1 << kSelDigit;
 constexpr int kBinCap = 256;     // keys per round of the binary shrinkage
+constexpr int kSpecBins = 1024;  // read-ahead score histogram: bin = -32 score
 static_assert(kBinCap <= 4 * kWave, "one wave sorts a round");
 
 struct RowState {
@@ -165,11 +166,10 @@ struct DParams {
   unsigned long long *candk;
   float *candw, *candq;  // w~ and r of each candidate
   double *dpart;         // [row][kSelWG][2] float64 sums below the bound
-  // speculative reads (prefetch): per row m_L + log D~_L; per group the
-  // selection's score bin and its slot counter; per group the bitmap of S,
-  // of the rows read and each word's first slot; the rows [group][spec_m]
-  float *sp_c;
-  int32_t *sp_thr;
+  // read-ahead: per group a sampled score histogram and a slot counter, the
+  // bitmaps of S and of the rows read ahead with each word's first slot;
+  // the rows [group][spec_m]
+  uint32_t *sp_hist;
   uint32_t *sp_cnt;
   uint32_t *sp_res, *sp_bits, *sp_base;
   int32_t *sp_list;  // [group][spec_m] positions to read, in slot order
@@ -690,6 +690,13 @@ __device__ __forceinline__ void scan_setup(const DParams &p, int c, int g,
     }
   }
   clear_bin_hist<GRP>(p, c, b, g);
+  if (p.spec_m > 0) {  // the read-ahead's histogram and slot counter
+    int lo, hi;
+    split_range(kSpecBins, p.nch, c, lo, hi);
+    for (int t = lo + (int)threadIdx.x; t < hi; t += kBlock)
+      p.sp_hist[(size_t)bg * kSpecBins + t] = 0u;
+    if (c == 0 && threadIdx.x == 0) p.sp_cnt[bg] = 0u;
+  }
   if (p.smap_next) {  // this step's staging map starts empty
     const int i1 = min((c + 1) * p.chunk, p.n);
     for (int i = c * p.chunk + (int)threadIdx.x; i < i1; i += kBlock)
@@ -699,6 +706,7 @@ __device__ __forceinline__ void scan_setup(const DParams &p, int c, int g,
   for (int w = threadIdx.x; w < nw; w += kBlock) {
     if (w0 + w < p.nwords) {
       p.fbits[(size_t)bg * p.nwords + w0 + w] = 0u;
+      if (p.spec_m > 0) p.sp_res[(size_t)bg * p.nwords + w0 + w] = 0u;
       for (int h = 0; h < GRP; ++h)
         p.hbits[(size_t)row_of(p, b, g, h, GRP) * p.nwords + w0 + w] = 0u;
     }
@@ -3918,12 +3926,15 @@ __device__ __forceinline__ void gather_attend(const DParams &p, int j, int g,
 // finds it. A row is the same bytes wherever it is read from, so no output
 // depends on the read-ahead; a row read ahead but not fetched costs only
 // host-link time that the planning leaves idle.
-constexpr int kSpecBins = 1024;         // score histogram: bin = -32 score
 constexpr float kSpecBinScale = 32.0f;  // (bin 1023 takes every score < -32)
 constexpr int kSpecRun = 64;            // tokens sampled per kChunk tokens
 constexpr int kSpecUnroll = 8;          // samples per thread in flight
-constexpr int kSpecMoveUnroll = 8;      // rows per half-wave in flight
-constexpr int kSpecMovers = 64;         // copying workgroups (compute units)
+// Rows in flight for the copy: 32 workgroups x 8 half-waves x 2 rows, about
+// 256 KB, what the host link needs to stay busy. More (64 x 8 x 8) flooded
+// the memory path and held up the planning launches' HBM loads on every
+// compute unit (c2 step 0.196 against 0.163 ms).
+constexpr int kSpecMoveUnroll = 2;      // rows per half-wave in flight
+constexpr int kSpecMovers = 32;         // copying workgroups (compute units)
 // dynamic LDS each copying workgroup asks for: with its own few bytes, the
 // 160 KB of a compute unit less less than the smallest planning
 // workgroup's LDS (8.4 KB), so no planning workgroup fits beside it
@@ -3955,52 +3966,25 @@ __device__ __forceinline__ void spec_samples(const DParams &p, int b, int g,
   }
 }
 
-// Per KV head (one workgroup each): m_L + log D~_L of every query head from
-// the scan chunks' pass-0 records, the bitmap of the resident positions, and
-// from a sample of L (the first kSpecRun tokens of every kChunk) the score
-// bin above which about spec_m tokens lie. The first samples, the records
-// and the resident list are all loaded before any of them is used.
+// m_h + log D~_L,h of the group's query heads into s_c (LDS), from the scan
+// chunks' pass-0 records (one wave per head; +inf for a head without
+// weight on L). Ends with a workgroup barrier.
 constexpr int kSpecRecPerLane = kMaxTokens / kChunk / kWave;
 template <int GRP>
-__global__ __launch_bounds__(kBlock) void sp_pick(DParams p) {
-  const int g = blockIdx.x, b = blockIdx.y, bg = b * p.G + g;
+__device__ __forceinline__ void spec_norms(const DParams &p, int b, int g,
+                                           float *s_c) {
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   constexpr int W = kBlock / kWave;
-  constexpr int kResPerThread = 32;  // resident positions loaded at once
-  const int np = p.nch + p.nrr, nw = p.nwords;
-  __shared__ float s_c[GRP];
-  __shared__ uint32_t s_hist[kSpecBins];
-  __shared__ uint32_t s_res[kMaxTokens / 32];
-  __shared__ uint32_t s_scan[W + 1];
-  __shared__ int s_best[W];
-  const int nsamp = (p.n + kChunk - 1) / kChunk * kSpecRun;
-  int ii[kSpecUnroll];
-  float rv[kSpecUnroll], sv[kSpecUnroll][GRP];
-  spec_samples<GRP>(p, b, g, 0, nsamp, ii, rv, sv);
-  // (the records of head `wave`, and of head wave + W, ... in later rounds)
-  float pm[kSpecRecPerLane], pw[kSpecRecPerLane];
-  auto load_rec = [](const DParams &q, int row, int np_, int ln, float (&m_)[kSpecRecPerLane],
-                     float (&w_)[kSpecRecPerLane]) {
+  const int np = p.nch + p.nrr;
+  for (int h = wave; h < GRP; h += W) {
+    const int row = row_of(p, b, g, h, GRP);
+    float pm[kSpecRecPerLane], pw[kSpecRecPerLane];
 #pragma unroll
     for (int k = 0; k < kSpecRecPerLane; ++k) {
-      const int t = ln + k * kWave;
-      m_[k] = t < q.nch ? q.pmax[(size_t)row * np_ + t] : -INFINITY;
-      w_[k] = t < q.nch ? (float)q.p0part[((size_t)row * np_ + t) * 4] : 0.0f;
+      const int t = lane + k * kWave;
+      pm[k] = t < p.nch ? p.pmax[(size_t)row * np + t] : -INFINITY;
+      pw[k] = t < p.nch ? (float)p.p0part[((size_t)row * np + t) * 4] : 0.0f;
     }
-  };
-  if (wave < GRP) load_rec(p, row_of(p, b, g, wave, GRP), np, lane, pm, pw);
-  const int cnt = min(p.rcount[bg], p.cap);
-  const int32_t *ri = p.ridx + (size_t)bg * p.cap;
-  int rp[kResPerThread];
-#pragma unroll
-  for (int k = 0; k < kResPerThread; ++k) {
-    const int j = (int)threadIdx.x + k * kBlock;
-    rp[k] = j < cnt ? ri[j] : -1;
-  }
-  for (int i = threadIdx.x; i < kSpecBins; i += kBlock) s_hist[i] = 0u;
-  for (int i = threadIdx.x; i < nw; i += kBlock) s_res[i] = 0u;
-  for (int h = wave; h < GRP; h += W) {
-    if (h != wave) load_rec(p, row_of(p, b, g, h, GRP), np, lane, pm, pw);
     float m = -INFINITY;
 #pragma unroll
     for (int k = 0; k < kSpecRecPerLane; ++k) m = fmaxf(m, pm[k]);
@@ -4010,47 +3994,81 @@ __global__ __launch_bounds__(kBlock) void sp_pick(DParams p) {
     for (int k = 0; k < kSpecRecPerLane; ++k)
       if (pw[k] > 0.0f) sw += pw[k] * __expf(pm[k] - m);
     sw = wave_fold<float, OpSum<float>>(sw);
-    if (lane == 0) {
-      const float c = sw > 0.0f ? m + __logf(sw) : INFINITY;  // inf: no L
-      s_c[h] = c;
-      p.sp_c[row_of(p, b, g, h, GRP)] = c;
-    }
-  }
-  __syncthreads();  // s_res cleared, s_c written
-#pragma unroll
-  for (int k = 0; k < kResPerThread; ++k)
-    if (rp[k] >= 0 && rp[k] < p.n) atomicOr(&s_res[rp[k] / 32], 1u << (rp[k] % 32));
-  for (int j = (int)threadIdx.x + kResPerThread * kBlock; j < cnt; j += kBlock) {
-    const int pos = ri[j];
-    if (pos >= 0 && pos < p.n) atomicOr(&s_res[pos / 32], 1u << (pos % 32));
+    if (lane == 0) s_c[h] = sw > 0.0f ? m + __logf(sw) : INFINITY;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < nw; i += kBlock) p.sp_res[(size_t)bg * nw + i] = s_res[i];
+}
+
+// Per kSpecHistSamples samples of a KV head (sample k is token (k /
+// kSpecRun) kChunk + k % kSpecRun: the first kSpecRun tokens of every
+// kChunk): their scores into the group's histogram (cleared by the front
+// launch), and this workgroup's share of the resident list into the group's
+// bitmap of S (cleared likewise). The samples are loaded before anything
+// else; the histogram counts the tokens of L, S included.
+constexpr int kSpecHistSamples = kBlock * kSpecUnroll;
+constexpr int kSpecResUnroll = 8;
+template <int GRP>
+__global__ __launch_bounds__(kBlock) void sp_hist(DParams p) {
+  const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z, bg = b * p.G + g;
+  __shared__ float s_c[GRP];
+  __shared__ uint32_t s_hist[kSpecBins];
+  const int nsamp = (p.n + kChunk - 1) / kChunk * kSpecRun;
+  int ii[kSpecUnroll];
+  float rv[kSpecUnroll], sv[kSpecUnroll][GRP];
+  spec_samples<GRP>(p, b, g, j * kSpecHistSamples, nsamp, ii, rv, sv);
+  const int cnt = min(p.rcount[bg], p.cap);
+  int k0, k1;
+  split_range(max(cnt, 0), (int)gridDim.x, j, k0, k1);
+  const int32_t *ri = p.ridx + (size_t)bg * p.cap;
+  int rp[kSpecResUnroll];
+#pragma unroll
+  for (int u = 0; u < kSpecResUnroll; ++u) {
+    const int k = k0 + (int)threadIdx.x + u * kBlock;
+    rp[u] = k < k1 ? ri[k] : -1;
+  }
+  for (int i = threadIdx.x; i < kSpecBins; i += kBlock) s_hist[i] = 0u;
+  spec_norms<GRP>(p, b, g, s_c);
+  uint32_t *res = p.sp_res + (size_t)bg * p.nwords;
+#pragma unroll
+  for (int u = 0; u < kSpecResUnroll; ++u)
+    if (rp[u] >= 0 && rp[u] < p.n) atomicOr(&res[rp[u] / 32], 1u << (rp[u] % 32));
+  for (int k = k0 + (int)threadIdx.x + kSpecResUnroll * kBlock; k < k1; k += kBlock) {
+    const int pos = ri[k];
+    if (pos >= 0 && pos < p.n) atomicOr(&res[pos / 32], 1u << (pos % 32));
+  }
   float c[GRP];
 #pragma unroll
   for (int h = 0; h < GRP; ++h) c[h] = s_c[h];
-  for (int s0 = 0; s0 < nsamp; s0 += kBlock * kSpecUnroll) {
-    if (s0 > 0) spec_samples<GRP>(p, b, g, s0, nsamp, ii, rv, sv);
 #pragma unroll
-    for (int u = 0; u < kSpecUnroll; ++u) {
-      const int i = ii[u];
-      if (i < 0 || !(rv[u] < 1.0f) || ((s_res[i / 32] >> (i % 32)) & 1u)) continue;
-      float sc = -INFINITY;
+  for (int u = 0; u < kSpecUnroll; ++u) {
+    if (ii[u] < 0 || !(rv[u] < 1.0f)) continue;
+    float sc = -INFINITY;
 #pragma unroll
-      for (int h = 0; h < GRP; ++h) sc = fmaxf(sc, sv[u][h] - c[h]);
-      sc += __logf(1.0f - rv[u]);
-      if (sc == sc) atomicAdd(&s_hist[spec_bin(sc)], 1u);
-    }
+    for (int h = 0; h < GRP; ++h) sc = fmaxf(sc, sv[u][h] - c[h]);
+    sc += __logf(1.0f - rv[u]);
+    if (sc == sc) atomicAdd(&s_hist[spec_bin(sc)], 1u);
   }
   __syncthreads();
-  // the last bin (best first) whose cumulative count stays within the
-  // sample's share of spec_m
-  const uint32_t tgt = (uint32_t)(((long long)p.spec_m * kSpecRun) / kChunk);
+  uint32_t *gh = p.sp_hist + (size_t)bg * kSpecBins;
+  for (int i = threadIdx.x; i < kSpecBins; i += kBlock)
+    if (s_hist[i] != 0u) atomicAdd(&gh[i], s_hist[i]);
+}
+
+// The score bin at and above which about spec_m tokens of the group lie:
+// the last bin (best first) whose cumulative sampled count stays within the
+// sample's share of spec_m (at least bin 0). Every workgroup of the group
+// forms it from the same histogram, so all agree.
+__device__ __forceinline__ int spec_threshold(const DParams &p, int bg,
+                                              uint32_t *s_scan, int *s_best) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  constexpr int W = kBlock / kWave;
   constexpr int BPT = kSpecBins / kBlock;
+  const uint32_t tgt = (uint32_t)(((long long)p.spec_m * kSpecRun) / kChunk);
+  const uint32_t *gh = p.sp_hist + (size_t)bg * kSpecBins;
   uint32_t loc[BPT], mine = 0u;
 #pragma unroll
   for (int k = 0; k < BPT; ++k) {
-    loc[k] = s_hist[threadIdx.x * BPT + k];
+    loc[k] = gh[threadIdx.x * BPT + k];
     mine += loc[k];
   }
   uint32_t tot;
@@ -4064,13 +4082,10 @@ __global__ __launch_bounds__(kBlock) void sp_pick(DParams p) {
   best = wave_fold<int, OpMax<int>>(best);
   if (lane == 0) s_best[wave] = best;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int bb = s_best[0];
+  int bb = s_best[0];
 #pragma unroll
-    for (int w = 1; w < W; ++w) bb = max(bb, s_best[w]);
-    p.sp_thr[bg] = max(bb, 0);
-    p.sp_cnt[bg] = 0u;
-  }
+  for (int w = 1; w < W; ++w) bb = max(bb, s_best[w]);
+  return max(bb, 0);
 }
 
 // Per kChunk tokens of a KV head: the tokens of L outside S (and not staged
@@ -4090,10 +4105,9 @@ __global__ __launch_bounds__(kBlock) void sp_sel(DParams p) {
   __shared__ uint32_t s_bits[NW], s_keep[NW], s_before[NW];
   __shared__ int s_list[kChunk];
   __shared__ uint32_t s_base;
-  const int thr = p.sp_thr[bg];
-  float cc[GRP];
-#pragma unroll
-  for (int h = 0; h < GRP; ++h) cc[h] = p.sp_c[row_of(p, b, g, h, GRP)];
+  __shared__ float s_c[GRP];
+  __shared__ uint32_t s_scan[kBlock / kWave + 1];
+  __shared__ int s_best[kBlock / kWave];
   const float *rr = p.r + (size_t)bg * p.ns;
   const uint32_t *res = p.sp_res + (size_t)bg * nw;
   float rv[TPT], sv[TPT][GRP];
@@ -4108,6 +4122,11 @@ __global__ __launch_bounds__(kBlock) void sp_sel(DParams p) {
     for (int h = 0; h < GRP; ++h)
       sv[k][h] = in ? p.shat[(size_t)row_of(p, b, g, h, GRP) * p.n + i] : 0.0f;
   }
+  spec_norms<GRP>(p, b, g, s_c);
+  const int thr = spec_threshold(p, bg, s_scan, s_best);
+  float cc[GRP];
+#pragma unroll
+  for (int h = 0; h < GRP; ++h) cc[h] = s_c[h];
 #pragma unroll
   for (int k = 0; k < TPT; ++k) {
     const int i = t0 + k * kBlock + (int)threadIdx.x;
@@ -4196,10 +4215,12 @@ __global__ __launch_bounds__(kBlock) void sp_move(DParams p) {
     }
     uint4 v[kSpecMoveUnroll];
 #pragma unroll
-    for (int u = 0; u < kSpecMoveUnroll; ++u)
+    for (int u = 0; u < kSpecMoveUnroll; ++u) {
+      v[u] = make_uint4(0u, 0u, 0u, 0u);
       if (pos[u] >= 0)
         v[u] = reinterpret_cast<const uint4 *>(
             p.host_kv + ((size_t)bgs[u] * p.ns + pos[u]) * 2 * kHeadDim)[unit];
+    }
 #pragma unroll
     for (int u = 0; u < kSpecMoveUnroll; ++u) {
       if (pos[u] < 0) continue;
@@ -4611,7 +4632,11 @@ hipError_t run(const DParams &p, hipStream_t s, int sd, void **events,
   if (sx) {
     hipError_t e = hipStreamWaitEvent(sx->side, sx->fork, 0);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(sp_pick<GRP>, dim3((unsigned)p.G, (unsigned)p.B), blk, 0, sx->side, p);
+    const int nsamp = (p.n + kChunk - 1) / kChunk * kSpecRun;
+    hipLaunchKernelGGL(sp_hist<GRP>,
+                       dim3((unsigned)((nsamp + kSpecHistSamples - 1) / kSpecHistSamples),
+                            (unsigned)p.G, (unsigned)p.B),
+                       blk, 0, sx->side, p);
     hipLaunchKernelGGL(sp_sel<GRP>,
                        dim3((unsigned)((p.n + kChunk - 1) / kChunk), (unsigned)p.G,
                             (unsigned)p.B),
@@ -4808,8 +4833,7 @@ DecodeLayout decode_layout(const vkv_decode_args &a) {
   L.skey = c.take<uint32_t>(groups * n);  // (2-bit sketch only)
   L.spec_m = spec_rows(a);
   if (L.spec_m > 0) {
-    L.sp_c = c.take<float>(rows);
-    L.sp_thr = c.take<int32_t>(groups);
+    L.sp_hist = c.take<uint32_t>(groups * (size_t)kSpecBins);
     L.sp_cnt = c.take<uint32_t>(groups);
     L.sp_res = c.take<uint32_t>(groups * L.nwords);
     L.sp_bits = c.take<uint32_t>(groups * L.nwords);
@@ -4888,8 +4912,7 @@ hipError_t launch_decode(const vkv_decode_args &a, const DecodeLayout &L,
   p.npad = L.npad;
   p.spec_m = L.spec_m;
   if (L.spec_m > 0) {
-    p.sp_c = at<float>(w, L.sp_c);
-    p.sp_thr = at<int32_t>(w, L.sp_thr);
+    p.sp_hist = at<uint32_t>(w, L.sp_hist);
     p.sp_cnt = at<uint32_t>(w, L.sp_cnt);
     p.sp_res = at<uint32_t>(w, L.sp_res);
     p.sp_bits = at<uint32_t>(w, L.sp_bits);

@@ -58,7 +58,7 @@ hipError_t launch_compress(const vkv_compress_args &a, const CompressLayout &L,
 struct DecodeLayout {
   int grp, nch, nrr, ncr, ncf, npad, nwords, chunk, nrc, nsub, rsub, nsel;
   int spec_m;  // rows per (request, KV head) read ahead (0: none)
-  size_t sp_c, sp_thr, sp_cnt, sp_res, sp_bits, sp_base, sp_list, spec_kv;
+  size_t sp_hist, sp_cnt, sp_res, sp_bits, sp_base, sp_list, spec_kv;
   size_t shat, ell, hpart, fstat, fbits, hbits, pmax, p0part, hres, rows,
       bpart, band,
       bstate,
