@@ -28,6 +28,13 @@
 //               loads (zero-copy) with the attention over those rows.
 //  dk_attn      merge of the partial softmax sums by log-sum-exp.
 //
+// With read-ahead (prefetch_rows), a second stream forks once the pass-0
+// records exist and runs beside the planning launches: sp_hist (a sampled
+// histogram of a planning score per KV head), sp_sel (the tokens above its
+// threshold take slots of a device area) and sp_move (their rows copied
+// from pinned host memory); dk_fetch waits for it and reads a fetched row
+// from that area when it was read ahead.
+//
 // Passes over a row's tokens run as many workgroups per row; every
 // workgroup combines the partial records of the previous launch itself, so
 // no workgroup waits for another.
@@ -3935,9 +3942,9 @@ constexpr int kSpecUnroll = 8;          // samples per thread in flight
 // compute unit (c2 step 0.196 against 0.163 ms).
 constexpr int kSpecMoveUnroll = 2;      // rows per half-wave in flight
 constexpr int kSpecMovers = 32;         // copying workgroups (compute units)
-// dynamic LDS each copying workgroup asks for: with its own few bytes, the
-// 160 KB of a compute unit less less than the smallest planning
-// workgroup's LDS (8.4 KB), so no planning workgroup fits beside it
+// dynamic LDS each copying workgroup asks for: with its own few bytes it
+// leaves less of a compute unit's 160 KB free than the smallest planning
+// workgroup needs (8.4 KB), so no planning workgroup fits beside it
 constexpr int kSpecMoveLds = 156 * 1024;
 
 __device__ __forceinline__ int spec_bin(float sc) {
