@@ -65,6 +65,10 @@ def parse():
                          "while the planning launches run (-1: the library's "
                          "choice for the shapes, 0: none); each decode block "
                          "also times the same steps without it")
+    ap.add_argument("--no-prefetch-compare", action="store_true",
+                    help="do not time the decode steps a second time without "
+                         "read-ahead (kernel traces then hold one mode only; "
+                         "fetch_pct then counts the rows read ahead too)")
     ap.add_argument("--weights", default="sketch", choices=["sketch", "sketch2"],
                     help="planning weights of the main line: the projected "
                          "sketch (default) or the pages' 2-bit sketch with "
@@ -613,7 +617,7 @@ def measure(config, args, dev, headline, weights=0):
     ra_rows = vk.vkv_decode_prefetch_rows(step.args)
     read_ahead = None
     fetched_bytes, t_gather_f = host_bytes, t_gather
-    if ra_rows > 0:
+    if ra_rows > 0 and not args.no_prefetch_compare:
         step0 = make_step(0)
         for i in range(max(2, min(args.warmup, 5))):
             step0.args.q = vk._ptr(t_qs[i % nq])
