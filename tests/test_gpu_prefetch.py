@@ -76,6 +76,8 @@ def test_full_c2():
     ("c2", od.W_SKETCH, 2, dict(n=6000, G=2)),
     ("c2", od.W_SKETCH, 1, dict(n=4321, G=2, B=2)),
     ("c4", od.W_SKETCH, 0, dict(n=20000, B=1, G=2)),
+    ("c2", od.W_SKETCH, 0, dict(n=5000, G=2, grp=8)),
+    ("c2", od.W_SKETCH, 0, dict(n=5000, G=4, grp=1)),
 ])
 def test_modes(cfg, weights, est, kw):
     """Every planning-weight mode (the fork follows the pass-0 launch with
@@ -83,7 +85,9 @@ def test_modes(cfg, weights, est, kw):
     gc.say(f"prefetch {cfg} weights={weights} est={est} {kw}")
     w = gc.build_case(cfg, **kw)
     dev = gc.device_inputs(w)
-    _check(w, dev, [-1, 200], est, weights)
+    # (8 rows: more tokens pass the threshold than fit, so the area's slots
+    # run out and the rest are dropped)
+    _check(w, dev, [-1, 200, 8], est, weights)
 
 
 def test_every_row_read_ahead():
