@@ -4027,21 +4027,38 @@ __global__ __launch_bounds__(kBlock) void sp_hist(DParams p) {
   int k0, k1;
   split_range(max(cnt, 0), (int)gridDim.x, j, k0, k1);
   const int32_t *ri = p.ridx + (size_t)bg * p.cap;
+  // each thread a run of kSpecResUnroll consecutive entries of the
+  // (ascending) resident list: the bits of a run that share a bitmap word
+  // go out in one atomic
   int rp[kSpecResUnroll];
+  const int kr = k0 + (int)threadIdx.x * kSpecResUnroll;
 #pragma unroll
-  for (int u = 0; u < kSpecResUnroll; ++u) {
-    const int k = k0 + (int)threadIdx.x + u * kBlock;
-    rp[u] = k < k1 ? ri[k] : -1;
-  }
+  for (int u = 0; u < kSpecResUnroll; ++u) rp[u] = kr + u < k1 ? ri[kr + u] : -1;
   for (int i = threadIdx.x; i < kSpecBins; i += kBlock) s_hist[i] = 0u;
   spec_norms<GRP>(p, b, g, s_c);
   uint32_t *res = p.sp_res + (size_t)bg * p.nwords;
+  auto or_run = [res](const int (&pos)[kSpecResUnroll], int n) {
+    int word = -1;
+    uint32_t bits = 0u;
 #pragma unroll
-  for (int u = 0; u < kSpecResUnroll; ++u)
-    if (rp[u] >= 0 && rp[u] < p.n) atomicOr(&res[rp[u] / 32], 1u << (rp[u] % 32));
-  for (int k = k0 + (int)threadIdx.x + kSpecResUnroll * kBlock; k < k1; k += kBlock) {
-    const int pos = ri[k];
-    if (pos >= 0 && pos < p.n) atomicOr(&res[pos / 32], 1u << (pos % 32));
+    for (int u = 0; u < kSpecResUnroll; ++u) {
+      const int q = pos[u];
+      if (q < 0 || q >= n) continue;
+      if (q / 32 != word) {
+        if (word >= 0) atomicOr(&res[word], bits);
+        word = q / 32;
+        bits = 0u;
+      }
+      bits |= 1u << (q % 32);
+    }
+    if (word >= 0) atomicOr(&res[word], bits);
+  };
+  or_run(rp, p.n);
+  for (int kb = k0 + kBlock * kSpecResUnroll; kb < k1; kb += kBlock * kSpecResUnroll) {
+    const int kt = kb + (int)threadIdx.x * kSpecResUnroll;
+#pragma unroll
+    for (int u = 0; u < kSpecResUnroll; ++u) rp[u] = kt + u < k1 ? ri[kt + u] : -1;
+    or_run(rp, p.n);
   }
   float c[GRP];
 #pragma unroll
