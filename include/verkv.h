@@ -218,7 +218,10 @@ typedef struct {
  *          library's choice for the shapes; otherwise 1..n_tokens. The
  *          workspace grows by prefetch_rows * 2 d * 2 bytes per (request,
  *          KV head). Steps on one device that read ahead share its second
- *          stream and are ordered on it in call order.
+ *          stream and are ordered on it in call order. Code under HIP graph
+ *          capture passes 0 (or calls vkv_decode_step_noalloc, which reads
+ *          nothing ahead): the second stream is the library's, not the
+ *          caller's.
  * status   dev u32 [1], cleared at the start of the call.
  * phase_events  optional timing hook: NULL, or vkv_decode_phase_count() + 1
  *          hipEvent_t handles (created by the caller); event 0 is recorded on
