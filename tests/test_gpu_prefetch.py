@@ -78,6 +78,8 @@ def test_full_c2():
     ("c4", od.W_SKETCH, 0, dict(n=20000, B=1, G=2)),
     ("c2", od.W_SKETCH, 0, dict(n=5000, G=2, grp=8)),
     ("c2", od.W_SKETCH, 0, dict(n=5000, G=4, grp=1)),
+    ("c2", od.W_SKETCH, 0, dict(n=300, G=2, budget=160)),
+    ("c3", od.W_SKETCH, 0, dict(n=2049, B=3, G=1, shift_from=0)),
 ])
 def test_modes(cfg, weights, est, kw):
     """Every planning-weight mode (the fork follows the pass-0 launch with
