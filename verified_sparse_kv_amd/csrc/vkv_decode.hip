@@ -182,6 +182,7 @@ struct DParams {
   int32_t *sp_list;  // [group][spec_m] positions to read, in slot order
   uint16_t *spec_kv;
   int spec_m;        // rows per group read ahead (0: none)
+  int spec_cpw;      // kChunk chunks per selection workgroup
   float2 *apart;     // [row][ncr + ncf] (shift, sum of weights)
   float *aparto;     // [row][d][npad] weighted sums of V, part index fastest
   int B, Hq, G, n, cap, fetch_cap, nch, nrr, ncr, ncf, npad, nwords, chunk, nrc;
@@ -4112,32 +4113,18 @@ __device__ __forceinline__ int spec_threshold(const DParams &p, int bg,
   return max(bb, 0);
 }
 
-// Per kChunk tokens of a KV head: the tokens of L outside S (and not staged
-// by the previous step) whose score bin is within the threshold take slots
-// of the KV head's area in position order (one slot counter per KV head;
-// tokens past spec_m are dropped); their bits and each word's first slot
-// are written for the gather, and their positions into the KV head's list
-// of rows to read.
+// The r, S-bitmap word and plan logits of this thread's tokens of the
+// kChunk tokens from t0 (token t0 + k kBlock + thread).
 template <int GRP>
-__global__ __launch_bounds__(kBlock) void sp_sel(DParams p) {
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z, bg = b * p.G + g;
-  constexpr int NW = kChunk / 32;
-  constexpr int TPT = kChunk / kBlock;
-  static_assert(TPT * kBlock == kChunk && kBlock == 4 * kWave, "token layout");
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int t0 = c * kChunk, nw = p.nwords;
-  __shared__ uint32_t s_bits[NW], s_keep[NW], s_before[NW];
-  __shared__ int s_list[kChunk];
-  __shared__ uint32_t s_base;
-  __shared__ float s_c[GRP];
-  __shared__ uint32_t s_scan[kBlock / kWave + 1];
-  __shared__ int s_best[kBlock / kWave];
+__device__ __forceinline__ void spec_chunk(const DParams &p, int b, int g, int t0,
+                                           float (&rv)[kChunk / kBlock],
+                                           uint32_t (&rw)[kChunk / kBlock],
+                                           float (&sv)[kChunk / kBlock][GRP]) {
+  const int bg = b * p.G + g;
   const float *rr = p.r + (size_t)bg * p.ns;
-  const uint32_t *res = p.sp_res + (size_t)bg * nw;
-  float rv[TPT], sv[TPT][GRP];
-  uint32_t rw[TPT];
+  const uint32_t *res = p.sp_res + (size_t)bg * p.nwords;
 #pragma unroll
-  for (int k = 0; k < TPT; ++k) {
+  for (int k = 0; k < kChunk / kBlock; ++k) {
     const int i = t0 + k * kBlock + (int)threadIdx.x;
     const bool in = i < p.n;
     rv[k] = in ? rr[i] : 1.0f;
@@ -4146,68 +4133,113 @@ __global__ __launch_bounds__(kBlock) void sp_sel(DParams p) {
     for (int h = 0; h < GRP; ++h)
       sv[k][h] = in ? p.shat[(size_t)row_of(p, b, g, h, GRP) * p.n + i] : 0.0f;
   }
+}
+
+// Per spec_cpw consecutive kChunk-token chunks of a KV head (one at batch 1,
+// up to kSpecSelMax when the launch would otherwise hold far more
+// workgroups than run at once): the tokens of L outside S (and not staged
+// by the previous step) whose score bin is within the threshold take slots
+// of the KV head's area in position order (one slot counter per KV head,
+// one atomic add per workgroup; tokens past spec_m are dropped); their bits
+// and each word's first slot are written for the gather, and their
+// positions into the KV head's list of rows to read. The next chunk's
+// tokens load while one is scored.
+constexpr int kSpecSelMax = 8;
+template <int GRP>
+__global__ __launch_bounds__(kBlock) void sp_sel(DParams p) {
+  const int g = blockIdx.y, b = blockIdx.z, bg = b * p.G + g;
+  constexpr int NW = kChunk / 32;
+  constexpr int TPT = kChunk / kBlock;
+  static_assert(TPT * kBlock == kChunk && kBlock == 4 * kWave, "token layout");
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int nw = p.nwords;
+  const int nchunk = (p.n + kChunk - 1) / kChunk;
+  const int c0 = (int)blockIdx.x * p.spec_cpw;
+  const int nc = min(p.spec_cpw, nchunk - c0);  // >= 1 (grid)
+  __shared__ uint32_t s_bits[kSpecSelMax * NW], s_keep[kSpecSelMax * NW];
+  __shared__ uint32_t s_before[kSpecSelMax * NW];
+  __shared__ int s_list[kSpecSelMax * kChunk];
+  __shared__ uint32_t s_base;
+  __shared__ float s_c[GRP];
+  __shared__ uint32_t s_scan[kBlock / kWave + 1];
+  __shared__ int s_best[kBlock / kWave];
+  float rv[TPT], sv[TPT][GRP], nrv[TPT], nsv[TPT][GRP];
+  uint32_t rw[TPT], nrw[TPT];
+  spec_chunk<GRP>(p, b, g, c0 * kChunk, rv, rw, sv);
   spec_norms<GRP>(p, b, g, s_c);
   const int thr = spec_threshold(p, bg, s_scan, s_best);
   float cc[GRP];
 #pragma unroll
   for (int h = 0; h < GRP; ++h) cc[h] = s_c[h];
+  for (int q = 0; q < nc; ++q) {
+    const int t0 = (c0 + q) * kChunk;
+    if (q + 1 < nc) spec_chunk<GRP>(p, b, g, t0 + kChunk, nrv, nrw, nsv);
 #pragma unroll
-  for (int k = 0; k < TPT; ++k) {
-    const int i = t0 + k * kBlock + (int)threadIdx.x;
-    bool sel = false;
-    if (i < p.n && rv[k] < 1.0f && !((rw[k] >> (i % 32)) & 1u)) {
-      float sc = -INFINITY;
+    for (int k = 0; k < TPT; ++k) {
+      const int i = t0 + k * kBlock + (int)threadIdx.x;
+      bool sel = false;
+      if (i < p.n && rv[k] < 1.0f && !((rw[k] >> (i % 32)) & 1u)) {
+        float sc = -INFINITY;
 #pragma unroll
-      for (int h = 0; h < GRP; ++h) sc = fmaxf(sc, sv[k][h] - cc[h]);
-      sc += __logf(1.0f - rv[k]);
-      sel = sc == sc && spec_bin(sc) <= thr;
+        for (int h = 0; h < GRP; ++h) sc = fmaxf(sc, sv[k][h] - cc[h]);
+        sc += __logf(1.0f - rv[k]);
+        sel = sc == sc && spec_bin(sc) <= thr;
+      }
+      if (sel && p.smap_prev) {
+        const int sl = p.smap_prev[(size_t)bg * p.ns + i];
+        sel = !(sl >= 0 && sl < p.fetch_cap);
+      }
+      const unsigned long long m = __ballot(sel);
+      if (lane == 0) {
+        s_bits[q * NW + k * (kBlock / 32) + 2 * wave] = (uint32_t)m;
+        s_bits[q * NW + k * (kBlock / 32) + 2 * wave + 1] = (uint32_t)(m >> 32);
+      }
     }
-    if (sel && p.smap_prev) {
-      const int sl = p.smap_prev[(size_t)bg * p.ns + i];
-      sel = !(sl >= 0 && sl < p.fetch_cap);
-    }
-    const unsigned long long m = __ballot(sel);
-    if (lane == 0) {
-      s_bits[k * (kBlock / 32) + 2 * wave] = (uint32_t)m;
-      s_bits[k * (kBlock / 32) + 2 * wave + 1] = (uint32_t)(m >> 32);
+#pragma unroll
+    for (int k = 0; k < TPT; ++k) {
+      rv[k] = nrv[k];
+      rw[k] = nrw[k];
+#pragma unroll
+      for (int h = 0; h < GRP; ++h) sv[k][h] = nsv[k][h];
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t tot = 0u;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) tot += (uint32_t)__popc(s_bits[w]);
-    s_base = tot > 0u ? atomicAdd(&p.sp_cnt[bg], tot) : 0u;
-  }
+  // the words in (chunk, word) order: one per thread, an exclusive prefix of
+  // their counts, one slot claim for all of them
+  const int nwt = nc * NW;
+  static_assert(kSpecSelMax * NW <= kBlock, "one word per thread");
+  const uint32_t pc = (int)threadIdx.x < nwt ? (uint32_t)__popc(s_bits[threadIdx.x]) : 0u;
+  uint32_t tot;
+  uint32_t before = block_exclusive_scan<uint32_t>(pc, s_scan, &tot);
+  if (threadIdx.x == 0) s_base = tot > 0u ? atomicAdd(&p.sp_cnt[bg], tot) : 0u;
   __syncthreads();
   const uint32_t base = s_base;
   const uint32_t room = base >= (uint32_t)p.spec_m ? 0u : (uint32_t)p.spec_m - base;
-  if (threadIdx.x < NW) {
-    const int w = threadIdx.x;
-    uint32_t before = 0u;
-    for (int v = 0; v < w; ++v) before += (uint32_t)__popc(s_bits[v]);
-    uint32_t bits = s_bits[w];
+  if ((int)threadIdx.x < nwt) {
+    uint32_t bits = s_bits[threadIdx.x];
     // (the rows past the KV head's area: the highest positions go first)
     while (bits != 0u && before + (uint32_t)__popc(bits) > room)
       bits &= ~(1u << (31 - __clz(bits)));
     if (before > room) before = room;
-    s_before[w] = before;
-    const int gw = c * NW + w;
+    s_before[threadIdx.x] = before;
+    s_keep[threadIdx.x] = bits;
+    const int gw = c0 * NW + (int)threadIdx.x;
     if (gw < nw) {
       p.sp_bits[(size_t)bg * nw + gw] = bits;
       p.sp_base[(size_t)bg * nw + gw] = base + before;
     }
-    s_keep[w] = bits;
   }
   __syncthreads();
+  for (int q = 0; q < nc; ++q) {
 #pragma unroll
-  for (int k = 0; k < TPT; ++k) {
-    const int o = k * kBlock + (int)threadIdx.x, w = o / 32, bit = o % 32;
-    const uint32_t wb = s_keep[w];
-    if ((wb >> bit) & 1u)
-      s_list[s_before[w] + (uint32_t)__popc(wb & ((1u << bit) - 1u))] = t0 + o;
+    for (int k = 0; k < TPT; ++k) {
+      const int o = q * kChunk + k * kBlock + (int)threadIdx.x, w = o / 32, bit = o % 32;
+      const uint32_t wb = s_keep[w];
+      if ((wb >> bit) & 1u)
+        s_list[s_before[w] + (uint32_t)__popc(wb & ((1u << bit) - 1u))] = c0 * kChunk + o;
+    }
   }
-  const uint32_t kept = s_before[NW - 1] + (uint32_t)__popc(s_keep[NW - 1]);
+  const uint32_t kept = s_before[nwt - 1] + (uint32_t)__popc(s_keep[nwt - 1]);
   __syncthreads();
   int32_t *list = p.sp_list + (size_t)bg * p.spec_m + base;
   for (uint32_t k = threadIdx.x; k < kept; k += kBlock) list[k] = s_list[k];
@@ -4661,9 +4693,10 @@ hipError_t run(const DParams &p, hipStream_t s, int sd, void **events,
                        dim3((unsigned)((nsamp + kSpecHistSamples - 1) / kSpecHistSamples),
                             (unsigned)p.G, (unsigned)p.B),
                        blk, 0, sx->side, p);
+    const int nchunk = (p.n + kChunk - 1) / kChunk;
     hipLaunchKernelGGL(sp_sel<GRP>,
-                       dim3((unsigned)((p.n + kChunk - 1) / kChunk), (unsigned)p.G,
-                            (unsigned)p.B),
+                       dim3((unsigned)((nchunk + p.spec_cpw - 1) / p.spec_cpw),
+                            (unsigned)p.G, (unsigned)p.B),
                        blk, 0, sx->side, p);
     hipLaunchKernelGGL(sp_move, dim3((unsigned)kSpecMovers), blk,
                        (size_t)kSpecMoveLds, sx->side, p);
@@ -4935,6 +4968,13 @@ hipError_t launch_decode(const vkv_decode_args &a, const DecodeLayout &L,
   p.skey = at<uint32_t>(w, L.skey);
   p.npad = L.npad;
   p.spec_m = L.spec_m;
+  {
+    // selection workgroups: one chunk each while a launch holds about 512,
+    // more chunks per workgroup (at most kSpecSelMax) at large batches
+    const long long nchunk = (a.n_tokens + kChunk - 1) / kChunk;
+    const long long wgs = (long long)a.batch * a.n_kv_heads * nchunk;
+    p.spec_cpw = (int)std::max<long long>(1, std::min<long long>(kSpecSelMax, wgs / 512));
+  }
   if (L.spec_m > 0) {
     p.sp_hist = at<uint32_t>(w, L.sp_hist);
     p.sp_cnt = at<uint32_t>(w, L.sp_cnt);
