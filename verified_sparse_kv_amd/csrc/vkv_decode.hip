@@ -3955,15 +3955,15 @@ __device__ __forceinline__ int spec_bin(float sc) {
 
 // kSpecUnroll samples of a thread (sample k is token (k / kSpecRun) kChunk
 // + k % kSpecRun): position (-1: none), r and the group's plan logits.
-template <int GRP>
+template <int GRP, int U>
 __device__ __forceinline__ void spec_samples(const DParams &p, int b, int g,
                                              int s0, int nsamp,
-                                             int (&ii)[kSpecUnroll],
-                                             float (&rv)[kSpecUnroll],
-                                             float (&sv)[kSpecUnroll][GRP]) {
+                                             int (&ii)[U],
+                                             float (&rv)[U],
+                                             float (&sv)[U][GRP]) {
   const float *rr = p.r + (size_t)(b * p.G + g) * p.ns;
 #pragma unroll
-  for (int u = 0; u < kSpecUnroll; ++u) {
+  for (int u = 0; u < U; ++u) {
     const int sidx = s0 + u * kBlock + (int)threadIdx.x;
     const int i = (sidx / kSpecRun) * kChunk + sidx % kSpecRun;
     ii[u] = sidx < nsamp && i < p.n ? i : -1;
@@ -4013,7 +4013,8 @@ __device__ __forceinline__ void spec_norms(const DParams &p, int b, int g,
 // launch), and this workgroup's share of the resident list into the group's
 // bitmap of S (cleared likewise). The samples are loaded before anything
 // else; the histogram counts the tokens of L, S included.
-constexpr int kSpecHistSamples = kBlock * kSpecUnroll;
+constexpr int kSpecHistUnroll = 2;
+constexpr int kSpecHistSamples = kBlock * kSpecHistUnroll;
 constexpr int kSpecResUnroll = 8;
 template <int GRP>
 __global__ __launch_bounds__(kBlock) void sp_hist(DParams p) {
@@ -4021,9 +4022,9 @@ __global__ __launch_bounds__(kBlock) void sp_hist(DParams p) {
   __shared__ float s_c[GRP];
   __shared__ uint32_t s_hist[kSpecBins];
   const int nsamp = (p.n + kChunk - 1) / kChunk * kSpecRun;
-  int ii[kSpecUnroll];
-  float rv[kSpecUnroll], sv[kSpecUnroll][GRP];
-  spec_samples<GRP>(p, b, g, j * kSpecHistSamples, nsamp, ii, rv, sv);
+  int ii[kSpecHistUnroll];
+  float rv[kSpecHistUnroll], sv[kSpecHistUnroll][GRP];
+  spec_samples<GRP, kSpecHistUnroll>(p, b, g, j * kSpecHistSamples, nsamp, ii, rv, sv);
   const int cnt = min(p.rcount[bg], p.cap);
   int k0, k1;
   split_range(max(cnt, 0), (int)gridDim.x, j, k0, k1);
@@ -4065,7 +4066,7 @@ __global__ __launch_bounds__(kBlock) void sp_hist(DParams p) {
 #pragma unroll
   for (int h = 0; h < GRP; ++h) c[h] = s_c[h];
 #pragma unroll
-  for (int u = 0; u < kSpecUnroll; ++u) {
+  for (int u = 0; u < kSpecHistUnroll; ++u) {
     if (ii[u] < 0 || !(rv[u] < 1.0f)) continue;
     float sc = -INFINITY;
 #pragma unroll
