@@ -138,3 +138,26 @@ def test_with_staging():
         _same(staged, plain)
         if t < 2:
             sv.append()
+
+
+def test_noalloc_reads_nothing_ahead():
+    """The no-allocation entry point takes prefetch_rows as 0: asked for the
+    library's count, it gives the plain step's outputs and host bytes."""
+    w = gc.build_case("c2", n=5000, G=2, seed=5)
+    dev = gc.device_inputs(w)
+    plain = _run(w, dev, 0)
+    step = vk.DecodeStep(w["B"], w["Hq"], w["G"], w["n"], w["s"], w["cap"],
+                         w["n"], gc.torch_mod().device("cuda"), prefetch_rows=-1)
+    assert vk.vkv_decode_prefetch_rows(step.args) > 0
+    step.bind(dev["q"], dev["resident_kv"], dev["resident_idx"],
+              dev["resident_count"], dev["sketch"], dev["proj"], dev["r"],
+              dev["host_kv"], w["eps"], w["delta"])
+    step.args.workspace = None
+    step.args.workspace_bytes = 0
+    assert vk.vkv_decode_step_noalloc(step.args, vk._stream(None)) == vk.VKV_OK, \
+        vk.vkv_last_error()
+    rc, bits = step.check_status()
+    assert rc == 0, bits
+    got = {k: v.cpu().numpy() for k, v in step.out.items()}
+    _same(got, plain)
+    assert int(got["host_bytes"][0]) == int(plain["host_bytes"][0])
